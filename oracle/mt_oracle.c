@@ -1,0 +1,426 @@
+/*
+ * mt_oracle.c -- plain CPU oracle for the MuScriptor INT4 decoder step.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  It shares no code,
+ * header, table or helper with the HIP library; both sides are fed from the
+ * seeded input generator and nothing else.
+ *
+ * What it computes (the quantised model, written out by definition):
+ *   - weights: symmetric round-to-nearest INT4 with groups of 32 along the
+ *     input axis, FP32 scale per group (medium ONNX README, "Model variant":
+ *     backbone projections are symmetric RTN INT4 with group size 32);
+ *   - everything else in FP32 (same table: activations, KV cache,
+ *     embeddings and LM head stay FP32);
+ *   - one decoder call appends P prefix rows and S token rows at position
+ *     T_past of a fixed-capacity cache [L, B, T_cap, H, 64] and returns the
+ *     logits of the last row (small ONNX conversion page, decoder inputs and
+ *     outputs; medium ONNX README, "Model variant", for the fixed-capacity
+ *     shared past/present buffer);
+ *   - greedy argmax (small ONNX conversion page; model card, "Model
+ *     description").
+ *
+ * Readings where the pages are silent (all listed in the design notes):
+ * pre-norm residual blocks with LayerNorm (eps 1e-5, biased variance, gain and
+ * bias), four bias-free projections per layer (fused QKV ordered Q|K|V,
+ * O, FFN-up, FFN-down), exact-erf GELU, attention scale 1/8, attention causal
+ * over the whole cache including the prefix, no positional term, a final
+ * LayerNorm before an untied LM head, round-half-to-even in the quantiser,
+ * low nibble = even input index, lowest index wins an argmax tie.
+ *
+ * Precision: every named tensor is stored as binary32; every dot product,
+ * LayerNorm moment, softmax and GELU is evaluated in binary64 and rounded once.
+ * Must be compiled without fast-math and with FP contraction off.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_OK 0
+#define ORACLE_EINVAL (-1)
+#define ORACLE_EFULL (-2)
+#define ORACLE_ENOMEM (-4)
+
+/* ------------------------------------------------------------------ */
+/* Quantise one [N, K] FP32 matrix to INT4, groups of 32 along K.
+ *   m = max |w| over the group; s = m / 7 (binary32 division);
+ *   q = clamp(rint(w / s), -8, 7) (binary32 division, ties to even);
+ *   an all-zero group (s == 0) gets q = 0;
+ *   stored as u = q + 8; byte j of a row holds u[2j] in its low nibble and
+ *   u[2j+1] in its high nibble.  q is [N, K/2] bytes, s is [N, K/32]. */
+int oracle_quantize_int4(const float* W, int64_t N, int64_t K, uint8_t* q, float* s)
+{
+    if (!W || !q || !s || N < 0 || K <= 0 || K % 32 != 0) return ORACLE_EINVAL;
+    const int64_t ng = K / 32;
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t g = 0; g < ng; ++g) {
+            const float* w = W + n * K + g * 32;
+            float m = 0.0f;
+            for (int k = 0; k < 32; ++k) {
+                float a = fabsf(w[k]);
+                if (a > m) m = a;
+            }
+            float sc = m / 7.0f;
+            s[n * ng + g] = sc;
+            for (int k = 0; k < 32; ++k) {
+                int code = 0;
+                if (sc != 0.0f) {
+                    float r = rintf(w[k] / sc);
+                    if (r < -8.0f) r = -8.0f;
+                    if (r > 7.0f) r = 7.0f;
+                    code = (int)r;
+                }
+                uint8_t u = (uint8_t)(code + 8);
+                int64_t byte = (n * K + g * 32 + k) / 2;
+                if ((k & 1) == 0)
+                    q[byte] = (uint8_t)((q[byte] & 0xF0u) | u);
+                else
+                    q[byte] = (uint8_t)((q[byte] & 0x0Fu) | (uint8_t)(u << 4));
+            }
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* w'[n,k] = (float)(u - 8) * s[n, k/32]: one binary32 multiply. */
+int oracle_dequantize_int4(const uint8_t* q, const float* s, int64_t N, int64_t K, float* Wd)
+{
+    if (!q || !s || !Wd || N < 0 || K <= 0 || K % 32 != 0) return ORACLE_EINVAL;
+    const int64_t ng = K / 32;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            uint8_t byte = q[(n * K + k) / 2];
+            int u = (k & 1) ? (byte >> 4) : (byte & 0x0F);
+            float qv = (float)(u - 8);
+            Wd[n * K + k] = qv * s[n * ng + k / 32];
+        }
+    return ORACLE_OK;
+}
+
+/* Y[m, n] = sum_k A[m, k] * W[n, k], binary64 sum, rounded once. */
+int oracle_matmul(const float* A, int64_t M, int64_t K, const float* W, int64_t N, float* Y)
+{
+    if (!A || !W || !Y || M < 0 || N < 0 || K < 0) return ORACLE_EINVAL;
+    /* Loop over output features outermost so each weight row is read once. */
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        const float* w = W + n * K;
+        for (int64_t m = 0; m < M; ++m) {
+            const float* a = A + m * K;
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; ++k) acc += (double)a[k] * (double)w[k];
+            Y[m * N + n] = (float)acc;
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* y = (x - mean) / sqrt(var + eps) * g + b, biased variance, per row. */
+int oracle_layernorm(const float* X, int64_t M, int64_t d, const float* g, const float* b,
+                     float eps, float* Y)
+{
+    if (!X || !g || !b || !Y || M < 0 || d <= 0) return ORACLE_EINVAL;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        const float* x = X + m * d;
+        double mu = 0.0;
+        for (int64_t j = 0; j < d; ++j) mu += (double)x[j];
+        mu /= (double)d;
+        double var = 0.0;
+        for (int64_t j = 0; j < d; ++j) {
+            double c = (double)x[j] - mu;
+            var += c * c;
+        }
+        var /= (double)d;
+        double rstd = 1.0 / sqrt(var + (double)eps);
+        for (int64_t j = 0; j < d; ++j)
+            Y[m * d + j] = (float)(((double)x[j] - mu) * rstd * (double)g[j] + (double)b[j]);
+    }
+    return ORACLE_OK;
+}
+
+/* GELU, exact erf form, evaluated in binary64. */
+static float gelu1(float x)
+{
+    double v = (double)x;
+    return (float)(0.5 * v * (1.0 + erf(v / sqrt(2.0))));
+}
+
+int oracle_gelu(const float* X, int64_t n, float* Y)
+{
+    if (!X || !Y || n < 0) return ORACLE_EINVAL;
+    for (int64_t i = 0; i < n; ++i) Y[i] = gelu1(X[i]);
+    return ORACLE_OK;
+}
+
+/* One query row against T cached keys of one head.
+ *   score_t = (q . K_t) * 0.125 ; p = softmax(score) ; out = sum_t p_t V_t
+ * k and v point at key/value 0 of this head; consecutive positions are
+ * `stride` floats apart.  Computed in binary64, rounded once. */
+static void attend_row(const float* qh, const float* k, const float* v, int64_t T,
+                       int64_t stride, double* scratch, float* out)
+{
+    double mx = -INFINITY;
+    for (int64_t t = 0; t < T; ++t) {
+        const float* kt = k + t * stride;
+        double acc = 0.0;
+        for (int j = 0; j < 64; ++j) acc += (double)qh[j] * (double)kt[j];
+        scratch[t] = acc * 0.125;
+        if (scratch[t] > mx) mx = scratch[t];
+    }
+    double den = 0.0;
+    for (int64_t t = 0; t < T; ++t) {
+        scratch[t] = exp(scratch[t] - mx);
+        den += scratch[t];
+    }
+    for (int j = 0; j < 64; ++j) {
+        double acc = 0.0;
+        for (int64_t t = 0; t < T; ++t) acc += scratch[t] * (double)v[t * stride + j];
+        out[j] = (float)(acc / den);
+    }
+}
+
+/* Attention for one row, all heads: q [H*64]; kc/vc [T, H, 64]; out [H*64]. */
+int oracle_attention(const float* q, const float* kc, const float* vc, int64_t T, int64_t H,
+                     float* out)
+{
+    if (!q || !kc || !vc || !out || T < 1 || H < 1) return ORACLE_EINVAL;
+    double* scratch = (double*)malloc(sizeof(double) * (size_t)T);
+    if (!scratch) return ORACLE_ENOMEM;
+    for (int64_t h = 0; h < H; ++h)
+        attend_row(q + h * 64, kc + h * 64, vc + h * 64, T, H * 64, scratch, out + h * 64);
+    free(scratch);
+    return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* The model: B sequences advancing in lockstep over a shared T_past.      */
+
+typedef struct {
+    int64_t L, d, H, F, V, B, Tcap;
+    float eps;
+    int64_t tpast;
+    float* tok_emb; /* [V, d] */
+    float* lm_head; /* [V, d] */
+    float* lnf;     /* [2, d] gain, bias */
+    float** wqkv;   /* dequantised [3d, d] */
+    float** wo;     /* [d, d] */
+    float** wup;    /* [F, d] */
+    float** wdown;  /* [d, F] */
+    float** ln;     /* [4, d]: g1, b1, g2, b2 */
+    float* kc;      /* [L, B, Tcap, H, 64] */
+    float* vc;
+} oracle_model;
+
+static void model_free(oracle_model* m)
+{
+    if (!m) return;
+    if (m->wqkv)
+        for (int64_t l = 0; l < m->L; ++l) {
+            free(m->wqkv[l]); free(m->wo[l]); free(m->wup[l]); free(m->wdown[l]); free(m->ln[l]);
+        }
+    free(m->wqkv); free(m->wo); free(m->wup); free(m->wdown); free(m->ln);
+    free(m->tok_emb); free(m->lm_head); free(m->lnf); free(m->kc); free(m->vc);
+    free(m);
+}
+
+void oracle_model_free(oracle_model* m) { model_free(m); }
+
+oracle_model* oracle_model_new(int64_t L, int64_t d, int64_t H, int64_t F, int64_t V,
+                               int64_t B, int64_t Tcap, float eps)
+{
+    if (L < 1 || d < 32 || d % 32 || H < 1 || H * 64 != d || F < 32 || F % 32 || V < 1 ||
+        B < 1 || Tcap < 1)
+        return NULL;
+    oracle_model* m = (oracle_model*)calloc(1, sizeof(oracle_model));
+    if (!m) return NULL;
+    m->L = L; m->d = d; m->H = H; m->F = F; m->V = V; m->B = B; m->Tcap = Tcap; m->eps = eps;
+    m->wqkv = (float**)calloc((size_t)L, sizeof(float*));
+    m->wo = (float**)calloc((size_t)L, sizeof(float*));
+    m->wup = (float**)calloc((size_t)L, sizeof(float*));
+    m->wdown = (float**)calloc((size_t)L, sizeof(float*));
+    m->ln = (float**)calloc((size_t)L, sizeof(float*));
+    m->tok_emb = (float*)calloc((size_t)(V * d), sizeof(float));
+    m->lm_head = (float*)calloc((size_t)(V * d), sizeof(float));
+    m->lnf = (float*)calloc((size_t)(2 * d), sizeof(float));
+    size_t kv = (size_t)(L * B * Tcap * d);
+    m->kc = (float*)calloc(kv, sizeof(float));
+    m->vc = (float*)calloc(kv, sizeof(float));
+    if (!m->wqkv || !m->wo || !m->wup || !m->wdown || !m->ln || !m->tok_emb || !m->lm_head ||
+        !m->lnf || !m->kc || !m->vc) {
+        model_free(m);
+        return NULL;
+    }
+    return m;
+}
+
+int oracle_model_set_embed(oracle_model* m, const float* tok_emb, const float* lm_head,
+                           const float* lnf_g, const float* lnf_b)
+{
+    if (!m || !tok_emb || !lm_head || !lnf_g || !lnf_b) return ORACLE_EINVAL;
+    memcpy(m->tok_emb, tok_emb, sizeof(float) * (size_t)(m->V * m->d));
+    memcpy(m->lm_head, lm_head, sizeof(float) * (size_t)(m->V * m->d));
+    memcpy(m->lnf, lnf_g, sizeof(float) * (size_t)m->d);
+    memcpy(m->lnf + m->d, lnf_b, sizeof(float) * (size_t)m->d);
+    return ORACLE_OK;
+}
+
+/* Quantise then dequantise one FP32 projection into a fresh buffer. */
+static float* quant_dequant(const float* W, int64_t N, int64_t K)
+{
+    uint8_t* q = (uint8_t*)calloc((size_t)(N * K / 2), 1);
+    float* s = (float*)malloc(sizeof(float) * (size_t)(N * K / 32));
+    float* wd = (float*)malloc(sizeof(float) * (size_t)(N * K));
+    if (!q || !s || !wd) { free(q); free(s); free(wd); return NULL; }
+    oracle_quantize_int4(W, N, K, q, s);
+    oracle_dequantize_int4(q, s, N, K, wd);
+    free(q); free(s);
+    return wd;
+}
+
+/* Layer l from FP32 weights (quantised here).  If `quantize` is 0 the
+ * matrices are taken as already dequantised values (used by closed-form
+ * tests whose weights are exactly representable). */
+int oracle_model_set_layer(oracle_model* m, int64_t l, const float* wqkv, const float* wo,
+                           const float* wup, const float* wdown, const float* g1,
+                           const float* b1, const float* g2, const float* b2, int quantize)
+{
+    if (!m || l < 0 || l >= m->L || !wqkv || !wo || !wup || !wdown || !g1 || !b1 || !g2 || !b2)
+        return ORACLE_EINVAL;
+    const int64_t d = m->d, F = m->F;
+    free(m->wqkv[l]); free(m->wo[l]); free(m->wup[l]); free(m->wdown[l]); free(m->ln[l]);
+    m->wqkv[l] = m->wo[l] = m->wup[l] = m->wdown[l] = m->ln[l] = NULL;
+    if (quantize) {
+        m->wqkv[l] = quant_dequant(wqkv, 3 * d, d);
+        m->wo[l] = quant_dequant(wo, d, d);
+        m->wup[l] = quant_dequant(wup, F, d);
+        m->wdown[l] = quant_dequant(wdown, d, F);
+    } else {
+        m->wqkv[l] = (float*)malloc(sizeof(float) * (size_t)(3 * d * d));
+        m->wo[l] = (float*)malloc(sizeof(float) * (size_t)(d * d));
+        m->wup[l] = (float*)malloc(sizeof(float) * (size_t)(F * d));
+        m->wdown[l] = (float*)malloc(sizeof(float) * (size_t)(d * F));
+        if (m->wqkv[l]) memcpy(m->wqkv[l], wqkv, sizeof(float) * (size_t)(3 * d * d));
+        if (m->wo[l]) memcpy(m->wo[l], wo, sizeof(float) * (size_t)(d * d));
+        if (m->wup[l]) memcpy(m->wup[l], wup, sizeof(float) * (size_t)(F * d));
+        if (m->wdown[l]) memcpy(m->wdown[l], wdown, sizeof(float) * (size_t)(d * F));
+    }
+    m->ln[l] = (float*)malloc(sizeof(float) * (size_t)(4 * d));
+    if (!m->wqkv[l] || !m->wo[l] || !m->wup[l] || !m->wdown[l] || !m->ln[l]) return ORACLE_ENOMEM;
+    memcpy(m->ln[l], g1, sizeof(float) * (size_t)d);
+    memcpy(m->ln[l] + d, b1, sizeof(float) * (size_t)d);
+    memcpy(m->ln[l] + 2 * d, g2, sizeof(float) * (size_t)d);
+    memcpy(m->ln[l] + 3 * d, b2, sizeof(float) * (size_t)d);
+    return ORACLE_OK;
+}
+
+int64_t oracle_model_position(const oracle_model* m) { return m ? m->tpast : -1; }
+
+void oracle_model_reset(oracle_model* m)
+{
+    if (m) m->tpast = 0;
+}
+
+int oracle_model_kv(oracle_model* m, float** k, float** v)
+{
+    if (!m || !k || !v) return ORACLE_EINVAL;
+    *k = m->kc;
+    *v = m->vc;
+    return ORACLE_OK;
+}
+
+/* One decoder call.  tokens [B, S] (may be NULL when S == 0), prefix
+ * [B, P, d] (may be NULL when P == 0).  Rows [prefix ; embed(tokens)] are
+ * appended at positions T_past .. T_past+P+S-1.  logits [B, V] and next [B]
+ * are those of the last appended row.  hidden_out, if not NULL, receives
+ * the final-LayerNorm output of the last row [B, d]. */
+int oracle_model_forward(oracle_model* m, const int64_t* tokens, int64_t S, const float* prefix,
+                         int64_t P, float* logits, int64_t* next, float* hidden_out)
+{
+    if (!m || S < 0 || P < 0 || P + S < 1 || !logits || !next) return ORACLE_EINVAL;
+    if ((S > 0 && !tokens) || (P > 0 && !prefix)) return ORACLE_EINVAL;
+    for (int64_t l = 0; l < m->L; ++l)
+        if (!m->wqkv[l] || !m->ln[l]) return ORACLE_EINVAL;
+    const int64_t L = m->L, d = m->d, H = m->H, F = m->F, V = m->V, B = m->B, Tc = m->Tcap;
+    const int64_t R = P + S, t0 = m->tpast;
+    if (t0 + R > Tc) return ORACLE_EFULL;
+    for (int64_t i = 0; i < B * S; ++i)
+        if (tokens[i] < 0 || tokens[i] >= V) return ORACLE_EINVAL;
+
+    const int64_t rows = B * R;
+    float* r = (float*)malloc(sizeof(float) * (size_t)(rows * d));
+    float* a = (float*)malloc(sizeof(float) * (size_t)(rows * d));
+    float* qkv = (float*)malloc(sizeof(float) * (size_t)(rows * 3 * d));
+    float* att = (float*)malloc(sizeof(float) * (size_t)(rows * d));
+    float* o = (float*)malloc(sizeof(float) * (size_t)(rows * d));
+    float* h1 = (float*)malloc(sizeof(float) * (size_t)(rows * F));
+    if (!r || !a || !qkv || !att || !o || !h1) {
+        free(r); free(a); free(qkv); free(att); free(o); free(h1);
+        return ORACLE_ENOMEM;
+    }
+
+    /* Rows of sequence b are r[(b*R + i) * d].  Prefix rows first, then the
+     * embeddings of the token ids (no scaling, no positional term). */
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t i = 0; i < R; ++i) {
+            const float* src = (i < P) ? prefix + (b * P + i) * d
+                                       : m->tok_emb + tokens[b * S + (i - P)] * d;
+            memcpy(r + (b * R + i) * d, src, sizeof(float) * (size_t)d);
+        }
+
+    for (int64_t l = 0; l < L; ++l) {
+        const float* ln = m->ln[l];
+        oracle_layernorm(r, rows, d, ln, ln + d, m->eps, a);
+        oracle_matmul(a, rows, d, m->wqkv[l], 3 * d, qkv);
+        /* cache write: K = columns [d, 2d), V = [2d, 3d); head h = 64 columns */
+        for (int64_t b = 0; b < B; ++b)
+            for (int64_t i = 0; i < R; ++i) {
+                const float* row = qkv + (b * R + i) * 3 * d;
+                int64_t slot = (((l * B + b) * Tc) + t0 + i) * d;
+                memcpy(m->kc + slot, row + d, sizeof(float) * (size_t)d);
+                memcpy(m->vc + slot, row + 2 * d, sizeof(float) * (size_t)d);
+            }
+        /* causal attention: row i sees cache positions [0, t0 + i] */
+#pragma omp parallel
+        {
+            double* scratch = (double*)malloc(sizeof(double) * (size_t)(t0 + R));
+#pragma omp for collapse(3) schedule(static)
+            for (int64_t b = 0; b < B; ++b)
+                for (int64_t i = 0; i < R; ++i)
+                    for (int64_t h = 0; h < H; ++h) {
+                        const float* qh = qkv + (b * R + i) * 3 * d + h * 64;
+                        int64_t base = ((l * B + b) * Tc) * d + h * 64;
+                        attend_row(qh, m->kc + base, m->vc + base, t0 + i + 1, d, scratch,
+                                   att + (b * R + i) * d + h * 64);
+                    }
+            free(scratch);
+        }
+        oracle_matmul(att, rows, d, m->wo[l], d, o);
+        for (int64_t j = 0; j < rows * d; ++j) r[j] = r[j] + o[j];
+        oracle_layernorm(r, rows, d, ln + 2 * d, ln + 3 * d, m->eps, a);
+        oracle_matmul(a, rows, d, m->wup[l], F, h1);
+        oracle_gelu(h1, rows * F, h1);
+        oracle_matmul(h1, rows, F, m->wdown[l], d, o);
+        for (int64_t j = 0; j < rows * d; ++j) r[j] = r[j] + o[j];
+    }
+
+    /* final LayerNorm and LM head on the last row of each sequence */
+    for (int64_t b = 0; b < B; ++b) {
+        const float* last = r + (b * R + R - 1) * d;
+        float* z = a + b * d;
+        oracle_layernorm(last, 1, d, m->lnf, m->lnf + d, m->eps, z);
+        if (hidden_out) memcpy(hidden_out + b * d, z, sizeof(float) * (size_t)d);
+    }
+    oracle_matmul(a, B, d, m->lm_head, V, logits);
+    for (int64_t b = 0; b < B; ++b) {
+        const float* lg = logits + b * V;
+        int64_t best = 0;
+        for (int64_t v = 1; v < V; ++v)
+            if (lg[v] > lg[best]) best = v;
+        next[b] = best;
+    }
+    m->tpast = t0 + R;
+    free(r); free(a); free(qkv); free(att); free(o); free(h1);
+    return ORACLE_OK;
+}

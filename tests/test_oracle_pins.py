@@ -1,0 +1,388 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle:
+hand-computed fixtures, closed forms, special cases that reduce to a
+textbook identity or a library routine, invariants and exact brute force on
+tiny inputs.  Each test names the mistake it is there to catch."""
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from audio_midi_transformer_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _read_int4_fixture():
+    cases = []
+    with open(os.path.join(GOLDEN, "int4_groups.txt")) as fh:
+        for line in fh:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            name, k, w, scales, hexbytes = [x.strip() for x in line.split("|")]
+            k = int(k)
+            row = np.zeros((1, k), dtype=np.float32)
+            vals = [float(x) for x in w.split()] if w else []
+            row[0, :len(vals)] = vals
+            cases.append((name, row, np.array([float(x) for x in scales.split()], np.float32),
+                          bytes(int(x, 16) for x in hexbytes.split())))
+    return cases
+
+
+# ---------------------------------------------------------------- quantiser
+
+@pytest.mark.parametrize("case", _read_int4_fixture(), ids=lambda c: c[0])
+def test_quantize_hand_fixture(oracle_mod, case):
+    """Hand-derived bytes and scales: catches nibble order, group axis,
+    rounding mode (ties to even), /7 scale and zero point 8."""
+    name, row, scales, expect = case
+    q, s = oracle_mod.quantize_int4(row)
+    assert s[0].tolist() == scales.tolist(), name
+    assert bytes(q[0].tobytes()) == expect, name
+
+
+def test_quantize_error_bound_and_range(oracle_mod):
+    """|w - deq| <= s/2 (plus the few-ulp rounding of w/s and q*s); codes
+    stay in [-7, 7]; the largest |w| of every group maps to +-7 exactly."""
+    rng = np.random.default_rng(5)
+    for scale in (0.02, 1.0, 3e-4):
+        W = (rng.standard_normal((48, 256)) * scale).astype(np.float32)
+        W[3, 32:64] = 0.0  # an all-zero group
+        q, s = oracle_mod.quantize_int4(W)
+        lo = (q & 0x0F).astype(np.int64)
+        hi = (q >> 4).astype(np.int64)
+        u = np.empty((48, 256), np.int64)
+        u[:, 0::2], u[:, 1::2] = lo, hi
+        code = u - 8
+        assert code.min() >= -7 and code.max() <= 7
+        wd = oracle_mod.dequantize_int4(q, s)
+        sg = np.repeat(s.astype(np.float64), 32, axis=1)
+        err = np.abs(W.astype(np.float64) - wd.astype(np.float64))
+        assert np.all(err <= sg * (0.5 + 16 * 2.0 ** -24) + 1e-45)
+        groups = np.abs(W).reshape(48, 8, 32)
+        arg = groups.argmax(axis=2)
+        cg = np.abs(code.reshape(48, 8, 32))
+        picked = np.take_along_axis(cg, arg[..., None], axis=2)[..., 0]
+        nonzero = groups.max(axis=2) > 0
+        assert np.all(picked[nonzero] == 7)
+        assert np.all(s[~nonzero] == 0) and np.all(code.reshape(48, 8, 32)[~nonzero] == 0)
+
+
+def test_quantize_idempotent(oracle_mod):
+    """Re-quantising the dequantised matrix returns the same codes and scales."""
+    W = synth.random_matrix(7, 64, 512)
+    q, s = oracle_mod.quantize_int4(W)
+    q2, s2 = oracle_mod.quantize_int4(oracle_mod.dequantize_int4(q, s))
+    assert np.array_equal(q, q2) and np.array_equal(s, s2)
+
+
+def test_dequantize_power_of_two_exact(oracle_mod):
+    """With power-of-two scales every dequantised weight is exactly code * s;
+    catches an off-by-one zero point or a swapped nibble in the reader."""
+    rng = np.random.default_rng(3)
+    u = rng.integers(0, 16, size=(8, 64))
+    q = (u[:, 0::2] | (u[:, 1::2] << 4)).astype(np.uint8)
+    s = (2.0 ** rng.integers(-10, 4, size=(8, 2))).astype(np.float32)
+    wd = oracle_mod.dequantize_int4(q, s)
+    expect = (u - 8) * np.repeat(s.astype(np.float64), 32, axis=1)
+    assert np.array_equal(wd.astype(np.float64), expect)
+
+
+# ---------------------------------------------------------------- matmul
+
+def test_matmul_exact_brute_force(oracle_mod):
+    """Tiny non-square A . W^T against exact rational arithmetic; the result
+    is the exact sum rounded once (catches a transposed operand or a dropped
+    term)."""
+    rng = np.random.default_rng(11)
+    A = rng.standard_normal((3, 40)).astype(np.float32)
+    W = rng.standard_normal((5, 40)).astype(np.float32)
+    Y = oracle_mod.matmul(A, W)
+    assert Y.shape == (3, 5)
+    for m in range(3):
+        for n in range(5):
+            exact = sum(Fraction(float(A[m, k])) * Fraction(float(W[n, k])) for k in range(40))
+            assert abs(Fraction(float(Y[m, n])) - exact) <= abs(exact) * Fraction(1, 2 ** 23) + Fraction(1, 2 ** 120)
+
+
+def test_matmul_one_hot_column(oracle_mod):
+    """e_k . W^T returns column k of W exactly."""
+    W = synth.random_matrix(2, 24, 96)
+    A = np.zeros((96, 96), np.float32)
+    np.fill_diagonal(A, 1.0)
+    Y = oracle_mod.matmul(A, W)
+    assert np.array_equal(Y, W.T)
+
+
+# ---------------------------------------------------------------- LayerNorm, GELU
+
+def test_layernorm_closed_forms(oracle_mod):
+    d = 64
+    g = np.linspace(0.5, 1.5, d).astype(np.float32)
+    b = np.linspace(-1, 1, d).astype(np.float32)
+    # constant row -> x - mean == 0 -> output is the bias exactly
+    y = oracle_mod.layernorm(np.full((1, d), 3.25, np.float32), g, b)
+    assert np.array_equal(y[0], b)
+    # unit gain, zero bias: mean 0, variance var/(var+eps)
+    x = np.random.default_rng(1).standard_normal((4, d)).astype(np.float32) * 3
+    y = oracle_mod.layernorm(x, np.ones(d, np.float32), np.zeros(d, np.float32)).astype(np.float64)
+    var = x.astype(np.float64).var(axis=1)
+    assert np.allclose(y.mean(axis=1), 0, atol=1e-6)
+    assert np.allclose(y.var(axis=1), var / (var + 1e-5), rtol=1e-6)
+    # [1, 2, 3, 4] with gain 2 and bias 1: (x - 2.5) / sqrt(1.25 + 1e-5) * 2 + 1
+    y = oracle_mod.layernorm(np.array([[1, 2, 3, 4]], np.float32), np.full(4, 2, np.float32),
+                             np.ones(4, np.float32))
+    want = [(v - 2.5) / math.sqrt(1.25 + 1e-5) * 2 + 1 for v in (1, 2, 3, 4)]
+    assert np.allclose(y[0], want, rtol=0, atol=2e-7)
+
+
+def test_gelu_closed_forms(oracle_mod):
+    x = np.linspace(-6, 6, 241).astype(np.float32)
+    y = oracle_mod.gelu(x).astype(np.float64)
+    ym = oracle_mod.gelu(-x).astype(np.float64)
+    assert oracle_mod.gelu(np.zeros(1, np.float32))[0] == 0.0
+    assert np.allclose(y - ym, x, atol=4e-7)           # x*Phi(x) - (-x)*Phi(-x) = x
+    # Phi(1) = 0.8413447460685429 (standard normal CDF); the tanh form is 1.5e-4 off
+    assert abs(oracle_mod.gelu(np.ones(1, np.float32))[0] - 0.8413447460685429) < 1e-7
+    # Phi(-2) = 0.022750131948179195
+    assert abs(oracle_mod.gelu(np.full(1, -2, np.float32))[0] - (-2 * 0.022750131948179195)) < 1e-7
+
+
+# ---------------------------------------------------------------- attention
+
+def test_attention_single_key_returns_value(oracle_mod):
+    rng = np.random.default_rng(4)
+    q = rng.standard_normal((3, 64)).astype(np.float32)
+    k = rng.standard_normal((1, 3, 64)).astype(np.float32)
+    v = rng.standard_normal((1, 3, 64)).astype(np.float32)
+    assert np.array_equal(oracle_mod.attention(q, k, v), v[0])
+
+
+def test_attention_zero_query_is_mean(oracle_mod):
+    rng = np.random.default_rng(6)
+    k = rng.standard_normal((37, 2, 64)).astype(np.float32)
+    v = rng.standard_normal((37, 2, 64)).astype(np.float32)
+    out = oracle_mod.attention(np.zeros((2, 64), np.float32), k, v)
+    assert np.allclose(out, v.astype(np.float64).mean(axis=0), rtol=0, atol=1e-7)
+
+
+def test_attention_two_keys_logistic(oracle_mod):
+    """q . K0 = 8 and q . K1 = 0: with the 1/8 scale the scores are 1 and 0,
+    so the weights are e/(1+e) and 1/(1+e) (catches a missing scale or a sign);
+    the second head is independent (catches a head-stride mistake)."""
+    q = np.zeros((2, 64), np.float32)
+    q[0, 5] = 8.0
+    q[1, 9] = -16.0
+    k = np.zeros((2, 2, 64), np.float32)
+    k[0, 0, 5] = 1.0
+    k[1, 1, 9] = 1.0
+    v = np.zeros((2, 2, 64), np.float32)
+    v[0, :, 0] = 1.0
+    v[1, :, 1] = 1.0
+    out = oracle_mod.attention(q, k, v)
+    p0 = math.e / (1 + math.e)
+    assert abs(out[0, 0] - p0) < 1e-7 and abs(out[0, 1] - (1 - p0)) < 1e-7
+    # head 1: scores 0 and -2 -> weights 1/(1+e^-2), e^-2/(1+e^-2)
+    p1 = 1 / (1 + math.exp(-2))
+    assert abs(out[1, 0] - p1) < 1e-7 and abs(out[1, 1] - (1 - p1)) < 1e-7
+
+
+def test_attention_softmax_sums_to_one(oracle_mod):
+    """All values equal to 1 -> output 1 whatever the scores (weights sum to 1)."""
+    rng = np.random.default_rng(8)
+    q = rng.standard_normal((1, 64)).astype(np.float32) * 3
+    k = rng.standard_normal((300, 1, 64)).astype(np.float32)
+    v = np.ones((300, 1, 64), np.float32)
+    assert np.allclose(oracle_mod.attention(q, k, v), 1.0, atol=300 * 2.0 ** -24)
+
+
+# ---------------------------------------------------------------- whole model
+
+def _ln64(x, g, b, eps=1e-5):
+    x = np.asarray(x, np.float64)
+    mu = x.mean(-1, keepdims=True)
+    var = ((x - mu) ** 2).mean(-1, keepdims=True)
+    return (x - mu) / np.sqrt(var + eps) * g + b
+
+
+def _tiny_weights(shape, seed=21):
+    return synth.model_weights(shape, seed)
+
+
+def test_model_zero_projections(oracle_mod):
+    """All four projections zero: qkv = attn = o = 0 and f = GELU(0) W = 0, so
+    the residual is the input row and logits = W_lm . LN_f(x_last)."""
+    shape = synth.tiny_shape(n_layers=2, d_model=64, n_heads=1, d_ff=128, vocab=53)
+    w = _tiny_weights(shape)
+    for l in range(shape.n_layers):
+        for lst in (w.w_qkv, w.w_o, w.w_up, w.w_down):
+            lst[l] = np.zeros_like(lst[l])
+    B, P, S = 2, 3, 2
+    rng = np.random.default_rng(2)
+    prefix = rng.standard_normal((B, P, 64)).astype(np.float32)
+    tokens = rng.integers(0, 53, size=(B, S))
+    m = oracle_mod.OracleModel.from_weights(w, batch=B, t_cap=16)
+    logits, nxt = m.forward(tokens=tokens, prefix=prefix)
+    for b in range(B):
+        z = _ln64(w.tok_emb[tokens[b, -1]], w.lnf_g, w.lnf_b)
+        want = w.lm_head.astype(np.float64) @ z
+        assert np.allclose(logits[b], want, rtol=0, atol=2e-6)
+        assert nxt[b] == int(np.argmax(logits[b]))
+    # prefix only: last row is the last prefix row
+    m.reset()
+    logits, _ = m.forward(prefix=prefix)
+    z = _ln64(prefix[1, -1], w.lnf_g, w.lnf_b)
+    assert np.allclose(logits[1], w.lm_head.astype(np.float64) @ z, atol=2e-6)
+    assert m.position == P
+
+
+def _perm(n, seed):
+    p = np.random.default_rng(seed).permutation(n)
+    M = np.zeros((n, n), np.float32)
+    M[np.arange(n), p] = 1.0
+    return M
+
+
+def _gelu64(x):
+    from scipy.special import erf
+    return 0.5 * x * (1 + erf(x / np.sqrt(2)))
+
+
+def test_model_permutation_closed_form(oracle_mod):
+    """Exactly representable 0/1 weights give a closed form the pages' steps
+    reduce to: Q = 0 (uniform causal attention), K and V permutations (checks
+    the Q|K|V split and the cache layout [L,B,T,H,64]), O, FFN-up and
+    FFN-down permutations (checks operand orientation, GELU and both residual
+    adds).  Two layers make layer 1's cache depend on layer 0's causal means."""
+    d, F, V, L, H = 128, 256, 41, 2, 2
+    shape = synth.tiny_shape(n_layers=L, d_model=d, n_heads=H, d_ff=F, vocab=V)
+    w = _tiny_weights(shape, seed=5)
+    Pk, Pv, Po, Pu, Pd = (_perm(d, s) for s in (1, 2, 3, 4, 5))
+    for l in range(L):
+        qkv = np.zeros((3 * d, d), np.float32)
+        qkv[d:2 * d] = Pk
+        qkv[2 * d:] = Pv
+        up = np.zeros((F, d), np.float32)
+        up[:d] = Pu
+        down = np.zeros((d, F), np.float32)
+        down[:, d:] = Pd          # reads the second half of the FFN width
+        up[d:2 * d] = Pu.T        # ... which holds a different permutation
+        w.w_qkv[l], w.w_o[l], w.w_up[l], w.w_down[l] = qkv, Po, up, down
+    B, R = 1, 6
+    x = np.random.default_rng(9).standard_normal((B, R, d)).astype(np.float32)
+    m = oracle_mod.OracleModel.from_weights(w, batch=B, t_cap=8, quantize=False)
+    logits, _ = m.forward(prefix=x)
+    K, Vc = m.kv()
+    r = x[0].astype(np.float64)
+    for l in range(L):
+        a = _ln64(r, w.ln1_g[l], w.ln1_b[l])
+        k_rows, v_rows = a @ Pk.T, a @ Pv.T
+        assert np.allclose(K[l, 0, :R].reshape(R, d), k_rows, atol=2e-6)
+        assert np.allclose(Vc[l, 0, :R].reshape(R, d), v_rows, atol=2e-6)
+        att = np.cumsum(v_rows, axis=0) / np.arange(1, R + 1)[:, None]   # causal mean
+        r = r + att @ Po.T
+        a2 = _ln64(r, w.ln2_g[l], w.ln2_b[l])
+        h = np.zeros((R, F))
+        h[:, :d] = a2 @ Pu.T
+        h[:, d:2 * d] = a2 @ Pu
+        r = r + _gelu64(h) @ down.astype(np.float64).T
+    z = _ln64(r[-1], w.lnf_g, w.lnf_b)
+    assert np.allclose(logits[0], w.lm_head.astype(np.float64) @ z, atol=1e-5)
+
+
+def test_model_query_key_scores(oracle_mod):
+    """One layer, Q and K permutations with V = O = identity and FFN zero:
+    the output is x + softmax-weighted causal average of LN(x) rows with scores
+    (P_q a_p) . (P_k a_t) / 8 per head."""
+    d, F, V, H = 128, 128, 17, 2
+    shape = synth.tiny_shape(n_layers=1, d_model=d, n_heads=H, d_ff=F, vocab=V)
+    w = _tiny_weights(shape, seed=8)
+    Pq, Pk = _perm(d, 11), _perm(d, 12)
+    I = np.eye(d, dtype=np.float32)
+    w.w_qkv[0] = np.concatenate([Pq, Pk, I]).astype(np.float32)
+    w.w_o[0] = I
+    w.w_up[0] = np.zeros((F, d), np.float32)
+    w.w_down[0] = np.zeros((d, F), np.float32)
+    R = 5
+    x = np.random.default_rng(3).standard_normal((1, R, d)).astype(np.float32)
+    m = oracle_mod.OracleModel.from_weights(w, batch=1, t_cap=R, quantize=False)
+    logits, _ = m.forward(prefix=x)
+    a = _ln64(x[0], w.ln1_g[0], w.ln1_b[0])
+    q, k = a @ Pq.T, a @ Pk.T
+    out = np.zeros(d)
+    for h in range(H):
+        sl = slice(64 * h, 64 * h + 64)
+        s = k[:, sl] @ q[-1, sl] / 8.0
+        p = np.exp(s - s.max())
+        p /= p.sum()
+        out[sl] = p @ a[:, sl]
+    r = x[0, -1].astype(np.float64) + out
+    z = _ln64(r, w.lnf_g, w.lnf_b)
+    assert np.allclose(logits[0], w.lm_head.astype(np.float64) @ z, atol=1e-5)
+
+
+def test_model_incremental_equals_one_shot(oracle_mod):
+    """prefill(P + S) == prefill(P + S - 1) + decode(1), bit for bit, and the
+    caches agree: causality and slot indexing (the rows are computed the same
+    way whichever call appends them)."""
+    shape = synth.tiny_shape()
+    w = _tiny_weights(shape, seed=31)
+    rng = np.random.default_rng(12)
+    prefix = rng.standard_normal((2, 5, shape.d_model)).astype(np.float32)
+    tokens = rng.integers(0, shape.vocab, size=(2, 4))
+    a = oracle_mod.OracleModel.from_weights(w, batch=2, t_cap=12)
+    la, na = a.forward(tokens=tokens, prefix=prefix)
+    b = oracle_mod.OracleModel.from_weights(w, batch=2, t_cap=12)
+    b.forward(prefix=prefix)
+    b.forward(tokens=tokens[:, :2])
+    b.forward(tokens=tokens[:, 2:3])
+    lb, nb = b.forward(tokens=tokens[:, 3:])
+    assert np.array_equal(la, lb) and np.array_equal(na, nb)
+    Ka, Va = a.kv()
+    Kb, Vb = b.kv()
+    assert np.array_equal(Ka[:, :, :9], Kb[:, :, :9]) and np.array_equal(Va[:, :, :9], Vb[:, :, :9])
+    assert a.position == b.position == 9
+
+
+def test_model_batch_rows_independent(oracle_mod):
+    """Sequence b's result does not depend on the other sequences."""
+    shape = synth.tiny_shape()
+    w = _tiny_weights(shape, seed=32)
+    rng = np.random.default_rng(13)
+    prefix = rng.standard_normal((3, 4, shape.d_model)).astype(np.float32)
+    m3 = oracle_mod.OracleModel.from_weights(w, batch=3, t_cap=6)
+    l3, _ = m3.forward(prefix=prefix)
+    m1 = oracle_mod.OracleModel.from_weights(w, batch=1, t_cap=6)
+    l1, _ = m1.forward(prefix=prefix[1:2])
+    assert np.array_equal(l3[1], l1[0])
+
+
+def test_model_cache_full_and_bad_token(oracle_mod):
+    shape = synth.tiny_shape()
+    w = _tiny_weights(shape, seed=33)
+    m = oracle_mod.OracleModel.from_weights(w, batch=1, t_cap=3)
+    m.forward(tokens=np.array([[1, 2]]))
+    with pytest.raises(OverflowError):
+        m.forward(tokens=np.array([[1, 2]]))
+    assert m.position == 2
+    with pytest.raises(RuntimeError):
+        m.forward(tokens=np.array([[shape.vocab]]))
+    m.forward(tokens=np.array([[0]]))
+    assert m.position == 3
+
+
+def test_model_quantized_equals_dequantized_input(oracle_mod):
+    """Quantising inside the model is the same as handing it the dequantised
+    weights (ties the model's weight path to the pinned quantiser)."""
+    shape = synth.tiny_shape(n_layers=1)
+    w = _tiny_weights(shape, seed=34)
+    x = np.random.default_rng(1).standard_normal((1, 3, shape.d_model)).astype(np.float32)
+    mq = oracle_mod.OracleModel.from_weights(w, batch=1, t_cap=3)
+    lq, _ = mq.forward(prefix=x)
+    for lst in (w.w_qkv, w.w_o, w.w_up, w.w_down):
+        lst[0] = oracle_mod.dequantize_int4(*oracle_mod.quantize_int4(lst[0]))
+    md = oracle_mod.OracleModel.from_weights(w, batch=1, t_cap=3, quantize=False)
+    ld, _ = md.forward(prefix=x)
+    assert np.array_equal(lq, ld)
