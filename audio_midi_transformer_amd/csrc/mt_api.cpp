@@ -1,0 +1,438 @@
+// Host runtime and C ABI of the MuScriptor INT4 decoder step (see include/mt.h).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <thread>
+#include <vector>
+
+#include "../../include/mt.h"
+#include "mt_internal.h"
+
+using namespace mt;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+#define HIP_TRY(expr)                                                                          \
+    do {                                                                                       \
+        hipError_t e_ = (expr);                                                                \
+        if (e_ != hipSuccess)                                                                  \
+            return fail(MT_ERR_HIP, "%s failed: %s (%s:%d)", #expr, hipGetErrorString(e_),     \
+                        __FILE__, __LINE__);                                                   \
+    } while (0)
+
+constexpr int kPart = 68;      // floats per attention partial (m, l, acc[64], pad)
+constexpr int kMaxSplit = 64;  // split-K bound of the decode attention
+
+}  // namespace
+
+struct mt_model {
+    mt_config c{};
+    int device = 0;
+    hipStream_t last_stream = nullptr;
+    // weights
+    float* tok_emb = nullptr;
+    float* lm_head = nullptr;
+    float* ln = nullptr;   // [L, 4, d]
+    float* lnf = nullptr;  // [2, d]
+    uint8_t* wq_all = nullptr;
+    float* ws_all = nullptr;
+    std::vector<Int4Mat> proj;  // [L*4]
+    const uint8_t** wq_ptrs = nullptr;  // device copies of the pointer tables
+    const float** ws_ptrs = nullptr;
+    // cache
+    float* kc = nullptr;
+    float* vc = nullptr;
+    int t_past = 0;
+    int* err = nullptr;
+    // decode scratch
+    float* x = nullptr;
+    float* a = nullptr;
+    float* q = nullptr;
+    float* att = nullptr;
+    float* h = nullptr;
+    float* part = nullptr;
+    float* z = nullptr;
+    // persistent decode
+    int decode_path = MT_DECODE_AUTO;
+    bool persistent_ok = false;
+    void* xbuf = nullptr;
+    uint32_t epoch = 0;
+    // prefill workspace
+    size_t pf_rows = 0;
+    float* pf = nullptr;
+};
+
+namespace {
+
+template <typename T>
+hipError_t dmalloc(T** p, size_t count) {
+    return hipMalloc(reinterpret_cast<void**>(p), std::max<size_t>(count, 1) * sizeof(T));
+}
+
+void free_model(mt_model* m) {
+    if (!m) return;
+    void* ptrs[] = {m->tok_emb, m->lm_head, m->ln, m->lnf, m->wq_all, m->ws_all, m->wq_ptrs,
+                    m->ws_ptrs, m->kc, m->vc, m->err, m->x, m->a, m->q, m->att, m->h, m->part,
+                    m->z, m->xbuf, m->pf};
+    for (void* p : ptrs)
+        if (p) (void)hipFree(p);
+    delete m;
+}
+
+int check_config(const mt_config* c) {
+    if (!c) return fail(MT_ERR_INVALID_ARG, "config is NULL");
+    if (c->head_dim != 64) return fail(MT_ERR_UNSUPPORTED, "head_dim must be 64 (got %d)", c->head_dim);
+    if (c->group != 32) return fail(MT_ERR_UNSUPPORTED, "group must be 32 (got %d)", c->group);
+    if (c->flags != 0) return fail(MT_ERR_UNSUPPORTED, "flags must be 0");
+    if (c->n_layers < 1 || c->n_heads < 1 || c->vocab < 1 || c->batch < 1 || c->batch > 64 ||
+        c->t_cap < 1 || c->d_ff < 32)
+        return fail(MT_ERR_INVALID_ARG, "non-positive or out-of-range size in config");
+    if (c->d_model != c->n_heads * 64)
+        return fail(MT_ERR_INVALID_ARG, "d_model (%d) must equal n_heads * 64", c->d_model);
+    if (c->d_model % 32 || c->d_ff % 32)
+        return fail(MT_ERR_UNSUPPORTED, "d_model and d_ff must be multiples of 32");
+    if (c->d_model > 2048) return fail(MT_ERR_UNSUPPORTED, "d_model above 2048 is not supported");
+    if (!(c->ln_eps > 0.f) || !std::isfinite(c->ln_eps))
+        return fail(MT_ERR_INVALID_ARG, "ln_eps must be positive");
+    return MT_OK;
+}
+
+// Split-K layout of the decode attention over T keys.
+void attn_split(int B, int H, int T, int* nsplit, int* chunk) {
+    int want = std::max(1, (512 + B * H - 1) / (B * H));
+    int ch = (T + want - 1) / want;
+    ch = std::max(16, (ch + 15) / 16 * 16);
+    int ns = (T + ch - 1) / ch;
+    if (ns > kMaxSplit) {
+        ns = kMaxSplit;
+        ch = ((T + ns - 1) / ns + 15) / 16 * 16;
+        ns = (T + ch - 1) / ch;
+    }
+    *nsplit = ns;
+    *chunk = ch;
+}
+
+int ensure_prefill_ws(mt_model* m, size_t rows) {
+    if (rows <= m->pf_rows) return MT_OK;
+    if (m->pf) HIP_TRY(hipFree(m->pf));
+    m->pf = nullptr;
+    m->pf_rows = 0;
+    const size_t d = m->c.d_model, F = m->c.d_ff;
+    if (dmalloc(&m->pf, rows * (4 * d + F)) != hipSuccess)
+        return fail(MT_ERR_OOM, "prefill workspace of %zu rows", rows);
+    m->pf_rows = rows;
+    return MT_OK;
+}
+
+// Run every layer over M = B * R rows held in x (row m = b * R + i, position
+// t0 + i).  `decode` selects the split-K decode attention (R == 1).
+int run_layers(mt_model* m, float* x, float* a, float* q, float* att, float* h, int R, int t0,
+               bool decode, hipStream_t st) {
+    const mt_config& c = m->c;
+    const int d = c.d_model, F = c.d_ff, B = c.batch, M = B * R;
+    for (int l = 0; l < c.n_layers; ++l) {
+        const float* ln = m->ln + (size_t)l * 4 * d;
+        HIP_TRY(launch_layernorm(x, d, ln, ln + d, c.ln_eps, d, M, a, d, st));
+        QkvDest dst{q, m->kc, m->vc, d, l, B, c.t_cap, t0, R};
+        HIP_TRY(launch_w4_matmul(a, d, M, m->proj[l * 4 + 0], nullptr, 0, EPI_QKV, &dst, false, st));
+        if (decode) {
+            int ns, ch;
+            attn_split(B, c.n_heads, t0 + 1, &ns, &ch);
+            HIP_TRY(launch_attn_decode(q, m->kc, m->vc, l, B, c.n_heads, c.t_cap, t0 + 1, m->part, ns,
+                                       ch, att, st));
+        } else {
+            HIP_TRY(launch_attn_prefill(q, m->kc, m->vc, l, B, c.n_heads, c.t_cap, t0, R, att, st));
+        }
+        HIP_TRY(launch_w4_matmul(att, d, M, m->proj[l * 4 + 1], x, d, EPI_RESID, nullptr, false, st));
+        HIP_TRY(launch_layernorm(x, d, ln + 2 * d, ln + 3 * d, c.ln_eps, d, M, a, d, st));
+        HIP_TRY(launch_w4_matmul(a, d, M, m->proj[l * 4 + 2], h, F, EPI_GELU, nullptr, false, st));
+        HIP_TRY(launch_w4_matmul(h, F, M, m->proj[l * 4 + 3], x, d, EPI_RESID, nullptr, false, st));
+    }
+    return MT_OK;
+}
+
+int run_head(mt_model* m, const float* x, int R, float* logits, int64_t* next, hipStream_t st) {
+    const mt_config& c = m->c;
+    const int d = c.d_model;
+    // final LayerNorm of the last row of every sequence
+    HIP_TRY(launch_layernorm(x + (size_t)(R - 1) * d, (long)R * d, m->lnf, m->lnf + d, c.ln_eps, d,
+                             c.batch, m->z, d, st));
+    HIP_TRY(launch_lm_head(m->z, c.batch, m->lm_head, c.vocab, d, logits, st));
+    HIP_TRY(launch_argmax(logits, c.batch, c.vocab, next, st));
+    return MT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mt_last_error(void) { return g_last_error.c_str(); }
+
+int mt_pack_int4(const float* W, int32_t N, int32_t K, uint8_t* q, float* s) {
+    if (!W || !q || !s) return fail(MT_ERR_INVALID_ARG, "mt_pack_int4: NULL pointer");
+    if (N < 0 || K <= 0 || K % 32) return fail(MT_ERR_INVALID_ARG, "mt_pack_int4: K must be a positive multiple of 32");
+    const int64_t G = K / 32;
+    auto work = [&](int64_t n0, int64_t n1) {
+        for (int64_t n = n0; n < n1; ++n)
+            for (int64_t g = 0; g < G; ++g) {
+                const float* w = W + n * (int64_t)K + g * 32;
+                float mx = 0.0f;
+                for (int k = 0; k < 32; ++k) mx = std::max(mx, std::fabs(w[k]));
+                const float sc = mx / 7.0f;
+                s[n * G + g] = sc;
+                uint8_t* dst = q + n * (int64_t)(K / 2) + g * 16;
+                for (int j = 0; j < 16; ++j) {
+                    int code[2] = {0, 0};
+                    if (sc != 0.0f)
+                        for (int e = 0; e < 2; ++e) {
+                            float r = std::rint(w[2 * j + e] / sc);
+                            r = std::min(7.0f, std::max(-8.0f, r));
+                            code[e] = (int)r;
+                        }
+                    dst[j] = (uint8_t)((code[0] + 8) | ((code[1] + 8) << 4));
+                }
+            }
+    };
+    const int64_t nthreads = std::max<int64_t>(1, std::min<int64_t>(std::thread::hardware_concurrency(), N / 256));
+    if (nthreads <= 1) {
+        work(0, N);
+    } else {
+        std::vector<std::thread> th;
+        const int64_t per = (N + nthreads - 1) / nthreads;
+        for (int64_t t = 0; t < nthreads; ++t)
+            th.emplace_back(work, std::min<int64_t>(N, t * per), std::min<int64_t>(N, (t + 1) * per));
+        for (auto& t : th) t.join();
+    }
+    return MT_OK;
+}
+
+int mt_create(const mt_config* cfg, const mt_weights* w, int weights_on_device, void* stream,
+              mt_model** out) {
+    if (!out) return fail(MT_ERR_INVALID_ARG, "mt_create: out is NULL");
+    *out = nullptr;
+    int rc = check_config(cfg);
+    if (rc) return rc;
+    if (!w || !w->tok_emb || !w->lm_head || !w->ln_final || !w->ln || !w->proj)
+        return fail(MT_ERR_INVALID_ARG, "mt_create: NULL weight pointer");
+    const mt_config c = *cfg;
+    const int L = c.n_layers, d = c.d_model, F = c.d_ff, V = c.vocab, B = c.batch, H = c.n_heads;
+    for (int i = 0; i < L * 4; ++i)
+        if (!w->proj[i].q || !w->proj[i].s) return fail(MT_ERR_INVALID_ARG, "mt_create: NULL projection %d", i);
+    hipStream_t st = (hipStream_t)stream;
+    const hipMemcpyKind kind = weights_on_device ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice;
+
+    mt_model* m = new mt_model();
+    m->c = c;
+    auto bail = [&](int code) {
+        free_model(m);
+        return code;
+    };
+    if (hipGetDevice(&m->device) != hipSuccess) return bail(fail(MT_ERR_HIP, "hipGetDevice failed"));
+
+    // projection shapes [N, K]
+    size_t qbytes = 0, sfloats = 0;
+    m->proj.resize((size_t)L * 4);
+    for (int l = 0; l < L; ++l) {
+        const int NK[4][2] = {{3 * d, d}, {d, d}, {F, d}, {d, F}};
+        for (int p = 0; p < 4; ++p) {
+            Int4Mat& pm = m->proj[l * 4 + p];
+            pm.N = NK[p][0];
+            pm.K = NK[p][1];
+            qbytes += (size_t)pm.N * pm.K / 2;
+            sfloats += (size_t)pm.N * pm.K / 32;
+        }
+    }
+    const size_t kv = (size_t)L * B * c.t_cap * d;
+    if (dmalloc(&m->tok_emb, (size_t)V * d) || dmalloc(&m->lm_head, (size_t)V * d) ||
+        dmalloc(&m->ln, (size_t)L * 4 * d) || dmalloc(&m->lnf, 2 * (size_t)d) ||
+        dmalloc(&m->wq_all, qbytes) || dmalloc(&m->ws_all, sfloats) || dmalloc(&m->kc, kv) ||
+        dmalloc(&m->vc, kv) || dmalloc(&m->err, 16) || dmalloc(&m->x, (size_t)B * d) ||
+        dmalloc(&m->a, (size_t)B * std::max(d, F)) || dmalloc(&m->q, (size_t)B * d) ||
+        dmalloc(&m->att, (size_t)B * d) || dmalloc(&m->h, (size_t)B * F) || dmalloc(&m->part, (size_t)B * H * kMaxSplit * kPart) ||
+        dmalloc(&m->z, (size_t)B * d) || dmalloc(&m->wq_ptrs, (size_t)L * 4) ||
+        dmalloc(&m->ws_ptrs, (size_t)L * 4))
+        return bail(fail(MT_ERR_OOM, "mt_create: device allocation failed (KV cache %zu bytes)", 2 * kv * 4));
+
+    auto cpy = [&](void* dst, const void* src, size_t bytes) {
+        return hipMemcpyAsync(dst, src, bytes, kind, st);
+    };
+    if (cpy(m->tok_emb, w->tok_emb, (size_t)V * d * 4) || cpy(m->lm_head, w->lm_head, (size_t)V * d * 4) ||
+        cpy(m->ln, w->ln, (size_t)L * 4 * d * 4) || cpy(m->lnf, w->ln_final, (size_t)2 * d * 4))
+        return bail(fail(MT_ERR_HIP, "mt_create: weight copy failed"));
+    size_t qo = 0, so = 0;
+    std::vector<const uint8_t*> hq(L * 4);
+    std::vector<const float*> hs(L * 4);
+    for (int i = 0; i < L * 4; ++i) {
+        Int4Mat& pm = m->proj[i];
+        const size_t nb = (size_t)pm.N * pm.K / 2, ns = (size_t)pm.N * pm.K / 32;
+        if (cpy(m->wq_all + qo, w->proj[i].q, nb) || cpy(m->ws_all + so, w->proj[i].s, ns * 4))
+            return bail(fail(MT_ERR_HIP, "mt_create: projection copy failed"));
+        pm.q = m->wq_all + qo;
+        pm.s = m->ws_all + so;
+        hq[i] = pm.q;
+        hs[i] = pm.s;
+        qo += nb;
+        so += ns;
+    }
+    if (hipMemcpyAsync(m->wq_ptrs, hq.data(), hq.size() * sizeof(void*), hipMemcpyHostToDevice, st) ||
+        hipMemcpyAsync(m->ws_ptrs, hs.data(), hs.size() * sizeof(void*), hipMemcpyHostToDevice, st) ||
+        hipMemsetAsync(m->err, 0, 16, st))
+        return bail(fail(MT_ERR_HIP, "mt_create: table copy failed"));
+    m->persistent_ok = persistent_supported(d, F, H, B, V);
+    if (m->persistent_ok) {
+        const size_t xb = persistent_xbuf_bytes(L, d, F, H, B, V);
+        if (hipMalloc(&m->xbuf, xb) != hipSuccess || hipMemsetAsync(m->xbuf, 0, xb, st) != hipSuccess)
+            return bail(fail(MT_ERR_OOM, "mt_create: exchange buffer of %zu bytes", xb));
+    }
+    if (hipStreamSynchronize(st) != hipSuccess) return bail(fail(MT_ERR_HIP, "mt_create: synchronise failed"));
+    m->last_stream = st;
+    *out = m;
+    return MT_OK;
+}
+
+int mt_prefill(mt_model* m, const int64_t* tokens, int32_t S, const float* prefix, int32_t P,
+               float* logits, int64_t* next, void* stream) {
+    if (!m || !logits || !next) return fail(MT_ERR_INVALID_ARG, "mt_prefill: NULL model or output");
+    if (S < 0 || P < 0 || (int64_t)S + P < 1) return fail(MT_ERR_INVALID_ARG, "mt_prefill: need P + S >= 1 (P=%d S=%d)", P, S);
+    if ((S > 0 && !tokens) || (P > 0 && !prefix)) return fail(MT_ERR_INVALID_ARG, "mt_prefill: NULL tokens or prefix");
+    const mt_config& c = m->c;
+    const int R = P + S;
+    if ((int64_t)m->t_past + R > c.t_cap)
+        return fail(MT_ERR_CACHE_FULL, "mt_prefill: %d rows at position %d exceed capacity %d", R, m->t_past, c.t_cap);
+    hipStream_t st = (hipStream_t)stream;
+    const size_t M = (size_t)c.batch * R;
+    int rc = ensure_prefill_ws(m, M);
+    if (rc) return rc;
+    const int d = c.d_model;
+    float* x = m->pf;
+    float* a = x + M * d;
+    float* q = a + M * d;
+    float* att = q + M * d;
+    float* h = att + M * d;
+    HIP_TRY(launch_embed(tokens, S, prefix, P, m->tok_emb, c.vocab, d, c.batch, x, m->err, st));
+    rc = run_layers(m, x, a, q, att, h, R, m->t_past, false, st);
+    if (rc) return rc;
+    rc = run_head(m, x, R, logits, next, st);
+    if (rc) return rc;
+    m->t_past += R;
+    m->last_stream = st;
+    return MT_OK;
+}
+
+int mt_decode_step(mt_model* m, const int64_t* token, float* logits, int64_t* next, void* stream) {
+    if (!m || !token || !logits || !next) return fail(MT_ERR_INVALID_ARG, "mt_decode_step: NULL argument");
+    const mt_config& c = m->c;
+    if (m->t_past + 1 > c.t_cap)
+        return fail(MT_ERR_CACHE_FULL, "mt_decode_step: cache full at position %d (capacity %d)", m->t_past, c.t_cap);
+    hipStream_t st = (hipStream_t)stream;
+    const bool persistent = m->persistent_ok && m->decode_path != MT_DECODE_KERNELS;
+    if (persistent) {
+        PersistentArgs pa{};
+        pa.L = c.n_layers; pa.d = c.d_model; pa.H = c.n_heads; pa.F = c.d_ff; pa.V = c.vocab;
+        pa.B = c.batch; pa.t_cap = c.t_cap; pa.eps = c.ln_eps;
+        pa.tok_emb = m->tok_emb; pa.lm_head = m->lm_head; pa.ln = m->ln; pa.ln_final = m->lnf;
+        pa.wq = m->wq_ptrs; pa.ws = m->ws_ptrs; pa.kc = m->kc; pa.vc = m->vc;
+        pa.token = token; pa.logits = logits; pa.next = next; pa.t0 = m->t_past;
+        pa.epoch = ++m->epoch;
+        pa.resid = m->x; pa.xbuf = m->xbuf; pa.err = m->err;
+        HIP_TRY(launch_persistent_decode(pa, st));
+    } else {
+        const int d = c.d_model;
+        HIP_TRY(launch_embed(token, 1, nullptr, 0, m->tok_emb, c.vocab, d, c.batch, m->x, m->err, st));
+        int rc = run_layers(m, m->x, m->a, m->q, m->att, m->h, 1, m->t_past, true, st);
+        if (rc) return rc;
+        rc = run_head(m, m->x, 1, logits, next, st);
+        if (rc) return rc;
+    }
+    m->t_past += 1;
+    m->last_stream = st;
+    return MT_OK;
+}
+
+int mt_reset(mt_model* m) {
+    if (!m) return fail(MT_ERR_INVALID_ARG, "mt_reset: NULL model");
+    m->t_past = 0;
+    return MT_OK;
+}
+
+int mt_position(const mt_model* m, int32_t* t_past) {
+    if (!m || !t_past) return fail(MT_ERR_INVALID_ARG, "mt_position: NULL argument");
+    *t_past = m->t_past;
+    return MT_OK;
+}
+
+int mt_kv_cache(mt_model* m, const float** k, const float** v) {
+    if (!m || !k || !v) return fail(MT_ERR_INVALID_ARG, "mt_kv_cache: NULL argument");
+    *k = m->kc;
+    *v = m->vc;
+    return MT_OK;
+}
+
+int mt_check(mt_model* m) {
+    if (!m) return fail(MT_ERR_INVALID_ARG, "mt_check: NULL model");
+    HIP_TRY(hipStreamSynchronize(m->last_stream));
+    int h = 0;
+    HIP_TRY(hipMemcpy(&h, m->err, sizeof(int), hipMemcpyDeviceToHost));
+    if (h) {
+        HIP_TRY(hipMemset(m->err, 0, sizeof(int)));
+        if (h & 2) return fail(MT_ERR_HIP, "persistent decode step gave up waiting on an exchange");
+        return fail(MT_ERR_INVALID_ARG, "a token id outside [0, vocab) reached the device");
+    }
+    return MT_OK;
+}
+
+int mt_set_decode_path(mt_model* m, int32_t path) {
+    if (!m) return fail(MT_ERR_INVALID_ARG, "mt_set_decode_path: NULL model");
+    if (path != MT_DECODE_AUTO && path != MT_DECODE_KERNELS && path != MT_DECODE_PERSISTENT)
+        return fail(MT_ERR_INVALID_ARG, "mt_set_decode_path: unknown path %d", path);
+    if (path == MT_DECODE_PERSISTENT && !m->persistent_ok)
+        return fail(MT_ERR_UNSUPPORTED, "persistent decode does not support this configuration");
+    m->decode_path = path;
+    return MT_OK;
+}
+
+void mt_destroy(mt_model* m) {
+    if (!m) return;
+    (void)hipDeviceSynchronize();
+    free_model(m);
+}
+
+int mt_debug_dequant(mt_model* m, int32_t layer, int32_t proj, float* out, void* stream) {
+    if (!m || !out) return fail(MT_ERR_INVALID_ARG, "mt_debug_dequant: NULL argument");
+    if (layer < 0 || layer >= m->c.n_layers || proj < 0 || proj > 3)
+        return fail(MT_ERR_INVALID_ARG, "mt_debug_dequant: bad layer/projection");
+    HIP_TRY(launch_dequant(m->proj[layer * 4 + proj], out, (hipStream_t)stream));
+    return MT_OK;
+}
+
+int mt_debug_matmul(mt_model* m, int32_t layer, int32_t proj, const float* x, int32_t M, float* y,
+                    void* stream) {
+    if (!m || !x || !y || M < 1) return fail(MT_ERR_INVALID_ARG, "mt_debug_matmul: bad argument");
+    const int p = proj & 0xFF;
+    const bool force_gemm = (proj & 0x100) != 0;
+    if (layer < 0 || layer >= m->c.n_layers || p > 3)
+        return fail(MT_ERR_INVALID_ARG, "mt_debug_matmul: bad layer/projection");
+    const Int4Mat& w = m->proj[layer * 4 + p];
+    HIP_TRY(launch_w4_matmul(x, w.K, M, w, y, w.N, EPI_STORE, nullptr, force_gemm || M > 8,
+                             (hipStream_t)stream));
+    return MT_OK;
+}
+
+}  // extern "C"

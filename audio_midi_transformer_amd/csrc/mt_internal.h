@@ -1,0 +1,83 @@
+// Internal declarations shared by the host runtime and the kernel launchers.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mt {
+
+// Epilogues of the INT4 matmul kernels.
+enum Epilogue : int {
+    EPI_STORE = 0,  // y[m, n] = acc
+    EPI_GELU = 1,   // y[m, n] = GELU(acc), exact erf form
+    EPI_RESID = 2,  // y[m, n] += acc (residual stream updated in place)
+    EPI_QKV = 3,    // n <  d: q[m, n]; d <= n < 2d: K cache; 2d <= n: V cache
+};
+
+// Where the QKV epilogue scatters K and V: rows m = b * rows_per_seq + i land
+// at cache position t0 + i of sequence b in layer `layer`.
+struct QkvDest {
+    float* q;        // [M, d]
+    float* kc;       // [L, B, t_cap, H, 64]
+    float* vc;
+    int d;
+    int layer;
+    int batch;
+    int t_cap;
+    int t0;
+    int rows_per_seq;
+};
+
+struct Int4Mat {
+    const uint8_t* q;  // [N, K/2]
+    const float* s;    // [N, K/32]
+    int N;
+    int K;
+};
+
+// ---- launchers (mt_kernels.hip); all return hipGetLastError() ----
+hipError_t launch_embed(const int64_t* tokens, int S, const float* prefix, int P, const float* emb,
+                        int V, int d, int B, float* x, int* err, hipStream_t st);
+hipError_t launch_layernorm(const float* x, long ldx, const float* g, const float* b, float eps,
+                            int d, int rows, float* y, long ldy, hipStream_t st);
+hipError_t launch_w4_matmul(const float* x, int ldx, int M, const Int4Mat& w, float* y, int ldy,
+                            Epilogue epi, const QkvDest* qkv, bool force_gemm, hipStream_t st);
+hipError_t launch_attn_decode(const float* q, const float* kc, const float* vc, int layer, int B,
+                              int H, int t_cap, int T, float* part, int nsplit, int chunk,
+                              float* out, hipStream_t st);
+hipError_t launch_attn_prefill(const float* q, const float* kc, const float* vc, int layer, int B,
+                               int H, int t_cap, int t0, int R, float* out, hipStream_t st);
+hipError_t launch_lm_head(const float* z, int B, const float* w, int V, int d, float* logits,
+                          hipStream_t st);
+hipError_t launch_argmax(const float* logits, int B, int V, int64_t* next, hipStream_t st);
+hipError_t launch_dequant(const Int4Mat& w, float* out, hipStream_t st);
+
+// Persistent single-launch decode step (mt_decode_persistent.hip).
+struct PersistentPlan;
+struct PersistentArgs {
+    // model
+    int L, d, H, F, V, B, t_cap;
+    float eps;
+    const float* tok_emb;
+    const float* lm_head;
+    const float* ln;        // [L, 4, d]
+    const float* ln_final;  // [2, d]
+    const uint8_t* const* wq;  // device array [L*4] of pointers
+    const float* const* ws;    // device array [L*4]
+    float* kc;
+    float* vc;
+    // step
+    const int64_t* token;  // [B]
+    float* logits;         // [B, V]
+    int64_t* next;         // [B]
+    int t0;                // position of the appended row
+    uint32_t epoch;        // unique per step (tags exchanged data)
+    // workspace
+    float* resid;          // [B, d] residual stream
+    void* xbuf;            // exchange buffers
+    int* err;
+};
+bool persistent_supported(int d, int F, int H, int B, int V);
+size_t persistent_xbuf_bytes(int L, int d, int F, int H, int B, int V);
+hipError_t launch_persistent_decode(const PersistentArgs& a, hipStream_t st);
+
+}  // namespace mt

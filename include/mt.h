@@ -1,0 +1,178 @@
+/*
+ * mt.h -- C ABI of the MuScriptor INT4 decoder step on MI355X (gfx950).
+ *
+ * The library runs the transcription decoder of MuScriptor: a decoder-only,
+ * pre-norm transformer ("MuScriptor -- small" model card, "Model
+ * description" and "Model variants") whose four per-layer projections are
+ * stored as symmetric round-to-nearest INT4 with groups of 32 while
+ * activations, the KV cache, the embeddings and the LM head stay FP32
+ * ("MuScriptor Medium -- optimized W4A32 ONNX Runtime" README, "Model
+ * variant").  One call appends rows to a fixed-capacity cache and returns
+ * the logits of the last row; positions are implied by how many rows the
+ * cache already holds ("unifolia/muscriptor-small-onnx", decoder section).
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are DEVICE pointers unless stated otherwise.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     All work is stream-ordered and asynchronous; outputs are valid once
+ *     the stream has been synchronised.  Entry points on the decode path do
+ *     not synchronise and do not allocate.
+ *   - Return value: 0 on success, a negative MT_ERR_* code on failure.  On
+ *     failure nothing has been launched and the cache and position are
+ *     unchanged; mt_last_error() returns a message for the calling thread.
+ *   - The model object is not thread-safe: calls on one model must be
+ *     serialised by the caller.
+ */
+#ifndef MT_H
+#define MT_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MT_OK 0
+#define MT_ERR_INVALID_ARG (-1) /* null pointer, bad size, bad config, bad token id */
+#define MT_ERR_CACHE_FULL (-2)  /* T_past + rows > t_cap */
+#define MT_ERR_HIP (-3)         /* a HIP runtime call failed */
+#define MT_ERR_OOM (-4)         /* device or host allocation failed */
+#define MT_ERR_UNSUPPORTED (-5) /* head_dim != 64, widths not multiples of 32, ... */
+
+typedef struct mt_model mt_model;
+
+/* Model and run configuration.  Sizes of the pages' three models:
+ * small 14 x 768 x 12 heads, medium 24 x 1024 x 16, large 48 x 1536 x 24
+ * (Core AI conversion table; model card "Model variants"); vocabulary 1393
+ * (small ONNX conversion page); head width 64 (cache layout on the same
+ * page). */
+typedef struct {
+    int32_t n_layers;  /* L */
+    int32_t d_model;   /* d = n_heads * 64 */
+    int32_t n_heads;   /* H */
+    int32_t head_dim;  /* must be 64 */
+    int32_t d_ff;      /* F, FFN width; multiple of 32 */
+    int32_t vocab;     /* V (1393 for MT3 tokens) */
+    int32_t group;     /* must be 32 */
+    int32_t batch;     /* B sequences that advance in lockstep, 1..64 */
+    int32_t t_cap;     /* fixed cache capacity per sequence (positions) */
+    float ln_eps;      /* LayerNorm epsilon (1e-5) */
+    uint32_t flags;    /* must be 0 */
+} mt_config;
+
+/* One INT4 projection in the canonical packed form.
+ * For a matrix W [N, K] (row n = output feature n, K = input width):
+ *   s[n, g]  (FP32, [N, K/32]) = max |W[n, 32g .. 32g+31]| / 7;
+ *   code     = clamp(round-half-even(W / s), -8, 7), 0 for an all-zero group;
+ *   q[n, j]  (uint8, [N, K/2]) = (code[2j] + 8) | (code[2j+1] + 8) << 4,
+ *            i.e. the low nibble holds the even input index;
+ *   dequantised weight = (float)(nibble - 8) * s  (one FP32 multiply).
+ * Format: medium ONNX README, "Model variant" (symmetric RTN INT4, group
+ * 32).  Nibble order, tie rule and FP32 scales are this library's reading. */
+typedef struct {
+    const uint8_t* q;
+    const float* s;
+} mt_int4;
+
+/* Model weights.  Caller-owned and only read during mt_create; host or
+ * device memory per the `weights_on_device` argument of mt_create.
+ *   tok_emb  [V, d]           FP32 token embedding (not quantised)
+ *   lm_head  [V, d]           FP32, row v produces logit v (untied, no bias)
+ *   ln_final [2, d]           final LayerNorm gain, bias
+ *   ln       [L, 4, d]        per layer: gain1, bias1, gain2, bias2
+ *   proj     [L * 4]          per layer, in this order:
+ *                               QKV  [3d, d]  rows Q | K | V, head h = rows 64h..64h+63 of each
+ *                               O    [d, d]
+ *                               up   [F, d]
+ *                               down [d, F]
+ * No projection has a bias. */
+typedef struct {
+    const float* tok_emb;
+    const float* lm_head;
+    const float* ln_final;
+    const float* ln;
+    const mt_int4* proj;
+} mt_weights;
+
+/* Host-side canonical packer (host pointers).  W [N, K] FP32 -> q [N, K/2],
+ * s [N, K/32] as described for mt_int4.  K must be a multiple of 32.
+ * Uses IEEE binary32 division and round-half-even. */
+int mt_pack_int4(const float* W, int32_t N, int32_t K, uint8_t* q, float* s);
+
+/* Create a model: validates the config, copies the weights to the current
+ * HIP device and allocates the KV cache [L, B, t_cap, H, 64] twice (K, V,
+ * FP32, 2*L*B*t_cap*d*4 bytes) plus decode scratch.  weights_on_device: 0 =
+ * host pointers, 1 = device pointers.  The caller may free its weight
+ * buffers once mt_create returns.  T_past starts at 0. */
+int mt_create(const mt_config* cfg, const mt_weights* w, int weights_on_device, void* stream,
+              mt_model** out);
+
+/* Append rows at positions T_past .. T_past+P+S-1 of every sequence:
+ * first P prefix rows (the conditioner's output [B, P, d]), then the
+ * embeddings of S token ids [B, S] (int64).  Either part may be empty
+ * (NULL with size 0) but P + S >= 1.  Each appended row attends causally
+ * to every cached position up to and including its own.  Writes the
+ * logits of the last appended row [B, V] and its greedy argmax [B]
+ * (int64, lowest index on ties).  T_past advances by P + S.
+ * Small ONNX conversion page, decoder section: prefix rows, token rows,
+ * past cache, last-position logits.  Allocates a row workspace the first
+ * time a larger P + S is seen (not on the decode path).
+ * Errors: MT_ERR_CACHE_FULL if T_past + P + S > t_cap.  A token id outside
+ * [0, V) is not checked on the host (it lives on the device): the row's
+ * embedding becomes NaN and mt_check reports MT_ERR_INVALID_ARG. */
+int mt_prefill(mt_model* m, const int64_t* tokens, int32_t S, const float* prefix, int32_t P,
+               float* logits, int64_t* next, void* stream);
+
+/* One greedy decode step: token [B] (int64) is appended at T_past;
+ * logits [B, V] and next [B] as for mt_prefill.  `next` may be passed back
+ * as `token` of the following call, so greedy decoding never returns to the
+ * host.  Same semantics as mt_prefill with P = 0, S = 1, on the dedicated
+ * decode kernels.  No allocation, no synchronisation. */
+int mt_decode_step(mt_model* m, const int64_t* token, float* logits, int64_t* next, void* stream);
+
+/* Set T_past to 0.  Cache contents are left as they are (they are
+ * overwritten before they are read again). */
+int mt_reset(mt_model* m);
+
+/* Current T_past (host pointer out). */
+int mt_position(const mt_model* m, int32_t* t_past);
+
+/* Device pointers to the cache, [L, B, t_cap, H, 64] FP32 each.  The cache
+ * is updated in place: past and present are the same buffer. */
+int mt_kv_cache(mt_model* m, const float** k, const float** v);
+
+/* Synchronise the model's last stream and report sticky device errors
+ * (MT_ERR_INVALID_ARG after an out-of-range token id).  Clears the flag. */
+int mt_check(mt_model* m);
+
+/* Decode implementation selector (for measurement and parity of both):
+ *   MT_DECODE_AUTO       persistent single-launch step when supported
+ *   MT_DECODE_KERNELS    one kernel per operation
+ *   MT_DECODE_PERSISTENT one persistent launch per step (B <= 4 only) */
+#define MT_DECODE_AUTO 0
+#define MT_DECODE_KERNELS 1
+#define MT_DECODE_PERSISTENT 2
+int mt_set_decode_path(mt_model* m, int32_t path);
+
+/* Destroy: synchronises the device, frees every buffer.  NULL is a no-op. */
+void mt_destroy(mt_model* m);
+
+/* Message for the last failing call on this thread ("" if none). */
+const char* mt_last_error(void);
+
+/* ---- Test-only entry points (stable names, unstable semantics). ---- */
+
+/* Dequantise projection `proj` (0 QKV, 1 O, 2 up, 3 down) of layer `layer`
+ * from the device copy: out [N, K] FP32 = (nibble - 8) * s, bit-exact. */
+int mt_debug_dequant(mt_model* m, int32_t layer, int32_t proj, float* out, void* stream);
+
+/* y [M, N] = x [M, K] . dequant(W)^T for one projection, on the decode
+ * GEMV kernel (M <= 8) or the prefill GEMM kernel (M > 8). */
+int mt_debug_matmul(mt_model* m, int32_t layer, int32_t proj, const float* x, int32_t M, float* y,
+                    void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MT_H */

@@ -1,0 +1,97 @@
+"""CPU-side checks of the C-ABI library: it loads, exports every entry point
+include/mt.h declares, its host packer matches the oracle's quantiser bit for
+bit, and host-side argument checks reject bad calls before any device work."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from audio_midi_transformer_amd import binding, synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "mt.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mt_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_expected_set():
+    assert set(_declared_functions()) == set(binding.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = binding.lib()
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+@pytest.mark.parametrize("shape", [(64, 1024), (48, 4096), (96, 768), (3, 1536), (5, 32)])
+def test_packer_bit_exact_vs_oracle(oracle_mod, shape):
+    N, K = shape
+    W = synth.random_matrix(N * 7 + K, N, K)
+    W[0, :32] = 0.0                      # all-zero group
+    W[1, :32] = np.linspace(-3.5, 3.5, 32) / 7 * 3  # exact .5 ties at s = 3/7 ... plus others
+    q1, s1 = binding.mt_pack_int4(W)
+    q2, s2 = oracle_mod.quantize_int4(W)
+    assert np.array_equal(s1.view(np.uint32), s2.view(np.uint32))
+    assert np.array_equal(q1, q2)
+
+
+def test_packer_on_workload_shapes(oracle_mod):
+    """Every projection shape of the three model sizes, one seeded matrix each."""
+    for shape in (synth.SMALL, synth.MEDIUM, synth.LARGE):
+        d, f = shape.d_model, shape.d_ff
+        for i, (n, k) in enumerate([(3 * d, d), (d, d), (f, d), (d, f)]):
+            W = synth.random_matrix(1000 + i, n, k)
+            q1, s1 = binding.mt_pack_int4(W)
+            q2, s2 = oracle_mod.quantize_int4(W)
+            assert np.array_equal(q1, q2) and np.array_equal(s1.view(np.uint32), s2.view(np.uint32))
+
+
+def test_packer_rejects_bad_width():
+    with pytest.raises(binding.MTError) as e:
+        binding.mt_pack_int4(np.zeros((2, 40), np.float32))
+    assert e.value.code == binding.MT_ERR_INVALID_ARG
+
+
+def _cfg(**kw):
+    c = dict(n_layers=2, d_model=128, n_heads=2, head_dim=64, d_ff=512, vocab=97, group=32,
+             batch=1, t_cap=16, ln_eps=1e-5, flags=0)
+    c.update(kw)
+    return binding.mt_config(**c)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=128), binding.MT_ERR_UNSUPPORTED),
+    (dict(group=64), binding.MT_ERR_UNSUPPORTED),
+    (dict(d_model=130), binding.MT_ERR_INVALID_ARG),
+    (dict(d_ff=500), binding.MT_ERR_UNSUPPORTED),
+    (dict(batch=0), binding.MT_ERR_INVALID_ARG),
+    (dict(t_cap=0), binding.MT_ERR_INVALID_ARG),
+    (dict(ln_eps=0.0), binding.MT_ERR_INVALID_ARG),
+    (dict(flags=1), binding.MT_ERR_UNSUPPORTED),
+])
+def test_create_rejects_bad_config_before_device_work(kw, code):
+    lib = binding.lib()
+    cfg = _cfg(**kw)
+    w = binding.mt_weights()
+    out = ctypes.c_void_p()
+    rc = lib.mt_create(ctypes.byref(cfg), ctypes.byref(w), 0, None, ctypes.byref(out))
+    assert rc == code
+    assert out.value is None
+    assert lib.mt_last_error()
+
+
+def test_calls_reject_null_model():
+    lib = binding.lib()
+    assert lib.mt_prefill(None, None, 0, None, 1, None, None, None) == binding.MT_ERR_INVALID_ARG
+    assert lib.mt_decode_step(None, None, None, None, None) == binding.MT_ERR_INVALID_ARG
+    assert lib.mt_reset(None) == binding.MT_ERR_INVALID_ARG
+    t = ctypes.c_int32()
+    assert lib.mt_position(None, ctypes.byref(t)) == binding.MT_ERR_INVALID_ARG
+    assert lib.mt_set_decode_path(None, 0) == binding.MT_ERR_INVALID_ARG
+    lib.mt_destroy(None)  # no-op
