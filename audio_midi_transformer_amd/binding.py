@@ -30,7 +30,7 @@ MT_DECODE_PERSISTENT = 2
 # Names declared in include/mt.h; the CPU test checks the library exports all.
 EXPORTED = ("mt_pack_int4", "mt_create", "mt_prefill", "mt_decode_step", "mt_reset",
             "mt_position", "mt_kv_cache", "mt_check", "mt_set_decode_path", "mt_destroy",
-            "mt_last_error", "mt_debug_dequant", "mt_debug_matmul")
+            "mt_last_error", "mt_debug_dequant", "mt_debug_matmul", "mt_debug_trace")
 
 
 class mt_config(ctypes.Structure):
@@ -85,9 +85,10 @@ def lib() -> ctypes.CDLL:
     L.mt_last_error.restype = ctypes.c_char_p
     L.mt_debug_dequant.argtypes = [vp, i32, i32, vp, vp]
     L.mt_debug_matmul.argtypes = [vp, i32, i32, vp, i32, vp, vp]
+    L.mt_debug_trace.argtypes = [vp, vp, i64]
     for name in ("mt_pack_int4", "mt_create", "mt_prefill", "mt_decode_step", "mt_reset",
                  "mt_position", "mt_kv_cache", "mt_check", "mt_set_decode_path",
-                 "mt_debug_dequant", "mt_debug_matmul"):
+                 "mt_debug_dequant", "mt_debug_matmul", "mt_debug_trace"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -257,6 +258,13 @@ class Decoder:
         check(lib().mt_debug_matmul(self._h, layer, proj | (0x100 if force_gemm else 0), _ptr(x), M,
                                     _ptr(y), _stream(stream)), "mt_debug_matmul")
         return y
+
+    def debug_trace(self) -> np.ndarray:
+        """Phase timestamps of the last persistent step: [256, L + 1, 24]
+        (needs MT_TRACE=1 when the model was created)."""
+        out = np.zeros((256, self.L + 1, 24), dtype=np.uint64)
+        check(lib().mt_debug_trace(self._h, out.ctypes.data, out.size), "mt_debug_trace")
+        return out
 
     def proj_shape(self, proj: int) -> Tuple[int, int]:
         d, F = self.d, self.F

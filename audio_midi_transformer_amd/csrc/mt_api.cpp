@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 #include <thread>
@@ -73,6 +74,7 @@ struct mt_model {
     int decode_path = MT_DECODE_AUTO;
     bool persistent_ok = false;
     void* xbuf = nullptr;
+    void* trace = nullptr;  // phase timestamps of the last persistent step (MT_TRACE=1)
     uint32_t epoch = 0;
     // prefill workspace
     size_t pf_rows = 0;
@@ -90,7 +92,7 @@ void free_model(mt_model* m) {
     if (!m) return;
     void* ptrs[] = {m->tok_emb, m->lm_head, m->ln, m->lnf, m->wq_all, m->ws_all, m->wq_ptrs,
                     m->ws_ptrs, m->kc, m->vc, m->err, m->x, m->a, m->q, m->att, m->h, m->part,
-                    m->z, m->xbuf, m->pf};
+                    m->z, m->xbuf, m->trace, m->pf};
     for (void* p : ptrs)
         if (p) (void)hipFree(p);
     delete m;
@@ -300,6 +302,12 @@ int mt_create(const mt_config* cfg, const mt_weights* w, int weights_on_device, 
         const size_t xb = persistent_xbuf_bytes(L, d, F, H, B, V);
         if (hipMalloc(&m->xbuf, xb) != hipSuccess || hipMemsetAsync(m->xbuf, 0, xb, st) != hipSuccess)
             return bail(fail(MT_ERR_OOM, "mt_create: exchange buffer of %zu bytes", xb));
+        const char* tr = getenv("MT_TRACE");
+        if (tr && tr[0] == '1') {
+            const size_t tb = persistent_trace_bytes(L);
+            if (hipMalloc(&m->trace, tb) != hipSuccess || hipMemsetAsync(m->trace, 0, tb, st) != hipSuccess)
+                return bail(fail(MT_ERR_OOM, "mt_create: trace buffer"));
+        }
     }
     if (hipStreamSynchronize(st) != hipSuccess) return bail(fail(MT_ERR_HIP, "mt_create: synchronise failed"));
     m->last_stream = st;
@@ -342,7 +350,8 @@ int mt_decode_step(mt_model* m, const int64_t* token, float* logits, int64_t* ne
     if (m->t_past + 1 > c.t_cap)
         return fail(MT_ERR_CACHE_FULL, "mt_decode_step: cache full at position %d (capacity %d)", m->t_past, c.t_cap);
     hipStream_t st = (hipStream_t)stream;
-    const bool persistent = m->persistent_ok && m->decode_path != MT_DECODE_KERNELS;
+    const bool persistent = m->persistent_ok && m->decode_path != MT_DECODE_KERNELS &&
+                            m->t_past <= persistent_max_position();
     if (persistent) {
         PersistentArgs pa{};
         pa.L = c.n_layers; pa.d = c.d_model; pa.H = c.n_heads; pa.F = c.d_ff; pa.V = c.vocab;
@@ -351,7 +360,7 @@ int mt_decode_step(mt_model* m, const int64_t* token, float* logits, int64_t* ne
         pa.wq = m->wq_ptrs; pa.ws = m->ws_ptrs; pa.kc = m->kc; pa.vc = m->vc;
         pa.token = token; pa.logits = logits; pa.next = next; pa.t0 = m->t_past;
         pa.epoch = ++m->epoch;
-        pa.resid = m->x; pa.xbuf = m->xbuf; pa.err = m->err;
+        pa.resid = m->x; pa.xbuf = m->xbuf; pa.err = m->err; pa.trace = m->trace;
         HIP_TRY(launch_persistent_decode(pa, st));
     } else {
         const int d = c.d_model;
@@ -419,6 +428,16 @@ int mt_debug_dequant(mt_model* m, int32_t layer, int32_t proj, float* out, void*
     if (layer < 0 || layer >= m->c.n_layers || proj < 0 || proj > 3)
         return fail(MT_ERR_INVALID_ARG, "mt_debug_dequant: bad layer/projection");
     HIP_TRY(launch_dequant(m->proj[layer * 4 + proj], out, (hipStream_t)stream));
+    return MT_OK;
+}
+
+int mt_debug_trace(mt_model* m, uint64_t* out, int64_t n) {
+    if (!m || !out) return fail(MT_ERR_INVALID_ARG, "mt_debug_trace: NULL argument");
+    if (!m->trace) return fail(MT_ERR_UNSUPPORTED, "mt_debug_trace: create the model with MT_TRACE=1");
+    const size_t tb = persistent_trace_bytes(m->c.n_layers);
+    if ((size_t)n * sizeof(uint64_t) < tb) return fail(MT_ERR_INVALID_ARG, "mt_debug_trace: need %zu words", tb / 8);
+    HIP_TRY(hipStreamSynchronize(m->last_stream));
+    HIP_TRY(hipMemcpy(out, m->trace, tb, hipMemcpyDeviceToHost));
     return MT_OK;
 }
 

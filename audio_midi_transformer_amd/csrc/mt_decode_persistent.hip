@@ -1,8 +1,998 @@
-// Persistent single-launch decode step (placeholder until implemented).
+// Persistent single-launch decode step for B = 1 on MI355X (gfx950).
+//
+// One launch computes one greedy decode step of the whole decoder: token
+// embedding, for every layer the pre-norm attention block (LayerNorm, fused
+// QKV projection, attention over the fixed-capacity cache with the new K/V
+// row written in place, O projection, residual) and the pre-norm FFN block
+// (LayerNorm, FFN-up + GELU, FFN-down, residual), then the final LayerNorm,
+// the FP32 LM head and the greedy argmax.  These are the decoder operations
+// the pages list: four INT4 group-32 MatMulNBits projections, one
+// GroupQueryAttention and two SkipLayerNormalization nodes per layer, FP32
+// cache and activations ("MuScriptor Medium -- optimized W4A32 ONNX Runtime"
+// README, "Model variant"); one decoder call appends a row at T_past and
+// returns last-position logits ("unifolia/muscriptor-small-onnx", decoder).
+//
+// Execution model.  256 workgroups, one per CU, stay resident for the whole
+// step.  Data moves between workgroups through exchange words of 64 bits,
+// {float value, 32-bit step tag}, each written by one atomic 8-byte store;
+// a consumer issues all its reads at once and re-reads only the words whose
+// tag is not yet this step's.  No barrier counters, no cache flushes.  Every
+// workgroup keeps its own copy of the residual stream in LDS and recomputes
+// LayerNorm locally.  Weights for a phase are loaded into registers one
+// phase ahead; each attention workgroup DMAs its K/V chunk of the next layer
+// into LDS as soon as the current chunk is consumed.
+//
+// Roles (a table built on the host, see build_roles):
+//   attention WGs  (head h, split s), 8 splits per head, all on one XCD.
+//                  Each recomputes q_h and the softmax partial over its
+//                  chunk of cached positions; splits 1..7 publish
+//                  (max, sum, acc[64]); split 0 (the head leader) merges them
+//                  with the new position and publishes attn_h.
+//   free WGs       the rest: the new K/V rows of the fused projection (to the
+//                  cache slot T_past and to the exchange), 64 of them the O
+//                  projection, 64 of them FFN-down.
+//   all WGs        FFN-up rows + GELU.
+// Per layer: A (attention partials / K,V rows) -> A2 (head merge) -> B (O)
+// -> C (LN2 + up) -> D (down) -> next layer's A; after the last layer E
+// (LN_f + LM-head rows + local argmax) and F (workgroup 0: global argmax,
+// lowest index on ties).
+//
+// Every wait is bounded: past the spin limit the workgroup sets bit 2 of the
+// error word and all workgroups leave; mt_check reports it.
 #include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
 #include "mt_internal.h"
+
 namespace mt {
-bool persistent_supported(int, int, int, int, int) { return false; }
-size_t persistent_xbuf_bytes(int, int, int, int, int, int) { return 0; }
-hipError_t launch_persistent_decode(const PersistentArgs&, hipStream_t) { return hipErrorNotSupported; }
+namespace pd {
+
+constexpr int NT = 256;      // threads per workgroup
+constexpr int NWG = 256;     // workgroups (one per CU)
+constexpr int NXCD = 8;      // workgroup w runs on XCD w % 8
+constexpr int ATT_S = 8;     // attention splits per head
+constexpr int NO_WG = 64;    // workgroups computing the O projection
+constexpr int ND_WG = 64;    // workgroups computing FFN-down
+constexpr int PW = 66;       // words per attention partial: m, l, acc[64]
+constexpr int MAXPOS = 256;  // cached positions per attention workgroup (LDS)
+constexpr int LM_ROWS = 6;   // vocabulary rows per workgroup
+constexpr uint32_t SPIN_LIMIT = 1u << 21;
+constexpr int TRACE_SLOTS = 24;
+
+constexpr int lpr_for(int K) {
+    const int G = K / 32;
+    for (int c = 1; c <= 4; ++c) {
+        if (G % c) continue;
+        const int l = G / c;
+        if (l <= 64 && (l & (l - 1)) == 0) return l;
+    }
+    return 0;
+}
+constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
+constexpr int rup(int a, int b) { return cdiv(a, b) * b; }
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+// lane of an LPR-lane group that holds the group sum after group_reduce
+constexpr int res_lane(int lpr) { return lpr == 64 ? 48 : (lpr == 32 ? 16 : 0); }
+
+// Role of one workgroup (host-built table, constant for a model).
+struct Role {
+    int head;     // attention head, -1 if none
+    int split;    // attention split (0 = head leader)
+    int o_idx;    // O-projection block, -1 if none
+    int d_idx;    // FFN-down block, -1 if none
+    int kv_row0;  // first row of the 2D K|V rows of the fused projection
+    int kv_rows;  // number of K|V rows, 0 if none
+    int pad0, pad1;
+};
+
+template <int D, int F>
+struct Cfg {
+    static constexpr int H = D / 64;
+    static constexpr int GD = D / 32, GF = F / 32;
+    static constexpr int LPR_D = lpr_for(D), CPL_D = GD / (LPR_D ? LPR_D : 1), RP_D = NT / (LPR_D ? LPR_D : 1);
+    static constexpr int LPR_F = lpr_for(F), CPL_F = GF / (LPR_F ? LPR_F : 1), RP_F = NT / (LPR_F ? LPR_F : 1);
+    static constexpr int NATT = H * ATT_S;
+    static constexpr int NFREE = NWG - NATT;
+    static constexpr int KV_ROWS = cdiv(2 * D, NFREE);
+    static constexpr int UP_ROWS = cdiv(F, NWG);
+    static constexpr int O_ROWS = cdiv(D, NO_WG);
+    static constexpr int DN_ROWS = cdiv(D, ND_WG);
+    static constexpr int NP_Q = cdiv(64, RP_D);
+    static constexpr int NP_KV = cdiv(KV_ROWS, RP_D);
+    static constexpr int NP_O = cdiv(O_ROWS, RP_D);
+    static constexpr int NP_UP = cdiv(UP_ROWS, RP_D);
+    static constexpr int NP_DN = cdiv(DN_ROWS, RP_F);
+    // exchange layout per layer (64-bit words)
+    static constexpr int XA_KV = 0;                     // new K|V row [2D]
+    static constexpr int XA_PART = XA_KV + 2 * D;       // partials [H][ATT_S][PW]
+    static constexpr int XB_ATT = XA_PART + NATT * PW;  // merged attention [D]
+    static constexpr int XB_O = XB_ATT + D;             // o [D]
+    static constexpr int XC = XB_O + D;                 // u [F]
+    static constexpr int XD = XC + F;                   // f [D]
+    static constexpr int LAYER_WORDS = rup(XD + D, 2);
+    // LDS layout (floats)
+    static constexpr int BIG = cmax(2 * MAXPOS * 64, F);  // K|V chunk, or u
+    static constexpr int OFF_R = BIG;
+    static constexpr int OFF_ACT = OFF_R + D;
+    static constexpr int OFF_XS = OFF_ACT + D;
+    static constexpr int OFF_US = OFF_XS + GD;
+    static constexpr int OFF_QH = OFF_US + GF;
+    static constexpr int OFF_SC = OFF_QH + 64;            // scores [MAXPOS]
+    static constexpr int OFF_PART = OFF_SC + MAXPOS;      // own partial [PW] + gathered [7][PW] + kv_new [128]
+    static constexpr int OFF_COMB = rup(OFF_PART + 8 * PW + 128, 4);
+    static constexpr int OFF_DELTA = OFF_COMB + 4 * 64;   // exchanged D-vector (f or o)
+    static constexpr int OFF_RED = OFF_DELTA + D;
+    static constexpr int OFF_FLAG = OFF_RED + 16;
+    static constexpr int LDS_FLOATS = OFF_FLAG + 16;
+    static_assert(D % 64 == 0 && F % 32 == 0, "widths");
+    static_assert(LPR_D > 0 && LPR_F > 0, "width has no GEMV lane mapping");
+    static_assert(NFREE >= 64, "need at least 64 workgroups without attention duty");
+    static_assert(LDS_FLOATS * 4 <= 160 * 1024, "LDS budget");
+};
+
+struct Args {
+    int L, V, t_cap;
+    float eps;
+    const float* tok_emb;
+    const float* lm_head;
+    const float* ln;
+    const float* ln_final;
+    const uint8_t* const* wq;
+    const float* const* ws;
+    float* kc;
+    float* vc;
+    const int64_t* token;
+    float* logits;
+    int64_t* next;
+    int t0;       // position of the appended row (T_past)
+    int chunk;    // cached positions per attention split
+    uint32_t epoch;
+    uint64_t* x;  // exchange words
+    const Role* roles;
+    int* err;
+    uint64_t* trace;  // optional: [NWG][L + 1][TRACE_SLOTS] wall-clock stamps
+};
+
+__device__ __forceinline__ void stamp(const Args& a, int l, int k) {
+    if (a.trace && threadIdx.x == 0)
+        a.trace[((size_t)blockIdx.x * (a.L + 1) + l) * TRACE_SLOTS + k] = wall_clock64();
+}
+
+// Loads through the global address space.  The weight pointers come from a
+// device-side table; without the cast the compiler emits flat loads, which
+// also count against the LDS wait counter.
+template <typename T>
+__device__ __forceinline__ T gload(const T* p) {
+    return *(const __attribute__((address_space(1))) T*)(p);
+}
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 gload(const uint4* p) {
+    const u32x4_t v = *(const __attribute__((address_space(1))) u32x4_t*)(p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ float4 gload(const float4* p) {
+    const f32x4_t v = *(const __attribute__((address_space(1))) f32x4_t*)(p);
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+
+// ---------------------------------------------------------------- cross-lane sums (DPP)
+
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF, false));
+}
+
+// Sum over groups of W consecutive lanes.  W <= 16: every lane of the group
+// holds the sum; W = 32: lanes 16..31 of the group; W = 64: lanes 48..63.
+template <int W>
+__device__ __forceinline__ float group_reduce(float v) {
+    if (W >= 2) v += dpp<0xB1>(v);         // quad_perm [1,0,3,2]
+    if (W >= 4) v += dpp<0x4E>(v);         // quad_perm [2,3,0,1]
+    if (W >= 8) v += dpp<0x141>(v);        // row_half_mirror
+    if (W >= 16) v += dpp<0x140>(v);       // row_mirror
+    if (W >= 32) v += dpp<0x142, 0xA>(v);  // row_bcast15 into rows 1, 3
+    if (W >= 64) v += dpp<0x143, 0x8>(v);  // row_bcast31 into row 3
+    return v;
+}
+
+template <bool MAX>
+__device__ __forceinline__ float row_reduce16(float v) {
+    if (MAX) {
+        v = fmaxf(v, dpp<0xB1>(v));
+        v = fmaxf(v, dpp<0x4E>(v));
+        v = fmaxf(v, dpp<0x141>(v));
+        v = fmaxf(v, dpp<0x140>(v));
+    } else {
+        v = group_reduce<16>(v);
+    }
+    return v;
+}
+
+// Whole-wave sum / max, returned in every lane.
+template <bool MAX>
+__device__ __forceinline__ float wave_reduce(float v) {
+    v = row_reduce16<MAX>(v);
+    const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return MAX ? fmaxf(fmaxf(a, b), fmaxf(c, d)) : (a + b) + (c + d);
+}
+
+// Whole-workgroup sum / max; `red` holds 4 floats owned by this call site.
+template <bool MAX>
+__device__ __forceinline__ float block_reduce(float v, float* red) {
+    v = wave_reduce<MAX>(v);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    return MAX ? fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])) : (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+// ---------------------------------------------------------------- exchange words
+
+__device__ __forceinline__ void ll_put(uint64_t* p, float v, uint32_t ep) {
+    __hip_atomic_store(p, ((uint64_t)ep << 32) | (uint64_t)__float_as_uint(v), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint64_t ll_get(const uint64_t* p) {
+    return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ bool aborted(int* err) {
+    return (__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & 2) != 0;
+}
+
+// Position of element k of a vector in the swizzled LDS layout: the eight
+// 16-byte sub-blocks of each 32-element group are rotated by the group index
+// so that lanes reading different groups hit different banks.
+__device__ __forceinline__ int swz(int k) {
+    const int c = k >> 5, j = (k >> 2) & 7;
+    return (c << 5) + (((j + c) & 7) << 2) + (k & 3);
+}
+
+struct Range {
+    const uint64_t* src;
+    int n;
+    float* dst;
+};
+
+// Wait for up to three ranges of exchange words (n0 + n1 + n2 <= NT * U) and
+// store their values to LDS (range 0 optionally swizzled).  All first reads
+// are issued together; re-reads of stale words too.
+template <int U, bool SWZ0>
+__device__ bool ll_gather(Range r0, Range r1, Range r2, uint32_t ep, int* err, int* s_flag) {
+    const int n01 = r0.n + r1.n, n = n01 + r2.n;
+    const uint64_t* src[U];
+    uint64_t w[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int i = u * NT + threadIdx.x;
+        src[u] = i < r0.n ? r0.src + i : (i < n01 ? r1.src + (i - r0.n) : r2.src + (i - n01));
+        w[u] = (i < n) ? ll_get(src[u]) : ((uint64_t)ep << 32);
+    }
+    bool ok = true;
+    for (uint32_t it = 0;; ++it) {
+        bool all = true;
+#pragma unroll
+        for (int u = 0; u < U; ++u) all &= (uint32_t)(w[u] >> 32) == ep;
+        if (all) break;
+        if (it > SPIN_LIMIT || ((it & 255u) == 255u && aborted(err))) {
+            ok = false;
+            break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if ((uint32_t)(w[u] >> 32) != ep) w[u] = ll_get(src[u]);
+    }
+    if (ok) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = u * NT + threadIdx.x;
+            const float v = __uint_as_float((uint32_t)w[u]);
+            if (i < r0.n) r0.dst[SWZ0 ? swz(i) : i] = v;
+            else if (i < n01) r1.dst[i - r0.n] = v;
+            else if (i < n) r2.dst[i - n01] = v;
+        }
+    } else {
+        atomicOr(err, 2);
+        *s_flag = 1;
+    }
+    __syncthreads();
+    return *s_flag == 0;
+}
+
+template <int U, bool SWZ>
+__device__ __forceinline__ bool ll_gather1(const uint64_t* src, int n, float* dst, uint32_t ep, int* err,
+                                           int* s_flag) {
+    return ll_gather<U, SWZ>(Range{src, n, dst}, Range{src, 0, dst}, Range{src, 0, dst}, ep, err, s_flag);
+}
+
+// ---------------------------------------------------------------- LayerNorm
+
+// xs[c] = sum of the 32 elements of group c (its elements stay within its
+// 32 slots in either layout).  Eight lanes per group.
+__device__ __forceinline__ void group_sums(const float* act, int K, float* xs) {
+    const int G = K / 32;
+    for (int base = 0; base < G * 8; base += NT) {
+        const int i = base + threadIdx.x;
+        const int c = i >> 3, part = i & 7;
+        float t = 0.f;
+        if (c < G) {
+            const float4 v = *reinterpret_cast<const float4*>(act + c * 32 + part * 4);
+            t = (v.x + v.y) + (v.z + v.w);
+        }
+        t = group_reduce<8>(t);
+        if (c < G && part == 0) xs[c] = t;
+    }
+    __syncthreads();
+}
+
+// LayerNorm gain and bias held in registers (element k = threadIdx.x + i*NT).
+template <int D>
+struct LnRegs {
+    static constexpr int PER = (D + NT - 1) / NT;
+    float g[PER], b[PER];
+};
+
+template <int D>
+__device__ __forceinline__ void ln_load(LnRegs<D>& p, const float* __restrict__ g, const float* __restrict__ b) {
+#pragma unroll
+    for (int i = 0; i < LnRegs<D>::PER; ++i) {
+        const int k = threadIdx.x + i * NT;
+        p.g[i] = k < D ? gload(g + k) : 0.f;
+        p.b[i] = k < D ? gload(b + k) : 0.f;
+    }
+}
+
+// r += delta (if given); y = LN(r) * g + b into act (swizzled when SWZ),
+// plus group sums into xs (if given).  Biased variance, two passes.
+template <int D, bool SWZ>
+__device__ __forceinline__ void residual_layernorm(float* r, const float* delta, const LnRegs<D>& p, float eps,
+                                                   float* act, float* xs, float* red) {
+    constexpr int PER = LnRegs<D>::PER;
+    float v[PER];
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int k = threadIdx.x + i * NT;
+        v[i] = 0.f;
+        if (k < D) {
+            v[i] = r[k];
+            if (delta) {
+                v[i] += delta[k];
+                r[k] = v[i];
+            }
+        }
+        s += v[i];
+    }
+    const float mean = block_reduce<false>(s, red) / (float)D;
+    float q = 0.f;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int k = threadIdx.x + i * NT;
+        const float c = k < D ? v[i] - mean : 0.f;
+        q = fmaf(c, c, q);
+    }
+    const float var = block_reduce<false>(q, red + 4) / (float)D;
+    const float rstd = 1.0f / sqrtf(var + eps);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int k = threadIdx.x + i * NT;
+        if (k < D) act[SWZ ? swz(k) : k] = (v[i] - mean) * rstd * p.g[i] + p.b[i];
+    }
+    __syncthreads();
+    if (xs) group_sums(act, D, xs);
+}
+
+// ---------------------------------------------------------------- INT4 rows held in registers
+
+template <int CPL, int NP>
+struct WBlk {
+    uint4 q[NP][CPL];
+    float s[NP][CPL];
+};
+
+// Rows row0 .. row0+nrows-1 of an [N, K] INT4 matrix; a lane group of LPR
+// lanes per row, lane r holding groups r, r + LPR, ... of its row.
+template <int LPR, int CPL, int NP>
+__device__ __forceinline__ void wblk_load(WBlk<CPL, NP>& w, const uint8_t* __restrict__ Wq,
+                                          const float* __restrict__ Ws, int K, int row0, int nrows) {
+    constexpr int RP = NT / LPR;
+    const int sub = threadIdx.x / LPR, lr = threadIdx.x % LPR;
+    const int G = K / 32;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        const int r = p * RP + sub;
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+            const int c = lr + LPR * j;
+            if (r < nrows) {
+                const size_t row = (size_t)(row0 + r);
+                w.q[p][j] = gload(reinterpret_cast<const uint4*>(Wq + row * (K / 2) + (size_t)c * 16));
+                w.s[p][j] = gload(Ws + row * G + c);
+            } else {
+                w.q[p][j] = make_uint4(0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u);
+                w.s[p][j] = 0.f;
+            }
+        }
+    }
+}
+
+// Activation group c (32 floats) from the swizzled LDS vector, in input order.
+__device__ __forceinline__ void load_group(const float* act, int c, float (&x)[32]) {
+    const float* base = act + (c << 5);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const float4 v = *reinterpret_cast<const float4*>(base + (((j + c) & 7) << 2));
+        x[4 * j + 0] = v.x;
+        x[4 * j + 1] = v.y;
+        x[4 * j + 2] = v.z;
+        x[4 * j + 3] = v.w;
+    }
+}
+
+// sum_k u_k x_k over one group.  Byte j of the group holds input 2j (low
+// nibble) and 2j+1 (high nibble).
+__device__ __forceinline__ float dot_u(uint4 w, const float (&x)[32]) {
+    const unsigned wd[4] = {w.x, w.y, w.z, w.w};
+    float acc = 0.f;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const unsigned lo = wd[m] & 0x0F0F0F0Fu;
+        const unsigned hi = (wd[m] >> 4) & 0x0F0F0F0Fu;
+        const float* xm = x + 8 * m;
+        acc = fmaf((float)(lo & 0xFFu), xm[0], acc);
+        acc = fmaf((float)(hi & 0xFFu), xm[1], acc);
+        acc = fmaf((float)((lo >> 8) & 0xFFu), xm[2], acc);
+        acc = fmaf((float)((hi >> 8) & 0xFFu), xm[3], acc);
+        acc = fmaf((float)((lo >> 16) & 0xFFu), xm[4], acc);
+        acc = fmaf((float)((hi >> 16) & 0xFFu), xm[5], acc);
+        acc = fmaf((float)(lo >> 24), xm[6], acc);
+        acc = fmaf((float)(hi >> 24), xm[7], acc);
+    }
+    return acc;
+}
+
+// out[p] = row . a, valid in lane res_lane(LPR) of each row group.  The
+// stored nibble is code + 8, so row . a = s * (sum u a - 8 sum a) per group.
+// A lane holds the same groups for all of its rows, so each activation group
+// is read from LDS once and used for every row.
+template <int LPR, int CPL, int NP>
+__device__ __forceinline__ void wblk_dot(const WBlk<CPL, NP>& w, const float* act, const float* xs,
+                                         float (&out)[NP]) {
+    const int lr = threadIdx.x % LPR;
+    float acc[NP];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) acc[p] = 0.f;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+        const int c = lr + LPR * j;
+        float x[32];
+        load_group(act, c, x);
+        const float x8 = -8.f * xs[c];
+#pragma unroll
+        for (int p = 0; p < NP; ++p) acc[p] = fmaf(w.s[p][j], dot_u(w.q[p][j], x) + x8, acc[p]);
+    }
+#pragma unroll
+    for (int p = 0; p < NP; ++p) out[p] = group_reduce<LPR>(acc[p]);
+}
+
+// Row handled by this lane in pass p, or -1 if this lane does not write.
+template <int LPR>
+__device__ __forceinline__ int out_row(int p) {
+    constexpr int RP = NT / LPR;
+    return (threadIdx.x % LPR) == res_lane(LPR) ? p * RP + threadIdx.x / LPR : -1;
+}
+
+__device__ __forceinline__ float gelu_erf(float x) {
+    return 0.5f * x * (1.0f + erff(x * 0.70710678118654752440f));
+}
+
+// K/V rows of one head at positions [p0, p0 + npos) of one layer's cache,
+// DMA'd into LDS: K at big[0 ..), V at big[MAXPOS * 64 ..), 64 floats each.
+template <int D>
+__device__ __forceinline__ void kv_chunk_dma(const float* kc_l, const float* vc_l, int head, int p0,
+                                             int npos, float* big) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int rounds = (npos + 15) / 16;
+    for (int rd = 0; rd < rounds; ++rd) {
+        const int pl = rd * 16 + wave * 4;
+        int pos = p0 + pl + (lane >> 4);
+        if (pos >= p0 + npos) pos = p0;  // in-range address; the slot is never read
+        const size_t off = (size_t)pos * D + head * 64 + (lane & 15) * 4;
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kc_l + off),
+                                         (__attribute__((address_space(3))) void*)(big + pl * 64), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vc_l + off),
+                                         (__attribute__((address_space(3))) void*)(big + MAXPOS * 64 + pl * 64),
+                                         16, 0, 0);
+    }
+}
+
+// Softmax partial of q over the npos cached positions in LDS: one lane per
+// position for the scores (rotated 16-byte reads, no cross-lane reduction),
+// then lanes = dimensions for sum_t p_t V_t.  Writes (max, sum, acc[64])
+// to part[0], part[1], part[2 ..].
+__device__ __forceinline__ void attend_chunk(const float* big, const float* qh, int npos, float* sc,
+                                             float* comb, float* red, float* part) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    float s = -INFINITY;
+    if (tid < npos) {
+        const float* kr = big + tid * 64;
+        float acc = 0.f;
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+            const int cc = (c + tid) & 15;
+            const float4 k4 = *reinterpret_cast<const float4*>(kr + cc * 4);
+            const float4 q4 = *reinterpret_cast<const float4*>(qh + cc * 4);
+            acc = fmaf(q4.x, k4.x, fmaf(q4.y, k4.y, fmaf(q4.z, k4.z, fmaf(q4.w, k4.w, acc))));
+        }
+        s = acc * 0.125f;
+    }
+    const float M = block_reduce<true>(s, red);
+    const float pe = (tid < npos) ? expf(s - M) : 0.f;
+    if (tid < MAXPOS) sc[tid] = pe;
+    const float Ls = block_reduce<false>(pe, red + 4);
+    // sum_t p_t V_t: wave w takes positions w, w + 4, ...; lane = dimension
+    const float* vbase = big + MAXPOS * 64;
+    float acc = 0.f;
+    for (int t = wave; t < npos; t += 4) acc = fmaf(sc[t], vbase[t * 64 + lane], acc);
+    comb[wave * 64 + lane] = acc;
+    __syncthreads();
+    if (tid < 64) {
+        part[2 + tid] = npos > 0 ? (comb[tid] + comb[64 + tid]) + (comb[128 + tid] + comb[192 + tid]) : 0.f;
+        if (tid == 0) {
+            part[0] = npos > 0 ? M : -INFINITY;
+            part[1] = npos > 0 ? Ls : 0.f;
+        }
+    }
+    __syncthreads();
+}
+
+// LM-head rows of this workgroup (wave w: rows w and w + 4 of its six).
+template <int D>
+__device__ __forceinline__ void lm_rows_load(float4 (&wrow)[2][D / 256], const float* lm_head, int V) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int v = blockIdx.x * LM_ROWS + wave + 4 * i;
+        const bool ok = v < V && wave + 4 * i < LM_ROWS;
+#pragma unroll
+        for (int c = 0; c < D / 256; ++c)
+            wrow[i][c] = ok ? gload(reinterpret_cast<const float4*>(lm_head + (size_t)v * D) + lane + 64 * c)
+                            : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+}
+
+// ---------------------------------------------------------------- the kernel
+
+template <int D, int F>
+__global__ __launch_bounds__(NT, 1) void k_decode_step(Args a) {
+    using C = Cfg<D, F>;
+    extern __shared__ float lds[];
+    float* big = lds;
+    float* r = lds + C::OFF_R;
+    float* act = lds + C::OFF_ACT;
+    float* xs = lds + C::OFF_XS;
+    float* us = lds + C::OFF_US;
+    float* qh = lds + C::OFF_QH;
+    float* sc = lds + C::OFF_SC;
+    float* own = lds + C::OFF_PART;  // own partial [PW]
+    float* gpart = own + PW;         // splits 1..7 [7][PW]
+    float* knew = gpart + 7 * PW;    // [64]
+    float* vnew = knew + 64;         // [64]
+    float* comb = lds + C::OFF_COMB; // [4][64] scratch
+    float* delta = lds + C::OFF_DELTA;  // exchanged D-vector (f or o)
+    float* red = lds + C::OFF_RED;
+    int* s_flag = reinterpret_cast<int*>(lds + C::OFF_FLAG);
+
+    const int wg = blockIdx.x, tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const uint32_t ep = a.epoch;
+    const Role role = a.roles[wg];
+    const bool attn = role.head >= 0;
+    const bool leader = attn && role.split == 0;
+    const int p0 = role.split * a.chunk;
+    const int npos = attn ? max(0, min(a.t0, p0 + a.chunk) - p0) : 0;
+    const size_t lstride = (size_t)a.t_cap * D;  // one layer of the cache (B = 1)
+    if (tid == 0) *s_flag = 0;
+
+    // weights of phase A of layer 0
+    WBlk<C::CPL_D, C::NP_Q> wqh;
+    WBlk<C::CPL_D, C::NP_KV> wkv;
+    LnRegs<D> ln1;
+    if (npos > 0) kv_chunk_dma<D>(a.kc, a.vc, role.head, p0, npos, big);
+    if (attn) wblk_load<C::LPR_D, C::CPL_D, C::NP_Q>(wqh, a.wq[0], a.ws[0], D, role.head * 64, 64);
+    else if (role.kv_rows > 0)
+        wblk_load<C::LPR_D, C::CPL_D, C::NP_KV>(wkv, a.wq[0], a.ws[0], D, D + role.kv_row0, role.kv_rows);
+    ln_load<D>(ln1, a.ln, a.ln + D);
+
+    // embedding of the token into the residual copy
+    {
+        const int64_t tok = gload(a.token);
+        const bool bad = tok < 0 || tok >= a.V;
+        if (bad && wg == 0 && tid == 0) atomicOr(a.err, 1);
+        for (int k = tid; k < D; k += NT) r[k] = bad ? __builtin_nanf("") : gload(a.tok_emb + (size_t)tok * D + k);
+        __syncthreads();
+    }
+
+    float4 wrow[2][D / 256];  // LM-head rows, loaded during the last layer
+    LnRegs<D> lnf;
+
+    for (int l = 0; l < a.L; ++l) {
+        uint64_t* X = a.x + (size_t)l * C::LAYER_WORDS;
+        const uint8_t* const* wq = a.wq + 4 * l;
+        const float* const* ws = a.ws + 4 * l;
+        const float* ln = a.ln + (size_t)l * 4 * D;
+        float* kc_l = a.kc + (size_t)l * lstride;
+        float* vc_l = a.vc + (size_t)l * lstride;
+        const bool last = l + 1 == a.L;
+
+        // ===================== phase A: r += f_prev; LN1; q / K,V rows; attention partial
+        stamp(a, l, 0);
+        if (l > 0) {
+            if (!ll_gather1<cdiv(D, NT), false>(a.x + (size_t)(l - 1) * C::LAYER_WORDS + C::XD, D, delta, ep,
+                                                a.err, s_flag))
+                return;
+        }
+        stamp(a, l, 1);
+        residual_layernorm<D, true>(r, l > 0 ? delta : nullptr, ln1, a.eps, act, xs, red);
+        stamp(a, l, 2);
+
+        WBlk<C::CPL_D, C::NP_O> wo;
+        WBlk<C::CPL_D, C::NP_UP> wu;
+        WBlk<C::CPL_F, C::NP_DN> wd;
+        LnRegs<D> ln2;
+        const int urow = wg * C::UP_ROWS;
+        if (attn) {
+            float o[C::NP_Q];
+            wblk_dot<C::LPR_D, C::CPL_D, C::NP_Q>(wqh, act, xs, o);
+#pragma unroll
+            for (int p = 0; p < C::NP_Q; ++p) {
+                const int rr = out_row<C::LPR_D>(p);
+                if (rr >= 0 && rr < 64) qh[rr] = o[p];
+            }
+            __builtin_amdgcn_s_waitcnt(0);  // K/V chunk DMA (and earlier loads) complete
+            __syncthreads();
+            stamp(a, l, 3);
+            // phase-C weights load behind the attention
+            wblk_load<C::LPR_D, C::CPL_D, C::NP_UP>(wu, wq[2], ws[2], D, urow, max(0, min(C::UP_ROWS, F - urow)));
+            ln_load<D>(ln2, ln + 2 * D, ln + 3 * D);
+            attend_chunk(big, qh, npos, sc, comb, red + 8, own);
+            stamp(a, l, 4);
+            if (!leader) {
+                if (!last && npos > 0) kv_chunk_dma<D>(kc_l + lstride, vc_l + lstride, role.head, p0, npos, big);
+                uint64_t* pw = X + C::XA_PART + (size_t)(role.head * ATT_S + role.split) * PW;
+                if (tid < PW) ll_put(pw + tid, own[tid], ep);
+            }
+        } else {
+            if (role.kv_rows > 0) {
+                float o[C::NP_KV];
+                wblk_dot<C::LPR_D, C::CPL_D, C::NP_KV>(wkv, act, xs, o);
+#pragma unroll
+                for (int p = 0; p < C::NP_KV; ++p) {
+                    const int rr = out_row<C::LPR_D>(p);
+                    if (rr >= 0 && rr < role.kv_rows) {
+                        const int row = role.kv_row0 + rr;
+                        const size_t slot = (size_t)a.t0 * D;
+                        if (row < D) kc_l[slot + row] = o[p];
+                        else vc_l[slot + row - D] = o[p];
+                        ll_put(X + C::XA_KV + row, o[p], ep);
+                    }
+                }
+            }
+            // weights of phases B, C, D
+            if (role.o_idx >= 0) {
+                const int orow = role.o_idx * C::O_ROWS;
+                wblk_load<C::LPR_D, C::CPL_D, C::NP_O>(wo, wq[1], ws[1], D, orow, min(C::O_ROWS, D - orow));
+            }
+            wblk_load<C::LPR_D, C::CPL_D, C::NP_UP>(wu, wq[2], ws[2], D, urow, max(0, min(C::UP_ROWS, F - urow)));
+            ln_load<D>(ln2, ln + 2 * D, ln + 3 * D);
+            if (role.d_idx >= 0) {
+                const int drow = role.d_idx * C::DN_ROWS;
+                wblk_load<C::LPR_F, C::CPL_F, C::NP_DN>(wd, wq[3], ws[3], F, drow, min(C::DN_ROWS, D - drow));
+            }
+        }
+
+        // ===================== phase A2: head leader merges the splits and the new position
+        if (leader) {
+            const int h = role.head;
+            if (!ll_gather<cdiv(7 * PW + 128, NT), false>(
+                    Range{X + C::XA_PART + (size_t)(h * ATT_S + 1) * PW, 7 * PW, gpart},
+                    Range{X + C::XA_KV + h * 64, 64, knew}, Range{X + C::XA_KV + D + h * 64, 64, vnew}, ep, a.err,
+                    s_flag))
+                return;
+            stamp(a, l, 5);
+            if (!last && npos > 0) kv_chunk_dma<D>(kc_l + lstride, vc_l + lstride, h, p0, npos, big);
+            if (tid < 64) {
+                const float snew = wave_reduce<false>(qh[tid] * knew[tid]) * 0.125f;
+                float M = fmaxf(snew, own[0]);
+                for (int s = 0; s < 7; ++s) M = fmaxf(M, gpart[s * PW]);
+                float Ls = expf(snew - M);
+                float A = Ls * vnew[tid];
+                if (own[0] != -INFINITY) {
+                    const float wgt = expf(own[0] - M);
+                    Ls = fmaf(wgt, own[1], Ls);
+                    A = fmaf(wgt, own[2 + tid], A);
+                }
+                for (int s = 0; s < 7; ++s) {
+                    const float ms = gpart[s * PW];
+                    if (ms == -INFINITY) continue;
+                    const float wgt = expf(ms - M);
+                    Ls = fmaf(wgt, gpart[s * PW + 1], Ls);
+                    A = fmaf(wgt, gpart[s * PW + 2 + tid], A);
+                }
+                ll_put(X + C::XB_ATT + h * 64 + tid, A / Ls, ep);
+            }
+        }
+
+        // ===================== phase B: O rows
+        if (role.o_idx >= 0) {
+            if (!ll_gather1<cdiv(D, NT), true>(X + C::XB_ATT, D, act, ep, a.err, s_flag)) return;
+            stamp(a, l, 6);
+            group_sums(act, D, xs);
+            float o[C::NP_O];
+            wblk_dot<C::LPR_D, C::CPL_D, C::NP_O>(wo, act, xs, o);
+            const int row0 = role.o_idx * C::O_ROWS;
+#pragma unroll
+            for (int p = 0; p < C::NP_O; ++p) {
+                const int rr = out_row<C::LPR_D>(p);
+                if (rr >= 0 && rr < C::O_ROWS && row0 + rr < D) ll_put(X + C::XB_O + row0 + rr, o[p], ep);
+            }
+            stamp(a, l, 7);
+        }
+
+        // ===================== phase C: r += o; LN2; FFN-up rows + GELU
+        if (!ll_gather1<cdiv(D, NT), false>(X + C::XB_O, D, delta, ep, a.err, s_flag)) return;
+        stamp(a, l, 8);
+        residual_layernorm<D, true>(r, delta, ln2, a.eps, act, xs, red);
+        {
+            float o[C::NP_UP];
+            wblk_dot<C::LPR_D, C::CPL_D, C::NP_UP>(wu, act, xs, o);
+#pragma unroll
+            for (int p = 0; p < C::NP_UP; ++p) {
+                const int rr = out_row<C::LPR_D>(p);
+                if (rr >= 0 && rr < C::UP_ROWS && urow + rr < F) ll_put(X + C::XC + urow + rr, gelu_erf(o[p]), ep);
+            }
+        }
+        stamp(a, l, 9);
+        // next layer's phase-A weights (workgroups without FFN-down load them now)
+        const uint8_t* const* wqn = wq + 4;
+        const float* const* wsn = ws + 4;
+        if (role.d_idx < 0) {
+            if (!last) {
+                if (attn) wblk_load<C::LPR_D, C::CPL_D, C::NP_Q>(wqh, wqn[0], wsn[0], D, role.head * 64, 64);
+                else if (role.kv_rows > 0)
+                    wblk_load<C::LPR_D, C::CPL_D, C::NP_KV>(wkv, wqn[0], wsn[0], D, D + role.kv_row0, role.kv_rows);
+                ln_load<D>(ln1, ln + 4 * D, ln + 5 * D);
+            } else {
+                lm_rows_load<D>(wrow, a.lm_head, a.V);
+                ln_load<D>(lnf, a.ln_final, a.ln_final + D);
+            }
+        }
+
+        // ===================== phase D: FFN-down rows
+        if (role.d_idx >= 0) {
+            float* u = big;  // swizzled [F]
+            if (!ll_gather1<cdiv(F, NT), true>(X + C::XC, F, u, ep, a.err, s_flag)) return;
+            stamp(a, l, 10);
+            if (!last) {
+                if (role.kv_rows > 0)
+                    wblk_load<C::LPR_D, C::CPL_D, C::NP_KV>(wkv, wqn[0], wsn[0], D, D + role.kv_row0, role.kv_rows);
+                ln_load<D>(ln1, ln + 4 * D, ln + 5 * D);
+            } else {
+                lm_rows_load<D>(wrow, a.lm_head, a.V);
+                ln_load<D>(lnf, a.ln_final, a.ln_final + D);
+            }
+            group_sums(u, F, us);
+            float o[C::NP_DN];
+            wblk_dot<C::LPR_F, C::CPL_F, C::NP_DN>(wd, u, us, o);
+            const int row0 = role.d_idx * C::DN_ROWS;
+#pragma unroll
+            for (int p = 0; p < C::NP_DN; ++p) {
+                const int rr = out_row<C::LPR_F>(p);
+                if (rr >= 0 && rr < C::DN_ROWS && row0 + rr < D) ll_put(X + C::XD + row0 + rr, o[p], ep);
+            }
+            stamp(a, l, 11);
+        }
+    }
+
+    // ===================== phase E: r += f; z = LN_f(r); LM-head rows + local argmax
+    uint64_t* XE = a.x + (size_t)a.L * C::LAYER_WORDS;
+    {
+        stamp(a, a.L, 0);
+        if (!ll_gather1<cdiv(D, NT), false>(a.x + (size_t)(a.L - 1) * C::LAYER_WORDS + C::XD, D, delta, ep, a.err,
+                                            s_flag))
+            return;
+        stamp(a, a.L, 1);
+        residual_layernorm<D, false>(r, delta, lnf, a.eps, act, nullptr, red);
+        float* cand_v = comb;                                 // [8]
+        int* cand_i = reinterpret_cast<int*>(comb + 8);       // [8]
+        if (tid < 8) {
+            cand_v[tid] = -INFINITY;
+            cand_i[tid] = 0x7fffffff;
+        }
+        __syncthreads();
+        const int v0 = wg * LM_ROWS;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int v = v0 + wave + 4 * i;
+            float acc = 0.f;
+#pragma unroll
+            for (int c = 0; c < D / 256; ++c) {
+                const float4 z = reinterpret_cast<const float4*>(act)[lane + 64 * c];
+                acc = fmaf(wrow[i][c].x, z.x, fmaf(wrow[i][c].y, z.y, fmaf(wrow[i][c].z, z.z, fmaf(wrow[i][c].w, z.w, acc))));
+            }
+            acc = wave_reduce<false>(acc);
+            if (lane == 0 && v < a.V && wave + 4 * i < LM_ROWS) {
+                a.logits[v] = acc;
+                cand_v[wave + 4 * i] = acc;
+                cand_i[wave + 4 * i] = v;
+            }
+        }
+        __syncthreads();
+        if (tid == 0) {
+            float bv = -INFINITY;
+            int bi = 0x7fffffff;
+            for (int i = 0; i < 8; ++i) {
+                const int ii = cand_i[i];
+                if (ii == 0x7fffffff) continue;
+                if (bi == 0x7fffffff || cand_v[i] > bv || (cand_v[i] == bv && ii < bi)) {
+                    bv = cand_v[i];
+                    bi = ii;
+                }
+            }
+            ll_put(XE + 2 * wg, bv, ep);
+            ll_put(XE + 2 * wg + 1, __int_as_float(bi), ep);
+        }
+    }
+
+    // ===================== phase F: global argmax (workgroup 0)
+    if (wg == 0) {
+        float* cv = big;
+        if (!ll_gather1<cdiv(2 * NWG, NT), false>(XE, 2 * NWG, cv, ep, a.err, s_flag)) return;
+        if (tid < 64) {
+            float bv = -INFINITY;
+            int bi = 0x7fffffff;
+            for (int i = tid; i < NWG; i += 64) {
+                const float v = cv[2 * i];
+                const int ii = __float_as_int(cv[2 * i + 1]);
+                if (ii == 0x7fffffff) continue;
+                if (bi == 0x7fffffff || v > bv || (v == bv && ii < bi)) {
+                    bv = v;
+                    bi = ii;
+                }
+            }
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) {
+                const float ov = __shfl_xor(bv, o);
+                const int oi = __shfl_xor(bi, o);
+                if (oi != 0x7fffffff && (bi == 0x7fffffff || ov > bv || (ov == bv && oi < bi))) {
+                    bv = ov;
+                    bi = oi;
+                }
+            }
+            if (tid == 0) a.next[0] = bi == 0x7fffffff ? 0 : bi;
+        }
+        stamp(a, a.L, 2);
+    }
+}
+
+// Role table for the shape: attention heads spread over the XCDs with the 8
+// splits of a head on one XCD; O, FFN-down and K/V-row duties on the rest.
+template <int D, int F>
+static void build_roles(Role* roles) {
+    using C = Cfg<D, F>;
+    int free_list[NWG];
+    int nfree = 0;
+    int nh_x[NXCD] = {0};
+    for (int h = 0; h < C::H; ++h) ++nh_x[h % NXCD];
+    for (int w = 0; w < NWG; ++w) {
+        Role& r = roles[w];
+        r = Role{-1, 0, -1, -1, 0, 0, 0, 0};
+        const int x = w % NXCD, slot = w / NXCD;
+        if (slot < nh_x[x] * ATT_S) {
+            r.head = (slot / ATT_S) * NXCD + x;
+            r.split = slot % ATT_S;
+        } else {
+            free_list[nfree++] = w;
+        }
+    }
+    for (int i = 0; i < nfree; ++i) {
+        Role& r = roles[free_list[i]];
+        if (nfree >= NO_WG + ND_WG) {
+            if (i < NO_WG) r.o_idx = i;
+            else if (i < NO_WG + ND_WG) r.d_idx = i - NO_WG;
+        } else {
+            if (i < NO_WG) r.o_idx = i;
+            if (i < ND_WG) r.d_idx = i;
+        }
+        const int row0 = i * C::KV_ROWS;
+        r.kv_row0 = row0;
+        r.kv_rows = row0 < 2 * D ? (2 * D - row0 < C::KV_ROWS ? 2 * D - row0 : C::KV_ROWS) : 0;
+    }
+}
+
+}  // namespace pd
+
+// ---------------------------------------------------------------- host side
+
+bool persistent_supported(int d, int F, int H, int B, int V) {
+    if (B != 1 || V > pd::NWG * pd::LM_ROWS) return false;
+    const bool shape = (d == 768 && F == 3072) || (d == 1024 && F == 4096) || (d == 1536 && F == 6144);
+    if (!shape) return false;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return false;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return false;
+    return cus >= pd::NWG;
+}
+
+template <int D, int F>
+static size_t layer_words() {
+    return pd::Cfg<D, F>::LAYER_WORDS;
+}
+
+size_t persistent_xbuf_bytes(int L, int d, int F, int H, int B, int V) {
+    size_t lw = 0;
+    if (d == 768) lw = layer_words<768, 3072>();
+    else if (d == 1024) lw = layer_words<1024, 4096>();
+    else lw = layer_words<1536, 6144>();
+    // exchange words + exchange E + the role table
+    return 8 * (lw * L + 2 * pd::NWG) + sizeof(pd::Role) * pd::NWG + 256;
+}
+
+// The largest T_past the persistent step handles (8 splits of <= MAXPOS).
+int persistent_max_position() { return pd::ATT_S * pd::MAXPOS; }
+
+size_t persistent_trace_bytes(int L) { return sizeof(uint64_t) * pd::NWG * (L + 1) * pd::TRACE_SLOTS; }
+
+template <int D, int F>
+static hipError_t launch_t(const PersistentArgs& p, hipStream_t st) {
+    using C = pd::Cfg<D, F>;
+    const size_t lw = C::LAYER_WORDS;
+    uint64_t* x = static_cast<uint64_t*>(p.xbuf);
+    pd::Role* roles = reinterpret_cast<pd::Role*>(x + lw * p.L + 2 * pd::NWG);
+    // the role table lives at the end of the exchange buffer; built once per buffer
+    static thread_local const void* built_for = nullptr;
+    if (built_for != p.xbuf) {
+        pd::Role host[pd::NWG];
+        pd::build_roles<D, F>(host);
+        hipError_t e = hipMemcpyAsync(roles, host, sizeof host, hipMemcpyHostToDevice, st);
+        if (e != hipSuccess) return e;
+        e = hipStreamSynchronize(st);
+        if (e != hipSuccess) return e;
+        built_for = p.xbuf;
+    }
+    pd::Args a{};
+    a.L = p.L; a.V = p.V; a.t_cap = p.t_cap; a.eps = p.eps;
+    a.tok_emb = p.tok_emb; a.lm_head = p.lm_head; a.ln = p.ln; a.ln_final = p.ln_final;
+    a.wq = p.wq; a.ws = p.ws; a.kc = p.kc; a.vc = p.vc; a.token = p.token; a.logits = p.logits;
+    a.next = p.next; a.t0 = p.t0; a.epoch = p.epoch; a.x = x; a.roles = roles; a.err = p.err;
+    a.trace = static_cast<uint64_t*>(p.trace);
+    const int chunk = (p.t0 + pd::ATT_S - 1) / pd::ATT_S;
+    if (chunk > pd::MAXPOS) return hipErrorInvalidValue;
+    a.chunk = chunk < 1 ? 1 : chunk;
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void*)pd::k_decode_step<D, F>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           (int)(sizeof(float) * C::LDS_FLOATS));
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    pd::k_decode_step<D, F><<<dim3(pd::NWG), dim3(pd::NT), sizeof(float) * C::LDS_FLOATS, st>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_persistent_decode(const PersistentArgs& p, hipStream_t st) {
+    if (p.B != 1) return hipErrorInvalidValue;
+    if (p.d == 768 && p.F == 3072) return launch_t<768, 3072>(p, st);
+    if (p.d == 1024 && p.F == 4096) return launch_t<1024, 4096>(p, st);
+    if (p.d == 1536 && p.F == 6144) return launch_t<1536, 6144>(p, st);
+    return hipErrorInvalidValue;
+}
+
 }  // namespace mt

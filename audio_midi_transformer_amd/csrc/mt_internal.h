@@ -75,9 +75,12 @@ struct PersistentArgs {
     float* resid;          // [B, d] residual stream
     void* xbuf;            // exchange buffers
     int* err;
+    void* trace;           // optional phase timestamps (NULL = off)
 };
 bool persistent_supported(int d, int F, int H, int B, int V);
 size_t persistent_xbuf_bytes(int L, int d, int F, int H, int B, int V);
 hipError_t launch_persistent_decode(const PersistentArgs& a, hipStream_t st);
+int persistent_max_position();
+size_t persistent_trace_bytes(int L);
 
 }  // namespace mt

@@ -1,0 +1,256 @@
+"""Benchmark of the MuScriptor INT4 decoder step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2] [--path auto]
+
+One bench step is one whole pass of the hot path over one batch: the prefill
+of the workload's prefix / prompt rows followed by every greedy decode step
+of the workload (for the medium workload: 504 prefix rows, then decoding
+until the cache holds 2048 positions).  Inputs are seeded synthetic tensors
+already resident in GPU memory; decoding feeds the device argmax back without
+returning to the host.
+
+Printed (one JSON line): steady-state decode ms/token (steps 8 onward) as
+`value`, tokens/s, achieved HBM GB/s from algorithmic bytes, prefill time and
+MFMA utilisation, a roofline object for the decode launch, and the CPU
+oracle timed on a bounded sample of the same workload on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode ms/token + achieved HBM GB/s, medium W4g32 decoder, cache 2504, B=1"
+HBM_PEAK_GBPS = 8000.0
+FP32_MFMA_PEAK_TFLOPS = 157.3
+STEADY_FROM = 8
+
+
+def step_bytes(shape, B: int, T: int) -> float:
+    """Algorithmic HBM bytes of one decode step over B sequences with T keys
+    (the new row included): packed INT4 nibbles + FP32 group scales of the
+    four projections, FP32 LM head, LayerNorm parameters, live K/V read, new
+    K/V row written, embedding row, logits, token in / argmax out."""
+    L, d, F, V = shape.n_layers, shape.d_model, shape.d_ff, shape.vocab
+    w_per_layer = 3 * d * d + d * d + 2 * d * F
+    weights = 0.625 * w_per_layer * L + 4.0 * V * d + 4.0 * (4 * L * d + 2 * d)
+    per_seq = 8.0 * L * d * T + 8.0 * L * d + 4.0 * d + 4.0 * V + 16.0
+    return weights + B * per_seq
+
+
+def prefill_flops(shape, B: int, M: int) -> float:
+    L, d, F, V = shape.n_layers, shape.d_model, shape.d_ff, shape.vocab
+    w_per_layer = 3 * d * d + d * d + 2 * d * F
+    return B * (2.0 * M * w_per_layer * L + 2.0 * L * d * M * (M + 1) + 2.0 * d * V)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "audio_midi_transformer_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as fh:
+            h.update(name.encode())
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel: str, workload_key: str):
+    """HBM traffic per launch from committed rocprofv3 counter summaries, or
+    None when they are missing or were taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_wl{workload_key}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(wl, weights, prefix_np, tokens_np, max_steps: int = 8):
+    """The CPU oracle as it stands, on this host, on a bounded sample of the
+    workload: its prefill, then `max_steps` greedy decode steps."""
+    import oracle
+    cores = len(os.sched_getaffinity(0))
+    cores = min(cores, int(os.environ.get("OMP_NUM_THREADS", cores)))
+    os.environ["OMP_NUM_THREADS"] = str(cores)
+    m = oracle.OracleModel.from_weights(weights, batch=wl.batch, t_cap=wl.t_cap)
+    t0 = time.perf_counter()
+    _, nxt = m.forward(tokens=tokens_np, prefix=prefix_np)
+    t1 = time.perf_counter()
+    n = min(max_steps, wl.decode_steps)
+    for _ in range(n):
+        _, nxt = m.forward(tokens=nxt.reshape(wl.batch, 1))
+    t2 = time.perf_counter()
+    m.close()
+    return {
+        "value": (t2 - t1) * 1000.0 / n,
+        "unit": "ms/token",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": (f"oracle prefill of {wl.prefix_len + wl.n_tokens} rows "
+                   f"({(t1 - t0) * 1000.0:.0f} ms) then {n} greedy decode steps of the same "
+                   f"workload, B={wl.batch}; value = mean ms per decode step"),
+        "prefill_ms": (t1 - t0) * 1000.0,
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="2")
+    ap.add_argument("--path", choices=["auto", "kernels", "persistent"], default="auto")
+    ap.add_argument("--decode-steps", type=int, default=None,
+                    help="override the number of decode steps per pass (default: the workload's)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the decoder step's natural shard is independent "
+              "sequences (no collective), so N GPUs run N copies of this bench; "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        return 2
+
+    import torch
+    from audio_midi_transformer_amd import binding, synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    torch.cuda.set_device(0)
+    wl = synth.WORKLOADS[args.workload]
+    shape, B = wl.shape, wl.batch
+    n_dec = wl.decode_steps if args.decode_steps is None else args.decode_steps
+    R0 = wl.prefix_len + wl.n_tokens
+    assert R0 + n_dec <= wl.t_cap
+
+    print(f"[bench] workload {wl.key}: {wl.name}; generating weights", file=sys.stderr, flush=True)
+    weights = synth.model_weights(shape, wl.model_seed)
+    prefix_np = synth.workload_prefix(wl) if wl.prefix_len else None
+    tokens_np = synth.workload_tokens(wl) if wl.n_tokens else None
+    dec = binding.Decoder(weights, batch=B, t_cap=wl.t_cap)
+    path = {"auto": binding.MT_DECODE_AUTO, "kernels": binding.MT_DECODE_KERNELS,
+            "persistent": binding.MT_DECODE_PERSISTENT}[args.path]
+    persistent = path != binding.MT_DECODE_KERNELS and dec_is_persistent(dec)
+    dec.set_decode_path(path)
+    dev = torch.device("cuda", 0)
+    prefix = torch.from_numpy(prefix_np).to(dev) if prefix_np is not None else None
+    tokens = torch.from_numpy(tokens_np).to(dev) if tokens_np is not None else None
+    logits = torch.empty((B, shape.vocab), dtype=torch.float32, device=dev)
+    nxt = [torch.empty((B,), dtype=torch.int64, device=dev) for _ in range(2)]
+    stream = torch.cuda.current_stream()
+
+    def one_pass(ev=None):
+        dec.reset()
+        if ev is not None:
+            ev["p0"].record(stream)
+        dec.prefill(tokens, prefix, logits, nxt[0])
+        if ev is not None:
+            ev["p1"].record(stream)
+        for k in range(n_dec):
+            if ev is not None and k == STEADY_FROM:
+                ev["s0"].record(stream)
+            if ev is not None and "per" in ev:
+                ev["per"][k][0].record(stream)
+            dec.decode_step(nxt[k & 1], logits, nxt[(k + 1) & 1])
+            if ev is not None and "per" in ev:
+                ev["per"][k][1].record(stream)
+        if ev is not None:
+            ev["s1"].record(stream)
+
+    for _ in range(args.warmup):
+        one_pass()
+    torch.cuda.synchronize()
+    dec.check()
+    print("[bench] warmup done", file=sys.stderr, flush=True)
+
+    mk = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    evs = [dict(p0=mk(), p1=mk(), s0=mk(), s1=mk()) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        one_pass(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    dec.check()
+    prefill_ms = float(np.median([e["p0"].elapsed_time(e["p1"]) for e in evs]))
+    steady_ms = float(np.mean([e["s0"].elapsed_time(e["s1"]) for e in evs]))
+    n_steady = n_dec - STEADY_FROM
+    ms_tok = steady_ms / n_steady
+    steady_bytes = sum(step_bytes(shape, B, R0 + k + 1) for k in range(STEADY_FROM, n_dec))
+    gbps = steady_bytes / (steady_ms * 1e-3) / 1e9
+
+    # per-launch pass: events around every decode call (one launch each on the
+    # persistent path) for the distribution and the roofline
+    per = dict(p0=mk(), p1=mk(), s0=mk(), s1=mk(), per=[(mk(), mk()) for _ in range(n_dec)])
+    one_pass(per)
+    torch.cuda.synchronize()
+    step_ms = np.array([a.elapsed_time(b) for a, b in per["per"]])[STEADY_FROM:]
+    launch_bytes = np.array([step_bytes(shape, B, R0 + k + 1) for k in range(STEADY_FROM, n_dec)])
+    kernel_name = "mt_decode_step_persistent" if persistent else "decode_step_kernels"
+    achieved = float(launch_bytes.sum() / (step_ms.sum() * 1e-3) / 1e9)
+    traffic = traffic_from_profiles(kernel_name, wl.key)
+    pf_flops = prefill_flops(shape, B, R0)
+
+    out = {
+        "metric": METRIC,
+        "value": round(ms_tok, 5),
+        "unit": "ms/token",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1000.0 / args.steps, 3),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "weights": "int4 symmetric RTN, group 32, fp32 scales",
+        "data": "synthetic (seeded N(0,0.02) weights, N(0,1) prefix; no checkpoint)",
+        "config": {"workload": f"{wl.key}: {wl.name}", "layers": shape.n_layers,
+                   "d_model": shape.d_model, "heads": shape.n_heads, "d_ff": shape.d_ff,
+                   "vocab": shape.vocab, "batch": B, "prefix_rows": wl.prefix_len,
+                   "prompt_tokens": wl.n_tokens, "decode_steps": n_dec, "t_cap": wl.t_cap,
+                   "decode_path": "persistent" if persistent else "kernels"},
+        "decode_tokens_per_s": round(B * 1000.0 / ms_tok, 1),
+        "decode_ms_per_token": {"mean": round(float(step_ms.mean()), 5),
+                                "median": round(float(np.median(step_ms)), 5),
+                                "p90": round(float(np.percentile(step_ms, 90)), 5)},
+        "achieved_GBps": round(gbps, 1),
+        "hbm_frac_of_8TBps": round(gbps / HBM_PEAK_GBPS, 4),
+        "prefill_ms": round(prefill_ms, 3),
+        "prefill_fp32_mfma_frac": round(pf_flops / (prefill_ms * 1e-3) / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4),
+        "roofline": {"kernel": kernel_name, "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic,
+                     "algorithmic_bytes_per_launch": round(float(launch_bytes.mean()), 1)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(wl, weights, prefix_np, tokens_np)
+    dec.close()
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def dec_is_persistent(dec) -> bool:
+    from audio_midi_transformer_amd import binding
+    try:
+        dec.set_decode_path(binding.MT_DECODE_PERSISTENT)
+    except binding.MTError:
+        return False
+    return True
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -171,6 +171,12 @@ int mt_debug_dequant(mt_model* m, int32_t layer, int32_t proj, float* out, void*
 int mt_debug_matmul(mt_model* m, int32_t layer, int32_t proj, const float* x, int32_t M, float* y,
                     void* stream);
 
+/* Phase timestamps of the last persistent decode step (wall clock, 100 MHz
+ * ticks), [256 workgroups][L + 1][24] words, copied to the host buffer `out`
+ * of n words.  Only available when the model was created with the
+ * environment variable MT_TRACE=1; synchronises the model's stream. */
+int mt_debug_trace(mt_model* m, uint64_t* out, int64_t n);
+
 #ifdef __cplusplus
 }
 #endif

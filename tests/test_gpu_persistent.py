@@ -1,0 +1,119 @@
+"""GPU parity of the persistent single-launch decode step: against the CPU
+oracle at the three model widths (few layers, so the oracle is quick), with
+prefixes that leave some attention splits empty or ragged, across the
+position where decoding hands over to the per-operation kernels, and against
+the per-operation kernel path on full-depth models."""
+import numpy as np
+import pytest
+
+from audio_midi_transformer_amd import binding, synth
+from parity import TOL, check_argmax, compare_logits, top2
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+WIDTHS = {"small": synth.SMALL, "medium": synth.MEDIUM, "large": synth.LARGE}
+
+
+def _dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda", 0)
+
+
+def _t(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(_dev())
+
+
+def _teacher_forced(oracle_mod, w, B, t_cap, prefix, tokens, steps, tol, path):
+    om = oracle_mod.OracleModel.from_weights(w, batch=B, t_cap=t_cap)
+    dec = binding.Decoder(w, batch=B, t_cap=t_cap)
+    dec.set_decode_path(path)
+    lo, no = om.forward(tokens=tokens, prefix=prefix)
+    lg, ng = dec.prefill(_t(tokens) if tokens is not None else None, _t(prefix) if prefix is not None else None)
+    compare_logits(lg.cpu().numpy(), lo, tol, "prefill")
+    worst, ties = 0.0, 0
+    for k in range(steps):
+        tok = no.reshape(B, 1)
+        lo, no = om.forward(tokens=tok)
+        lg, ng = dec.decode_step(_t(tok.reshape(B)))
+        g = lg.cpu().numpy()
+        worst = max(worst, compare_logits(g, lo, tol, f"step {k} (position {om.position - 1})"))
+        ties += check_argmax(ng.cpu().numpy(), *top2(lo), None, tol)
+    dec.check()
+    K, V = dec.kv_cache()
+    Ko, Vo = om.kv()
+    T = om.position
+    np.testing.assert_allclose(K[:, :, :T].cpu().numpy(), Ko[:, :, :T], rtol=0, atol=5e-5)
+    np.testing.assert_allclose(V[:, :, :T].cpu().numpy(), Vo[:, :, :T], rtol=0, atol=5e-5)
+    dec.close()
+    om.close()
+    return worst, ties
+
+
+@pytest.mark.parametrize("width", ["small", "medium", "large"])
+@pytest.mark.parametrize("prefix_len", [3, 70, 301])
+def test_persistent_vs_oracle(oracle_mod, width, prefix_len):
+    """Prefix 3 leaves most of the 8 attention splits empty; 70 and 301 give
+    ragged chunks."""
+    _dev()
+    base = WIDTHS[width]
+    shape = synth.ModelShape(base.name, 2, base.d_model, base.n_heads, base.d_ff)
+    w = synth.model_weights(shape, 41)
+    prefix = np.random.default_rng(prefix_len).standard_normal((1, prefix_len, shape.d_model)).astype(np.float32)
+    _teacher_forced(oracle_mod, w, 1, prefix_len + 16, prefix, None, 10, TOL[width],
+                    binding.MT_DECODE_PERSISTENT)
+
+
+def test_persistent_tokens_only(oracle_mod):
+    """Config-0 style start: token rows only, decoding from position 8."""
+    _dev()
+    shape = synth.ModelShape("small", 3, 768, 12, 3072)
+    w = synth.model_weights(shape, 42)
+    tokens = np.random.default_rng(8).integers(0, shape.vocab, size=(1, 8))
+    _teacher_forced(oracle_mod, w, 1, 40, None, tokens, 16, TOL["small"], binding.MT_DECODE_PERSISTENT)
+
+
+def test_decode_across_persistent_limit(oracle_mod):
+    """Positions 2040 .. 2055: the persistent step covers T_past <= 2048, the
+    per-operation kernels take over after that; both must match the oracle."""
+    _dev()
+    shape = synth.ModelShape("small", 1, 768, 12, 3072)
+    w = synth.model_weights(shape, 43)
+    prefix = np.random.default_rng(9).standard_normal((1, 2040, 768)).astype(np.float32)
+    _teacher_forced(oracle_mod, w, 1, 2060, prefix, None, 16, TOL["small"], binding.MT_DECODE_AUTO)
+
+
+@pytest.mark.parametrize("width", ["small", "medium", "large"])
+def test_persistent_equals_kernel_path_full_depth(width):
+    """Full-depth models, 40 teacher-forced steps after a 504-row prefix: the
+    persistent step and the per-operation kernels agree within the tolerance
+    (both are checked against the oracle elsewhere)."""
+    dev = _dev()
+    shape = WIDTHS[width]
+    w = synth.model_weights(shape, 44)
+    packed = binding.pack_weights(w)
+    prefix = _t(np.random.default_rng(10).standard_normal((1, 504, shape.d_model)).astype(np.float32))
+    a = binding.Decoder(w, batch=1, t_cap=600, packed=packed)
+    b = binding.Decoder(w, batch=1, t_cap=600, packed=packed)
+    a.set_decode_path(binding.MT_DECODE_PERSISTENT)
+    b.set_decode_path(binding.MT_DECODE_KERNELS)
+    la, na = a.prefill(None, prefix)
+    lb, nb = b.prefill(None, prefix)
+    tol = TOL[width]
+    for k in range(40):
+        tok = nb.clone()
+        la, na = a.decode_step(tok)
+        lb, nb = b.decode_step(tok)
+        d = float((la - lb).abs().max())
+        assert d <= tol, f"step {k}: persistent vs kernels max |delta| {d}"
+    a.check()
+    b.check()
+    ka, va = a.kv_cache()
+    kb, vb = b.kv_cache()
+    T = a.position
+    assert float((ka[:, :, :T] - kb[:, :, :T]).abs().max()) <= 5e-5
+    assert float((va[:, :, :T] - vb[:, :, :T]).abs().max()) <= 5e-5
+    a.close()
+    b.close()
