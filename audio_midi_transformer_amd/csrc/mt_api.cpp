@@ -302,6 +302,8 @@ int mt_create(const mt_config* cfg, const mt_weights* w, int weights_on_device, 
         const size_t xb = persistent_xbuf_bytes(L, d, F, H, B, V);
         if (hipMalloc(&m->xbuf, xb) != hipSuccess || hipMemsetAsync(m->xbuf, 0, xb, st) != hipSuccess)
             return bail(fail(MT_ERR_OOM, "mt_create: exchange buffer of %zu bytes", xb));
+        if (persistent_prepare(m->xbuf, L, d, F, st) != hipSuccess)
+            return bail(fail(MT_ERR_HIP, "mt_create: persistent role table"));
         const char* tr = getenv("MT_TRACE");
         if (tr && tr[0] == '1') {
             const size_t tb = persistent_trace_bytes(L);

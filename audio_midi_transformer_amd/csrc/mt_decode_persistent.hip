@@ -950,22 +950,31 @@ int persistent_max_position() { return pd::ATT_S * pd::MAXPOS; }
 size_t persistent_trace_bytes(int L) { return sizeof(uint64_t) * pd::NWG * (L + 1) * pd::TRACE_SLOTS; }
 
 template <int D, int F>
+static pd::Role* role_table(void* xbuf, int L) {
+    return reinterpret_cast<pd::Role*>(static_cast<uint64_t*>(xbuf) + pd::Cfg<D, F>::LAYER_WORDS * L + 2 * pd::NWG);
+}
+
+template <int D, int F>
+static hipError_t prepare_t(void* xbuf, int L, hipStream_t st) {
+    pd::Role host[pd::NWG];
+    pd::build_roles<D, F>(host);
+    hipError_t e = hipMemcpyAsync(role_table<D, F>(xbuf, L), host, sizeof host, hipMemcpyHostToDevice, st);
+    if (e != hipSuccess) return e;
+    return hipStreamSynchronize(st);
+}
+
+hipError_t persistent_prepare(void* xbuf, int L, int d, int F, hipStream_t st) {
+    if (d == 768 && F == 3072) return prepare_t<768, 3072>(xbuf, L, st);
+    if (d == 1024 && F == 4096) return prepare_t<1024, 4096>(xbuf, L, st);
+    if (d == 1536 && F == 6144) return prepare_t<1536, 6144>(xbuf, L, st);
+    return hipErrorInvalidValue;
+}
+
+template <int D, int F>
 static hipError_t launch_t(const PersistentArgs& p, hipStream_t st) {
     using C = pd::Cfg<D, F>;
-    const size_t lw = C::LAYER_WORDS;
     uint64_t* x = static_cast<uint64_t*>(p.xbuf);
-    pd::Role* roles = reinterpret_cast<pd::Role*>(x + lw * p.L + 2 * pd::NWG);
-    // the role table lives at the end of the exchange buffer; built once per buffer
-    static thread_local const void* built_for = nullptr;
-    if (built_for != p.xbuf) {
-        pd::Role host[pd::NWG];
-        pd::build_roles<D, F>(host);
-        hipError_t e = hipMemcpyAsync(roles, host, sizeof host, hipMemcpyHostToDevice, st);
-        if (e != hipSuccess) return e;
-        e = hipStreamSynchronize(st);
-        if (e != hipSuccess) return e;
-        built_for = p.xbuf;
-    }
+    pd::Role* roles = role_table<D, F>(p.xbuf, p.L);
     pd::Args a{};
     a.L = p.L; a.V = p.V; a.t_cap = p.t_cap; a.eps = p.eps;
     a.tok_emb = p.tok_emb; a.lm_head = p.lm_head; a.ln = p.ln; a.ln_final = p.ln_final;

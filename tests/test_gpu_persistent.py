@@ -117,3 +117,15 @@ def test_persistent_equals_kernel_path_full_depth(width):
     assert float((va[:, :, :T] - vb[:, :, :T]).abs().max()) <= 5e-5
     a.close()
     b.close()
+
+
+def test_second_model_of_same_size(oracle_mod):
+    """A model created after another of the same size has been destroyed (its
+    buffers may land at the same addresses) still runs the persistent step:
+    per-model state is rebuilt at creation, not cached by address."""
+    _dev()
+    shape = synth.ModelShape("small", 2, 768, 12, 3072)
+    w = synth.model_weights(shape, 45)
+    prefix = np.random.default_rng(11).standard_normal((1, 20, 768)).astype(np.float32)
+    for _ in range(3):
+        _teacher_forced(oracle_mod, w, 1, 40, prefix, None, 4, TOL["small"], binding.MT_DECODE_PERSISTENT)

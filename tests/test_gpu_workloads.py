@@ -1,0 +1,116 @@
+"""Full-size workload parity: the HIP path, teacher-forced along the CPU
+oracle's greedy tokens, against the oracle's stored values (written by
+tests/golden/make_goldens.py, which calls only the oracle).
+
+Per workload: prefill, then every stored decode step.  At sampled steps the
+whole logit vector must match (max |delta| <= 1e-4 small/medium, 5e-4 large);
+at every step the logit of the oracle's argmax must match and the argmax must
+agree outside epsilon-ties; K/V rows of the first and last layer match at
+sampled positions.  The 576-slot medium batch run must refuse the call after
+the cache is full and leave the cache unchanged."""
+import os
+
+import numpy as np
+import pytest
+
+from audio_midi_transformer_amd import binding, synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+TOL = {"small": 1e-4, "medium": 1e-4, "large": 5e-4}
+KV_TOL = {"small": 5e-5, "medium": 5e-5, "large": 2e-4}
+
+_weights_cache = {}
+
+
+def _weights(wl):
+    key = (wl.shape.name, wl.model_seed)
+    if key not in _weights_cache:
+        _weights_cache.clear()  # keep one model's FP32 weights at a time
+        w = synth.model_weights(wl.shape, wl.model_seed)
+        _weights_cache[key] = (w, binding.pack_weights(w))
+    return _weights_cache[key]
+
+
+def _fingerprint(w):
+    return np.array([float(np.sum(w.tok_emb, dtype=np.float64)), float(np.sum(w.w_qkv[0], dtype=np.float64)),
+                     float(np.sum(w.w_down[-1], dtype=np.float64)), float(np.sum(w.lm_head, dtype=np.float64))])
+
+
+CASES = [("0", None), ("1", None), ("2", None), ("2", binding.MT_DECODE_KERNELS), ("3", None),
+         ("3c576", None), ("4", None), ("4b8", None)]
+
+
+@pytest.mark.parametrize("key,path", CASES, ids=[f"{k}-{'kernels' if p else 'auto'}" for k, p in CASES])
+def test_workload_teacher_forced(key, path):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    gpath = os.path.join(GOLDEN, f"wl_{key}.npz")
+    if not os.path.exists(gpath):
+        pytest.skip(f"golden {gpath} not generated")
+    g = np.load(gpath)
+    wl = synth.WORKLOADS[key]
+    tol, kvtol = TOL[wl.shape.name], KV_TOL[wl.shape.name]
+    dev = torch.device("cuda", 0)
+    w, packed = _weights(wl)
+    np.testing.assert_allclose(_fingerprint(w), g["weights_check"], rtol=0, atol=0)
+    B, V = wl.batch, wl.shape.vocab
+    dec = binding.Decoder(w, batch=B, t_cap=wl.t_cap, packed=packed)
+    if path is not None:
+        dec.set_decode_path(path)
+    fed = g["tokens"].astype(np.int64)
+    steps = fed.shape[0]
+    n_calls = steps + 1
+    fed_dev = torch.from_numpy(fed).to(dev)
+    logits_all = torch.empty((n_calls, B, V), dtype=torch.float32, device=dev)
+    nxt_all = torch.empty((n_calls, B), dtype=torch.int64, device=dev)
+    prefix = torch.from_numpy(synth.workload_prefix(wl)).to(dev) if wl.prefix_len else None
+    tokens = torch.from_numpy(synth.workload_tokens(wl)).to(dev) if wl.n_tokens else None
+    dec.prefill(tokens, prefix, logits_all[0], nxt_all[0])
+    for k in range(steps):
+        dec.decode_step(fed_dev[k], logits_all[k + 1], nxt_all[k + 1])
+    torch.cuda.synchronize()
+    dec.check()
+    assert dec.position == int(g["position"])
+    lg = logits_all.cpu().numpy()
+    nx = nxt_all.cpu().numpy()
+    assert np.all(np.isfinite(lg))
+    # full vectors at sampled calls
+    for j, k in enumerate(g["sample_idx"]):
+        d = float(np.abs(lg[k].astype(np.float64) - g["sample_logits"][j]).max())
+        assert d <= tol, f"call {k}: max |delta logits| {d:.3g} > {tol}"
+    # every call: logit at the oracle's argmax, and the argmax itself
+    idx = g["top1"]
+    at_top = np.take_along_axis(lg, idx[..., None].astype(np.int64), axis=2)[..., 0]
+    dtop = np.abs(at_top.astype(np.float64) - g["top1v"])
+    assert dtop.max() <= tol, f"logit at the oracle argmax differs by {dtop.max():.3g}"
+    margin = g["top1v"].astype(np.float64) - g["top2v"]
+    decided = margin > 2 * tol
+    mism = decided & (nx != idx)
+    assert not mism.any(), f"argmax differs at (call, seq) {np.argwhere(mism)[:5].tolist()}"
+    ties = np.argwhere(~decided)
+    for k, b in ties:
+        assert lg[k, b, nx[k, b]] >= g["top1v"][k, b] - 2 * tol
+    # cache rows of the first and last layer at sampled positions
+    K, Vc = dec.kv_cache()
+    pos = torch.from_numpy(g["kv_pos"].astype(np.int64)).to(dev)
+    for li, layer in enumerate(g["kv_layers"]):
+        kg = K[int(layer)].index_select(1, pos).cpu().numpy()
+        vg = Vc[int(layer)].index_select(1, pos).cpu().numpy()
+        np.testing.assert_allclose(kg, g["kv_k"][li], rtol=0, atol=kvtol)
+        np.testing.assert_allclose(vg, g["kv_v"][li], rtol=0, atol=kvtol)
+    if key == "3c576":
+        # the cache is full: the next call is refused and changes nothing
+        k_before = K.clone()
+        with pytest.raises(binding.MTError) as e:
+            dec.decode_step(fed_dev[-1], logits_all[0], nxt_all[0])
+        assert e.value.code == binding.MT_ERR_CACHE_FULL
+        K2, _ = dec.kv_cache()
+        assert torch.equal(K2, k_before)
+        assert dec.position == wl.t_cap
+    print(f"workload {key}: {n_calls} calls, {len(ties)} epsilon-ties, "
+          f"max |delta| at oracle argmax {dtop.max():.2e}")
+    dec.close()
