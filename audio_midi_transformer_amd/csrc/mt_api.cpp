@@ -359,7 +359,7 @@ int mt_decode_step(mt_model* m, const int64_t* token, float* logits, int64_t* ne
         pa.L = c.n_layers; pa.d = c.d_model; pa.H = c.n_heads; pa.F = c.d_ff; pa.V = c.vocab;
         pa.B = c.batch; pa.t_cap = c.t_cap; pa.eps = c.ln_eps;
         pa.tok_emb = m->tok_emb; pa.lm_head = m->lm_head; pa.ln = m->ln; pa.ln_final = m->lnf;
-        pa.wq = m->wq_ptrs; pa.ws = m->ws_ptrs; pa.kc = m->kc; pa.vc = m->vc;
+        pa.wq_base = m->wq_all; pa.ws_base = m->ws_all; pa.kc = m->kc; pa.vc = m->vc;
         pa.token = token; pa.logits = logits; pa.next = next; pa.t0 = m->t_past;
         pa.epoch = ++m->epoch;
         pa.resid = m->x; pa.xbuf = m->xbuf; pa.err = m->err; pa.trace = m->trace;

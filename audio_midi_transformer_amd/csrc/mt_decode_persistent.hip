@@ -110,7 +110,13 @@ struct Cfg {
     static constexpr int XB_O = XB_ATT + D;             // o [D]
     static constexpr int XC = XB_O + D;                 // u [F]
     static constexpr int XD = XC + F;                   // f [D]
-    static constexpr int LAYER_WORDS = rup(XD + D, 2);
+    // one "done" word per producer of each broadcast exchange: consumers
+    // poll these (a few hundred words) instead of the whole vector
+    static constexpr int XN_ATT = rup(XD + D, 2);       // [H]   head leaders
+    static constexpr int XN_O = XN_ATT + rup(H, 2);     // [NO_WG]
+    static constexpr int XN_U = XN_O + NO_WG;           // [NWG]
+    static constexpr int XN_F = XN_U + NWG;             // [ND_WG]
+    static constexpr int LAYER_WORDS = rup(XN_F + ND_WG, 2);
     // LDS layout (floats)
     static constexpr int BIG = cmax(2 * MAXPOS * 64, F);  // K|V chunk, or u
     static constexpr int OFF_R = BIG;
@@ -138,8 +144,12 @@ struct Args {
     const float* lm_head;
     const float* ln;
     const float* ln_final;
-    const uint8_t* const* wq;
-    const float* const* ws;
+    // INT4 projections of all layers, laid out layer after layer:
+    // QKV [3D, D], O [D, D], up [F, D], down [D, F] (nibbles / scales)
+    const uint8_t* wq;
+    const float* ws;
+    long wq_layer;  // bytes per layer
+    long ws_layer;  // floats per layer
     float* kc;
     float* vc;
     const int64_t* token;
@@ -175,6 +185,16 @@ __device__ __forceinline__ uint4 gload(const uint4* p) {
 __device__ __forceinline__ float4 gload(const float4* p) {
     const f32x4_t v = *(const __attribute__((address_space(1))) f32x4_t*)(p);
     return make_float4(v.x, v.y, v.z, v.w);
+}
+
+// Workgroup barrier that orders LDS only.  Exchange data goes through
+// agent-scope atomics, so no barrier here needs to wait for global memory;
+// a full __syncthreads() would also wait for every outstanding global load
+// and store (prefetches included) before it.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // ---------------------------------------------------------------- cross-lane sums (DPP)
@@ -226,7 +246,7 @@ template <bool MAX>
 __device__ __forceinline__ float block_reduce(float v, float* red) {
     v = wave_reduce<MAX>(v);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-    __syncthreads();
+    lds_barrier();
     return MAX ? fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])) : (red[0] + red[1]) + (red[2] + red[3]);
 }
 
@@ -263,14 +283,14 @@ struct Range {
 // store their values to LDS (range 0 optionally swizzled).  All first reads
 // are issued together; re-reads of stale words too.
 template <int U, bool SWZ0>
-__device__ bool ll_gather(Range r0, Range r1, Range r2, uint32_t ep, int* err, int* s_flag) {
+__device__ bool ll_gather_single(Range r0, Range r1, Range r2, uint32_t ep, int* err, int* s_flag) {
     const int n01 = r0.n + r1.n, n = n01 + r2.n;
     const uint64_t* src[U];
     uint64_t w[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int i = u * NT + threadIdx.x;
-        src[u] = i < r0.n ? r0.src + i : (i < n01 ? r1.src + (i - r0.n) : r2.src + (i - n01));
+        src[u] = i < r0.n ? r0.src + i : (i < n01 ? r1.src + (i - r0.n) : (i < n ? r2.src + (i - n01) : r0.src));
         w[u] = (i < n) ? ll_get(src[u]) : ((uint64_t)ep << 32);
     }
     bool ok = true;
@@ -301,8 +321,31 @@ __device__ bool ll_gather(Range r0, Range r1, Range r2, uint32_t ep, int* err, i
         atomicOr(err, 2);
         *s_flag = 1;
     }
-    __syncthreads();
+    lds_barrier();
     return *s_flag == 0;
+}
+
+template <int U, bool SWZ0>
+__device__ __forceinline__ bool ll_gather(Range r0, Range r1, Range r2, uint32_t ep, int* err, int* s_flag) {
+    return ll_gather_single<U, SWZ0>(r0, r1, r2, ep, err, s_flag);
+}
+
+// Broadcast exchange: wait until the `nd` producers' done words carry this
+// step's tag (light polling traffic), then read the n data words once
+// (their tags are still checked; stragglers are re-read).
+template <int U, bool SWZ>
+__device__ __forceinline__ bool ll_bcast(const uint64_t* done, int nd, const uint64_t* src, int n, float* dst,
+                                         uint32_t ep, int* err, int* s_flag, float* scratch) {
+    if (!ll_gather_single<1, false>(Range{done, nd, scratch}, Range{done, 0, scratch}, Range{done, 0, scratch}, ep,
+                                    err, s_flag))
+        return false;
+    return ll_gather_single<U, SWZ>(Range{src, n, dst}, Range{src, 0, dst}, Range{src, 0, dst}, ep, err, s_flag);
+}
+
+// Publish this workgroup's done word once every thread has issued its data stores.
+__device__ __forceinline__ void ll_done(uint64_t* done, int idx, uint32_t ep) {
+    lds_barrier();
+    if (threadIdx.x == 0) ll_put(done + idx, 0.f, ep);
 }
 
 template <int U, bool SWZ>
@@ -328,7 +371,7 @@ __device__ __forceinline__ void group_sums(const float* act, int K, float* xs) {
         t = group_reduce<8>(t);
         if (c < G && part == 0) xs[c] = t;
     }
-    __syncthreads();
+    lds_barrier();
 }
 
 // LayerNorm gain and bias held in registers (element k = threadIdx.x + i*NT).
@@ -384,7 +427,7 @@ __device__ __forceinline__ void residual_layernorm(float* r, const float* delta,
         const int k = threadIdx.x + i * NT;
         if (k < D) act[SWZ ? swz(k) : k] = (v[i] - mean) * rstd * p.g[i] + p.b[i];
     }
-    __syncthreads();
+    lds_barrier();
     if (xs) group_sums(act, D, xs);
 }
 
@@ -435,6 +478,18 @@ __device__ __forceinline__ void load_group(const float* act, int c, float (&x)[3
     }
 }
 
+// Unsigned byte n of x converted to float (v_cvt_f32_ubyte<n>): one
+// instruction per weight once the nibbles sit in separate bytes.
+template <int N>
+__device__ __forceinline__ float ubyte(unsigned x) {
+    float r;
+    if constexpr (N == 0) asm("v_cvt_f32_ubyte0 %0, %1" : "=v"(r) : "v"(x));
+    else if constexpr (N == 1) asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(r) : "v"(x));
+    else if constexpr (N == 2) asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(r) : "v"(x));
+    else asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(r) : "v"(x));
+    return r;
+}
+
 // sum_k u_k x_k over one group.  Byte j of the group holds input 2j (low
 // nibble) and 2j+1 (high nibble).
 __device__ __forceinline__ float dot_u(uint4 w, const float (&x)[32]) {
@@ -445,14 +500,14 @@ __device__ __forceinline__ float dot_u(uint4 w, const float (&x)[32]) {
         const unsigned lo = wd[m] & 0x0F0F0F0Fu;
         const unsigned hi = (wd[m] >> 4) & 0x0F0F0F0Fu;
         const float* xm = x + 8 * m;
-        acc = fmaf((float)(lo & 0xFFu), xm[0], acc);
-        acc = fmaf((float)(hi & 0xFFu), xm[1], acc);
-        acc = fmaf((float)((lo >> 8) & 0xFFu), xm[2], acc);
-        acc = fmaf((float)((hi >> 8) & 0xFFu), xm[3], acc);
-        acc = fmaf((float)((lo >> 16) & 0xFFu), xm[4], acc);
-        acc = fmaf((float)((hi >> 16) & 0xFFu), xm[5], acc);
-        acc = fmaf((float)(lo >> 24), xm[6], acc);
-        acc = fmaf((float)(hi >> 24), xm[7], acc);
+        acc = fmaf(ubyte<0>(lo), xm[0], acc);
+        acc = fmaf(ubyte<0>(hi), xm[1], acc);
+        acc = fmaf(ubyte<1>(lo), xm[2], acc);
+        acc = fmaf(ubyte<1>(hi), xm[3], acc);
+        acc = fmaf(ubyte<2>(lo), xm[4], acc);
+        acc = fmaf(ubyte<2>(hi), xm[5], acc);
+        acc = fmaf(ubyte<3>(lo), xm[6], acc);
+        acc = fmaf(ubyte<3>(hi), xm[7], acc);
     }
     return acc;
 }
@@ -513,35 +568,71 @@ __device__ __forceinline__ void kv_chunk_dma(const float* kc_l, const float* vc_
 }
 
 // Softmax partial of q over the npos cached positions in LDS: one lane per
-// position for the scores (rotated 16-byte reads, no cross-lane reduction),
-// then lanes = dimensions for sum_t p_t V_t.  Writes (max, sum, acc[64])
-// to part[0], part[1], part[2 ..].
+// position for the scores (rotated 16-byte reads, four in flight, no
+// cross-lane reduction), then lanes = dimensions for sum_t p_t V_t.  Writes
+// (max, sum, acc[64]) to part[0], part[1], part[2 ..].
 __device__ __forceinline__ void attend_chunk(const float* big, const float* qh, int npos, float* sc,
-                                             float* comb, float* red, float* part) {
+                                             float* comb, float* red, float* part, const Args& a, int l) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     float s = -INFINITY;
     if (tid < npos) {
         const float* kr = big + tid * 64;
-        float acc = 0.f;
+        float acc0 = 0.f, acc1 = 0.f;
 #pragma unroll
-        for (int c = 0; c < 16; ++c) {
-            const int cc = (c + tid) & 15;
-            const float4 k4 = *reinterpret_cast<const float4*>(kr + cc * 4);
-            const float4 q4 = *reinterpret_cast<const float4*>(qh + cc * 4);
-            acc = fmaf(q4.x, k4.x, fmaf(q4.y, k4.y, fmaf(q4.z, k4.z, fmaf(q4.w, k4.w, acc))));
+        for (int c0 = 0; c0 < 16; c0 += 4) {
+            float4 k4[4], q4[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int cc = (c0 + c + tid) & 15;
+                k4[c] = *reinterpret_cast<const float4*>(kr + cc * 4);
+                q4[c] = *reinterpret_cast<const float4*>(qh + cc * 4);
+            }
+#pragma unroll
+            for (int c = 0; c < 4; c += 2) {
+                acc0 = fmaf(q4[c].x, k4[c].x, fmaf(q4[c].y, k4[c].y, fmaf(q4[c].z, k4[c].z, fmaf(q4[c].w, k4[c].w, acc0))));
+                acc1 = fmaf(q4[c + 1].x, k4[c + 1].x,
+                            fmaf(q4[c + 1].y, k4[c + 1].y, fmaf(q4[c + 1].z, k4[c + 1].z, fmaf(q4[c + 1].w, k4[c + 1].w, acc1))));
+            }
         }
-        s = acc * 0.125f;
+        s = (acc0 + acc1) * 0.125f;
     }
+    stamp(a, l, 12);
     const float M = block_reduce<true>(s, red);
     const float pe = (tid < npos) ? expf(s - M) : 0.f;
     if (tid < MAXPOS) sc[tid] = pe;
     const float Ls = block_reduce<false>(pe, red + 4);
-    // sum_t p_t V_t: wave w takes positions w, w + 4, ...; lane = dimension
+    stamp(a, l, 13);
+    // sum_t p_t V_t: lane (wave w, row r, c) takes dims 4c..4c+3 of positions
+    // 4w + r + 16i; the 4 rows of a wave are summed lane-wise, then the 4
+    // waves through LDS.
     const float* vbase = big + MAXPOS * 64;
-    float acc = 0.f;
-    for (int t = wave; t < npos; t += 4) acc = fmaf(sc[t], vbase[t * 64 + lane], acc);
-    comb[wave * 64 + lane] = acc;
-    __syncthreads();
+    const int row = lane >> 4, c4 = lane & 15;
+    float4 a0 = make_float4(0.f, 0.f, 0.f, 0.f), a1 = a0;
+    int t = 4 * wave + row;
+    for (; t + 16 < npos; t += 32) {
+        const float p0 = sc[t], p1 = sc[t + 16];
+        const float4 v0 = *reinterpret_cast<const float4*>(vbase + t * 64 + c4 * 4);
+        const float4 v1 = *reinterpret_cast<const float4*>(vbase + (t + 16) * 64 + c4 * 4);
+        a0.x = fmaf(p0, v0.x, a0.x); a0.y = fmaf(p0, v0.y, a0.y); a0.z = fmaf(p0, v0.z, a0.z); a0.w = fmaf(p0, v0.w, a0.w);
+        a1.x = fmaf(p1, v1.x, a1.x); a1.y = fmaf(p1, v1.y, a1.y); a1.z = fmaf(p1, v1.z, a1.z); a1.w = fmaf(p1, v1.w, a1.w);
+    }
+    for (; t < npos; t += 16) {
+        const float p0 = sc[t];
+        const float4 v0 = *reinterpret_cast<const float4*>(vbase + t * 64 + c4 * 4);
+        a0.x = fmaf(p0, v0.x, a0.x); a0.y = fmaf(p0, v0.y, a0.y); a0.z = fmaf(p0, v0.z, a0.z); a0.w = fmaf(p0, v0.w, a0.w);
+    }
+    float r4[4] = {a0.x + a1.x, a0.y + a1.y, a0.z + a1.z, a0.w + a1.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {  // lane-wise sum of the 4 rows
+        r4[k] += __shfl_xor(r4[k], 16);
+        r4[k] += __shfl_xor(r4[k], 32);
+    }
+    if (row == 0) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) comb[wave * 64 + c4 * 4 + k] = r4[k];
+    }
+    stamp(a, l, 14);
+    lds_barrier();
     if (tid < 64) {
         part[2 + tid] = npos > 0 ? (comb[tid] + comb[64 + tid]) + (comb[128 + tid] + comb[192 + tid]) : 0.f;
         if (tid == 0) {
@@ -549,7 +640,7 @@ __device__ __forceinline__ void attend_chunk(const float* big, const float* qh, 
             part[1] = npos > 0 ? Ls : 0.f;
         }
     }
-    __syncthreads();
+    lds_barrier();
 }
 
 // LM-head rows of this workgroup (wave w: rows w and w + 4 of its six).
@@ -569,253 +660,330 @@ __device__ __forceinline__ void lm_rows_load(float4 (&wrow)[2][D / 256], const f
 
 // ---------------------------------------------------------------- the kernel
 
+// LDS regions of one workgroup.
+template <int D, int F>
+struct Lds {
+    float *big, *r, *act, *xs, *us, *qh, *sc, *own, *gpart, *knew, *vnew, *comb, *delta, *red;
+    int* s_flag;
+    __device__ explicit Lds(float* lds) {
+        using C = Cfg<D, F>;
+        big = lds;
+        r = lds + C::OFF_R;
+        act = lds + C::OFF_ACT;
+        xs = lds + C::OFF_XS;
+        us = lds + C::OFF_US;
+        qh = lds + C::OFF_QH;
+        sc = lds + C::OFF_SC;
+        own = lds + C::OFF_PART;  // own partial [PW]
+        gpart = own + PW;         // splits 1..7 [7][PW]
+        knew = gpart + 7 * PW;    // [64]
+        vnew = knew + 64;         // [64]
+        comb = lds + C::OFF_COMB; // [4][64] scratch
+        delta = lds + C::OFF_DELTA;
+        red = lds + C::OFF_RED;
+        s_flag = reinterpret_cast<int*>(lds + C::OFF_FLAG);
+    }
+};
+
+// Byte / float offsets of the four projections inside one layer.
+template <int D, int F>
+struct Off {
+    static constexpr long QO = 0, OO = 3L * D * D / 2, UO = 4L * D * D / 2, DO = (4L * D * D + (long)F * D) / 2;
+    static constexpr long QS = 0, OS = 3L * D * D / 32, US = 4L * D * D / 32, DS = (4L * D * D + (long)F * D) / 32;
+};
+
+// Phase C (every workgroup): r += o; LN2; FFN-up rows + GELU -> exchange.
+template <int D, int F>
+__device__ __forceinline__ bool phase_c(const Args& a, const Lds<D, F>& S, uint64_t* X,
+                                        const WBlk<Cfg<D, F>::CPL_D, Cfg<D, F>::NP_UP>& wu, const LnRegs<D>& ln2,
+                                        int l) {
+    using C = Cfg<D, F>;
+    const uint32_t ep = a.epoch;
+    if (!ll_bcast<cdiv(D, NT), false>(X + C::XN_O, NO_WG, X + C::XB_O, D, S.delta, ep, a.err, S.s_flag, S.sc))
+        return false;
+    stamp(a, l, 8);
+    residual_layernorm<D, true>(S.r, S.delta, ln2, a.eps, S.act, S.xs, S.red);
+    float o[C::NP_UP];
+    wblk_dot<C::LPR_D, C::CPL_D, C::NP_UP>(wu, S.act, S.xs, o);
+    const int urow = blockIdx.x * C::UP_ROWS;
+#pragma unroll
+    for (int p = 0; p < C::NP_UP; ++p) {
+        const int rr = out_row<C::LPR_D>(p);
+        if (rr >= 0 && rr < C::UP_ROWS && urow + rr < F) ll_put(X + C::XC + urow + rr, gelu_erf(o[p]), ep);
+    }
+    ll_done(X + C::XN_U, blockIdx.x, ep);
+    stamp(a, l, 9);
+    return true;
+}
+
+// Every layer for an attention workgroup (head h, split s).
+template <int D, int F>
+__device__ __forceinline__ bool attention_role(const Args& a, const Lds<D, F>& S, const Role& role,
+                                               float4 (&wrow)[2][D / 256], LnRegs<D>& lnf) {
+    using C = Cfg<D, F>;
+    using O = Off<D, F>;
+    const uint32_t ep = a.epoch;
+    const int tid = threadIdx.x;
+    const bool leader = role.split == 0;
+    const int h = role.head;
+    const int p0 = role.split * a.chunk;
+    const int npos = max(0, min(a.t0, p0 + a.chunk) - p0);
+    const size_t lstride = (size_t)a.t_cap * D;  // one layer of the cache (B = 1)
+    const int urow = blockIdx.x * C::UP_ROWS;
+    WBlk<C::CPL_D, C::NP_Q> wqh;
+    WBlk<C::CPL_D, C::NP_UP> wu;
+    LnRegs<D> ln1, ln2;
+    if (npos > 0) kv_chunk_dma<D>(a.kc, a.vc, h, p0, npos, S.big);
+    wblk_load<C::LPR_D, C::CPL_D, C::NP_Q>(wqh, a.wq + O::QO, a.ws + O::QS, D, h * 64, 64);
+    ln_load<D>(ln1, a.ln, a.ln + D);
+    for (int l = 0; l < a.L; ++l) {
+        uint64_t* X = a.x + (size_t)l * C::LAYER_WORDS;
+        const uint8_t* wq = a.wq + l * a.wq_layer;
+        const float* ws = a.ws + l * a.ws_layer;
+        const float* ln = a.ln + (size_t)l * 4 * D;
+        const float* kc_l = a.kc + (size_t)l * lstride;
+        const float* vc_l = a.vc + (size_t)l * lstride;
+        const bool last = l + 1 == a.L;
+        // ---- A: r += f_prev; LN1; q_h; softmax partial over the chunk
+        stamp(a, l, 0);
+        if (l > 0) {
+            const uint64_t* Xp = a.x + (size_t)(l - 1) * C::LAYER_WORDS;
+            if (!ll_bcast<cdiv(D, NT), false>(Xp + C::XN_F, ND_WG, Xp + C::XD, D, S.delta, ep, a.err, S.s_flag, S.sc))
+                return false;
+        }
+        stamp(a, l, 1);
+        residual_layernorm<D, true>(S.r, l > 0 ? S.delta : nullptr, ln1, a.eps, S.act, S.xs, S.red);
+        stamp(a, l, 2);
+        {
+            float o[C::NP_Q];
+            wblk_dot<C::LPR_D, C::CPL_D, C::NP_Q>(wqh, S.act, S.xs, o);
+#pragma unroll
+            for (int p = 0; p < C::NP_Q; ++p) {
+                const int rr = out_row<C::LPR_D>(p);
+                if (rr >= 0 && rr < 64) S.qh[rr] = o[p];
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0);  // the K/V chunk DMA (and every earlier load) has landed
+        lds_barrier();
+        stamp(a, l, 3);
+        // phase-C weights load behind the attention
+        wblk_load<C::LPR_D, C::CPL_D, C::NP_UP>(wu, wq + O::UO, ws + O::US, D, urow, max(0, min(C::UP_ROWS, F - urow)));
+        ln_load<D>(ln2, ln + 2 * D, ln + 3 * D);
+        attend_chunk(S.big, S.qh, npos, S.sc, S.comb, S.red + 8, S.own, a, l);
+        stamp(a, l, 4);
+        if (!leader) {
+            uint64_t* pw = X + C::XA_PART + (size_t)(h * ATT_S + role.split) * PW;
+            if (tid < PW) ll_put(pw + tid, S.own[tid], ep);
+            // publish first: loads issued before a store can hold it up
+            if (!last && npos > 0) kv_chunk_dma<D>(kc_l + lstride, vc_l + lstride, h, p0, npos, S.big);
+        } else {
+            // ---- A2: merge the 8 splits and the new position -> attn_h
+            if (!ll_gather<cdiv(7 * PW + 128, NT), false>(
+                    Range{X + C::XA_PART + (size_t)(h * ATT_S + 1) * PW, 7 * PW, S.gpart},
+                    Range{X + C::XA_KV + h * 64, 64, S.knew}, Range{X + C::XA_KV + D + h * 64, 64, S.vnew}, ep,
+                    a.err, S.s_flag))
+                return false;
+            stamp(a, l, 5);
+            if (tid < 64) {
+                const float snew = wave_reduce<false>(S.qh[tid] * S.knew[tid]) * 0.125f;
+                float M = fmaxf(snew, S.own[0]);
+                for (int s = 0; s < 7; ++s) M = fmaxf(M, S.gpart[s * PW]);
+                float Ls = expf(snew - M);
+                float A = Ls * S.vnew[tid];
+                if (S.own[0] != -INFINITY) {
+                    const float wgt = expf(S.own[0] - M);
+                    Ls = fmaf(wgt, S.own[1], Ls);
+                    A = fmaf(wgt, S.own[2 + tid], A);
+                }
+                for (int s = 0; s < 7; ++s) {
+                    const float ms = S.gpart[s * PW];
+                    if (ms == -INFINITY) continue;
+                    const float wgt = expf(ms - M);
+                    Ls = fmaf(wgt, S.gpart[s * PW + 1], Ls);
+                    A = fmaf(wgt, S.gpart[s * PW + 2 + tid], A);
+                }
+                ll_put(X + C::XB_ATT + h * 64 + tid, A / Ls, ep);
+            }
+            ll_done(X + C::XN_ATT, h, ep);
+            if (!last && npos > 0) kv_chunk_dma<D>(kc_l + lstride, vc_l + lstride, h, p0, npos, S.big);
+        }
+        // ---- C
+        if (!phase_c<D, F>(a, S, X, wu, ln2, l)) return false;
+        if (!last) {
+            const uint8_t* wqn = wq + a.wq_layer;
+            const float* wsn = ws + a.ws_layer;
+            wblk_load<C::LPR_D, C::CPL_D, C::NP_Q>(wqh, wqn + O::QO, wsn + O::QS, D, h * 64, 64);
+            ln_load<D>(ln1, ln + 4 * D, ln + 5 * D);
+        } else {
+            lm_rows_load<D>(wrow, a.lm_head, a.V);
+            ln_load<D>(lnf, a.ln_final, a.ln_final + D);
+        }
+    }
+    return true;
+}
+
+// Every layer for a workgroup without attention duty: new K/V rows, and
+// (by role) the O projection and FFN-down; FFN-up like everyone.
+template <int D, int F>
+__device__ __forceinline__ bool free_role(const Args& a, const Lds<D, F>& S, const Role& role,
+                                          float4 (&wrow)[2][D / 256], LnRegs<D>& lnf) {
+    using C = Cfg<D, F>;
+    using O = Off<D, F>;
+    const uint32_t ep = a.epoch;
+    const size_t lstride = (size_t)a.t_cap * D;
+    const int urow = blockIdx.x * C::UP_ROWS;
+    const bool o_role = role.o_idx >= 0, d_role = role.d_idx >= 0;
+    const int orow = o_role ? role.o_idx * C::O_ROWS : 0;
+    const int drow = d_role ? role.d_idx * C::DN_ROWS : 0;
+    WBlk<C::CPL_D, C::NP_KV> wkv;
+    WBlk<C::CPL_D, C::NP_O> wo;
+    WBlk<C::CPL_D, C::NP_UP> wu;
+    WBlk<C::CPL_F, C::NP_DN> wd;
+    LnRegs<D> ln1, ln2;
+    if (role.kv_rows > 0)
+        wblk_load<C::LPR_D, C::CPL_D, C::NP_KV>(wkv, a.wq + O::QO, a.ws + O::QS, D, D + role.kv_row0, role.kv_rows);
+    ln_load<D>(ln1, a.ln, a.ln + D);
+    for (int l = 0; l < a.L; ++l) {
+        uint64_t* X = a.x + (size_t)l * C::LAYER_WORDS;
+        const uint8_t* wq = a.wq + l * a.wq_layer;
+        const float* ws = a.ws + l * a.ws_layer;
+        const float* ln = a.ln + (size_t)l * 4 * D;
+        float* kc_l = a.kc + (size_t)l * lstride;
+        float* vc_l = a.vc + (size_t)l * lstride;
+        const bool last = l + 1 == a.L;
+        // ---- A: r += f_prev; LN1; new K/V rows
+        stamp(a, l, 0);
+        if (l > 0) {
+            const uint64_t* Xp = a.x + (size_t)(l - 1) * C::LAYER_WORDS;
+            if (!ll_bcast<cdiv(D, NT), false>(Xp + C::XN_F, ND_WG, Xp + C::XD, D, S.delta, ep, a.err, S.s_flag, S.sc))
+                return false;
+        }
+        stamp(a, l, 1);
+        residual_layernorm<D, true>(S.r, l > 0 ? S.delta : nullptr, ln1, a.eps, S.act, S.xs, S.red);
+        stamp(a, l, 2);
+        if (role.kv_rows > 0) {
+            float o[C::NP_KV];
+            wblk_dot<C::LPR_D, C::CPL_D, C::NP_KV>(wkv, S.act, S.xs, o);
+#pragma unroll
+            for (int p = 0; p < C::NP_KV; ++p) {
+                const int rr = out_row<C::LPR_D>(p);
+                if (rr >= 0 && rr < role.kv_rows) {
+                    const int row = role.kv_row0 + rr;
+                    const size_t slot = (size_t)a.t0 * D;
+                    if (row < D) kc_l[slot + row] = o[p];
+                    else vc_l[slot + row - D] = o[p];
+                    ll_put(X + C::XA_KV + row, o[p], ep);
+                }
+            }
+        }
+        // weights of phases B, C, D
+        if (o_role)
+            wblk_load<C::LPR_D, C::CPL_D, C::NP_O>(wo, wq + O::OO, ws + O::OS, D, orow, min(C::O_ROWS, D - orow));
+        wblk_load<C::LPR_D, C::CPL_D, C::NP_UP>(wu, wq + O::UO, ws + O::US, D, urow, max(0, min(C::UP_ROWS, F - urow)));
+        ln_load<D>(ln2, ln + 2 * D, ln + 3 * D);
+        if (d_role)
+            wblk_load<C::LPR_F, C::CPL_F, C::NP_DN>(wd, wq + O::DO, ws + O::DS, F, drow, min(C::DN_ROWS, D - drow));
+        // ---- B: O rows
+        if (o_role) {
+            if (!ll_bcast<cdiv(D, NT), true>(X + C::XN_ATT, C::H, X + C::XB_ATT, D, S.act, ep, a.err, S.s_flag, S.sc))
+                return false;
+            stamp(a, l, 6);
+            group_sums(S.act, D, S.xs);
+            float o[C::NP_O];
+            wblk_dot<C::LPR_D, C::CPL_D, C::NP_O>(wo, S.act, S.xs, o);
+#pragma unroll
+            for (int p = 0; p < C::NP_O; ++p) {
+                const int rr = out_row<C::LPR_D>(p);
+                if (rr >= 0 && rr < C::O_ROWS && orow + rr < D) ll_put(X + C::XB_O + orow + rr, o[p], ep);
+            }
+            ll_done(X + C::XN_O, role.o_idx, ep);
+            stamp(a, l, 7);
+        }
+        // ---- C
+        if (!phase_c<D, F>(a, S, X, wu, ln2, l)) return false;
+        const uint8_t* wqn = wq + a.wq_layer;
+        const float* wsn = ws + a.ws_layer;
+        if (!d_role) {
+            if (!last) {
+                if (role.kv_rows > 0)
+                    wblk_load<C::LPR_D, C::CPL_D, C::NP_KV>(wkv, wqn + O::QO, wsn + O::QS, D, D + role.kv_row0, role.kv_rows);
+                ln_load<D>(ln1, ln + 4 * D, ln + 5 * D);
+            } else {
+                lm_rows_load<D>(wrow, a.lm_head, a.V);
+                ln_load<D>(lnf, a.ln_final, a.ln_final + D);
+            }
+            continue;
+        }
+        // ---- D: FFN-down rows
+        float* u = S.big;  // swizzled [F]
+        if (!ll_bcast<cdiv(F, NT), true>(X + C::XN_U, NWG, X + C::XC, F, u, ep, a.err, S.s_flag, S.sc)) return false;
+        stamp(a, l, 10);
+        group_sums(u, F, S.us);
+        {
+            float o[C::NP_DN];
+            wblk_dot<C::LPR_F, C::CPL_F, C::NP_DN>(wd, u, S.us, o);
+#pragma unroll
+            for (int p = 0; p < C::NP_DN; ++p) {
+                const int rr = out_row<C::LPR_F>(p);
+                if (rr >= 0 && rr < C::DN_ROWS && drow + rr < D) ll_put(X + C::XD + drow + rr, o[p], ep);
+            }
+        }
+        ll_done(X + C::XN_F, role.d_idx, ep);
+        stamp(a, l, 11);
+        if (!last) {
+            if (role.kv_rows > 0)
+                wblk_load<C::LPR_D, C::CPL_D, C::NP_KV>(wkv, wqn + O::QO, wsn + O::QS, D, D + role.kv_row0, role.kv_rows);
+            ln_load<D>(ln1, ln + 4 * D, ln + 5 * D);
+        } else {
+            lm_rows_load<D>(wrow, a.lm_head, a.V);
+            ln_load<D>(lnf, a.ln_final, a.ln_final + D);
+        }
+    }
+    return true;
+}
+
 template <int D, int F>
 __global__ __launch_bounds__(NT, 1) void k_decode_step(Args a) {
     using C = Cfg<D, F>;
     extern __shared__ float lds[];
-    float* big = lds;
-    float* r = lds + C::OFF_R;
-    float* act = lds + C::OFF_ACT;
-    float* xs = lds + C::OFF_XS;
-    float* us = lds + C::OFF_US;
-    float* qh = lds + C::OFF_QH;
-    float* sc = lds + C::OFF_SC;
-    float* own = lds + C::OFF_PART;  // own partial [PW]
-    float* gpart = own + PW;         // splits 1..7 [7][PW]
-    float* knew = gpart + 7 * PW;    // [64]
-    float* vnew = knew + 64;         // [64]
-    float* comb = lds + C::OFF_COMB; // [4][64] scratch
-    float* delta = lds + C::OFF_DELTA;  // exchanged D-vector (f or o)
-    float* red = lds + C::OFF_RED;
-    int* s_flag = reinterpret_cast<int*>(lds + C::OFF_FLAG);
-
+    const Lds<D, F> S(lds);
     const int wg = blockIdx.x, tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const uint32_t ep = a.epoch;
     const Role role = a.roles[wg];
-    const bool attn = role.head >= 0;
-    const bool leader = attn && role.split == 0;
-    const int p0 = role.split * a.chunk;
-    const int npos = attn ? max(0, min(a.t0, p0 + a.chunk) - p0) : 0;
-    const size_t lstride = (size_t)a.t_cap * D;  // one layer of the cache (B = 1)
-    if (tid == 0) *s_flag = 0;
-
-    // weights of phase A of layer 0
-    WBlk<C::CPL_D, C::NP_Q> wqh;
-    WBlk<C::CPL_D, C::NP_KV> wkv;
-    LnRegs<D> ln1;
-    if (npos > 0) kv_chunk_dma<D>(a.kc, a.vc, role.head, p0, npos, big);
-    if (attn) wblk_load<C::LPR_D, C::CPL_D, C::NP_Q>(wqh, a.wq[0], a.ws[0], D, role.head * 64, 64);
-    else if (role.kv_rows > 0)
-        wblk_load<C::LPR_D, C::CPL_D, C::NP_KV>(wkv, a.wq[0], a.ws[0], D, D + role.kv_row0, role.kv_rows);
-    ln_load<D>(ln1, a.ln, a.ln + D);
+    if (tid == 0) *S.s_flag = 0;
 
     // embedding of the token into the residual copy
     {
         const int64_t tok = gload(a.token);
         const bool bad = tok < 0 || tok >= a.V;
         if (bad && wg == 0 && tid == 0) atomicOr(a.err, 1);
-        for (int k = tid; k < D; k += NT) r[k] = bad ? __builtin_nanf("") : gload(a.tok_emb + (size_t)tok * D + k);
-        __syncthreads();
+        for (int k = tid; k < D; k += NT) S.r[k] = bad ? __builtin_nanf("") : gload(a.tok_emb + (size_t)tok * D + k);
+        lds_barrier();
     }
 
     float4 wrow[2][D / 256];  // LM-head rows, loaded during the last layer
     LnRegs<D> lnf;
-
-    for (int l = 0; l < a.L; ++l) {
-        uint64_t* X = a.x + (size_t)l * C::LAYER_WORDS;
-        const uint8_t* const* wq = a.wq + 4 * l;
-        const float* const* ws = a.ws + 4 * l;
-        const float* ln = a.ln + (size_t)l * 4 * D;
-        float* kc_l = a.kc + (size_t)l * lstride;
-        float* vc_l = a.vc + (size_t)l * lstride;
-        const bool last = l + 1 == a.L;
-
-        // ===================== phase A: r += f_prev; LN1; q / K,V rows; attention partial
-        stamp(a, l, 0);
-        if (l > 0) {
-            if (!ll_gather1<cdiv(D, NT), false>(a.x + (size_t)(l - 1) * C::LAYER_WORDS + C::XD, D, delta, ep,
-                                                a.err, s_flag))
-                return;
-        }
-        stamp(a, l, 1);
-        residual_layernorm<D, true>(r, l > 0 ? delta : nullptr, ln1, a.eps, act, xs, red);
-        stamp(a, l, 2);
-
-        WBlk<C::CPL_D, C::NP_O> wo;
-        WBlk<C::CPL_D, C::NP_UP> wu;
-        WBlk<C::CPL_F, C::NP_DN> wd;
-        LnRegs<D> ln2;
-        const int urow = wg * C::UP_ROWS;
-        if (attn) {
-            float o[C::NP_Q];
-            wblk_dot<C::LPR_D, C::CPL_D, C::NP_Q>(wqh, act, xs, o);
-#pragma unroll
-            for (int p = 0; p < C::NP_Q; ++p) {
-                const int rr = out_row<C::LPR_D>(p);
-                if (rr >= 0 && rr < 64) qh[rr] = o[p];
-            }
-            __builtin_amdgcn_s_waitcnt(0);  // K/V chunk DMA (and earlier loads) complete
-            __syncthreads();
-            stamp(a, l, 3);
-            // phase-C weights load behind the attention
-            wblk_load<C::LPR_D, C::CPL_D, C::NP_UP>(wu, wq[2], ws[2], D, urow, max(0, min(C::UP_ROWS, F - urow)));
-            ln_load<D>(ln2, ln + 2 * D, ln + 3 * D);
-            attend_chunk(big, qh, npos, sc, comb, red + 8, own);
-            stamp(a, l, 4);
-            if (!leader) {
-                if (!last && npos > 0) kv_chunk_dma<D>(kc_l + lstride, vc_l + lstride, role.head, p0, npos, big);
-                uint64_t* pw = X + C::XA_PART + (size_t)(role.head * ATT_S + role.split) * PW;
-                if (tid < PW) ll_put(pw + tid, own[tid], ep);
-            }
-        } else {
-            if (role.kv_rows > 0) {
-                float o[C::NP_KV];
-                wblk_dot<C::LPR_D, C::CPL_D, C::NP_KV>(wkv, act, xs, o);
-#pragma unroll
-                for (int p = 0; p < C::NP_KV; ++p) {
-                    const int rr = out_row<C::LPR_D>(p);
-                    if (rr >= 0 && rr < role.kv_rows) {
-                        const int row = role.kv_row0 + rr;
-                        const size_t slot = (size_t)a.t0 * D;
-                        if (row < D) kc_l[slot + row] = o[p];
-                        else vc_l[slot + row - D] = o[p];
-                        ll_put(X + C::XA_KV + row, o[p], ep);
-                    }
-                }
-            }
-            // weights of phases B, C, D
-            if (role.o_idx >= 0) {
-                const int orow = role.o_idx * C::O_ROWS;
-                wblk_load<C::LPR_D, C::CPL_D, C::NP_O>(wo, wq[1], ws[1], D, orow, min(C::O_ROWS, D - orow));
-            }
-            wblk_load<C::LPR_D, C::CPL_D, C::NP_UP>(wu, wq[2], ws[2], D, urow, max(0, min(C::UP_ROWS, F - urow)));
-            ln_load<D>(ln2, ln + 2 * D, ln + 3 * D);
-            if (role.d_idx >= 0) {
-                const int drow = role.d_idx * C::DN_ROWS;
-                wblk_load<C::LPR_F, C::CPL_F, C::NP_DN>(wd, wq[3], ws[3], F, drow, min(C::DN_ROWS, D - drow));
-            }
-        }
-
-        // ===================== phase A2: head leader merges the splits and the new position
-        if (leader) {
-            const int h = role.head;
-            if (!ll_gather<cdiv(7 * PW + 128, NT), false>(
-                    Range{X + C::XA_PART + (size_t)(h * ATT_S + 1) * PW, 7 * PW, gpart},
-                    Range{X + C::XA_KV + h * 64, 64, knew}, Range{X + C::XA_KV + D + h * 64, 64, vnew}, ep, a.err,
-                    s_flag))
-                return;
-            stamp(a, l, 5);
-            if (!last && npos > 0) kv_chunk_dma<D>(kc_l + lstride, vc_l + lstride, h, p0, npos, big);
-            if (tid < 64) {
-                const float snew = wave_reduce<false>(qh[tid] * knew[tid]) * 0.125f;
-                float M = fmaxf(snew, own[0]);
-                for (int s = 0; s < 7; ++s) M = fmaxf(M, gpart[s * PW]);
-                float Ls = expf(snew - M);
-                float A = Ls * vnew[tid];
-                if (own[0] != -INFINITY) {
-                    const float wgt = expf(own[0] - M);
-                    Ls = fmaf(wgt, own[1], Ls);
-                    A = fmaf(wgt, own[2 + tid], A);
-                }
-                for (int s = 0; s < 7; ++s) {
-                    const float ms = gpart[s * PW];
-                    if (ms == -INFINITY) continue;
-                    const float wgt = expf(ms - M);
-                    Ls = fmaf(wgt, gpart[s * PW + 1], Ls);
-                    A = fmaf(wgt, gpart[s * PW + 2 + tid], A);
-                }
-                ll_put(X + C::XB_ATT + h * 64 + tid, A / Ls, ep);
-            }
-        }
-
-        // ===================== phase B: O rows
-        if (role.o_idx >= 0) {
-            if (!ll_gather1<cdiv(D, NT), true>(X + C::XB_ATT, D, act, ep, a.err, s_flag)) return;
-            stamp(a, l, 6);
-            group_sums(act, D, xs);
-            float o[C::NP_O];
-            wblk_dot<C::LPR_D, C::CPL_D, C::NP_O>(wo, act, xs, o);
-            const int row0 = role.o_idx * C::O_ROWS;
-#pragma unroll
-            for (int p = 0; p < C::NP_O; ++p) {
-                const int rr = out_row<C::LPR_D>(p);
-                if (rr >= 0 && rr < C::O_ROWS && row0 + rr < D) ll_put(X + C::XB_O + row0 + rr, o[p], ep);
-            }
-            stamp(a, l, 7);
-        }
-
-        // ===================== phase C: r += o; LN2; FFN-up rows + GELU
-        if (!ll_gather1<cdiv(D, NT), false>(X + C::XB_O, D, delta, ep, a.err, s_flag)) return;
-        stamp(a, l, 8);
-        residual_layernorm<D, true>(r, delta, ln2, a.eps, act, xs, red);
-        {
-            float o[C::NP_UP];
-            wblk_dot<C::LPR_D, C::CPL_D, C::NP_UP>(wu, act, xs, o);
-#pragma unroll
-            for (int p = 0; p < C::NP_UP; ++p) {
-                const int rr = out_row<C::LPR_D>(p);
-                if (rr >= 0 && rr < C::UP_ROWS && urow + rr < F) ll_put(X + C::XC + urow + rr, gelu_erf(o[p]), ep);
-            }
-        }
-        stamp(a, l, 9);
-        // next layer's phase-A weights (workgroups without FFN-down load them now)
-        const uint8_t* const* wqn = wq + 4;
-        const float* const* wsn = ws + 4;
-        if (role.d_idx < 0) {
-            if (!last) {
-                if (attn) wblk_load<C::LPR_D, C::CPL_D, C::NP_Q>(wqh, wqn[0], wsn[0], D, role.head * 64, 64);
-                else if (role.kv_rows > 0)
-                    wblk_load<C::LPR_D, C::CPL_D, C::NP_KV>(wkv, wqn[0], wsn[0], D, D + role.kv_row0, role.kv_rows);
-                ln_load<D>(ln1, ln + 4 * D, ln + 5 * D);
-            } else {
-                lm_rows_load<D>(wrow, a.lm_head, a.V);
-                ln_load<D>(lnf, a.ln_final, a.ln_final + D);
-            }
-        }
-
-        // ===================== phase D: FFN-down rows
-        if (role.d_idx >= 0) {
-            float* u = big;  // swizzled [F]
-            if (!ll_gather1<cdiv(F, NT), true>(X + C::XC, F, u, ep, a.err, s_flag)) return;
-            stamp(a, l, 10);
-            if (!last) {
-                if (role.kv_rows > 0)
-                    wblk_load<C::LPR_D, C::CPL_D, C::NP_KV>(wkv, wqn[0], wsn[0], D, D + role.kv_row0, role.kv_rows);
-                ln_load<D>(ln1, ln + 4 * D, ln + 5 * D);
-            } else {
-                lm_rows_load<D>(wrow, a.lm_head, a.V);
-                ln_load<D>(lnf, a.ln_final, a.ln_final + D);
-            }
-            group_sums(u, F, us);
-            float o[C::NP_DN];
-            wblk_dot<C::LPR_F, C::CPL_F, C::NP_DN>(wd, u, us, o);
-            const int row0 = role.d_idx * C::DN_ROWS;
-#pragma unroll
-            for (int p = 0; p < C::NP_DN; ++p) {
-                const int rr = out_row<C::LPR_F>(p);
-                if (rr >= 0 && rr < C::DN_ROWS && row0 + rr < D) ll_put(X + C::XD + row0 + rr, o[p], ep);
-            }
-            stamp(a, l, 11);
-        }
-    }
+    const bool ok = role.head >= 0 ? attention_role<D, F>(a, S, role, wrow, lnf)
+                                   : free_role<D, F>(a, S, role, wrow, lnf);
+    if (!ok) return;
 
     // ===================== phase E: r += f; z = LN_f(r); LM-head rows + local argmax
     uint64_t* XE = a.x + (size_t)a.L * C::LAYER_WORDS;
     {
         stamp(a, a.L, 0);
-        if (!ll_gather1<cdiv(D, NT), false>(a.x + (size_t)(a.L - 1) * C::LAYER_WORDS + C::XD, D, delta, ep, a.err,
-                                            s_flag))
+        const uint64_t* Xp = a.x + (size_t)(a.L - 1) * C::LAYER_WORDS;
+        if (!ll_bcast<cdiv(D, NT), false>(Xp + C::XN_F, ND_WG, Xp + C::XD, D, S.delta, ep, a.err, S.s_flag, S.sc))
             return;
         stamp(a, a.L, 1);
-        residual_layernorm<D, false>(r, delta, lnf, a.eps, act, nullptr, red);
-        float* cand_v = comb;                                 // [8]
-        int* cand_i = reinterpret_cast<int*>(comb + 8);       // [8]
+        residual_layernorm<D, false>(S.r, S.delta, lnf, a.eps, S.act, nullptr, S.red);
+        float* cand_v = S.comb;                              // [8]
+        int* cand_i = reinterpret_cast<int*>(S.comb + 8);    // [8]
         if (tid < 8) {
             cand_v[tid] = -INFINITY;
             cand_i[tid] = 0x7fffffff;
         }
-        __syncthreads();
+        lds_barrier();
         const int v0 = wg * LM_ROWS;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
@@ -823,7 +991,7 @@ __global__ __launch_bounds__(NT, 1) void k_decode_step(Args a) {
             float acc = 0.f;
 #pragma unroll
             for (int c = 0; c < D / 256; ++c) {
-                const float4 z = reinterpret_cast<const float4*>(act)[lane + 64 * c];
+                const float4 z = reinterpret_cast<const float4*>(S.act)[lane + 64 * c];
                 acc = fmaf(wrow[i][c].x, z.x, fmaf(wrow[i][c].y, z.y, fmaf(wrow[i][c].z, z.z, fmaf(wrow[i][c].w, z.w, acc))));
             }
             acc = wave_reduce<false>(acc);
@@ -833,7 +1001,7 @@ __global__ __launch_bounds__(NT, 1) void k_decode_step(Args a) {
                 cand_i[wave + 4 * i] = v;
             }
         }
-        __syncthreads();
+        lds_barrier();
         if (tid == 0) {
             float bv = -INFINITY;
             int bi = 0x7fffffff;
@@ -852,8 +1020,8 @@ __global__ __launch_bounds__(NT, 1) void k_decode_step(Args a) {
 
     // ===================== phase F: global argmax (workgroup 0)
     if (wg == 0) {
-        float* cv = big;
-        if (!ll_gather1<cdiv(2 * NWG, NT), false>(XE, 2 * NWG, cv, ep, a.err, s_flag)) return;
+        float* cv = S.big;
+        if (!ll_gather1<cdiv(2 * NWG, NT), false>(XE, 2 * NWG, cv, ep, a.err, S.s_flag)) return;
         if (tid < 64) {
             float bv = -INFINITY;
             int bi = 0x7fffffff;
@@ -978,7 +1146,10 @@ static hipError_t launch_t(const PersistentArgs& p, hipStream_t st) {
     pd::Args a{};
     a.L = p.L; a.V = p.V; a.t_cap = p.t_cap; a.eps = p.eps;
     a.tok_emb = p.tok_emb; a.lm_head = p.lm_head; a.ln = p.ln; a.ln_final = p.ln_final;
-    a.wq = p.wq; a.ws = p.ws; a.kc = p.kc; a.vc = p.vc; a.token = p.token; a.logits = p.logits;
+    a.wq = p.wq_base; a.ws = p.ws_base;
+    a.wq_layer = (3L * D * D + (long)D * D + 2L * F * D) / 2;
+    a.ws_layer = (3L * D * D + (long)D * D + 2L * F * D) / 32;
+    a.kc = p.kc; a.vc = p.vc; a.token = p.token; a.logits = p.logits;
     a.next = p.next; a.t0 = p.t0; a.epoch = p.epoch; a.x = x; a.roles = roles; a.err = p.err;
     a.trace = static_cast<uint64_t*>(p.trace);
     const int chunk = (p.t0 + pd::ATT_S - 1) / pd::ATT_S;

@@ -61,8 +61,8 @@ struct PersistentArgs {
     const float* lm_head;
     const float* ln;        // [L, 4, d]
     const float* ln_final;  // [2, d]
-    const uint8_t* const* wq;  // device array [L*4] of pointers
-    const float* const* ws;    // device array [L*4]
+    const uint8_t* wq_base;    // INT4 nibbles of all layers, layer after layer
+    const float* ws_base;      // group scales, same order
     float* kc;
     float* vc;
     // step
