@@ -103,6 +103,53 @@ def cpu_baseline(wl, weights, prefix_np, tokens_np, max_steps: int = 8):
     }
 
 
+KERNEL_SYMBOLS = {"mt_decode_step_persistent": "k_decode_step<"}
+
+
+def reduce_counters(fetch_csv: str, write_csv: str, workload_key: str, calib_mib: int,
+                    commands: list) -> dict:
+    """HBM bytes per launch of the persistent decode step from two rocprofv3
+    `--pmc FETCH_SIZE` / `--pmc WRITE_SIZE` counter files of one bench pass
+    (steps 1, warmup 0, with the calibration copy).  Each counter is scaled by
+    the bytes a plain device copy of `calib_mib` MiB really moves over what
+    that counter read for it (the largest copy dispatched before the
+    library's first kernel), then
+    averaged over the launches the bench's steady window covers."""
+    import csv
+
+    def load(path, counter):
+        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        first_mt = min(int(r["Dispatch_Id"]) for r in rows if "mt::" in r["Kernel_Name"])
+        # the calibration copy runs before any of the library's kernels
+        copies = [float(r["Counter_Value"]) for r in rows
+                  if "copyBuffer" in r["Kernel_Name"] and int(r["Dispatch_Id"]) < first_mt]
+        kern = [float(r["Counter_Value"]) for r in rows
+                if KERNEL_SYMBOLS["mt_decode_step_persistent"] in r["Kernel_Name"]]
+        return max(copies), kern
+
+    known_kib = float(calib_mib) * 1024.0
+    f_copy, f_kern = load(fetch_csv, "FETCH_SIZE")
+    w_copy, w_kern = load(write_csv, "WRITE_SIZE")
+    f_scale, w_scale = known_kib / f_copy, known_kib / w_copy
+    f_kern, w_kern = f_kern[STEADY_FROM:], w_kern[STEADY_FROM:]
+    fetch = float(np.mean(f_kern)) * 1024.0 * f_scale
+    write = float(np.mean(w_kern)) * 1024.0 * w_scale
+    return {
+        "kernel": "mt_decode_step_persistent",
+        "workload": workload_key,
+        "source_hash": kernel_source_hash(),
+        "launches": len(f_kern),
+        "calibration_copy_bytes": int(known_kib * 1024),
+        "fetch_scale": round(f_scale, 4),
+        "write_scale": round(w_scale, 4),
+        "fetch_bytes_per_launch": round(fetch, 1),
+        "write_bytes_per_launch": round(write, 1),
+        "bytes_per_launch": round(fetch + write, 1),
+        "commands": commands,
+    }
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -113,7 +160,20 @@ def main() -> int:
     ap.add_argument("--decode-steps", type=int, default=None,
                     help="override the number of decode steps per pass (default: the workload's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibration-copy-mib", type=int, default=0,
+                    help="before the bench, copy a buffer of this many MiB device-to-device three "
+                         "times (a plain copy of known size, to scale HBM byte counters)")
+    ap.add_argument("--reduce-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="reduce two rocprofv3 counter files of a --calibration-copy-mib run to the "
+                         "per-launch HBM traffic record (printed as JSON) and exit")
     args = ap.parse_args()
+    if args.reduce_counters:
+        cmds = [f"rocprofv3 --pmc {c} -f csv -d <dir> -o pmc -- python3 bench.py --workload {args.workload} "
+                f"--steps 1 --warmup 0 --no-cpu-baseline --calibration-copy-mib {args.calibration_copy_mib}"
+                for c in ("FETCH_SIZE", "WRITE_SIZE")]
+        print(json.dumps(reduce_counters(*args.reduce_counters, args.workload, args.calibration_copy_mib, cmds),
+                         indent=1))
+        return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the decoder step's natural shard is independent "
@@ -134,6 +194,15 @@ def main() -> int:
     R0 = wl.prefix_len + wl.n_tokens
     assert R0 + n_dec <= wl.t_cap
 
+    if args.calibration_copy_mib:
+        n = args.calibration_copy_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] calibration copy: 3 x {n} bytes read and written", file=sys.stderr, flush=True)
+        del src, dst
     print(f"[bench] workload {wl.key}: {wl.name}; generating weights", file=sys.stderr, flush=True)
     weights = synth.model_weights(shape, wl.model_seed)
     prefix_np = synth.workload_prefix(wl) if wl.prefix_len else None
@@ -174,8 +243,11 @@ def main() -> int:
     dec.check()
     print("[bench] warmup done", file=sys.stderr, flush=True)
 
+    # timed passes; events around every decode call (one launch each on the
+    # persistent path) give the per-launch durations for the roofline
     mk = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
-    evs = [dict(p0=mk(), p1=mk(), s0=mk(), s1=mk()) for _ in range(args.steps)]
+    evs = [dict(p0=mk(), p1=mk(), s0=mk(), s1=mk(), per=[(mk(), mk()) for _ in range(n_dec)])
+           for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
@@ -187,20 +259,19 @@ def main() -> int:
     steady_ms = float(np.mean([e["s0"].elapsed_time(e["s1"]) for e in evs]))
     n_steady = n_dec - STEADY_FROM
     ms_tok = steady_ms / n_steady
-    steady_bytes = sum(step_bytes(shape, B, R0 + k + 1) for k in range(STEADY_FROM, n_dec))
-    gbps = steady_bytes / (steady_ms * 1e-3) / 1e9
-
-    # per-launch pass: events around every decode call (one launch each on the
-    # persistent path) for the distribution and the roofline
-    per = dict(p0=mk(), p1=mk(), s0=mk(), s1=mk(), per=[(mk(), mk()) for _ in range(n_dec)])
-    one_pass(per)
-    torch.cuda.synchronize()
-    step_ms = np.array([a.elapsed_time(b) for a, b in per["per"]])[STEADY_FROM:]
     launch_bytes = np.array([step_bytes(shape, B, R0 + k + 1) for k in range(STEADY_FROM, n_dec)])
+    gbps = float(launch_bytes.sum()) / (steady_ms * 1e-3) / 1e9
+    step_ms = np.concatenate([np.array([a.elapsed_time(b) for a, b in e["per"]])[STEADY_FROM:] for e in evs])
     kernel_name = "mt_decode_step_persistent" if persistent else "decode_step_kernels"
-    achieved = float(launch_bytes.sum() / (step_ms.sum() * 1e-3) / 1e9)
+    achieved = float(launch_bytes.sum() * args.steps / (step_ms.sum() * 1e-3) / 1e9)
     traffic = traffic_from_profiles(kernel_name, wl.key)
     pf_flops = prefill_flops(shape, B, R0)
+
+    # point values at T = 505, 1024 and 2048 keys (where the pass reaches them)
+    t_keys = np.concatenate([np.arange(STEADY_FROM, n_dec) + R0 + 1] * args.steps)
+    points = {str(T): round(float(step_ms[t_keys == T].mean()), 5)
+              for T in (505, 1024, 2048) if np.any(t_keys == T)}
+    copy_gbps = measure_copy_peak(torch)
 
     out = {
         "metric": METRIC,
@@ -227,12 +298,16 @@ def main() -> int:
                                 "p90": round(float(np.percentile(step_ms, 90)), 5)},
         "achieved_GBps": round(gbps, 1),
         "hbm_frac_of_8TBps": round(gbps / HBM_PEAK_GBPS, 4),
+        "decode_ms_at_T": points,
+        "hbm_frac_of_measured_copy": round(gbps / copy_gbps, 4),
+        "measured_copy_GBps": round(copy_gbps, 1),
         "prefill_ms": round(prefill_ms, 3),
         "prefill_fp32_mfma_frac": round(pf_flops / (prefill_ms * 1e-3) / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4),
         "roofline": {"kernel": kernel_name, "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic,
-                     "algorithmic_bytes_per_launch": round(float(launch_bytes.mean()), 1)},
+                     "algorithmic_bytes_per_launch": round(float(launch_bytes.mean()), 1),
+                     "avg_launch_us": round(float(step_ms.mean()) * 1000.0, 2)},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
@@ -241,6 +316,26 @@ def main() -> int:
     dec.close()
     print(json.dumps(out), flush=True)
     return 0
+
+
+def measure_copy_peak(torch, gib: int = 4, reps: int = 5) -> float:
+    """Device-to-device copy of a buffer larger than the last-level cache:
+    (read + written bytes) / time, best of `reps`."""
+    n = gib << 30
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    best = float("inf")
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        b.synchronize()
+        best = min(best, a.elapsed_time(b))
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2.0 * n / (best * 1e-3) / 1e9
 
 
 def dec_is_persistent(dec) -> bool:
