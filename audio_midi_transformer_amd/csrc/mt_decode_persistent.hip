@@ -16,11 +16,14 @@
 // step.  Data moves between workgroups through exchange words of 64 bits,
 // {float value, 32-bit step tag}, each written by one atomic 8-byte store;
 // a consumer issues all its reads at once and re-reads only the words whose
-// tag is not yet this step's.  No barrier counters, no cache flushes.  Every
-// workgroup keeps its own copy of the residual stream in LDS and recomputes
-// LayerNorm locally.  Weights for a phase are loaded into registers one
-// phase ahead; each attention workgroup DMAs its K/V chunk of the next layer
-// into LDS as soon as the current chunk is consumed.
+// tag is not yet this step's.  No barrier counters, no cache flushes.  A
+// vector that every workgroup reads is written once per XCD and each XCD's
+// workgroups poll their own copy, which keeps the number of pollers per
+// cache line low.  Every workgroup keeps its own copy of the residual
+// stream in LDS and recomputes LayerNorm locally.  Weights for a phase are
+// loaded into registers one phase ahead; each attention workgroup DMAs its
+// K/V chunk of the next layer into LDS as soon as the current chunk is
+// consumed.
 //
 // Roles (a table built on the host, see build_roles):
 //   attention WGs  (head h, split s), 8 splits per head, all on one XCD.
@@ -29,9 +32,9 @@
 //                  (max, sum, acc[64]); split 0 (the head leader) merges them
 //                  with the new position and publishes attn_h.
 //   free WGs       the rest: the new K/V rows of the fused projection (to the
-//                  cache slot T_past and to the exchange), 64 of them the O
-//                  projection, 64 of them FFN-down.
-//   all WGs        FFN-up rows + GELU.
+//                  cache slot T_past and to the exchange).
+//   all WGs        D/256 rows of O, F/256 rows of FFN-up + GELU and D/256
+//                  rows of FFN-down.
 // Per layer: A (attention partials / K,V rows) -> A2 (head merge) -> B (O)
 // -> C (LN2 + up) -> D (down) -> next layer's A; after the last layer E
 // (LN_f + LM-head rows + local argmax) and F (workgroup 0: global argmax,
@@ -52,8 +55,7 @@ constexpr int NT = 256;      // threads per workgroup
 constexpr int NWG = 256;     // workgroups (one per CU)
 constexpr int NXCD = 8;      // workgroup w runs on XCD w % 8
 constexpr int ATT_S = 8;     // attention splits per head
-constexpr int NO_WG = 64;    // workgroups computing the O projection
-constexpr int ND_WG = 64;    // workgroups computing FFN-down
+constexpr int REP = NXCD;    // copies of each broadcast vector, one per XCD
 constexpr int PW = 66;       // words per attention partial: m, l, acc[64]
 constexpr int MAXPOS = 256;  // cached positions per attention workgroup (LDS)
 constexpr int LM_ROWS = 6;   // vocabulary rows per workgroup
@@ -79,11 +81,8 @@ constexpr int res_lane(int lpr) { return lpr == 64 ? 48 : (lpr == 32 ? 16 : 0); 
 struct Role {
     int head;     // attention head, -1 if none
     int split;    // attention split (0 = head leader)
-    int o_idx;    // O-projection block, -1 if none
-    int d_idx;    // FFN-down block, -1 if none
     int kv_row0;  // first row of the 2D K|V rows of the fused projection
     int kv_rows;  // number of K|V rows, 0 if none
-    int pad0, pad1;
 };
 
 template <int D, int F>
@@ -96,44 +95,43 @@ struct Cfg {
     static constexpr int NFREE = NWG - NATT;
     static constexpr int KV_ROWS = cdiv(2 * D, NFREE);
     static constexpr int UP_ROWS = cdiv(F, NWG);
-    static constexpr int O_ROWS = cdiv(D, NO_WG);
-    static constexpr int DN_ROWS = cdiv(D, ND_WG);
+    static constexpr int O_ROWS = cdiv(D, NWG);
+    static constexpr int DN_ROWS = cdiv(D, NWG);
     static constexpr int NP_Q = cdiv(64, RP_D);
     static constexpr int NP_KV = cdiv(KV_ROWS, RP_D);
     static constexpr int NP_O = cdiv(O_ROWS, RP_D);
     static constexpr int NP_UP = cdiv(UP_ROWS, RP_D);
     static constexpr int NP_DN = cdiv(DN_ROWS, RP_F);
-    // exchange layout per layer (64-bit words)
+    // exchange layout per layer (64-bit words).  Vectors every workgroup
+    // reads are written REP times; the workgroups of XCD x read copy x, so
+    // no line is polled by more than 32 workgroups.
     static constexpr int XA_KV = 0;                     // new K|V row [2D]
     static constexpr int XA_PART = XA_KV + 2 * D;       // partials [H][ATT_S][PW]
-    static constexpr int XB_ATT = XA_PART + NATT * PW;  // merged attention [D]
-    static constexpr int XB_O = XB_ATT + D;             // o [D]
-    static constexpr int XC = XB_O + D;                 // u [F]
-    static constexpr int XD = XC + F;                   // f [D]
-    // one "done" word per producer of each broadcast exchange: consumers
-    // poll these (a few hundred words) instead of the whole vector
-    static constexpr int XN_ATT = rup(XD + D, 2);       // [H]   head leaders
-    static constexpr int XN_O = XN_ATT + rup(H, 2);     // [NO_WG]
-    static constexpr int XN_U = XN_O + NO_WG;           // [NWG]
-    static constexpr int XN_F = XN_U + NWG;             // [ND_WG]
-    static constexpr int LAYER_WORDS = rup(XN_F + ND_WG, 2);
-    // LDS layout (floats)
-    static constexpr int BIG = cmax(2 * MAXPOS * 64, F);  // K|V chunk, or u
-    static constexpr int OFF_R = BIG;
-    static constexpr int OFF_ACT = OFF_R + D;
-    static constexpr int OFF_XS = OFF_ACT + D;
-    static constexpr int OFF_US = OFF_XS + GD;
-    static constexpr int OFF_QH = OFF_US + GF;
-    static constexpr int OFF_SC = OFF_QH + 64;            // scores [MAXPOS]
-    static constexpr int OFF_PART = OFF_SC + MAXPOS;      // own partial [PW] + gathered [7][PW] + kv_new [128]
-    static constexpr int OFF_COMB = rup(OFF_PART + 8 * PW + 128, 4);
-    static constexpr int OFF_DELTA = OFF_COMB + 4 * 64;   // exchanged D-vector (f or o)
-    static constexpr int OFF_RED = OFF_DELTA + D;
+    static constexpr int XB_ATT = XA_PART + NATT * PW;  // merged attention [REP][D]
+    static constexpr int XB_O = XB_ATT + REP * D;       // o [REP][D]
+    static constexpr int XC = XB_O + REP * D;           // u [REP][F]
+    static constexpr int XD = XC + REP * F;             // f [REP][D]
+    static constexpr int LAYER_WORDS = rup(XD + REP * D, 2);
+    // LDS layout (floats).  The K|V chunk of an attention split stays
+    // resident across phases B..D (it is the next layer's chunk by then), so
+    // u of phase D shares one region with the vectors of phases A..C.
+    static constexpr int BIG = 2 * MAXPOS * 64;           // K|V chunk
+    static constexpr int OFF_R = BIG;                     // residual [D]
+    static constexpr int OFF_XS = OFF_R + D;              // group sums of act [GD]
+    static constexpr int OFF_US = OFF_XS + GD;            // group sums of u [GF]
+    static constexpr int OFF_U = rup(OFF_US + GF, 4);     // u [F] (phase D) or:
+    static constexpr int OFF_ACT = OFF_U;                 //   act [D]
+    static constexpr int OFF_DELTA = OFF_ACT + D;         //   exchanged D-vector (f or o) [D]
+    static constexpr int OFF_QH = OFF_DELTA + D;          //   q_h [64]
+    static constexpr int OFF_SC = OFF_QH + 64;            //   scores [MAXPOS]
+    static constexpr int OFF_PART = OFF_SC + MAXPOS;      //   own partial [PW] + gathered [7][PW] + kv_new [128]
+    static constexpr int OFF_COMB = rup(OFF_PART + 8 * PW + 128, 4);  // [4][64] scratch
+    static constexpr int OFF_RED = rup(cmax(OFF_U + F, OFF_COMB + 4 * 64), 4);
     static constexpr int OFF_FLAG = OFF_RED + 16;
     static constexpr int LDS_FLOATS = OFF_FLAG + 16;
     static_assert(D % 64 == 0 && F % 32 == 0, "widths");
     static_assert(LPR_D > 0 && LPR_F > 0, "width has no GEMV lane mapping");
-    static_assert(NFREE >= 64, "need at least 64 workgroups without attention duty");
+    static_assert(NFREE > 0 && KV_ROWS * NFREE >= 2 * D, "K/V rows need workgroups without attention duty");
     static_assert(LDS_FLOATS * 4 <= 160 * 1024, "LDS budget");
 };
 
@@ -285,13 +283,14 @@ struct Range {
 template <int U, bool SWZ0>
 __device__ bool ll_gather_single(Range r0, Range r1, Range r2, uint32_t ep, int* err, int* s_flag) {
     const int n01 = r0.n + r1.n, n = n01 + r2.n;
-    const uint64_t* src[U];
+    auto src = [&](int i) -> const uint64_t* {
+        return i < r0.n ? r0.src + i : (i < n01 ? r1.src + (i - r0.n) : r2.src + (i - n01));
+    };
     uint64_t w[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int i = u * NT + threadIdx.x;
-        src[u] = i < r0.n ? r0.src + i : (i < n01 ? r1.src + (i - r0.n) : (i < n ? r2.src + (i - n01) : r0.src));
-        w[u] = (i < n) ? ll_get(src[u]) : ((uint64_t)ep << 32);
+        w[u] = (i < n) ? ll_get(src(i)) : ((uint64_t)ep << 32);
     }
     bool ok = true;
     for (uint32_t it = 0;; ++it) {
@@ -306,8 +305,10 @@ __device__ bool ll_gather_single(Range r0, Range r1, Range r2, uint32_t ep, int*
         __builtin_amdgcn_s_sleep(1);
 #pragma unroll
         for (int u = 0; u < U; ++u)
-            if ((uint32_t)(w[u] >> 32) != ep) w[u] = ll_get(src[u]);
+            if ((uint32_t)(w[u] >> 32) != ep) w[u] = ll_get(src(u * NT + threadIdx.x));
     }
+    // the destination may still be read by other waves of the previous phase
+    lds_barrier();
     if (ok) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -330,22 +331,15 @@ __device__ __forceinline__ bool ll_gather(Range r0, Range r1, Range r2, uint32_t
     return ll_gather_single<U, SWZ0>(r0, r1, r2, ep, err, s_flag);
 }
 
-// Broadcast exchange: wait until the `nd` producers' done words carry this
-// step's tag (light polling traffic), then read the n data words once
-// (their tags are still checked; stragglers are re-read).
-template <int U, bool SWZ>
-__device__ __forceinline__ bool ll_bcast(const uint64_t* done, int nd, const uint64_t* src, int n, float* dst,
-                                         uint32_t ep, int* err, int* s_flag, float* scratch) {
-    if (!ll_gather_single<1, false>(Range{done, nd, scratch}, Range{done, 0, scratch}, Range{done, 0, scratch}, ep,
-                                    err, s_flag))
-        return false;
-    return ll_gather_single<U, SWZ>(Range{src, n, dst}, Range{src, 0, dst}, Range{src, 0, dst}, ep, err, s_flag);
+// Word i of all REP copies of a broadcast vector of n words.
+__device__ __forceinline__ void ll_put_rep(uint64_t* base, int n, int i, float v, uint32_t ep) {
+#pragma unroll
+    for (int r = 0; r < REP; ++r) ll_put(base + (size_t)r * n + i, v, ep);
 }
 
-// Publish this workgroup's done word once every thread has issued its data stores.
-__device__ __forceinline__ void ll_done(uint64_t* done, int idx, uint32_t ep) {
-    lds_barrier();
-    if (threadIdx.x == 0) ll_put(done + idx, 0.f, ep);
+// The copy of a broadcast vector this workgroup reads (its XCD's).
+__device__ __forceinline__ const uint64_t* rep_of(const uint64_t* base, int n) {
+    return base + (size_t)(blockIdx.x % REP) * n;
 }
 
 template <int U, bool SWZ>
@@ -663,15 +657,17 @@ __device__ __forceinline__ void lm_rows_load(float4 (&wrow)[2][D / 256], const f
 // LDS regions of one workgroup.
 template <int D, int F>
 struct Lds {
-    float *big, *r, *act, *xs, *us, *qh, *sc, *own, *gpart, *knew, *vnew, *comb, *delta, *red;
+    float *big, *r, *xs, *us, *u, *act, *delta, *qh, *sc, *own, *gpart, *knew, *vnew, *comb, *red;
     int* s_flag;
     __device__ explicit Lds(float* lds) {
         using C = Cfg<D, F>;
         big = lds;
         r = lds + C::OFF_R;
-        act = lds + C::OFF_ACT;
         xs = lds + C::OFF_XS;
         us = lds + C::OFF_US;
+        u = lds + C::OFF_U;
+        act = lds + C::OFF_ACT;
+        delta = lds + C::OFF_DELTA;
         qh = lds + C::OFF_QH;
         sc = lds + C::OFF_SC;
         own = lds + C::OFF_PART;  // own partial [PW]
@@ -679,7 +675,6 @@ struct Lds {
         knew = gpart + 7 * PW;    // [64]
         vnew = knew + 64;         // [64]
         comb = lds + C::OFF_COMB; // [4][64] scratch
-        delta = lds + C::OFF_DELTA;
         red = lds + C::OFF_RED;
         s_flag = reinterpret_cast<int*>(lds + C::OFF_FLAG);
     }
@@ -692,34 +687,115 @@ struct Off {
     static constexpr long QS = 0, OS = 3L * D * D / 32, US = 4L * D * D / 32, DS = (4L * D * D + (long)F * D) / 32;
 };
 
-// Phase C (every workgroup): r += o; LN2; FFN-up rows + GELU -> exchange.
+// Weights of phases B, C and D of one layer for this workgroup, plus LN2.
 template <int D, int F>
-__device__ __forceinline__ bool phase_c(const Args& a, const Lds<D, F>& S, uint64_t* X,
-                                        const WBlk<Cfg<D, F>::CPL_D, Cfg<D, F>::NP_UP>& wu, const LnRegs<D>& ln2,
-                                        int l) {
+struct BcdW {
+    using C = Cfg<D, F>;
+    WBlk<C::CPL_D, C::NP_O> wo;
+    WBlk<C::CPL_D, C::NP_UP> wu;
+    WBlk<C::CPL_F, C::NP_DN> wd;
+    LnRegs<D> ln2;
+};
+
+// Loads of the O and up rows and of LN2 (issued during phase A).
+template <int D, int F>
+__device__ __forceinline__ void load_bc(BcdW<D, F>& w, const uint8_t* wq, const float* ws, const float* ln) {
+    using C = Cfg<D, F>;
+    using O = Off<D, F>;
+    const int orow = blockIdx.x * C::O_ROWS, urow = blockIdx.x * C::UP_ROWS;
+    wblk_load<C::LPR_D, C::CPL_D, C::NP_O>(w.wo, wq + O::OO, ws + O::OS, D, orow, max(0, min(C::O_ROWS, D - orow)));
+    wblk_load<C::LPR_D, C::CPL_D, C::NP_UP>(w.wu, wq + O::UO, ws + O::US, D, urow, max(0, min(C::UP_ROWS, F - urow)));
+    ln_load<D>(w.ln2, ln + 2 * D, ln + 3 * D);
+}
+
+// Loads of the FFN-down rows (issued after phase B).
+template <int D, int F>
+__device__ __forceinline__ void load_d(BcdW<D, F>& w, const uint8_t* wq, const float* ws) {
+    using C = Cfg<D, F>;
+    using O = Off<D, F>;
+    const int drow = blockIdx.x * C::DN_ROWS;
+    wblk_load<C::LPR_F, C::CPL_F, C::NP_DN>(w.wd, wq + O::DO, ws + O::DS, F, drow, max(0, min(C::DN_ROWS, D - drow)));
+}
+
+// Phase B (every workgroup): attn -> O rows of this workgroup -> exchange.
+template <int D, int F>
+__device__ __forceinline__ bool phase_b(const Args& a, const Lds<D, F>& S, uint64_t* X, const BcdW<D, F>& w, int l) {
     using C = Cfg<D, F>;
     const uint32_t ep = a.epoch;
-    if (!ll_bcast<cdiv(D, NT), false>(X + C::XN_O, NO_WG, X + C::XB_O, D, S.delta, ep, a.err, S.s_flag, S.sc))
-        return false;
+    if (!ll_gather1<cdiv(D, NT), true>(rep_of(X + C::XB_ATT, D), D, S.act, ep, a.err, S.s_flag)) return false;
+    stamp(a, l, 6);
+    group_sums(S.act, D, S.xs);
+    float o[C::NP_O];
+    wblk_dot<C::LPR_D, C::CPL_D, C::NP_O>(w.wo, S.act, S.xs, o);
+    const int orow = blockIdx.x * C::O_ROWS;
+#pragma unroll
+    for (int p = 0; p < C::NP_O; ++p) {
+        const int rr = out_row<C::LPR_D>(p);
+        if (rr >= 0 && rr < C::O_ROWS && orow + rr < D) ll_put_rep(X + C::XB_O, D, orow + rr, o[p], ep);
+    }
+    stamp(a, l, 7);
+    return true;
+}
+
+// Phase C (every workgroup): r += o; LN2; FFN-up rows + GELU -> exchange.
+template <int D, int F>
+__device__ __forceinline__ bool phase_c(const Args& a, const Lds<D, F>& S, uint64_t* X, const BcdW<D, F>& w, int l) {
+    using C = Cfg<D, F>;
+    const uint32_t ep = a.epoch;
+    if (!ll_gather1<cdiv(D, NT), false>(rep_of(X + C::XB_O, D), D, S.delta, ep, a.err, S.s_flag)) return false;
     stamp(a, l, 8);
-    residual_layernorm<D, true>(S.r, S.delta, ln2, a.eps, S.act, S.xs, S.red);
+    residual_layernorm<D, true>(S.r, S.delta, w.ln2, a.eps, S.act, S.xs, S.red);
     float o[C::NP_UP];
-    wblk_dot<C::LPR_D, C::CPL_D, C::NP_UP>(wu, S.act, S.xs, o);
+    wblk_dot<C::LPR_D, C::CPL_D, C::NP_UP>(w.wu, S.act, S.xs, o);
     const int urow = blockIdx.x * C::UP_ROWS;
 #pragma unroll
     for (int p = 0; p < C::NP_UP; ++p) {
         const int rr = out_row<C::LPR_D>(p);
-        if (rr >= 0 && rr < C::UP_ROWS && urow + rr < F) ll_put(X + C::XC + urow + rr, gelu_erf(o[p]), ep);
+        if (rr >= 0 && rr < C::UP_ROWS && urow + rr < F) ll_put_rep(X + C::XC, F, urow + rr, gelu_erf(o[p]), ep);
     }
-    ll_done(X + C::XN_U, blockIdx.x, ep);
     stamp(a, l, 9);
+    return true;
+}
+
+// Phase D (every workgroup): u -> FFN-down rows of this workgroup -> exchange.
+template <int D, int F>
+__device__ __forceinline__ bool phase_d(const Args& a, const Lds<D, F>& S, uint64_t* X, const BcdW<D, F>& w, int l) {
+    using C = Cfg<D, F>;
+    const uint32_t ep = a.epoch;
+    if (!ll_gather1<cdiv(F, NT), true>(rep_of(X + C::XC, F), F, S.u, ep, a.err, S.s_flag)) return false;
+    stamp(a, l, 10);
+    group_sums(S.u, F, S.us);
+    float o[C::NP_DN];
+    wblk_dot<C::LPR_F, C::CPL_F, C::NP_DN>(w.wd, S.u, S.us, o);
+    const int drow = blockIdx.x * C::DN_ROWS;
+#pragma unroll
+    for (int p = 0; p < C::NP_DN; ++p) {
+        const int rr = out_row<C::LPR_F>(p);
+        if (rr >= 0 && rr < C::DN_ROWS && drow + rr < D) ll_put_rep(X + C::XD, D, drow + rr, o[p], ep);
+    }
+    stamp(a, l, 11);
+    return true;
+}
+
+// Start of phase A: r += f of the previous layer (if any); LN1 into act.
+template <int D, int F>
+__device__ __forceinline__ bool phase_a_ln(const Args& a, const Lds<D, F>& S, const LnRegs<D>& ln1, int l) {
+    using C = Cfg<D, F>;
+    stamp(a, l, 0);
+    if (l > 0) {
+        const uint64_t* Xp = a.x + (size_t)(l - 1) * C::LAYER_WORDS;
+        if (!ll_gather1<cdiv(D, NT), false>(rep_of(Xp + C::XD, D), D, S.delta, a.epoch, a.err, S.s_flag))
+            return false;
+    }
+    stamp(a, l, 1);
+    residual_layernorm<D, true>(S.r, l > 0 ? S.delta : nullptr, ln1, a.eps, S.act, S.xs, S.red);
+    stamp(a, l, 2);
     return true;
 }
 
 // Every layer for an attention workgroup (head h, split s).
 template <int D, int F>
-__device__ __forceinline__ bool attention_role(const Args& a, const Lds<D, F>& S, const Role& role,
-                                               float4 (&wrow)[2][D / 256], LnRegs<D>& lnf) {
+__device__ __forceinline__ bool attention_role(const Args& a, const Lds<D, F>& S, const Role& role) {
     using C = Cfg<D, F>;
     using O = Off<D, F>;
     const uint32_t ep = a.epoch;
@@ -729,10 +805,9 @@ __device__ __forceinline__ bool attention_role(const Args& a, const Lds<D, F>& S
     const int p0 = role.split * a.chunk;
     const int npos = max(0, min(a.t0, p0 + a.chunk) - p0);
     const size_t lstride = (size_t)a.t_cap * D;  // one layer of the cache (B = 1)
-    const int urow = blockIdx.x * C::UP_ROWS;
     WBlk<C::CPL_D, C::NP_Q> wqh;
-    WBlk<C::CPL_D, C::NP_UP> wu;
-    LnRegs<D> ln1, ln2;
+    BcdW<D, F> w;
+    LnRegs<D> ln1;
     if (npos > 0) kv_chunk_dma<D>(a.kc, a.vc, h, p0, npos, S.big);
     wblk_load<C::LPR_D, C::CPL_D, C::NP_Q>(wqh, a.wq + O::QO, a.ws + O::QS, D, h * 64, 64);
     ln_load<D>(ln1, a.ln, a.ln + D);
@@ -745,15 +820,7 @@ __device__ __forceinline__ bool attention_role(const Args& a, const Lds<D, F>& S
         const float* vc_l = a.vc + (size_t)l * lstride;
         const bool last = l + 1 == a.L;
         // ---- A: r += f_prev; LN1; q_h; softmax partial over the chunk
-        stamp(a, l, 0);
-        if (l > 0) {
-            const uint64_t* Xp = a.x + (size_t)(l - 1) * C::LAYER_WORDS;
-            if (!ll_bcast<cdiv(D, NT), false>(Xp + C::XN_F, ND_WG, Xp + C::XD, D, S.delta, ep, a.err, S.s_flag, S.sc))
-                return false;
-        }
-        stamp(a, l, 1);
-        residual_layernorm<D, true>(S.r, l > 0 ? S.delta : nullptr, ln1, a.eps, S.act, S.xs, S.red);
-        stamp(a, l, 2);
+        if (!phase_a_ln<D, F>(a, S, ln1, l)) return false;
         {
             float o[C::NP_Q];
             wblk_dot<C::LPR_D, C::CPL_D, C::NP_Q>(wqh, S.act, S.xs, o);
@@ -766,9 +833,8 @@ __device__ __forceinline__ bool attention_role(const Args& a, const Lds<D, F>& S
         __builtin_amdgcn_s_waitcnt(0);  // the K/V chunk DMA (and every earlier load) has landed
         lds_barrier();
         stamp(a, l, 3);
-        // phase-C weights load behind the attention
-        wblk_load<C::LPR_D, C::CPL_D, C::NP_UP>(wu, wq + O::UO, ws + O::US, D, urow, max(0, min(C::UP_ROWS, F - urow)));
-        ln_load<D>(ln2, ln + 2 * D, ln + 3 * D);
+        // phase B and C weights load behind the attention
+        load_bc<D, F>(w, wq, ws, ln);
         attend_chunk(S.big, S.qh, npos, S.sc, S.comb, S.red + 8, S.own, a, l);
         stamp(a, l, 4);
         if (!leader) {
@@ -802,44 +868,36 @@ __device__ __forceinline__ bool attention_role(const Args& a, const Lds<D, F>& S
                     Ls = fmaf(wgt, S.gpart[s * PW + 1], Ls);
                     A = fmaf(wgt, S.gpart[s * PW + 2 + tid], A);
                 }
-                ll_put(X + C::XB_ATT + h * 64 + tid, A / Ls, ep);
+                ll_put_rep(X + C::XB_ATT, D, h * 64 + tid, A / Ls, ep);
             }
-            ll_done(X + C::XN_ATT, h, ep);
             if (!last && npos > 0) kv_chunk_dma<D>(kc_l + lstride, vc_l + lstride, h, p0, npos, S.big);
         }
-        // ---- C
-        if (!phase_c<D, F>(a, S, X, wu, ln2, l)) return false;
+        // ---- B, C, D
+        if (!phase_b<D, F>(a, S, X, w, l)) return false;
+        load_d<D, F>(w, wq, ws);
+        if (!phase_c<D, F>(a, S, X, w, l)) return false;
         if (!last) {
             const uint8_t* wqn = wq + a.wq_layer;
             const float* wsn = ws + a.ws_layer;
             wblk_load<C::LPR_D, C::CPL_D, C::NP_Q>(wqh, wqn + O::QO, wsn + O::QS, D, h * 64, 64);
             ln_load<D>(ln1, ln + 4 * D, ln + 5 * D);
-        } else {
-            lm_rows_load<D>(wrow, a.lm_head, a.V);
-            ln_load<D>(lnf, a.ln_final, a.ln_final + D);
         }
+        if (!phase_d<D, F>(a, S, X, w, l)) return false;
     }
     return true;
 }
 
-// Every layer for a workgroup without attention duty: new K/V rows, and
-// (by role) the O projection and FFN-down; FFN-up like everyone.
+// Every layer for a workgroup without attention duty: new K/V rows in
+// phase A; phases B, C, D like every workgroup.
 template <int D, int F>
-__device__ __forceinline__ bool free_role(const Args& a, const Lds<D, F>& S, const Role& role,
-                                          float4 (&wrow)[2][D / 256], LnRegs<D>& lnf) {
+__device__ __forceinline__ bool free_role(const Args& a, const Lds<D, F>& S, const Role& role) {
     using C = Cfg<D, F>;
     using O = Off<D, F>;
     const uint32_t ep = a.epoch;
     const size_t lstride = (size_t)a.t_cap * D;
-    const int urow = blockIdx.x * C::UP_ROWS;
-    const bool o_role = role.o_idx >= 0, d_role = role.d_idx >= 0;
-    const int orow = o_role ? role.o_idx * C::O_ROWS : 0;
-    const int drow = d_role ? role.d_idx * C::DN_ROWS : 0;
     WBlk<C::CPL_D, C::NP_KV> wkv;
-    WBlk<C::CPL_D, C::NP_O> wo;
-    WBlk<C::CPL_D, C::NP_UP> wu;
-    WBlk<C::CPL_F, C::NP_DN> wd;
-    LnRegs<D> ln1, ln2;
+    BcdW<D, F> w;
+    LnRegs<D> ln1;
     if (role.kv_rows > 0)
         wblk_load<C::LPR_D, C::CPL_D, C::NP_KV>(wkv, a.wq + O::QO, a.ws + O::QS, D, D + role.kv_row0, role.kv_rows);
     ln_load<D>(ln1, a.ln, a.ln + D);
@@ -852,15 +910,7 @@ __device__ __forceinline__ bool free_role(const Args& a, const Lds<D, F>& S, con
         float* vc_l = a.vc + (size_t)l * lstride;
         const bool last = l + 1 == a.L;
         // ---- A: r += f_prev; LN1; new K/V rows
-        stamp(a, l, 0);
-        if (l > 0) {
-            const uint64_t* Xp = a.x + (size_t)(l - 1) * C::LAYER_WORDS;
-            if (!ll_bcast<cdiv(D, NT), false>(Xp + C::XN_F, ND_WG, Xp + C::XD, D, S.delta, ep, a.err, S.s_flag, S.sc))
-                return false;
-        }
-        stamp(a, l, 1);
-        residual_layernorm<D, true>(S.r, l > 0 ? S.delta : nullptr, ln1, a.eps, S.act, S.xs, S.red);
-        stamp(a, l, 2);
+        if (!phase_a_ln<D, F>(a, S, ln1, l)) return false;
         if (role.kv_rows > 0) {
             float o[C::NP_KV];
             wblk_dot<C::LPR_D, C::CPL_D, C::NP_KV>(wkv, S.act, S.xs, o);
@@ -876,68 +926,18 @@ __device__ __forceinline__ bool free_role(const Args& a, const Lds<D, F>& S, con
                 }
             }
         }
-        // weights of phases B, C, D
-        if (o_role)
-            wblk_load<C::LPR_D, C::CPL_D, C::NP_O>(wo, wq + O::OO, ws + O::OS, D, orow, min(C::O_ROWS, D - orow));
-        wblk_load<C::LPR_D, C::CPL_D, C::NP_UP>(wu, wq + O::UO, ws + O::US, D, urow, max(0, min(C::UP_ROWS, F - urow)));
-        ln_load<D>(ln2, ln + 2 * D, ln + 3 * D);
-        if (d_role)
-            wblk_load<C::LPR_F, C::CPL_F, C::NP_DN>(wd, wq + O::DO, ws + O::DS, F, drow, min(C::DN_ROWS, D - drow));
-        // ---- B: O rows
-        if (o_role) {
-            if (!ll_bcast<cdiv(D, NT), true>(X + C::XN_ATT, C::H, X + C::XB_ATT, D, S.act, ep, a.err, S.s_flag, S.sc))
-                return false;
-            stamp(a, l, 6);
-            group_sums(S.act, D, S.xs);
-            float o[C::NP_O];
-            wblk_dot<C::LPR_D, C::CPL_D, C::NP_O>(wo, S.act, S.xs, o);
-#pragma unroll
-            for (int p = 0; p < C::NP_O; ++p) {
-                const int rr = out_row<C::LPR_D>(p);
-                if (rr >= 0 && rr < C::O_ROWS && orow + rr < D) ll_put(X + C::XB_O + orow + rr, o[p], ep);
-            }
-            ll_done(X + C::XN_O, role.o_idx, ep);
-            stamp(a, l, 7);
-        }
-        // ---- C
-        if (!phase_c<D, F>(a, S, X, wu, ln2, l)) return false;
-        const uint8_t* wqn = wq + a.wq_layer;
-        const float* wsn = ws + a.ws_layer;
-        if (!d_role) {
-            if (!last) {
-                if (role.kv_rows > 0)
-                    wblk_load<C::LPR_D, C::CPL_D, C::NP_KV>(wkv, wqn + O::QO, wsn + O::QS, D, D + role.kv_row0, role.kv_rows);
-                ln_load<D>(ln1, ln + 4 * D, ln + 5 * D);
-            } else {
-                lm_rows_load<D>(wrow, a.lm_head, a.V);
-                ln_load<D>(lnf, a.ln_final, a.ln_final + D);
-            }
-            continue;
-        }
-        // ---- D: FFN-down rows
-        float* u = S.big;  // swizzled [F]
-        if (!ll_bcast<cdiv(F, NT), true>(X + C::XN_U, NWG, X + C::XC, F, u, ep, a.err, S.s_flag, S.sc)) return false;
-        stamp(a, l, 10);
-        group_sums(u, F, S.us);
-        {
-            float o[C::NP_DN];
-            wblk_dot<C::LPR_F, C::CPL_F, C::NP_DN>(wd, u, S.us, o);
-#pragma unroll
-            for (int p = 0; p < C::NP_DN; ++p) {
-                const int rr = out_row<C::LPR_F>(p);
-                if (rr >= 0 && rr < C::DN_ROWS && drow + rr < D) ll_put(X + C::XD + drow + rr, o[p], ep);
-            }
-        }
-        ll_done(X + C::XN_F, role.d_idx, ep);
-        stamp(a, l, 11);
+        load_bc<D, F>(w, wq, ws, ln);
+        // ---- B, C, D
+        if (!phase_b<D, F>(a, S, X, w, l)) return false;
+        load_d<D, F>(w, wq, ws);
+        if (!phase_c<D, F>(a, S, X, w, l)) return false;
         if (!last) {
             if (role.kv_rows > 0)
-                wblk_load<C::LPR_D, C::CPL_D, C::NP_KV>(wkv, wqn + O::QO, wsn + O::QS, D, D + role.kv_row0, role.kv_rows);
+                wblk_load<C::LPR_D, C::CPL_D, C::NP_KV>(wkv, wq + a.wq_layer + O::QO, ws + a.ws_layer + O::QS, D,
+                                                        D + role.kv_row0, role.kv_rows);
             ln_load<D>(ln1, ln + 4 * D, ln + 5 * D);
-        } else {
-            lm_rows_load<D>(wrow, a.lm_head, a.V);
-            ln_load<D>(lnf, a.ln_final, a.ln_final + D);
         }
+        if (!phase_d<D, F>(a, S, X, w, l)) return false;
     }
     return true;
 }
@@ -962,19 +962,21 @@ __global__ __launch_bounds__(NT, 1) void k_decode_step(Args a) {
         lds_barrier();
     }
 
-    float4 wrow[2][D / 256];  // LM-head rows, loaded during the last layer
-    LnRegs<D> lnf;
-    const bool ok = role.head >= 0 ? attention_role<D, F>(a, S, role, wrow, lnf)
-                                   : free_role<D, F>(a, S, role, wrow, lnf);
+    const bool ok = role.head >= 0 ? attention_role<D, F>(a, S, role) : free_role<D, F>(a, S, role);
     if (!ok) return;
+    // LM-head rows and LN_f, loaded while the last layer's FFN-down output
+    // is still in flight
+    float4 wrow[2][D / 256];
+    LnRegs<D> lnf;
+    lm_rows_load<D>(wrow, a.lm_head, a.V);
+    ln_load<D>(lnf, a.ln_final, a.ln_final + D);
 
     // ===================== phase E: r += f; z = LN_f(r); LM-head rows + local argmax
     uint64_t* XE = a.x + (size_t)a.L * C::LAYER_WORDS;
     {
         stamp(a, a.L, 0);
         const uint64_t* Xp = a.x + (size_t)(a.L - 1) * C::LAYER_WORDS;
-        if (!ll_bcast<cdiv(D, NT), false>(Xp + C::XN_F, ND_WG, Xp + C::XD, D, S.delta, ep, a.err, S.s_flag, S.sc))
-            return;
+        if (!ll_gather1<cdiv(D, NT), false>(rep_of(Xp + C::XD, D), D, S.delta, ep, a.err, S.s_flag)) return;
         stamp(a, a.L, 1);
         residual_layernorm<D, false>(S.r, S.delta, lnf, a.eps, S.act, nullptr, S.red);
         float* cand_v = S.comb;                              // [8]
@@ -1060,7 +1062,7 @@ static void build_roles(Role* roles) {
     for (int h = 0; h < C::H; ++h) ++nh_x[h % NXCD];
     for (int w = 0; w < NWG; ++w) {
         Role& r = roles[w];
-        r = Role{-1, 0, -1, -1, 0, 0, 0, 0};
+        r = Role{-1, 0, 0, 0};
         const int x = w % NXCD, slot = w / NXCD;
         if (slot < nh_x[x] * ATT_S) {
             r.head = (slot / ATT_S) * NXCD + x;
@@ -1071,13 +1073,6 @@ static void build_roles(Role* roles) {
     }
     for (int i = 0; i < nfree; ++i) {
         Role& r = roles[free_list[i]];
-        if (nfree >= NO_WG + ND_WG) {
-            if (i < NO_WG) r.o_idx = i;
-            else if (i < NO_WG + ND_WG) r.d_idx = i - NO_WG;
-        } else {
-            if (i < NO_WG) r.o_idx = i;
-            if (i < ND_WG) r.d_idx = i;
-        }
         const int row0 = i * C::KV_ROWS;
         r.kv_row0 = row0;
         r.kv_rows = row0 < 2 * D ? (2 * D - row0 < C::KV_ROWS ? 2 * D - row0 : C::KV_ROWS) : 0;
