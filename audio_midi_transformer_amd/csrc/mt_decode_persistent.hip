@@ -116,13 +116,11 @@ struct Cfg {
     // resident across phases B..D (it is the next layer's chunk by then), so
     // u of phase D shares one region with the vectors of phases A..C.
     static constexpr int BIG = 2 * MAXPOS * 64;           // K|V chunk
-    static constexpr int OFF_R = BIG;                     // residual [D]
-    static constexpr int OFF_XS = OFF_R + D;              // group sums of act [GD]
+    static constexpr int OFF_XS = BIG;                    // group sums of act [GD]
     static constexpr int OFF_US = OFF_XS + GD;            // group sums of u [GF]
     static constexpr int OFF_U = rup(OFF_US + GF, 4);     // u [F] (phase D) or:
     static constexpr int OFF_ACT = OFF_U;                 //   act [D]
-    static constexpr int OFF_DELTA = OFF_ACT + D;         //   exchanged D-vector (f or o) [D]
-    static constexpr int OFF_QH = OFF_DELTA + D;          //   q_h [64]
+    static constexpr int OFF_QH = OFF_ACT + D;            //   q_h [64]
     static constexpr int OFF_SC = OFF_QH + 64;            //   scores [MAXPOS]
     static constexpr int OFF_PART = OFF_SC + MAXPOS;      //   own partial [PW] + gathered [7][PW] + kv_new [128]
     static constexpr int OFF_COMB = rup(OFF_PART + 8 * PW + 128, 4);  // [4][64] scratch
@@ -159,6 +157,7 @@ struct Args {
     uint64_t* x;  // exchange words
     const Role* roles;
     int* err;
+    unsigned nib;     // 0x0F0F0F0F (nibble mask, see dot_u)
     uint64_t* trace;  // optional: [NWG][L + 1][TRACE_SLOTS] wall-clock stamps
 };
 
@@ -348,6 +347,39 @@ __device__ __forceinline__ bool ll_gather1(const uint64_t* src, int n, float* ds
     return ll_gather<U, SWZ>(Range{src, n, dst}, Range{src, 0, dst}, Range{src, 0, dst}, ep, err, s_flag);
 }
 
+// Wait for words t + i * NT (i < U) of an n-word vector and return their
+// values in registers (thread t), the element mapping of the LayerNorm.  On
+// a failed wait the error bit is set and false returned; the caller flags
+// the workgroup.
+template <int U>
+__device__ __forceinline__ bool ll_gather_regs(const uint64_t* src, int n, float (&v)[U], uint32_t ep, int* err) {
+    uint64_t w[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int i = u * NT + threadIdx.x;
+        w[u] = (i < n) ? ll_get(src + i) : ((uint64_t)ep << 32);
+    }
+    bool ok = true;
+    for (uint32_t it = 0;; ++it) {
+        bool all = true;
+#pragma unroll
+        for (int u = 0; u < U; ++u) all &= (uint32_t)(w[u] >> 32) == ep;
+        if (all) break;
+        if (it > SPIN_LIMIT || ((it & 255u) == 255u && aborted(err))) {
+            ok = false;
+            break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if ((uint32_t)(w[u] >> 32) != ep) w[u] = ll_get(src + u * NT + threadIdx.x);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = __uint_as_float((uint32_t)w[u]);
+    if (!ok) atomicOr(err, 2);
+    return ok;
+}
+
 // ---------------------------------------------------------------- LayerNorm
 
 // xs[c] = sum of the 32 elements of group c (its elements stay within its
@@ -385,33 +417,33 @@ __device__ __forceinline__ void ln_load(LnRegs<D>& p, const float* __restrict__ 
     }
 }
 
-// r += delta (if given); y = LN(r) * g + b into act (swizzled when SWZ),
-// plus group sums into xs (if given).  Biased variance, two passes.
+// r += delta (if add); y = LN(r) * g + b into act (swizzled when SWZ),
+// plus the group sums of y into xs (if given).  Biased variance, two
+// passes.  Thread t holds elements t + i * NT of r and delta in registers;
+// with this mapping the 32 elements of a group sit in 32 consecutive lanes,
+// so group sums are lane reductions.  Returns false (for every thread) if
+// a thread of the workgroup flagged a failed exchange before the call.
 template <int D, bool SWZ>
-__device__ __forceinline__ void residual_layernorm(float* r, const float* delta, const LnRegs<D>& p, float eps,
-                                                   float* act, float* xs, float* red) {
+__device__ __forceinline__ bool residual_layernorm(float (&r)[LnRegs<D>::PER], const float (&delta)[LnRegs<D>::PER],
+                                                   bool add, const LnRegs<D>& p, float eps, float* act, float* xs, float* red,
+                                                   const int* s_flag) {
     constexpr int PER = LnRegs<D>::PER;
-    float v[PER];
     float s = 0.f;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
         const int k = threadIdx.x + i * NT;
-        v[i] = 0.f;
         if (k < D) {
-            v[i] = r[k];
-            if (delta) {
-                v[i] += delta[k];
-                r[k] = v[i];
-            }
+            if (add) r[i] += delta[i];
+            s += r[i];
         }
-        s += v[i];
     }
     const float mean = block_reduce<false>(s, red) / (float)D;
+    if (*s_flag) return false;
     float q = 0.f;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
         const int k = threadIdx.x + i * NT;
-        const float c = k < D ? v[i] - mean : 0.f;
+        const float c = k < D ? r[i] - mean : 0.f;
         q = fmaf(c, c, q);
     }
     const float var = block_reduce<false>(q, red + 4) / (float)D;
@@ -419,10 +451,15 @@ __device__ __forceinline__ void residual_layernorm(float* r, const float* delta,
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
         const int k = threadIdx.x + i * NT;
-        if (k < D) act[SWZ ? swz(k) : k] = (v[i] - mean) * rstd * p.g[i] + p.b[i];
+        const float y = k < D ? (r[i] - mean) * rstd * p.g[i] + p.b[i] : 0.f;
+        if (k < D) act[SWZ ? swz(k) : k] = y;
+        if (xs) {
+            const float t = group_reduce<32>(y);
+            if ((threadIdx.x & 31) == res_lane(32) && k < D) xs[k >> 5] = t;
+        }
     }
     lds_barrier();
-    if (xs) group_sums(act, D, xs);
+    return true;
 }
 
 // ---------------------------------------------------------------- INT4 rows held in registers
@@ -472,28 +509,25 @@ __device__ __forceinline__ void load_group(const float* act, int c, float (&x)[3
     }
 }
 
-// Unsigned byte n of x converted to float (v_cvt_f32_ubyte<n>): one
-// instruction per weight once the nibbles sit in separate bytes.
+// Unsigned byte N of x as float: one v_cvt_f32_ubyte<N> per weight.
 template <int N>
 __device__ __forceinline__ float ubyte(unsigned x) {
-    float r;
-    if constexpr (N == 0) asm("v_cvt_f32_ubyte0 %0, %1" : "=v"(r) : "v"(x));
-    else if constexpr (N == 1) asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(r) : "v"(x));
-    else if constexpr (N == 2) asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(r) : "v"(x));
-    else asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(r) : "v"(x));
-    return r;
+    return (float)(uint8_t)(x >> (8 * N));
 }
 
 // sum_k u_k x_k over one group.  Byte j of the group holds input 2j (low
-// nibble) and 2j+1 (high nibble).
-__device__ __forceinline__ float dot_u(uint4 w, const float (&x)[32]) {
+// nibble) and 2j+1 (high nibble).  `m` is 0x0F0F0F0F, passed in at run time:
+// with a literal mask the compiler knows the upper bits of each byte are
+// zero and extracts every nibble with a bit-field instruction before the
+// conversion instead of converting bytes directly.
+__device__ __forceinline__ float dot_u(uint4 w, const float (&x)[32], unsigned m) {
     const unsigned wd[4] = {w.x, w.y, w.z, w.w};
     float acc = 0.f;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        const unsigned lo = wd[m] & 0x0F0F0F0Fu;
-        const unsigned hi = (wd[m] >> 4) & 0x0F0F0F0Fu;
-        const float* xm = x + 8 * m;
+    for (int k = 0; k < 4; ++k) {
+        const unsigned lo = wd[k] & m;
+        const unsigned hi = (wd[k] >> 4) & m;
+        const float* xm = x + 8 * k;
         acc = fmaf(ubyte<0>(lo), xm[0], acc);
         acc = fmaf(ubyte<0>(hi), xm[1], acc);
         acc = fmaf(ubyte<1>(lo), xm[2], acc);
@@ -512,7 +546,7 @@ __device__ __forceinline__ float dot_u(uint4 w, const float (&x)[32]) {
 // is read from LDS once and used for every row.
 template <int LPR, int CPL, int NP>
 __device__ __forceinline__ void wblk_dot(const WBlk<CPL, NP>& w, const float* act, const float* xs,
-                                         float (&out)[NP]) {
+                                         float (&out)[NP], unsigned m) {
     const int lr = threadIdx.x % LPR;
     float acc[NP];
 #pragma unroll
@@ -524,7 +558,7 @@ __device__ __forceinline__ void wblk_dot(const WBlk<CPL, NP>& w, const float* ac
         load_group(act, c, x);
         const float x8 = -8.f * xs[c];
 #pragma unroll
-        for (int p = 0; p < NP; ++p) acc[p] = fmaf(w.s[p][j], dot_u(w.q[p][j], x) + x8, acc[p]);
+        for (int p = 0; p < NP; ++p) acc[p] = fmaf(w.s[p][j], dot_u(w.q[p][j], x, m) + x8, acc[p]);
     }
 #pragma unroll
     for (int p = 0; p < NP; ++p) out[p] = group_reduce<LPR>(acc[p]);
@@ -657,17 +691,15 @@ __device__ __forceinline__ void lm_rows_load(float4 (&wrow)[2][D / 256], const f
 // LDS regions of one workgroup.
 template <int D, int F>
 struct Lds {
-    float *big, *r, *xs, *us, *u, *act, *delta, *qh, *sc, *own, *gpart, *knew, *vnew, *comb, *red;
+    float *big, *xs, *us, *u, *act, *qh, *sc, *own, *gpart, *knew, *vnew, *comb, *red;
     int* s_flag;
     __device__ explicit Lds(float* lds) {
         using C = Cfg<D, F>;
         big = lds;
-        r = lds + C::OFF_R;
         xs = lds + C::OFF_XS;
         us = lds + C::OFF_US;
         u = lds + C::OFF_U;
         act = lds + C::OFF_ACT;
-        delta = lds + C::OFF_DELTA;
         qh = lds + C::OFF_QH;
         sc = lds + C::OFF_SC;
         own = lds + C::OFF_PART;  // own partial [PW]
@@ -726,7 +758,7 @@ __device__ __forceinline__ bool phase_b(const Args& a, const Lds<D, F>& S, uint6
     stamp(a, l, 6);
     group_sums(S.act, D, S.xs);
     float o[C::NP_O];
-    wblk_dot<C::LPR_D, C::CPL_D, C::NP_O>(w.wo, S.act, S.xs, o);
+    wblk_dot<C::LPR_D, C::CPL_D, C::NP_O>(w.wo, S.act, S.xs, o, a.nib);
     const int orow = blockIdx.x * C::O_ROWS;
 #pragma unroll
     for (int p = 0; p < C::NP_O; ++p) {
@@ -739,14 +771,16 @@ __device__ __forceinline__ bool phase_b(const Args& a, const Lds<D, F>& S, uint6
 
 // Phase C (every workgroup): r += o; LN2; FFN-up rows + GELU -> exchange.
 template <int D, int F>
-__device__ __forceinline__ bool phase_c(const Args& a, const Lds<D, F>& S, uint64_t* X, const BcdW<D, F>& w, int l) {
+__device__ __forceinline__ bool phase_c(const Args& a, const Lds<D, F>& S, uint64_t* X, const BcdW<D, F>& w,
+                                        float (&r)[LnRegs<D>::PER], int l) {
     using C = Cfg<D, F>;
     const uint32_t ep = a.epoch;
-    if (!ll_gather1<cdiv(D, NT), false>(rep_of(X + C::XB_O, D), D, S.delta, ep, a.err, S.s_flag)) return false;
+    float o_in[LnRegs<D>::PER];
+    if (!ll_gather_regs<LnRegs<D>::PER>(rep_of(X + C::XB_O, D), D, o_in, ep, a.err)) *S.s_flag = 1;
     stamp(a, l, 8);
-    residual_layernorm<D, true>(S.r, S.delta, w.ln2, a.eps, S.act, S.xs, S.red);
+    if (!residual_layernorm<D, true>(r, o_in, true, w.ln2, a.eps, S.act, S.xs, S.red, S.s_flag)) return false;
     float o[C::NP_UP];
-    wblk_dot<C::LPR_D, C::CPL_D, C::NP_UP>(w.wu, S.act, S.xs, o);
+    wblk_dot<C::LPR_D, C::CPL_D, C::NP_UP>(w.wu, S.act, S.xs, o, a.nib);
     const int urow = blockIdx.x * C::UP_ROWS;
 #pragma unroll
     for (int p = 0; p < C::NP_UP; ++p) {
@@ -766,7 +800,7 @@ __device__ __forceinline__ bool phase_d(const Args& a, const Lds<D, F>& S, uint6
     stamp(a, l, 10);
     group_sums(S.u, F, S.us);
     float o[C::NP_DN];
-    wblk_dot<C::LPR_F, C::CPL_F, C::NP_DN>(w.wd, S.u, S.us, o);
+    wblk_dot<C::LPR_F, C::CPL_F, C::NP_DN>(w.wd, S.u, S.us, o, a.nib);
     const int drow = blockIdx.x * C::DN_ROWS;
 #pragma unroll
     for (int p = 0; p < C::NP_DN; ++p) {
@@ -779,23 +813,25 @@ __device__ __forceinline__ bool phase_d(const Args& a, const Lds<D, F>& S, uint6
 
 // Start of phase A: r += f of the previous layer (if any); LN1 into act.
 template <int D, int F>
-__device__ __forceinline__ bool phase_a_ln(const Args& a, const Lds<D, F>& S, const LnRegs<D>& ln1, int l) {
+__device__ __forceinline__ bool phase_a_ln(const Args& a, const Lds<D, F>& S, const LnRegs<D>& ln1,
+                                           float (&r)[LnRegs<D>::PER], int l) {
     using C = Cfg<D, F>;
     stamp(a, l, 0);
+    float f[LnRegs<D>::PER] = {};
     if (l > 0) {
         const uint64_t* Xp = a.x + (size_t)(l - 1) * C::LAYER_WORDS;
-        if (!ll_gather1<cdiv(D, NT), false>(rep_of(Xp + C::XD, D), D, S.delta, a.epoch, a.err, S.s_flag))
-            return false;
+        if (!ll_gather_regs<LnRegs<D>::PER>(rep_of(Xp + C::XD, D), D, f, a.epoch, a.err)) *S.s_flag = 1;
     }
     stamp(a, l, 1);
-    residual_layernorm<D, true>(S.r, l > 0 ? S.delta : nullptr, ln1, a.eps, S.act, S.xs, S.red);
+    if (!residual_layernorm<D, true>(r, f, l > 0, ln1, a.eps, S.act, S.xs, S.red, S.s_flag)) return false;
     stamp(a, l, 2);
     return true;
 }
 
 // Every layer for an attention workgroup (head h, split s).
 template <int D, int F>
-__device__ __forceinline__ bool attention_role(const Args& a, const Lds<D, F>& S, const Role& role) {
+__device__ __forceinline__ bool attention_role(const Args& a, const Lds<D, F>& S, const Role& role,
+                                               float (&r)[LnRegs<D>::PER]) {
     using C = Cfg<D, F>;
     using O = Off<D, F>;
     const uint32_t ep = a.epoch;
@@ -820,16 +856,17 @@ __device__ __forceinline__ bool attention_role(const Args& a, const Lds<D, F>& S
         const float* vc_l = a.vc + (size_t)l * lstride;
         const bool last = l + 1 == a.L;
         // ---- A: r += f_prev; LN1; q_h; softmax partial over the chunk
-        if (!phase_a_ln<D, F>(a, S, ln1, l)) return false;
+        if (!phase_a_ln<D, F>(a, S, ln1, r, l)) return false;
         {
             float o[C::NP_Q];
-            wblk_dot<C::LPR_D, C::CPL_D, C::NP_Q>(wqh, S.act, S.xs, o);
+            wblk_dot<C::LPR_D, C::CPL_D, C::NP_Q>(wqh, S.act, S.xs, o, a.nib);
 #pragma unroll
             for (int p = 0; p < C::NP_Q; ++p) {
                 const int rr = out_row<C::LPR_D>(p);
                 if (rr >= 0 && rr < 64) S.qh[rr] = o[p];
             }
         }
+        stamp(a, l, 15);
         __builtin_amdgcn_s_waitcnt(0);  // the K/V chunk DMA (and every earlier load) has landed
         lds_barrier();
         stamp(a, l, 3);
@@ -875,7 +912,7 @@ __device__ __forceinline__ bool attention_role(const Args& a, const Lds<D, F>& S
         // ---- B, C, D
         if (!phase_b<D, F>(a, S, X, w, l)) return false;
         load_d<D, F>(w, wq, ws);
-        if (!phase_c<D, F>(a, S, X, w, l)) return false;
+        if (!phase_c<D, F>(a, S, X, w, r, l)) return false;
         if (!last) {
             const uint8_t* wqn = wq + a.wq_layer;
             const float* wsn = ws + a.ws_layer;
@@ -890,7 +927,8 @@ __device__ __forceinline__ bool attention_role(const Args& a, const Lds<D, F>& S
 // Every layer for a workgroup without attention duty: new K/V rows in
 // phase A; phases B, C, D like every workgroup.
 template <int D, int F>
-__device__ __forceinline__ bool free_role(const Args& a, const Lds<D, F>& S, const Role& role) {
+__device__ __forceinline__ bool free_role(const Args& a, const Lds<D, F>& S, const Role& role,
+                                          float (&r)[LnRegs<D>::PER]) {
     using C = Cfg<D, F>;
     using O = Off<D, F>;
     const uint32_t ep = a.epoch;
@@ -910,10 +948,10 @@ __device__ __forceinline__ bool free_role(const Args& a, const Lds<D, F>& S, con
         float* vc_l = a.vc + (size_t)l * lstride;
         const bool last = l + 1 == a.L;
         // ---- A: r += f_prev; LN1; new K/V rows
-        if (!phase_a_ln<D, F>(a, S, ln1, l)) return false;
+        if (!phase_a_ln<D, F>(a, S, ln1, r, l)) return false;
         if (role.kv_rows > 0) {
             float o[C::NP_KV];
-            wblk_dot<C::LPR_D, C::CPL_D, C::NP_KV>(wkv, S.act, S.xs, o);
+            wblk_dot<C::LPR_D, C::CPL_D, C::NP_KV>(wkv, S.act, S.xs, o, a.nib);
 #pragma unroll
             for (int p = 0; p < C::NP_KV; ++p) {
                 const int rr = out_row<C::LPR_D>(p);
@@ -930,7 +968,7 @@ __device__ __forceinline__ bool free_role(const Args& a, const Lds<D, F>& S, con
         // ---- B, C, D
         if (!phase_b<D, F>(a, S, X, w, l)) return false;
         load_d<D, F>(w, wq, ws);
-        if (!phase_c<D, F>(a, S, X, w, l)) return false;
+        if (!phase_c<D, F>(a, S, X, w, r, l)) return false;
         if (!last) {
             if (role.kv_rows > 0)
                 wblk_load<C::LPR_D, C::CPL_D, C::NP_KV>(wkv, wq + a.wq_layer + O::QO, ws + a.ws_layer + O::QS, D,
@@ -953,16 +991,22 @@ __global__ __launch_bounds__(NT, 1) void k_decode_step(Args a) {
     const Role role = a.roles[wg];
     if (tid == 0) *S.s_flag = 0;
 
-    // embedding of the token into the residual copy
+    // embedding of the token: this workgroup's copy of the residual stream,
+    // element tid + i * NT in r[i]
+    float r[LnRegs<D>::PER];
     {
         const int64_t tok = gload(a.token);
         const bool bad = tok < 0 || tok >= a.V;
         if (bad && wg == 0 && tid == 0) atomicOr(a.err, 1);
-        for (int k = tid; k < D; k += NT) S.r[k] = bad ? __builtin_nanf("") : gload(a.tok_emb + (size_t)tok * D + k);
-        lds_barrier();
+#pragma unroll
+        for (int i = 0; i < LnRegs<D>::PER; ++i) {
+            const int k = tid + i * NT;
+            r[i] = k >= D ? 0.f : (bad ? __builtin_nanf("") : gload(a.tok_emb + (size_t)tok * D + k));
+        }
+        lds_barrier();  // s_flag initialised
     }
 
-    const bool ok = role.head >= 0 ? attention_role<D, F>(a, S, role) : free_role<D, F>(a, S, role);
+    const bool ok = role.head >= 0 ? attention_role<D, F>(a, S, role, r) : free_role<D, F>(a, S, role, r);
     if (!ok) return;
     // LM-head rows and LN_f, loaded while the last layer's FFN-down output
     // is still in flight
@@ -976,9 +1020,10 @@ __global__ __launch_bounds__(NT, 1) void k_decode_step(Args a) {
     {
         stamp(a, a.L, 0);
         const uint64_t* Xp = a.x + (size_t)(a.L - 1) * C::LAYER_WORDS;
-        if (!ll_gather1<cdiv(D, NT), false>(rep_of(Xp + C::XD, D), D, S.delta, ep, a.err, S.s_flag)) return;
+        float f[LnRegs<D>::PER];
+        if (!ll_gather_regs<LnRegs<D>::PER>(rep_of(Xp + C::XD, D), D, f, ep, a.err)) *S.s_flag = 1;
         stamp(a, a.L, 1);
-        residual_layernorm<D, false>(S.r, S.delta, lnf, a.eps, S.act, nullptr, S.red);
+        if (!residual_layernorm<D, false>(r, f, true, lnf, a.eps, S.act, nullptr, S.red, S.s_flag)) return;
         float* cand_v = S.comb;                              // [8]
         int* cand_i = reinterpret_cast<int*>(S.comb + 8);    // [8]
         if (tid < 8) {
@@ -1146,6 +1191,7 @@ static hipError_t launch_t(const PersistentArgs& p, hipStream_t st) {
     a.ws_layer = (3L * D * D + (long)D * D + 2L * F * D) / 32;
     a.kc = p.kc; a.vc = p.vc; a.token = p.token; a.logits = p.logits;
     a.next = p.next; a.t0 = p.t0; a.epoch = p.epoch; a.x = x; a.roles = roles; a.err = p.err;
+    a.nib = 0x0F0F0F0Fu;
     a.trace = static_cast<uint64_t*>(p.trace);
     const int chunk = (p.t0 + pd::ATT_S - 1) / pd::ATT_S;
     if (chunk > pd::MAXPOS) return hipErrorInvalidValue;
