@@ -40,6 +40,8 @@ int fail(int code, const char* fmt, ...) {
 
 constexpr int kPart = 68;      // floats per attention partial (m, l, acc[64], pad)
 constexpr int kMaxSplit = 64;  // split-K bound of the decode attention
+constexpr int kMaxChunk = 256; // positions per split of the decode attention
+constexpr int kMaxTcap = kMaxSplit * kMaxChunk;
 
 }  // namespace
 
@@ -104,7 +106,7 @@ int check_config(const mt_config* c) {
     if (c->group != 32) return fail(MT_ERR_UNSUPPORTED, "group must be 32 (got %d)", c->group);
     if (c->flags != 0) return fail(MT_ERR_UNSUPPORTED, "flags must be 0");
     if (c->n_layers < 1 || c->n_heads < 1 || c->vocab < 1 || c->batch < 1 || c->batch > 64 ||
-        c->t_cap < 1 || c->d_ff < 32)
+        c->t_cap < 1 || c->t_cap > kMaxTcap || c->d_ff < 32)
         return fail(MT_ERR_INVALID_ARG, "non-positive or out-of-range size in config");
     if (c->d_model != c->n_heads * 64)
         return fail(MT_ERR_INVALID_ARG, "d_model (%d) must equal n_heads * 64", c->d_model);
@@ -116,18 +118,13 @@ int check_config(const mt_config* c) {
     return MT_OK;
 }
 
-// Split-K layout of the decode attention over T keys.
+// Split-K layout of the decode attention over T keys: about 512 workgroups,
+// chunks of 16 .. 256 positions (a multiple of 16).
 void attn_split(int B, int H, int T, int* nsplit, int* chunk) {
     int want = std::max(1, (512 + B * H - 1) / (B * H));
     int ch = (T + want - 1) / want;
-    ch = std::max(16, (ch + 15) / 16 * 16);
-    int ns = (T + ch - 1) / ch;
-    if (ns > kMaxSplit) {
-        ns = kMaxSplit;
-        ch = ((T + ns - 1) / ns + 15) / 16 * 16;
-        ns = (T + ch - 1) / ch;
-    }
-    *nsplit = ns;
+    ch = std::min(kMaxChunk, std::max(16, (ch + 15) / 16 * 16));
+    *nsplit = (T + ch - 1) / ch;
     *chunk = ch;
 }
 
@@ -149,23 +146,42 @@ int run_layers(mt_model* m, float* x, float* a, float* q, float* att, float* h, 
                bool decode, hipStream_t st) {
     const mt_config& c = m->c;
     const int d = c.d_model, F = c.d_ff, B = c.batch, M = B * R;
+    // with few rows the GEMV applies both LayerNorms itself
+    const bool fuse_ln = gemv_fuses_layernorm(M, d);
     for (int l = 0; l < c.n_layers; ++l) {
         const float* ln = m->ln + (size_t)l * 4 * d;
-        HIP_TRY(launch_layernorm(x, d, ln, ln + d, c.ln_eps, d, M, a, d, st));
         QkvDest dst{q, m->kc, m->vc, d, l, B, c.t_cap, t0, R};
-        HIP_TRY(launch_w4_matmul(a, d, M, m->proj[l * 4 + 0], nullptr, 0, EPI_QKV, &dst, false, st));
-        if (decode) {
+        if (fuse_ln) {
+            HIP_TRY(launch_w4_matmul(x, d, M, m->proj[l * 4 + 0], ln, ln + d, c.ln_eps, nullptr, 0, EPI_QKV, &dst,
+                                     false, st));
+        } else {
+            HIP_TRY(launch_layernorm(x, d, ln, ln + d, c.ln_eps, d, M, a, d, st));
+            HIP_TRY(launch_w4_matmul(a, d, M, m->proj[l * 4 + 0], nullptr, nullptr, 0.f, nullptr, 0, EPI_QKV, &dst,
+                                     false, st));
+        }
+        if (decode && gemv_fuses_layernorm(M, d)) {
+            // split-K attention; the O projection merges the partials
             int ns, ch;
             attn_split(B, c.n_heads, t0 + 1, &ns, &ch);
-            HIP_TRY(launch_attn_decode(q, m->kc, m->vc, l, B, c.n_heads, c.t_cap, t0 + 1, m->part, ns,
-                                       ch, att, st));
+            HIP_TRY(launch_attn_decode(q, m->kc, m->vc, l, B, c.n_heads, c.t_cap, t0 + 1, m->part, ns, ch, st));
+            const AttnParts ap{m->part, c.n_heads, ns};
+            HIP_TRY(launch_w4_matmul(nullptr, d, M, m->proj[l * 4 + 1], nullptr, nullptr, 0.f, x, d, EPI_RESID,
+                                     nullptr, false, st, &ap));
         } else {
             HIP_TRY(launch_attn_prefill(q, m->kc, m->vc, l, B, c.n_heads, c.t_cap, t0, R, att, st));
+            HIP_TRY(launch_w4_matmul(att, d, M, m->proj[l * 4 + 1], nullptr, nullptr, 0.f, x, d, EPI_RESID, nullptr,
+                                     false, st));
         }
-        HIP_TRY(launch_w4_matmul(att, d, M, m->proj[l * 4 + 1], x, d, EPI_RESID, nullptr, false, st));
-        HIP_TRY(launch_layernorm(x, d, ln + 2 * d, ln + 3 * d, c.ln_eps, d, M, a, d, st));
-        HIP_TRY(launch_w4_matmul(a, d, M, m->proj[l * 4 + 2], h, F, EPI_GELU, nullptr, false, st));
-        HIP_TRY(launch_w4_matmul(h, F, M, m->proj[l * 4 + 3], x, d, EPI_RESID, nullptr, false, st));
+        if (fuse_ln) {
+            HIP_TRY(launch_w4_matmul(x, d, M, m->proj[l * 4 + 2], ln + 2 * d, ln + 3 * d, c.ln_eps, h, F, EPI_GELU,
+                                     nullptr, false, st));
+        } else {
+            HIP_TRY(launch_layernorm(x, d, ln + 2 * d, ln + 3 * d, c.ln_eps, d, M, a, d, st));
+            HIP_TRY(launch_w4_matmul(a, d, M, m->proj[l * 4 + 2], nullptr, nullptr, 0.f, h, F, EPI_GELU, nullptr,
+                                     false, st));
+        }
+        HIP_TRY(launch_w4_matmul(h, F, M, m->proj[l * 4 + 3], nullptr, nullptr, 0.f, x, d, EPI_RESID, nullptr,
+                                 false, st));
     }
     return MT_OK;
 }
@@ -451,7 +467,7 @@ int mt_debug_matmul(mt_model* m, int32_t layer, int32_t proj, const float* x, in
     if (layer < 0 || layer >= m->c.n_layers || p > 3)
         return fail(MT_ERR_INVALID_ARG, "mt_debug_matmul: bad layer/projection");
     const Int4Mat& w = m->proj[layer * 4 + p];
-    HIP_TRY(launch_w4_matmul(x, w.K, M, w, y, w.N, EPI_STORE, nullptr, force_gemm || M > 8,
+    HIP_TRY(launch_w4_matmul(x, w.K, M, w, nullptr, nullptr, 0.f, y, w.N, EPI_STORE, nullptr, force_gemm || M > 8,
                              (hipStream_t)stream));
     return MT_OK;
 }

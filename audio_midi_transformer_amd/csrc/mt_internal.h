@@ -39,11 +39,24 @@ hipError_t launch_embed(const int64_t* tokens, int S, const float* prefix, int P
                         int V, int d, int B, float* x, int* err, hipStream_t st);
 hipError_t launch_layernorm(const float* x, long ldx, const float* g, const float* b, float eps,
                             int d, int rows, float* y, long ldy, hipStream_t st);
-hipError_t launch_w4_matmul(const float* x, int ldx, int M, const Int4Mat& w, float* y, int ldy,
-                            Epilogue epi, const QkvDest* qkv, bool force_gemm, hipStream_t st);
+// Split-K partials of the decode attention, [B, H, nsplit, 68] floats.
+struct AttnParts {
+    const float* part;
+    int H;
+    int nsplit;
+};
+
+// y = x . W'^T (+ epilogue).  When ln_g is given, x is replaced by
+// LayerNorm(x) inside the kernel (only where gemv_fuses_layernorm(M, K));
+// when parts is given, x is the attention output merged from the partials
+// (x is not read; GEMV path only).
+hipError_t launch_w4_matmul(const float* x, int ldx, int M, const Int4Mat& w, const float* ln_g,
+                            const float* ln_b, float eps, float* y, int ldy, Epilogue epi, const QkvDest* qkv,
+                            bool force_gemm, hipStream_t st, const AttnParts* parts = nullptr);
+bool gemv_fuses_layernorm(int M, int K);
+// Writes the split-K partials only; the O projection merges them.
 hipError_t launch_attn_decode(const float* q, const float* kc, const float* vc, int layer, int B,
-                              int H, int t_cap, int T, float* part, int nsplit, int chunk,
-                              float* out, hipStream_t st);
+                              int H, int t_cap, int T, float* part, int nsplit, int chunk, hipStream_t st);
 hipError_t launch_attn_prefill(const float* q, const float* kc, const float* vc, int layer, int B,
                                int H, int t_cap, int t0, int R, float* out, hipStream_t st);
 hipError_t launch_lm_head(const float* z, int B, const float* w, int V, int d, float* logits,

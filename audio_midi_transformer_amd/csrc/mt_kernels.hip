@@ -14,6 +14,8 @@
 //                              ONNX conversion page (greedy decoding)
 #include <hip/hip_runtime.h>
 #include <math.h>
+
+#include <algorithm>
 #include <stdint.h>
 
 #include "mt_internal.h"
@@ -40,32 +42,6 @@ __device__ __forceinline__ float group_sum(float v) {
 
 __device__ __forceinline__ float gelu_erf(float x) {
     return 0.5f * x * (1.0f + erff(x * 0.70710678118654752440f));
-}
-
-// Dot product of one 32-weight group with 32 activations.
-// Byte j of the group holds input 2j in its low nibble and 2j+1 in its high
-// nibble; the stored nibble is code + 8.  Returns sum_k (u_k - 8) * x_k,
-// evaluated as sum_k u_k x_k - 8 sum_k x_k.
-__device__ __forceinline__ float group_dot(uint4 w, const float* __restrict__ x) {
-    const float4* x4 = reinterpret_cast<const float4*>(x);
-    const unsigned wd[4] = {w.x, w.y, w.z, w.w};
-    float acc = 0.f, xs = 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const float4 xa = x4[2 * j], xb = x4[2 * j + 1];
-        const unsigned lo = wd[j] & 0x0F0F0F0Fu;
-        const unsigned hi = (wd[j] >> 4) & 0x0F0F0F0Fu;
-        acc = fmaf((float)(lo & 0xFFu), xa.x, acc);
-        acc = fmaf((float)(hi & 0xFFu), xa.y, acc);
-        acc = fmaf((float)((lo >> 8) & 0xFFu), xa.z, acc);
-        acc = fmaf((float)((hi >> 8) & 0xFFu), xa.w, acc);
-        acc = fmaf((float)((lo >> 16) & 0xFFu), xb.x, acc);
-        acc = fmaf((float)((hi >> 16) & 0xFFu), xb.y, acc);
-        acc = fmaf((float)(lo >> 24), xb.z, acc);
-        acc = fmaf((float)(hi >> 24), xb.w, acc);
-        xs += ((xa.x + xa.y) + (xa.z + xa.w)) + ((xb.x + xb.y) + (xb.z + xb.w));
-    }
-    return fmaf(-8.f, xs, acc);
 }
 
 struct EpiArgs {
@@ -156,45 +132,208 @@ __global__ __launch_bounds__(256) void k_layernorm(const float* __restrict__ x, 
     for (int j = tid; j < d; j += 256, ++n) yr[j] = (v[n] - mean) * rstd * g[j] + bta[j];
 }
 
-// ---------------------------------------------------------------- INT4 GEMV (M <= 8)
+// Decode-attention partial of one (sequence, head, split): max score, sum of
+// exp, two pad floats, then sum of exp * V (16-byte aligned).
+constexpr int PART = 68;
+constexpr int PART_ACC = 4;
 
-// Lane group of LPR lanes owns one output row; lane r of the group holds
-// groups r, r + LPR, ... (cpl of them) of that row.  The group dot products
-// are summed over the LPR lanes with cross-lane adds.
-template <int LPR>
-__global__ __launch_bounds__(256) void k_gemv_w4(const float* __restrict__ X, int ldx, int M, int K,
-                                                 const uint8_t* __restrict__ Wq,
-                                                 const float* __restrict__ Ws, int N, int cpl,
-                                                 float* __restrict__ Y, int ldy, EpiArgs ep) {
-    constexpr int RPW = 64 / LPR;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int sub = lane / LPR, lr = lane % LPR;
-    const int row = (blockIdx.x * 4 + wave) * RPW + sub;
-    const bool valid = row < N;
+// ---------------------------------------------------------------- INT4 GEMV (M <= 8) on MFMA
+
+// Position of element k of an activation row in LDS: the eight 16-byte
+// sub-blocks of each 32-element group are rotated by the group index, so the
+// lanes of a row group (consecutive groups) read different banks.
+__device__ __forceinline__ int xswz(int k) {
+    const int c = k >> 5, j = (k >> 2) & 7;
+    return (c << 5) + (((j + c) & 7) << 2) + (k & 3);
+}
+
+constexpr int GV_MAXSPAN = 2048;  // activation columns staged in LDS at a time
+constexpr int GV_M = 8;           // activation rows held in LDS
+
+// Y[m, n] = sum_k W'[n, k] x[m, k] for M <= 8 rows with v_mfma_f32_16x16x4f32
+// (A = 16 output rows of W' x 4 columns, B = 4 columns x 16 activation rows,
+// 8 of them used).  x is read from X, or (part != NULL) merged from
+// decode-attention partials of H heads and ns splits; optionally replaced
+// by LayerNorm(x) (gain ln_g, bias ln_b, biased variance; whole rows).
+// Workgroup (n block, k split): 16 output rows over columns
+// [ks * kspan, (ks + 1) * kspan), staged through LDS transposed ([k][8])
+// in chunks of <= GV_MAXSPAN columns; the four waves take interleaved
+// quarters of each chunk's groups and their 16 x 16 tiles are summed in
+// LDS.  With more than one k split the results are added to Y atomically
+// (the += epilogue only).  Lane l converts weight W'[n0 + l % 16][k + l / 16]
+// as s * u - 8 s (one rounding, equal to (u - 8) * s).
+__global__ __launch_bounds__(256) void k_gemv_w4(const float* __restrict__ X, int ldx, int M, int K, int kspan,
+                                                 const float* __restrict__ ln_g, const float* __restrict__ ln_b,
+                                                 float eps, const float* __restrict__ part, int H, int ns,
+                                                 const uint8_t* __restrict__ Wq, const float* __restrict__ Ws,
+                                                 int N, float* __restrict__ Y, int ldy, EpiArgs ep) {
+    extern __shared__ float xt[];  // [GV_M][chunk + 4]
+    __shared__ float dred[4][16][17];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n0 = blockIdx.x * 16;
     const int G = K / 32;
-    uint4 w[4];
-    float s[4];
+    const int kb0 = blockIdx.y * kspan;
+    const int row = n0 + (lane & 15), kq = lane >> 4;
+    const bool rvalid = row < N;
+    const int bm = lane & 15;  // activation row this lane feeds into B
+    const int xm = tid >> 5, xr = tid & 31;  // staging: row, thread in row (32 per row)
+    const bool xrow = xm < M;
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+    for (int c0 = 0; c0 < kspan; c0 += GV_MAXSPAN) {
+        const int cw = min(GV_MAXSPAN, kspan - c0);  // columns in this chunk
+        const int XS = cw + 4;                       // LDS row stride: B reads hit 32 banks
+        const int kbase = kb0 + c0;
+        const int gch = cw / 32, gbase = kbase / 32;
+        // this wave's groups of the chunk (g = wave, wave + 4, ...; ngw of
+        // them, uniform over the wave): all requested before the activations
+        // are staged
+        const int wv = __builtin_amdgcn_readfirstlane(wave);
+        const int ngw = (gch - wv + 3) / 4;
+        uint4 wq[GV_MAXSPAN / 128];
+        float sc[GV_MAXSPAN / 128];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        w[j] = make_uint4(0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u);
-        s[j] = 0.f;
-        const int c = lr + LPR * j;
-        if (valid && j < cpl) {
-            w[j] = *reinterpret_cast<const uint4*>(Wq + (size_t)row * (K / 2) + (size_t)c * 16);
-            s[j] = Ws[(size_t)row * G + c];
-        }
-    }
-    for (int m = 0; m < M; ++m) {
-        float acc = 0.f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            if (j < cpl) {
-                const int c = lr + LPR * j;
-                acc = fmaf(s[j], group_dot(w[j], X + (size_t)m * ldx + (size_t)c * 32), acc);
+        for (int i = 0; i < GV_MAXSPAN / 128; ++i) {
+            wq[i] = make_uint4(0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u);
+            sc[i] = 0.f;
+            if (i < ngw && rvalid) {
+                const int g = gbase + wv + 4 * i;
+                wq[i] = *reinterpret_cast<const uint4*>(Wq + (size_t)row * (K / 2) + (size_t)g * 16);
+                sc[i] = Ws[(size_t)row * G + g];
             }
         }
-        acc = group_sum<LPR>(acc);
-        if (valid && lr == 0) epilogue(ep, Y, ldy, m, row, acc);
+        if (c0) __syncthreads();
+        // ---- stage x[m][kbase .. kbase + cw) into xt[m][k]
+        const int nf4 = (cw / 4 + 31) / 32;
+        if (part) {
+            // attention output merged from the partials: first the weight
+            // e^(m_s - M) / sum_s e^(m_s - M) l_s of every (row, head, split),
+            // one (row, head) per thread, then the weighted sums of acc_s
+            const int nh = cw / 64, h0 = kbase / 64;
+            float* wts = xt + (size_t)XS * GV_M;  // [M][nh][ns]
+            if (tid < M * nh) {
+                const int m = tid / nh, hl = tid % nh;
+                const float* pp = part + (size_t)(m * H + h0 + hl) * ns * PART;
+                float* wr = wts + (size_t)(m * nh + hl) * ns;
+                float Mx = -INFINITY;
+#pragma unroll 8
+                for (int sp = 0; sp < ns; ++sp) {
+                    wr[sp] = pp[sp * PART];
+                    Mx = fmaxf(Mx, wr[sp]);
+                }
+                float L = 0.f;
+#pragma unroll 8
+                for (int sp = 0; sp < ns; ++sp) {
+                    const float e = wr[sp] == -INFINITY ? 0.f : expf(wr[sp] - Mx);
+                    wr[sp] = e;
+                    L = fmaf(e, pp[sp * PART + 1], L);
+                }
+                const float inv = 1.0f / L;
+                for (int sp = 0; sp < ns; ++sp) wr[sp] *= inv;
+            }
+            __syncthreads();
+            for (int i = 0; i < nf4; ++i) {
+                const int k = (xr + i * 32) * 4;
+                if (k < cw) {
+                    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+                    if (xrow) {
+                        const int hl = k >> 6, j = k & 63;
+                        const float* pp = part + (size_t)(xm * H + h0 + hl) * ns * PART + PART_ACC + j;
+                        const float* wr = wts + (size_t)(xm * nh + hl) * ns;
+#pragma unroll 8
+                        for (int sp = 0; sp < ns; ++sp) {
+                            const float4 a = *reinterpret_cast<const float4*>(pp + sp * PART);
+                            const float wgt = wr[sp];
+                            v.x = fmaf(wgt, a.x, v.x);
+                            v.y = fmaf(wgt, a.y, v.y);
+                            v.z = fmaf(wgt, a.z, v.z);
+                            v.w = fmaf(wgt, a.w, v.w);
+                        }
+                    }
+                    *reinterpret_cast<float4*>(xt + xm * XS + k) = v;
+                }
+            }
+        } else {
+            float4 v[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int k = (xr + i * 32) * 4;
+                v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (i < nf4 && k < cw && xrow)
+                    v[i] = *reinterpret_cast<const float4*>(X + (size_t)xm * ldx + kbase + k);
+            }
+            if (ln_g) {  // one chunk holds the whole row
+                float sm = 0.f;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) sm += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+                const float mean = group_sum<32>(sm) / (float)K;
+                float q = 0.f;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int k = (xr + i * 32) * 4;
+                    if (i < nf4 && k < cw) {
+                        const float a0 = v[i].x - mean, a1 = v[i].y - mean, a2 = v[i].z - mean, a3 = v[i].w - mean;
+                        q = fmaf(a0, a0, fmaf(a1, a1, fmaf(a2, a2, fmaf(a3, a3, q))));
+                    }
+                }
+                const float var = group_sum<32>(q) / (float)K;
+                const float rstd = 1.0f / sqrtf(var + eps);
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int k = (xr + i * 32) * 4;
+                    if (i < nf4 && k < cw && xrow) {
+                        const float4 gg = *reinterpret_cast<const float4*>(ln_g + k);
+                        const float4 bb = *reinterpret_cast<const float4*>(ln_b + k);
+                        v[i].x = (v[i].x - mean) * rstd * gg.x + bb.x;
+                        v[i].y = (v[i].y - mean) * rstd * gg.y + bb.y;
+                        v[i].z = (v[i].z - mean) * rstd * gg.z + bb.z;
+                        v[i].w = (v[i].w - mean) * rstd * gg.w + bb.w;
+                    }
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int k = (xr + i * 32) * 4;
+                if (i < nf4 && k < cw) *reinterpret_cast<float4*>(xt + xm * XS + k) = v[i];
+            }
+        }
+        __syncthreads();
+        // ---- MFMA over this wave's groups, alternate groups into two
+        // accumulators.  Column 4 s + kq of a group: byte 2 s + kq / 2, low
+        // nibble for even kq.  Lanes feeding B columns 8..15 read row
+        // bm - 8 and pass zero.
+        const int sh = (kq >> 1) * 8 + (kq & 1) * 4;
+        const bool bvalid = bm < GV_M;
+        const float* xb = xt + (bm & (GV_M - 1)) * XS + kq;
+#pragma unroll
+        for (int i = 0; i < GV_MAXSPAN / 128; ++i) {
+            if (i < ngw) {
+                const int gi = wv + 4 * i;
+                const float s8 = -8.f * sc[i];
+                const unsigned wd[4] = {wq[i].x, wq[i].y, wq[i].z, wq[i].w};
+                float bv[8];
+#pragma unroll
+                for (int s = 0; s < 8; ++s) bv[s] = xb[gi * 32 + 4 * s];
+#pragma unroll
+                for (int s = 0; s < 8; ++s) {
+                    const float u = (float)((wd[s >> 1] >> (sh + 16 * (s & 1))) & 15u);
+                    const float a = fmaf(sc[i], u, s8);
+                    const float b = bvalid ? bv[s] : 0.f;
+                    if (i & 1) acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc1, 0, 0, 0);
+                    else acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc0, 0, 0, 0);
+                }
+            }
+        }
+    }
+    const f32x4 acc = acc0 + acc1;
+    // ---- sum the four waves' tiles; lane l holds D[4 (l / 16) + r][l % 16]
+#pragma unroll
+    for (int r = 0; r < 4; ++r) dred[wave][4 * kq + r][lane & 15] = acc[r];
+    __syncthreads();
+    const int n = tid >> 4, m = tid & 15;
+    if (m < M && n0 + n < N) {
+        const float v = (dred[0][n][m] + dred[1][n][m]) + (dred[2][n][m] + dred[3][n][m]);
+        if (gridDim.y > 1) atomicAdd(Y + (size_t)m * ldy + n0 + n, v);
+        else epilogue(ep, Y, ldy, m, n0 + n, v);
     }
 }
 
@@ -288,89 +427,85 @@ __global__ __launch_bounds__(256) void k_gemm_w4(const float* __restrict__ X, in
 // ---------------------------------------------------------------- decode attention
 
 // Split-K decode attention.  Workgroup (split, h, b) covers positions
-// [split * chunk, min(T, (split + 1) * chunk)) of head h of sequence b and
-// writes the unnormalised partial (max score, sum of exp, sum of exp * V).
-// 16 lane groups of 16 lanes; a group handles one position at a time, each
-// lane 4 of the 64 dimensions.
-constexpr int PART = 68;  // floats per partial: m, l, acc[64], pad
-
+// [split * chunk, min(T, (split + 1) * chunk)), chunk <= 256, of head h of
+// sequence b and writes the unnormalised partial: max score, sum of exp, and
+// sum of exp * V at offset PART_ACC.  16 lane groups of 16 lanes: group g
+// takes positions g, g + 16, ... of the split, lane l of the group the
+// dimensions 4l .. 4l + 3.  Every K and V row of the split is requested
+// before the first is used.  The splits are merged where the attention
+// output is read (the O projection's activation staging).
 __global__ __launch_bounds__(256) void k_attn_decode(const float* __restrict__ q,
                                                      const float* __restrict__ kc,
                                                      const float* __restrict__ vc, int layer,
                                                      int B, int H, int t_cap, int T, int chunk,
                                                      float* __restrict__ part) {
-    __shared__ float sm[16], sl[16];
-    __shared__ float sacc[16][64];
-    const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    __shared__ float red[8];
+    __shared__ float sacc[4][64];
+    const int split = blockIdx.x, ns = gridDim.x, h = blockIdx.y, b = blockIdx.z;
     const int d = H * 64;
-    const int tid = threadIdx.x, g = tid >> 4, ql = tid & 15;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = tid >> 4, ql = tid & 15;
     const float4 q4 = *reinterpret_cast<const float4*>(q + (size_t)b * d + h * 64 + ql * 4);
     const size_t base = ((size_t)(layer * B + b) * t_cap) * d + h * 64 + ql * 4;
-    const int t_begin = split * chunk;
-    const int t_end = min(T, t_begin + chunk);
-    float m = -INFINITY, l = 0.f;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int t = t_begin + g; t < t_end; t += 16) {
-        const float4 k4 = *reinterpret_cast<const float4*>(kc + base + (size_t)t * d);
-        const float4 v4 = *reinterpret_cast<const float4*>(vc + base + (size_t)t * d);
-        float s = q4.x * k4.x + q4.y * k4.y + q4.z * k4.z + q4.w * k4.w;
+    const int t0 = split * chunk;
+    const int n = max(0, min(T - t0, chunk));
+    float4 k4[16], v4[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int t = g + 16 * i;
+        k4[i] = v4[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (t < n) {
+            k4[i] = *reinterpret_cast<const float4*>(kc + base + (size_t)(t0 + t) * d);
+            v4[i] = *reinterpret_cast<const float4*>(vc + base + (size_t)(t0 + t) * d);
+        }
+    }
+    float sc[16];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        float s = q4.x * k4[i].x + q4.y * k4[i].y + q4.z * k4[i].z + q4.w * k4[i].w;
         s = group_sum<16>(s) * 0.125f;
-        const float mn = fmaxf(m, s);
-        const float corr = expf(m - mn);
-        const float p = expf(s - mn);
-        l = fmaf(l, corr, p);
-        acc.x = fmaf(acc.x, corr, p * v4.x);
-        acc.y = fmaf(acc.y, corr, p * v4.y);
-        acc.z = fmaf(acc.z, corr, p * v4.z);
-        acc.w = fmaf(acc.w, corr, p * v4.w);
-        m = mn;
+        sc[i] = g + 16 * i < n ? s : -INFINITY;
+        mx = fmaxf(mx, sc[i]);
     }
-    if (ql == 0) {
-        sm[g] = m;
-        sl[g] = l;
-    }
-    sacc[g][ql * 4 + 0] = acc.x;
-    sacc[g][ql * 4 + 1] = acc.y;
-    sacc[g][ql * 4 + 2] = acc.z;
-    sacc[g][ql * 4 + 3] = acc.w;
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    if (lane == 0) red[wave] = mx;
     __syncthreads();
+    const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    float ls = 0.f;
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (M != -INFINITY) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const float p = sc[i] == -INFINITY ? 0.f : expf(sc[i] - M);
+            ls += p;
+            a.x = fmaf(p, v4[i].x, a.x);
+            a.y = fmaf(p, v4[i].y, a.y);
+            a.z = fmaf(p, v4[i].z, a.z);
+            a.w = fmaf(p, v4[i].w, a.w);
+        }
+    }
+#pragma unroll
+    for (int o = 16; o <= 32; o <<= 1) {
+        ls += __shfl_xor(ls, o);
+        a.x += __shfl_xor(a.x, o);
+        a.y += __shfl_xor(a.y, o);
+        a.z += __shfl_xor(a.z, o);
+        a.w += __shfl_xor(a.w, o);
+    }
+    if (lane < 16) {
+        *reinterpret_cast<float4*>(&sacc[wave][ql * 4]) = a;
+        if (ql == 0) red[4 + wave] = ls;
+    }
+    __syncthreads();
+    float* pp = part + ((size_t)(b * H + h) * ns + split) * PART;
     if (tid < 64) {
-        float M = -INFINITY;
-        for (int i = 0; i < 16; ++i) M = fmaxf(M, sm[i]);
-        float L = 0.f, A = 0.f;
-        if (M != -INFINITY) {
-            for (int i = 0; i < 16; ++i) {
-                if (sm[i] == -INFINITY) continue;
-                const float w = expf(sm[i] - M);
-                L = fmaf(w, sl[i], L);
-                A = fmaf(w, sacc[i][tid], A);
-            }
-        }
-        float* out = part + ((size_t)(b * H + h) * gridDim.x + split) * PART;
+        pp[PART_ACC + tid] = (sacc[0][tid] + sacc[1][tid]) + (sacc[2][tid] + sacc[3][tid]);
         if (tid == 0) {
-            out[0] = M;
-            out[1] = L;
+            pp[0] = M;
+            pp[1] = (red[4] + red[5]) + (red[6] + red[7]);
         }
-        out[2 + tid] = A;
     }
-}
-
-// Merge the splits of one (b, h): out = sum_s e^(m_s - M) acc_s / sum_s e^(m_s - M) l_s.
-__global__ __launch_bounds__(64) void k_attn_merge(const float* __restrict__ part, int nsplit, int H,
-                                                   float* __restrict__ out) {
-    const int h = blockIdx.x, b = blockIdx.y, j = threadIdx.x;
-    const float* p = part + (size_t)(b * H + h) * nsplit * PART;
-    float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, p[s * PART]);
-    float L = 0.f, A = 0.f;
-    for (int s = 0; s < nsplit; ++s) {
-        const float ms = p[s * PART];
-        if (ms == -INFINITY) continue;
-        const float w = expf(ms - M);
-        L = fmaf(w, p[s * PART + 1], L);
-        A = fmaf(w, p[s * PART + 2 + j], A);
-    }
-    out[(size_t)b * H * 64 + h * 64 + j] = A / L;
 }
 
 // ---------------------------------------------------------------- prefill attention
@@ -545,57 +680,70 @@ hipError_t launch_layernorm(const float* x, long ldx, const float* g, const floa
     return hipGetLastError();
 }
 
-static bool pick_gemv(int K, int* lpr, int* cpl) {
-    const int G = K / 32;
-    for (int c = 1; c <= 4; ++c) {
-        if (G % c) continue;
-        const int l = G / c;
-        if (l > 64 || (l & (l - 1))) continue;
-        *lpr = l;
-        *cpl = c;
-        return true;
-    }
-    return false;
+constexpr size_t kGemvMaxLds = 152 * 1024;  // dynamic LDS of the GEMV (static: 4.3 KB)
+
+// GEMV plan: k split (grid.y) and columns per split.  The += epilogue
+// splits K so that about 256 workgroups run; the other epilogues keep one
+// split per output block.
+static void plan_gemv(int N, int K, Epilogue epi, int granule, int* ksplit, int* kspan) {
+    const int G = K / granule, nblk = (N + 15) / 16;
+    int want = epi == EPI_RESID ? std::max(1, 256 / nblk) : 1;
+    want = std::max(want, epi == EPI_RESID ? (K + GV_MAXSPAN - 1) / GV_MAXSPAN : 1);
+    int ks = 1;
+    for (int c = std::min(want, G); c >= 1; --c)
+        if (G % c == 0) {
+            ks = c;
+            break;
+        }
+    *ksplit = ks;
+    *kspan = K / ks;
 }
 
-hipError_t launch_w4_matmul(const float* x, int ldx, int M, const Int4Mat& w, float* y, int ldy,
-                            Epilogue epi, const QkvDest* qkv, bool force_gemm, hipStream_t st) {
+hipError_t launch_w4_matmul(const float* x, int ldx, int M, const Int4Mat& w, const float* ln_g,
+                            const float* ln_b, float eps, float* y, int ldy, Epilogue epi, const QkvDest* qkv,
+                            bool force_gemm, hipStream_t st, const AttnParts* parts) {
+    const AttnParts ap = parts ? *parts : AttnParts{nullptr, 0, 0};
     EpiArgs ep{};
     ep.epi = epi;
     if (qkv) ep.qkv = *qkv;
-    int lpr = 0, cpl = 0;
-    if (!force_gemm && M <= 8 && pick_gemv(w.K, &lpr, &cpl)) {
-        const int rows_per_block = 4 * (64 / lpr);
-        const dim3 grid((w.N + rows_per_block - 1) / rows_per_block);
-#define MT_GEMV(L)                                                                                  \
-    case L:                                                                                         \
-        hipLaunchKernelGGL(k_gemv_w4<L>, grid, dim3(256), 0, st, x, ldx, M, w.K, w.q, w.s, w.N, cpl, \
-                           y, ldy, ep);                                                             \
-        break;
-        switch (lpr) {
-            MT_GEMV(1)
-            MT_GEMV(2)
-            MT_GEMV(4)
-            MT_GEMV(8)
-            MT_GEMV(16)
-            MT_GEMV(32)
-            MT_GEMV(64)
-            default: return hipErrorInvalidValue;
+    if (!force_gemm && M >= 1 && M <= GV_M) {
+        if (ln_g && w.K > GV_MAXSPAN) return hipErrorInvalidValue;
+        if (ap.part && (ln_g || ap.H * 64 != w.K)) return hipErrorInvalidValue;
+        int ksplit, kspan;
+        // merged partials: whole heads (64 columns) per k split
+        plan_gemv(w.N, w.K, ln_g ? EPI_STORE : epi, ap.part ? 64 : 32, &ksplit, &kspan);
+        // activation rows (stride span + 4); merged partials also need their
+        // weights [M][heads][splits]
+        const int span = std::min(kspan, GV_MAXSPAN);
+        const size_t wts = ap.part ? (size_t)M * (span / 64) * ap.nsplit : 0;
+        if (ap.part && (span % 64 || (int)(M * (span / 64)) > 256)) return hipErrorInvalidValue;
+        const size_t lds = sizeof(float) * ((size_t)(span + 4) * GV_M + wts);
+        if (lds > kGemvMaxLds) return hipErrorInvalidValue;
+        static bool attr = false;
+        if (!attr) {
+            hipError_t e = hipFuncSetAttribute((const void*)k_gemv_w4, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               (int)kGemvMaxLds);
+            if (e != hipSuccess) return e;
+            attr = true;
         }
-#undef MT_GEMV
+        const dim3 grid((w.N + 15) / 16, ksplit);
+        hipLaunchKernelGGL(k_gemv_w4, grid, dim3(256), lds, st, x, ldx, M, w.K, kspan, ln_g, ln_b, eps, ap.part,
+                           ap.H, ap.nsplit, w.q, w.s, w.N, y, ldy, ep);
         return hipGetLastError();
     }
+    if (ln_g || ap.part) return hipErrorInvalidValue;  // the GEMM path takes plain rows
     const dim3 grid((w.N + GT - 1) / GT, (M + GT - 1) / GT);
     hipLaunchKernelGGL(k_gemm_w4, grid, dim3(256), 0, st, x, ldx, M, w.K, w.q, w.s, w.N, y, ldy, ep);
     return hipGetLastError();
 }
 
+bool gemv_fuses_layernorm(int M, int K) { return M >= 1 && M <= GV_M && K <= GV_MAXSPAN; }
+
 hipError_t launch_attn_decode(const float* q, const float* kc, const float* vc, int layer, int B,
-                              int H, int t_cap, int T, float* part, int nsplit, int chunk,
-                              float* out, hipStream_t st) {
+                              int H, int t_cap, int T, float* part, int nsplit, int chunk, hipStream_t st) {
+    if (chunk > 256 || nsplit * chunk < T) return hipErrorInvalidValue;
     hipLaunchKernelGGL(k_attn_decode, dim3(nsplit, H, B), dim3(256), 0, st, q, kc, vc, layer, B, H,
                        t_cap, T, chunk, part);
-    hipLaunchKernelGGL(k_attn_merge, dim3(H, B), dim3(64), 0, st, part, nsplit, H, out);
     return hipGetLastError();
 }
 

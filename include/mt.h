@@ -55,7 +55,7 @@ typedef struct {
     int32_t vocab;     /* V (1393 for MT3 tokens) */
     int32_t group;     /* must be 32 */
     int32_t batch;     /* B sequences that advance in lockstep, 1..64 */
-    int32_t t_cap;     /* fixed cache capacity per sequence (positions) */
+    int32_t t_cap;     /* fixed cache capacity per sequence (positions), 1..16384 */
     float ln_eps;      /* LayerNorm epsilon (1e-5) */
     uint32_t flags;    /* must be 0 */
 } mt_config;
