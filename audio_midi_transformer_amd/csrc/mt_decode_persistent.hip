@@ -336,6 +336,16 @@ __device__ __forceinline__ void ll_put_rep(uint64_t* base, int n, int i, float v
     for (int r = 0; r < REP; ++r) ll_put(base + (size_t)r * n + i, v, ep);
 }
 
+// Publish nv consecutive words i0 .. i0 + nv - 1 of a broadcast vector of n
+// words to all REP copies.  The values were staged in LDS (stg) by the lanes
+// that computed them; thread t then writes word t % nv of copy t / nv, so
+// each copy goes out as contiguous stores of one wave instead of scattered
+// single words.
+__device__ __forceinline__ void publish_rep(uint64_t* base, int n, int i0, const float* stg, int nv, uint32_t ep) {
+    lds_barrier();
+    for (int t = threadIdx.x; t < nv * REP; t += NT) ll_put(base + (size_t)(t / nv) * n + i0 + t % nv, stg[t % nv], ep);
+}
+
 // The copy of a broadcast vector this workgroup reads (its XCD's).
 __device__ __forceinline__ const uint64_t* rep_of(const uint64_t* base, int n) {
     return base + (size_t)(blockIdx.x % REP) * n;
@@ -763,8 +773,9 @@ __device__ __forceinline__ bool phase_b(const Args& a, const Lds<D, F>& S, uint6
 #pragma unroll
     for (int p = 0; p < C::NP_O; ++p) {
         const int rr = out_row<C::LPR_D>(p);
-        if (rr >= 0 && rr < C::O_ROWS && orow + rr < D) ll_put_rep(X + C::XB_O, D, orow + rr, o[p], ep);
+        if (rr >= 0 && rr < C::O_ROWS && orow + rr < D) S.comb[rr] = o[p];
     }
+    publish_rep(X + C::XB_O, D, orow, S.comb, min(C::O_ROWS, D - orow), ep);
     stamp(a, l, 7);
     return true;
 }
@@ -785,8 +796,9 @@ __device__ __forceinline__ bool phase_c(const Args& a, const Lds<D, F>& S, uint6
 #pragma unroll
     for (int p = 0; p < C::NP_UP; ++p) {
         const int rr = out_row<C::LPR_D>(p);
-        if (rr >= 0 && rr < C::UP_ROWS && urow + rr < F) ll_put_rep(X + C::XC, F, urow + rr, gelu_erf(o[p]), ep);
+        if (rr >= 0 && rr < C::UP_ROWS && urow + rr < F) S.comb[rr] = gelu_erf(o[p]);
     }
+    publish_rep(X + C::XC, F, urow, S.comb, max(0, min(C::UP_ROWS, F - urow)), ep);
     stamp(a, l, 9);
     return true;
 }
@@ -805,8 +817,9 @@ __device__ __forceinline__ bool phase_d(const Args& a, const Lds<D, F>& S, uint6
 #pragma unroll
     for (int p = 0; p < C::NP_DN; ++p) {
         const int rr = out_row<C::LPR_F>(p);
-        if (rr >= 0 && rr < C::DN_ROWS && drow + rr < D) ll_put_rep(X + C::XD, D, drow + rr, o[p], ep);
+        if (rr >= 0 && rr < C::DN_ROWS && drow + rr < D) S.comb[rr] = o[p];
     }
+    publish_rep(X + C::XD, D, drow, S.comb, min(C::DN_ROWS, D - drow), ep);
     stamp(a, l, 11);
     return true;
 }
