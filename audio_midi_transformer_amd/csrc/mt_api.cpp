@@ -369,7 +369,7 @@ int mt_decode_step(mt_model* m, const int64_t* token, float* logits, int64_t* ne
         return fail(MT_ERR_CACHE_FULL, "mt_decode_step: cache full at position %d (capacity %d)", m->t_past, c.t_cap);
     hipStream_t st = (hipStream_t)stream;
     const bool persistent = m->persistent_ok && m->decode_path != MT_DECODE_KERNELS &&
-                            m->t_past <= persistent_max_position();
+                            m->t_past <= persistent_max_position(c.d_model, c.d_ff);
     if (persistent) {
         PersistentArgs pa{};
         pa.L = c.n_layers; pa.d = c.d_model; pa.H = c.n_heads; pa.F = c.d_ff; pa.V = c.vocab;

@@ -26,11 +26,11 @@
 // consumed.
 //
 // Roles (a table built on the host, see build_roles):
-//   attention WGs  (head h, split s), 8 splits per head, all on one XCD.
-//                  Each recomputes q_h and the softmax partial over its
-//                  chunk of cached positions; splits 1..7 publish
-//                  (max, sum, acc[64]); split 0 (the head leader) merges them
-//                  with the new position and publishes attn_h.
+//   attention WGs  (head h, split s), 16 splits per head at small width, 8
+//                  otherwise, all on one XCD.  Each recomputes q_h and the
+//                  softmax partial over its chunk of cached positions; splits
+//                  1.. publish (max, sum, acc[64]); split 0 (the head leader)
+//                  merges them with the new position and publishes attn_h.
 //   free WGs       the rest: the new K/V rows of the fused projection (to the
 //                  cache slot T_past and to the exchange).
 //   all WGs        D/256 rows of O, F/256 rows of FFN-up + GELU and D/256
@@ -54,7 +54,6 @@ namespace pd {
 constexpr int NT = 256;      // threads per workgroup
 constexpr int NWG = 256;     // workgroups (one per CU)
 constexpr int NXCD = 8;      // workgroup w runs on XCD w % 8
-constexpr int ATT_S = 8;     // attention splits per head
 constexpr int REP = NXCD;    // copies of each broadcast vector, one per XCD
 constexpr int PW = 66;       // words per attention partial: m, l, acc[64]
 constexpr int MAXPOS = 256;  // cached positions per attention workgroup (LDS)
@@ -91,6 +90,11 @@ struct Cfg {
     static constexpr int GD = D / 32, GF = F / 32;
     static constexpr int LPR_D = lpr_for(D), CPL_D = GD / (LPR_D ? LPR_D : 1), RP_D = NT / (LPR_D ? LPR_D : 1);
     static constexpr int LPR_F = lpr_for(F), CPL_F = GF / (LPR_F ? LPR_F : 1), RP_F = NT / (LPR_F ? LPR_F : 1);
+    // attention splits per head: 16 where that leaves at least 64 workgroups
+    // for the new K/V rows, else 8 (16 splits at medium width measured slower:
+    // the q projection is recomputed by twice as many workgroups and the head
+    // merge gathers twice as many partials)
+    static constexpr int ATT_S = H * 16 + 64 <= NWG ? 16 : 8;
     static constexpr int NATT = H * ATT_S;
     static constexpr int NFREE = NWG - NATT;
     static constexpr int KV_ROWS = cdiv(2 * D, NFREE);
@@ -122,14 +126,14 @@ struct Cfg {
     static constexpr int OFF_ACT = OFF_U;                 //   act [D]
     static constexpr int OFF_QH = OFF_ACT + D;            //   q_h [64]
     static constexpr int OFF_SC = OFF_QH + 64;            //   scores [MAXPOS]
-    static constexpr int OFF_PART = OFF_SC + MAXPOS;      //   own partial [PW] + gathered [7][PW] + kv_new [128]
-    static constexpr int OFF_COMB = rup(OFF_PART + 8 * PW + 128, 4);  // [4][64] scratch
+    static constexpr int OFF_PART = OFF_SC + MAXPOS;      //   own partial [PW] + gathered [ATT_S-1][PW] + kv_new [128]
+    static constexpr int OFF_COMB = rup(OFF_PART + ATT_S * PW + 128, 4);  // [4][64] scratch
     static constexpr int OFF_RED = rup(cmax(OFF_U + F, OFF_COMB + 4 * 64), 4);
     static constexpr int OFF_FLAG = OFF_RED + 16;
     static constexpr int LDS_FLOATS = OFF_FLAG + 16;
     static_assert(D % 64 == 0 && F % 32 == 0, "widths");
     static_assert(LPR_D > 0 && LPR_F > 0, "width has no GEMV lane mapping");
-    static_assert(NFREE > 0 && KV_ROWS * NFREE >= 2 * D, "K/V rows need workgroups without attention duty");
+    static_assert(NFREE >= 64 && KV_ROWS * NFREE >= 2 * D, "K/V rows need workgroups without attention duty");
     static_assert(LDS_FLOATS * 4 <= 160 * 1024, "LDS budget");
 };
 
@@ -713,8 +717,8 @@ struct Lds {
         qh = lds + C::OFF_QH;
         sc = lds + C::OFF_SC;
         own = lds + C::OFF_PART;  // own partial [PW]
-        gpart = own + PW;         // splits 1..7 [7][PW]
-        knew = gpart + 7 * PW;    // [64]
+        gpart = own + PW;                   // splits 1 .. ATT_S-1 [ATT_S-1][PW]
+        knew = gpart + (C::ATT_S - 1) * PW; // [64]
         vnew = knew + 64;         // [64]
         comb = lds + C::OFF_COMB; // [4][64] scratch
         red = lds + C::OFF_RED;
@@ -849,6 +853,7 @@ __device__ __forceinline__ bool attention_role(const Args& a, const Lds<D, F>& S
     using O = Off<D, F>;
     const uint32_t ep = a.epoch;
     const int tid = threadIdx.x;
+    constexpr int AS = C::ATT_S;
     const bool leader = role.split == 0;
     const int h = role.head;
     const int p0 = role.split * a.chunk;
@@ -888,14 +893,14 @@ __device__ __forceinline__ bool attention_role(const Args& a, const Lds<D, F>& S
         attend_chunk(S.big, S.qh, npos, S.sc, S.comb, S.red + 8, S.own, a, l);
         stamp(a, l, 4);
         if (!leader) {
-            uint64_t* pw = X + C::XA_PART + (size_t)(h * ATT_S + role.split) * PW;
+            uint64_t* pw = X + C::XA_PART + (size_t)(h * AS + role.split) * PW;
             if (tid < PW) ll_put(pw + tid, S.own[tid], ep);
             // publish first: loads issued before a store can hold it up
             if (!last && npos > 0) kv_chunk_dma<D>(kc_l + lstride, vc_l + lstride, h, p0, npos, S.big);
         } else {
-            // ---- A2: merge the 8 splits and the new position -> attn_h
-            if (!ll_gather<cdiv(7 * PW + 128, NT), false>(
-                    Range{X + C::XA_PART + (size_t)(h * ATT_S + 1) * PW, 7 * PW, S.gpart},
+            // ---- A2: merge the splits and the new position -> attn_h
+            if (!ll_gather<cdiv((AS - 1) * PW + 128, NT), false>(
+                    Range{X + C::XA_PART + (size_t)(h * AS + 1) * PW, (AS - 1) * PW, S.gpart},
                     Range{X + C::XA_KV + h * 64, 64, S.knew}, Range{X + C::XA_KV + D + h * 64, 64, S.vnew}, ep,
                     a.err, S.s_flag))
                 return false;
@@ -903,7 +908,7 @@ __device__ __forceinline__ bool attention_role(const Args& a, const Lds<D, F>& S
             if (tid < 64) {
                 const float snew = wave_reduce<false>(S.qh[tid] * S.knew[tid]) * 0.125f;
                 float M = fmaxf(snew, S.own[0]);
-                for (int s = 0; s < 7; ++s) M = fmaxf(M, S.gpart[s * PW]);
+                for (int s = 0; s < AS - 1; ++s) M = fmaxf(M, S.gpart[s * PW]);
                 float Ls = expf(snew - M);
                 float A = Ls * S.vnew[tid];
                 if (S.own[0] != -INFINITY) {
@@ -911,7 +916,7 @@ __device__ __forceinline__ bool attention_role(const Args& a, const Lds<D, F>& S
                     Ls = fmaf(wgt, S.own[1], Ls);
                     A = fmaf(wgt, S.own[2 + tid], A);
                 }
-                for (int s = 0; s < 7; ++s) {
+                for (int s = 0; s < AS - 1; ++s) {
                     const float ms = S.gpart[s * PW];
                     if (ms == -INFINITY) continue;
                     const float wgt = expf(ms - M);
@@ -1122,9 +1127,9 @@ static void build_roles(Role* roles) {
         Role& r = roles[w];
         r = Role{-1, 0, 0, 0};
         const int x = w % NXCD, slot = w / NXCD;
-        if (slot < nh_x[x] * ATT_S) {
-            r.head = (slot / ATT_S) * NXCD + x;
-            r.split = slot % ATT_S;
+        if (slot < nh_x[x] * C::ATT_S) {
+            r.head = (slot / C::ATT_S) * NXCD + x;
+            r.split = slot % C::ATT_S;
         } else {
             free_list[nfree++] = w;
         }
@@ -1165,8 +1170,14 @@ size_t persistent_xbuf_bytes(int L, int d, int F, int H, int B, int V) {
     return 8 * (lw * L + 2 * pd::NWG) + sizeof(pd::Role) * pd::NWG + 256;
 }
 
-// The largest T_past the persistent step handles (8 splits of <= MAXPOS).
-int persistent_max_position() { return pd::ATT_S * pd::MAXPOS; }
+// The largest T_past the persistent step handles (its splits of <= MAXPOS
+// positions each).
+int persistent_max_position(int d, int F) {
+    if (d == 768 && F == 3072) return pd::Cfg<768, 3072>::ATT_S * pd::MAXPOS;
+    if (d == 1024 && F == 4096) return pd::Cfg<1024, 4096>::ATT_S * pd::MAXPOS;
+    if (d == 1536 && F == 6144) return pd::Cfg<1536, 6144>::ATT_S * pd::MAXPOS;
+    return 0;
+}
 
 size_t persistent_trace_bytes(int L) { return sizeof(uint64_t) * pd::NWG * (L + 1) * pd::TRACE_SLOTS; }
 
@@ -1206,7 +1217,7 @@ static hipError_t launch_t(const PersistentArgs& p, hipStream_t st) {
     a.next = p.next; a.t0 = p.t0; a.epoch = p.epoch; a.x = x; a.roles = roles; a.err = p.err;
     a.nib = 0x0F0F0F0Fu;
     a.trace = static_cast<uint64_t*>(p.trace);
-    const int chunk = (p.t0 + pd::ATT_S - 1) / pd::ATT_S;
+    const int chunk = (p.t0 + C::ATT_S - 1) / C::ATT_S;
     if (chunk > pd::MAXPOS) return hipErrorInvalidValue;
     a.chunk = chunk < 1 ? 1 : chunk;
     static bool attr_set = false;

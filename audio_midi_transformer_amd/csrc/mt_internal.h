@@ -95,7 +95,7 @@ size_t persistent_xbuf_bytes(int L, int d, int F, int H, int B, int V);
 hipError_t launch_persistent_decode(const PersistentArgs& a, hipStream_t st);
 // Writes the workgroup role table into a freshly zeroed exchange buffer.
 hipError_t persistent_prepare(void* xbuf, int L, int d, int F, hipStream_t st);
-int persistent_max_position();
+int persistent_max_position(int d, int F);
 size_t persistent_trace_bytes(int L);
 
 }  // namespace mt

@@ -76,13 +76,24 @@ def test_persistent_tokens_only(oracle_mod):
 
 
 def test_decode_across_persistent_limit(oracle_mod):
-    """Positions 2040 .. 2055: the persistent step covers T_past <= 2048, the
-    per-operation kernels take over after that; both must match the oracle."""
+    """Large width (8 attention splits of <= 256 positions): positions
+    2040 .. 2055 cross T_past = 2048, where the per-operation kernels take
+    over; both must match the oracle."""
+    _dev()
+    shape = synth.ModelShape("large", 1, 1536, 24, 6144)
+    w = synth.model_weights(shape, 43)
+    prefix = np.random.default_rng(9).standard_normal((1, 2040, 1536)).astype(np.float32)
+    _teacher_forced(oracle_mod, w, 1, 2060, prefix, None, 16, TOL["large"], binding.MT_DECODE_AUTO)
+
+
+def test_persistent_long_cache_small_width(oracle_mod):
+    """Small width runs 16 attention splits (up to 4096 cached positions):
+    positions beyond 2048 stay on the single-launch step."""
     _dev()
     shape = synth.ModelShape("small", 1, 768, 12, 3072)
-    w = synth.model_weights(shape, 43)
-    prefix = np.random.default_rng(9).standard_normal((1, 2040, 768)).astype(np.float32)
-    _teacher_forced(oracle_mod, w, 1, 2060, prefix, None, 16, TOL["small"], binding.MT_DECODE_AUTO)
+    w = synth.model_weights(shape, 46)
+    prefix = np.random.default_rng(12).standard_normal((1, 2100, 768)).astype(np.float32)
+    _teacher_forced(oracle_mod, w, 1, 2110, prefix, None, 8, TOL["small"], binding.MT_DECODE_PERSISTENT)
 
 
 @pytest.mark.parametrize("width", ["small", "medium", "large"])
