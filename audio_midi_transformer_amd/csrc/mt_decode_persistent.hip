@@ -33,8 +33,8 @@
 //                  merges them with the new position and publishes attn_h.
 //   free WGs       the rest: the new K/V rows of the fused projection (to the
 //                  cache slot T_past and to the exchange).
-//   all WGs        D/256 rows of O, F/256 rows of FFN-up + GELU and D/256
-//                  rows of FFN-down.
+//   free WGs       also the O projection (D / free WGs rows each).
+//   all WGs        F/256 rows of FFN-up + GELU and D/256 rows of FFN-down.
 // Per layer: A (attention partials / K,V rows) -> A2 (head merge) -> B (O)
 // -> C (LN2 + up) -> D (down) -> next layer's A; after the last layer E
 // (LN_f + LM-head rows + local argmax) and F (workgroup 0: global argmax,
@@ -82,6 +82,8 @@ struct Role {
     int split;    // attention split (0 = head leader)
     int kv_row0;  // first row of the 2D K|V rows of the fused projection
     int kv_rows;  // number of K|V rows, 0 if none
+    int o_row0;   // first of this workgroup's O-projection rows, -1 if none
+    int pad0, pad1, pad2;
 };
 
 template <int D, int F>
@@ -99,7 +101,7 @@ struct Cfg {
     static constexpr int NFREE = NWG - NATT;
     static constexpr int KV_ROWS = cdiv(2 * D, NFREE);
     static constexpr int UP_ROWS = cdiv(F, NWG);
-    static constexpr int O_ROWS = cdiv(D, NWG);
+    static constexpr int O_ROWS = cdiv(D, NFREE);  // O rows: free workgroups only
     static constexpr int DN_ROWS = cdiv(D, NWG);
     static constexpr int NP_Q = cdiv(64, RP_D);
     static constexpr int NP_KV = cdiv(KV_ROWS, RP_D);
@@ -131,7 +133,7 @@ struct Cfg {
     static constexpr int OFF_RED = rup(cmax(OFF_U + F, OFF_COMB + 4 * 64), 4);
     static constexpr int OFF_FLAG = OFF_RED + 16;
     static constexpr int LDS_FLOATS = OFF_FLAG + 16;
-    static_assert(D % 64 == 0 && F % 32 == 0, "widths");
+    static_assert(D % NT == 0 && F % NT == 0 && NT == 256, "widths");
     static_assert(LPR_D > 0 && LPR_F > 0, "width has no GEMV lane mapping");
     static_assert(NFREE >= 64 && KV_ROWS * NFREE >= 2 * D, "K/V rows need workgroups without attention duty");
     static_assert(LDS_FLOATS * 4 <= 160 * 1024, "LDS budget");
@@ -396,6 +398,27 @@ __device__ __forceinline__ bool ll_gather_regs(const uint64_t* src, int n, float
 
 // ---------------------------------------------------------------- LayerNorm
 
+// Wait for an n-word vector (n a multiple of NT), store it swizzled to LDS
+// (dst) with the sums of its 32-element groups (xs).  Thread t holds words
+// t + i NT, so each group lies in 32 consecutive lanes and its sum is a lane
+// reduction.  False (for the whole workgroup) if a wait failed.
+template <int U>
+__device__ __forceinline__ bool gather_to_lds(const uint64_t* src, int n, float* dst, float* xs, uint32_t ep,
+                                              int* err, int* s_flag) {
+    float v[U];
+    if (!ll_gather_regs<U>(src, n, v, ep, err)) *s_flag = 1;
+    lds_barrier();  // dst and xs may still be read by other waves of the previous phase
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int i = u * NT + threadIdx.x;
+        dst[swz(i)] = v[u];
+        const float t = group_reduce<32>(v[u]);
+        if ((threadIdx.x & 31) == res_lane(32)) xs[i >> 5] = t;
+    }
+    lds_barrier();
+    return *s_flag == 0;
+}
+
 // xs[c] = sum of the 32 elements of group c (its elements stay within its
 // 32 slots in either layout).  Eight lanes per group.
 __device__ __forceinline__ void group_sums(const float* act, int K, float* xs) {
@@ -442,25 +465,36 @@ __device__ __forceinline__ bool residual_layernorm(float (&r)[LnRegs<D>::PER], c
                                                    bool add, const LnRegs<D>& p, float eps, float* act, float* xs, float* red,
                                                    const int* s_flag) {
     constexpr int PER = LnRegs<D>::PER;
+    // mean and sum of squared deviations of each wave's 64 PER elements
+    // (two passes within the wave), then combined across the four waves:
+    // M2 = sum_w M2_w + n_w sum_w (mean_w - mean)^2 (exact combination).
     float s = 0.f;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-        const int k = threadIdx.x + i * NT;
-        if (k < D) {
-            if (add) r[i] += delta[i];
-            s += r[i];
-        }
+        if (add) r[i] += delta[i];
+        s += r[i];
     }
-    const float mean = block_reduce<false>(s, red) / (float)D;
-    if (*s_flag) return false;
+    constexpr float NW = 64.f * PER;
+    const float mw = wave_reduce<false>(s) / NW;
     float q = 0.f;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-        const int k = threadIdx.x + i * NT;
-        const float c = k < D ? r[i] - mean : 0.f;
+        const float c = r[i] - mw;
         q = fmaf(c, c, q);
     }
-    const float var = block_reduce<false>(q, red + 4) / (float)D;
+    q = wave_reduce<false>(q);
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) {
+        red[2 * wave] = mw;
+        red[2 * wave + 1] = q;
+    }
+    lds_barrier();
+    if (*s_flag) return false;
+    const float mean = ((red[0] + red[2]) + (red[4] + red[6])) * 0.25f;
+    const float d0 = red[0] - mean, d1 = red[2] - mean, d2 = red[4] - mean, d3 = red[6] - mean;
+    const float m2 = ((red[1] + red[3]) + (red[5] + red[7])) +
+                     NW * ((d0 * d0 + d1 * d1) + (d2 * d2 + d3 * d3));
+    const float var = m2 / (float)D;
     const float rstd = 1.0f / sqrtf(var + eps);
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
@@ -743,13 +777,15 @@ struct BcdW {
     LnRegs<D> ln2;
 };
 
-// Loads of the O and up rows and of LN2 (issued during phase A).
+// Loads of the O rows (orow < 0: none), the up rows and LN2 (issued during
+// phase A).
 template <int D, int F>
-__device__ __forceinline__ void load_bc(BcdW<D, F>& w, const uint8_t* wq, const float* ws, const float* ln) {
+__device__ __forceinline__ void load_bc(BcdW<D, F>& w, const uint8_t* wq, const float* ws, const float* ln, int orow) {
     using C = Cfg<D, F>;
     using O = Off<D, F>;
-    const int orow = blockIdx.x * C::O_ROWS, urow = blockIdx.x * C::UP_ROWS;
-    wblk_load<C::LPR_D, C::CPL_D, C::NP_O>(w.wo, wq + O::OO, ws + O::OS, D, orow, max(0, min(C::O_ROWS, D - orow)));
+    const int urow = blockIdx.x * C::UP_ROWS;
+    if (orow >= 0)
+        wblk_load<C::LPR_D, C::CPL_D, C::NP_O>(w.wo, wq + O::OO, ws + O::OS, D, orow, max(0, min(C::O_ROWS, D - orow)));
     wblk_load<C::LPR_D, C::CPL_D, C::NP_UP>(w.wu, wq + O::UO, ws + O::US, D, urow, max(0, min(C::UP_ROWS, F - urow)));
     ln_load<D>(w.ln2, ln + 2 * D, ln + 3 * D);
 }
@@ -763,17 +799,19 @@ __device__ __forceinline__ void load_d(BcdW<D, F>& w, const uint8_t* wq, const f
     wblk_load<C::LPR_F, C::CPL_F, C::NP_DN>(w.wd, wq + O::DO, ws + O::DS, F, drow, max(0, min(C::DN_ROWS, D - drow)));
 }
 
-// Phase B (every workgroup): attn -> O rows of this workgroup -> exchange.
+// Phase B (workgroups without attention duty): attn -> O rows -> exchange.
+// The attention workgroups skip it: their next-layer K/V chunk DMA, issued
+// just before, would hold up their exchange reads (loads complete in order).
 template <int D, int F>
-__device__ __forceinline__ bool phase_b(const Args& a, const Lds<D, F>& S, uint64_t* X, const BcdW<D, F>& w, int l) {
+__device__ __forceinline__ bool phase_b(const Args& a, const Lds<D, F>& S, uint64_t* X, const BcdW<D, F>& w, int orow,
+                                        int l) {
     using C = Cfg<D, F>;
     const uint32_t ep = a.epoch;
-    if (!ll_gather1<cdiv(D, NT), true>(rep_of(X + C::XB_ATT, D), D, S.act, ep, a.err, S.s_flag)) return false;
+    if (orow < 0) return true;
+    if (!gather_to_lds<D / NT>(rep_of(X + C::XB_ATT, D), D, S.act, S.xs, ep, a.err, S.s_flag)) return false;
     stamp(a, l, 6);
-    group_sums(S.act, D, S.xs);
     float o[C::NP_O];
     wblk_dot<C::LPR_D, C::CPL_D, C::NP_O>(w.wo, S.act, S.xs, o, a.nib);
-    const int orow = blockIdx.x * C::O_ROWS;
 #pragma unroll
     for (int p = 0; p < C::NP_O; ++p) {
         const int rr = out_row<C::LPR_D>(p);
@@ -812,9 +850,8 @@ template <int D, int F>
 __device__ __forceinline__ bool phase_d(const Args& a, const Lds<D, F>& S, uint64_t* X, const BcdW<D, F>& w, int l) {
     using C = Cfg<D, F>;
     const uint32_t ep = a.epoch;
-    if (!ll_gather1<cdiv(F, NT), true>(rep_of(X + C::XC, F), F, S.u, ep, a.err, S.s_flag)) return false;
+    if (!gather_to_lds<F / NT>(rep_of(X + C::XC, F), F, S.u, S.us, ep, a.err, S.s_flag)) return false;
     stamp(a, l, 10);
-    group_sums(S.u, F, S.us);
     float o[C::NP_DN];
     wblk_dot<C::LPR_F, C::CPL_F, C::NP_DN>(w.wd, S.u, S.us, o, a.nib);
     const int drow = blockIdx.x * C::DN_ROWS;
@@ -889,13 +926,14 @@ __device__ __forceinline__ bool attention_role(const Args& a, const Lds<D, F>& S
         lds_barrier();
         stamp(a, l, 3);
         // phase B and C weights load behind the attention
-        load_bc<D, F>(w, wq, ws, ln);
+        load_bc<D, F>(w, wq, ws, ln, -1);
         attend_chunk(S.big, S.qh, npos, S.sc, S.comb, S.red + 8, S.own, a, l);
         stamp(a, l, 4);
         if (!leader) {
             uint64_t* pw = X + C::XA_PART + (size_t)(h * AS + role.split) * PW;
             if (tid < PW) ll_put(pw + tid, S.own[tid], ep);
-            // publish first: loads issued before a store can hold it up
+            // the next layer's chunk: this workgroup's next exchange read
+            // (phase C) is microseconds away
             if (!last && npos > 0) kv_chunk_dma<D>(kc_l + lstride, vc_l + lstride, h, p0, npos, S.big);
         } else {
             // ---- A2: merge the splits and the new position -> attn_h
@@ -927,8 +965,7 @@ __device__ __forceinline__ bool attention_role(const Args& a, const Lds<D, F>& S
             }
             if (!last && npos > 0) kv_chunk_dma<D>(kc_l + lstride, vc_l + lstride, h, p0, npos, S.big);
         }
-        // ---- B, C, D
-        if (!phase_b<D, F>(a, S, X, w, l)) return false;
+        // ---- C, D (no phase B)
         load_d<D, F>(w, wq, ws);
         if (!phase_c<D, F>(a, S, X, w, r, l)) return false;
         if (!last) {
@@ -982,9 +1019,9 @@ __device__ __forceinline__ bool free_role(const Args& a, const Lds<D, F>& S, con
                 }
             }
         }
-        load_bc<D, F>(w, wq, ws, ln);
+        load_bc<D, F>(w, wq, ws, ln, role.o_row0);
         // ---- B, C, D
-        if (!phase_b<D, F>(a, S, X, w, l)) return false;
+        if (!phase_b<D, F>(a, S, X, w, role.o_row0, l)) return false;
         load_d<D, F>(w, wq, ws);
         if (!phase_c<D, F>(a, S, X, w, r, l)) return false;
         if (!last) {
@@ -1125,7 +1162,7 @@ static void build_roles(Role* roles) {
     for (int h = 0; h < C::H; ++h) ++nh_x[h % NXCD];
     for (int w = 0; w < NWG; ++w) {
         Role& r = roles[w];
-        r = Role{-1, 0, 0, 0};
+        r = Role{-1, 0, 0, 0, -1, 0, 0, 0};
         const int x = w % NXCD, slot = w / NXCD;
         if (slot < nh_x[x] * C::ATT_S) {
             r.head = (slot / C::ATT_S) * NXCD + x;
@@ -1137,6 +1174,7 @@ static void build_roles(Role* roles) {
     for (int i = 0; i < nfree; ++i) {
         Role& r = roles[free_list[i]];
         const int row0 = i * C::KV_ROWS;
+        r.o_row0 = i * C::O_ROWS < D ? i * C::O_ROWS : -1;
         r.kv_row0 = row0;
         r.kv_rows = row0 < 2 * D ? (2 * D - row0 < C::KV_ROWS ? 2 * D - row0 : C::KV_ROWS) : 0;
     }
