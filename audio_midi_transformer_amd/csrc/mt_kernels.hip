@@ -340,65 +340,85 @@ __global__ __launch_bounds__(256) void k_gemv_w4(const float* __restrict__ X, in
 // ---------------------------------------------------------------- INT4 GEMM (FP32 MFMA)
 
 // Y[M, N] = X[M, K] . W'^T with W' = (u - 8) * s dequantised exactly into LDS.
-// Tile 64 x 64 per workgroup, K step 32 (one quantisation group); four waves
-// as 2 x 2, each a 32 x 32 sub-tile of 2 x 2 v_mfma_f32_16x16x4f32 blocks.
-// Operand layout of that instruction: lane l supplies A[l % 16][l / 16] and
-// B[l / 16][l % 16]; it receives D[4 (l / 16) + r][l % 16], r = 0..3.
+// Tile 64 x 64 per workgroup, K step 64 (two quantisation groups) per LDS
+// stage, the next stage's activations and nibbles loaded into registers
+// while the current one is multiplied.  Four waves as 2 x 2, each a 32 x 32
+// sub-tile of 2 x 2 v_mfma_f32_16x16x4f32 blocks.  Operand layout of that
+// instruction: lane l supplies A[l % 16][l / 16] and B[l / 16][l % 16]; it
+// receives D[4 (l / 16) + r][l % 16], r = 0..3.  blockIdx.z splits K into
+// kspan-column ranges whose results are added atomically (+= epilogue only).
 constexpr int GT = 64;
-constexpr int GS = 34;  // LDS row stride in floats (conflict-free column reads)
+constexpr int GK = 64;
+constexpr int GS = GK + 4;  // LDS row stride in floats
 
 __global__ __launch_bounds__(256) void k_gemm_w4(const float* __restrict__ X, int ldx, int M, int K,
                                                  const uint8_t* __restrict__ Wq,
                                                  const float* __restrict__ Ws, int N,
-                                                 float* __restrict__ Y, int ldy, EpiArgs ep) {
-    __shared__ float As[GT * GS];
-    __shared__ float Bs[GT * GS];
+                                                 float* __restrict__ Y, int ldy, EpiArgs ep, int kspan) {
+    extern __shared__ float gsm[];
+    float* As = gsm;            // [64][GS]
+    float* Bs = gsm + GT * GS;  // [64][GS]
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const int m0 = blockIdx.y * GT, n0 = blockIdx.x * GT;
     const int G = K / 32;
+    const int kb = blockIdx.z * kspan, ke = min(K, kb + kspan);
     f32x4 acc[2][2];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // A tile load: 64 rows x 32 floats = 512 float4, two per thread.
-    // W tile load: 64 rows x 4 dwords of nibbles, one dword (8 weights) per thread.
-    const int wr = tid >> 2, wdw = tid & 3;
-    for (int g = 0; g < G; ++g) {
-        __syncthreads();
+    // stage loads.  Activations: 64 rows x 64 columns = 1024 float4, four
+    // per thread.  Nibbles: 64 rows x 8 dwords, two per thread (thread t: row
+    // t / 4, group (t % 4) / 2, dwords 2 (t % 2) .. +1), with that group's
+    // scale.
+    constexpr int NA = GT * GK / 4 / 256, NWD = 2;
+    float4 pa[NA];
+    unsigned pw[NWD];
+    float ps = 0.f;
+    const int wrow = tid >> 2, wg = (tid & 3) >> 1, wh = tid & 1;
+    auto load_stage = [&](int k0) {
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
+        for (int e = 0; e < NA; ++e) {
             const int idx = tid + e * 256;
-            const int r = idx >> 3, c4 = idx & 7;
-            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (m0 + r < M) v = *reinterpret_cast<const float4*>(X + (size_t)(m0 + r) * ldx + g * 32 + c4 * 4);
-            float* dst = As + r * GS + c4 * 4;
-            *reinterpret_cast<float2*>(dst) = make_float2(v.x, v.y);
-            *reinterpret_cast<float2*>(dst + 2) = make_float2(v.z, v.w);
+            const int r = idx / (GK / 4), c = (idx % (GK / 4)) * 4;
+            pa[e] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (m0 + r < M && k0 + c < ke) pa[e] = *reinterpret_cast<const float4*>(X + (size_t)(m0 + r) * ldx + k0 + c);
+        }
+        const int g = k0 / 32 + wg;
+        const bool ok = n0 + wrow < N && g * 32 < ke;
+#pragma unroll
+        for (int i = 0; i < NWD; ++i)
+            pw[i] = ok ? *reinterpret_cast<const unsigned*>(Wq + (size_t)(n0 + wrow) * (K / 2) + (size_t)g * 16 +
+                                                             (wh * NWD + i) * 4)
+                       : 0x88888888u;
+        ps = ok ? Ws[(size_t)(n0 + wrow) * G + g] : 0.f;
+    };
+    load_stage(kb);
+    for (int k0 = kb; k0 < ke; k0 += GK) {
+        if (k0 != kb) __syncthreads();  // the previous stage has been multiplied
+#pragma unroll
+        for (int e = 0; e < NA; ++e) {
+            const int idx = tid + e * 256;
+            *reinterpret_cast<float4*>(As + (idx / (GK / 4)) * GS + (idx % (GK / 4)) * 4) = pa[e];
         }
         {
-            float* dst = Bs + wr * GS + wdw * 8;
-            if (n0 + wr < N) {
-                const unsigned word = *reinterpret_cast<const unsigned*>(
-                    Wq + (size_t)(n0 + wr) * (K / 2) + (size_t)g * 16 + wdw * 4);
-                const float sc = Ws[(size_t)(n0 + wr) * G + g];
+            float* dst = Bs + wrow * GS + wg * 32 + wh * NWD * 8;
+#pragma unroll
+            for (int i = 0; i < NWD; ++i)
 #pragma unroll
                 for (int b = 0; b < 4; ++b) {
-                    const unsigned byte = (word >> (8 * b)) & 0xFFu;
-                    const float lo = (float)((int)(byte & 15u) - 8) * sc;
-                    const float hi = (float)((int)(byte >> 4) - 8) * sc;
-                    *reinterpret_cast<float2*>(dst + 2 * b) = make_float2(lo, hi);
+                    const unsigned byte = (pw[i] >> (8 * b)) & 0xFFu;
+                    const float lo = (float)((int)(byte & 15u) - 8) * ps;
+                    const float hi = (float)((int)(byte >> 4) - 8) * ps;
+                    *reinterpret_cast<float2*>(dst + i * 8 + 2 * b) = make_float2(lo, hi);
                 }
-            } else {
-#pragma unroll
-                for (int b = 0; b < 4; ++b) *reinterpret_cast<float2*>(dst + 2 * b) = make_float2(0.f, 0.f);
-            }
         }
         __syncthreads();
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
+        if (k0 + GK < ke) load_stage(k0 + GK);
+        const int ksteps = min(GK, ke - k0) / 4;
+        for (int kk = 0; kk < ksteps; ++kk) {
             const int k = kk * 4 + (lane >> 4);
             float a[2], b[2];
 #pragma unroll
@@ -420,7 +440,10 @@ __global__ __launch_bounds__(256) void k_gemm_w4(const float* __restrict__ X, in
             for (int r = 0; r < 4; ++r) {
                 const int m = m0 + wm * 32 + i * 16 + 4 * (lane >> 4) + r;
                 const int n = n0 + wn * 32 + j * 16 + (lane & 15);
-                if (m < M && n < N) epilogue(ep, Y, ldy, m, n, acc[i][j][r]);
+                if (m < M && n < N) {
+                    if (gridDim.z > 1) atomicAdd(Y + (size_t)m * ldy + n, acc[i][j][r]);
+                    else epilogue(ep, Y, ldy, m, n, acc[i][j][r]);
+                }
             }
 }
 
@@ -732,8 +755,19 @@ hipError_t launch_w4_matmul(const float* x, int ldx, int M, const Int4Mat& w, co
         return hipGetLastError();
     }
     if (ln_g || ap.part) return hipErrorInvalidValue;  // the GEMM path takes plain rows
-    const dim3 grid((w.N + GT - 1) / GT, (M + GT - 1) / GT);
-    hipLaunchKernelGGL(k_gemm_w4, grid, dim3(256), 0, st, x, ldx, M, w.K, w.q, w.s, w.N, y, ldy, ep);
+    // one workgroup per tile over all of K: results do not depend on the
+    // order of atomic additions (prefill is bit-reproducible)
+    const int ksplit = 1;
+    const int kspan = (w.K + GK - 1) / GK * GK;
+    static bool attr = false;
+    const size_t lds = sizeof(float) * 2 * GT * GS;
+    if (!attr) {
+        hipError_t e = hipFuncSetAttribute((const void*)k_gemm_w4, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        attr = true;
+    }
+    const dim3 grid((w.N + GT - 1) / GT, (M + GT - 1) / GT, ksplit);
+    hipLaunchKernelGGL(k_gemm_w4, grid, dim3(256), lds, st, x, ldx, M, w.K, w.q, w.s, w.N, y, ldy, ep, kspan);
     return hipGetLastError();
 }
 
