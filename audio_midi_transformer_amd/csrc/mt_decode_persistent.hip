@@ -419,24 +419,6 @@ __device__ __forceinline__ bool gather_to_lds(const uint64_t* src, int n, float*
     return *s_flag == 0;
 }
 
-// xs[c] = sum of the 32 elements of group c (its elements stay within its
-// 32 slots in either layout).  Eight lanes per group.
-__device__ __forceinline__ void group_sums(const float* act, int K, float* xs) {
-    const int G = K / 32;
-    for (int base = 0; base < G * 8; base += NT) {
-        const int i = base + threadIdx.x;
-        const int c = i >> 3, part = i & 7;
-        float t = 0.f;
-        if (c < G) {
-            const float4 v = *reinterpret_cast<const float4*>(act + c * 32 + part * 4);
-            t = (v.x + v.y) + (v.z + v.w);
-        }
-        t = group_reduce<8>(t);
-        if (c < G && part == 0) xs[c] = t;
-    }
-    lds_barrier();
-}
-
 // LayerNorm gain and bias held in registers (element k = threadIdx.x + i*NT).
 template <int D>
 struct LnRegs {
