@@ -40,6 +40,24 @@ __device__ __forceinline__ float group_sum(float v) {
     return v;
 }
 
+// Max / sum over each row of 16 lanes (DPP row = 16 lanes), in every lane.
+template <int CTRL>
+__device__ __forceinline__ float dppf(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row_max16(float v) {
+    v = fmaxf(v, dppf<0xB1>(v));   // quad_perm [1,0,3,2]
+    v = fmaxf(v, dppf<0x4E>(v));   // quad_perm [2,3,0,1]
+    v = fmaxf(v, dppf<0x141>(v));  // row_half_mirror
+    return fmaxf(v, dppf<0x140>(v));  // row_mirror
+}
+__device__ __forceinline__ float row_sum16(float v) {
+    v += dppf<0xB1>(v);
+    v += dppf<0x4E>(v);
+    v += dppf<0x141>(v);
+    return v + dppf<0x140>(v);
+}
+
 __device__ __forceinline__ float gelu_erf(float x) {
     return 0.5f * x * (1.0f + erff(x * 0.70710678118654752440f));
 }
@@ -534,35 +552,51 @@ __global__ __launch_bounds__(256) void k_attn_decode(const float* __restrict__ q
 // ---------------------------------------------------------------- prefill attention
 
 // Causal attention of R new rows per sequence (positions t0 .. t0+R-1) over
-// the cache.  Workgroup (row block, h, b) handles 64 query rows; wave w rows
-// 16w .. 16w+15; four lanes per row, each 16 of the 64 dimensions.  Keys
-// and values are staged through LDS 64 positions at a time.
+// the cache, on v_mfma_f32_16x16x4f32 (A = 16 rows x 4 columns, B = 4 x 16,
+// lane l supplies A[l % 16][l / 16] and B[l / 16][l % 16] and receives
+// D[4 (l / 16) + r][l % 16]).  Workgroup (row block, h, b): 64 query rows,
+// wave w rows 16 w .. 16 w + 15.  Keys and values are staged through LDS 64
+// positions at a time.  Per block a wave computes S = Q K^T / 8 (four 16 x 16
+// tiles), updates each row's running max and sum of exp (a row's 64 scores
+// sit in one 16-lane DPP row), rescales its output, stores P = e^(S - m)
+// in LDS (the D layout of S is not the A layout P needs) and adds P V.
+constexpr int PS = 68;  // LDS row stride (floats) of the K, V and P tiles
+
 __global__ __launch_bounds__(256) void k_attn_prefill(const float* __restrict__ q,
                                                       const float* __restrict__ kc,
                                                       const float* __restrict__ vc, int layer,
                                                       int B, int H, int t_cap, int t0, int R,
                                                       float* __restrict__ out) {
-    __shared__ float Ks[64 * 68];
-    __shared__ float Vs[64 * 68];
+    __shared__ float Ks[64 * PS];
+    __shared__ float Vs[64 * PS];
+    __shared__ float Pw[4][16 * PS];
     const int d = H * 64;
     const int i0 = blockIdx.x * 64, h = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int r = lane >> 2, qd = lane & 3;
-    const int i = i0 + wave * 16 + r;
-    const bool valid = i < R;
-    const int p = t0 + i;
-    float qv[16], acc[16];
-    const float* qrow = q + ((size_t)b * R + (valid ? i : 0)) * d + h * 64 + qd * 16;
+    const int lr = lane & 15, lq = lane >> 4;
+    float* P = Pw[wave];
+    // A operand of Q K^T: row i0 + 16 w + lr, dimensions 4 s + lq
+    const int qi = i0 + 16 * wave + lr;
+    float qa[16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        qv[j] = valid ? qrow[j] : 0.f;
-        acc[j] = 0.f;
+    for (int s = 0; s < 16; ++s) qa[s] = qi < R ? q[((size_t)b * R + qi) * d + h * 64 + 4 * s + lq] : 0.f;
+    // rows 4 lq + r of this wave's 16 (query positions)
+    int qpos[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) qpos[r] = t0 + i0 + 16 * wave + 4 * lq + r;
+    float m[4], l[4];
+    f32x4 o[4];  // output tiles: dimensions 16 n + lr
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        m[r] = -INFINITY;
+        l[r] = 0.f;
     }
-    float m = -INFINITY, l = 0.f;
-    const int kmax = t0 + min(i0 + 63, R - 1);
+#pragma unroll
+    for (int n = 0; n < 4; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int kmax = t0 + min(i0 + 63, R - 1);  // last key any row of the block sees
     const size_t base = ((size_t)(layer * B + b) * t_cap) * d + h * 64;
     for (int kb = 0; kb <= kmax; kb += 64) {
-        __syncthreads();
+        __syncthreads();  // the previous block's K and V have been used
         for (int e = tid; e < 64 * 16; e += 256) {
             const int kk = e >> 4, c4 = e & 15, t = kb + kk;
             float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), vv = kv;
@@ -570,34 +604,72 @@ __global__ __launch_bounds__(256) void k_attn_prefill(const float* __restrict__ 
                 kv = *reinterpret_cast<const float4*>(kc + base + (size_t)t * d + c4 * 4);
                 vv = *reinterpret_cast<const float4*>(vc + base + (size_t)t * d + c4 * 4);
             }
-            *reinterpret_cast<float4*>(Ks + kk * 68 + c4 * 4) = kv;
-            *reinterpret_cast<float4*>(Vs + kk * 68 + c4 * 4) = vv;
+            *reinterpret_cast<float4*>(Ks + kk * PS + c4 * 4) = kv;
+            *reinterpret_cast<float4*>(Vs + kk * PS + c4 * 4) = vv;
         }
         __syncthreads();
-        const int nk = p - kb + 1;  // keys of this block visible to row i
-        for (int kk = 0; kk < 64; ++kk) {
-            const float* kr = Ks + kk * 68 + qd * 16;
-            float s = 0.f;
+        // S tiles n: keys kb + 16 n + lr
+        f32x4 sc[4];
 #pragma unroll
-            for (int j = 0; j < 16; ++j) s = fmaf(qv[j], kr[j], s);
-            s = group_sum<4>(s) * 0.125f;
-            if (valid && kk < nk) {
-                const float mn = fmaxf(m, s);
-                const float corr = expf(m - mn);
-                const float pe = expf(s - mn);
-                l = fmaf(l, corr, pe);
-                const float* vr = Vs + kk * 68 + qd * 16;
+        for (int n = 0; n < 4; ++n) {
+            sc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int j = 0; j < 16; ++j) acc[j] = fmaf(acc[j], corr, pe * vr[j]);
-                m = mn;
+            for (int s = 0; s < 16; ++s)
+                sc[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[s], Ks[(16 * n + lr) * PS + 4 * s + lq], sc[n], 0, 0, 0);
+        }
+        // mask, row max over the block (in-lane over n, then the 16-lane row)
+        float bm[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            bm[r] = -INFINITY;
+#pragma unroll
+            for (int n = 0; n < 4; ++n) {
+                const int key = kb + 16 * n + lr;
+                float v = sc[n][r] * 0.125f;
+                if (key > qpos[r]) v = -INFINITY;
+                sc[n][r] = v;
+                bm[r] = fmaxf(bm[r], v);
             }
+            bm[r] = row_max16(bm[r]);
+        }
+        float rs[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float mn = fmaxf(m[r], bm[r]);
+            const float corr = mn == -INFINITY ? 1.f : expf(m[r] - mn);
+            float ps = 0.f;
+#pragma unroll
+            for (int n = 0; n < 4; ++n) {
+                const float p = mn == -INFINITY ? 0.f : expf(sc[n][r] - mn);
+                P[(4 * lq + r) * PS + 16 * n + lr] = p;
+                ps += p;
+            }
+            rs[r] = corr;
+            l[r] = fmaf(l[r], corr, row_sum16(ps));
+            m[r] = mn;
+        }
+#pragma unroll
+        for (int n = 0; n < 4; ++n)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o[n][r] *= rs[r];
+        // O += P V (P rows written by this wave only: no workgroup barrier)
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+#pragma unroll 4
+        for (int s = 0; s < 16; ++s) {
+            const float pa = P[lr * PS + 4 * s + lq];
+#pragma unroll
+            for (int n = 0; n < 4; ++n)
+                o[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa, Vs[(4 * s + lq) * PS + 16 * n + lr], o[n], 0, 0, 0);
         }
     }
-    if (valid) {
-        float* o = out + ((size_t)b * R + i) * d + h * 64 + qd * 16;
-        const float inv = 1.0f / l;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) o[j] = acc[j] * inv;
+    for (int r = 0; r < 4; ++r) {
+        const int i = i0 + 16 * wave + 4 * lq + r;
+        if (i < R) {
+            const float inv = 1.0f / l[r];
+#pragma unroll
+            for (int n = 0; n < 4; ++n) out[((size_t)b * R + i) * d + h * 64 + 16 * n + lr] = o[n][r] * inv;
+        }
     }
 }
 
