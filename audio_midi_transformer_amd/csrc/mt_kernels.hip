@@ -358,44 +358,50 @@ __global__ __launch_bounds__(256) void k_gemv_w4(const float* __restrict__ X, in
 // ---------------------------------------------------------------- INT4 GEMM (FP32 MFMA)
 
 // Y[M, N] = X[M, K] . W'^T with W' = (u - 8) * s dequantised exactly into LDS.
-// Tile 64 x 64 per workgroup, K step 64 (two quantisation groups) per LDS
-// stage, the next stage's activations and nibbles loaded into registers
-// while the current one is multiplied.  Four waves as 2 x 2, each a 32 x 32
-// sub-tile of 2 x 2 v_mfma_f32_16x16x4f32 blocks.  Operand layout of that
-// instruction: lane l supplies A[l % 16][l / 16] and B[l / 16][l % 16]; it
-// receives D[4 (l / 16) + r][l % 16], r = 0..3.  blockIdx.z splits K into
-// kspan-column ranges whose results are added atomically (+= epilogue only).
-constexpr int GT = 64;
-constexpr int GK = 64;
-constexpr int GS = GK + 4;  // LDS row stride in floats
+// Tile TM x 64 per workgroup, K step GK per LDS stage, the next stage's
+// activations and nibbles loaded into registers while the current one is
+// multiplied.  Two shapes: TM = 64 with GK = 64 for long inputs (many
+// workgroups, four per CU by LDS), TM = 32 with GK = 128 for short prompts,
+// where 64-row tiles would leave CUs idle and each workgroup needs more MFMA
+// work per stage to cover the load latency.  Four waves as 2 x 2, each a
+// (TM / 2) x 32 sub-tile of (TM / 32) x 2 v_mfma_f32_16x16x4f32 blocks.
+// Operand layout of that instruction: lane l supplies A[l % 16][l / 16] and
+// B[l / 16][l % 16]; it receives D[4 (l / 16) + r][l % 16], r = 0..3.
+// blockIdx.z splits K into kspan-column ranges whose results are added
+// atomically (+= epilogue only).
+constexpr int GN = 64;
+constexpr size_t gemm_lds(int tm, int gk) { return sizeof(float) * (tm + GN) * (gk + 4); }
 
+template <int TM, int GK>
 __global__ __launch_bounds__(256) void k_gemm_w4(const float* __restrict__ X, int ldx, int M, int K,
                                                  const uint8_t* __restrict__ Wq,
                                                  const float* __restrict__ Ws, int N,
                                                  float* __restrict__ Y, int ldy, EpiArgs ep, int kspan) {
+    constexpr int GS = GK + 4;   // LDS row stride in floats
+    constexpr int MI = TM / 32;  // 16-row MFMA blocks per wave
     extern __shared__ float gsm[];
-    float* As = gsm;            // [64][GS]
-    float* Bs = gsm + GT * GS;  // [64][GS]
+    float* As = gsm;            // [TM][GS]
+    float* Bs = gsm + TM * GS;  // [64][GS]
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
-    const int m0 = blockIdx.y * GT, n0 = blockIdx.x * GT;
+    const int m0 = blockIdx.y * TM, n0 = blockIdx.x * GN;
     const int G = K / 32;
     const int kb = blockIdx.z * kspan, ke = min(K, kb + kspan);
-    f32x4 acc[2][2];
+    f32x4 acc[MI][2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // stage loads.  Activations: 64 rows x 64 columns = 1024 float4, four
-    // per thread.  Nibbles: 64 rows x 8 dwords, two per thread (thread t: row
-    // t / 4, group (t % 4) / 2, dwords 2 (t % 2) .. +1), with that group's
-    // scale.
-    constexpr int NA = GT * GK / 4 / 256, NWD = 2;
+    // stage loads.  Activations: TM rows x GK columns, TM * GK / 1024 float4
+    // per thread.  Nibbles: thread t takes quarter t % 4 (GK / 4 columns,
+    // inside one group) of weight row t / 4, with that group's scale.
+    constexpr int NA = TM * GK / 4 / 256;
+    constexpr int NW = GK / 32;  // nibble dwords per thread
     float4 pa[NA];
-    unsigned pw[NWD];
+    unsigned pw[NW];
     float ps = 0.f;
-    const int wrow = tid >> 2, wg = (tid & 3) >> 1, wh = tid & 1;
+    const int wrow = tid >> 2, wq = tid & 3;
     auto load_stage = [&](int k0) {
 #pragma unroll
         for (int e = 0; e < NA; ++e) {
@@ -404,12 +410,11 @@ __global__ __launch_bounds__(256) void k_gemm_w4(const float* __restrict__ X, in
             pa[e] = make_float4(0.f, 0.f, 0.f, 0.f);
             if (m0 + r < M && k0 + c < ke) pa[e] = *reinterpret_cast<const float4*>(X + (size_t)(m0 + r) * ldx + k0 + c);
         }
-        const int g = k0 / 32 + wg;
-        const bool ok = n0 + wrow < N && g * 32 < ke;
+        const int c0 = k0 + wq * (GK / 4), g = c0 / 32;
+        const bool ok = n0 + wrow < N && c0 < ke;
 #pragma unroll
-        for (int i = 0; i < NWD; ++i)
-            pw[i] = ok ? *reinterpret_cast<const unsigned*>(Wq + (size_t)(n0 + wrow) * (K / 2) + (size_t)g * 16 +
-                                                             (wh * NWD + i) * 4)
+        for (int i = 0; i < NW; ++i)
+            pw[i] = ok ? *reinterpret_cast<const unsigned*>(Wq + (size_t)(n0 + wrow) * (K / 2) + c0 / 2 + 4 * i)
                        : 0x88888888u;
         ps = ok ? Ws[(size_t)(n0 + wrow) * G + g] : 0.f;
     };
@@ -422,15 +427,20 @@ __global__ __launch_bounds__(256) void k_gemm_w4(const float* __restrict__ X, in
             *reinterpret_cast<float4*>(As + (idx / (GK / 4)) * GS + (idx % (GK / 4)) * 4) = pa[e];
         }
         {
-            float* dst = Bs + wrow * GS + wg * 32 + wh * NWD * 8;
+            // dword i holds inputs 8 i .. 8 i + 7 of the quarter, low nibble first
+            float* dst = Bs + wrow * GS + wq * (GK / 4);
 #pragma unroll
-            for (int i = 0; i < NWD; ++i)
+            for (int i = 0; i < NW; ++i)
 #pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    const unsigned byte = (pw[i] >> (8 * b)) & 0xFFu;
-                    const float lo = (float)((int)(byte & 15u) - 8) * ps;
-                    const float hi = (float)((int)(byte >> 4) - 8) * ps;
-                    *reinterpret_cast<float2*>(dst + i * 8 + 2 * b) = make_float2(lo, hi);
+                for (int h = 0; h < 2; ++h) {
+                    float v[4];
+#pragma unroll
+                    for (int b = 0; b < 2; ++b) {
+                        const unsigned byte = (pw[i] >> (8 * (2 * h + b))) & 0xFFu;
+                        v[2 * b] = (float)((int)(byte & 15u) - 8) * ps;
+                        v[2 * b + 1] = (float)((int)(byte >> 4) - 8) * ps;
+                    }
+                    *reinterpret_cast<float4*>(dst + i * 8 + h * 4) = make_float4(v[0], v[1], v[2], v[3]);
                 }
         }
         __syncthreads();
@@ -438,25 +448,25 @@ __global__ __launch_bounds__(256) void k_gemm_w4(const float* __restrict__ X, in
         const int ksteps = min(GK, ke - k0) / 4;
         for (int kk = 0; kk < ksteps; ++kk) {
             const int k = kk * 4 + (lane >> 4);
-            float a[2], b[2];
+            float a[MI], b[2];
 #pragma unroll
-            for (int i = 0; i < 2; ++i) a[i] = As[(wm * 32 + i * 16 + (lane & 15)) * GS + k];
+            for (int i = 0; i < MI; ++i) a[i] = As[(wm * (TM / 2) + i * 16 + (lane & 15)) * GS + k];
 #pragma unroll
             for (int j = 0; j < 2; ++j) b[j] = Bs[(wn * 32 + j * 16 + (lane & 15)) * GS + k];
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < MI; ++i)
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[j], acc[i][j], 0, 0, 0);
         }
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int m = m0 + wm * 32 + i * 16 + 4 * (lane >> 4) + r;
+                const int m = m0 + wm * (TM / 2) + i * 16 + 4 * (lane >> 4) + r;
                 const int n = n0 + wn * 32 + j * 16 + (lane & 15);
                 if (m < M && n < N) {
                     if (gridDim.z > 1) atomicAdd(Y + (size_t)m * ldy + n, acc[i][j][r]);
@@ -554,15 +564,180 @@ __global__ __launch_bounds__(256) void k_attn_decode(const float* __restrict__ q
 // Causal attention of R new rows per sequence (positions t0 .. t0+R-1) over
 // the cache, on v_mfma_f32_16x16x4f32 (A = 16 rows x 4 columns, B = 4 x 16,
 // lane l supplies A[l % 16][l / 16] and B[l / 16][l % 16] and receives
-// D[4 (l / 16) + r][l % 16]).  Workgroup (row block, h, b): 64 query rows,
-// wave w rows 16 w .. 16 w + 15.  Keys and values are staged through LDS 64
-// positions at a time.  Per block a wave computes S = Q K^T / 8 (four 16 x 16
-// tiles), updates each row's running max and sum of exp (a row's 64 scores
-// sit in one 16-lane DPP row), rescales its output, stores P = e^(S - m)
-// in LDS (the D layout of S is not the A layout P needs) and adds P V.
-constexpr int PS = 68;  // LDS row stride (floats) of the K, V and P tiles
+// D[4 (l / 16) + r][l % 16]).  Workgroup (row block, h, b): 16 query rows.
+// The keys the block sees are cut into blocks of 32; wave w takes blocks w,
+// w + 4, ..., so the long rows at the end of a prompt are shared by four
+// waves instead of one.  Per key block a wave stages K and V in its own LDS
+// tiles, computes S = Q K^T / 8 (two 16 x 16 tiles), updates each row's
+// running max and sum of exp (a row's scores sit in one 16-lane DPP row),
+// rescales its output, stores P = e^(S - m) in LDS (the D layout of S is not
+// the A layout P needs) and adds P V.  At the end the four waves' (max, sum,
+// output) are merged through LDS.
+constexpr int PS = 68;   // LDS row stride (floats) of the K, V and P tiles
+constexpr int PKB = 32;  // keys per block (two 16-key S tiles)
+constexpr size_t kAttnPrefillLds = sizeof(float) * 4 * (2 * PKB + 16) * PS;
 
 __global__ __launch_bounds__(256) void k_attn_prefill(const float* __restrict__ q,
+                                                      const float* __restrict__ kc,
+                                                      const float* __restrict__ vc, int layer,
+                                                      int B, int H, int t_cap, int t0, int R,
+                                                      float* __restrict__ out) {
+    extern __shared__ float asm_lds[];
+    const int d = H * 64;
+    const int i0 = blockIdx.x * 16, h = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int lr = lane & 15, lq = lane >> 4;
+    float* Kw = asm_lds + wave * (2 * PKB + 16) * PS;  // [PKB][PS]
+    float* Vw = Kw + PKB * PS;                          // [PKB][PS]
+    float* P = Vw + PKB * PS;                           // [16][PS]
+    // A operand of Q K^T: row i0 + lr, dimensions 4 s + lq
+    const int qi = i0 + lr;
+    float qa[16];
+#pragma unroll
+    for (int s = 0; s < 16; ++s) qa[s] = qi < R ? q[((size_t)b * R + qi) * d + h * 64 + 4 * s + lq] : 0.f;
+    // rows 4 lq + r of the block (query positions)
+    int qpos[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) qpos[r] = t0 + i0 + 4 * lq + r;
+    float m[4], l[4];
+    f32x4 o[4];  // output tiles: dimensions 16 n + lr
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        m[r] = -INFINITY;
+        l[r] = 0.f;
+    }
+#pragma unroll
+    for (int n = 0; n < 4; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int kmax = t0 + min(i0 + 15, R - 1);  // last key any row of the block sees
+    const size_t base = ((size_t)(layer * B + b) * t_cap) * d + h * 64;
+    // K and V rows of a block go through registers: the next block of this
+    // wave is requested before the current one is multiplied
+    constexpr int NE = PKB * 16 / 64;
+    float4 pk[NE], pv[NE];
+    auto load_block = [&](int kb) {
+#pragma unroll
+        for (int e = 0; e < NE; ++e) {
+            const int idx = lane + 64 * e, t = kb + (idx >> 4), c4 = idx & 15;
+            pk[e] = make_float4(0.f, 0.f, 0.f, 0.f);
+            pv[e] = pk[e];
+            if (t <= kmax) {
+                pk[e] = *reinterpret_cast<const float4*>(kc + base + (size_t)t * d + c4 * 4);
+                pv[e] = *reinterpret_cast<const float4*>(vc + base + (size_t)t * d + c4 * 4);
+            }
+        }
+    };
+    if (PKB * wave <= kmax) load_block(PKB * wave);
+    for (int kb = PKB * wave; kb <= kmax; kb += 4 * PKB) {
+        // this wave's K and V block (its own tiles: no workgroup barrier)
+#pragma unroll
+        for (int e = 0; e < NE; ++e) {
+            const int idx = lane + 64 * e, kk = idx >> 4, c4 = idx & 15;
+            *reinterpret_cast<float4*>(Kw + kk * PS + c4 * 4) = pk[e];
+            *reinterpret_cast<float4*>(Vw + kk * PS + c4 * 4) = pv[e];
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        if (kb + 4 * PKB <= kmax) load_block(kb + 4 * PKB);
+        // S tiles n: keys kb + 16 n + lr
+        f32x4 sc[2];
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+            sc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 16; ++s)
+                sc[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[s], Kw[(16 * n + lr) * PS + 4 * s + lq], sc[n], 0, 0, 0);
+        }
+        // mask, row max over the block (in-lane over n, then the 16-lane row)
+        float bm[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            bm[r] = -INFINITY;
+#pragma unroll
+            for (int n = 0; n < 2; ++n) {
+                const int key = kb + 16 * n + lr;
+                float v = sc[n][r] * 0.125f;
+                if (key > qpos[r]) v = -INFINITY;
+                sc[n][r] = v;
+                bm[r] = fmaxf(bm[r], v);
+            }
+            bm[r] = row_max16(bm[r]);
+        }
+        float rs[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float mn = fmaxf(m[r], bm[r]);
+            const float corr = mn == -INFINITY ? 1.f : expf(m[r] - mn);
+            float ps = 0.f;
+#pragma unroll
+            for (int n = 0; n < 2; ++n) {
+                const float p = mn == -INFINITY ? 0.f : expf(sc[n][r] - mn);
+                P[(4 * lq + r) * PS + 16 * n + lr] = p;
+                ps += p;
+            }
+            rs[r] = corr;
+            l[r] = fmaf(l[r], corr, row_sum16(ps));
+            m[r] = mn;
+        }
+#pragma unroll
+        for (int n = 0; n < 4; ++n)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o[n][r] *= rs[r];
+        // O += P V (P rows written by this wave only)
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+#pragma unroll
+        for (int s = 0; s < PKB / 4; ++s) {
+            const float pa = P[lr * PS + 4 * s + lq];
+#pragma unroll
+            for (int n = 0; n < 4; ++n)
+                o[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa, Vw[(4 * s + lq) * PS + 16 * n + lr], o[n], 0, 0, 0);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");  // tiles read before the next block overwrites them
+    }
+    // merge the four waves: output tiles [wave][16][64], (max, sum) [wave][16]
+    __syncthreads();
+    float* mo = asm_lds;
+    float* ml = asm_lds + 4 * 16 * 64;
+#pragma unroll
+    for (int n = 0; n < 4; ++n)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mo[wave * 1024 + (4 * lq + r) * 64 + 16 * n + lr] = o[n][r];
+    if (lr == 0) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            ml[(wave * 16 + 4 * lq + r) * 2] = m[r];
+            ml[(wave * 16 + 4 * lq + r) * 2 + 1] = l[r];
+        }
+    }
+    __syncthreads();
+    const int row = tid >> 4, c = (tid & 15) * 4;
+    if (i0 + row < R) {
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) M = fmaxf(M, ml[(w * 16 + row) * 2]);
+        float L = 0.f;
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const float mw = ml[(w * 16 + row) * 2];
+            if (mw == -INFINITY) continue;
+            const float e = expf(mw - M);
+            L = fmaf(e, ml[(w * 16 + row) * 2 + 1], L);
+            const float4 v = *reinterpret_cast<const float4*>(mo + w * 1024 + row * 64 + c);
+            acc.x = fmaf(e, v.x, acc.x);
+            acc.y = fmaf(e, v.y, acc.y);
+            acc.z = fmaf(e, v.z, acc.z);
+            acc.w = fmaf(e, v.w, acc.w);
+        }
+        const float inv = 1.0f / L;
+        *reinterpret_cast<float4*>(out + ((size_t)b * R + i0 + row) * d + h * 64 + c) =
+            make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+    }
+}
+
+// The same attention with 64 query rows per workgroup (wave w: rows
+// 16 w .. 16 w + 15) and K/V blocks of 64 keys staged once for all four
+// waves.  Used when there are enough row blocks (batched prompts) to fill the
+// GPU: it reads each K/V block once per 64 rows instead of once per 16.
+__global__ __launch_bounds__(256) void k_attn_prefill_wide(const float* __restrict__ q,
                                                       const float* __restrict__ kc,
                                                       const float* __restrict__ vc, int layer,
                                                       int B, int H, int t_cap, int t0, int R,
@@ -828,18 +1003,30 @@ hipError_t launch_w4_matmul(const float* x, int ldx, int M, const Int4Mat& w, co
     }
     if (ln_g || ap.part) return hipErrorInvalidValue;  // the GEMM path takes plain rows
     // one workgroup per tile over all of K: results do not depend on the
-    // order of atomic additions (prefill is bit-reproducible)
+    // order of atomic additions (prefill is bit-reproducible).  32-row tiles
+    // when 64-row tiles would give fewer than two workgroups per CU.
     const int ksplit = 1;
-    const int kspan = (w.K + GK - 1) / GK * GK;
+    const int ntile = (w.N + GN - 1) / GN;
+    const bool small = (long)ntile * ((M + 63) / 64) < 512;
+    const int TM = small ? 32 : 64, GKs = small ? 128 : 64;
+    const int kspan = (w.K + GKs - 1) / GKs * GKs;
     static bool attr = false;
-    const size_t lds = sizeof(float) * 2 * GT * GS;
     if (!attr) {
-        hipError_t e = hipFuncSetAttribute((const void*)k_gemm_w4, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        hipError_t e = hipFuncSetAttribute((const void*)k_gemm_w4<64, 64>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           (int)gemm_lds(64, 64));
+        if (e == hipSuccess)
+            e = hipFuncSetAttribute((const void*)k_gemm_w4<32, 128>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                    (int)gemm_lds(32, 128));
         if (e != hipSuccess) return e;
         attr = true;
     }
-    const dim3 grid((w.N + GT - 1) / GT, (M + GT - 1) / GT, ksplit);
-    hipLaunchKernelGGL(k_gemm_w4, grid, dim3(256), lds, st, x, ldx, M, w.K, w.q, w.s, w.N, y, ldy, ep, kspan);
+    const dim3 grid(ntile, (M + TM - 1) / TM, ksplit);
+    if (small)
+        hipLaunchKernelGGL((k_gemm_w4<32, 128>), grid, dim3(256), gemm_lds(32, 128), st, x, ldx, M, w.K, w.q, w.s,
+                           w.N, y, ldy, ep, kspan);
+    else
+        hipLaunchKernelGGL((k_gemm_w4<64, 64>), grid, dim3(256), gemm_lds(64, 64), st, x, ldx, M, w.K, w.q, w.s,
+                           w.N, y, ldy, ep, kspan);
     return hipGetLastError();
 }
 
@@ -855,8 +1042,20 @@ hipError_t launch_attn_decode(const float* q, const float* kc, const float* vc, 
 
 hipError_t launch_attn_prefill(const float* q, const float* kc, const float* vc, int layer, int B,
                                int H, int t_cap, int t0, int R, float* out, hipStream_t st) {
-    hipLaunchKernelGGL(k_attn_prefill, dim3((R + 63) / 64, H, B), dim3(256), 0, st, q, kc, vc, layer,
-                       B, H, t_cap, t0, R, out);
+    if ((long)((R + 63) / 64) * H * B >= 512) {
+        hipLaunchKernelGGL(k_attn_prefill_wide, dim3((R + 63) / 64, H, B), dim3(256), 0, st, q, kc, vc, layer, B, H,
+                           t_cap, t0, R, out);
+        return hipGetLastError();
+    }
+    static bool attr = false;
+    if (!attr) {
+        hipError_t e = hipFuncSetAttribute((const void*)k_attn_prefill, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           (int)kAttnPrefillLds);
+        if (e != hipSuccess) return e;
+        attr = true;
+    }
+    hipLaunchKernelGGL(k_attn_prefill, dim3((R + 15) / 16, H, B), dim3(256), kAttnPrefillLds, st, q, kc, vc,
+                       layer, B, H, t_cap, t0, R, out);
     return hipGetLastError();
 }
 
