@@ -445,8 +445,10 @@ __global__ __launch_bounds__(256) void k_gemm_w4(const float* __restrict__ X, in
         }
         __syncthreads();
         if (k0 + GK < ke) load_stage(k0 + GK);
-        const int ksteps = min(GK, ke - k0) / 4;
-        for (int kk = 0; kk < ksteps; ++kk) {
+        // all GK / 4 steps, also in a partial last stage: its missing columns
+        // were staged as zero activations and zero weights
+#pragma unroll
+        for (int kk = 0; kk < GK / 4; ++kk) {
             const int k = kk * 4 + (lane >> 4);
             float a[MI], b[2];
 #pragma unroll
