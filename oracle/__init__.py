@@ -25,6 +25,7 @@ _LIB_PATH = os.path.join(_HERE, "_build", "libmt_oracle.so")
 
 _f32p = ctypes.POINTER(ctypes.c_float)
 _u8p = ctypes.POINTER(ctypes.c_uint8)
+_i8p = ctypes.POINTER(ctypes.c_int8)
 _i64p = ctypes.POINTER(ctypes.c_int64)
 
 
@@ -56,6 +57,9 @@ def lib() -> ctypes.CDLL:
         L.oracle_quantize_int4.argtypes = [_f32p, i64, i64, _u8p, _f32p]
         L.oracle_dequantize_int4.argtypes = [_u8p, _f32p, i64, i64, _f32p]
         L.oracle_matmul.argtypes = [_f32p, i64, i64, _f32p, i64, _f32p]
+        L.oracle_quantize_act_int8.argtypes = [_f32p, i64, i64, _i8p, _f32p]
+        L.oracle_matmul_w4a8.argtypes = [_f32p, i64, i64, _u8p, _f32p, i64, _f32p]
+        L.oracle_model_set_w4a8.argtypes = [ctypes.c_void_p, ctypes.c_int]
         L.oracle_layernorm.argtypes = [_f32p, i64, i64, _f32p, _f32p, ctypes.c_float, _f32p]
         L.oracle_gelu.argtypes = [_f32p, i64, _f32p]
         L.oracle_attention.argtypes = [_f32p, _f32p, _f32p, i64, i64, _f32p]
@@ -118,6 +122,30 @@ def matmul(A: np.ndarray, W: np.ndarray) -> np.ndarray:
     return Y
 
 
+def quantize_act_int8(X: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """W4A8 activation codes: [M, K] float32 -> (codes int8 [M, K], scales float32 [M, K/32])."""
+    X = _f32(np.atleast_2d(X))
+    M, K = X.shape
+    q = np.zeros((M, K), dtype=np.int8)
+    s = np.zeros((M, K // 32), dtype=np.float32)
+    _check(lib().oracle_quantize_act_int8(_p(X, _f32p), M, K, _p(q, _i8p), _p(s, _f32p)), "quantize_act")
+    return q, s
+
+
+def matmul_w4a8(A: np.ndarray, q: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """W4A8 product of rows A [M, K] with packed INT4 weights (q [N, K/2], s [N, K/32]) -> [M, N]."""
+    A = _f32(np.atleast_2d(A))
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    s = _f32(s)
+    M, K = A.shape
+    N = q.shape[0]
+    assert q.shape[1] * 2 == K
+    Y = np.zeros((M, N), dtype=np.float32)
+    _check(lib().oracle_matmul_w4a8(_p(A, _f32p), M, K, _p(q, _u8p), _p(s, _f32p), N, _p(Y, _f32p)),
+           "matmul_w4a8")
+    return Y
+
+
 def layernorm(X: np.ndarray, g: np.ndarray, b: np.ndarray, eps: float = 1e-5) -> np.ndarray:
     X = _f32(np.atleast_2d(X))
     M, d = X.shape
@@ -157,9 +185,12 @@ class OracleModel:
             raise ValueError("oracle_model_new rejected the configuration or ran out of memory")
 
     @classmethod
-    def from_weights(cls, w, batch: int, t_cap: int, eps: float = 1e-5, quantize: bool = True):
+    def from_weights(cls, w, batch: int, t_cap: int, eps: float = 1e-5, quantize: bool = True,
+                     w4a8: bool = False):
         s = w.shape
         m = cls(s.n_layers, s.d_model, s.n_heads, s.d_ff, s.vocab, batch, t_cap, eps)
+        if w4a8:
+            m.set_w4a8(True)
         m.set_embed(w.tok_emb, w.lm_head, w.lnf_g, w.lnf_b)
         for l in range(s.n_layers):
             m.set_layer(l, w.w_qkv[l], w.w_o[l], w.w_up[l], w.w_down[l],
@@ -185,6 +216,10 @@ class OracleModel:
         arrs = [_f32(x) for x in (wqkv, wo, wup, wdown, g1, b1, g2, b2)]
         _check(lib().oracle_model_set_layer(self._h, l, *[_p(a, _f32p) for a in arrs],
                                             1 if quantize else 0), "set_layer")
+
+    def set_w4a8(self, on: bool) -> None:
+        """Run the four projections as the W4A8 product (INT8 activation codes)."""
+        _check(lib().oracle_model_set_w4a8(self._h, 1 if on else 0), "set_w4a8")
 
     @property
     def position(self) -> int:

@@ -28,6 +28,16 @@
  * LayerNorm before an untied LM head, round-half-to-even in the quantiser,
  * low nibble = even input index, lowest index wins an argmax tie.
  *
+ * W4A8 variant (one mode flag of the model): the medium ONNX README, "Model
+ * variant", says the quantised MatMuls dynamically quantise their
+ * activations to INT8 and accumulate in INT32.  Block, scale and rounding
+ * are not on the pages; this oracle reads them as: per activation row and
+ * group of 32 inputs (the weight group), s = max|x| / 127 (binary32
+ * division), r = 1 / s (binary32 division), code = clamp(rint(x * r), -127,
+ * 127) (binary32 multiply, ties to even), all-zero group -> codes 0; the
+ * group product sum_k (u_k - 8) * code_k is an exact integer and the output
+ * is sum_g s_w * s_a * I_g, accumulated in binary64 and rounded once.
+ *
  * Precision: every named tensor is stored as binary32; every dot product,
  * LayerNorm moment, softmax and GELU is evaluated in binary64 and rounded once.
  * Must be compiled without fast-math and with FP contraction off.
@@ -113,6 +123,69 @@ int oracle_matmul(const float* A, int64_t M, int64_t K, const float* W, int64_t 
             Y[m * N + n] = (float)acc;
         }
     }
+    return ORACLE_OK;
+}
+
+/* W4A8: INT8 codes of activation rows, per row and group of 32.
+ *   m = max |x| over the group; s = m / 127 (binary32 division);
+ *   r = 1 / s (binary32 division); code = clamp(rint(x * r), -127, 127);
+ *   an all-zero group (s == 0) gets codes 0.  q is [M, K], s is [M, K/32]. */
+int oracle_quantize_act_int8(const float* X, int64_t M, int64_t K, int8_t* q, float* s)
+{
+    if (!X || !q || !s || M < 0 || K <= 0 || K % 32 != 0) return ORACLE_EINVAL;
+    const int64_t ng = K / 32;
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t g = 0; g < ng; ++g) {
+            const float* x = X + m * K + g * 32;
+            float mx = 0.0f;
+            for (int k = 0; k < 32; ++k) {
+                float a = fabsf(x[k]);
+                if (a > mx) mx = a;
+            }
+            float sc = mx / 127.0f;
+            s[m * ng + g] = sc;
+            float r = sc != 0.0f ? 1.0f / sc : 0.0f;
+            for (int k = 0; k < 32; ++k) {
+                float v = rintf(x[k] * r);
+                if (v < -127.0f) v = -127.0f;
+                if (v > 127.0f) v = 127.0f;
+                q[m * K + g * 32 + k] = (int8_t)v;
+            }
+        }
+    return ORACLE_OK;
+}
+
+/* W4A8 product: Y[m, n] = sum_g ws[n, g] * sa[m, g] * I_g with
+ * I_g = sum_{k in g} (u[n, k] - 8) * code[m, k] (exact integer), the codes
+ * from oracle_quantize_act_int8 and the weights as packed INT4 (wq [N, K/2],
+ * ws [N, K/32]).  Binary64 sum over groups, rounded once. */
+int oracle_matmul_w4a8(const float* A, int64_t M, int64_t K, const uint8_t* wq, const float* ws,
+                       int64_t N, float* Y)
+{
+    if (!A || !wq || !ws || !Y || M < 0 || N < 0 || K <= 0 || K % 32 != 0) return ORACLE_EINVAL;
+    const int64_t ng = K / 32;
+    int8_t* qa = (int8_t*)malloc((size_t)(M * K) + 1);
+    float* sa = (float*)malloc(sizeof(float) * (size_t)(M * ng) + 1);
+    if (!qa || !sa) { free(qa); free(sa); return ORACLE_ENOMEM; }
+    oracle_quantize_act_int8(A, M, K, qa, sa);
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t m = 0; m < M; ++m) {
+            double acc = 0.0;
+            for (int64_t g = 0; g < ng; ++g) {
+                int64_t I = 0;
+                for (int k = 0; k < 32; ++k) {
+                    const int64_t kk = g * 32 + k;
+                    const uint8_t byte = wq[(n * K + kk) / 2];
+                    const int u = (kk & 1) ? (byte >> 4) : (byte & 0x0F);
+                    I += (int64_t)(u - 8) * (int64_t)qa[m * K + kk];
+                }
+                acc += (double)ws[n * ng + g] * (double)sa[m * ng + g] * (double)I;
+            }
+            Y[m * N + n] = (float)acc;
+        }
+    free(qa);
+    free(sa);
     return ORACLE_OK;
 }
 
@@ -209,6 +282,9 @@ typedef struct {
     float** wup;    /* [F, d] */
     float** wdown;  /* [d, F] */
     float** ln;     /* [4, d]: g1, b1, g2, b2 */
+    uint8_t** cq;   /* W4A8: packed codes of the 4 projections of layer l, or NULL */
+    float** cs;     /*       their group scales */
+    int w4a8;       /* 1: the projections run the W4A8 product */
     float* kc;      /* [L, B, Tcap, H, 64] */
     float* vc;
 } oracle_model;
@@ -219,8 +295,9 @@ static void model_free(oracle_model* m)
     if (m->wqkv)
         for (int64_t l = 0; l < m->L; ++l) {
             free(m->wqkv[l]); free(m->wo[l]); free(m->wup[l]); free(m->wdown[l]); free(m->ln[l]);
+            free(m->cq[l]); free(m->cs[l]);
         }
-    free(m->wqkv); free(m->wo); free(m->wup); free(m->wdown); free(m->ln);
+    free(m->wqkv); free(m->wo); free(m->wup); free(m->wdown); free(m->ln); free(m->cq); free(m->cs);
     free(m->tok_emb); free(m->lm_head); free(m->lnf); free(m->kc); free(m->vc);
     free(m);
 }
@@ -241,13 +318,15 @@ oracle_model* oracle_model_new(int64_t L, int64_t d, int64_t H, int64_t F, int64
     m->wup = (float**)calloc((size_t)L, sizeof(float*));
     m->wdown = (float**)calloc((size_t)L, sizeof(float*));
     m->ln = (float**)calloc((size_t)L, sizeof(float*));
+    m->cq = (uint8_t**)calloc((size_t)L, sizeof(uint8_t*));
+    m->cs = (float**)calloc((size_t)L, sizeof(float*));
     m->tok_emb = (float*)calloc((size_t)(V * d), sizeof(float));
     m->lm_head = (float*)calloc((size_t)(V * d), sizeof(float));
     m->lnf = (float*)calloc((size_t)(2 * d), sizeof(float));
     size_t kv = (size_t)(L * B * Tcap * d);
     m->kc = (float*)calloc(kv, sizeof(float));
     m->vc = (float*)calloc(kv, sizeof(float));
-    if (!m->wqkv || !m->wo || !m->wup || !m->wdown || !m->ln || !m->tok_emb || !m->lm_head ||
+    if (!m->wqkv || !m->wo || !m->wup || !m->wdown || !m->ln || !m->cq || !m->cs || !m->tok_emb || !m->lm_head ||
         !m->lnf || !m->kc || !m->vc) {
         model_free(m);
         return NULL;
@@ -290,8 +369,23 @@ int oracle_model_set_layer(oracle_model* m, int64_t l, const float* wqkv, const 
         return ORACLE_EINVAL;
     const int64_t d = m->d, F = m->F;
     free(m->wqkv[l]); free(m->wo[l]); free(m->wup[l]); free(m->wdown[l]); free(m->ln[l]);
+    free(m->cq[l]); free(m->cs[l]);
     m->wqkv[l] = m->wo[l] = m->wup[l] = m->wdown[l] = m->ln[l] = NULL;
+    m->cq[l] = NULL;
+    m->cs[l] = NULL;
     if (quantize) {
+        /* codes of QKV [3d, d], O [d, d], up [F, d], down [d, F], in that order */
+        const int64_t nw = 4 * d * d + 2 * F * d;
+        m->cq[l] = (uint8_t*)calloc((size_t)(nw / 2), 1);
+        m->cs[l] = (float*)malloc(sizeof(float) * (size_t)(nw / 32));
+        if (!m->cq[l] || !m->cs[l]) return ORACLE_ENOMEM;
+        const float* mats[4] = {wqkv, wo, wup, wdown};
+        const int64_t Ns[4] = {3 * d, d, F, d}, Ks[4] = {d, d, d, F};
+        int64_t off = 0;
+        for (int i = 0; i < 4; ++i) {
+            oracle_quantize_int4(mats[i], Ns[i], Ks[i], m->cq[l] + off / 2, m->cs[l] + off / 32);
+            off += Ns[i] * Ks[i];
+        }
         m->wqkv[l] = quant_dequant(wqkv, 3 * d, d);
         m->wo[l] = quant_dequant(wo, d, d);
         m->wup[l] = quant_dequant(wup, F, d);
@@ -317,6 +411,29 @@ int oracle_model_set_layer(oracle_model* m, int64_t l, const float* wqkv, const 
 
 int64_t oracle_model_position(const oracle_model* m) { return m ? m->tpast : -1; }
 
+/* 1: the four projections run the W4A8 product (needs quantised layers). */
+int oracle_model_set_w4a8(oracle_model* m, int on)
+{
+    if (!m) return ORACLE_EINVAL;
+    m->w4a8 = on ? 1 : 0;
+    return ORACLE_OK;
+}
+
+/* Projection i (0 QKV, 1 O, 2 up, 3 down) of layer l applied to rows A. */
+static void project(const oracle_model* m, int64_t l, int i, const float* A, int64_t rows, float* Y)
+{
+    const int64_t d = m->d, F = m->F;
+    const int64_t Ns[4] = {3 * d, d, F, d}, Ks[4] = {d, d, d, F};
+    if (m->w4a8) {
+        int64_t off = 0;
+        for (int j = 0; j < i; ++j) off += Ns[j] * Ks[j];
+        oracle_matmul_w4a8(A, rows, Ks[i], m->cq[l] + off / 2, m->cs[l] + off / 32, Ns[i], Y);
+        return;
+    }
+    const float* W[4] = {m->wqkv[l], m->wo[l], m->wup[l], m->wdown[l]};
+    oracle_matmul(A, rows, Ks[i], W[i], Ns[i], Y);
+}
+
 void oracle_model_reset(oracle_model* m)
 {
     if (m) m->tpast = 0;
@@ -341,7 +458,7 @@ int oracle_model_forward(oracle_model* m, const int64_t* tokens, int64_t S, cons
     if (!m || S < 0 || P < 0 || P + S < 1 || !logits || !next) return ORACLE_EINVAL;
     if ((S > 0 && !tokens) || (P > 0 && !prefix)) return ORACLE_EINVAL;
     for (int64_t l = 0; l < m->L; ++l)
-        if (!m->wqkv[l] || !m->ln[l]) return ORACLE_EINVAL;
+        if (!m->wqkv[l] || !m->ln[l] || (m->w4a8 && !m->cq[l])) return ORACLE_EINVAL;
     const int64_t L = m->L, d = m->d, H = m->H, F = m->F, V = m->V, B = m->B, Tc = m->Tcap;
     const int64_t R = P + S, t0 = m->tpast;
     if (t0 + R > Tc) return ORACLE_EFULL;
@@ -372,7 +489,7 @@ int oracle_model_forward(oracle_model* m, const int64_t* tokens, int64_t S, cons
     for (int64_t l = 0; l < L; ++l) {
         const float* ln = m->ln[l];
         oracle_layernorm(r, rows, d, ln, ln + d, m->eps, a);
-        oracle_matmul(a, rows, d, m->wqkv[l], 3 * d, qkv);
+        project(m, l, 0, a, rows, qkv);
         /* cache write: K = columns [d, 2d), V = [2d, 3d); head h = 64 columns */
         for (int64_t b = 0; b < B; ++b)
             for (int64_t i = 0; i < R; ++i) {
@@ -396,12 +513,12 @@ int oracle_model_forward(oracle_model* m, const int64_t* tokens, int64_t S, cons
                     }
             free(scratch);
         }
-        oracle_matmul(att, rows, d, m->wo[l], d, o);
+        project(m, l, 1, att, rows, o);
         for (int64_t j = 0; j < rows * d; ++j) r[j] = r[j] + o[j];
         oracle_layernorm(r, rows, d, ln + 2 * d, ln + 3 * d, m->eps, a);
-        oracle_matmul(a, rows, d, m->wup[l], F, h1);
+        project(m, l, 2, a, rows, h1);
         oracle_gelu(h1, rows * F, h1);
-        oracle_matmul(h1, rows, F, m->wdown[l], d, o);
+        project(m, l, 3, h1, rows, o);
         for (int64_t j = 0; j < rows * d; ++j) r[j] = r[j] + o[j];
     }
 

@@ -386,3 +386,114 @@ def test_model_quantized_equals_dequantized_input(oracle_mod):
     md = oracle_mod.OracleModel.from_weights(w, batch=1, t_cap=3, quantize=False)
     ld, _ = md.forward(prefix=x)
     assert np.array_equal(lq, ld)
+
+
+# ---------------------------------------------------------------- W4A8 variant
+
+def _act_ref(x):
+    """The activation-code definition in numpy binary32, element by element."""
+    x = np.asarray(x, np.float32)
+    m = np.float32(np.max(np.abs(x)))
+    s = np.float32(m / np.float32(127.0))
+    if s == 0:
+        return np.zeros(x.shape, np.int8), s
+    r = np.float32(np.float32(1.0) / s)
+    q = np.clip(np.rint((x * r).astype(np.float32)), -127, 127).astype(np.int8)
+    return q, s
+
+
+def test_act_int8_hand_cases(oracle_mod):
+    """Hand-computed groups: scale exactly 1, 0.5 and 2, ties to even, an
+    all-zero group (catches a round-away-from-zero, a 128 divisor or a
+    missing zero guard)."""
+    g = np.zeros((4, 32), np.float32)
+    g[0, :5] = [127.0, 2.5, 3.5, -2.5, 0.5]          # s = 1
+    g[1, :5] = [63.5, 1.25, 0.75, -0.25, -63.5]       # s = 0.5
+    g[2, :4] = [-254.0, 3.0, 1.0, -5.0]               # s = 2
+    q, s = oracle_mod.quantize_act_int8(g.reshape(1, 128))
+    assert np.array_equal(s[0], np.array([1.0, 0.5, 2.0, 0.0], np.float32))
+    q = q.reshape(4, 32)
+    assert list(q[0, :5]) == [127, 2, 4, -2, 0]
+    assert list(q[1, :5]) == [127, 2, 2, 0, -127]
+    assert list(q[2, :4]) == [-127, 2, 0, -2]
+    assert not q[0, 5:].any() and not q[3].any()
+
+
+def test_act_int8_matches_definition_and_bound(oracle_mod):
+    """Random rows over a wide range: codes equal the binary32 definition,
+    |x - s q| <= s / 2, the largest element maps to +-127, codes are odd in x."""
+    rng = np.random.default_rng(40)
+    X = (rng.standard_normal((6, 256)) * np.exp(rng.uniform(-8, 8, (6, 256)))).astype(np.float32)
+    q, s = oracle_mod.quantize_act_int8(X)
+    qn, sn = oracle_mod.quantize_act_int8(-X)
+    assert np.array_equal(qn, -q) and np.array_equal(sn, s)
+    for m in range(6):
+        for g in range(8):
+            x = X[m, 32 * g:32 * g + 32]
+            qr, sr = _act_ref(x)
+            assert s[m, g] == sr
+            assert np.array_equal(q[m, 32 * g:32 * g + 32], qr)
+            err = np.abs(x.astype(np.float64) - np.float64(sr) * q[m, 32 * g:32 * g + 32])
+            assert np.all(err <= 0.5 * np.float64(sr) * (1 + 2.0 ** -20))
+            assert np.max(np.abs(q[m, 32 * g:32 * g + 32])) == 127
+
+
+def test_matmul_w4a8_exact_brute_force(oracle_mod):
+    """The W4A8 product against exact rational arithmetic from the codes
+    (catches a dropped scale, a wrong nibble order or a group index slip)."""
+    rng = np.random.default_rng(41)
+    A = rng.standard_normal((3, 96)).astype(np.float32)
+    W = (0.05 * rng.standard_normal((4, 96))).astype(np.float32)
+    wq, ws = oracle_mod.quantize_int4(W)
+    Y = oracle_mod.matmul_w4a8(A, wq, ws)
+    assert Y.shape == (3, 4)
+    u = np.zeros((4, 96), np.int64)
+    u[:, 0::2] = wq & 15
+    u[:, 1::2] = wq >> 4
+    for m in range(3):
+        qa, sa = zip(*[_act_ref(A[m, 32 * g:32 * g + 32]) for g in range(3)])
+        for n in range(4):
+            exact = Fraction(0)
+            for g in range(3):
+                I = int(np.sum((u[n, 32 * g:32 * g + 32] - 8) * qa[g].astype(np.int64)))
+                exact += Fraction(float(ws[n, g])) * Fraction(float(sa[g])) * I
+            assert abs(Fraction(float(Y[m, n])) - exact) <= abs(exact) * Fraction(1, 2 ** 23) + Fraction(1, 2 ** 120)
+
+
+def test_matmul_w4a8_integer_activations_equal_w4a32(oracle_mod):
+    """Activations that are integers with a group maximum of 127 have scale 1
+    and codes equal to themselves; with power-of-two weight scales both
+    products are the same exact sum, so the results are bit-equal."""
+    rng = np.random.default_rng(42)
+    A = rng.integers(-127, 128, (2, 64)).astype(np.float32)
+    A[:, 0] = 127.0
+    A[:, 32] = -127.0
+    W = rng.integers(-7, 8, (5, 64)).astype(np.float32) * np.float32(0.25)
+    W[:, 0] = 7 * 0.25
+    W[:, 32] = -7 * 0.25
+    wq, ws = oracle_mod.quantize_int4(W)
+    assert np.all(ws == 0.25)
+    y8 = oracle_mod.matmul_w4a8(A, wq, ws)
+    y32 = oracle_mod.matmul(A, oracle_mod.dequantize_int4(wq, ws))
+    assert np.array_equal(y8, y32)
+
+
+def test_model_w4a8_projections_use_w4a8_product(oracle_mod):
+    """In W4A8 mode the layer-0 K and V cache rows are the W4A8 product of
+    LayerNorm(prefix) with the layer's QKV codes (ties the model to the pinned
+    product), and they differ from the W4A32 rows."""
+    shape = synth.tiny_shape(n_layers=1)
+    w = _tiny_weights(shape, seed=43)
+    d = shape.d_model
+    x = np.random.default_rng(2).standard_normal((1, 3, d)).astype(np.float32)
+    m8 = oracle_mod.OracleModel.from_weights(w, batch=1, t_cap=3, w4a8=True)
+    m8.forward(prefix=x)
+    k8, v8 = m8.kv()
+    a = oracle_mod.layernorm(x[0], w.ln1_g[0], w.ln1_b[0])
+    qkv = oracle_mod.matmul_w4a8(a, *oracle_mod.quantize_int4(w.w_qkv[0]))
+    assert np.array_equal(k8[0, 0].reshape(3, d), qkv[:, d:2 * d])
+    assert np.array_equal(v8[0, 0].reshape(3, d), qkv[:, 2 * d:])
+    m32 = oracle_mod.OracleModel.from_weights(w, batch=1, t_cap=3)
+    m32.forward(prefix=x)
+    k32, _ = m32.kv()
+    assert not np.array_equal(k8, k32)
