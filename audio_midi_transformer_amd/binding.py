@@ -27,6 +27,8 @@ MT_DECODE_AUTO = 0
 MT_DECODE_KERNELS = 1
 MT_DECODE_PERSISTENT = 2
 
+MT_FLAG_W4A8 = 1
+
 # Names declared in include/mt.h; the CPU test checks the library exports all.
 EXPORTED = ("mt_pack_int4", "mt_create", "mt_prefill", "mt_decode_step", "mt_reset",
             "mt_position", "mt_kv_cache", "mt_check", "mt_set_decode_path", "mt_destroy",
@@ -139,13 +141,13 @@ class Decoder:
     """Owns one mt_model.  Inputs and outputs are torch tensors on the GPU."""
 
     def __init__(self, weights, batch: int, t_cap: int, eps: float = 1e-5,
-                 packed: Optional[Sequence[Tuple[np.ndarray, np.ndarray]]] = None):
+                 packed: Optional[Sequence[Tuple[np.ndarray, np.ndarray]]] = None, flags: int = 0):
         import torch
         s = weights.shape
         self.shape, self.batch, self.t_cap = s, batch, t_cap
         self.L, self.d, self.H, self.F, self.V = s.n_layers, s.d_model, s.n_heads, s.d_ff, s.vocab
         cfg = mt_config(s.n_layers, s.d_model, s.n_heads, 64, s.d_ff, s.vocab, 32, batch, t_cap,
-                        eps, 0)
+                        eps, flags)
         if packed is None:
             packed = pack_weights(weights)
         keep = []

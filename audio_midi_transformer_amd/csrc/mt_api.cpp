@@ -104,7 +104,7 @@ int check_config(const mt_config* c) {
     if (!c) return fail(MT_ERR_INVALID_ARG, "config is NULL");
     if (c->head_dim != 64) return fail(MT_ERR_UNSUPPORTED, "head_dim must be 64 (got %d)", c->head_dim);
     if (c->group != 32) return fail(MT_ERR_UNSUPPORTED, "group must be 32 (got %d)", c->group);
-    if (c->flags != 0) return fail(MT_ERR_UNSUPPORTED, "flags must be 0");
+    if (c->flags & ~(uint32_t)MT_FLAG_W4A8) return fail(MT_ERR_UNSUPPORTED, "unknown flags 0x%x", c->flags);
     if (c->n_layers < 1 || c->n_heads < 1 || c->vocab < 1 || c->batch < 1 || c->batch > 64 ||
         c->t_cap < 1 || c->t_cap > kMaxTcap || c->d_ff < 32)
         return fail(MT_ERR_INVALID_ARG, "non-positive or out-of-range size in config");
@@ -146,6 +146,7 @@ int run_layers(mt_model* m, float* x, float* a, float* q, float* att, float* h, 
                bool decode, hipStream_t st) {
     const mt_config& c = m->c;
     const int d = c.d_model, F = c.d_ff, B = c.batch, M = B * R;
+    const bool a8 = (c.flags & MT_FLAG_W4A8) != 0;
     // with few rows the GEMV applies both LayerNorms itself
     const bool fuse_ln = gemv_fuses_layernorm(M, d);
     for (int l = 0; l < c.n_layers; ++l) {
@@ -153,11 +154,11 @@ int run_layers(mt_model* m, float* x, float* a, float* q, float* att, float* h, 
         QkvDest dst{q, m->kc, m->vc, d, l, B, c.t_cap, t0, R};
         if (fuse_ln) {
             HIP_TRY(launch_w4_matmul(x, d, M, m->proj[l * 4 + 0], ln, ln + d, c.ln_eps, nullptr, 0, EPI_QKV, &dst,
-                                     false, st));
+                                     false, st, nullptr, a8));
         } else {
             HIP_TRY(launch_layernorm(x, d, ln, ln + d, c.ln_eps, d, M, a, d, st));
             HIP_TRY(launch_w4_matmul(a, d, M, m->proj[l * 4 + 0], nullptr, nullptr, 0.f, nullptr, 0, EPI_QKV, &dst,
-                                     false, st));
+                                     false, st, nullptr, a8));
         }
         if (decode && gemv_fuses_layernorm(M, d)) {
             // split-K attention; the O projection merges the partials
@@ -166,22 +167,22 @@ int run_layers(mt_model* m, float* x, float* a, float* q, float* att, float* h, 
             HIP_TRY(launch_attn_decode(q, m->kc, m->vc, l, B, c.n_heads, c.t_cap, t0 + 1, m->part, ns, ch, st));
             const AttnParts ap{m->part, c.n_heads, ns};
             HIP_TRY(launch_w4_matmul(nullptr, d, M, m->proj[l * 4 + 1], nullptr, nullptr, 0.f, x, d, EPI_RESID,
-                                     nullptr, false, st, &ap));
+                                     nullptr, false, st, &ap, a8));
         } else {
             HIP_TRY(launch_attn_prefill(q, m->kc, m->vc, l, B, c.n_heads, c.t_cap, t0, R, att, st));
             HIP_TRY(launch_w4_matmul(att, d, M, m->proj[l * 4 + 1], nullptr, nullptr, 0.f, x, d, EPI_RESID, nullptr,
-                                     false, st));
+                                     false, st, nullptr, a8));
         }
         if (fuse_ln) {
             HIP_TRY(launch_w4_matmul(x, d, M, m->proj[l * 4 + 2], ln + 2 * d, ln + 3 * d, c.ln_eps, h, F, EPI_GELU,
-                                     nullptr, false, st));
+                                     nullptr, false, st, nullptr, a8));
         } else {
             HIP_TRY(launch_layernorm(x, d, ln + 2 * d, ln + 3 * d, c.ln_eps, d, M, a, d, st));
             HIP_TRY(launch_w4_matmul(a, d, M, m->proj[l * 4 + 2], nullptr, nullptr, 0.f, h, F, EPI_GELU, nullptr,
-                                     false, st));
+                                     false, st, nullptr, a8));
         }
         HIP_TRY(launch_w4_matmul(h, F, M, m->proj[l * 4 + 3], nullptr, nullptr, 0.f, x, d, EPI_RESID, nullptr,
-                                 false, st));
+                                 false, st, nullptr, a8));
     }
     return MT_OK;
 }
@@ -313,7 +314,8 @@ int mt_create(const mt_config* cfg, const mt_weights* w, int weights_on_device, 
         hipMemcpyAsync(m->ws_ptrs, hs.data(), hs.size() * sizeof(void*), hipMemcpyHostToDevice, st) ||
         hipMemsetAsync(m->err, 0, 16, st))
         return bail(fail(MT_ERR_HIP, "mt_create: table copy failed"));
-    m->persistent_ok = persistent_supported(d, F, H, B, V);
+    // the persistent step computes the W4A32 projections only
+    m->persistent_ok = persistent_supported(d, F, H, B, V) && !(m->c.flags & MT_FLAG_W4A8);
     if (m->persistent_ok) {
         const size_t xb = persistent_xbuf_bytes(L, d, F, H, B, V);
         if (hipMalloc(&m->xbuf, xb) != hipSuccess || hipMemsetAsync(m->xbuf, 0, xb, st) != hipSuccess)
@@ -468,7 +470,7 @@ int mt_debug_matmul(mt_model* m, int32_t layer, int32_t proj, const float* x, in
         return fail(MT_ERR_INVALID_ARG, "mt_debug_matmul: bad layer/projection");
     const Int4Mat& w = m->proj[layer * 4 + p];
     HIP_TRY(launch_w4_matmul(x, w.K, M, w, nullptr, nullptr, 0.f, y, w.N, EPI_STORE, nullptr, force_gemm || M > 8,
-                             (hipStream_t)stream));
+                             (hipStream_t)stream, nullptr, (m->c.flags & MT_FLAG_W4A8) != 0));
     return MT_OK;
 }
 

@@ -52,7 +52,7 @@ struct AttnParts {
 // (x is not read; GEMV path only).
 hipError_t launch_w4_matmul(const float* x, int ldx, int M, const Int4Mat& w, const float* ln_g,
                             const float* ln_b, float eps, float* y, int ldy, Epilogue epi, const QkvDest* qkv,
-                            bool force_gemm, hipStream_t st, const AttnParts* parts = nullptr);
+                            bool force_gemm, hipStream_t st, const AttnParts* parts = nullptr, bool a8 = false);
 bool gemv_fuses_layernorm(int M, int K);
 // Writes the split-K partials only; the O projection merges them.
 hipError_t launch_attn_decode(const float* q, const float* kc, const float* vc, int layer, int B,

@@ -23,6 +23,7 @@
 namespace mt {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------- helpers
 
@@ -180,6 +181,14 @@ constexpr int GV_M = 8;           // activation rows held in LDS
 // LDS.  With more than one k split the results are added to Y atomically
 // (the += epilogue only).  Lane l converts weight W'[n0 + l % 16][k + l / 16]
 // as s * u - 8 s (one rounding, equal to (u - 8) * s).
+//
+// A8 (W4A8 variant): after staging, each (row, group of 32) of the staged
+// activations is coded to INT8 (s_a = max|x| / 127, code = clamp(rint(x *
+// (1 / s_a)), +-127)) in LDS, and each group is one v_mfma_i32_16x16x32_i8
+// with A = activation codes (16 rows, 8 used) and B = 16 (u - 8) of 16
+// weight rows; the INT32 tile is exact and is added to the FP32 result as
+// I * s_a * s_w / 16.
+template <bool A8>
 __global__ __launch_bounds__(256) void k_gemv_w4(const float* __restrict__ X, int ldx, int M, int K, int kspan,
                                                  const float* __restrict__ ln_g, const float* __restrict__ ln_b,
                                                  float eps, const float* __restrict__ part, int H, int ns,
@@ -315,6 +324,76 @@ __global__ __launch_bounds__(256) void k_gemv_w4(const float* __restrict__ X, in
             }
         }
         __syncthreads();
+        if constexpr (A8) {
+            // ---- INT8 codes of the staged rows, one (row, group) per thread
+            // and pass: codes [GV_M][cw] bytes, scales [gch][GV_M]
+            const size_t wfl = part ? (size_t)M * (cw / 64) * ns : 0;
+            int8_t* xq = reinterpret_cast<int8_t*>(xt + (size_t)XS * GV_M + ((wfl + 3) & ~(size_t)3));
+            float* xsa = reinterpret_cast<float*>(xq + (size_t)GV_M * cw);
+            for (int p = tid; p < GV_M * gch; p += 256) {
+                const int m = p & (GV_M - 1), g = p / GV_M;
+                const float* src = xt + m * XS + g * 32;
+                float v[32];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const float4 t = *reinterpret_cast<const float4*>(src + 4 * j);
+                    v[4 * j] = t.x;
+                    v[4 * j + 1] = t.y;
+                    v[4 * j + 2] = t.z;
+                    v[4 * j + 3] = t.w;
+                }
+                float amax = 0.f;
+#pragma unroll
+                for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(v[j]));
+                const float sa = amax / 127.0f;
+                const float ra = sa != 0.f ? 1.0f / sa : 0.f;
+                unsigned pk[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    unsigned w = 0;
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) {
+                        const float c = fminf(fmaxf(rintf(__fmul_rn(v[4 * j + b], ra)), -127.f), 127.f);
+                        w |= ((unsigned)(int)c & 0xFFu) << (8 * b);
+                    }
+                    pk[j] = w;
+                }
+                uint4* dst = reinterpret_cast<uint4*>(xq + (size_t)m * cw + g * 32);
+                dst[0] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+                dst[1] = make_uint4(pk[4], pk[5], pk[6], pk[7]);
+                xsa[g * GV_M + m] = sa;
+            }
+            __syncthreads();
+            // ---- one INT8 MFMA per group.  A: lane l gives codes k = 8 kq ..
+            // 8 kq + 7 of activation row l % 16 (zero for rows >= GV_M); B:
+            // 16 (u - 8) of weight row n0 + l % 16 at the same k, built from
+            // dword kq of the group (low nibbles = even k) by sign-flipping
+            // the nibbles and interleaving the two halves with v_perm.
+            const bool avalid = bm < GV_M;
+            const int8_t* xa = xq + (size_t)(bm & (GV_M - 1)) * cw + 8 * kq;
+#pragma unroll
+            for (int i = 0; i < GV_MAXSPAN / 128; ++i) {
+                if (i < ngw) {
+                    const int gi = wv + 4 * i;
+                    const unsigned wd = kq == 0 ? wq[i].x : kq == 1 ? wq[i].y : kq == 2 ? wq[i].z : wq[i].w;
+                    const unsigned x8 = wd ^ 0x88888888u;
+                    const unsigned lo = (x8 << 4) & 0xF0F0F0F0u, hi = x8 & 0xF0F0F0F0u;
+                    const unsigned b0 = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
+                    const unsigned b1 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
+                    const long bop = (long)(((unsigned long)b1 << 32) | b0);
+                    const long aop = avalid ? *reinterpret_cast<const long*>(xa + gi * 32) : 0L;
+                    const i32x4 d = __builtin_amdgcn_mfma_i32_16x16x32_i8(aop, bop, i32x4{0, 0, 0, 0}, 0, 0, 0);
+                    const float sw = sc[i] * 0.0625f;
+                    const float4 sa = *reinterpret_cast<const float4*>(xsa + gi * GV_M + 4 * (kq & 1));
+                    f32x4& ac = (i & 1) ? acc1 : acc0;
+                    ac[0] = fmaf((float)d[0], sa.x * sw, ac[0]);
+                    ac[1] = fmaf((float)d[1], sa.y * sw, ac[1]);
+                    ac[2] = fmaf((float)d[2], sa.z * sw, ac[2]);
+                    ac[3] = fmaf((float)d[3], sa.w * sw, ac[3]);
+                }
+            }
+            continue;
+        }
         // ---- MFMA over this wave's groups, alternate groups into two
         // accumulators.  Column 4 s + kq of a group: byte 2 s + kq / 2, low
         // nibble for even kq.  Lanes feeding B columns 8..15 read row
@@ -344,8 +423,12 @@ __global__ __launch_bounds__(256) void k_gemv_w4(const float* __restrict__ X, in
     }
     const f32x4 acc = acc0 + acc1;
     // ---- sum the four waves' tiles; lane l holds D[4 (l / 16) + r][l % 16]
+    // (weight row x activation row; transposed in the A8 form)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) dred[wave][4 * kq + r][lane & 15] = acc[r];
+    for (int r = 0; r < 4; ++r) {
+        if (A8) dred[wave][lane & 15][4 * kq + r] = acc[r];
+        else dred[wave][4 * kq + r][lane & 15] = acc[r];
+    }
     __syncthreads();
     const int n = tid >> 4, m = tid & 15;
     if (m < M && n0 + n < N) {
@@ -474,6 +557,138 @@ __global__ __launch_bounds__(256) void k_gemm_w4(const float* __restrict__ X, in
                     if (gridDim.z > 1) atomicAdd(Y + (size_t)m * ldy + n, acc[i][j][r]);
                     else epilogue(ep, Y, ldy, m, n, acc[i][j][r]);
                 }
+            }
+}
+
+// W4A8 form of the GEMM: Y[M, N] = sum_g s_w s_a I_g, I_g the exact INT32
+// product of a group's activation codes (coded per row and group of 32 while
+// staged: s_a = max|x| / 127, code = clamp(rint(x * (1 / s_a)), +-127)) and
+// the weights' (u - 8).  Tile TM x 64, K stages of GK columns, four waves as
+// 2 x 2 of (TM / 2) x 32; per group one v_mfma_i32_16x16x32_i8 per 16 x 16
+// block, A = activation codes (lane l: row l % 16, k = 8 (l / 16) .. + 7),
+// B = 16 (u - 8) (lane l: weight row l % 16, same k), D[4 (l / 16) + r][l % 16];
+// the INT32 block is added to the FP32 result as I * s_a * s_w / 16.
+constexpr int QS = 8;  // LDS row padding (bytes) of the code tiles
+
+template <int TM, int GK>
+__global__ __launch_bounds__(256) void k_gemm_w4a8(const float* __restrict__ X, int ldx, int M, int K,
+                                                   const uint8_t* __restrict__ Wq,
+                                                   const float* __restrict__ Ws, int N,
+                                                   float* __restrict__ Y, int ldy, EpiArgs ep) {
+    constexpr int MI = TM / 32;
+    constexpr int NG = GK / 32;       // groups per stage
+    constexpr int RS = GK + QS;       // code row stride (bytes)
+    __shared__ __align__(16) int8_t Aq[TM * RS];
+    __shared__ __align__(16) int8_t Bq[GN * RS];
+    __shared__ __align__(16) float As_s[NG][TM];  // activation scales [group][row]
+    __shared__ float Bs_s[NG][GN];    // weight scales / 16 [group][row]
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int m0 = blockIdx.y * TM, n0 = blockIdx.x * GN;
+    const int G = K / 32;
+    f32x4 acc[MI][2];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // stage loads as in the FP32 GEMM: TM * GK / 1024 float4 of X per thread;
+    // thread t: quarter t % 4 of weight row t / 4 (GK / 4 columns in one group)
+    constexpr int NA = TM * GK / 4 / 256;
+    constexpr int NW = GK / 32;
+    float4 pa[NA];
+    unsigned pw[NW];
+    float ps = 0.f;
+    const int wrow = tid >> 2, wq = tid & 3;
+    auto load_stage = [&](int k0) {
+#pragma unroll
+        for (int e = 0; e < NA; ++e) {
+            const int idx = tid + e * 256;
+            const int r = idx / (GK / 4), c = (idx % (GK / 4)) * 4;
+            pa[e] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (m0 + r < M && k0 + c < K) pa[e] = *reinterpret_cast<const float4*>(X + (size_t)(m0 + r) * ldx + k0 + c);
+        }
+        const int c0 = k0 + wq * (GK / 4), g = c0 / 32;
+        const bool ok = n0 + wrow < N && c0 < K;
+#pragma unroll
+        for (int i = 0; i < NW; ++i)
+            pw[i] = ok ? *reinterpret_cast<const unsigned*>(Wq + (size_t)(n0 + wrow) * (K / 2) + c0 / 2 + 4 * i)
+                       : 0x88888888u;
+        ps = ok ? Ws[(size_t)(n0 + wrow) * G + g] : 0.f;
+    };
+    load_stage(0);
+    for (int k0 = 0; k0 < K; k0 += GK) {
+        if (k0) __syncthreads();  // the previous stage has been multiplied
+        // activation codes: the 8 float4 of a (row, group) sit in 8
+        // consecutive lanes; their maximum by DPP within the 8 lanes
+#pragma unroll
+        for (int e = 0; e < NA; ++e) {
+            const int idx = tid + e * 256;
+            const int r = idx / (GK / 4), c = (idx % (GK / 4)) * 4;
+            float am = fmaxf(fmaxf(fabsf(pa[e].x), fabsf(pa[e].y)), fmaxf(fabsf(pa[e].z), fabsf(pa[e].w)));
+            am = fmaxf(am, dppf<0xB1>(am));   // quad_perm [1,0,3,2]
+            am = fmaxf(am, dppf<0x4E>(am));   // quad_perm [2,3,0,1]
+            am = fmaxf(am, dppf<0x141>(am));  // row_half_mirror: the 8-lane group
+            const float sa = am / 127.0f;
+            const float ra = sa != 0.f ? 1.0f / sa : 0.f;
+            const float v[4] = {pa[e].x, pa[e].y, pa[e].z, pa[e].w};
+            unsigned w = 0;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const float cd = fminf(fmaxf(rintf(__fmul_rn(v[b], ra)), -127.f), 127.f);
+                w |= ((unsigned)(int)cd & 0xFFu) << (8 * b);
+            }
+            *reinterpret_cast<unsigned*>(Aq + r * RS + c) = w;
+            if ((c & 31) == 0) As_s[c >> 5][r] = sa;
+        }
+        // weight codes 16 (u - 8): sign-flip the nibbles, split even / odd
+        // k, interleave back to k order with v_perm
+        {
+            int8_t* dst = Bq + wrow * RS + wq * (GK / 4);
+#pragma unroll
+            for (int i = 0; i < NW; ++i) {
+                const unsigned x8 = pw[i] ^ 0x88888888u;
+                const unsigned lo = (x8 << 4) & 0xF0F0F0F0u, hi = x8 & 0xF0F0F0F0u;
+                *reinterpret_cast<uint2*>(dst + 8 * i) =
+                    make_uint2(__builtin_amdgcn_perm(hi, lo, 0x05010400u), __builtin_amdgcn_perm(hi, lo, 0x07030602u));
+            }
+            if (((wq * (GK / 4)) & 31) == 0) Bs_s[(wq * (GK / 4)) >> 5][wrow] = ps * 0.0625f;
+        }
+        __syncthreads();
+        if (k0 + GK < K) load_stage(k0 + GK);
+        const int kq = lane >> 4, l16 = lane & 15;
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            long a[MI], b[2];
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+                a[i] = *reinterpret_cast<const long*>(Aq + (wm * (TM / 2) + i * 16 + l16) * RS + g * 32 + 8 * kq);
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                b[j] = *reinterpret_cast<const long*>(Bq + (wn * 32 + j * 16 + l16) * RS + g * 32 + 8 * kq);
+#pragma unroll
+            for (int i = 0; i < MI; ++i) {
+                const float4 sa = *reinterpret_cast<const float4*>(&As_s[g][wm * (TM / 2) + i * 16 + 4 * kq]);
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const i32x4 d = __builtin_amdgcn_mfma_i32_16x16x32_i8(a[i], b[j], i32x4{0, 0, 0, 0}, 0, 0, 0);
+                    const float sw = Bs_s[g][wn * 32 + j * 16 + l16];
+                    acc[i][j][0] = fmaf((float)d[0], sa.x * sw, acc[i][j][0]);
+                    acc[i][j][1] = fmaf((float)d[1], sa.y * sw, acc[i][j][1]);
+                    acc[i][j][2] = fmaf((float)d[2], sa.z * sw, acc[i][j][2]);
+                    acc[i][j][3] = fmaf((float)d[3], sa.w * sw, acc[i][j][3]);
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = m0 + wm * (TM / 2) + i * 16 + 4 * (lane >> 4) + r;
+                const int n = n0 + wn * 32 + j * 16 + (lane & 15);
+                if (m < M && n < N) epilogue(ep, Y, ldy, m, n, acc[i][j][r]);
             }
 }
 
@@ -973,7 +1188,7 @@ static void plan_gemv(int N, int K, Epilogue epi, int granule, int* ksplit, int*
 
 hipError_t launch_w4_matmul(const float* x, int ldx, int M, const Int4Mat& w, const float* ln_g,
                             const float* ln_b, float eps, float* y, int ldy, Epilogue epi, const QkvDest* qkv,
-                            bool force_gemm, hipStream_t st, const AttnParts* parts) {
+                            bool force_gemm, hipStream_t st, const AttnParts* parts, bool a8) {
     const AttnParts ap = parts ? *parts : AttnParts{nullptr, 0, 0};
     EpiArgs ep{};
     ep.epi = epi;
@@ -985,22 +1200,32 @@ hipError_t launch_w4_matmul(const float* x, int ldx, int M, const Int4Mat& w, co
         // merged partials: whole heads (64 columns) per k split
         plan_gemv(w.N, w.K, ln_g ? EPI_STORE : epi, ap.part ? 64 : 32, &ksplit, &kspan);
         // activation rows (stride span + 4); merged partials also need their
-        // weights [M][heads][splits]
+        // weights [M][heads][splits]; the A8 form adds the INT8 codes
+        // [GV_M][span] and their scales [span / 32][GV_M]
         const int span = std::min(kspan, GV_MAXSPAN);
         const size_t wts = ap.part ? (size_t)M * (span / 64) * ap.nsplit : 0;
         if (ap.part && (span % 64 || (int)(M * (span / 64)) > 256)) return hipErrorInvalidValue;
-        const size_t lds = sizeof(float) * ((size_t)(span + 4) * GV_M + wts);
+        size_t lds = sizeof(float) * ((size_t)(span + 4) * GV_M + wts);
+        if (a8) lds = sizeof(float) * ((size_t)(span + 4) * GV_M + ((wts + 3) & ~(size_t)3)) + (size_t)GV_M * span +
+                      sizeof(float) * (size_t)(span / 32) * GV_M;
         if (lds > kGemvMaxLds) return hipErrorInvalidValue;
         static bool attr = false;
         if (!attr) {
-            hipError_t e = hipFuncSetAttribute((const void*)k_gemv_w4, hipFuncAttributeMaxDynamicSharedMemorySize,
+            hipError_t e = hipFuncSetAttribute((const void*)k_gemv_w4<false>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                                (int)kGemvMaxLds);
+            if (e == hipSuccess)
+                e = hipFuncSetAttribute((const void*)k_gemv_w4<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                        (int)kGemvMaxLds);
             if (e != hipSuccess) return e;
             attr = true;
         }
         const dim3 grid((w.N + 15) / 16, ksplit);
-        hipLaunchKernelGGL(k_gemv_w4, grid, dim3(256), lds, st, x, ldx, M, w.K, kspan, ln_g, ln_b, eps, ap.part,
-                           ap.H, ap.nsplit, w.q, w.s, w.N, y, ldy, ep);
+        if (a8)
+            hipLaunchKernelGGL(k_gemv_w4<true>, grid, dim3(256), lds, st, x, ldx, M, w.K, kspan, ln_g, ln_b, eps,
+                               ap.part, ap.H, ap.nsplit, w.q, w.s, w.N, y, ldy, ep);
+        else
+            hipLaunchKernelGGL(k_gemv_w4<false>, grid, dim3(256), lds, st, x, ldx, M, w.K, kspan, ln_g, ln_b, eps,
+                               ap.part, ap.H, ap.nsplit, w.q, w.s, w.N, y, ldy, ep);
         return hipGetLastError();
     }
     if (ln_g || ap.part) return hipErrorInvalidValue;  // the GEMM path takes plain rows
@@ -1011,6 +1236,16 @@ hipError_t launch_w4_matmul(const float* x, int ldx, int M, const Int4Mat& w, co
     const int ntile = (w.N + GN - 1) / GN;
     const bool small = (long)ntile * ((M + 63) / 64) < 512;
     const int TM = small ? 32 : 64, GKs = small ? 128 : 64;
+    const dim3 grid(ntile, (M + TM - 1) / TM, ksplit);
+    if (a8) {
+        if (small)
+            hipLaunchKernelGGL((k_gemm_w4a8<32, 128>), grid, dim3(256), 0, st, x, ldx, M, w.K, w.q, w.s, w.N, y, ldy,
+                               ep);
+        else
+            hipLaunchKernelGGL((k_gemm_w4a8<64, 64>), grid, dim3(256), 0, st, x, ldx, M, w.K, w.q, w.s, w.N, y, ldy,
+                               ep);
+        return hipGetLastError();
+    }
     const int kspan = (w.K + GKs - 1) / GKs * GKs;
     static bool attr = false;
     if (!attr) {
@@ -1022,7 +1257,6 @@ hipError_t launch_w4_matmul(const float* x, int ldx, int M, const Int4Mat& w, co
         if (e != hipSuccess) return e;
         attr = true;
     }
-    const dim3 grid(ntile, (M + TM - 1) / TM, ksplit);
     if (small)
         hipLaunchKernelGGL((k_gemm_w4<32, 128>), grid, dim3(256), gemm_lds(32, 128), st, x, ldx, M, w.K, w.q, w.s,
                            w.N, y, ldy, ep, kspan);

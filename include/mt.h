@@ -57,8 +57,20 @@ typedef struct {
     int32_t batch;     /* B sequences that advance in lockstep, 1..64 */
     int32_t t_cap;     /* fixed cache capacity per sequence (positions), 1..16384 */
     float ln_eps;      /* LayerNorm epsilon (1e-5) */
-    uint32_t flags;    /* must be 0 */
+    uint32_t flags;    /* 0 or MT_FLAG_W4A8 */
 } mt_config;
+
+/* W4A8 variant of the four projections.  The medium ONNX README ("Model
+ * variant") states that the quantised MatMuls dynamically quantise their
+ * activations to INT8 and accumulate in INT32; block, scale and rounding are
+ * this library's reading: for each activation row and group of 32 inputs
+ * (the weight group) s_a = max|x| / 127, code = clamp(rint(x * (1 / s_a)),
+ * -127, 127) with binary32 division and multiply (codes 0 for an all-zero
+ * group); the group sum I = sum (u - 8) * code is exact and the projection
+ * is sum_g s_w * s_a * I_g in FP32.  Attention, LayerNorm, the LM head and
+ * the cache stay FP32.  Decode runs on the per-operation kernels in this
+ * mode (MT_DECODE_PERSISTENT is refused with MT_ERR_UNSUPPORTED). */
+#define MT_FLAG_W4A8 1u
 
 /* One INT4 projection in the canonical packed form.
  * For a matrix W [N, K] (row n = output feature n, K = input width):

@@ -73,7 +73,10 @@ def _cfg(**kw):
     (dict(batch=0), binding.MT_ERR_INVALID_ARG),
     (dict(t_cap=0), binding.MT_ERR_INVALID_ARG),
     (dict(ln_eps=0.0), binding.MT_ERR_INVALID_ARG),
-    (dict(flags=1), binding.MT_ERR_UNSUPPORTED),
+    (dict(flags=2), binding.MT_ERR_UNSUPPORTED),
+    (dict(flags=6), binding.MT_ERR_UNSUPPORTED),
+    # W4A8 is a valid mode: the config passes and the NULL weights are refused
+    (dict(flags=binding.MT_FLAG_W4A8), binding.MT_ERR_INVALID_ARG),
 ])
 def test_create_rejects_bad_config_before_device_work(kw, code):
     lib = binding.lib()
