@@ -314,8 +314,7 @@ int mt_create(const mt_config* cfg, const mt_weights* w, int weights_on_device, 
         hipMemcpyAsync(m->ws_ptrs, hs.data(), hs.size() * sizeof(void*), hipMemcpyHostToDevice, st) ||
         hipMemsetAsync(m->err, 0, 16, st))
         return bail(fail(MT_ERR_HIP, "mt_create: table copy failed"));
-    // the persistent step computes the W4A32 projections only
-    m->persistent_ok = persistent_supported(d, F, H, B, V) && !(m->c.flags & MT_FLAG_W4A8);
+    m->persistent_ok = persistent_supported(d, F, H, B, V);
     if (m->persistent_ok) {
         const size_t xb = persistent_xbuf_bytes(L, d, F, H, B, V);
         if (hipMalloc(&m->xbuf, xb) != hipSuccess || hipMemsetAsync(m->xbuf, 0, xb, st) != hipSuccess)
@@ -380,6 +379,7 @@ int mt_decode_step(mt_model* m, const int64_t* token, float* logits, int64_t* ne
         pa.wq_base = m->wq_all; pa.ws_base = m->ws_all; pa.kc = m->kc; pa.vc = m->vc;
         pa.token = token; pa.logits = logits; pa.next = next; pa.t0 = m->t_past;
         pa.epoch = ++m->epoch;
+        pa.a8 = (c.flags & MT_FLAG_W4A8) ? 1 : 0;
         pa.resid = m->x; pa.xbuf = m->xbuf; pa.err = m->err; pa.trace = m->trace;
         HIP_TRY(launch_persistent_decode(pa, st));
     } else {

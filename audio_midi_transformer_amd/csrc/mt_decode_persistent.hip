@@ -164,6 +164,7 @@ struct Args {
     const Role* roles;
     int* err;
     unsigned nib;     // 0x0F0F0F0F (nibble mask, see dot_u)
+    int a8;           // 1: W4A8 projections (INT8 activation codes, INT32 group sums)
     uint64_t* trace;  // optional: [NWG][L + 1][TRACE_SLOTS] wall-clock stamps
 };
 
@@ -251,6 +252,35 @@ __device__ __forceinline__ float block_reduce(float v, float* red) {
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
     lds_barrier();
     return MAX ? fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])) : (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+// ---------------------------------------------------------------- W4A8 codes
+
+// Maximum over each group of 32 consecutive lanes, in every lane.
+__device__ __forceinline__ float max32(float v) {
+    v = fmaxf(v, dpp<0xB1>(v));   // quad_perm [1,0,3,2]
+    v = fmaxf(v, dpp<0x4E>(v));   // quad_perm [2,3,0,1]
+    v = fmaxf(v, dpp<0x141>(v));  // row_half_mirror
+    v = fmaxf(v, dpp<0x140>(v));  // row_mirror: the 16-lane row
+    return fmaxf(v, __shfl_xor(v, 16));
+}
+
+// Byte position of input k in the W4A8 code layout: in each block of 8
+// inputs the even ones first, then the odd ones, the order in which the
+// low and high nibbles of a weight dword come apart.
+__device__ __forceinline__ int cpos(int k) {
+    const int j = k & 7;
+    return (k & ~7) | ((j & 1) << 2) | (j >> 1);
+}
+
+// The INT8 code of y in a group whose largest magnitude is amax (every lane
+// of the group computes the same scale): s = amax / 127, code =
+// clamp(rint(y * (1 / s)), -127, 127), 0 when s == 0.
+__device__ __forceinline__ int code8(float y, float amax, float* s_out) {
+    const float s = amax / 127.0f;
+    const float r = s != 0.f ? 1.0f / s : 0.f;
+    *s_out = s;
+    return (int)fminf(fmaxf(rintf(__fmul_rn(y, r)), -127.f), 127.f);
 }
 
 // ---------------------------------------------------------------- exchange words
@@ -402,18 +432,31 @@ __device__ __forceinline__ bool ll_gather_regs(const uint64_t* src, int n, float
 // (dst) with the sums of its 32-element groups (xs).  Thread t holds words
 // t + i NT, so each group lies in 32 consecutive lanes and its sum is a lane
 // reduction.  False (for the whole workgroup) if a wait failed.
+// With a8 the vector is stored as W4A8 codes (bytes at cpos(i) of dst) and
+// xs receives the group scales instead.
 template <int U>
 __device__ __forceinline__ bool gather_to_lds(const uint64_t* src, int n, float* dst, float* xs, uint32_t ep,
-                                              int* err, int* s_flag) {
+                                              int* err, int* s_flag, bool a8) {
     float v[U];
     if (!ll_gather_regs<U>(src, n, v, ep, err)) *s_flag = 1;
     lds_barrier();  // dst and xs may still be read by other waves of the previous phase
+    if (a8) {
+        int8_t* d8 = reinterpret_cast<int8_t*>(dst);
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int i = u * NT + threadIdx.x;
-        dst[swz(i)] = v[u];
-        const float t = group_reduce<32>(v[u]);
-        if ((threadIdx.x & 31) == res_lane(32)) xs[i >> 5] = t;
+        for (int u = 0; u < U; ++u) {
+            const int i = u * NT + threadIdx.x;
+            float s;
+            d8[cpos(i)] = (int8_t)code8(v[u], max32(fabsf(v[u])), &s);
+            if ((threadIdx.x & 31) == 0) xs[i >> 5] = s;
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = u * NT + threadIdx.x;
+            dst[swz(i)] = v[u];
+            const float t = group_reduce<32>(v[u]);
+            if ((threadIdx.x & 31) == res_lane(32)) xs[i >> 5] = t;
+        }
     }
     lds_barrier();
     return *s_flag == 0;
@@ -445,7 +488,7 @@ __device__ __forceinline__ void ln_load(LnRegs<D>& p, const float* __restrict__ 
 template <int D, bool SWZ>
 __device__ __forceinline__ bool residual_layernorm(float (&r)[LnRegs<D>::PER], const float (&delta)[LnRegs<D>::PER],
                                                    bool add, const LnRegs<D>& p, float eps, float* act, float* xs, float* red,
-                                                   const int* s_flag) {
+                                                   const int* s_flag, bool a8 = false) {
     constexpr int PER = LnRegs<D>::PER;
     // mean and sum of squared deviations of each wave's 64 PER elements
     // (two passes within the wave), then combined across the four waves:
@@ -478,6 +521,20 @@ __device__ __forceinline__ bool residual_layernorm(float (&r)[LnRegs<D>::PER], c
                      NW * ((d0 * d0 + d1 * d1) + (d2 * d2 + d3 * d3));
     const float var = m2 / (float)D;
     const float rstd = 1.0f / sqrtf(var + eps);
+    if (a8 && xs) {
+        // W4A8: codes and group scales of y (D is a multiple of NT)
+        int8_t* a8p = reinterpret_cast<int8_t*>(act);
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int k = threadIdx.x + i * NT;
+            const float y = (r[i] - mean) * rstd * p.g[i] + p.b[i];
+            float s;
+            a8p[cpos(k)] = (int8_t)code8(y, max32(fabsf(y)), &s);
+            if ((threadIdx.x & 31) == 0) xs[k >> 5] = s;
+        }
+        lds_barrier();
+        return true;
+    }
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
         const int k = threadIdx.x + i * NT;
@@ -592,6 +649,49 @@ __device__ __forceinline__ void wblk_dot(const WBlk<CPL, NP>& w, const float* ac
     }
 #pragma unroll
     for (int p = 0; p < NP; ++p) out[p] = group_reduce<LPR>(acc[p]);
+}
+
+// W4A8 form of wblk_dot: per group the exact INT32 sum of code * 16 (u - 8)
+// with v_dot4 (nibbles sign-flipped by xor 8, even inputs from the low and
+// odd inputs from the high nibbles, against the codes stored in that order),
+// then out += I * s_a * s_w / 16.  `sa` holds the group scales of the codes.
+template <int LPR, int CPL, int NP>
+__device__ __forceinline__ void wblk_dot8(const WBlk<CPL, NP>& w, const int8_t* act8, const float* sa,
+                                          float (&out)[NP]) {
+    const int lr = threadIdx.x % LPR;
+    float acc[NP];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) acc[p] = 0.f;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+        const int c = lr + LPR * j;
+        const uint4 a0 = *reinterpret_cast<const uint4*>(act8 + c * 32);
+        const uint4 a1 = *reinterpret_cast<const uint4*>(act8 + c * 32 + 16);
+        const unsigned av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+        const float s16 = sa[c] * 0.0625f;
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            const unsigned wd[4] = {w.q[p][j].x, w.q[p][j].y, w.q[p][j].z, w.q[p][j].w};
+            int I = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const unsigned x8 = wd[i] ^ 0x88888888u;
+                I = __builtin_amdgcn_sdot4((int)((x8 << 4) & 0xF0F0F0F0u), (int)av[2 * i], I, false);
+                I = __builtin_amdgcn_sdot4((int)(x8 & 0xF0F0F0F0u), (int)av[2 * i + 1], I, false);
+            }
+            acc[p] = fmaf((float)I, s16 * w.s[p][j], acc[p]);
+        }
+    }
+#pragma unroll
+    for (int p = 0; p < NP; ++p) out[p] = group_reduce<LPR>(acc[p]);
+}
+
+// The rows' dot products in the arithmetic the step runs (W4A32 or W4A8).
+template <int LPR, int CPL, int NP>
+__device__ __forceinline__ void dot_rows(const WBlk<CPL, NP>& w, const float* act, const float* xs, float (&out)[NP],
+                                         const Args& a) {
+    if (a.a8) wblk_dot8<LPR, CPL, NP>(w, reinterpret_cast<const int8_t*>(act), xs, out);
+    else wblk_dot<LPR, CPL, NP>(w, act, xs, out, a.nib);
 }
 
 // Row handled by this lane in pass p, or -1 if this lane does not write.
@@ -790,10 +890,10 @@ __device__ __forceinline__ bool phase_b(const Args& a, const Lds<D, F>& S, uint6
     using C = Cfg<D, F>;
     const uint32_t ep = a.epoch;
     if (orow < 0) return true;
-    if (!gather_to_lds<D / NT>(rep_of(X + C::XB_ATT, D), D, S.act, S.xs, ep, a.err, S.s_flag)) return false;
+    if (!gather_to_lds<D / NT>(rep_of(X + C::XB_ATT, D), D, S.act, S.xs, ep, a.err, S.s_flag, a.a8)) return false;
     stamp(a, l, 6);
     float o[C::NP_O];
-    wblk_dot<C::LPR_D, C::CPL_D, C::NP_O>(w.wo, S.act, S.xs, o, a.nib);
+    dot_rows<C::LPR_D, C::CPL_D, C::NP_O>(w.wo, S.act, S.xs, o, a);
 #pragma unroll
     for (int p = 0; p < C::NP_O; ++p) {
         const int rr = out_row<C::LPR_D>(p);
@@ -813,9 +913,9 @@ __device__ __forceinline__ bool phase_c(const Args& a, const Lds<D, F>& S, uint6
     float o_in[LnRegs<D>::PER];
     if (!ll_gather_regs<LnRegs<D>::PER>(rep_of(X + C::XB_O, D), D, o_in, ep, a.err)) *S.s_flag = 1;
     stamp(a, l, 8);
-    if (!residual_layernorm<D, true>(r, o_in, true, w.ln2, a.eps, S.act, S.xs, S.red, S.s_flag)) return false;
+    if (!residual_layernorm<D, true>(r, o_in, true, w.ln2, a.eps, S.act, S.xs, S.red, S.s_flag, a.a8)) return false;
     float o[C::NP_UP];
-    wblk_dot<C::LPR_D, C::CPL_D, C::NP_UP>(w.wu, S.act, S.xs, o, a.nib);
+    dot_rows<C::LPR_D, C::CPL_D, C::NP_UP>(w.wu, S.act, S.xs, o, a);
     const int urow = blockIdx.x * C::UP_ROWS;
 #pragma unroll
     for (int p = 0; p < C::NP_UP; ++p) {
@@ -832,10 +932,10 @@ template <int D, int F>
 __device__ __forceinline__ bool phase_d(const Args& a, const Lds<D, F>& S, uint64_t* X, const BcdW<D, F>& w, int l) {
     using C = Cfg<D, F>;
     const uint32_t ep = a.epoch;
-    if (!gather_to_lds<F / NT>(rep_of(X + C::XC, F), F, S.u, S.us, ep, a.err, S.s_flag)) return false;
+    if (!gather_to_lds<F / NT>(rep_of(X + C::XC, F), F, S.u, S.us, ep, a.err, S.s_flag, a.a8)) return false;
     stamp(a, l, 10);
     float o[C::NP_DN];
-    wblk_dot<C::LPR_F, C::CPL_F, C::NP_DN>(w.wd, S.u, S.us, o, a.nib);
+    dot_rows<C::LPR_F, C::CPL_F, C::NP_DN>(w.wd, S.u, S.us, o, a);
     const int drow = blockIdx.x * C::DN_ROWS;
 #pragma unroll
     for (int p = 0; p < C::NP_DN; ++p) {
@@ -859,7 +959,7 @@ __device__ __forceinline__ bool phase_a_ln(const Args& a, const Lds<D, F>& S, co
         if (!ll_gather_regs<LnRegs<D>::PER>(rep_of(Xp + C::XD, D), D, f, a.epoch, a.err)) *S.s_flag = 1;
     }
     stamp(a, l, 1);
-    if (!residual_layernorm<D, true>(r, f, l > 0, ln1, a.eps, S.act, S.xs, S.red, S.s_flag)) return false;
+    if (!residual_layernorm<D, true>(r, f, l > 0, ln1, a.eps, S.act, S.xs, S.red, S.s_flag, a.a8)) return false;
     stamp(a, l, 2);
     return true;
 }
@@ -896,7 +996,7 @@ __device__ __forceinline__ bool attention_role(const Args& a, const Lds<D, F>& S
         if (!phase_a_ln<D, F>(a, S, ln1, r, l)) return false;
         {
             float o[C::NP_Q];
-            wblk_dot<C::LPR_D, C::CPL_D, C::NP_Q>(wqh, S.act, S.xs, o, a.nib);
+            dot_rows<C::LPR_D, C::CPL_D, C::NP_Q>(wqh, S.act, S.xs, o, a);
 #pragma unroll
             for (int p = 0; p < C::NP_Q; ++p) {
                 const int rr = out_row<C::LPR_D>(p);
@@ -988,7 +1088,7 @@ __device__ __forceinline__ bool free_role(const Args& a, const Lds<D, F>& S, con
         if (!phase_a_ln<D, F>(a, S, ln1, r, l)) return false;
         if (role.kv_rows > 0) {
             float o[C::NP_KV];
-            wblk_dot<C::LPR_D, C::CPL_D, C::NP_KV>(wkv, S.act, S.xs, o, a.nib);
+            dot_rows<C::LPR_D, C::CPL_D, C::NP_KV>(wkv, S.act, S.xs, o, a);
 #pragma unroll
             for (int p = 0; p < C::NP_KV; ++p) {
                 const int rr = out_row<C::LPR_D>(p);
@@ -1236,6 +1336,7 @@ static hipError_t launch_t(const PersistentArgs& p, hipStream_t st) {
     a.kc = p.kc; a.vc = p.vc; a.token = p.token; a.logits = p.logits;
     a.next = p.next; a.t0 = p.t0; a.epoch = p.epoch; a.x = x; a.roles = roles; a.err = p.err;
     a.nib = 0x0F0F0F0Fu;
+    a.a8 = p.a8;
     a.trace = static_cast<uint64_t*>(p.trace);
     const int chunk = (p.t0 + C::ATT_S - 1) / C::ATT_S;
     if (chunk > pd::MAXPOS) return hipErrorInvalidValue;

@@ -84,6 +84,7 @@ struct PersistentArgs {
     int64_t* next;         // [B]
     int t0;                // position of the appended row
     uint32_t epoch;        // unique per step (tags exchanged data)
+    int a8;                // 1: W4A8 projections
     // workspace
     float* resid;          // [B, d] residual stream
     void* xbuf;            // exchange buffers

@@ -68,8 +68,7 @@ typedef struct {
  * -127, 127) with binary32 division and multiply (codes 0 for an all-zero
  * group); the group sum I = sum (u - 8) * code is exact and the projection
  * is sum_g s_w * s_a * I_g in FP32.  Attention, LayerNorm, the LM head and
- * the cache stay FP32.  Decode runs on the per-operation kernels in this
- * mode (MT_DECODE_PERSISTENT is refused with MT_ERR_UNSUPPORTED). */
+ * the cache stay FP32.  Every decode path and the prefill support it. */
 #define MT_FLAG_W4A8 1u
 
 /* One INT4 projection in the canonical packed form.

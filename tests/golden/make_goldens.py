@@ -1,6 +1,6 @@
 """Write the oracle's expected values for the workload parity tests.
 
-    python tests/golden/make_goldens.py [keys...]     (default: 0 1 2 3 3c576 4 4b8)
+    python tests/golden/make_goldens.py [keys...]     (default: every key of STEPS)
 
 Calls only the CPU oracle (oracle/) and the seeded input generator.  For
 each workload the oracle runs the prefill, then greedy decoding along its own
@@ -30,7 +30,14 @@ OUT = os.path.dirname(os.path.abspath(__file__))
 
 # decode steps stored per workload (the full run where the oracle finishes in
 # minutes; the large B=8 run is sampled at its start)
-STEPS = {"0": 16, "1": 256, "2": 1544, "3": 512, "3c576": 72, "4": 1544, "4b8": 48}
+STEPS = {"0": 16, "1": 256, "2": 1544, "3": 512, "3c576": 72, "4": 1544, "4b8": 48,
+         # the W4A8 variant (oracle in its W4A8 mode) of three workloads
+         "0a8": 16, "2a8": 1544, "3a8": 512}
+
+
+def workload_of(key: str):
+    """Workload and arithmetic of a golden key: '<workload>' or '<workload>a8'."""
+    return (key[:-2], True) if key.endswith("a8") else (key, False)
 
 
 def weights_fingerprint(w: synth.ModelWeights) -> np.ndarray:
@@ -49,11 +56,12 @@ def sample_calls(n_calls: int, batch: int):
 
 
 def run(key: str) -> None:
-    wl = synth.WORKLOADS[key]
+    base, w4a8 = workload_of(key)
+    wl = synth.WORKLOADS[base]
     steps = STEPS[key]
     t_start = time.time()
     w = synth.model_weights(wl.shape, wl.model_seed)
-    m = oracle.OracleModel.from_weights(w, batch=wl.batch, t_cap=wl.t_cap)
+    m = oracle.OracleModel.from_weights(w, batch=wl.batch, t_cap=wl.t_cap, w4a8=w4a8)
     prefix = synth.workload_prefix(wl) if wl.prefix_len else None
     tokens = synth.workload_tokens(wl) if wl.n_tokens else None
     n_calls = steps + 1

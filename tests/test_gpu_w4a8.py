@@ -132,12 +132,30 @@ def test_w4a8_model_batch8_medium_width(oracle_mod):
     _run_pair(oracle_mod, w, 8, 48, prefix, None, steps=6)
 
 
-def test_w4a8_persistent_refused(oracle_mod):
+@pytest.mark.parametrize("width", ["small", "medium", "large"])
+def test_w4a8_persistent_vs_kernels_and_oracle(oracle_mod, width):
+    """The persistent single-launch step in W4A8 mode, against the oracle's
+    W4A8 mode and against the per-operation kernels on the same inputs."""
     _dev()
-    shape = synth.ModelShape("small", 1, 768, 12, 3072)
+    base = {"small": synth.SMALL, "medium": synth.MEDIUM, "large": synth.LARGE}[width]
+    shape = synth.ModelShape(base.name, 2, base.d_model, base.n_heads, base.d_ff)
     w = synth.model_weights(shape, 9)
-    dec = binding.Decoder(w, batch=1, t_cap=16, flags=A8)
-    with pytest.raises(binding.MTError) as e:
-        dec.set_decode_path(binding.MT_DECODE_PERSISTENT)
-    assert e.value.code == binding.MT_ERR_UNSUPPORTED
-    dec.close()
+    prefix = np.random.default_rng(6).standard_normal((1, 40, shape.d_model)).astype(np.float32)
+    om = oracle_mod.OracleModel.from_weights(w, batch=1, t_cap=64, w4a8=True)
+    decs = []
+    for path in (binding.MT_DECODE_PERSISTENT, binding.MT_DECODE_KERNELS):
+        dec = binding.Decoder(w, batch=1, t_cap=64, flags=A8)
+        dec.set_decode_path(path)
+        dec.prefill(None, _t(prefix))
+        decs.append(dec)
+    lo, no = om.forward(prefix=prefix)
+    for k in range(12):
+        tok = no.reshape(1, 1)
+        lo, no = om.forward(tokens=tok)
+        outs = [d.decode_step(_t(tok.reshape(1)))[0].cpu().numpy() for d in decs]
+        for o, name in zip(outs, ("persistent", "kernels")):
+            _compare(o, lo, f"{name} step {k}")
+    for d in decs:
+        d.check()
+        d.close()
+    om.close()
