@@ -256,13 +256,29 @@ __device__ __forceinline__ float block_reduce(float v, float* red) {
 
 // ---------------------------------------------------------------- W4A8 codes
 
-// Maximum over each group of 32 consecutive lanes, in every lane.
-__device__ __forceinline__ float max32(float v) {
-    v = fmaxf(v, dpp<0xB1>(v));   // quad_perm [1,0,3,2]
-    v = fmaxf(v, dpp<0x4E>(v));   // quad_perm [2,3,0,1]
-    v = fmaxf(v, dpp<0x141>(v));  // row_half_mirror
-    v = fmaxf(v, dpp<0x140>(v));  // row_mirror: the 16-lane row
-    return fmaxf(v, __shfl_xor(v, 16));
+// Maximum over each group of 32 consecutive lanes, valid in lanes 16..31 of
+// the group (the layout of group_reduce<32>).
+__device__ __forceinline__ float max32_hi(float v) {
+    v = fmaxf(v, dpp<0xB1>(v));        // quad_perm [1,0,3,2]
+    v = fmaxf(v, dpp<0x4E>(v));        // quad_perm [2,3,0,1]
+    v = fmaxf(v, dpp<0x141>(v));       // row_half_mirror
+    v = fmaxf(v, dpp<0x140>(v));       // row_mirror: the 16-lane row
+    return fmaxf(v, dpp<0x142, 0xA>(v));  // row_bcast15 into rows 1, 3
+}
+
+// Group scales from group maxima: thread g turns xs[g] (max |x| of group g)
+// into s = max / 127 (kept in xs) and its reciprocal rr[g]; ng groups.
+__device__ __forceinline__ void group_scales(float* xs, float* rr, int ng) {
+    for (int g = threadIdx.x; g < ng; g += NT) {
+        const float sc = xs[g] / 127.0f;
+        xs[g] = sc;
+        rr[g] = sc != 0.f ? 1.0f / sc : 0.f;
+    }
+}
+
+// The INT8 code of x with reciprocal scale r.
+__device__ __forceinline__ int8_t code8r(float x, float r) {
+    return (int8_t)(int)fminf(fmaxf(rintf(__fmul_rn(x, r)), -127.f), 127.f);
 }
 
 // Byte position of input k in the W4A8 code layout: in each block of 8
@@ -273,15 +289,6 @@ __device__ __forceinline__ int cpos(int k) {
     return (k & ~7) | ((j & 1) << 2) | (j >> 1);
 }
 
-// The INT8 code of y in a group whose largest magnitude is amax (every lane
-// of the group computes the same scale): s = amax / 127, code =
-// clamp(rint(y * (1 / s)), -127, 127), 0 when s == 0.
-__device__ __forceinline__ int code8(float y, float amax, float* s_out) {
-    const float s = amax / 127.0f;
-    const float r = s != 0.f ? 1.0f / s : 0.f;
-    *s_out = s;
-    return (int)fminf(fmaxf(rintf(__fmul_rn(y, r)), -127.f), 127.f);
-}
 
 // ---------------------------------------------------------------- exchange words
 
@@ -397,12 +404,17 @@ __device__ __forceinline__ bool ll_gather1(const uint64_t* src, int n, float* ds
 // values in registers (thread t), the element mapping of the LayerNorm.  On
 // a failed wait the error bit is set and false returned; the caller flags
 // the workgroup.
-template <int U>
-__device__ __forceinline__ bool ll_gather_regs(const uint64_t* src, int n, float (&v)[U], uint32_t ep, int* err) {
+struct StrideIdx {  // word u of thread t: t + u * NT
+    __device__ int operator()(int u) const { return u * NT + (int)threadIdx.x; }
+};
+
+template <int U, typename Idx = StrideIdx>
+__device__ __forceinline__ bool ll_gather_regs(const uint64_t* src, int n, float (&v)[U], uint32_t ep, int* err,
+                                               Idx idx = Idx()) {
     uint64_t w[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const int i = u * NT + threadIdx.x;
+        const int i = idx(u);
         w[u] = (i < n) ? ll_get(src + i) : ((uint64_t)ep << 32);
     }
     bool ok = true;
@@ -418,13 +430,25 @@ __device__ __forceinline__ bool ll_gather_regs(const uint64_t* src, int n, float
         __builtin_amdgcn_s_sleep(1);
 #pragma unroll
         for (int u = 0; u < U; ++u)
-            if ((uint32_t)(w[u] >> 32) != ep) w[u] = ll_get(src + u * NT + threadIdx.x);
+            if ((uint32_t)(w[u] >> 32) != ep) w[u] = ll_get(src + idx(u));
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) v[u] = __uint_as_float((uint32_t)w[u]);
     if (!ok) atomicOr(err, 2);
     return ok;
 }
+
+// Word order of a vector gathered as W4A8 codes: dword q = rho * NT + t of the
+// code layout (thread t, rho < U / 4) holds the codes of inputs 8 (q / 2) +
+// (q % 2) + 2 j, j < 4 (the even or the odd inputs of one block of 8), so a
+// thread's four values make one code dword and the 32 inputs of a group are
+// eight consecutive lanes.
+struct CodeIdx {
+    __device__ int operator()(int u) const {
+        const int q = (u >> 2) * NT + (int)threadIdx.x;
+        return 8 * (q >> 1) + (q & 1) + 2 * (u & 3);
+    }
+};
 
 // ---------------------------------------------------------------- LayerNorm
 
@@ -438,16 +462,58 @@ template <int U>
 __device__ __forceinline__ bool gather_to_lds(const uint64_t* src, int n, float* dst, float* xs, uint32_t ep,
                                               int* err, int* s_flag, bool a8) {
     float v[U];
+    if (a8 && U % 4 == 0) {
+        // codes: one dword per four gathered values (CodeIdx order); group
+        // maxima over eight lanes by DPP, scales and reciprocals (after the
+        // n code bytes) once per group
+        if (!ll_gather_regs<U>(src, n, v, ep, err, CodeIdx())) *s_flag = 1;
+        lds_barrier();  // dst and xs may still be read by other waves of the previous phase
+        unsigned* d32 = reinterpret_cast<unsigned*>(dst);
+        float* rr = dst + n / 4;
+#pragma unroll
+        for (int rho = 0; rho < U / 4; ++rho) {
+            float am = fmaxf(fmaxf(fabsf(v[4 * rho]), fabsf(v[4 * rho + 1])),
+                             fmaxf(fabsf(v[4 * rho + 2]), fabsf(v[4 * rho + 3])));
+            am = fmaxf(am, dpp<0xB1>(am));   // quad_perm [1,0,3,2]
+            am = fmaxf(am, dpp<0x4E>(am));   // quad_perm [2,3,0,1]
+            am = fmaxf(am, dpp<0x141>(am));  // row_half_mirror: the 8 lanes
+            const int q = rho * NT + threadIdx.x;
+            if ((threadIdx.x & 7) == 0) xs[q >> 3] = am;
+        }
+        lds_barrier();
+        group_scales(xs, rr, n / 32);
+        lds_barrier();
+#pragma unroll
+        for (int rho = 0; rho < U / 4; ++rho) {
+            const int q = rho * NT + threadIdx.x;
+            const float r = rr[q >> 3];
+            unsigned wd = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) wd |= ((unsigned)(uint8_t)code8r(v[4 * rho + j], r)) << (8 * j);
+            d32[q] = wd;
+        }
+        lds_barrier();
+        return *s_flag == 0;
+    }
     if (!ll_gather_regs<U>(src, n, v, ep, err)) *s_flag = 1;
     lds_barrier();  // dst and xs may still be read by other waves of the previous phase
     if (a8) {
+        // codes byte by byte (vectors whose length is not a multiple of 4 NT):
+        // group maxima to xs, scales and reciprocals once per group
         int8_t* d8 = reinterpret_cast<int8_t*>(dst);
+        float* rr = dst + n / 4;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const float am = max32_hi(fabsf(v[u]));
+            if ((threadIdx.x & 31) == res_lane(32)) xs[(u * NT + threadIdx.x) >> 5] = am;
+        }
+        lds_barrier();
+        group_scales(xs, rr, n / 32);
+        lds_barrier();
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int i = u * NT + threadIdx.x;
-            float s;
-            d8[cpos(i)] = (int8_t)code8(v[u], max32(fabsf(v[u])), &s);
-            if ((threadIdx.x & 31) == 0) xs[i >> 5] = s;
+            d8[cpos(i)] = code8r(v[u], rr[i >> 5]);
         }
     } else {
 #pragma unroll
@@ -522,15 +588,26 @@ __device__ __forceinline__ bool residual_layernorm(float (&r)[LnRegs<D>::PER], c
     const float var = m2 / (float)D;
     const float rstd = 1.0f / sqrtf(var + eps);
     if (a8 && xs) {
-        // W4A8: codes and group scales of y (D is a multiple of NT)
+        // W4A8: codes and group scales of y (D is a multiple of NT); group
+        // maxima to xs, scales and reciprocals (after the D code bytes) once
+        // per group, then the codes
         int8_t* a8p = reinterpret_cast<int8_t*>(act);
+        float* rr = act + D / 4;
+        float y[PER];
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int k = threadIdx.x + i * NT;
-            const float y = (r[i] - mean) * rstd * p.g[i] + p.b[i];
-            float s;
-            a8p[cpos(k)] = (int8_t)code8(y, max32(fabsf(y)), &s);
-            if ((threadIdx.x & 31) == 0) xs[k >> 5] = s;
+            y[i] = (r[i] - mean) * rstd * p.g[i] + p.b[i];
+            const float am = max32_hi(fabsf(y[i]));
+            if ((threadIdx.x & 31) == res_lane(32)) xs[k >> 5] = am;
+        }
+        lds_barrier();
+        group_scales(xs, rr, D / 32);
+        lds_barrier();
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int k = threadIdx.x + i * NT;
+            a8p[cpos(k)] = code8r(y[i], rr[k >> 5]);
         }
         lds_barrier();
         return true;
