@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 METRIC = "decode ms/token + achieved HBM GB/s, medium W4g32 decoder, cache 2504, B=1"
 HBM_PEAK_GBPS = 8000.0
 FP32_MFMA_PEAK_TFLOPS = 157.3
+INT8_MFMA_PEAK_TOPS = 5000.0
 STEADY_FROM = 8
 
 
@@ -75,14 +76,14 @@ def traffic_from_profiles(kernel: str, workload_key: str):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(wl, weights, prefix_np, tokens_np, max_steps: int = 8):
+def cpu_baseline(wl, weights, prefix_np, tokens_np, max_steps: int = 8, w4a8: bool = False):
     """The CPU oracle as it stands, on this host, on a bounded sample of the
     workload: its prefill, then `max_steps` greedy decode steps."""
     import oracle
     cores = len(os.sched_getaffinity(0))
     cores = min(cores, int(os.environ.get("OMP_NUM_THREADS", cores)))
     os.environ["OMP_NUM_THREADS"] = str(cores)
-    m = oracle.OracleModel.from_weights(weights, batch=wl.batch, t_cap=wl.t_cap)
+    m = oracle.OracleModel.from_weights(weights, batch=wl.batch, t_cap=wl.t_cap, w4a8=w4a8)
     t0 = time.perf_counter()
     _, nxt = m.forward(tokens=tokens_np, prefix=prefix_np)
     t1 = time.perf_counter()
@@ -160,6 +161,8 @@ def main() -> int:
     ap.add_argument("--decode-steps", type=int, default=None,
                     help="override the number of decode steps per pass (default: the workload's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--w4a8", action="store_true",
+                    help="the W4A8 variant: INT8 activation codes per row and group of 32, INT32 group sums")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="before the bench, copy a buffer of this many MiB device-to-device three "
                          "times (a plain copy of known size, to scale HBM byte counters)")
@@ -207,7 +210,7 @@ def main() -> int:
     weights = synth.model_weights(shape, wl.model_seed)
     prefix_np = synth.workload_prefix(wl) if wl.prefix_len else None
     tokens_np = synth.workload_tokens(wl) if wl.n_tokens else None
-    dec = binding.Decoder(weights, batch=B, t_cap=wl.t_cap)
+    dec = binding.Decoder(weights, batch=B, t_cap=wl.t_cap, flags=binding.MT_FLAG_W4A8 if args.w4a8 else 0)
     path = {"auto": binding.MT_DECODE_AUTO, "kernels": binding.MT_DECODE_KERNELS,
             "persistent": binding.MT_DECODE_PERSISTENT}[args.path]
     persistent = path != binding.MT_DECODE_KERNELS and dec_is_persistent(dec)
@@ -275,6 +278,8 @@ def main() -> int:
     copy_gbps = measure_copy_peak(torch)
 
     metric = METRIC if wl.key == "2" else f"decode ms/token + achieved HBM GB/s, workload {wl.key}"
+    if args.w4a8:
+        metric += " (W4A8 variant)"
     out = {
         "metric": metric,
         "value": round(ms_tok, 5),
@@ -286,8 +291,9 @@ def main() -> int:
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "i8 x i4 -> i32 projections, f32 elsewhere" if args.w4a8 else "f32",
         "weights": "int4 symmetric RTN, group 32, fp32 scales",
+        "activations": ("int8 symmetric per row and group of 32, dynamic" if args.w4a8 else "fp32"),
         "data": "synthetic (seeded N(0,0.02) weights, N(0,1) prefix; no checkpoint)",
         "config": {"workload": f"{wl.key}: {wl.name}", "layers": shape.n_layers,
                    "d_model": shape.d_model, "heads": shape.n_heads, "d_ff": shape.d_ff,
@@ -304,7 +310,8 @@ def main() -> int:
         "hbm_frac_of_measured_copy": round(gbps / copy_gbps, 4),
         "measured_copy_GBps": round(copy_gbps, 1),
         "prefill_ms": round(prefill_ms, 3),
-        "prefill_fp32_mfma_frac": round(pf_flops / (prefill_ms * 1e-3) / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4),
+        ("prefill_int8_mfma_frac" if args.w4a8 else "prefill_fp32_mfma_frac"):
+            round(pf_flops / (prefill_ms * 1e-3) / 1e12 / (INT8_MFMA_PEAK_TOPS if args.w4a8 else FP32_MFMA_PEAK_TFLOPS), 4),
         "roofline": {"kernel": kernel_name, "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic,
@@ -314,7 +321,7 @@ def main() -> int:
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(wl, weights, prefix_np, tokens_np)
+        out["cpu_baseline"] = cpu_baseline(wl, weights, prefix_np, tokens_np, w4a8=args.w4a8)
     dec.close()
     print(json.dumps(out), flush=True)
     return 0
