@@ -75,6 +75,10 @@ def lib() -> ctypes.CDLL:
         L.oracle_model_reset.restype = None
         L.oracle_model_kv.argtypes = [ctypes.c_void_p, ctypes.POINTER(_f32p), ctypes.POINTER(_f32p)]
         L.oracle_model_forward.argtypes = [ctypes.c_void_p, _i64p, i64, _f32p, i64, _f32p, _i64p, _f32p]
+        L.oracle_model_forward_seq.argtypes = [ctypes.c_void_p, i64, _i64p, i64, _f32p, i64, _f32p, _i64p]
+        L.oracle_model_position_seq.argtypes = [ctypes.c_void_p, i64]
+        L.oracle_model_position_seq.restype = i64
+        L.oracle_model_reset_seq.argtypes = [ctypes.c_void_p, i64]
         _lib = L
     return _lib
 
@@ -249,6 +253,28 @@ class OracleModel:
             raise OverflowError("oracle cache full")
         _check(rc, "forward")
         return (logits, nxt, hid) if return_hidden else (logits, nxt)
+
+    def position_seq(self, b: int) -> int:
+        return int(lib().oracle_model_position_seq(self._h, b))
+
+    def reset_seq(self, b: int) -> None:
+        _check(lib().oracle_model_reset_seq(self._h, b), "reset_seq")
+
+    def forward_seq(self, b: int, tokens: Optional[np.ndarray] = None, prefix: Optional[np.ndarray] = None):
+        """Sequence b only (ragged batch): tokens [S] int64 and/or prefix [P, d],
+        appended at that sequence's own position -> (logits [V], next)."""
+        d = self.d
+        tokens = np.zeros((0,), np.int64) if tokens is None else np.ascontiguousarray(tokens, np.int64).reshape(-1)
+        prefix = np.zeros((0, d), np.float32) if prefix is None else _f32(prefix).reshape(-1, d)
+        S, P = tokens.shape[0], prefix.shape[0]
+        logits = np.zeros((self.V,), dtype=np.float32)
+        nxt = np.zeros((1,), dtype=np.int64)
+        rc = lib().oracle_model_forward_seq(self._h, b, _p(tokens, _i64p) if S else None, S,
+                                            _p(prefix, _f32p) if P else None, P, _p(logits, _f32p), _p(nxt, _i64p))
+        if rc == -2:
+            raise OverflowError("oracle cache full")
+        _check(rc, "forward_seq")
+        return logits, int(nxt[0])
 
     def kv(self) -> Tuple[np.ndarray, np.ndarray]:
         """Views of the cache, [L, B, T_cap, H, 64] each (valid until close)."""

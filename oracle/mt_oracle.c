@@ -273,7 +273,7 @@ int oracle_attention(const float* q, const float* kc, const float* vc, int64_t T
 typedef struct {
     int64_t L, d, H, F, V, B, Tcap;
     float eps;
-    int64_t tpast;
+    int64_t* tpos;  /* [B] positions already in the cache, per sequence */
     float* tok_emb; /* [V, d] */
     float* lm_head; /* [V, d] */
     float* lnf;     /* [2, d] gain, bias */
@@ -298,7 +298,7 @@ static void model_free(oracle_model* m)
             free(m->cq[l]); free(m->cs[l]);
         }
     free(m->wqkv); free(m->wo); free(m->wup); free(m->wdown); free(m->ln); free(m->cq); free(m->cs);
-    free(m->tok_emb); free(m->lm_head); free(m->lnf); free(m->kc); free(m->vc);
+    free(m->tok_emb); free(m->lm_head); free(m->lnf); free(m->kc); free(m->vc); free(m->tpos);
     free(m);
 }
 
@@ -319,6 +319,7 @@ oracle_model* oracle_model_new(int64_t L, int64_t d, int64_t H, int64_t F, int64
     m->wdown = (float**)calloc((size_t)L, sizeof(float*));
     m->ln = (float**)calloc((size_t)L, sizeof(float*));
     m->cq = (uint8_t**)calloc((size_t)L, sizeof(uint8_t*));
+    m->tpos = (int64_t*)calloc((size_t)B, sizeof(int64_t));
     m->cs = (float**)calloc((size_t)L, sizeof(float*));
     m->tok_emb = (float*)calloc((size_t)(V * d), sizeof(float));
     m->lm_head = (float*)calloc((size_t)(V * d), sizeof(float));
@@ -326,7 +327,7 @@ oracle_model* oracle_model_new(int64_t L, int64_t d, int64_t H, int64_t F, int64
     size_t kv = (size_t)(L * B * Tcap * d);
     m->kc = (float*)calloc(kv, sizeof(float));
     m->vc = (float*)calloc(kv, sizeof(float));
-    if (!m->wqkv || !m->wo || !m->wup || !m->wdown || !m->ln || !m->cq || !m->cs || !m->tok_emb || !m->lm_head ||
+    if (!m->wqkv || !m->wo || !m->wup || !m->wdown || !m->ln || !m->cq || !m->cs || !m->tpos || !m->tok_emb || !m->lm_head ||
         !m->lnf || !m->kc || !m->vc) {
         model_free(m);
         return NULL;
@@ -409,7 +410,14 @@ int oracle_model_set_layer(oracle_model* m, int64_t l, const float* wqkv, const 
     return ORACLE_OK;
 }
 
-int64_t oracle_model_position(const oracle_model* m) { return m ? m->tpast : -1; }
+/* Position of sequence 0 (all sequences share it unless single sequences
+ * were appended with oracle_model_forward_seq). */
+int64_t oracle_model_position(const oracle_model* m) { return m ? m->tpos[0] : -1; }
+
+int64_t oracle_model_position_seq(const oracle_model* m, int64_t b)
+{
+    return (m && b >= 0 && b < m->B) ? m->tpos[b] : -1;
+}
 
 /* 1: the four projections run the W4A8 product (needs quantised layers). */
 int oracle_model_set_w4a8(oracle_model* m, int on)
@@ -436,7 +444,8 @@ static void project(const oracle_model* m, int64_t l, int i, const float* A, int
 
 void oracle_model_reset(oracle_model* m)
 {
-    if (m) m->tpast = 0;
+    if (m)
+        for (int64_t b = 0; b < m->B; ++b) m->tpos[b] = 0;
 }
 
 int oracle_model_kv(oracle_model* m, float** k, float** v)
@@ -447,25 +456,34 @@ int oracle_model_kv(oracle_model* m, float** k, float** v)
     return ORACLE_OK;
 }
 
-/* One decoder call.  tokens [B, S] (may be NULL when S == 0), prefix
- * [B, P, d] (may be NULL when P == 0).  Rows [prefix ; embed(tokens)] are
- * appended at positions T_past .. T_past+P+S-1.  logits [B, V] and next [B]
- * are those of the last appended row.  hidden_out, if not NULL, receives
- * the final-LayerNorm output of the last row [B, d]. */
-int oracle_model_forward(oracle_model* m, const int64_t* tokens, int64_t S, const float* prefix,
-                         int64_t P, float* logits, int64_t* next, float* hidden_out)
+/* One decoder call for the nb sequences bsel[0 .. nb) (all B in order when
+ * bsel is NULL).  tokens [nb, S] (may be NULL when S == 0), prefix
+ * [nb, P, d] (may be NULL when P == 0).  The rows [prefix ; embed(tokens)]
+ * of selected sequence k are appended at that sequence's own positions
+ * T_k .. T_k+P+S-1 (ragged batch: each sequence attends to its own cache
+ * only).  logits [nb, V] and next [nb] are those of the last appended row;
+ * hidden_out, if not NULL, receives the final-LayerNorm output of that row
+ * [nb, d]. */
+static int forward_seqs(oracle_model* m, int64_t nb, const int64_t* bsel, const int64_t* tokens, int64_t S,
+                        const float* prefix, int64_t P, float* logits, int64_t* next, float* hidden_out)
 {
-    if (!m || S < 0 || P < 0 || P + S < 1 || !logits || !next) return ORACLE_EINVAL;
+    if (!m || S < 0 || P < 0 || P + S < 1 || !logits || !next || nb < 1) return ORACLE_EINVAL;
     if ((S > 0 && !tokens) || (P > 0 && !prefix)) return ORACLE_EINVAL;
     for (int64_t l = 0; l < m->L; ++l)
         if (!m->wqkv[l] || !m->ln[l] || (m->w4a8 && !m->cq[l])) return ORACLE_EINVAL;
     const int64_t L = m->L, d = m->d, H = m->H, F = m->F, V = m->V, B = m->B, Tc = m->Tcap;
-    const int64_t R = P + S, t0 = m->tpast;
-    if (t0 + R > Tc) return ORACLE_EFULL;
-    for (int64_t i = 0; i < B * S; ++i)
+    const int64_t R = P + S;
+    int64_t tmax = 0;
+    for (int64_t k = 0; k < nb; ++k) {
+        const int64_t bs = bsel ? bsel[k] : k;
+        if (bs < 0 || bs >= B) return ORACLE_EINVAL;
+        if (m->tpos[bs] + R > Tc) return ORACLE_EFULL;
+        if (m->tpos[bs] > tmax) tmax = m->tpos[bs];
+    }
+    for (int64_t i = 0; i < nb * S; ++i)
         if (tokens[i] < 0 || tokens[i] >= V) return ORACLE_EINVAL;
 
-    const int64_t rows = B * R;
+    const int64_t rows = nb * R;
     float* r = (float*)malloc(sizeof(float) * (size_t)(rows * d));
     float* a = (float*)malloc(sizeof(float) * (size_t)(rows * d));
     float* qkv = (float*)malloc(sizeof(float) * (size_t)(rows * 3 * d));
@@ -477,13 +495,13 @@ int oracle_model_forward(oracle_model* m, const int64_t* tokens, int64_t S, cons
         return ORACLE_ENOMEM;
     }
 
-    /* Rows of sequence b are r[(b*R + i) * d].  Prefix rows first, then the
-     * embeddings of the token ids (no scaling, no positional term). */
-    for (int64_t b = 0; b < B; ++b)
+    /* Rows of selected sequence k are r[(k*R + i) * d].  Prefix rows first,
+     * then the embeddings of the token ids (no scaling, no positional term). */
+    for (int64_t k = 0; k < nb; ++k)
         for (int64_t i = 0; i < R; ++i) {
-            const float* src = (i < P) ? prefix + (b * P + i) * d
-                                       : m->tok_emb + tokens[b * S + (i - P)] * d;
-            memcpy(r + (b * R + i) * d, src, sizeof(float) * (size_t)d);
+            const float* src = (i < P) ? prefix + (k * P + i) * d
+                                       : m->tok_emb + tokens[k * S + (i - P)] * d;
+            memcpy(r + (k * R + i) * d, src, sizeof(float) * (size_t)d);
         }
 
     for (int64_t l = 0; l < L; ++l) {
@@ -491,25 +509,28 @@ int oracle_model_forward(oracle_model* m, const int64_t* tokens, int64_t S, cons
         oracle_layernorm(r, rows, d, ln, ln + d, m->eps, a);
         project(m, l, 0, a, rows, qkv);
         /* cache write: K = columns [d, 2d), V = [2d, 3d); head h = 64 columns */
-        for (int64_t b = 0; b < B; ++b)
+        for (int64_t k = 0; k < nb; ++k) {
+            const int64_t bs = bsel ? bsel[k] : k, t0 = m->tpos[bs];
             for (int64_t i = 0; i < R; ++i) {
-                const float* row = qkv + (b * R + i) * 3 * d;
-                int64_t slot = (((l * B + b) * Tc) + t0 + i) * d;
+                const float* row = qkv + (k * R + i) * 3 * d;
+                int64_t slot = (((l * B + bs) * Tc) + t0 + i) * d;
                 memcpy(m->kc + slot, row + d, sizeof(float) * (size_t)d);
                 memcpy(m->vc + slot, row + 2 * d, sizeof(float) * (size_t)d);
             }
-        /* causal attention: row i sees cache positions [0, t0 + i] */
+        }
+        /* causal attention: row i of a sequence at T0 sees positions [0, T0 + i] */
 #pragma omp parallel
         {
-            double* scratch = (double*)malloc(sizeof(double) * (size_t)(t0 + R));
+            double* scratch = (double*)malloc(sizeof(double) * (size_t)(tmax + R));
 #pragma omp for collapse(3) schedule(static)
-            for (int64_t b = 0; b < B; ++b)
+            for (int64_t k = 0; k < nb; ++k)
                 for (int64_t i = 0; i < R; ++i)
                     for (int64_t h = 0; h < H; ++h) {
-                        const float* qh = qkv + (b * R + i) * 3 * d + h * 64;
-                        int64_t base = ((l * B + b) * Tc) * d + h * 64;
+                        const int64_t bs = bsel ? bsel[k] : k, t0 = m->tpos[bs];
+                        const float* qh = qkv + (k * R + i) * 3 * d + h * 64;
+                        int64_t base = ((l * B + bs) * Tc) * d + h * 64;
                         attend_row(qh, m->kc + base, m->vc + base, t0 + i + 1, d, scratch,
-                                   att + (b * R + i) * d + h * 64);
+                                   att + (k * R + i) * d + h * 64);
                     }
             free(scratch);
         }
@@ -522,22 +543,44 @@ int oracle_model_forward(oracle_model* m, const int64_t* tokens, int64_t S, cons
         for (int64_t j = 0; j < rows * d; ++j) r[j] = r[j] + o[j];
     }
 
-    /* final LayerNorm and LM head on the last row of each sequence */
-    for (int64_t b = 0; b < B; ++b) {
-        const float* last = r + (b * R + R - 1) * d;
-        float* z = a + b * d;
+    /* final LayerNorm and LM head on the last row of each selected sequence */
+    for (int64_t k = 0; k < nb; ++k) {
+        const float* last = r + (k * R + R - 1) * d;
+        float* z = a + k * d;
         oracle_layernorm(last, 1, d, m->lnf, m->lnf + d, m->eps, z);
-        if (hidden_out) memcpy(hidden_out + b * d, z, sizeof(float) * (size_t)d);
+        if (hidden_out) memcpy(hidden_out + k * d, z, sizeof(float) * (size_t)d);
     }
-    oracle_matmul(a, B, d, m->lm_head, V, logits);
-    for (int64_t b = 0; b < B; ++b) {
-        const float* lg = logits + b * V;
+    oracle_matmul(a, nb, d, m->lm_head, V, logits);
+    for (int64_t k = 0; k < nb; ++k) {
+        const float* lg = logits + k * V;
         int64_t best = 0;
         for (int64_t v = 1; v < V; ++v)
             if (lg[v] > lg[best]) best = v;
-        next[b] = best;
+        next[k] = best;
+        m->tpos[bsel ? bsel[k] : k] += R;
     }
-    m->tpast = t0 + R;
     free(r); free(a); free(qkv); free(att); free(o); free(h1);
+    return ORACLE_OK;
+}
+
+/* Every sequence: tokens [B, S], prefix [B, P, d], logits [B, V], next [B]. */
+int oracle_model_forward(oracle_model* m, const int64_t* tokens, int64_t S, const float* prefix,
+                         int64_t P, float* logits, int64_t* next, float* hidden_out)
+{
+    return m ? forward_seqs(m, m->B, NULL, tokens, S, prefix, P, logits, next, hidden_out) : ORACLE_EINVAL;
+}
+
+/* Sequence b only: tokens [S], prefix [P, d], logits [V], next [1]. */
+int oracle_model_forward_seq(oracle_model* m, int64_t b, const int64_t* tokens, int64_t S, const float* prefix,
+                             int64_t P, float* logits, int64_t* next)
+{
+    return forward_seqs(m, 1, &b, tokens, S, prefix, P, logits, next, NULL);
+}
+
+/* Sequence b starts over at position 0 (its cache rows are overwritten). */
+int oracle_model_reset_seq(oracle_model* m, int64_t b)
+{
+    if (!m || b < 0 || b >= m->B) return ORACLE_EINVAL;
+    m->tpos[b] = 0;
     return ORACLE_OK;
 }

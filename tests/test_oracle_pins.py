@@ -497,3 +497,52 @@ def test_model_w4a8_projections_use_w4a8_product(oracle_mod):
     m32.forward(prefix=x)
     k32, _ = m32.kv()
     assert not np.array_equal(k8, k32)
+
+
+# ---------------------------------------------------------------- ragged batch
+
+def test_model_ragged_batch_equals_independent_sequences(oracle_mod):
+    """Sequences of one batch with their own positions (single-sequence
+    appends, a restart, lockstep decode at different positions) give
+    bit-identical logits to independent one-sequence models fed the same
+    rows (catches a shared position, a wrong cache slot or cross-sequence
+    attention)."""
+    shape = synth.tiny_shape(n_layers=2)
+    w = _tiny_weights(shape, seed=50)
+    d, V = shape.d_model, shape.vocab
+    rng = np.random.default_rng(7)
+    B = 3
+    mb = oracle_mod.OracleModel.from_weights(w, batch=B, t_cap=40)
+    ms = [oracle_mod.OracleModel.from_weights(w, batch=1, t_cap=40) for _ in range(B)]
+    # staggered single-sequence prefills
+    for b, P in ((0, 5), (1, 9), (2, 2)):
+        x = rng.standard_normal((P, d)).astype(np.float32)
+        lb, nb = mb.forward_seq(b, prefix=x)
+        ls, ns = ms[b].forward(prefix=x[None])
+        assert np.array_equal(lb, ls[0]) and nb == int(ns[0])
+    # sequence 1 appends two prompt tokens on its own
+    t = rng.integers(0, V, 2)
+    lb, _ = mb.forward_seq(1, tokens=t)
+    ls, _ = ms[1].forward(tokens=t[None])
+    assert np.array_equal(lb, ls[0])
+    assert [mb.position_seq(b) for b in range(B)] == [5, 11, 2]
+    for step in range(4):
+        tok = rng.integers(0, V, B)
+        lb, _ = mb.forward(tokens=tok[:, None])
+        for b in range(B):
+            ls, _ = ms[b].forward(tokens=tok[b:b + 1, None])
+            assert np.array_equal(lb[b], ls[0]), f"step {step} sequence {b}"
+        if step == 1:
+            # sequence 2 restarts with a new chunk while the others continue
+            mb.reset_seq(2)
+            ms[2].reset()
+            x = rng.standard_normal((3, d)).astype(np.float32)
+            lb2, _ = mb.forward_seq(2, prefix=x)
+            ls2, _ = ms[2].forward(prefix=x[None])
+            assert np.array_equal(lb2, ls2[0])
+    assert [mb.position_seq(b) for b in range(B)] == [9, 15, 5]
+    for b in range(B):
+        kb, vb = mb.kv()
+        ks, vs = ms[b].kv()
+        T = ms[b].position
+        assert np.array_equal(kb[:, b, :T], ks[:, 0, :T]) and np.array_equal(vb[:, b, :T], vs[:, 0, :T])
