@@ -129,8 +129,11 @@ struct Cfg {
     static constexpr int OFF_QH = OFF_ACT + D;            //   q_h [64]
     static constexpr int OFF_SC = OFF_QH + 64;            //   scores [MAXPOS]
     static constexpr int OFF_PART = OFF_SC + MAXPOS;      //   own partial [PW] + gathered [ATT_S-1][PW] + kv_new [128]
-    static constexpr int OFF_COMB = rup(OFF_PART + ATT_S * PW + 128, 4);  // [4][64] scratch
-    static constexpr int OFF_RED = rup(cmax(OFF_U + F, OFF_COMB + 4 * 64), 4);
+    // [4][64] scratch, also the staging of each phase's outputs: outside the
+    // u region, because phase D writes it while other waves may still be
+    // reading u
+    static constexpr int OFF_COMB = rup(cmax(OFF_PART + ATT_S * PW + 128, OFF_U + F), 4);
+    static constexpr int OFF_RED = rup(OFF_COMB + 4 * 64, 4);
     static constexpr int OFF_FLAG = OFF_RED + 16;
     static constexpr int LDS_FLOATS = OFF_FLAG + 16;
     static_assert(D % NT == 0 && F % NT == 0 && NT == 256, "widths");
