@@ -32,7 +32,8 @@ MT_FLAG_W4A8 = 1
 # Names declared in include/mt.h; the CPU test checks the library exports all.
 EXPORTED = ("mt_pack_int4", "mt_create", "mt_prefill", "mt_decode_step", "mt_reset",
             "mt_position", "mt_kv_cache", "mt_check", "mt_set_decode_path", "mt_destroy",
-            "mt_last_error", "mt_debug_dequant", "mt_debug_matmul", "mt_debug_trace")
+            "mt_last_error", "mt_debug_dequant", "mt_debug_matmul", "mt_debug_trace",
+            "mt_prefill_seq", "mt_reset_seq", "mt_position_seq")
 
 
 class mt_config(ctypes.Structure):
@@ -88,9 +89,13 @@ def lib() -> ctypes.CDLL:
     L.mt_debug_dequant.argtypes = [vp, i32, i32, vp, vp]
     L.mt_debug_matmul.argtypes = [vp, i32, i32, vp, i32, vp, vp]
     L.mt_debug_trace.argtypes = [vp, vp, i64]
+    L.mt_prefill_seq.argtypes = [vp, i32, vp, i32, vp, i32, vp, vp, vp]
+    L.mt_reset_seq.argtypes = [vp, i32]
+    L.mt_position_seq.argtypes = [vp, i32, ctypes.POINTER(i32)]
     for name in ("mt_pack_int4", "mt_create", "mt_prefill", "mt_decode_step", "mt_reset",
                  "mt_position", "mt_kv_cache", "mt_check", "mt_set_decode_path",
-                 "mt_debug_dequant", "mt_debug_matmul", "mt_debug_trace"):
+                 "mt_debug_dequant", "mt_debug_matmul", "mt_debug_trace",
+                 "mt_prefill_seq", "mt_reset_seq", "mt_position_seq"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -204,6 +209,30 @@ class Decoder:
         check(lib().mt_prefill(self._h, _ptr(tokens), S, _ptr(prefix), P, _ptr(logits), _ptr(next),
                                _stream(stream)), "mt_prefill")
         return logits, next
+
+    def prefill_seq(self, b: int, tokens=None, prefix=None, logits=None, next=None, stream=None):
+        """Sequence b only (ragged batch): tokens [S] and/or prefix [P, d] ->
+        (logits [V], next [1])."""
+        import torch
+        if logits is None:
+            logits = torch.empty((self.V,), dtype=torch.float32, device=self.device)
+        if next is None:
+            next = torch.empty((1,), dtype=torch.int64, device=self.device)
+        S = 0 if tokens is None else int(tokens.shape[-1])
+        P = 0 if prefix is None else int(prefix.shape[-2])
+        if prefix is not None:
+            assert prefix.is_contiguous() and prefix.shape[-1] == self.d
+        check(lib().mt_prefill_seq(self._h, b, _ptr(tokens), S, _ptr(prefix), P, _ptr(logits), _ptr(next),
+                                   _stream(stream)), "mt_prefill_seq")
+        return logits, next
+
+    def reset_seq(self, b: int) -> None:
+        check(lib().mt_reset_seq(self._h, b), "mt_reset_seq")
+
+    def position_seq(self, b: int) -> int:
+        t = ctypes.c_int32()
+        check(lib().mt_position_seq(self._h, b, ctypes.byref(t)), "mt_position_seq")
+        return t.value
 
     def decode_step(self, token, logits=None, next=None, stream=None):
         logits, next = self._outputs(logits, next)

@@ -62,7 +62,7 @@ struct mt_model {
     // cache
     float* kc = nullptr;
     float* vc = nullptr;
-    int t_past = 0;
+    SeqPos pos{};  // positions already in the cache, per sequence
     int* err = nullptr;
     // decode scratch
     float* x = nullptr;
@@ -105,7 +105,7 @@ int check_config(const mt_config* c) {
     if (c->head_dim != 64) return fail(MT_ERR_UNSUPPORTED, "head_dim must be 64 (got %d)", c->head_dim);
     if (c->group != 32) return fail(MT_ERR_UNSUPPORTED, "group must be 32 (got %d)", c->group);
     if (c->flags & ~(uint32_t)MT_FLAG_W4A8) return fail(MT_ERR_UNSUPPORTED, "unknown flags 0x%x", c->flags);
-    if (c->n_layers < 1 || c->n_heads < 1 || c->vocab < 1 || c->batch < 1 || c->batch > 64 ||
+    if (c->n_layers < 1 || c->n_heads < 1 || c->vocab < 1 || c->batch < 1 || c->batch > kMaxBatch ||
         c->t_cap < 1 || c->t_cap > kMaxTcap || c->d_ff < 32)
         return fail(MT_ERR_INVALID_ARG, "non-positive or out-of-range size in config");
     if (c->d_model != c->n_heads * 64)
@@ -142,16 +142,16 @@ int ensure_prefill_ws(mt_model* m, size_t rows) {
 
 // Run every layer over M = B * R rows held in x (row m = b * R + i, position
 // t0 + i).  `decode` selects the split-K decode attention (R == 1).
-int run_layers(mt_model* m, float* x, float* a, float* q, float* att, float* h, int R, int t0,
+int run_layers(mt_model* m, float* x, float* a, float* q, float* att, float* h, int R, int b0, int nb,
                bool decode, hipStream_t st) {
     const mt_config& c = m->c;
-    const int d = c.d_model, F = c.d_ff, B = c.batch, M = B * R;
+    const int d = c.d_model, F = c.d_ff, M = nb * R;
     const bool a8 = (c.flags & MT_FLAG_W4A8) != 0;
     // with few rows the GEMV applies both LayerNorms itself
     const bool fuse_ln = gemv_fuses_layernorm(M, d);
     for (int l = 0; l < c.n_layers; ++l) {
         const float* ln = m->ln + (size_t)l * 4 * d;
-        QkvDest dst{q, m->kc, m->vc, d, l, B, c.t_cap, t0, R};
+        QkvDest dst{q, m->kc, m->vc, d, l, c.batch, c.t_cap, b0, R, m->pos};
         if (fuse_ln) {
             HIP_TRY(launch_w4_matmul(x, d, M, m->proj[l * 4 + 0], ln, ln + d, c.ln_eps, nullptr, 0, EPI_QKV, &dst,
                                      false, st, nullptr, a8));
@@ -162,14 +162,20 @@ int run_layers(mt_model* m, float* x, float* a, float* q, float* att, float* h, 
         }
         if (decode && gemv_fuses_layernorm(M, d)) {
             // split-K attention; the O projection merges the partials
+            SeqPos T{};
+            int tmax = 0;
+            for (int b = 0; b < c.batch; ++b) {
+                T.t[b] = m->pos.t[b] + 1;
+                tmax = std::max(tmax, T.t[b]);
+            }
             int ns, ch;
-            attn_split(B, c.n_heads, t0 + 1, &ns, &ch);
-            HIP_TRY(launch_attn_decode(q, m->kc, m->vc, l, B, c.n_heads, c.t_cap, t0 + 1, m->part, ns, ch, st));
+            attn_split(c.batch, c.n_heads, tmax, &ns, &ch);
+            HIP_TRY(launch_attn_decode(q, m->kc, m->vc, l, c.batch, c.n_heads, c.t_cap, T, m->part, ns, ch, st));
             const AttnParts ap{m->part, c.n_heads, ns};
             HIP_TRY(launch_w4_matmul(nullptr, d, M, m->proj[l * 4 + 1], nullptr, nullptr, 0.f, x, d, EPI_RESID,
                                      nullptr, false, st, &ap, a8));
         } else {
-            HIP_TRY(launch_attn_prefill(q, m->kc, m->vc, l, B, c.n_heads, c.t_cap, t0, R, att, st));
+            HIP_TRY(launch_attn_prefill(q, m->kc, m->vc, l, c.batch, b0, nb, c.n_heads, c.t_cap, m->pos, R, att, st));
             HIP_TRY(launch_w4_matmul(att, d, M, m->proj[l * 4 + 1], nullptr, nullptr, 0.f, x, d, EPI_RESID, nullptr,
                                      false, st, nullptr, a8));
         }
@@ -187,14 +193,14 @@ int run_layers(mt_model* m, float* x, float* a, float* q, float* att, float* h, 
     return MT_OK;
 }
 
-int run_head(mt_model* m, const float* x, int R, float* logits, int64_t* next, hipStream_t st) {
+int run_head(mt_model* m, const float* x, int R, int nb, float* logits, int64_t* next, hipStream_t st) {
     const mt_config& c = m->c;
     const int d = c.d_model;
     // final LayerNorm of the last row of every sequence
     HIP_TRY(launch_layernorm(x + (size_t)(R - 1) * d, (long)R * d, m->lnf, m->lnf + d, c.ln_eps, d,
-                             c.batch, m->z, d, st));
-    HIP_TRY(launch_lm_head(m->z, c.batch, m->lm_head, c.vocab, d, logits, st));
-    HIP_TRY(launch_argmax(logits, c.batch, c.vocab, next, st));
+                             nb, m->z, d, st));
+    HIP_TRY(launch_lm_head(m->z, nb, m->lm_head, c.vocab, d, logits, st));
+    HIP_TRY(launch_argmax(logits, nb, c.vocab, next, st));
     return MT_OK;
 }
 
@@ -334,17 +340,24 @@ int mt_create(const mt_config* cfg, const mt_weights* w, int weights_on_device, 
     return MT_OK;
 }
 
-int mt_prefill(mt_model* m, const int64_t* tokens, int32_t S, const float* prefix, int32_t P,
-               float* logits, int64_t* next, void* stream) {
-    if (!m || !logits || !next) return fail(MT_ERR_INVALID_ARG, "mt_prefill: NULL model or output");
-    if (S < 0 || P < 0 || (int64_t)S + P < 1) return fail(MT_ERR_INVALID_ARG, "mt_prefill: need P + S >= 1 (P=%d S=%d)", P, S);
-    if ((S > 0 && !tokens) || (P > 0 && !prefix)) return fail(MT_ERR_INVALID_ARG, "mt_prefill: NULL tokens or prefix");
+}  // extern "C"
+
+namespace {
+
+// Rows [prefix ; embed(tokens)] of sequences b0 .. b0+nb-1, each appended at
+// its own position.
+int prefill_rows(mt_model* m, int b0, int nb, const int64_t* tokens, int32_t S, const float* prefix, int32_t P,
+                 float* logits, int64_t* next, void* stream, const char* who) {
+    if (S < 0 || P < 0 || (int64_t)S + P < 1) return fail(MT_ERR_INVALID_ARG, "%s: need P + S >= 1 (P=%d S=%d)", who, P, S);
+    if ((S > 0 && !tokens) || (P > 0 && !prefix)) return fail(MT_ERR_INVALID_ARG, "%s: NULL tokens or prefix", who);
     const mt_config& c = m->c;
     const int R = P + S;
-    if ((int64_t)m->t_past + R > c.t_cap)
-        return fail(MT_ERR_CACHE_FULL, "mt_prefill: %d rows at position %d exceed capacity %d", R, m->t_past, c.t_cap);
+    for (int b = b0; b < b0 + nb; ++b)
+        if ((int64_t)m->pos.t[b] + R > c.t_cap)
+            return fail(MT_ERR_CACHE_FULL, "%s: %d rows at position %d of sequence %d exceed capacity %d", who, R,
+                        m->pos.t[b], b, c.t_cap);
     hipStream_t st = (hipStream_t)stream;
-    const size_t M = (size_t)c.batch * R;
+    const size_t M = (size_t)nb * R;
     int rc = ensure_prefill_ws(m, M);
     if (rc) return rc;
     const int d = c.d_model;
@@ -353,31 +366,50 @@ int mt_prefill(mt_model* m, const int64_t* tokens, int32_t S, const float* prefi
     float* q = a + M * d;
     float* att = q + M * d;
     float* h = att + M * d;
-    HIP_TRY(launch_embed(tokens, S, prefix, P, m->tok_emb, c.vocab, d, c.batch, x, m->err, st));
-    rc = run_layers(m, x, a, q, att, h, R, m->t_past, false, st);
+    HIP_TRY(launch_embed(tokens, S, prefix, P, m->tok_emb, c.vocab, d, nb, x, m->err, st));
+    rc = run_layers(m, x, a, q, att, h, R, b0, nb, false, st);
     if (rc) return rc;
-    rc = run_head(m, x, R, logits, next, st);
+    rc = run_head(m, x, R, nb, logits, next, st);
     if (rc) return rc;
-    m->t_past += R;
+    for (int b = b0; b < b0 + nb; ++b) m->pos.t[b] += R;
     m->last_stream = st;
     return MT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mt_prefill(mt_model* m, const int64_t* tokens, int32_t S, const float* prefix, int32_t P,
+               float* logits, int64_t* next, void* stream) {
+    if (!m || !logits || !next) return fail(MT_ERR_INVALID_ARG, "mt_prefill: NULL model or output");
+    return prefill_rows(m, 0, m->c.batch, tokens, S, prefix, P, logits, next, stream, "mt_prefill");
+}
+
+int mt_prefill_seq(mt_model* m, int32_t b, const int64_t* tokens, int32_t S, const float* prefix, int32_t P,
+                   float* logits, int64_t* next, void* stream) {
+    if (!m || !logits || !next) return fail(MT_ERR_INVALID_ARG, "mt_prefill_seq: NULL model or output");
+    if (b < 0 || b >= m->c.batch) return fail(MT_ERR_INVALID_ARG, "mt_prefill_seq: sequence %d of %d", b, m->c.batch);
+    return prefill_rows(m, b, 1, tokens, S, prefix, P, logits, next, stream, "mt_prefill_seq");
 }
 
 int mt_decode_step(mt_model* m, const int64_t* token, float* logits, int64_t* next, void* stream) {
     if (!m || !token || !logits || !next) return fail(MT_ERR_INVALID_ARG, "mt_decode_step: NULL argument");
     const mt_config& c = m->c;
-    if (m->t_past + 1 > c.t_cap)
-        return fail(MT_ERR_CACHE_FULL, "mt_decode_step: cache full at position %d (capacity %d)", m->t_past, c.t_cap);
+    for (int b = 0; b < c.batch; ++b)
+        if (m->pos.t[b] + 1 > c.t_cap)
+            return fail(MT_ERR_CACHE_FULL, "mt_decode_step: cache of sequence %d full at position %d (capacity %d)", b,
+                        m->pos.t[b], c.t_cap);
     hipStream_t st = (hipStream_t)stream;
     const bool persistent = m->persistent_ok && m->decode_path != MT_DECODE_KERNELS &&
-                            m->t_past <= persistent_max_position(c.d_model, c.d_ff);
+                            m->pos.t[0] <= persistent_max_position(c.d_model, c.d_ff);
     if (persistent) {
         PersistentArgs pa{};
         pa.L = c.n_layers; pa.d = c.d_model; pa.H = c.n_heads; pa.F = c.d_ff; pa.V = c.vocab;
         pa.B = c.batch; pa.t_cap = c.t_cap; pa.eps = c.ln_eps;
         pa.tok_emb = m->tok_emb; pa.lm_head = m->lm_head; pa.ln = m->ln; pa.ln_final = m->lnf;
         pa.wq_base = m->wq_all; pa.ws_base = m->ws_all; pa.kc = m->kc; pa.vc = m->vc;
-        pa.token = token; pa.logits = logits; pa.next = next; pa.t0 = m->t_past;
+        pa.token = token; pa.logits = logits; pa.next = next; pa.t0 = m->pos.t[0];
         pa.epoch = ++m->epoch;
         pa.a8 = (c.flags & MT_FLAG_W4A8) ? 1 : 0;
         pa.resid = m->x; pa.xbuf = m->xbuf; pa.err = m->err; pa.trace = m->trace;
@@ -385,25 +417,39 @@ int mt_decode_step(mt_model* m, const int64_t* token, float* logits, int64_t* ne
     } else {
         const int d = c.d_model;
         HIP_TRY(launch_embed(token, 1, nullptr, 0, m->tok_emb, c.vocab, d, c.batch, m->x, m->err, st));
-        int rc = run_layers(m, m->x, m->a, m->q, m->att, m->h, 1, m->t_past, true, st);
+        int rc = run_layers(m, m->x, m->a, m->q, m->att, m->h, 1, 0, c.batch, true, st);
         if (rc) return rc;
-        rc = run_head(m, m->x, 1, logits, next, st);
+        rc = run_head(m, m->x, 1, c.batch, logits, next, st);
         if (rc) return rc;
     }
-    m->t_past += 1;
+    for (int b = 0; b < c.batch; ++b) m->pos.t[b] += 1;
     m->last_stream = st;
     return MT_OK;
 }
 
 int mt_reset(mt_model* m) {
     if (!m) return fail(MT_ERR_INVALID_ARG, "mt_reset: NULL model");
-    m->t_past = 0;
+    m->pos = SeqPos{};
+    return MT_OK;
+}
+
+int mt_reset_seq(mt_model* m, int32_t b) {
+    if (!m) return fail(MT_ERR_INVALID_ARG, "mt_reset_seq: NULL model");
+    if (b < 0 || b >= m->c.batch) return fail(MT_ERR_INVALID_ARG, "mt_reset_seq: sequence %d of %d", b, m->c.batch);
+    m->pos.t[b] = 0;
+    return MT_OK;
+}
+
+int mt_position_seq(const mt_model* m, int32_t b, int32_t* t_past) {
+    if (!m || !t_past) return fail(MT_ERR_INVALID_ARG, "mt_position_seq: NULL argument");
+    if (b < 0 || b >= m->c.batch) return fail(MT_ERR_INVALID_ARG, "mt_position_seq: sequence %d of %d", b, m->c.batch);
+    *t_past = m->pos.t[b];
     return MT_OK;
 }
 
 int mt_position(const mt_model* m, int32_t* t_past) {
     if (!m || !t_past) return fail(MT_ERR_INVALID_ARG, "mt_position: NULL argument");
-    *t_past = m->t_past;
+    *t_past = m->pos.t[0];
     return MT_OK;
 }
 

@@ -13,18 +13,27 @@ enum Epilogue : int {
     EPI_QKV = 3,    // n <  d: q[m, n]; d <= n < 2d: K cache; 2d <= n: V cache
 };
 
-// Where the QKV epilogue scatters K and V: rows m = b * rows_per_seq + i land
-// at cache position t0 + i of sequence b in layer `layer`.
+constexpr int kMaxBatch = 64;
+
+// A value per sequence of the batch (positions, key counts), passed by value.
+struct SeqPos {
+    int t[kMaxBatch];
+};
+
+// Where the QKV epilogue scatters K and V: rows m = b * rows_per_seq + i
+// (b < the number of sequences in the call) land at cache position
+// pos.t[b0 + b] + i of sequence b0 + b in layer `layer`.
 struct QkvDest {
     float* q;        // [M, d]
-    float* kc;       // [L, B, t_cap, H, 64]
+    float* kc;       // [L, batch, t_cap, H, 64]
     float* vc;
     int d;
     int layer;
-    int batch;
+    int batch;       // sequences in the cache
     int t_cap;
-    int t0;
+    int b0;          // first sequence of the rows
     int rows_per_seq;
+    SeqPos pos;      // cache position of each sequence's first row
 };
 
 struct Int4Mat {
@@ -54,11 +63,15 @@ hipError_t launch_w4_matmul(const float* x, int ldx, int M, const Int4Mat& w, co
                             const float* ln_b, float eps, float* y, int ldy, Epilogue epi, const QkvDest* qkv,
                             bool force_gemm, hipStream_t st, const AttnParts* parts = nullptr, bool a8 = false);
 bool gemv_fuses_layernorm(int M, int K);
-// Writes the split-K partials only; the O projection merges them.
+// Writes the split-K partials only; the O projection merges them.  Sequence
+// b attends to its first T.t[b] cache positions.
 hipError_t launch_attn_decode(const float* q, const float* kc, const float* vc, int layer, int B,
-                              int H, int t_cap, int T, float* part, int nsplit, int chunk, hipStream_t st);
-hipError_t launch_attn_prefill(const float* q, const float* kc, const float* vc, int layer, int B,
-                               int H, int t_cap, int t0, int R, float* out, hipStream_t st);
+                              int H, int t_cap, const SeqPos& T, float* part, int nsplit, int chunk,
+                              hipStream_t st);
+// Causal attention of R new rows of nb sequences b0 .. b0+nb-1 (of Btot in
+// the cache); sequence b0 + b's rows sit at positions t0.t[b0 + b] + i.
+hipError_t launch_attn_prefill(const float* q, const float* kc, const float* vc, int layer, int Btot, int b0,
+                               int nb, int H, int t_cap, const SeqPos& t0, int R, float* out, hipStream_t st);
 hipError_t launch_lm_head(const float* z, int B, const float* w, int V, int d, float* logits,
                           hipStream_t st);
 hipError_t launch_argmax(const float* logits, int B, int V, int64_t* next, hipStream_t st);

@@ -79,8 +79,8 @@ __device__ __forceinline__ void epilogue(const EpiArgs& e, float* __restrict__ y
             if (n < q.d) {
                 q.q[(size_t)m * q.d + n] = v;
             } else {
-                const int b = m / q.rows_per_seq, i = m % q.rows_per_seq;
-                const size_t slot = ((size_t)(q.layer * q.batch + b) * q.t_cap + q.t0 + i) * q.d;
+                const int b = q.b0 + m / q.rows_per_seq, i = m % q.rows_per_seq;
+                const size_t slot = ((size_t)(q.layer * q.batch + b) * q.t_cap + q.pos.t[b] + i) * q.d;
                 if (n < 2 * q.d) q.kc[slot + (n - q.d)] = v;
                 else q.vc[slot + (n - 2 * q.d)] = v;
             }
@@ -705,11 +705,12 @@ __global__ __launch_bounds__(256) void k_gemm_w4a8(const float* __restrict__ X, 
 __global__ __launch_bounds__(256) void k_attn_decode(const float* __restrict__ q,
                                                      const float* __restrict__ kc,
                                                      const float* __restrict__ vc, int layer,
-                                                     int B, int H, int t_cap, int T, int chunk,
+                                                     int B, int H, int t_cap, SeqPos Tn, int chunk,
                                                      float* __restrict__ part) {
     __shared__ float red[8];
     __shared__ float sacc[4][64];
     const int split = blockIdx.x, ns = gridDim.x, h = blockIdx.y, b = blockIdx.z;
+    const int T = Tn.t[b];
     const int d = H * 64;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = tid >> 4, ql = tid & 15;
     const float4 q4 = *reinterpret_cast<const float4*>(q + (size_t)b * d + h * 64 + ql * 4);
@@ -797,11 +798,12 @@ constexpr size_t kAttnPrefillLds = sizeof(float) * 4 * (2 * PKB + 16) * PS;
 __global__ __launch_bounds__(256) void k_attn_prefill(const float* __restrict__ q,
                                                       const float* __restrict__ kc,
                                                       const float* __restrict__ vc, int layer,
-                                                      int B, int H, int t_cap, int t0, int R,
+                                                      int Btot, int b0, int H, int t_cap, SeqPos tp, int R,
                                                       float* __restrict__ out) {
     extern __shared__ float asm_lds[];
     const int d = H * 64;
     const int i0 = blockIdx.x * 16, h = blockIdx.y, b = blockIdx.z;
+    const int bs = b0 + b, t0 = tp.t[bs];  // sequence in the cache, its first new position
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int lr = lane & 15, lq = lane >> 4;
     float* Kw = asm_lds + wave * (2 * PKB + 16) * PS;  // [PKB][PS]
@@ -826,7 +828,7 @@ __global__ __launch_bounds__(256) void k_attn_prefill(const float* __restrict__ 
 #pragma unroll
     for (int n = 0; n < 4; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int kmax = t0 + min(i0 + 15, R - 1);  // last key any row of the block sees
-    const size_t base = ((size_t)(layer * B + b) * t_cap) * d + h * 64;
+    const size_t base = ((size_t)(layer * Btot + bs) * t_cap) * d + h * 64;
     // K and V rows of a block go through registers: the next block of this
     // wave is requested before the current one is multiplied
     constexpr int NE = PKB * 16 / 64;
@@ -957,13 +959,14 @@ __global__ __launch_bounds__(256) void k_attn_prefill(const float* __restrict__ 
 __global__ __launch_bounds__(256) void k_attn_prefill_wide(const float* __restrict__ q,
                                                       const float* __restrict__ kc,
                                                       const float* __restrict__ vc, int layer,
-                                                      int B, int H, int t_cap, int t0, int R,
+                                                      int Btot, int b0, int H, int t_cap, SeqPos tp, int R,
                                                       float* __restrict__ out) {
     __shared__ float Ks[64 * PS];
     __shared__ float Vs[64 * PS];
     __shared__ float Pw[4][16 * PS];
     const int d = H * 64;
     const int i0 = blockIdx.x * 64, h = blockIdx.y, b = blockIdx.z;
+    const int bs = b0 + b, t0 = tp.t[bs];  // sequence in the cache, its first new position
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int lr = lane & 15, lq = lane >> 4;
     float* P = Pw[wave];
@@ -986,7 +989,7 @@ __global__ __launch_bounds__(256) void k_attn_prefill_wide(const float* __restri
 #pragma unroll
     for (int n = 0; n < 4; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int kmax = t0 + min(i0 + 63, R - 1);  // last key any row of the block sees
-    const size_t base = ((size_t)(layer * B + b) * t_cap) * d + h * 64;
+    const size_t base = ((size_t)(layer * Btot + bs) * t_cap) * d + h * 64;
     for (int kb = 0; kb <= kmax; kb += 64) {
         __syncthreads();  // the previous block's K and V have been used
         for (int e = tid; e < 64 * 16; e += 256) {
@@ -1269,18 +1272,24 @@ hipError_t launch_w4_matmul(const float* x, int ldx, int M, const Int4Mat& w, co
 bool gemv_fuses_layernorm(int M, int K) { return M >= 1 && M <= GV_M && K <= GV_MAXSPAN; }
 
 hipError_t launch_attn_decode(const float* q, const float* kc, const float* vc, int layer, int B,
-                              int H, int t_cap, int T, float* part, int nsplit, int chunk, hipStream_t st) {
-    if (chunk > 256 || nsplit * chunk < T) return hipErrorInvalidValue;
+                              int H, int t_cap, const SeqPos& T, float* part, int nsplit, int chunk,
+                              hipStream_t st) {
+    if (B > kMaxBatch || chunk > 256) return hipErrorInvalidValue;
+    for (int b = 0; b < B; ++b)
+        if (T.t[b] < 1 || T.t[b] > t_cap || nsplit * chunk < T.t[b]) return hipErrorInvalidValue;
     hipLaunchKernelGGL(k_attn_decode, dim3(nsplit, H, B), dim3(256), 0, st, q, kc, vc, layer, B, H,
                        t_cap, T, chunk, part);
     return hipGetLastError();
 }
 
-hipError_t launch_attn_prefill(const float* q, const float* kc, const float* vc, int layer, int B,
-                               int H, int t_cap, int t0, int R, float* out, hipStream_t st) {
-    if ((long)((R + 63) / 64) * H * B >= 512) {
-        hipLaunchKernelGGL(k_attn_prefill_wide, dim3((R + 63) / 64, H, B), dim3(256), 0, st, q, kc, vc, layer, B, H,
-                           t_cap, t0, R, out);
+hipError_t launch_attn_prefill(const float* q, const float* kc, const float* vc, int layer, int Btot, int b0,
+                               int nb, int H, int t_cap, const SeqPos& t0, int R, float* out, hipStream_t st) {
+    if (b0 < 0 || nb < 1 || b0 + nb > Btot || Btot > kMaxBatch) return hipErrorInvalidValue;
+    for (int b = b0; b < b0 + nb; ++b)
+        if (t0.t[b] < 0 || t0.t[b] + R > t_cap) return hipErrorInvalidValue;
+    if ((long)((R + 63) / 64) * H * nb >= 512) {
+        hipLaunchKernelGGL(k_attn_prefill_wide, dim3((R + 63) / 64, H, nb), dim3(256), 0, st, q, kc, vc, layer, Btot,
+                           b0, H, t_cap, t0, R, out);
         return hipGetLastError();
     }
     static bool attr = false;
@@ -1290,8 +1299,8 @@ hipError_t launch_attn_prefill(const float* q, const float* kc, const float* vc,
         if (e != hipSuccess) return e;
         attr = true;
     }
-    hipLaunchKernelGGL(k_attn_prefill, dim3((R + 15) / 16, H, B), dim3(256), kAttnPrefillLds, st, q, kc, vc,
-                       layer, B, H, t_cap, t0, R, out);
+    hipLaunchKernelGGL(k_attn_prefill, dim3((R + 15) / 16, H, nb), dim3(256), kAttnPrefillLds, st, q, kc, vc,
+                       layer, Btot, b0, H, t_cap, t0, R, out);
     return hipGetLastError();
 }
 

@@ -118,7 +118,9 @@ int mt_pack_int4(const float* W, int32_t N, int32_t K, uint8_t* q, float* s);
 int mt_create(const mt_config* cfg, const mt_weights* w, int weights_on_device, void* stream,
               mt_model** out);
 
-/* Append rows at positions T_past .. T_past+P+S-1 of every sequence:
+/* Append rows to every sequence, each at its own position T_b (all equal
+ * unless sequences were appended to or restarted one at a time, see
+ * mt_prefill_seq), i.e. at T_b .. T_b+P+S-1:
  * first P prefix rows (the conditioner's output [B, P, d]), then the
  * embeddings of S token ids [B, S] (int64).  Either part may be empty
  * (NULL with size 0) but P + S >= 1.  Each appended row attends causally
@@ -128,13 +130,14 @@ int mt_create(const mt_config* cfg, const mt_weights* w, int weights_on_device, 
  * Small ONNX conversion page, decoder section: prefix rows, token rows,
  * past cache, last-position logits.  Allocates a row workspace the first
  * time a larger P + S is seen (not on the decode path).
- * Errors: MT_ERR_CACHE_FULL if T_past + P + S > t_cap.  A token id outside
+ * Errors: MT_ERR_CACHE_FULL if T_b + P + S > t_cap for some b.  A token id outside
  * [0, V) is not checked on the host (it lives on the device): the row's
  * embedding becomes NaN and mt_check reports MT_ERR_INVALID_ARG. */
 int mt_prefill(mt_model* m, const int64_t* tokens, int32_t S, const float* prefix, int32_t P,
                float* logits, int64_t* next, void* stream);
 
-/* One greedy decode step: token [B] (int64) is appended at T_past;
+/* One greedy decode step: token[b] (int64) is appended to sequence b at
+ * its own position T_b;
  * logits [B, V] and next [B] as for mt_prefill.  `next` may be passed back
  * as `token` of the following call, so greedy decoding never returns to the
  * host.  Same semantics as mt_prefill with P = 0, S = 1, on the dedicated
@@ -147,12 +150,34 @@ int mt_prefill(mt_model* m, const int64_t* tokens, int32_t S, const float* prefi
  * MT_ERR_HIP. */
 int mt_decode_step(mt_model* m, const int64_t* token, float* logits, int64_t* next, void* stream);
 
-/* Set T_past to 0.  Cache contents are left as they are (they are
+/* Set every T_b to 0.  Cache contents are left as they are (they are
  * overwritten before they are read again). */
 int mt_reset(mt_model* m);
 
-/* Current T_past (host pointer out). */
+/* Current position of sequence 0 (the shared T_past of a lockstep batch;
+ * host pointer out). */
 int mt_position(const mt_model* m, int32_t* t_past);
+
+/* ---- Ragged batch: sequences of one batch at their own positions. ----
+ * The pages' decoder is one call per chunk at a given T_past ("unifolia/
+ * muscriptor-small-onnx", decoder section; positions are implied by the
+ * cache length), and chunks of different tracks are independent; these calls
+ * let a batch hold sequences at different positions, so a new chunk can be
+ * prefilled into one slot of a running batch while the others keep decoding
+ * (mt_decode_step advances every sequence, each at its own position). */
+
+/* Append P prefix rows [P, d] and S token rows [S] (int64) to sequence b
+ * only, at its position T_b; writes the logits of its last row [V] and its
+ * argmax [1].  Same errors as mt_prefill (for sequence b); b outside
+ * [0, batch) -> MT_ERR_INVALID_ARG.  The other sequences are untouched. */
+int mt_prefill_seq(mt_model* m, int32_t b, const int64_t* tokens, int32_t S, const float* prefix, int32_t P,
+                   float* logits, int64_t* next, void* stream);
+
+/* Set T_b of sequence b to 0 (a new chunk or track starts in that slot). */
+int mt_reset_seq(mt_model* m, int32_t b);
+
+/* Current position T_b of sequence b (host pointer out). */
+int mt_position_seq(const mt_model* m, int32_t b, int32_t* t_past);
 
 /* Device pointers to the cache, [L, B, t_cap, H, 64] FP32 each.  The cache
  * is updated in place: past and present are the same buffer. */
