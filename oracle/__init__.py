@@ -57,6 +57,7 @@ def lib() -> ctypes.CDLL:
         L.oracle_quantize_int4.argtypes = [_f32p, i64, i64, _u8p, _f32p]
         L.oracle_dequantize_int4.argtypes = [_u8p, _f32p, i64, i64, _f32p]
         L.oracle_matmul.argtypes = [_f32p, i64, i64, _f32p, i64, _f32p]
+        L.oracle_round_half.argtypes = [_f32p, i64, _f32p]
         L.oracle_quantize_act_int8.argtypes = [_f32p, i64, i64, _i8p, _f32p]
         L.oracle_matmul_w4a8.argtypes = [_f32p, i64, i64, _u8p, _f32p, i64, _f32p]
         L.oracle_model_set_w4a8.argtypes = [ctypes.c_void_p, ctypes.c_int]
@@ -126,6 +127,14 @@ def matmul(A: np.ndarray, W: np.ndarray) -> np.ndarray:
     return Y
 
 
+def round_half(X: np.ndarray) -> np.ndarray:
+    """IEEE binary16 rounding (ties to even) of float32 values, returned as float32."""
+    X = _f32(X)
+    out = np.empty_like(X)
+    _check(lib().oracle_round_half(_p(X, _f32p), X.size, _p(out, _f32p)), "round_half")
+    return out
+
+
 def quantize_act_int8(X: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
     """W4A8 activation codes: [M, K] float32 -> (codes int8 [M, K], scales float32 [M, K/32])."""
     X = _f32(np.atleast_2d(X))
@@ -190,14 +199,21 @@ class OracleModel:
 
     @classmethod
     def from_weights(cls, w, batch: int, t_cap: int, eps: float = 1e-5, quantize: bool = True,
-                     w4a8: bool = False):
+                     w4a8: bool = False, dense: Optional[str] = None):
+        """dense: None (INT4 unless quantize is False), "f32" (unquantised
+        projections) or "f16" (projections rounded to binary16 first)."""
         s = w.shape
         m = cls(s.n_layers, s.d_model, s.n_heads, s.d_ff, s.vocab, batch, t_cap, eps)
         if w4a8:
             m.set_w4a8(True)
+        if dense is not None:
+            if dense not in ("f16", "f32") or w4a8:
+                raise ValueError(f"dense must be 'f16' or 'f32' without w4a8 (got {dense!r})")
+            quantize = False
+        conv = round_half if dense == "f16" else (lambda a: a)
         m.set_embed(w.tok_emb, w.lm_head, w.lnf_g, w.lnf_b)
         for l in range(s.n_layers):
-            m.set_layer(l, w.w_qkv[l], w.w_o[l], w.w_up[l], w.w_down[l],
+            m.set_layer(l, conv(w.w_qkv[l]), conv(w.w_o[l]), conv(w.w_up[l]), conv(w.w_down[l]),
                         w.ln1_g[l], w.ln1_b[l], w.ln2_g[l], w.ln2_b[l], quantize=quantize)
         return m
 

@@ -38,6 +38,13 @@
  * group product sum_k (u_k - 8) * code_k is an exact integer and the output
  * is sum_g s_w * s_a * I_g, accumulated in binary64 and rounded once.
  *
+ * Dense variants (set_layer with quantize = 0): the Core AI conversion page
+ * ships float32 models and a large model whose weights are cast to half
+ * (its file table).  The oracle takes the projection weights unquantised;
+ * for the half variant they are first rounded to IEEE binary16 by
+ * oracle_round_half (ties to even, gradual underflow, overflow to infinity)
+ * and everything downstream is unchanged.
+ *
  * Precision: every named tensor is stored as binary32; every dot product,
  * LayerNorm moment, softmax and GELU is evaluated in binary64 and rounded once.
  * Must be compiled without fast-math and with FP contraction off.
@@ -122,6 +129,33 @@ int oracle_matmul(const float* A, int64_t M, int64_t K, const float* W, int64_t 
             for (int64_t k = 0; k < K; ++k) acc += (double)a[k] * (double)w[k];
             Y[m * N + n] = (float)acc;
         }
+    }
+    return ORACLE_OK;
+}
+
+/* IEEE binary16 rounding of binary32 values, ties to even: 11 significant
+ * bits, quantum 2^(e - 10) for 2^e <= |x| < 2^(e + 1) and e >= -14, 2^-24
+ * below 2^-14 (subnormals); |x| >= 65520 (halfway above the largest finite
+ * half, 65504) becomes infinity.  Output as binary32 (exact). */
+int oracle_round_half(const float* x, int64_t n, float* out)
+{
+    if (n < 0 || (n && (!x || !out))) return ORACLE_EINVAL;
+    for (int64_t i = 0; i < n; ++i) {
+        const double v = x[i];
+        if (isnan(v)) {
+            out[i] = x[i];
+            continue;
+        }
+        const double a = fabs(v);
+        if (a >= 65520.0) {
+            out[i] = v > 0 ? INFINITY : -INFINITY;
+            continue;
+        }
+        int e;
+        frexp(a, &e); /* a = f 2^e, 0.5 <= f < 1, so 2^(e-1) <= a */
+        const int q = (e - 1 < -14 ? -14 : e - 1) - 10;
+        const double quantum = ldexp(1.0, q);
+        out[i] = (float)(nearbyint(v / quantum) * quantum); /* scaling by 2^q is exact */
     }
     return ORACLE_OK;
 }

@@ -32,12 +32,19 @@ OUT = os.path.dirname(os.path.abspath(__file__))
 # minutes; the large B=8 run is sampled at its start)
 STEPS = {"0": 16, "1": 256, "2": 1544, "3": 512, "3c576": 72, "4": 1544, "4b8": 48,
          # the W4A8 variant (oracle in its W4A8 mode) of three workloads
-         "0a8": 16, "2a8": 1544, "3a8": 512}
+         "0a8": 16, "2a8": 1544, "3a8": 512,
+         # dense-weight variants (oracle with unquantised, or binary16-rounded,
+         # projections); the large one is the pages' half-precision model
+         "0f32": 16, "0f16": 16, "2f16": 1544, "4f16": 1544}
 
 
 def workload_of(key: str):
-    """Workload and arithmetic of a golden key: '<workload>' or '<workload>a8'."""
-    return (key[:-2], True) if key.endswith("a8") else (key, False)
+    """Workload and arithmetic of a golden key: '<workload>' (INT4),
+    '<workload>a8' (W4A8), '<workload>f16' or '<workload>f32' (dense)."""
+    for suffix in ("a8", "f16", "f32"):
+        if key.endswith(suffix):
+            return key[:-len(suffix)], suffix
+    return key, None
 
 
 def weights_fingerprint(w: synth.ModelWeights) -> np.ndarray:
@@ -56,12 +63,13 @@ def sample_calls(n_calls: int, batch: int):
 
 
 def run(key: str) -> None:
-    base, w4a8 = workload_of(key)
+    base, mode = workload_of(key)
     wl = synth.WORKLOADS[base]
     steps = STEPS[key]
     t_start = time.time()
     w = synth.model_weights(wl.shape, wl.model_seed)
-    m = oracle.OracleModel.from_weights(w, batch=wl.batch, t_cap=wl.t_cap, w4a8=w4a8)
+    m = oracle.OracleModel.from_weights(w, batch=wl.batch, t_cap=wl.t_cap, w4a8=mode == "a8",
+                                        dense=mode if mode in ("f16", "f32") else None)
     prefix = synth.workload_prefix(wl) if wl.prefix_len else None
     tokens = synth.workload_tokens(wl) if wl.n_tokens else None
     n_calls = steps + 1

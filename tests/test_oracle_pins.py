@@ -546,3 +546,65 @@ def test_model_ragged_batch_equals_independent_sequences(oracle_mod):
         ks, vs = ms[b].kv()
         T = ms[b].position
         assert np.array_equal(kb[:, b, :T], ks[:, 0, :T]) and np.array_equal(vb[:, b, :T], vs[:, 0, :T])
+
+
+# ---------------------------------------------------------------- dense FP16 / FP32 variants
+
+@pytest.mark.parametrize("x,want", [
+    (1.0, 1.0),
+    (1.0 + 2.0 ** -11, 1.0),                    # tie between 1 and 1 + 2^-10: even mantissa
+    (1.0 + 3 * 2.0 ** -11, 1.0 + 2.0 ** -9),    # tie between odd and even: even wins, upward
+    (1.0 + 2.0 ** -11 + 2.0 ** -20, 1.0 + 2.0 ** -10),  # just above the tie
+    (-(2.0 - 2.0 ** -12), -2.0),                # rounds up into the next binade
+    (65504.0, 65504.0),                         # largest finite half
+    (65519.0, 65504.0),
+    (65520.0, math.inf),                        # halfway to 2^16: overflow
+    (-1e6, -math.inf),
+    (2.0 ** -14, 2.0 ** -14),                   # smallest normal
+    (2.0 ** -24, 2.0 ** -24),                   # smallest subnormal
+    (2.0 ** -25, 0.0),                          # tie between 0 and 2^-24: even (0)
+    (3 * 2.0 ** -26, 2.0 ** -24),
+    (3 * 2.0 ** -25, 2 * 2.0 ** -24),           # tie between 1 and 2 quanta: 2
+    (0.1, 1638.0 / 16384.0),                    # 0.1 = 1.6 * 2^-4: 1638.4 quanta of 2^-14
+    (-0.0, -0.0),
+])
+def test_round_half_hand_cases(oracle_mod, x, want):
+    """binary16 rounding from its definition: a wrong quantum (10 vs 11
+    bits), truncation instead of ties-to-even, a wrong subnormal threshold or
+    a wrong overflow threshold each fail one of these."""
+    got = oracle_mod.round_half(np.array([x], np.float32))[0]
+    assert got == np.float32(want) and math.copysign(1, got) == math.copysign(1, want), (x, got, want)
+
+
+def test_round_half_matches_numpy_binary16(oracle_mod):
+    """numpy's float16 conversion is an independent IEEE implementation."""
+    rng = np.random.default_rng(11)
+    x = (rng.standard_normal(200000) * np.exp2(rng.uniform(-30, 18, 200000))).astype(np.float32)
+    got = oracle_mod.round_half(x)
+    with np.errstate(over="ignore"):
+        want = x.astype(np.float16).astype(np.float32)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+def test_model_dense_modes_are_unquantised_models(oracle_mod):
+    """dense='f32' is the unquantised model and dense='f16' the unquantised
+    model of binary16-rounded projections (rounded here with numpy)."""
+    shape = synth.tiny_shape(n_layers=2)
+    w = _tiny_weights(shape, seed=35)
+    x = np.random.default_rng(2).standard_normal((1, 3, shape.d_model)).astype(np.float32)
+    m32 = oracle_mod.OracleModel.from_weights(w, batch=1, t_cap=3, dense="f32")
+    mu = oracle_mod.OracleModel.from_weights(w, batch=1, t_cap=3, quantize=False)
+    m16 = oracle_mod.OracleModel.from_weights(w, batch=1, t_cap=3, dense="f16")
+    l32, _ = m32.forward(prefix=x)
+    lu, _ = mu.forward(prefix=x)
+    l16, _ = m16.forward(prefix=x)
+    assert np.array_equal(l32, lu)
+    for lst in (w.w_qkv, w.w_o, w.w_up, w.w_down):
+        for l in range(shape.n_layers):
+            lst[l] = lst[l].astype(np.float16).astype(np.float32)
+    mr = oracle_mod.OracleModel.from_weights(w, batch=1, t_cap=3, quantize=False)
+    lr, _ = mr.forward(prefix=x)
+    assert np.array_equal(l16, lr)
+    assert not np.array_equal(l16, l32)
+    with pytest.raises(ValueError):
+        oracle_mod.OracleModel.from_weights(w, batch=1, t_cap=3, dense="bf16")
