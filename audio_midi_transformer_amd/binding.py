@@ -28,6 +28,8 @@ MT_DECODE_KERNELS = 1
 MT_DECODE_PERSISTENT = 2
 
 MT_FLAG_W4A8 = 1
+MT_FLAG_DENSE_F16 = 2
+MT_FLAG_DENSE_F32 = 4
 
 # Names declared in include/mt.h; the CPU test checks the library exports all.
 EXPORTED = ("mt_pack_int4", "mt_create", "mt_prefill", "mt_decode_step", "mt_reset",
@@ -51,7 +53,7 @@ class mt_int4(ctypes.Structure):
 class mt_weights(ctypes.Structure):
     _fields_ = [("tok_emb", ctypes.c_void_p), ("lm_head", ctypes.c_void_p),
                 ("ln_final", ctypes.c_void_p), ("ln", ctypes.c_void_p),
-                ("proj", ctypes.POINTER(mt_int4))]
+                ("proj", ctypes.POINTER(mt_int4)), ("dense", ctypes.POINTER(ctypes.c_void_p))]
 
 
 class MTError(RuntimeError):
@@ -153,20 +155,29 @@ class Decoder:
         self.L, self.d, self.H, self.F, self.V = s.n_layers, s.d_model, s.n_heads, s.d_ff, s.vocab
         cfg = mt_config(s.n_layers, s.d_model, s.n_heads, 64, s.d_ff, s.vocab, 32, batch, t_cap,
                         eps, flags)
-        if packed is None:
-            packed = pack_weights(weights)
         keep = []
+        dense_dt = np.float16 if flags & MT_FLAG_DENSE_F16 else np.float32 if flags & MT_FLAG_DENSE_F32 else None
         projs = (mt_int4 * (4 * s.n_layers))()
-        for i, (q, sc) in enumerate(packed):
-            keep += [q, sc]
-            projs[i] = mt_int4(q.ctypes.data, sc.ctypes.data)
+        dense = None
+        if dense_dt is None:
+            if packed is None:
+                packed = pack_weights(weights)
+            for i, (q, sc) in enumerate(packed):
+                keep += [q, sc]
+                projs[i] = mt_int4(q.ctypes.data, sc.ctypes.data)
+        else:
+            dense = (ctypes.c_void_p * (4 * s.n_layers))()
+            for i, W in enumerate(dense_weights(weights, dense_dt)):
+                keep.append(W)
+                dense[i] = W.ctypes.data
         ln = np.ascontiguousarray(np.stack([np.stack([weights.ln1_g[l], weights.ln1_b[l],
                                                       weights.ln2_g[l], weights.ln2_b[l]])
                                             for l in range(s.n_layers)]), dtype=np.float32)
         lnf = np.ascontiguousarray(np.stack([weights.lnf_g, weights.lnf_b]), dtype=np.float32)
         emb = np.ascontiguousarray(weights.tok_emb, dtype=np.float32)
         head = np.ascontiguousarray(weights.lm_head, dtype=np.float32)
-        w = mt_weights(emb.ctypes.data, head.ctypes.data, lnf.ctypes.data, ln.ctypes.data, projs)
+        w = mt_weights(emb.ctypes.data, head.ctypes.data, lnf.ctypes.data, ln.ctypes.data, projs,
+                       ctypes.cast(dense, ctypes.POINTER(ctypes.c_void_p)) if dense is not None else None)
         h = ctypes.c_void_p()
         check(lib().mt_create(ctypes.byref(cfg), ctypes.byref(w), 0, _stream(None), ctypes.byref(h)),
               "mt_create")
@@ -300,6 +311,16 @@ class Decoder:
     def proj_shape(self, proj: int) -> Tuple[int, int]:
         d, F = self.d, self.F
         return [(3 * d, d), (d, d), (F, d), (d, F)][proj]
+
+
+def dense_weights(weights, dtype=np.float32):
+    """Every projection as a contiguous row-major array of `dtype` (float16
+    rounds to nearest even), in mt_weights.dense order."""
+    out = []
+    for l in range(weights.shape.n_layers):
+        for W in (weights.w_qkv[l], weights.w_o[l], weights.w_up[l], weights.w_down[l]):
+            out.append(np.ascontiguousarray(np.asarray(W, dtype=np.float32).astype(dtype)))
+    return out
 
 
 def pack_weights(weights):

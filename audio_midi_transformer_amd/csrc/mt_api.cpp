@@ -57,8 +57,6 @@ struct mt_model {
     uint8_t* wq_all = nullptr;
     float* ws_all = nullptr;
     std::vector<Int4Mat> proj;  // [L*4]
-    const uint8_t** wq_ptrs = nullptr;  // device copies of the pointer tables
-    const float** ws_ptrs = nullptr;
     // cache
     float* kc = nullptr;
     float* vc = nullptr;
@@ -92,9 +90,8 @@ hipError_t dmalloc(T** p, size_t count) {
 
 void free_model(mt_model* m) {
     if (!m) return;
-    void* ptrs[] = {m->tok_emb, m->lm_head, m->ln, m->lnf, m->wq_all, m->ws_all, m->wq_ptrs,
-                    m->ws_ptrs, m->kc, m->vc, m->err, m->x, m->a, m->q, m->att, m->h, m->part,
-                    m->z, m->xbuf, m->trace, m->pf};
+    void* ptrs[] = {m->tok_emb, m->lm_head, m->ln, m->lnf, m->wq_all, m->ws_all, m->kc, m->vc, m->err, m->x,
+                    m->a, m->q, m->att, m->h, m->part, m->z, m->xbuf, m->trace, m->pf};
     for (void* p : ptrs)
         if (p) (void)hipFree(p);
     delete m;
@@ -104,7 +101,11 @@ int check_config(const mt_config* c) {
     if (!c) return fail(MT_ERR_INVALID_ARG, "config is NULL");
     if (c->head_dim != 64) return fail(MT_ERR_UNSUPPORTED, "head_dim must be 64 (got %d)", c->head_dim);
     if (c->group != 32) return fail(MT_ERR_UNSUPPORTED, "group must be 32 (got %d)", c->group);
-    if (c->flags & ~(uint32_t)MT_FLAG_W4A8) return fail(MT_ERR_UNSUPPORTED, "unknown flags 0x%x", c->flags);
+    const uint32_t known = MT_FLAG_W4A8 | MT_FLAG_DENSE_F16 | MT_FLAG_DENSE_F32;
+    if (c->flags & ~known) return fail(MT_ERR_UNSUPPORTED, "unknown flags 0x%x", c->flags);
+    if (__builtin_popcount(c->flags & known) > 1)
+        return fail(MT_ERR_UNSUPPORTED, "W4A8, dense FP16 and dense FP32 weights exclude each other (flags 0x%x)",
+                    c->flags);
     if (c->n_layers < 1 || c->n_heads < 1 || c->vocab < 1 || c->batch < 1 || c->batch > kMaxBatch ||
         c->t_cap < 1 || c->t_cap > kMaxTcap || c->d_ff < 32)
         return fail(MT_ERR_INVALID_ARG, "non-positive or out-of-range size in config");
@@ -254,12 +255,16 @@ int mt_create(const mt_config* cfg, const mt_weights* w, int weights_on_device, 
     *out = nullptr;
     int rc = check_config(cfg);
     if (rc) return rc;
-    if (!w || !w->tok_emb || !w->lm_head || !w->ln_final || !w->ln || !w->proj)
-        return fail(MT_ERR_INVALID_ARG, "mt_create: NULL weight pointer");
     const mt_config c = *cfg;
+    const int fmt = (c.flags & MT_FLAG_DENSE_F16) ? WF_F16 : (c.flags & MT_FLAG_DENSE_F32) ? WF_F32 : WF_INT4;
+    if (!w || !w->tok_emb || !w->lm_head || !w->ln_final || !w->ln || (fmt == WF_INT4 ? !w->proj : !w->dense))
+        return fail(MT_ERR_INVALID_ARG, "mt_create: NULL weight pointer");
     const int L = c.n_layers, d = c.d_model, F = c.d_ff, V = c.vocab, B = c.batch, H = c.n_heads;
     for (int i = 0; i < L * 4; ++i)
-        if (!w->proj[i].q || !w->proj[i].s) return fail(MT_ERR_INVALID_ARG, "mt_create: NULL projection %d", i);
+        if (fmt == WF_INT4 ? (!w->proj[i].q || !w->proj[i].s) : !w->dense[i])
+            return fail(MT_ERR_INVALID_ARG, "mt_create: NULL projection %d", i);
+    // bytes of a projection's weight values per input: 1/2 (nibbles), 2, 4
+    const size_t esz2 = fmt == WF_INT4 ? 1 : fmt == WF_F16 ? 4 : 8;
     hipStream_t st = (hipStream_t)stream;
     const hipMemcpyKind kind = weights_on_device ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice;
 
@@ -280,19 +285,19 @@ int mt_create(const mt_config* cfg, const mt_weights* w, int weights_on_device, 
             Int4Mat& pm = m->proj[l * 4 + p];
             pm.N = NK[p][0];
             pm.K = NK[p][1];
-            qbytes += (size_t)pm.N * pm.K / 2;
-            sfloats += (size_t)pm.N * pm.K / 32;
+            pm.fmt = fmt;
+            qbytes += (size_t)pm.N * pm.K / 2 * esz2;
+            if (fmt == WF_INT4) sfloats += (size_t)pm.N * pm.K / 32;
         }
     }
     const size_t kv = (size_t)L * B * c.t_cap * d;
     if (dmalloc(&m->tok_emb, (size_t)V * d) || dmalloc(&m->lm_head, (size_t)V * d) ||
         dmalloc(&m->ln, (size_t)L * 4 * d) || dmalloc(&m->lnf, 2 * (size_t)d) ||
-        dmalloc(&m->wq_all, qbytes) || dmalloc(&m->ws_all, sfloats) || dmalloc(&m->kc, kv) ||
+        dmalloc(&m->wq_all, qbytes) || dmalloc(&m->ws_all, std::max<size_t>(sfloats, 64)) || dmalloc(&m->kc, kv) ||
         dmalloc(&m->vc, kv) || dmalloc(&m->err, 16) || dmalloc(&m->x, (size_t)B * d) ||
         dmalloc(&m->a, (size_t)B * std::max(d, F)) || dmalloc(&m->q, (size_t)B * d) ||
         dmalloc(&m->att, (size_t)B * d) || dmalloc(&m->h, (size_t)B * F) || dmalloc(&m->part, (size_t)B * H * kMaxSplit * kPart) ||
-        dmalloc(&m->z, (size_t)B * d) || dmalloc(&m->wq_ptrs, (size_t)L * 4) ||
-        dmalloc(&m->ws_ptrs, (size_t)L * 4))
+        dmalloc(&m->z, (size_t)B * d))
         return bail(fail(MT_ERR_OOM, "mt_create: device allocation failed (KV cache %zu bytes)", 2 * kv * 4));
 
     auto cpy = [&](void* dst, const void* src, size_t bytes) {
@@ -302,25 +307,20 @@ int mt_create(const mt_config* cfg, const mt_weights* w, int weights_on_device, 
         cpy(m->ln, w->ln, (size_t)L * 4 * d * 4) || cpy(m->lnf, w->ln_final, (size_t)2 * d * 4))
         return bail(fail(MT_ERR_HIP, "mt_create: weight copy failed"));
     size_t qo = 0, so = 0;
-    std::vector<const uint8_t*> hq(L * 4);
-    std::vector<const float*> hs(L * 4);
     for (int i = 0; i < L * 4; ++i) {
         Int4Mat& pm = m->proj[i];
-        const size_t nb = (size_t)pm.N * pm.K / 2, ns = (size_t)pm.N * pm.K / 32;
-        if (cpy(m->wq_all + qo, w->proj[i].q, nb) || cpy(m->ws_all + so, w->proj[i].s, ns * 4))
+        const size_t nb = (size_t)pm.N * pm.K / 2 * esz2, ns = fmt == WF_INT4 ? (size_t)pm.N * pm.K / 32 : 0;
+        if (fmt == WF_INT4 ? (cpy(m->wq_all + qo, w->proj[i].q, nb) || cpy(m->ws_all + so, w->proj[i].s, ns * 4))
+                           : cpy(m->wq_all + qo, w->dense[i], nb) != hipSuccess)
             return bail(fail(MT_ERR_HIP, "mt_create: projection copy failed"));
         pm.q = m->wq_all + qo;
-        pm.s = m->ws_all + so;
-        hq[i] = pm.q;
-        hs[i] = pm.s;
+        pm.s = fmt == WF_INT4 ? m->ws_all + so : nullptr;
         qo += nb;
         so += ns;
     }
-    if (hipMemcpyAsync(m->wq_ptrs, hq.data(), hq.size() * sizeof(void*), hipMemcpyHostToDevice, st) ||
-        hipMemcpyAsync(m->ws_ptrs, hs.data(), hs.size() * sizeof(void*), hipMemcpyHostToDevice, st) ||
-        hipMemsetAsync(m->err, 0, 16, st))
-        return bail(fail(MT_ERR_HIP, "mt_create: table copy failed"));
-    m->persistent_ok = persistent_supported(d, F, H, B, V);
+    if (hipMemsetAsync(m->err, 0, 16, st)) return bail(fail(MT_ERR_HIP, "mt_create: clearing the error word failed"));
+    // the single-launch step reads nibbles only
+    m->persistent_ok = fmt == WF_INT4 && persistent_supported(d, F, H, B, V);
     if (m->persistent_ok) {
         const size_t xb = persistent_xbuf_bytes(L, d, F, H, B, V);
         if (hipMalloc(&m->xbuf, xb) != hipSuccess || hipMemsetAsync(m->xbuf, 0, xb, st) != hipSuccess)

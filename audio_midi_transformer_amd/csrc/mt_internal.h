@@ -36,11 +36,20 @@ struct QkvDest {
     SeqPos pos;      // cache position of each sequence's first row
 };
 
+// Storage format of a projection's weights.
+enum WeightFmt : int {
+    WF_INT4 = 0,  // packed nibbles [N, K/2] + FP32 group scales [N, K/32]
+    WF_F16 = 1,   // dense IEEE half [N, K]
+    WF_F32 = 2,   // dense float [N, K]
+};
+
+// One projection W [N, K] (row n = output feature n).
 struct Int4Mat {
-    const uint8_t* q;  // [N, K/2]
-    const float* s;    // [N, K/32]
+    const uint8_t* q;  // INT4: nibbles [N, K/2]; dense: the values [N, K]
+    const float* s;    // INT4: group scales [N, K/32]; dense: unused
     int N;
     int K;
+    int fmt = WF_INT4;
 };
 
 // ---- launchers (mt_kernels.hip); all return hipGetLastError() ----

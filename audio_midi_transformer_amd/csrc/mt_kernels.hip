@@ -12,6 +12,7 @@
 //                              (SkipLayerNormalization nodes)
 //   LM head + greedy argmax    medium ONNX README table (FP32 LM head); small
 //                              ONNX conversion page (greedy decoding)
+#include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -188,7 +189,15 @@ constexpr int GV_M = 8;           // activation rows held in LDS
 // with A = activation codes (16 rows, 8 used) and B = 16 (u - 8) of 16
 // weight rows; the INT32 tile is exact and is added to the FP32 result as
 // I * s_a * s_w / 16.
-template <bool A8>
+//
+// WF = WF_F16 / WF_F32 (dense weights): lane l reads the 8 contiguous
+// values W[n0 + l % 16][g * 32 + 8 (l / 16) + s], s < 8, of each of its
+// groups in one or two vector loads, and feeds the activations of the same
+// columns (no scales); everything around the MFMA is the same.  The raw
+// bits stay in registers until the MFMA loop widens them, so that every
+// group's load is in flight at once (a use next to the load would make each
+// wait for the previous one).
+template <int WF, bool A8>
 __global__ __launch_bounds__(256) void k_gemv_w4(const float* __restrict__ X, int ldx, int M, int K, int kspan,
                                                  const float* __restrict__ ln_g, const float* __restrict__ ln_b,
                                                  float eps, const float* __restrict__ part, int H, int ns,
@@ -216,16 +225,31 @@ __global__ __launch_bounds__(256) void k_gemv_w4(const float* __restrict__ X, in
         // are staged
         const int wv = __builtin_amdgcn_readfirstlane(wave);
         const int ngw = (gch - wv + 3) / 4;
+        // INT4: nibbles (wq) and scale (sc) of each group; F16: the 8
+        // halves (wq); F32: the 8 floats' bits (wq, then wq2)
         uint4 wq[GV_MAXSPAN / 128];
+        uint4 wq2[WF == WF_F32 ? GV_MAXSPAN / 128 : 1];
         float sc[GV_MAXSPAN / 128];
+        const unsigned fill = WF == WF_INT4 ? 0x88888888u : 0u;
 #pragma unroll
         for (int i = 0; i < GV_MAXSPAN / 128; ++i) {
-            wq[i] = make_uint4(0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u);
+            wq[i] = make_uint4(fill, fill, fill, fill);
+            if constexpr (WF == WF_F32) wq2[i] = make_uint4(0u, 0u, 0u, 0u);
             sc[i] = 0.f;
             if (i < ngw && rvalid) {
                 const int g = gbase + wv + 4 * i;
-                wq[i] = *reinterpret_cast<const uint4*>(Wq + (size_t)row * (K / 2) + (size_t)g * 16);
-                sc[i] = Ws[(size_t)row * G + g];
+                if constexpr (WF == WF_INT4) {
+                    wq[i] = *reinterpret_cast<const uint4*>(Wq + (size_t)row * (K / 2) + (size_t)g * 16);
+                    sc[i] = Ws[(size_t)row * G + g];
+                } else {
+                    const size_t e = (size_t)row * K + (size_t)g * 32 + 8 * kq;
+                    if constexpr (WF == WF_F16) {
+                        wq[i] = *reinterpret_cast<const uint4*>(Wq + 2 * e);
+                    } else {
+                        wq[i] = *reinterpret_cast<const uint4*>(Wq + 4 * e);
+                        wq2[i] = *reinterpret_cast<const uint4*>(Wq + 4 * e + 16);
+                    }
+                }
             }
         }
         if (c0) __syncthreads();
@@ -324,7 +348,7 @@ __global__ __launch_bounds__(256) void k_gemv_w4(const float* __restrict__ X, in
             }
         }
         __syncthreads();
-        if constexpr (A8) {
+        if constexpr (A8 && WF == WF_INT4) {
             // ---- INT8 codes of the staged rows, one (row, group) per thread
             // and pass: codes [GV_M][cw] bytes, scales [gch][GV_M]
             const size_t wfl = part ? (size_t)M * (cw / 64) * ns : 0;
@@ -400,7 +424,7 @@ __global__ __launch_bounds__(256) void k_gemv_w4(const float* __restrict__ X, in
         // bm - 8 and pass zero.
         const int sh = (kq >> 1) * 8 + (kq & 1) * 4;
         const bool bvalid = bm < GV_M;
-        const float* xb = xt + (bm & (GV_M - 1)) * XS + kq;
+        const float* xb = xt + (bm & (GV_M - 1)) * XS + (WF == WF_INT4 ? kq : 8 * kq);
 #pragma unroll
         for (int i = 0; i < GV_MAXSPAN / 128; ++i) {
             if (i < ngw) {
@@ -409,11 +433,19 @@ __global__ __launch_bounds__(256) void k_gemv_w4(const float* __restrict__ X, in
                 const unsigned wd[4] = {wq[i].x, wq[i].y, wq[i].z, wq[i].w};
                 float bv[8];
 #pragma unroll
-                for (int s = 0; s < 8; ++s) bv[s] = xb[gi * 32 + 4 * s];
+                for (int s = 0; s < 8; ++s) bv[s] = xb[gi * 32 + (WF == WF_INT4 ? 4 * s : s)];
 #pragma unroll
                 for (int s = 0; s < 8; ++s) {
-                    const float u = (float)((wd[s >> 1] >> (sh + 16 * (s & 1))) & 15u);
-                    const float a = fmaf(sc[i], u, s8);
+                    float a;
+                    if constexpr (WF == WF_INT4) {
+                        const float u = (float)((wd[s >> 1] >> (sh + 16 * (s & 1))) & 15u);
+                        a = fmaf(sc[i], u, s8);
+                    } else if constexpr (WF == WF_F16) {
+                        a = __half2float(__ushort_as_half((unsigned short)(wd[s >> 1] >> (16 * (s & 1)))));
+                    } else {
+                        const unsigned w2[4] = {wq2[i].x, wq2[i].y, wq2[i].z, wq2[i].w};
+                        a = __uint_as_float(s < 4 ? wd[s] : w2[s - 4]);
+                    }
                     const float b = bvalid ? bv[s] : 0.f;
                     if (i & 1) acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc1, 0, 0, 0);
                     else acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc0, 0, 0, 0);
@@ -455,7 +487,7 @@ __global__ __launch_bounds__(256) void k_gemv_w4(const float* __restrict__ X, in
 constexpr int GN = 64;
 constexpr size_t gemm_lds(int tm, int gk) { return sizeof(float) * (tm + GN) * (gk + 4); }
 
-template <int TM, int GK>
+template <int TM, int GK, int WF>
 __global__ __launch_bounds__(256) void k_gemm_w4(const float* __restrict__ X, int ldx, int M, int K,
                                                  const uint8_t* __restrict__ Wq,
                                                  const float* __restrict__ Ws, int N,
@@ -480,7 +512,9 @@ __global__ __launch_bounds__(256) void k_gemm_w4(const float* __restrict__ X, in
     // per thread.  Nibbles: thread t takes quarter t % 4 (GK / 4 columns,
     // inside one group) of weight row t / 4, with that group's scale.
     constexpr int NA = TM * GK / 4 / 256;
-    constexpr int NW = GK / 32;  // nibble dwords per thread
+    // weight dwords per thread: GK / 4 columns as nibbles, halves or floats
+    constexpr int NW = WF == WF_INT4 ? GK / 32 : WF == WF_F16 ? GK / 8 : GK / 4;
+    constexpr int ESZ2 = WF == WF_INT4 ? 1 : WF == WF_F16 ? 4 : 8;  // bytes per 2 columns
     float4 pa[NA];
     unsigned pw[NW];
     float ps = 0.f;
@@ -495,11 +529,22 @@ __global__ __launch_bounds__(256) void k_gemm_w4(const float* __restrict__ X, in
         }
         const int c0 = k0 + wq * (GK / 4), g = c0 / 32;
         const bool ok = n0 + wrow < N && c0 < ke;
+        const uint8_t* wrow_p = Wq + ((size_t)(n0 + wrow) * K + c0) / 2 * ESZ2;
+        const unsigned fill = WF == WF_INT4 ? 0x88888888u : 0u;
+        if constexpr (NW % 4 == 0) {
 #pragma unroll
-        for (int i = 0; i < NW; ++i)
-            pw[i] = ok ? *reinterpret_cast<const unsigned*>(Wq + (size_t)(n0 + wrow) * (K / 2) + c0 / 2 + 4 * i)
-                       : 0x88888888u;
-        ps = ok ? Ws[(size_t)(n0 + wrow) * G + g] : 0.f;
+            for (int i = 0; i < NW; i += 4) {
+                const uint4 t = ok ? *reinterpret_cast<const uint4*>(wrow_p + 4 * i) : make_uint4(fill, fill, fill, fill);
+                pw[i] = t.x, pw[i + 1] = t.y, pw[i + 2] = t.z, pw[i + 3] = t.w;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < NW; i += 2) {
+                const uint2 t = ok ? *reinterpret_cast<const uint2*>(wrow_p + 4 * i) : make_uint2(fill, fill);
+                pw[i] = t.x, pw[i + 1] = t.y;
+            }
+        }
+        if constexpr (WF == WF_INT4) ps = ok ? Ws[(size_t)(n0 + wrow) * G + g] : 0.f;
     };
     load_stage(kb);
     for (int k0 = kb; k0 < ke; k0 += GK) {
@@ -510,21 +555,36 @@ __global__ __launch_bounds__(256) void k_gemm_w4(const float* __restrict__ X, in
             *reinterpret_cast<float4*>(As + (idx / (GK / 4)) * GS + (idx % (GK / 4)) * 4) = pa[e];
         }
         {
-            // dword i holds inputs 8 i .. 8 i + 7 of the quarter, low nibble first
             float* dst = Bs + wrow * GS + wq * (GK / 4);
+            if constexpr (WF == WF_INT4) {
+                // dword i holds inputs 8 i .. 8 i + 7 of the quarter, low nibble first
 #pragma unroll
-            for (int i = 0; i < NW; ++i)
+                for (int i = 0; i < NW; ++i)
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    float v[4];
+                    for (int h = 0; h < 2; ++h) {
+                        float v[4];
 #pragma unroll
-                    for (int b = 0; b < 2; ++b) {
-                        const unsigned byte = (pw[i] >> (8 * (2 * h + b))) & 0xFFu;
-                        v[2 * b] = (float)((int)(byte & 15u) - 8) * ps;
-                        v[2 * b + 1] = (float)((int)(byte >> 4) - 8) * ps;
+                        for (int b = 0; b < 2; ++b) {
+                            const unsigned byte = (pw[i] >> (8 * (2 * h + b))) & 0xFFu;
+                            v[2 * b] = (float)((int)(byte & 15u) - 8) * ps;
+                            v[2 * b + 1] = (float)((int)(byte >> 4) - 8) * ps;
+                        }
+                        *reinterpret_cast<float4*>(dst + i * 8 + h * 4) = make_float4(v[0], v[1], v[2], v[3]);
                     }
-                    *reinterpret_cast<float4*>(dst + i * 8 + h * 4) = make_float4(v[0], v[1], v[2], v[3]);
+            } else if constexpr (WF == WF_F16) {
+                // dword i holds inputs 2 i, 2 i + 1
+#pragma unroll
+                for (int i = 0; i < NW; i += 2) {
+                    const float2 a = __half22float2(*reinterpret_cast<const __half2*>(&pw[i]));
+                    const float2 b = __half22float2(*reinterpret_cast<const __half2*>(&pw[i + 1]));
+                    *reinterpret_cast<float4*>(dst + 2 * i) = make_float4(a.x, a.y, b.x, b.y);
                 }
+            } else {
+#pragma unroll
+                for (int i = 0; i < NW; i += 4)
+                    *reinterpret_cast<float4*>(dst + i) = make_float4(__uint_as_float(pw[i]), __uint_as_float(pw[i + 1]),
+                                                                      __uint_as_float(pw[i + 2]), __uint_as_float(pw[i + 3]));
+            }
         }
         __syncthreads();
         if (k0 + GK < ke) load_stage(k0 + GK);
@@ -1154,6 +1214,13 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ q, 
     }
 }
 
+// Dense weights as float (half widened exactly).
+__global__ __launch_bounds__(256) void k_widen(const uint8_t* __restrict__ q, bool half, size_t n,
+                                               float* __restrict__ out) {
+    for (size_t j = blockIdx.x * (size_t)blockDim.x + threadIdx.x; j < n; j += (size_t)gridDim.x * blockDim.x)
+        out[j] = half ? __half2float(reinterpret_cast<const __half*>(q)[j]) : reinterpret_cast<const float*>(q)[j];
+}
+
 // ---------------------------------------------------------------- launchers
 
 hipError_t launch_embed(const int64_t* tokens, int S, const float* prefix, int P, const float* emb,
@@ -1192,6 +1259,7 @@ static void plan_gemv(int N, int K, Epilogue epi, int granule, int* ksplit, int*
 hipError_t launch_w4_matmul(const float* x, int ldx, int M, const Int4Mat& w, const float* ln_g,
                             const float* ln_b, float eps, float* y, int ldy, Epilogue epi, const QkvDest* qkv,
                             bool force_gemm, hipStream_t st, const AttnParts* parts, bool a8) {
+    if (a8 && w.fmt != WF_INT4) return hipErrorInvalidValue;  // A8 codes pair with nibbles only
     const AttnParts ap = parts ? *parts : AttnParts{nullptr, 0, 0};
     EpiArgs ep{};
     ep.epi = epi;
@@ -1214,21 +1282,23 @@ hipError_t launch_w4_matmul(const float* x, int ldx, int M, const Int4Mat& w, co
         if (lds > kGemvMaxLds) return hipErrorInvalidValue;
         static bool attr = false;
         if (!attr) {
-            hipError_t e = hipFuncSetAttribute((const void*)k_gemv_w4<false>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                               (int)kGemvMaxLds);
-            if (e == hipSuccess)
-                e = hipFuncSetAttribute((const void*)k_gemv_w4<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                        (int)kGemvMaxLds);
-            if (e != hipSuccess) return e;
+            const void* fns[4] = {(const void*)k_gemv_w4<WF_INT4, false>, (const void*)k_gemv_w4<WF_INT4, true>,
+                                  (const void*)k_gemv_w4<WF_F16, false>, (const void*)k_gemv_w4<WF_F32, false>};
+            for (const void* f : fns) {
+                const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGemvMaxLds);
+                if (e != hipSuccess) return e;
+            }
             attr = true;
         }
         const dim3 grid((w.N + 15) / 16, ksplit);
-        if (a8)
-            hipLaunchKernelGGL(k_gemv_w4<true>, grid, dim3(256), lds, st, x, ldx, M, w.K, kspan, ln_g, ln_b, eps,
-                               ap.part, ap.H, ap.nsplit, w.q, w.s, w.N, y, ldy, ep);
-        else
-            hipLaunchKernelGGL(k_gemv_w4<false>, grid, dim3(256), lds, st, x, ldx, M, w.K, kspan, ln_g, ln_b, eps,
-                               ap.part, ap.H, ap.nsplit, w.q, w.s, w.N, y, ldy, ep);
+#define MT_GEMV(WFV, A8V)                                                                                        \
+    hipLaunchKernelGGL((k_gemv_w4<WFV, A8V>), grid, dim3(256), lds, st, x, ldx, M, w.K, kspan, ln_g, ln_b, eps, \
+                       ap.part, ap.H, ap.nsplit, w.q, w.s, w.N, y, ldy, ep)
+        if (w.fmt == WF_F16) MT_GEMV(WF_F16, false);
+        else if (w.fmt == WF_F32) MT_GEMV(WF_F32, false);
+        else if (a8) MT_GEMV(WF_INT4, true);
+        else MT_GEMV(WF_INT4, false);
+#undef MT_GEMV
         return hipGetLastError();
     }
     if (ln_g || ap.part) return hipErrorInvalidValue;  // the GEMM path takes plain rows
@@ -1240,7 +1310,7 @@ hipError_t launch_w4_matmul(const float* x, int ldx, int M, const Int4Mat& w, co
     const bool small = (long)ntile * ((M + 63) / 64) < 512;
     const int TM = small ? 32 : 64, GKs = small ? 128 : 64;
     const dim3 grid(ntile, (M + TM - 1) / TM, ksplit);
-    if (a8) {
+    if (a8 && w.fmt == WF_INT4) {
         if (small)
             hipLaunchKernelGGL((k_gemm_w4a8<32, 128>), grid, dim3(256), 0, st, x, ldx, M, w.K, w.q, w.s, w.N, y, ldy,
                                ep);
@@ -1252,20 +1322,31 @@ hipError_t launch_w4_matmul(const float* x, int ldx, int M, const Int4Mat& w, co
     const int kspan = (w.K + GKs - 1) / GKs * GKs;
     static bool attr = false;
     if (!attr) {
-        hipError_t e = hipFuncSetAttribute((const void*)k_gemm_w4<64, 64>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           (int)gemm_lds(64, 64));
-        if (e == hipSuccess)
-            e = hipFuncSetAttribute((const void*)k_gemm_w4<32, 128>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                    (int)gemm_lds(32, 128));
-        if (e != hipSuccess) return e;
+        const void* f64[3] = {(const void*)k_gemm_w4<64, 64, WF_INT4>, (const void*)k_gemm_w4<64, 64, WF_F16>,
+                              (const void*)k_gemm_w4<64, 64, WF_F32>};
+        const void* f32[3] = {(const void*)k_gemm_w4<32, 128, WF_INT4>, (const void*)k_gemm_w4<32, 128, WF_F16>,
+                              (const void*)k_gemm_w4<32, 128, WF_F32>};
+        for (int i = 0; i < 3; ++i) {
+            hipError_t e = hipFuncSetAttribute(f64[i], hipFuncAttributeMaxDynamicSharedMemorySize, (int)gemm_lds(64, 64));
+            if (e == hipSuccess)
+                e = hipFuncSetAttribute(f32[i], hipFuncAttributeMaxDynamicSharedMemorySize, (int)gemm_lds(32, 128));
+            if (e != hipSuccess) return e;
+        }
         attr = true;
     }
-    if (small)
-        hipLaunchKernelGGL((k_gemm_w4<32, 128>), grid, dim3(256), gemm_lds(32, 128), st, x, ldx, M, w.K, w.q, w.s,
-                           w.N, y, ldy, ep, kspan);
-    else
-        hipLaunchKernelGGL((k_gemm_w4<64, 64>), grid, dim3(256), gemm_lds(64, 64), st, x, ldx, M, w.K, w.q, w.s,
-                           w.N, y, ldy, ep, kspan);
+#define MT_GEMM(TMV, GKV, WFV)                                                                                   \
+    hipLaunchKernelGGL((k_gemm_w4<TMV, GKV, WFV>), grid, dim3(256), gemm_lds(TMV, GKV), st, x, ldx, M, w.K, w.q, \
+                       w.s, w.N, y, ldy, ep, kspan)
+    if (small) {
+        if (w.fmt == WF_F16) MT_GEMM(32, 128, WF_F16);
+        else if (w.fmt == WF_F32) MT_GEMM(32, 128, WF_F32);
+        else MT_GEMM(32, 128, WF_INT4);
+    } else {
+        if (w.fmt == WF_F16) MT_GEMM(64, 64, WF_F16);
+        else if (w.fmt == WF_F32) MT_GEMM(64, 64, WF_F32);
+        else MT_GEMM(64, 64, WF_INT4);
+    }
+#undef MT_GEMM
     return hipGetLastError();
 }
 
@@ -1317,6 +1398,12 @@ hipError_t launch_argmax(const float* logits, int B, int V, int64_t* next, hipSt
 }
 
 hipError_t launch_dequant(const Int4Mat& w, float* out, hipStream_t st) {
+    if (w.fmt != WF_INT4) {
+        const size_t n = (size_t)w.N * w.K;
+        const int grid = (int)((n + 255) / 256 < 65536 ? (n + 255) / 256 : 65536);
+        hipLaunchKernelGGL(k_widen, dim3(grid), dim3(256), 0, st, w.q, w.fmt == WF_F16, n, out);
+        return hipGetLastError();
+    }
     const size_t nbytes = (size_t)w.N * w.K / 2;
     const int grid = (int)((nbytes + 255) / 256 < 65536 ? (nbytes + 255) / 256 : 65536);
     hipLaunchKernelGGL(k_dequant, dim3(grid), dim3(256), 0, st, w.q, w.s, w.N, w.K, out);

@@ -35,14 +35,19 @@ INT8_MFMA_PEAK_TOPS = 5000.0
 STEADY_FROM = 8
 
 
-def step_bytes(shape, B: int, T: int) -> float:
+# bytes per projection weight: INT4 nibble + FP32 scale per 32; binary16; binary32
+WEIGHT_BYTES = {"int4": 0.5 + 4.0 / 32, "f16": 2.0, "f32": 4.0}
+
+
+def step_bytes(shape, B: int, T: int, wbytes: float = WEIGHT_BYTES["int4"]) -> float:
     """Algorithmic HBM bytes of one decode step over B sequences with T keys
-    (the new row included): packed INT4 nibbles + FP32 group scales of the
-    four projections, FP32 LM head, LayerNorm parameters, live K/V read, new
-    K/V row written, embedding row, logits, token in / argmax out."""
+    (the new row included): the four projections' weights (packed INT4
+    nibbles + FP32 group scales, or dense values), FP32 LM head, LayerNorm
+    parameters, live K/V read, new K/V row written, embedding row, logits,
+    token in / argmax out."""
     L, d, F, V = shape.n_layers, shape.d_model, shape.d_ff, shape.vocab
     w_per_layer = 3 * d * d + d * d + 2 * d * F
-    weights = 0.625 * w_per_layer * L + 4.0 * V * d + 4.0 * (4 * L * d + 2 * d)
+    weights = wbytes * w_per_layer * L + 4.0 * V * d + 4.0 * (4 * L * d + 2 * d)
     per_seq = 8.0 * L * d * T + 8.0 * L * d + 4.0 * d + 4.0 * V + 16.0
     return weights + B * per_seq
 
@@ -63,10 +68,11 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(kernel: str, workload_key: str):
+def traffic_from_profiles(kernel: str, workload_key: str, variant: str = ""):
     """HBM traffic per launch from committed rocprofv3 counter summaries, or
-    None when they are missing or were taken on different kernel sources."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_wl{workload_key}.json")
+    None when they are missing or were taken on different kernel sources.
+    `variant` is "" (INT4 weights, FP32 activations), "a8", "f16" or "f32"."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_wl{workload_key}{variant}.json")
     if not os.path.exists(path):
         return None
     with open(path) as fh:
@@ -76,14 +82,15 @@ def traffic_from_profiles(kernel: str, workload_key: str):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(wl, weights, prefix_np, tokens_np, max_steps: int = 8, w4a8: bool = False):
+def cpu_baseline(wl, weights, prefix_np, tokens_np, max_steps: int = 8, w4a8: bool = False,
+                 dense=None):
     """The CPU oracle as it stands, on this host, on a bounded sample of the
     workload: its prefill, then `max_steps` greedy decode steps."""
     import oracle
     cores = len(os.sched_getaffinity(0))
     cores = min(cores, int(os.environ.get("OMP_NUM_THREADS", cores)))
     os.environ["OMP_NUM_THREADS"] = str(cores)
-    m = oracle.OracleModel.from_weights(weights, batch=wl.batch, t_cap=wl.t_cap, w4a8=w4a8)
+    m = oracle.OracleModel.from_weights(weights, batch=wl.batch, t_cap=wl.t_cap, w4a8=w4a8, dense=dense)
     t0 = time.perf_counter()
     _, nxt = m.forward(tokens=tokens_np, prefix=prefix_np)
     t1 = time.perf_counter()
@@ -163,6 +170,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--w4a8", action="store_true",
                     help="the W4A8 variant: INT8 activation codes per row and group of 32, INT32 group sums")
+    ap.add_argument("--weights", choices=["int4", "f16", "f32"], default="int4",
+                    help="projection weights: INT4 group-32 (default) or the dense binary16 / binary32 variants")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="before the bench, copy a buffer of this many MiB device-to-device three "
                          "times (a plain copy of known size, to scale HBM byte counters)")
@@ -170,6 +179,9 @@ def main() -> int:
                     help="reduce two rocprofv3 counter files of a --calibration-copy-mib run to the "
                          "per-launch HBM traffic record (printed as JSON) and exit")
     args = ap.parse_args()
+    if args.w4a8 and args.weights != "int4":
+        ap.error("--w4a8 needs --weights int4")
+    variant = "a8" if args.w4a8 else "" if args.weights == "int4" else args.weights
     if args.reduce_counters:
         cmds = [f"rocprofv3 --pmc {c} -f csv -d <dir> -o pmc -- python3 bench.py --workload {args.workload} "
                 f"--steps 1 --warmup 0 --no-cpu-baseline --calibration-copy-mib {args.calibration_copy_mib}"
@@ -210,7 +222,9 @@ def main() -> int:
     weights = synth.model_weights(shape, wl.model_seed)
     prefix_np = synth.workload_prefix(wl) if wl.prefix_len else None
     tokens_np = synth.workload_tokens(wl) if wl.n_tokens else None
-    dec = binding.Decoder(weights, batch=B, t_cap=wl.t_cap, flags=binding.MT_FLAG_W4A8 if args.w4a8 else 0)
+    flags = {"": 0, "a8": binding.MT_FLAG_W4A8, "f16": binding.MT_FLAG_DENSE_F16,
+             "f32": binding.MT_FLAG_DENSE_F32}[variant]
+    dec = binding.Decoder(weights, batch=B, t_cap=wl.t_cap, flags=flags)
     path = {"auto": binding.MT_DECODE_AUTO, "kernels": binding.MT_DECODE_KERNELS,
             "persistent": binding.MT_DECODE_PERSISTENT}[args.path]
     persistent = path != binding.MT_DECODE_KERNELS and dec_is_persistent(dec)
@@ -262,12 +276,13 @@ def main() -> int:
     steady_ms = float(np.mean([e["s0"].elapsed_time(e["s1"]) for e in evs]))
     n_steady = n_dec - STEADY_FROM
     ms_tok = steady_ms / n_steady
-    launch_bytes = np.array([step_bytes(shape, B, R0 + k + 1) for k in range(STEADY_FROM, n_dec)])
+    wbytes = WEIGHT_BYTES[args.weights]
+    launch_bytes = np.array([step_bytes(shape, B, R0 + k + 1, wbytes) for k in range(STEADY_FROM, n_dec)])
     gbps = float(launch_bytes.sum()) / (steady_ms * 1e-3) / 1e9
     step_ms = np.concatenate([np.array([a.elapsed_time(b) for a, b in e["per"]])[STEADY_FROM:] for e in evs])
     kernel_name = "mt_decode_step_persistent" if persistent else "decode_step_kernels"
     achieved = float(launch_bytes.sum() * args.steps / (step_ms.sum() * 1e-3) / 1e9)
-    traffic = traffic_from_profiles(kernel_name, wl.key)
+    traffic = traffic_from_profiles(kernel_name, wl.key, variant)
     pf_flops = prefill_flops(shape, B, R0)
 
     # point values at T = 505, 1024 and 2048 keys (where the pass reaches them)
@@ -280,6 +295,8 @@ def main() -> int:
     metric = METRIC if wl.key == "2" else f"decode ms/token + achieved HBM GB/s, workload {wl.key}"
     if args.w4a8:
         metric += " (W4A8 variant)"
+    elif args.weights != "int4":
+        metric += f" (dense {args.weights.upper()} weights)"
     out = {
         "metric": metric,
         "value": round(ms_tok, 5),
@@ -292,7 +309,8 @@ def main() -> int:
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "i8 x i4 -> i32 projections, f32 elsewhere" if args.w4a8 else "f32",
-        "weights": "int4 symmetric RTN, group 32, fp32 scales",
+        "weights": {"int4": "int4 symmetric RTN, group 32, fp32 scales", "f16": "dense binary16",
+                    "f32": "dense binary32"}[args.weights],
         "activations": ("int8 symmetric per row and group of 32, dynamic" if args.w4a8 else "fp32"),
         "data": "synthetic (seeded N(0,0.02) weights, N(0,1) prefix; no checkpoint)",
         "config": {"workload": f"{wl.key}: {wl.name}", "layers": shape.n_layers,
@@ -321,7 +339,8 @@ def main() -> int:
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(wl, weights, prefix_np, tokens_np, w4a8=args.w4a8)
+        out["cpu_baseline"] = cpu_baseline(wl, weights, prefix_np, tokens_np, w4a8=args.w4a8,
+                                           dense=None if args.weights == "int4" else args.weights)
     dec.close()
     print(json.dumps(out), flush=True)
     return 0

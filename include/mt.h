@@ -57,7 +57,7 @@ typedef struct {
     int32_t batch;     /* B sequences that advance in lockstep, 1..64 */
     int32_t t_cap;     /* fixed cache capacity per sequence (positions), 1..16384 */
     float ln_eps;      /* LayerNorm epsilon (1e-5) */
-    uint32_t flags;    /* 0 or MT_FLAG_W4A8 */
+    uint32_t flags;    /* 0, MT_FLAG_W4A8, MT_FLAG_DENSE_F16 or MT_FLAG_DENSE_F32 */
 } mt_config;
 
 /* W4A8 variant of the four projections.  The medium ONNX README ("Model
@@ -70,6 +70,19 @@ typedef struct {
  * is sum_g s_w * s_a * I_g in FP32.  Attention, LayerNorm, the LM head and
  * the cache stay FP32.  Every decode path and the prefill support it. */
 #define MT_FLAG_W4A8 1u
+
+/* Dense-weight variants: the four projections are given unquantised in
+ * mt_weights.dense (mt_weights.proj is not read) as row-major W [N, K] in
+ * IEEE binary16 (MT_FLAG_DENSE_F16) or binary32 (MT_FLAG_DENSE_F32); each
+ * value is widened exactly to FP32 and every other step is unchanged.  These
+ * are the Core AI conversion's float32 files and its large float16 file,
+ * whose weights are cast to half (its file table; "Faithfulness" on why
+ * small fp16 is not shipped).  At most
+ * one of MT_FLAG_W4A8, MT_FLAG_DENSE_F16 and MT_FLAG_DENSE_F32 may be set;
+ * otherwise mt_create returns MT_ERR_UNSUPPORTED.  Dense models run the
+ * multi-kernel decode step (MT_DECODE_PERSISTENT is refused). */
+#define MT_FLAG_DENSE_F16 2u
+#define MT_FLAG_DENSE_F32 4u
 
 /* One INT4 projection in the canonical packed form.
  * For a matrix W [N, K] (row n = output feature n, K = input width):
@@ -96,6 +109,9 @@ typedef struct {
  *                               O    [d, d]
  *                               up   [F, d]
  *                               down [d, F]
+ *   dense    [L * 4]          same order; only with MT_FLAG_DENSE_F16 / _F32:
+ *                               dense[i] points to W [N, K] row-major, binary16
+ *                               or binary32 per the flag (proj may be NULL)
  * No projection has a bias. */
 typedef struct {
     const float* tok_emb;
@@ -103,6 +119,7 @@ typedef struct {
     const float* ln_final;
     const float* ln;
     const mt_int4* proj;
+    const void* const* dense;
 } mt_weights;
 
 /* Host-side canonical packer (host pointers).  W [N, K] FP32 -> q [N, K/2],

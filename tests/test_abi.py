@@ -73,10 +73,15 @@ def _cfg(**kw):
     (dict(batch=0), binding.MT_ERR_INVALID_ARG),
     (dict(t_cap=0), binding.MT_ERR_INVALID_ARG),
     (dict(ln_eps=0.0), binding.MT_ERR_INVALID_ARG),
-    (dict(flags=2), binding.MT_ERR_UNSUPPORTED),
-    (dict(flags=6), binding.MT_ERR_UNSUPPORTED),
-    # W4A8 is a valid mode: the config passes and the NULL weights are refused
+    (dict(flags=8), binding.MT_ERR_UNSUPPORTED),
+    # the three weight/activation variants exclude each other
+    (dict(flags=binding.MT_FLAG_W4A8 | binding.MT_FLAG_DENSE_F16), binding.MT_ERR_UNSUPPORTED),
+    (dict(flags=binding.MT_FLAG_DENSE_F16 | binding.MT_FLAG_DENSE_F32), binding.MT_ERR_UNSUPPORTED),
+    (dict(flags=binding.MT_FLAG_W4A8 | binding.MT_FLAG_DENSE_F32), binding.MT_ERR_UNSUPPORTED),
+    # valid modes: the config passes and the NULL weights are refused
     (dict(flags=binding.MT_FLAG_W4A8), binding.MT_ERR_INVALID_ARG),
+    (dict(flags=binding.MT_FLAG_DENSE_F16), binding.MT_ERR_INVALID_ARG),
+    (dict(flags=binding.MT_FLAG_DENSE_F32), binding.MT_ERR_INVALID_ARG),
 ])
 def test_create_rejects_bad_config_before_device_work(kw, code):
     lib = binding.lib()

@@ -1,0 +1,135 @@
+"""GPU parity of the dense-weight variants (MT_FLAG_DENSE_F16 / _F32)
+against the CPU oracle's dense modes, through the C ABI.
+
+The kernels widen each binary16 or binary32 weight exactly to FP32, so the
+dequantisation check is bit-exact and the projections are held to the same
+rigorous FP32 bound as the INT4 ones (K 2^-24 sum |x| |w|).  Whole-model runs
+use the INT4 tolerances: only the weight values differ."""
+import numpy as np
+import pytest
+
+from audio_midi_transformer_amd import binding, synth
+from parity import TOL, check_argmax, compare_logits, top2
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+FLAG = {"f16": binding.MT_FLAG_DENSE_F16, "f32": binding.MT_FLAG_DENSE_F32}
+
+
+def _dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda", 0)
+
+
+def _t(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(_dev())
+
+
+def _widened(oracle_mod, W, fmt):
+    return oracle_mod.round_half(W) if fmt == "f16" else np.asarray(W, np.float32)
+
+
+@pytest.fixture(scope="module", params=[(w, f) for w in ("small", "medium", "large") for f in ("f16", "f32")],
+                ids=lambda p: f"{p[0]}-{p[1]}")
+def one_layer(request, oracle_mod):
+    width, fmt = request.param
+    _dev()
+    base = {"small": synth.SMALL, "medium": synth.MEDIUM, "large": synth.LARGE}[width]
+    shape = synth.ModelShape(base.name, 1, base.d_model, base.n_heads, base.d_ff)
+    w = synth.model_weights(shape, 79)
+    dec = binding.Decoder(w, batch=1, t_cap=8, flags=FLAG[fmt])
+    yield shape, w, dec, fmt
+    dec.close()
+
+
+def test_dense_widening_bit_exact(one_layer, oracle_mod):
+    shape, w, dec, fmt = one_layer
+    for p, W in enumerate((w.w_qkv[0], w.w_o[0], w.w_up[0], w.w_down[0])):
+        want = _widened(oracle_mod, W, fmt)
+        got = dec.debug_dequant(0, p).cpu().numpy()
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), f"projection {p}"
+
+
+@pytest.mark.parametrize("M,force_gemm", [(1, False), (3, False), (8, False), (1, True), (13, True),
+                                          (64, True), (130, True)])
+def test_dense_matmul_vs_oracle(one_layer, oracle_mod, M, force_gemm):
+    shape, w, dec, fmt = one_layer
+    rng = np.random.default_rng(200 + M)
+    for p, W in enumerate((w.w_qkv[0], w.w_o[0], w.w_up[0], w.w_down[0])):
+        Wd = _widened(oracle_mod, W, fmt)
+        x = rng.standard_normal((M, W.shape[1])).astype(np.float32)
+        want = oracle_mod.matmul(x, Wd)
+        got = dec.debug_matmul(0, p, _t(x), force_gemm=force_gemm).cpu().numpy()
+        err = np.abs(got.astype(np.float64) - want.astype(np.float64))
+        K = W.shape[1]
+        bound = K * 2.0 ** -24 * (np.abs(x.astype(np.float64)) @ np.abs(Wd.astype(np.float64)).T)
+        assert np.all(err <= bound + 2.0 ** -24 * np.abs(want) + 1e-30), f"projection {p}: max err {err.max():.3g}"
+
+
+def test_dense_one_hot_column_exact(one_layer, oracle_mod):
+    """e_k through the GEMV and the GEMM returns column k of the widened matrix exactly."""
+    shape, w, dec, fmt = one_layer
+    W = w.w_up[0]
+    Wd = _widened(oracle_mod, W, fmt)
+    for k in (0, 1, 7, 8, 31, 32, W.shape[1] - 1):
+        x = np.zeros((1, W.shape[1]), np.float32)
+        x[0, k] = 1.0
+        for force in (False, True):
+            got = dec.debug_matmul(0, 2, _t(x), force_gemm=force).cpu().numpy()[0]
+            assert np.array_equal(got, Wd[:, k]), (k, force)
+
+
+def test_dense_refuses_persistent_path(one_layer):
+    shape, w, dec, fmt = one_layer
+    with pytest.raises(binding.MTError) as e:
+        dec.set_decode_path(binding.MT_DECODE_PERSISTENT)
+    assert e.value.code == binding.MT_ERR_UNSUPPORTED
+
+
+def _run_pair(oracle_mod, w, fmt, B, t_cap, prefix, tokens, steps, tol):
+    om = oracle_mod.OracleModel.from_weights(w, batch=B, t_cap=t_cap, dense=fmt)
+    dec = binding.Decoder(w, batch=B, t_cap=t_cap, flags=FLAG[fmt])
+    lo, no = om.forward(tokens=tokens, prefix=prefix)
+    lg, ng = dec.prefill(_t(tokens) if tokens is not None else None, _t(prefix) if prefix is not None else None)
+    worst = compare_logits(lg.cpu().numpy(), lo, tol, "prefill")
+    check_argmax(ng.cpu().numpy(), *top2(lo), None, tol)
+    for k in range(steps):
+        tok = no.reshape(B, 1)
+        lo, no = om.forward(tokens=tok)
+        lg, ng = dec.decode_step(_t(tok.reshape(B)))
+        worst = max(worst, compare_logits(lg.cpu().numpy(), lo, tol, f"step {k}"))
+        check_argmax(ng.cpu().numpy(), *top2(lo), None, tol)
+    dec.check()
+    K, V = dec.kv_cache()
+    Ko, Vo = om.kv()
+    T = om.position
+    assert dec.position == T
+    np.testing.assert_allclose(K[:, :, :T].cpu().numpy(), Ko[:, :, :T], rtol=0, atol=2e-5)
+    np.testing.assert_allclose(V[:, :, :T].cpu().numpy(), Vo[:, :, :T], rtol=0, atol=2e-5)
+    om.close()
+    dec.close()
+    print(f"dense {fmt}: {steps + 1} calls, max |delta logits| {worst:.3g}")
+
+
+@pytest.mark.parametrize("fmt", ["f16", "f32"])
+def test_dense_model_prefix_tokens_decode(oracle_mod, fmt):
+    _dev()
+    shape = synth.tiny_shape(n_layers=2, d_model=128, n_heads=2, d_ff=512, vocab=97)
+    w = synth.model_weights(shape, 9)
+    rng = np.random.default_rng(6)
+    B, P, S = 2, 70, 5
+    prefix = rng.standard_normal((B, P, shape.d_model)).astype(np.float32)
+    tokens = rng.integers(0, shape.vocab, size=(B, S))
+    _run_pair(oracle_mod, w, fmt, B, 100, prefix, tokens, 16, TOL["tiny"])
+
+
+@pytest.mark.parametrize("fmt", ["f16", "f32"])
+def test_dense_model_batch8_medium_width(oracle_mod, fmt):
+    _dev()
+    shape = synth.tiny_shape(n_layers=1, d_model=1024, n_heads=16, d_ff=4096, vocab=1393)
+    w = synth.model_weights(shape, 10)
+    prefix = np.random.default_rng(7).standard_normal((8, 33, 1024)).astype(np.float32)
+    _run_pair(oracle_mod, w, fmt, 8, 48, prefix, None, 6, TOL["medium"])

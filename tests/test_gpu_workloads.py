@@ -28,6 +28,17 @@ KV_TOL = {"small": 5e-5, "medium": 5e-5, "large": 2e-4}
 # to 0.045 under a one-ulp change of its inputs; bounds: max |delta| 0.15,
 # greedy rule with tolerance 0.05, K/V rows within 5 % relative L2.
 A8_TOL, A8_TIE, A8_KV_RL2 = 0.15, 0.05, 0.05
+# Dense keys ('<workload>f16', '<workload>f32'): the same FP32 arithmetic as
+# INT4 with other weight values, held to the INT4 tolerances.
+MODE_FLAGS = {None: 0, "a8": binding.MT_FLAG_W4A8, "f16": binding.MT_FLAG_DENSE_F16,
+              "f32": binding.MT_FLAG_DENSE_F32}
+
+
+def _mode(key):
+    for suffix in ("a8", "f16", "f32"):
+        if key.endswith(suffix):
+            return key[:-len(suffix)], suffix
+    return key, None
 
 _weights_cache = {}
 
@@ -47,7 +58,8 @@ def _fingerprint(w):
 
 
 CASES = [("0", None), ("1", None), ("2", None), ("2", binding.MT_DECODE_KERNELS), ("3", None),
-         ("3c576", None), ("4", None), ("4b8", None), ("0a8", None), ("2a8", None), ("3a8", None)]
+         ("3c576", None), ("4", None), ("4b8", None), ("0a8", None), ("2a8", None), ("3a8", None),
+         ("0f32", None), ("0f16", None), ("2f16", None), ("4f16", None)]
 
 
 @pytest.mark.parametrize("key,path", CASES, ids=[f"{k}-{'kernels' if p else 'auto'}" for k, p in CASES])
@@ -58,8 +70,9 @@ def test_workload_teacher_forced(key, path):
     if not os.path.exists(gpath):
         pytest.skip(f"golden {gpath} not generated")
     g = np.load(gpath)
-    a8 = key.endswith("a8")
-    wl = synth.WORKLOADS[key[:-2] if a8 else key]
+    base, mode = _mode(key)
+    a8 = mode == "a8"
+    wl = synth.WORKLOADS[base]
     tol, kvtol = TOL[wl.shape.name], KV_TOL[wl.shape.name]
     tie = tol
     if a8:
@@ -68,7 +81,8 @@ def test_workload_teacher_forced(key, path):
     w, packed = _weights(wl)
     np.testing.assert_allclose(_fingerprint(w), g["weights_check"], rtol=0, atol=0)
     B, V = wl.batch, wl.shape.vocab
-    dec = binding.Decoder(w, batch=B, t_cap=wl.t_cap, packed=packed, flags=binding.MT_FLAG_W4A8 if a8 else 0)
+    dec = binding.Decoder(w, batch=B, t_cap=wl.t_cap, packed=packed if mode in (None, "a8") else None,
+                          flags=MODE_FLAGS[mode])
     if path is not None:
         dec.set_decode_path(path)
     fed = g["tokens"].astype(np.int64)
