@@ -159,14 +159,6 @@ constexpr int PART_ACC = 4;
 
 // ---------------------------------------------------------------- INT4 GEMV (M <= 8) on MFMA
 
-// Position of element k of an activation row in LDS: the eight 16-byte
-// sub-blocks of each 32-element group are rotated by the group index, so the
-// lanes of a row group (consecutive groups) read different banks.
-__device__ __forceinline__ int xswz(int k) {
-    const int c = k >> 5, j = (k >> 2) & 7;
-    return (c << 5) + (((j + c) & 7) << 2) + (k & 3);
-}
-
 constexpr int GV_MAXSPAN = 2048;  // activation columns staged in LDS at a time
 constexpr int GV_M = 8;           // activation rows held in LDS
 
@@ -176,12 +168,22 @@ constexpr int GV_M = 8;           // activation rows held in LDS
 // decode-attention partials of H heads and ns splits; optionally replaced
 // by LayerNorm(x) (gain ln_g, bias ln_b, biased variance; whole rows).
 // Workgroup (n block, k split): 16 output rows over columns
-// [ks * kspan, (ks + 1) * kspan), staged through LDS transposed ([k][8])
-// in chunks of <= GV_MAXSPAN columns; the four waves take interleaved
-// quarters of each chunk's groups and their 16 x 16 tiles are summed in
+// [ks * kspan, (ks + 1) * kspan), staged through LDS in chunks of <=
+// GV_MAXSPAN columns; the four waves take interleaved quarters of each
+// chunk's groups (at most NG each) and their 16 x 16 tiles are summed in
 // LDS.  With more than one k split the results are added to Y atomically
-// (the += epilogue only).  Lane l converts weight W'[n0 + l % 16][k + l / 16]
-// as s * u - 8 s (one rounding, equal to (u - 8) * s).
+// (the += epilogue only).
+//
+// Lane l = 16 kq + r works on weight row n0 + r and, in every group of 32
+// columns, on the 8 contiguous columns 8 kq .. 8 kq + 7: INT4 weights are one
+// dword of nibbles per lane and group (converted as s * u - 8 s, one
+// rounding, equal to (u - 8) * s), dense weights one or two 16-byte loads,
+// and the matching activations two 16-byte LDS reads, fetched one group
+// ahead.  Loads are issued activations first, then every weight group
+// (addresses clamped, never predicated), so that staging waits only for the
+// activations while the weights are still in flight, and each group's MFMAs
+// wait only for that group.  Rows past N load row N - 1; their results are
+// dropped.
 //
 // A8 (W4A8 variant): after staging, each (row, group of 32) of the staged
 // activations is coded to INT8 (s_a = max|x| / 127, code = clamp(rint(x *
@@ -189,15 +191,7 @@ constexpr int GV_M = 8;           // activation rows held in LDS
 // with A = activation codes (16 rows, 8 used) and B = 16 (u - 8) of 16
 // weight rows; the INT32 tile is exact and is added to the FP32 result as
 // I * s_a * s_w / 16.
-//
-// WF = WF_F16 / WF_F32 (dense weights): lane l reads the 8 contiguous
-// values W[n0 + l % 16][g * 32 + 8 (l / 16) + s], s < 8, of each of its
-// groups in one or two vector loads, and feeds the activations of the same
-// columns (no scales); everything around the MFMA is the same.  The raw
-// bits stay in registers until the MFMA loop widens them, so that every
-// group's load is in flight at once (a use next to the load would make each
-// wait for the previous one).
-template <int WF, bool A8>
+template <int WF, bool A8, int NG>
 __global__ __launch_bounds__(256) void k_gemv_w4(const float* __restrict__ X, int ldx, int M, int K, int kspan,
                                                  const float* __restrict__ ln_g, const float* __restrict__ ln_b,
                                                  float eps, const float* __restrict__ part, int H, int ns,
@@ -209,52 +203,55 @@ __global__ __launch_bounds__(256) void k_gemv_w4(const float* __restrict__ X, in
     const int n0 = blockIdx.x * 16;
     const int G = K / 32;
     const int kb0 = blockIdx.y * kspan;
-    const int row = n0 + (lane & 15), kq = lane >> 4;
-    const bool rvalid = row < N;
+    const int row = min(n0 + (lane & 15), N - 1), kq = lane >> 4;
     const int bm = lane & 15;  // activation row this lane feeds into B
     const int xm = tid >> 5, xr = tid & 31;  // staging: row, thread in row (32 per row)
     const bool xrow = xm < M;
+    const int xmc = min(xm, M - 1);  // rows past M load row M - 1 and store zeros
     f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
     for (int c0 = 0; c0 < kspan; c0 += GV_MAXSPAN) {
         const int cw = min(GV_MAXSPAN, kspan - c0);  // columns in this chunk
-        const int XS = cw + 4;                       // LDS row stride: B reads hit 32 banks
+        const int XS = cw + 4;                       // LDS row stride
         const int kbase = kb0 + c0;
         const int gch = cw / 32, gbase = kbase / 32;
-        // this wave's groups of the chunk (g = wave, wave + 4, ...; ngw of
-        // them, uniform over the wave): all requested before the activations
-        // are staged
+        // this wave's groups of the chunk: g = wave, wave + 4, ...; ngw <= NG
+        // of them, uniform over the wave
         const int wv = __builtin_amdgcn_readfirstlane(wave);
         const int ngw = (gch - wv + 3) / 4;
-        // INT4: nibbles (wq) and scale (sc) of each group; F16: the 8
-        // halves (wq); F32: the 8 floats' bits (wq, then wq2)
-        uint4 wq[GV_MAXSPAN / 128];
-        uint4 wq2[WF == WF_F32 ? GV_MAXSPAN / 128 : 1];
-        float sc[GV_MAXSPAN / 128];
-        const unsigned fill = WF == WF_INT4 ? 0x88888888u : 0u;
+        const int nf4 = (cw / 4 + 31) / 32;  // float4 per staging thread, <= NG
+        // ---- activations first (plain rows only)
+        float4 v[NG];
+        if (!part) {
 #pragma unroll
-        for (int i = 0; i < GV_MAXSPAN / 128; ++i) {
-            wq[i] = make_uint4(fill, fill, fill, fill);
-            if constexpr (WF == WF_F32) wq2[i] = make_uint4(0u, 0u, 0u, 0u);
-            sc[i] = 0.f;
-            if (i < ngw && rvalid) {
-                const int g = gbase + wv + 4 * i;
-                if constexpr (WF == WF_INT4) {
-                    wq[i] = *reinterpret_cast<const uint4*>(Wq + (size_t)row * (K / 2) + (size_t)g * 16);
-                    sc[i] = Ws[(size_t)row * G + g];
+            for (int i = 0; i < NG; ++i) {
+                const int k = min((xr + i * 32) * 4, cw - 4);
+                v[i] = *reinterpret_cast<const float4*>(X + (size_t)xmc * ldx + kbase + k);
+            }
+        }
+        // ---- then every weight group of this wave (INT4: nibble dword kq
+        // and the group scale; F16: 8 halves; F32: 8 floats' bits)
+        unsigned w4[WF == WF_INT4 ? NG : 1];
+        float sc[WF == WF_INT4 ? NG : 1];
+        uint4 wq[WF == WF_INT4 ? 1 : NG];
+        uint4 wq2[WF == WF_F32 ? NG : 1];
+#pragma unroll
+        for (int i = 0; i < NG; ++i) {
+            const int g = gbase + min(wv + 4 * i, gch - 1);
+            if constexpr (WF == WF_INT4) {
+                w4[i] = *reinterpret_cast<const unsigned*>(Wq + (size_t)row * (K / 2) + (size_t)g * 16 + 4 * kq);
+                sc[i] = Ws[(size_t)row * G + g];
+            } else {
+                const size_t e = (size_t)row * K + (size_t)g * 32 + 8 * kq;
+                if constexpr (WF == WF_F16) {
+                    wq[i] = *reinterpret_cast<const uint4*>(Wq + 2 * e);
                 } else {
-                    const size_t e = (size_t)row * K + (size_t)g * 32 + 8 * kq;
-                    if constexpr (WF == WF_F16) {
-                        wq[i] = *reinterpret_cast<const uint4*>(Wq + 2 * e);
-                    } else {
-                        wq[i] = *reinterpret_cast<const uint4*>(Wq + 4 * e);
-                        wq2[i] = *reinterpret_cast<const uint4*>(Wq + 4 * e + 16);
-                    }
+                    wq[i] = *reinterpret_cast<const uint4*>(Wq + 4 * e);
+                    wq2[i] = *reinterpret_cast<const uint4*>(Wq + 4 * e + 16);
                 }
             }
         }
         if (c0) __syncthreads();
         // ---- stage x[m][kbase .. kbase + cw) into xt[m][k]
-        const int nf4 = (cw / 4 + 31) / 32;
         if (part) {
             // attention output merged from the partials: first the weight
             // e^(m_s - M) / sum_s e^(m_s - M) l_s of every (row, head, split),
@@ -304,22 +301,19 @@ __global__ __launch_bounds__(256) void k_gemv_w4(const float* __restrict__ X, in
                 }
             }
         } else {
-            float4 v[16];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
+            for (int i = 0; i < NG; ++i) {
                 const int k = (xr + i * 32) * 4;
-                v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (i < nf4 && k < cw && xrow)
-                    v[i] = *reinterpret_cast<const float4*>(X + (size_t)xm * ldx + kbase + k);
+                if (!(i < nf4 && k < cw && xrow)) v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
             }
             if (ln_g) {  // one chunk holds the whole row
                 float sm = 0.f;
 #pragma unroll
-                for (int i = 0; i < 16; ++i) sm += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+                for (int i = 0; i < NG; ++i) sm += (v[i].x + v[i].y) + (v[i].z + v[i].w);
                 const float mean = group_sum<32>(sm) / (float)K;
                 float q = 0.f;
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
+                for (int i = 0; i < NG; ++i) {
                     const int k = (xr + i * 32) * 4;
                     if (i < nf4 && k < cw) {
                         const float a0 = v[i].x - mean, a1 = v[i].y - mean, a2 = v[i].z - mean, a3 = v[i].w - mean;
@@ -329,7 +323,7 @@ __global__ __launch_bounds__(256) void k_gemv_w4(const float* __restrict__ X, in
                 const float var = group_sum<32>(q) / (float)K;
                 const float rstd = 1.0f / sqrtf(var + eps);
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
+                for (int i = 0; i < NG; ++i) {
                     const int k = (xr + i * 32) * 4;
                     if (i < nf4 && k < cw && xrow) {
                         const float4 gg = *reinterpret_cast<const float4*>(ln_g + k);
@@ -342,7 +336,7 @@ __global__ __launch_bounds__(256) void k_gemv_w4(const float* __restrict__ X, in
                 }
             }
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
+            for (int i = 0; i < NG; ++i) {
                 const int k = (xr + i * 32) * 4;
                 if (i < nf4 && k < cw) *reinterpret_cast<float4*>(xt + xm * XS + k) = v[i];
             }
@@ -396,11 +390,10 @@ __global__ __launch_bounds__(256) void k_gemv_w4(const float* __restrict__ X, in
             const bool avalid = bm < GV_M;
             const int8_t* xa = xq + (size_t)(bm & (GV_M - 1)) * cw + 8 * kq;
 #pragma unroll
-            for (int i = 0; i < GV_MAXSPAN / 128; ++i) {
+            for (int i = 0; i < NG; ++i) {
                 if (i < ngw) {
                     const int gi = wv + 4 * i;
-                    const unsigned wd = kq == 0 ? wq[i].x : kq == 1 ? wq[i].y : kq == 2 ? wq[i].z : wq[i].w;
-                    const unsigned x8 = wd ^ 0x88888888u;
+                    const unsigned x8 = w4[i] ^ 0x88888888u;
                     const unsigned lo = (x8 << 4) & 0xF0F0F0F0u, hi = x8 & 0xF0F0F0F0u;
                     const unsigned b0 = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
                     const unsigned b1 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
@@ -419,36 +412,38 @@ __global__ __launch_bounds__(256) void k_gemv_w4(const float* __restrict__ X, in
             continue;
         }
         // ---- MFMA over this wave's groups, alternate groups into two
-        // accumulators.  Column 4 s + kq of a group: byte 2 s + kq / 2, low
-        // nibble for even kq.  Lanes feeding B columns 8..15 read row
-        // bm - 8 and pass zero.
-        const int sh = (kq >> 1) * 8 + (kq & 1) * 4;
-        const bool bvalid = bm < GV_M;
-        const float* xb = xt + (bm & (GV_M - 1)) * XS + (WF == WF_INT4 ? kq : 8 * kq);
+        // accumulators.  Step s of a group takes column 8 kq + s; the lanes
+        // feeding B columns 8..15 read row bm - 8, whose products land in
+        // D columns that are never read.
+        const float* xb = xt + (bm & (GV_M - 1)) * XS + 8 * kq;
+        float4 nb0 = make_float4(0.f, 0.f, 0.f, 0.f), nb1 = nb0;
+        if (ngw > 0) {
+            nb0 = *reinterpret_cast<const float4*>(xb + wv * 32);
+            nb1 = *reinterpret_cast<const float4*>(xb + wv * 32 + 4);
+        }
 #pragma unroll
-        for (int i = 0; i < GV_MAXSPAN / 128; ++i) {
+        for (int i = 0; i < NG; ++i) {
             if (i < ngw) {
-                const int gi = wv + 4 * i;
-                const float s8 = -8.f * sc[i];
-                const unsigned wd[4] = {wq[i].x, wq[i].y, wq[i].z, wq[i].w};
-                float bv[8];
-#pragma unroll
-                for (int s = 0; s < 8; ++s) bv[s] = xb[gi * 32 + (WF == WF_INT4 ? 4 * s : s)];
+                const float bv[8] = {nb0.x, nb0.y, nb0.z, nb0.w, nb1.x, nb1.y, nb1.z, nb1.w};
+                if (i + 1 < ngw) {
+                    nb0 = *reinterpret_cast<const float4*>(xb + (wv + 4 * i + 4) * 32);
+                    nb1 = *reinterpret_cast<const float4*>(xb + (wv + 4 * i + 4) * 32 + 4);
+                }
 #pragma unroll
                 for (int s = 0; s < 8; ++s) {
                     float a;
                     if constexpr (WF == WF_INT4) {
-                        const float u = (float)((wd[s >> 1] >> (sh + 16 * (s & 1))) & 15u);
-                        a = fmaf(sc[i], u, s8);
+                        a = fmaf(sc[i], (float)((w4[i] >> (4 * s)) & 15u), -8.f * sc[i]);
                     } else if constexpr (WF == WF_F16) {
-                        a = __half2float(__ushort_as_half((unsigned short)(wd[s >> 1] >> (16 * (s & 1)))));
+                        const unsigned hw[4] = {wq[i].x, wq[i].y, wq[i].z, wq[i].w};
+                        a = __half2float(__ushort_as_half((unsigned short)(hw[s >> 1] >> (16 * (s & 1)))));
                     } else {
-                        const unsigned w2[4] = {wq2[i].x, wq2[i].y, wq2[i].z, wq2[i].w};
-                        a = __uint_as_float(s < 4 ? wd[s] : w2[s - 4]);
+                        const unsigned fw[8] = {wq[i].x, wq[i].y, wq[i].z, wq[i].w,
+                                                wq2[i].x, wq2[i].y, wq2[i].z, wq2[i].w};
+                        a = __uint_as_float(fw[s]);
                     }
-                    const float b = bvalid ? bv[s] : 0.f;
-                    if (i & 1) acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc1, 0, 0, 0);
-                    else acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc0, 0, 0, 0);
+                    if (i & 1) acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bv[s], acc1, 0, 0, 0);
+                    else acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bv[s], acc0, 0, 0, 0);
                 }
             }
         }
@@ -1239,6 +1234,46 @@ hipError_t launch_layernorm(const float* x, long ldx, const float* g, const floa
 
 constexpr size_t kGemvMaxLds = 152 * 1024;  // dynamic LDS of the GEMV (static: 4.3 KB)
 
+struct GemvArgs {
+    const float* x;
+    int ldx, M, K, kspan;
+    const float *ln_g, *ln_b;
+    float eps;
+    const float* part;
+    int H, ns;
+    const uint8_t* q;
+    const float* s;
+    int N;
+    float* y;
+    int ldy;
+    EpiArgs ep;
+};
+
+template <int WF, bool A8>
+static hipError_t gemv_set_lds() {
+    const void* fns[4] = {(const void*)k_gemv_w4<WF, A8, 4>, (const void*)k_gemv_w4<WF, A8, 8>,
+                          (const void*)k_gemv_w4<WF, A8, 12>, (const void*)k_gemv_w4<WF, A8, 16>};
+    for (const void* f : fns) {
+        const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGemvMaxLds);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+template <int WF, bool A8>
+static void gemv_launch(int ng, dim3 grid, size_t lds, hipStream_t st, const GemvArgs& a) {
+#define MT_GEMV(NGV)                                                                                            \
+    hipLaunchKernelGGL((k_gemv_w4<WF, A8, NGV>), grid, dim3(256), lds, st, a.x, a.ldx, a.M, a.K, a.kspan, a.ln_g, \
+                       a.ln_b, a.eps, a.part, a.H, a.ns, a.q, a.s, a.N, a.y, a.ldy, a.ep)
+    switch (ng) {
+        case 4: MT_GEMV(4); break;
+        case 8: MT_GEMV(8); break;
+        case 12: MT_GEMV(12); break;
+        default: MT_GEMV(16); break;
+    }
+#undef MT_GEMV
+}
+
 // GEMV plan: k split (grid.y) and columns per split.  The += epilogue
 // splits K so that about 256 workgroups run; the other epilogues keep one
 // split per output block.
@@ -1280,25 +1315,23 @@ hipError_t launch_w4_matmul(const float* x, int ldx, int M, const Int4Mat& w, co
         if (a8) lds = sizeof(float) * ((size_t)(span + 4) * GV_M + ((wts + 3) & ~(size_t)3)) + (size_t)GV_M * span +
                       sizeof(float) * (size_t)(span / 32) * GV_M;
         if (lds > kGemvMaxLds) return hipErrorInvalidValue;
+        // groups per wave and chunk, rounded up to a multiple of 4
+        const int ng = std::min(16, ((span / 32 + 3) / 4 + 3) / 4 * 4);
         static bool attr = false;
         if (!attr) {
-            const void* fns[4] = {(const void*)k_gemv_w4<WF_INT4, false>, (const void*)k_gemv_w4<WF_INT4, true>,
-                                  (const void*)k_gemv_w4<WF_F16, false>, (const void*)k_gemv_w4<WF_F32, false>};
-            for (const void* f : fns) {
-                const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGemvMaxLds);
-                if (e != hipSuccess) return e;
-            }
+            hipError_t e = gemv_set_lds<WF_INT4, false>();
+            if (e == hipSuccess) e = gemv_set_lds<WF_INT4, true>();
+            if (e == hipSuccess) e = gemv_set_lds<WF_F16, false>();
+            if (e == hipSuccess) e = gemv_set_lds<WF_F32, false>();
+            if (e != hipSuccess) return e;
             attr = true;
         }
         const dim3 grid((w.N + 15) / 16, ksplit);
-#define MT_GEMV(WFV, A8V)                                                                                        \
-    hipLaunchKernelGGL((k_gemv_w4<WFV, A8V>), grid, dim3(256), lds, st, x, ldx, M, w.K, kspan, ln_g, ln_b, eps, \
-                       ap.part, ap.H, ap.nsplit, w.q, w.s, w.N, y, ldy, ep)
-        if (w.fmt == WF_F16) MT_GEMV(WF_F16, false);
-        else if (w.fmt == WF_F32) MT_GEMV(WF_F32, false);
-        else if (a8) MT_GEMV(WF_INT4, true);
-        else MT_GEMV(WF_INT4, false);
-#undef MT_GEMV
+        const GemvArgs ga{x, ldx, M, w.K, kspan, ln_g, ln_b, eps, ap.part, ap.H, ap.nsplit, w.q, w.s, w.N, y, ldy, ep};
+        if (w.fmt == WF_F16) gemv_launch<WF_F16, false>(ng, grid, lds, st, ga);
+        else if (w.fmt == WF_F32) gemv_launch<WF_F32, false>(ng, grid, lds, st, ga);
+        else if (a8) gemv_launch<WF_INT4, true>(ng, grid, lds, st, ga);
+        else gemv_launch<WF_INT4, false>(ng, grid, lds, st, ga);
         return hipGetLastError();
     }
     if (ln_g || ap.part) return hipErrorInvalidValue;  // the GEMM path takes plain rows
