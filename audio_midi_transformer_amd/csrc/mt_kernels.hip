@@ -191,7 +191,19 @@ constexpr int GV_M = 8;           // activation rows held in LDS
 // with A = activation codes (16 rows, 8 used) and B = 16 (u - 8) of 16
 // weight rows; the INT32 tile is exact and is added to the FP32 result as
 // I * s_a * s_w / 16.
-template <int WF, bool A8, int NG>
+// Source of the activation rows (a template parameter, so that every load
+// of a variant is straight-line code and each wait counts exactly the loads
+// it needs).
+enum GemvSrc : int { GS_ROWS = 0, GS_LN = 1, GS_PARTS = 2 };
+
+// Sum over each group of 32 lanes in every lane: DPP within rows of 16, one
+// swap between the two rows.
+__device__ __forceinline__ float sum32(float v) {
+    v = row_sum16(v);
+    return v + __shfl_xor(v, 16);
+}
+
+template <int WF, bool A8, int NG, int SRC>
 __global__ __launch_bounds__(256) void k_gemv_w4(const float* __restrict__ X, int ldx, int M, int K, int kspan,
                                                  const float* __restrict__ ln_g, const float* __restrict__ ln_b,
                                                  float eps, const float* __restrict__ part, int H, int ns,
@@ -219,13 +231,24 @@ __global__ __launch_bounds__(256) void k_gemv_w4(const float* __restrict__ X, in
         const int wv = __builtin_amdgcn_readfirstlane(wave);
         const int ngw = (gch - wv + 3) / 4;
         const int nf4 = (cw / 4 + 31) / 32;  // float4 per staging thread, <= NG
-        // ---- activations first (plain rows only)
+        // ---- activations first (plain rows only), with the LayerNorm gain
+        // and bias of the chunk when it is fused: float4 f < cw / 4 of the
+        // gain, then of the bias, spread over the workgroup
         float4 v[NG];
-        if (!part) {
+        float4 gb[NG / 4];
+        if constexpr (SRC != GS_PARTS) {
 #pragma unroll
             for (int i = 0; i < NG; ++i) {
                 const int k = min((xr + i * 32) * 4, cw - 4);
                 v[i] = *reinterpret_cast<const float4*>(X + (size_t)xmc * ldx + kbase + k);
+            }
+            if constexpr (SRC == GS_LN) {
+#pragma unroll
+                for (int j = 0; j < NG / 4; ++j) {
+                    const int f = min(tid + 256 * j, cw / 2 - 1);
+                    gb[j] = *reinterpret_cast<const float4*>(f < cw / 4 ? ln_g + kbase + 4 * f
+                                                                         : ln_b + kbase + 4 * (f - cw / 4));
+                }
             }
         }
         // ---- then every weight group of this wave (INT4: nibble dword kq
@@ -252,7 +275,7 @@ __global__ __launch_bounds__(256) void k_gemv_w4(const float* __restrict__ X, in
         }
         if (c0) __syncthreads();
         // ---- stage x[m][kbase .. kbase + cw) into xt[m][k]
-        if (part) {
+        if constexpr (SRC == GS_PARTS) {
             // attention output merged from the partials: first the weight
             // e^(m_s - M) / sum_s e^(m_s - M) l_s of every (row, head, split),
             // one (row, head) per thread, then the weighted sums of acc_s
@@ -306,11 +329,18 @@ __global__ __launch_bounds__(256) void k_gemv_w4(const float* __restrict__ X, in
                 const int k = (xr + i * 32) * 4;
                 if (!(i < nf4 && k < cw && xrow)) v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
             }
-            if (ln_g) {  // one chunk holds the whole row
+            if constexpr (SRC == GS_LN) {  // one chunk holds the whole row
+                // gain [cw] and bias [cw] go to LDS past the activation rows
+                float* lnb = xt + (size_t)XS * GV_M;
+#pragma unroll
+                for (int j = 0; j < NG / 4; ++j) {
+                    const int f = tid + 256 * j;
+                    if (f < cw / 2) *reinterpret_cast<float4*>(lnb + 4 * f) = gb[j];
+                }
                 float sm = 0.f;
 #pragma unroll
                 for (int i = 0; i < NG; ++i) sm += (v[i].x + v[i].y) + (v[i].z + v[i].w);
-                const float mean = group_sum<32>(sm) / (float)K;
+                const float mean = sum32(sm) / (float)K;
                 float q = 0.f;
 #pragma unroll
                 for (int i = 0; i < NG; ++i) {
@@ -320,14 +350,15 @@ __global__ __launch_bounds__(256) void k_gemv_w4(const float* __restrict__ X, in
                         q = fmaf(a0, a0, fmaf(a1, a1, fmaf(a2, a2, fmaf(a3, a3, q))));
                     }
                 }
-                const float var = group_sum<32>(q) / (float)K;
+                const float var = sum32(q) / (float)K;
                 const float rstd = 1.0f / sqrtf(var + eps);
+                __syncthreads();  // gain and bias in LDS
 #pragma unroll
                 for (int i = 0; i < NG; ++i) {
                     const int k = (xr + i * 32) * 4;
                     if (i < nf4 && k < cw && xrow) {
-                        const float4 gg = *reinterpret_cast<const float4*>(ln_g + k);
-                        const float4 bb = *reinterpret_cast<const float4*>(ln_b + k);
+                        const float4 gg = *reinterpret_cast<const float4*>(lnb + k);
+                        const float4 bb = *reinterpret_cast<const float4*>(lnb + cw + k);
                         v[i].x = (v[i].x - mean) * rstd * gg.x + bb.x;
                         v[i].y = (v[i].y - mean) * rstd * gg.y + bb.y;
                         v[i].z = (v[i].z - mean) * rstd * gg.z + bb.z;
@@ -345,7 +376,7 @@ __global__ __launch_bounds__(256) void k_gemv_w4(const float* __restrict__ X, in
         if constexpr (A8 && WF == WF_INT4) {
             // ---- INT8 codes of the staged rows, one (row, group) per thread
             // and pass: codes [GV_M][cw] bytes, scales [gch][GV_M]
-            const size_t wfl = part ? (size_t)M * (cw / 64) * ns : 0;
+            const size_t wfl = SRC == GS_PARTS ? (size_t)M * (cw / 64) * ns : 0;
             int8_t* xq = reinterpret_cast<int8_t*>(xt + (size_t)XS * GV_M + ((wfl + 3) & ~(size_t)3));
             float* xsa = reinterpret_cast<float*>(xq + (size_t)GV_M * cw);
             for (int p = tid; p < GV_M * gch; p += 256) {
@@ -1249,10 +1280,10 @@ struct GemvArgs {
     EpiArgs ep;
 };
 
-template <int WF, bool A8>
-static hipError_t gemv_set_lds() {
-    const void* fns[4] = {(const void*)k_gemv_w4<WF, A8, 4>, (const void*)k_gemv_w4<WF, A8, 8>,
-                          (const void*)k_gemv_w4<WF, A8, 12>, (const void*)k_gemv_w4<WF, A8, 16>};
+template <int WF, bool A8, int SRC>
+static hipError_t gemv_set_lds_src() {
+    const void* fns[4] = {(const void*)k_gemv_w4<WF, A8, 4, SRC>, (const void*)k_gemv_w4<WF, A8, 8, SRC>,
+                          (const void*)k_gemv_w4<WF, A8, 12, SRC>, (const void*)k_gemv_w4<WF, A8, 16, SRC>};
     for (const void* f : fns) {
         const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGemvMaxLds);
         if (e != hipSuccess) return e;
@@ -1261,9 +1292,17 @@ static hipError_t gemv_set_lds() {
 }
 
 template <int WF, bool A8>
-static void gemv_launch(int ng, dim3 grid, size_t lds, hipStream_t st, const GemvArgs& a) {
-#define MT_GEMV(NGV)                                                                                            \
-    hipLaunchKernelGGL((k_gemv_w4<WF, A8, NGV>), grid, dim3(256), lds, st, a.x, a.ldx, a.M, a.K, a.kspan, a.ln_g, \
+static hipError_t gemv_set_lds() {
+    hipError_t e = gemv_set_lds_src<WF, A8, GS_ROWS>();
+    if (e == hipSuccess) e = gemv_set_lds_src<WF, A8, GS_LN>();
+    if (e == hipSuccess) e = gemv_set_lds_src<WF, A8, GS_PARTS>();
+    return e;
+}
+
+template <int WF, bool A8, int SRC>
+static void gemv_launch_src(int ng, dim3 grid, size_t lds, hipStream_t st, const GemvArgs& a) {
+#define MT_GEMV(NGV)                                                                                                 \
+    hipLaunchKernelGGL((k_gemv_w4<WF, A8, NGV, SRC>), grid, dim3(256), lds, st, a.x, a.ldx, a.M, a.K, a.kspan, a.ln_g, \
                        a.ln_b, a.eps, a.part, a.H, a.ns, a.q, a.s, a.N, a.y, a.ldy, a.ep)
     switch (ng) {
         case 4: MT_GEMV(4); break;
@@ -1272,6 +1311,13 @@ static void gemv_launch(int ng, dim3 grid, size_t lds, hipStream_t st, const Gem
         default: MT_GEMV(16); break;
     }
 #undef MT_GEMV
+}
+
+template <int WF, bool A8>
+static void gemv_launch(int ng, dim3 grid, size_t lds, hipStream_t st, const GemvArgs& a) {
+    if (a.part) gemv_launch_src<WF, A8, GS_PARTS>(ng, grid, lds, st, a);
+    else if (a.ln_g) gemv_launch_src<WF, A8, GS_LN>(ng, grid, lds, st, a);
+    else gemv_launch_src<WF, A8, GS_ROWS>(ng, grid, lds, st, a);
 }
 
 // GEMV plan: k split (grid.y) and columns per split.  The += epilogue
@@ -1314,6 +1360,7 @@ hipError_t launch_w4_matmul(const float* x, int ldx, int M, const Int4Mat& w, co
         size_t lds = sizeof(float) * ((size_t)(span + 4) * GV_M + wts);
         if (a8) lds = sizeof(float) * ((size_t)(span + 4) * GV_M + ((wts + 3) & ~(size_t)3)) + (size_t)GV_M * span +
                       sizeof(float) * (size_t)(span / 32) * GV_M;
+        if (ln_g) lds = std::max(lds, sizeof(float) * ((size_t)(span + 4) * GV_M + 2 * (size_t)span));
         if (lds > kGemvMaxLds) return hipErrorInvalidValue;
         // groups per wave and chunk, rounded up to a multiple of 4
         const int ng = std::min(16, ((span / 32 + 3) / 4 + 3) / 4 * 4);
