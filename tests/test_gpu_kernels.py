@@ -140,6 +140,29 @@ def test_model_tokens_only_small_width(oracle_mod):
     _run_pair(oracle_mod, shape, w, 1, 40, None, tokens, steps=12)
 
 
+@pytest.mark.parametrize("ff", [544, 96])
+def test_ragged_group_counts(oracle_mod, ff):
+    """FFN widths whose group count is not a multiple of 4 (17 and 3 groups):
+    the GEMV waves take different numbers of groups (one takes none at 96)
+    and load clamped dummy groups; every projection and the whole model
+    still match the oracle."""
+    _dev()
+    shape, w = _tiny(oracle_mod, n_layers=2, d=128, heads=2, ff=ff, vocab=97, seed=21)
+    dec = binding.Decoder(w, batch=1, t_cap=8)
+    rng = np.random.default_rng(ff)
+    for M, force in ((1, False), (5, False), (8, False), (11, True)):
+        for p, W in enumerate((w.w_qkv[1], w.w_o[1], w.w_up[1], w.w_down[1])):
+            q, s = oracle_mod.quantize_int4(W)
+            x = rng.standard_normal((M, W.shape[1])).astype(np.float32)
+            want = oracle_mod.matmul(x, oracle_mod.dequantize_int4(q, s))
+            got = dec.debug_matmul(1, p, _t(x), force_gemm=force).cpu().numpy()
+            err = np.abs(got.astype(np.float64) - want.astype(np.float64))
+            assert np.all(err <= _matmul_bound(x, q, s) + 2.0 ** -24 * np.abs(want)), (M, p, float(err.max()))
+    dec.close()
+    prefix = rng.standard_normal((2, 9, shape.d_model)).astype(np.float32)
+    _run_pair(oracle_mod, shape, w, 2, 30, prefix, None, steps=6)
+
+
 def test_model_batch8_medium_width(oracle_mod):
     _dev()
     shape, w = _tiny(oracle_mod, n_layers=1, d=1024, heads=16, ff=4096, vocab=1393, seed=5)
