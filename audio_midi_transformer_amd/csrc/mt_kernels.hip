@@ -541,96 +541,131 @@ __global__ __launch_bounds__(256) void k_gemm_w4(const float* __restrict__ X, in
     // weight dwords per thread: GK / 4 columns as nibbles, halves or floats
     constexpr int NW = WF == WF_INT4 ? GK / 32 : WF == WF_F16 ? GK / 8 : GK / 4;
     constexpr int ESZ2 = WF == WF_INT4 ? 1 : WF == WF_F16 ? 4 : 8;  // bytes per 2 columns
-    float4 pa[NA];
-    unsigned pw[NW];
-    float ps = 0.f;
+    // The next stage is loaded into registers while the current one is
+    // multiplied.  Every load is issued (addresses clamped into the matrix,
+    // out-of-range values replaced afterwards), so each wait counts exactly
+    // one stage's loads.
+    struct Stage {
+        float4 a[NA];
+        unsigned w[NW];
+        float s;
+    };
+    Stage st;
     const int wrow = tid >> 2, wq = tid & 3;
-    auto load_stage = [&](int k0) {
+    const int klast = ke - 1;  // any column of the range, for clamping
+    auto load_stage = [&](int k0, Stage& S) {
 #pragma unroll
         for (int e = 0; e < NA; ++e) {
             const int idx = tid + e * 256;
             const int r = idx / (GK / 4), c = (idx % (GK / 4)) * 4;
-            pa[e] = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (m0 + r < M && k0 + c < ke) pa[e] = *reinterpret_cast<const float4*>(X + (size_t)(m0 + r) * ldx + k0 + c);
+            const bool ok = m0 + r < M && k0 + c < ke;
+            const int rr = min(m0 + r, M - 1), cc = min(k0 + c, (klast & ~3));
+            const float4 t = *reinterpret_cast<const float4*>(X + (size_t)rr * ldx + cc);
+            S.a[e] = ok ? t : make_float4(0.f, 0.f, 0.f, 0.f);
         }
-        const int c0 = k0 + wq * (GK / 4), g = c0 / 32;
+        const int c0 = k0 + wq * (GK / 4);
         const bool ok = n0 + wrow < N && c0 < ke;
-        const uint8_t* wrow_p = Wq + ((size_t)(n0 + wrow) * K + c0) / 2 * ESZ2;
+        const int cc0 = min(c0, (klast & ~(GK / 4 - 1)));
+        const int rw = min(n0 + wrow, N - 1);
+        const uint8_t* wrow_p = Wq + ((size_t)rw * K + cc0) / 2 * ESZ2;
         const unsigned fill = WF == WF_INT4 ? 0x88888888u : 0u;
         if constexpr (NW % 4 == 0) {
 #pragma unroll
             for (int i = 0; i < NW; i += 4) {
-                const uint4 t = ok ? *reinterpret_cast<const uint4*>(wrow_p + 4 * i) : make_uint4(fill, fill, fill, fill);
-                pw[i] = t.x, pw[i + 1] = t.y, pw[i + 2] = t.z, pw[i + 3] = t.w;
+                const uint4 t = *reinterpret_cast<const uint4*>(wrow_p + 4 * i);
+                S.w[i] = ok ? t.x : fill, S.w[i + 1] = ok ? t.y : fill;
+                S.w[i + 2] = ok ? t.z : fill, S.w[i + 3] = ok ? t.w : fill;
             }
         } else {
 #pragma unroll
             for (int i = 0; i < NW; i += 2) {
-                const uint2 t = ok ? *reinterpret_cast<const uint2*>(wrow_p + 4 * i) : make_uint2(fill, fill);
-                pw[i] = t.x, pw[i + 1] = t.y;
+                const uint2 t = *reinterpret_cast<const uint2*>(wrow_p + 4 * i);
+                S.w[i] = ok ? t.x : fill, S.w[i + 1] = ok ? t.y : fill;
             }
         }
-        if constexpr (WF == WF_INT4) ps = ok ? Ws[(size_t)(n0 + wrow) * G + g] : 0.f;
+        if constexpr (WF == WF_INT4) {
+            const float sv = Ws[(size_t)rw * G + cc0 / 32];
+            S.s = ok ? sv : 0.f;
+        }
     };
-    load_stage(kb);
-    for (int k0 = kb; k0 < ke; k0 += GK) {
+    // one stage: stage S into LDS, refill S with stage k0 + GK, multiply
+    auto run_stage = [&](int k0, Stage& S) {
         if (k0 != kb) __syncthreads();  // the previous stage has been multiplied
 #pragma unroll
         for (int e = 0; e < NA; ++e) {
             const int idx = tid + e * 256;
-            *reinterpret_cast<float4*>(As + (idx / (GK / 4)) * GS + (idx % (GK / 4)) * 4) = pa[e];
+            *reinterpret_cast<float4*>(As + (idx / (GK / 4)) * GS + (idx % (GK / 4)) * 4) = S.a[e];
         }
         {
             float* dst = Bs + wrow * GS + wq * (GK / 4);
             if constexpr (WF == WF_INT4) {
-                // dword i holds inputs 8 i .. 8 i + 7 of the quarter, low nibble first
+                // dword d holds inputs 8 d .. 8 d + 7 of the quarter, low
+                // nibble first.  The four threads of a row write their
+                // quarters GK / 4 floats apart, i.e. on the same banks at
+                // GK = 128; each thread therefore starts at dword rot and
+                // goes round, so one write instruction covers all 32 banks.
+                const int rot = GK == 128 ? wq : (wq >> 1);
 #pragma unroll
-                for (int i = 0; i < NW; ++i)
+                for (int t = 0; t < NW; ++t) {
+                    const int d = (t + rot) & (NW - 1);
+                    unsigned w = S.w[0];
+#pragma unroll
+                    for (int i = 1; i < NW; ++i) w = d == i ? S.w[i] : w;
 #pragma unroll
                     for (int h = 0; h < 2; ++h) {
                         float v[4];
 #pragma unroll
                         for (int b = 0; b < 2; ++b) {
-                            const unsigned byte = (pw[i] >> (8 * (2 * h + b))) & 0xFFu;
-                            v[2 * b] = (float)((int)(byte & 15u) - 8) * ps;
-                            v[2 * b + 1] = (float)((int)(byte >> 4) - 8) * ps;
+                            const unsigned byte = (w >> (8 * (2 * h + b))) & 0xFFu;
+                            v[2 * b] = (float)((int)(byte & 15u) - 8) * S.s;
+                            v[2 * b + 1] = (float)((int)(byte >> 4) - 8) * S.s;
                         }
-                        *reinterpret_cast<float4*>(dst + i * 8 + h * 4) = make_float4(v[0], v[1], v[2], v[3]);
+                        *reinterpret_cast<float4*>(dst + d * 8 + h * 4) = make_float4(v[0], v[1], v[2], v[3]);
                     }
+                }
             } else if constexpr (WF == WF_F16) {
                 // dword i holds inputs 2 i, 2 i + 1
 #pragma unroll
                 for (int i = 0; i < NW; i += 2) {
-                    const float2 a = __half22float2(*reinterpret_cast<const __half2*>(&pw[i]));
-                    const float2 b = __half22float2(*reinterpret_cast<const __half2*>(&pw[i + 1]));
+                    const float2 a = __half22float2(*reinterpret_cast<const __half2*>(&S.w[i]));
+                    const float2 b = __half22float2(*reinterpret_cast<const __half2*>(&S.w[i + 1]));
                     *reinterpret_cast<float4*>(dst + 2 * i) = make_float4(a.x, a.y, b.x, b.y);
                 }
             } else {
 #pragma unroll
                 for (int i = 0; i < NW; i += 4)
-                    *reinterpret_cast<float4*>(dst + i) = make_float4(__uint_as_float(pw[i]), __uint_as_float(pw[i + 1]),
-                                                                      __uint_as_float(pw[i + 2]), __uint_as_float(pw[i + 3]));
+                    *reinterpret_cast<float4*>(dst + i) = make_float4(__uint_as_float(S.w[i]), __uint_as_float(S.w[i + 1]),
+                                                                      __uint_as_float(S.w[i + 2]), __uint_as_float(S.w[i + 3]));
             }
         }
         __syncthreads();
-        if (k0 + GK < ke) load_stage(k0 + GK);
+        load_stage(k0 + GK, S);  // past the range: clamped loads, values unused
         // all GK / 4 steps, also in a partial last stage: its missing columns
-        // were staged as zero activations and zero weights
+        // were staged as zero activations and zero weights.  In each block of
+        // 16 columns lane l takes columns 4 (l / 16) .. + 3 with one 16-byte
+        // LDS read per operand and feeds them to four consecutive steps (the
+        // same permutation of k on both operands).
 #pragma unroll
-        for (int kk = 0; kk < GK / 4; ++kk) {
-            const int k = kk * 4 + (lane >> 4);
-            float a[MI], b[2];
-#pragma unroll
-            for (int i = 0; i < MI; ++i) a[i] = As[(wm * (TM / 2) + i * 16 + (lane & 15)) * GS + k];
-#pragma unroll
-            for (int j = 0; j < 2; ++j) b[j] = Bs[(wn * 32 + j * 16 + (lane & 15)) * GS + k];
+        for (int kc = 0; kc < GK / 16; ++kc) {
+            const int k = kc * 16 + 4 * (lane >> 4);
+            float4 a[MI], b[2];
 #pragma unroll
             for (int i = 0; i < MI; ++i)
+                a[i] = *reinterpret_cast<const float4*>(As + (wm * (TM / 2) + i * 16 + (lane & 15)) * GS + k);
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[j], acc[i][j], 0, 0, 0);
+            for (int j = 0; j < 2; ++j)
+                b[j] = *reinterpret_cast<const float4*>(Bs + (wn * 32 + j * 16 + (lane & 15)) * GS + k);
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int i = 0; i < MI; ++i)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i][s], b[j][s], acc[i][j], 0, 0, 0);
         }
-    }
+    };
+    load_stage(kb, st);
+    for (int k0 = kb; k0 < ke; k0 += GK) run_stage(k0, st);
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll

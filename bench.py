@@ -58,10 +58,16 @@ def prefill_flops(shape, B: int, M: int) -> float:
     return B * (2.0 * M * w_per_layer * L + 2.0 * L * d * M * (M + 1) + 2.0 * d * V)
 
 
-def kernel_source_hash() -> str:
+# sources that build and launch each profiled kernel (its traffic record is
+# void once any of them changes)
+KERNEL_SOURCES = {"mt_decode_step_persistent": ("mt_decode_persistent.hip", "mt_internal.h", "mt_api.cpp")}
+
+
+def kernel_source_hash(kernel: str = "mt_decode_step_persistent") -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "audio_midi_transformer_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    names = KERNEL_SOURCES.get(kernel) or sorted(os.listdir(csrc))
+    for name in names:
         with open(os.path.join(csrc, name), "rb") as fh:
             h.update(name.encode())
             h.update(fh.read())
@@ -77,7 +83,7 @@ def traffic_from_profiles(kernel: str, workload_key: str, variant: str = ""):
         return None
     with open(path) as fh:
         rec = json.load(fh)
-    if rec.get("source_hash") != kernel_source_hash():
+    if rec.get("source_hash") != kernel_source_hash(kernel):
         return None
     return rec.get("bytes_per_launch")
 
