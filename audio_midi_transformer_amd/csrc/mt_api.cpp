@@ -56,6 +56,8 @@ struct mt_model {
     float* lnf = nullptr;  // [2, d]
     uint8_t* wq_all = nullptr;
     float* ws_all = nullptr;
+    uint8_t* wt_all = nullptr;  // the projections in the GEMV tiling
+    float* wst_all = nullptr;
     std::vector<Int4Mat> proj;  // [L*4]
     // cache
     float* kc = nullptr;
@@ -90,7 +92,7 @@ hipError_t dmalloc(T** p, size_t count) {
 
 void free_model(mt_model* m) {
     if (!m) return;
-    void* ptrs[] = {m->tok_emb, m->lm_head, m->ln, m->lnf, m->wq_all, m->ws_all, m->kc, m->vc, m->err, m->x,
+    void* ptrs[] = {m->tok_emb, m->lm_head, m->ln, m->lnf, m->wq_all, m->ws_all, m->wt_all, m->wst_all, m->kc, m->vc, m->err, m->x,
                     m->a, m->q, m->att, m->h, m->part, m->z, m->xbuf, m->trace, m->pf};
     for (void* p : ptrs)
         if (p) (void)hipFree(p);
@@ -319,6 +321,23 @@ int mt_create(const mt_config* cfg, const mt_weights* w, int weights_on_device, 
         so += ns;
     }
     if (hipMemsetAsync(m->err, 0, 16, st)) return bail(fail(MT_ERR_HIP, "mt_create: clearing the error word failed"));
+    // second copy of the projections in the GEMV tiling (decode with B <= 8)
+    size_t tbytes = 0, tfloats = 0;
+    for (const Int4Mat& pm : m->proj) {
+        tbytes += tiled_weight_bytes(pm);
+        tfloats += tiled_scale_floats(pm);
+    }
+    if (dmalloc(&m->wt_all, tbytes) || dmalloc(&m->wst_all, std::max<size_t>(tfloats, 64)))
+        return bail(fail(MT_ERR_OOM, "mt_create: GEMV weight copy of %zu bytes", tbytes));
+    size_t to = 0, tso = 0;
+    for (Int4Mat& pm : m->proj) {
+        if (launch_tile_weights(pm, m->wt_all + to, m->wst_all + tso, st) != hipSuccess)
+            return bail(fail(MT_ERR_HIP, "mt_create: weight tiling failed"));
+        pm.qt = m->wt_all + to;
+        pm.st = fmt == WF_INT4 ? m->wst_all + tso : nullptr;
+        to += tiled_weight_bytes(pm);
+        tso += tiled_scale_floats(pm);
+    }
     // the single-launch step reads nibbles only
     m->persistent_ok = fmt == WF_INT4 && persistent_supported(d, F, H, B, V);
     if (m->persistent_ok) {

@@ -50,6 +50,8 @@ struct Int4Mat {
     int N;
     int K;
     int fmt = WF_INT4;
+    const uint8_t* qt = nullptr;  // the same weights in the GEMV tiling (launch_tile_weights)
+    const float* st = nullptr;    // INT4: scales in the GEMV tiling
 };
 
 // ---- launchers (mt_kernels.hip); all return hipGetLastError() ----
@@ -85,6 +87,11 @@ hipError_t launch_lm_head(const float* z, int B, const float* w, int V, int d, f
                           hipStream_t st);
 hipError_t launch_argmax(const float* logits, int B, int V, int64_t* next, hipStream_t st);
 hipError_t launch_dequant(const Int4Mat& w, float* out, hipStream_t st);
+// GEMV tiling of w.q / w.s into qt (tiled_weight_bytes(w)) and st
+// (tiled_scale_floats(w) floats, INT4 only).
+size_t tiled_weight_bytes(const Int4Mat& w);
+size_t tiled_scale_floats(const Int4Mat& w);
+hipError_t launch_tile_weights(const Int4Mat& w, uint8_t* qt, float* st, hipStream_t stream);
 
 // Persistent single-launch decode step (mt_decode_persistent.hip).
 struct PersistentPlan;

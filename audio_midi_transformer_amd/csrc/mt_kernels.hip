@@ -177,13 +177,15 @@ constexpr int GV_M = 8;           // activation rows held in LDS
 // Lane l = 16 kq + r works on weight row n0 + r and, in every group of 32
 // columns, on the 8 contiguous columns 8 kq .. 8 kq + 7: INT4 weights are one
 // dword of nibbles per lane and group (converted as s * u - 8 s, one
-// rounding, equal to (u - 8) * s), dense weights one or two 16-byte loads,
+// rounding, equal to (u - 8) * s), dense weights one or two 16-byte pieces,
 // and the matching activations two 16-byte LDS reads, fetched one group
-// ahead.  Loads are issued activations first, then every weight group
-// (addresses clamped, never predicated), so that staging waits only for the
-// activations while the weights are still in flight, and each group's MFMAs
-// wait only for that group.  Rows past N load row N - 1; their results are
-// dropped.
+// ahead.  The weights come from the GEMV tiling (launch_tile_weights): per
+// (16-row block, group) the 64 lanes' pieces are consecutive, so every load
+// instruction reads one contiguous block.  Loads are issued activations
+// first, then every weight group (addresses clamped, never predicated), so
+// that staging waits only for the activations while the weights are still in
+// flight, and each group's MFMAs wait only for that group.  Rows past N are
+// zero padding in the tiling; their results are dropped.
 //
 // A8 (W4A8 variant): after staging, each (row, group of 32) of the staged
 // activations is coded to INT8 (s_a = max|x| / 127, code = clamp(rint(x *
@@ -215,7 +217,7 @@ __global__ __launch_bounds__(256) void k_gemv_w4(const float* __restrict__ X, in
     const int n0 = blockIdx.x * 16;
     const int G = K / 32;
     const int kb0 = blockIdx.y * kspan;
-    const int row = min(n0 + (lane & 15), N - 1), kq = lane >> 4;
+    const int kq = lane >> 4;
     const int bm = lane & 15;  // activation row this lane feeds into B
     const int xm = tid >> 5, xr = tid & 31;  // staging: row, thread in row (32 per row)
     const bool xrow = xm < M;
@@ -259,18 +261,17 @@ __global__ __launch_bounds__(256) void k_gemv_w4(const float* __restrict__ X, in
         uint4 wq2[WF == WF_F32 ? NG : 1];
 #pragma unroll
         for (int i = 0; i < NG; ++i) {
-            const int g = gbase + min(wv + 4 * i, gch - 1);
+            // tile (row block, group): lane l's piece at unit l, so a wave
+            // reads one contiguous block (256 B INT4, 1 KB half, 2 KB float)
+            const size_t tg = (size_t)blockIdx.x * G + gbase + min(wv + 4 * i, gch - 1);
             if constexpr (WF == WF_INT4) {
-                w4[i] = *reinterpret_cast<const unsigned*>(Wq + (size_t)row * (K / 2) + (size_t)g * 16 + 4 * kq);
-                sc[i] = Ws[(size_t)row * G + g];
+                w4[i] = reinterpret_cast<const unsigned*>(Wq)[tg * 64 + lane];
+                sc[i] = Ws[tg * 16 + (lane & 15)];
+            } else if constexpr (WF == WF_F16) {
+                wq[i] = reinterpret_cast<const uint4*>(Wq)[tg * 64 + lane];
             } else {
-                const size_t e = (size_t)row * K + (size_t)g * 32 + 8 * kq;
-                if constexpr (WF == WF_F16) {
-                    wq[i] = *reinterpret_cast<const uint4*>(Wq + 2 * e);
-                } else {
-                    wq[i] = *reinterpret_cast<const uint4*>(Wq + 4 * e);
-                    wq2[i] = *reinterpret_cast<const uint4*>(Wq + 4 * e + 16);
-                }
+                wq[i] = reinterpret_cast<const uint4*>(Wq)[tg * 128 + lane];
+                wq2[i] = reinterpret_cast<const uint4*>(Wq)[tg * 128 + 64 + lane];
             }
         }
         if (c0) __syncthreads();
@@ -1275,6 +1276,59 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ q, 
     }
 }
 
+// GEMV tiling of a projection (see k_gemv_w4): unit (t, g, l) for row block
+// t, group g and lane l = 16 kq + r holds row 16 t + r's piece kq of group g:
+// INT4 its dword kq (8 nibbles) with the scale in a [t][g][16] array, half
+// its 8 values 8 kq .. 8 kq + 7 (16 B), float its 8 values as two 16-byte
+// units (the first four at unit l, the rest at unit 64 + l).  Rows past N
+// are zero (INT4: nibbles 8, scale 0).  One thread per 4-byte word of the
+// tiled copy.
+__global__ __launch_bounds__(256) void k_tile_weights(const uint8_t* __restrict__ q, const float* __restrict__ s,
+                                                      int N, int K, int fmt, uint32_t* __restrict__ qt,
+                                                      float* __restrict__ st, size_t nwords) {
+    const int G = K / 32;
+    const int wpu = fmt == WF_INT4 ? 1 : 4;             // words per 16-byte or 4-byte unit
+    const int upt = fmt == WF_F32 ? 128 : 64;           // units per (row block, group)
+    for (size_t j = blockIdx.x * (size_t)blockDim.x + threadIdx.x; j < nwords; j += (size_t)gridDim.x * blockDim.x) {
+        const size_t unit = j / wpu;
+        const int w = (int)(j % wpu);
+        const size_t tg = unit / upt;
+        const int u = (int)(unit % upt);
+        const int l = u & 63, half = u >> 6;            // half: second 16 bytes of a float piece
+        const int t = (int)(tg / G), g = (int)(tg % G);
+        const int r = l & 15, kq = l >> 4;
+        const int row = 16 * t + r;
+        uint32_t v;
+        if (fmt == WF_INT4) {
+            v = row < N ? *reinterpret_cast<const uint32_t*>(q + (size_t)row * (K / 2) + (size_t)g * 16 + 4 * kq)
+                        : 0x88888888u;
+            if (kq == 0) st[tg * 16 + r] = row < N ? s[(size_t)row * G + g] : 0.f;
+        } else {
+            const int esz = fmt == WF_F16 ? 2 : 4;
+            const size_t col = (size_t)g * 32 + 8 * kq + (size_t)half * 4;  // first column of the unit
+            v = row < N ? *reinterpret_cast<const uint32_t*>(q + ((size_t)row * K + col) * esz + 4 * w) : 0u;
+        }
+        qt[j] = v;
+    }
+}
+
+size_t tiled_weight_bytes(const Int4Mat& w) {
+    const size_t rows = (size_t)(w.N + 15) / 16 * 16;
+    return rows * w.K * (w.fmt == WF_INT4 ? 1 : w.fmt == WF_F16 ? 4 : 8) / 2;
+}
+size_t tiled_scale_floats(const Int4Mat& w) {
+    return w.fmt == WF_INT4 ? (size_t)(w.N + 15) / 16 * 16 * (w.K / 32) : 0;
+}
+
+hipError_t launch_tile_weights(const Int4Mat& w, uint8_t* qt, float* st, hipStream_t st_) {
+    if (w.K % 32) return hipErrorInvalidValue;
+    const size_t nwords = tiled_weight_bytes(w) / 4;
+    const int grid = (int)std::min<size_t>((nwords + 255) / 256, 65536);
+    hipLaunchKernelGGL(k_tile_weights, dim3(grid), dim3(256), 0, st_, w.q, w.s, w.N, w.K, w.fmt,
+                       reinterpret_cast<uint32_t*>(qt), st, nwords);
+    return hipGetLastError();
+}
+
 // Dense weights as float (half widened exactly).
 __global__ __launch_bounds__(256) void k_widen(const uint8_t* __restrict__ q, bool half, size_t n,
                                                float* __restrict__ out) {
@@ -1409,7 +1463,8 @@ hipError_t launch_w4_matmul(const float* x, int ldx, int M, const Int4Mat& w, co
             attr = true;
         }
         const dim3 grid((w.N + 15) / 16, ksplit);
-        const GemvArgs ga{x, ldx, M, w.K, kspan, ln_g, ln_b, eps, ap.part, ap.H, ap.nsplit, w.q, w.s, w.N, y, ldy, ep};
+        if (!w.qt || (w.fmt == WF_INT4 && !w.st)) return hipErrorInvalidValue;  // needs the GEMV tiling
+        const GemvArgs ga{x, ldx, M, w.K, kspan, ln_g, ln_b, eps, ap.part, ap.H, ap.nsplit, w.qt, w.st, w.N, y, ldy, ep};
         if (w.fmt == WF_F16) gemv_launch<WF_F16, false>(ng, grid, lds, st, ga);
         else if (w.fmt == WF_F32) gemv_launch<WF_F32, false>(ng, grid, lds, st, ga);
         else if (a8) gemv_launch<WF_INT4, true>(ng, grid, lds, st, ga);

@@ -129,9 +129,12 @@ int mt_pack_int4(const float* W, int32_t N, int32_t K, uint8_t* q, float* s);
 
 /* Create a model: validates the config, copies the weights to the current
  * HIP device and allocates the KV cache [L, B, t_cap, H, 64] twice (K, V,
- * FP32, 2*L*B*t_cap*d*4 bytes) plus decode scratch.  weights_on_device: 0 =
- * host pointers, 1 = device pointers.  The caller may free its weight
- * buffers once mt_create returns.  T_past starts at 0. */
+ * FP32, 2*L*B*t_cap*d*4 bytes) plus decode scratch.  The projections are
+ * held twice on the device: as given, and re-tiled for the batched decode
+ * kernels (16-row blocks per group, so each load instruction reads one
+ * contiguous block).  weights_on_device: 0 = host pointers, 1 = device
+ * pointers.  The caller may free its weight buffers once mt_create
+ * returns.  T_past starts at 0. */
 int mt_create(const mt_config* cfg, const mt_weights* w, int weights_on_device, void* stream,
               mt_model** out);
 
