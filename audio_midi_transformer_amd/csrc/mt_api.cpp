@@ -122,9 +122,11 @@ int check_config(const mt_config* c) {
 }
 
 // Split-K layout of the decode attention over T keys: about 512 workgroups,
-// chunks of 16 .. 256 positions (a multiple of 16).
+// chunks of 16 .. 256 positions (a multiple of 16), at most kMaxSplit splits
+// (the partials buffer holds that many per sequence and head; with
+// T <= kMaxTcap = kMaxSplit * kMaxChunk the chunk then stays <= 256).
 void attn_split(int B, int H, int T, int* nsplit, int* chunk) {
-    int want = std::max(1, (512 + B * H - 1) / (B * H));
+    const int want = std::min(kMaxSplit, std::max(1, (512 + B * H - 1) / (B * H)));
     int ch = (T + want - 1) / want;
     ch = std::min(kMaxChunk, std::max(16, (ch + 15) / 16 * 16));
     *nsplit = (T + ch - 1) / ch;
@@ -173,6 +175,7 @@ int run_layers(mt_model* m, float* x, float* a, float* q, float* att, float* h, 
             }
             int ns, ch;
             attn_split(c.batch, c.n_heads, tmax, &ns, &ch);
+            if (ns > kMaxSplit) return fail(MT_ERR_INVALID_ARG, "decode attention: %d splits exceed %d", ns, kMaxSplit);
             HIP_TRY(launch_attn_decode(q, m->kc, m->vc, l, c.batch, c.n_heads, c.t_cap, T, m->part, ns, ch, st));
             const AttnParts ap{m->part, c.n_heads, ns};
             HIP_TRY(launch_w4_matmul(nullptr, d, M, m->proj[l * 4 + 1], nullptr, nullptr, 0.f, x, d, EPI_RESID,
