@@ -162,6 +162,18 @@ constexpr int PART_ACC = 4;
 constexpr int GV_MAXSPAN = 2048;  // activation columns staged in LDS at a time
 constexpr int GV_M = 8;           // activation rows held in LDS
 
+// Source of the activation rows (a template parameter, so that every load
+// of a variant is straight-line code and each wait counts exactly the loads
+// it needs).
+enum GemvSrc : int { GS_ROWS = 0, GS_LN = 1, GS_PARTS = 2 };
+
+// Sum over each group of 32 lanes in every lane: DPP within rows of 16, one
+// swap between the two rows.
+__device__ __forceinline__ float sum32(float v) {
+    v = row_sum16(v);
+    return v + __shfl_xor(v, 16);
+}
+
 // Y[m, n] = sum_k W'[n, k] x[m, k] for M <= 8 rows with v_mfma_f32_16x16x4f32
 // (A = 16 output rows of W' x 4 columns, B = 4 columns x 16 activation rows,
 // 8 of them used).  x is read from X, or (part != NULL) merged from
@@ -193,18 +205,8 @@ constexpr int GV_M = 8;           // activation rows held in LDS
 // with A = activation codes (16 rows, 8 used) and B = 16 (u - 8) of 16
 // weight rows; the INT32 tile is exact and is added to the FP32 result as
 // I * s_a * s_w / 16.
-// Source of the activation rows (a template parameter, so that every load
-// of a variant is straight-line code and each wait counts exactly the loads
-// it needs).
-enum GemvSrc : int { GS_ROWS = 0, GS_LN = 1, GS_PARTS = 2 };
-
-// Sum over each group of 32 lanes in every lane: DPP within rows of 16, one
-// swap between the two rows.
-__device__ __forceinline__ float sum32(float v) {
-    v = row_sum16(v);
-    return v + __shfl_xor(v, 16);
-}
-
+//
+// NG: groups per wave and chunk at most (4, 8, 12 or 16); SRC: GemvSrc.
 template <int WF, bool A8, int NG, int SRC>
 __global__ __launch_bounds__(256) void k_gemv_w4(const float* __restrict__ X, int ldx, int M, int K, int kspan,
                                                  const float* __restrict__ ln_g, const float* __restrict__ ln_b,
