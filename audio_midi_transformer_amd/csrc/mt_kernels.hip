@@ -906,7 +906,9 @@ __global__ __launch_bounds__(256) void k_attn_decode(const float* __restrict__ q
 // Causal attention of R new rows per sequence (positions t0 .. t0+R-1) over
 // the cache, on v_mfma_f32_16x16x4f32 (A = 16 rows x 4 columns, B = 4 x 16,
 // lane l supplies A[l % 16][l / 16] and B[l / 16][l % 16] and receives
-// D[4 (l / 16) + r][l % 16]).  Workgroup (row block, h, b): 16 query rows.
+// D[4 (l / 16) + r][l % 16]).  Workgroup (x, h, b): the 16 query rows of
+// row block x, then those of row block nrb - 1 - x (nrb = ceil(R / 16)),
+// so that the short and the long rows of a causal prompt pair up.
 // The keys the block sees are cut into blocks of 32; wave w takes blocks w,
 // w + 4, ..., so the long rows at the end of a prompt are shared by four
 // waves instead of one.  Per key block a wave stages K and V in its own LDS
@@ -926,18 +928,32 @@ __global__ __launch_bounds__(256) void k_attn_prefill(const float* __restrict__ 
                                                       float* __restrict__ out) {
     extern __shared__ float asm_lds[];
     const int d = H * 64;
-    const int i0 = blockIdx.x * 16, h = blockIdx.y, b = blockIdx.z;
+    const int h = blockIdx.y, b = blockIdx.z;
     const int bs = b0 + b, t0 = tp.t[bs];  // sequence in the cache, its first new position
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int lr = lane & 15, lq = lane >> 4;
     float* Kw = asm_lds + wave * (2 * PKB + 16) * PS;  // [PKB][PS]
     float* Vw = Kw + PKB * PS;                          // [PKB][PS]
     float* P = Vw + PKB * PS;                           // [16][PS]
-    // A operand of Q K^T: row i0 + lr, dimensions 4 s + lq
+    // row blocks x and nrb - 1 - x: every workgroup does about the same
+    // causal work, so one round of workgroups covers the prompt
+    const int nrb = (R + 15) / 16;
+    for (int pass = 0; pass < 2; ++pass) {
+    const int rb = pass == 0 ? (int)blockIdx.x : nrb - 1 - (int)blockIdx.x;
+    if (pass == 1 && rb <= (int)blockIdx.x) break;
+    if (pass == 1) __syncthreads();  // the first block's merge has read the LDS
+    const int i0 = rb * 16;
+    // A operand of Q K^T: row i0 + lr; step 4 j + e takes dimension
+    // 16 j + 4 lq + e (the same order on the K side), so that a lane's K
+    // values for four steps are one 16-byte LDS read
     const int qi = i0 + lr;
     float qa[16];
 #pragma unroll
-    for (int s = 0; s < 16; ++s) qa[s] = qi < R ? q[((size_t)b * R + qi) * d + h * 64 + 4 * s + lq] : 0.f;
+    for (int j = 0; j < 4; ++j) {
+        const float4 v = qi < R ? *reinterpret_cast<const float4*>(q + ((size_t)b * R + qi) * d + h * 64 + 16 * j + 4 * lq)
+                                : make_float4(0.f, 0.f, 0.f, 0.f);
+        qa[4 * j] = v.x, qa[4 * j + 1] = v.y, qa[4 * j + 2] = v.z, qa[4 * j + 3] = v.w;
+    }
     // rows 4 lq + r of the block (query positions)
     int qpos[4];
 #pragma unroll
@@ -954,22 +970,23 @@ __global__ __launch_bounds__(256) void k_attn_prefill(const float* __restrict__ 
     const int kmax = t0 + min(i0 + 15, R - 1);  // last key any row of the block sees
     const size_t base = ((size_t)(layer * Btot + bs) * t_cap) * d + h * 64;
     // K and V rows of a block go through registers: the next block of this
-    // wave is requested before the current one is multiplied
+    // wave is requested before the current one is multiplied.  Every load is
+    // issued (key clamped to kmax) and keys past kmax are zeroed afterwards,
+    // so the waits count exactly one block's loads.
     constexpr int NE = PKB * 16 / 64;
     float4 pk[NE], pv[NE];
     auto load_block = [&](int kb) {
 #pragma unroll
         for (int e = 0; e < NE; ++e) {
             const int idx = lane + 64 * e, t = kb + (idx >> 4), c4 = idx & 15;
-            pk[e] = make_float4(0.f, 0.f, 0.f, 0.f);
-            pv[e] = pk[e];
-            if (t <= kmax) {
-                pk[e] = *reinterpret_cast<const float4*>(kc + base + (size_t)t * d + c4 * 4);
-                pv[e] = *reinterpret_cast<const float4*>(vc + base + (size_t)t * d + c4 * 4);
-            }
+            const size_t off = base + (size_t)min(t, kmax) * d + c4 * 4;
+            const float4 kv = *reinterpret_cast<const float4*>(kc + off);
+            const float4 vv = *reinterpret_cast<const float4*>(vc + off);
+            pk[e] = t <= kmax ? kv : make_float4(0.f, 0.f, 0.f, 0.f);
+            pv[e] = t <= kmax ? vv : make_float4(0.f, 0.f, 0.f, 0.f);
         }
     };
-    if (PKB * wave <= kmax) load_block(PKB * wave);
+    load_block(PKB * wave);
     for (int kb = PKB * wave; kb <= kmax; kb += 4 * PKB) {
         // this wave's K and V block (its own tiles: no workgroup barrier)
 #pragma unroll
@@ -978,16 +995,22 @@ __global__ __launch_bounds__(256) void k_attn_prefill(const float* __restrict__ 
             *reinterpret_cast<float4*>(Kw + kk * PS + c4 * 4) = pk[e];
             *reinterpret_cast<float4*>(Vw + kk * PS + c4 * 4) = pv[e];
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        if (kb + 4 * PKB <= kmax) load_block(kb + 4 * PKB);
+        // (LDS operations of one wave complete in order: the tiles written
+        // above are what the reads below see, with no barrier)
+        load_block(kb + 4 * PKB);
         // S tiles n: keys kb + 16 n + lr
         f32x4 sc[2];
 #pragma unroll
         for (int n = 0; n < 2; ++n) {
             sc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int s = 0; s < 16; ++s)
-                sc[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[s], Kw[(16 * n + lr) * PS + 4 * s + lq], sc[n], 0, 0, 0);
+            for (int j = 0; j < 4; ++j) {
+                const float4 kv = *reinterpret_cast<const float4*>(Kw + (16 * n + lr) * PS + 16 * j + 4 * lq);
+                sc[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[4 * j], kv.x, sc[n], 0, 0, 0);
+                sc[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[4 * j + 1], kv.y, sc[n], 0, 0, 0);
+                sc[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[4 * j + 2], kv.z, sc[n], 0, 0, 0);
+                sc[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[4 * j + 3], kv.w, sc[n], 0, 0, 0);
+            }
         }
         // mask, row max over the block (in-lane over n, then the 16-lane row)
         float bm[4];
@@ -1024,16 +1047,20 @@ __global__ __launch_bounds__(256) void k_attn_prefill(const float* __restrict__ 
         for (int n = 0; n < 4; ++n)
 #pragma unroll
             for (int r = 0; r < 4; ++r) o[n][r] *= rs[r];
-        // O += P V (P rows written by this wave only)
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        // O += P V (P rows written by this wave only).  Step 4 j + e takes key
+        // 16 j + 4 lq + e: one 16-byte read of P per four steps.
 #pragma unroll
-        for (int s = 0; s < PKB / 4; ++s) {
-            const float pa = P[lr * PS + 4 * s + lq];
+        for (int j = 0; j < PKB / 16; ++j) {
+            const float4 pa = *reinterpret_cast<const float4*>(P + lr * PS + 16 * j + 4 * lq);
+            const float pe[4] = {pa.x, pa.y, pa.z, pa.w};
 #pragma unroll
-            for (int n = 0; n < 4; ++n)
-                o[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa, Vw[(4 * s + lq) * PS + 16 * n + lr], o[n], 0, 0, 0);
+            for (int e = 0; e < 4; ++e) {
+                const float* vr = Vw + (16 * j + 4 * lq + e) * PS + lr;
+#pragma unroll
+                for (int n = 0; n < 4; ++n)
+                    o[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(pe[e], vr[16 * n], o[n], 0, 0, 0);
+            }
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");  // tiles read before the next block overwrites them
     }
     // merge the four waves: output tiles [wave][16][64], (max, sum) [wave][16]
     __syncthreads();
@@ -1073,6 +1100,7 @@ __global__ __launch_bounds__(256) void k_attn_prefill(const float* __restrict__ 
         const float inv = 1.0f / L;
         *reinterpret_cast<float4*>(out + ((size_t)b * R + i0 + row) * d + h * 64 + c) =
             make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+    }
     }
 }
 
@@ -1552,7 +1580,7 @@ hipError_t launch_attn_prefill(const float* q, const float* kc, const float* vc,
         if (e != hipSuccess) return e;
         attr = true;
     }
-    hipLaunchKernelGGL(k_attn_prefill, dim3((R + 15) / 16, H, nb), dim3(256), kAttnPrefillLds, st, q, kc, vc,
+    hipLaunchKernelGGL(k_attn_prefill, dim3(((R + 15) / 16 + 1) / 2, H, nb), dim3(256), kAttnPrefillLds, st, q, kc, vc,
                        layer, Btot, b0, H, t_cap, t0, R, out);
     return hipGetLastError();
 }
