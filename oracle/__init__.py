@@ -80,6 +80,7 @@ def lib() -> ctypes.CDLL:
         L.oracle_model_position_seq.argtypes = [ctypes.c_void_p, i64]
         L.oracle_model_position_seq.restype = i64
         L.oracle_model_reset_seq.argtypes = [ctypes.c_void_p, i64]
+        L.oracle_cfg_combine.argtypes = [_f32p, i64, i64, ctypes.c_float, _f32p, _i64p]
         _lib = L
     return _lib
 
@@ -133,6 +134,20 @@ def round_half(X: np.ndarray) -> np.ndarray:
     out = np.empty_like(X)
     _check(lib().oracle_round_half(_p(X, _f32p), X.size, _p(out, _f32p)), "round_half")
     return out
+
+
+def cfg_combine(logits: np.ndarray, cfg: float) -> Tuple[np.ndarray, np.ndarray]:
+    """Classifier-free guidance over row pairs: logits [2 Np, V] (rows
+    0 .. Np-1 conditional, row Np + i the unconditional partner of row i)
+    -> (guided float32 [Np, V], next int64 [Np])."""
+    lg = _f32(logits)
+    n2, V = lg.shape
+    assert n2 % 2 == 0 and n2 > 0
+    g = np.empty((n2 // 2, V), dtype=np.float32)
+    nx = np.empty(n2 // 2, dtype=np.int64)
+    _check(lib().oracle_cfg_combine(_p(lg, _f32p), n2 // 2, V, float(cfg), _p(g, _f32p), _p(nx, _i64p)),
+           "cfg_combine")
+    return g, nx
 
 
 def quantize_act_int8(X: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:

@@ -45,6 +45,16 @@
  * oracle_round_half (ties to even, gradual underflow, overflow to infinity)
  * and everything downstream is unchanged.
  *
+ * Classifier-free guidance over row pairs (oracle_cfg_combine): the model
+ * card offers optional CFG, the paper's scaling table is quoted at CFG = 2,
+ * the conditioner has an "unconditional" instrument class, and released
+ * models are run with the coefficient at 1; the combining rule itself is not
+ * on the pages.  Reading: the usual guidance of logits, cond + (cfg - 1) *
+ * (cond - uncond) (= uncond + cfg * (cond - uncond); cfg = 1 is the plain
+ * conditional model), the next token being the argmax of the guided row.
+ * Pinned by its special cases (cfg = 1, cfg = 0, equal rows) and by
+ * affinity in cfg; the rule for other coefficients is a reading.
+ *
  * Precision: every named tensor is stored as binary32; every dot product,
  * LayerNorm moment, softmax and GELU is evaluated in binary64 and rounded once.
  * Must be compiled without fast-math and with FP contraction off.
@@ -616,5 +626,32 @@ int oracle_model_reset_seq(oracle_model* m, int64_t b)
 {
     if (!m || b < 0 || b >= m->B) return ORACLE_EINVAL;
     m->tpos[b] = 0;
+    return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* Guided logits of `pairs` row pairs: logits [2 pairs, V]; row i is the
+ * conditional row and row pairs + i its unconditional partner.  guided[i, v]
+ * = c + (cfg - 1) * (c - u), the difference, product and sum each a binary64
+ * operation on the widened inputs, then rounded to binary32; next[i] is the
+ * argmax of guided row i, lowest index on ties. */
+int oracle_cfg_combine(const float* logits, int64_t pairs, int64_t V, float cfg, float* guided, int64_t* next)
+{
+    if (!logits || !guided || !next || pairs < 1 || V < 1) return ORACLE_EINVAL;
+    const double w = (double)cfg - 1.0;
+    for (int64_t i = 0; i < pairs; ++i) {
+        const float* c = logits + i * V;
+        const float* u = logits + (pairs + i) * V;
+        float* g = guided + i * V;
+        for (int64_t v = 0; v < V; ++v) {
+            const double diff = (double)c[v] - (double)u[v];
+            const double step = w * diff;
+            g[v] = (float)((double)c[v] + step);
+        }
+        int64_t best = 0;
+        for (int64_t v = 1; v < V; ++v)
+            if (g[v] > g[best]) best = v;
+        next[i] = best;
+    }
     return ORACLE_OK;
 }

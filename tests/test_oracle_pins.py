@@ -608,3 +608,118 @@ def test_model_dense_modes_are_unquantised_models(oracle_mod):
     assert not np.array_equal(l16, l32)
     with pytest.raises(ValueError):
         oracle_mod.OracleModel.from_weights(w, batch=1, t_cap=3, dense="bf16")
+
+
+# ---------------------------------------------------------------- classifier-free guidance
+
+def _pairs(rows_c, rows_u):
+    return np.asarray(list(rows_c) + list(rows_u), dtype=np.float32)
+
+
+def test_cfg_hand_cases(oracle_mod):
+    """Hand-computed guided rows of two pairs (rows 0, 1 conditional, rows
+    2, 3 their partners): catches a sign error, conditional and
+    unconditional swapped, row i paired with i + 1 instead of Np + i, and a
+    tie not resolved to the lowest index."""
+    lg = _pairs([[1, 3, 2], [1, 1, 0]], [[0, 4, 1], [0, 0, 5]])
+    g, nx = oracle_mod.cfg_combine(lg, 2.0)
+    # 2c - u
+    assert np.array_equal(g, np.array([[2, 2, 3], [2, 2, -5]], np.float32))
+    assert list(nx) == [2, 0]
+    g, nx = oracle_mod.cfg_combine(lg, 3.0)
+    # 3c - 2u
+    assert np.array_equal(g, np.array([[3, 1, 4], [3, 3, -10]], np.float32))
+    assert list(nx) == [2, 0]
+    g, nx = oracle_mod.cfg_combine(lg, 0.5)
+    # (c + u) / 2
+    assert np.array_equal(g, np.array([[0.5, 3.5, 1.5], [0.5, 0.5, 2.5]], np.float32))
+    assert list(nx) == [1, 2]
+
+
+def test_cfg_coefficient_one_is_the_conditional_model(oracle_mod):
+    """cfg = 1 returns the conditional logits bit for bit and numpy's first
+    argmax: the released models' setting is the plain path."""
+    rng = np.random.default_rng(90)
+    lg = (rng.standard_normal((6, 1393)) * 3).astype(np.float32)
+    g, nx = oracle_mod.cfg_combine(lg, 1.0)
+    assert np.array_equal(g.view(np.uint32), lg[:3].view(np.uint32))
+    assert list(nx) == [int(np.argmax(r)) for r in lg[:3]]
+
+
+def test_cfg_coefficient_zero_is_the_unconditional_model(oracle_mod):
+    """cfg = 0 returns the unconditional rows exactly (the differences of
+    these binary32 values are exact in binary64)."""
+    rng = np.random.default_rng(91)
+    lg = (rng.standard_normal((8, 257)) * 5).astype(np.float32)
+    g, nx = oracle_mod.cfg_combine(lg, 0.0)
+    assert np.array_equal(g, lg[4:])
+    assert list(nx) == [int(np.argmax(r)) for r in lg[4:]]
+
+
+def test_cfg_equal_rows_are_fixed_points(oracle_mod):
+    """Where both rows agree the coefficient does not matter."""
+    rng = np.random.default_rng(92)
+    c = rng.standard_normal((2, 100)).astype(np.float32)
+    for cfg in (-3.0, 0.0, 2.0, 7.5, 1e6):
+        g, nx = oracle_mod.cfg_combine(np.concatenate([c, c]), cfg)
+        assert np.array_equal(g, c), cfg
+        assert list(nx) == [int(np.argmax(r)) for r in c]
+
+
+def _f32_ulp(x):
+    x = np.float32(abs(x))
+    return Fraction(float(np.nextafter(x, np.float32(np.inf)) - x))
+
+
+@pytest.mark.parametrize("cfg", [2.0, 3.0, -0.75, 1.5, 10.0])
+def test_cfg_exact_within_half_ulp(oracle_mod, cfg):
+    """Each guided value is the exact rational u + cfg (c - u), computed
+    with fractions, rounded to binary32: within half an ulp (catches a
+    dropped term or a coefficient applied to the wrong operand for any
+    coefficient, not only the special cases)."""
+    rng = np.random.default_rng(93)
+    lg = (rng.standard_normal((4, 64)) * 4).astype(np.float32)
+    g, nx = oracle_mod.cfg_combine(lg, cfg)
+    k = Fraction(cfg)
+    for i in range(2):
+        for v in range(64):
+            c, u = Fraction(float(lg[i, v])), Fraction(float(lg[2 + i, v]))
+            exact = u + k * (c - u)
+            assert abs(Fraction(float(g[i, v])) - exact) <= _f32_ulp(g[i, v]) / 2, (i, v)
+        assert nx[i] == int(np.argmax(g[i]))
+
+
+def test_model_cfg_pairs_coefficient_one_equals_conditional_model(oracle_mod):
+    """A batch of two conditional rows and their unconditional partners
+    (different prefixes), decoded with the guided token fed to both rows of
+    each pair, gives at cfg = 1 the logits and tokens of a model that holds
+    the conditional rows alone; at cfg = 2 the unconditional rows change the
+    result (catches guidance that ignores the partner, or partners fed their
+    own tokens)."""
+    shape = synth.tiny_shape(n_layers=2)
+    w = _tiny_weights(shape, seed=51)
+    d = shape.d_model
+    rng = np.random.default_rng(8)
+    Np, P = 2, 7
+    cond = rng.standard_normal((Np, P, d)).astype(np.float32)
+    uncond = cond.copy()
+    uncond[:, -2:] = rng.standard_normal((Np, 2, d)).astype(np.float32)
+    runs = {}
+    for cfg in (1.0, 2.0):
+        mp = oracle_mod.OracleModel.from_weights(w, batch=2 * Np, t_cap=24)
+        lg, _ = mp.forward(prefix=np.concatenate([cond, uncond]))
+        g, nx = oracle_mod.cfg_combine(lg, cfg)
+        hist = [(g, nx)]
+        for _ in range(5):
+            lg, _ = mp.forward(tokens=np.concatenate([nx, nx])[:, None])
+            g, nx = oracle_mod.cfg_combine(lg, cfg)
+            hist.append((g, nx))
+        runs[cfg] = hist
+        mp.close()
+    mc = oracle_mod.OracleModel.from_weights(w, batch=Np, t_cap=24)
+    lc, nc = mc.forward(prefix=cond)
+    for step, (g, nx) in enumerate(runs[1.0]):
+        assert np.array_equal(g, lc) and np.array_equal(nx, nc), step
+        lc, nc = mc.forward(tokens=nc[:, None])
+    mc.close()
+    assert not np.array_equal(runs[2.0][0][0], runs[1.0][0][0])
