@@ -35,7 +35,7 @@ MT_FLAG_DENSE_F32 = 4
 EXPORTED = ("mt_pack_int4", "mt_create", "mt_prefill", "mt_decode_step", "mt_reset",
             "mt_position", "mt_kv_cache", "mt_check", "mt_set_decode_path", "mt_destroy",
             "mt_last_error", "mt_debug_dequant", "mt_debug_matmul", "mt_debug_trace",
-            "mt_prefill_seq", "mt_reset_seq", "mt_position_seq")
+            "mt_prefill_seq", "mt_reset_seq", "mt_position_seq", "mt_cfg_combine")
 
 
 class mt_config(ctypes.Structure):
@@ -94,10 +94,11 @@ def lib() -> ctypes.CDLL:
     L.mt_prefill_seq.argtypes = [vp, i32, vp, i32, vp, i32, vp, vp, vp]
     L.mt_reset_seq.argtypes = [vp, i32]
     L.mt_position_seq.argtypes = [vp, i32, ctypes.POINTER(i32)]
+    L.mt_cfg_combine.argtypes = [vp, i32, i32, ctypes.c_float, vp, vp, vp, vp]
     for name in ("mt_pack_int4", "mt_create", "mt_prefill", "mt_decode_step", "mt_reset",
                  "mt_position", "mt_kv_cache", "mt_check", "mt_set_decode_path",
                  "mt_debug_dequant", "mt_debug_matmul", "mt_debug_trace",
-                 "mt_prefill_seq", "mt_reset_seq", "mt_position_seq"):
+                 "mt_prefill_seq", "mt_reset_seq", "mt_position_seq", "mt_cfg_combine"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -119,6 +120,27 @@ def mt_pack_int4(W: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
     s = np.empty((N, K // 32), dtype=np.float32)
     check(lib().mt_pack_int4(W.ctypes.data, N, K, q.ctypes.data, s.ctypes.data), "mt_pack_int4")
     return q, s
+
+
+def cfg_combine(logits, cfg: float, guided=None, next=None, token_pair=None, store_guided: bool = True,
+                stream=None):
+    """mt_cfg_combine on device tensors: logits [2 Np, V] float32 (rows
+    0 .. Np-1 conditional, row Np + i the partner of row i) -> (guided
+    [Np, V] or None, next [Np] int64, token_pair [2 Np] int64)."""
+    import torch
+    n2, V = logits.shape
+    if n2 % 2:
+        raise ValueError("cfg_combine needs an even number of rows")
+    Np = n2 // 2
+    if store_guided and guided is None:
+        guided = torch.empty((Np, V), dtype=torch.float32, device=logits.device)
+    if next is None:
+        next = torch.empty((Np,), dtype=torch.int64, device=logits.device)
+    if token_pair is None:
+        token_pair = torch.empty((n2,), dtype=torch.int64, device=logits.device)
+    check(lib().mt_cfg_combine(_ptr(logits), Np, V, float(cfg), _ptr(guided) if store_guided else None,
+                               _ptr(next), _ptr(token_pair), _stream(stream)), "mt_cfg_combine")
+    return (guided if store_guided else None), next, token_pair
 
 
 def _ptr(t) -> Optional[int]:

@@ -152,8 +152,9 @@ int run_layers(mt_model* m, float* x, float* a, float* q, float* att, float* h, 
     const mt_config& c = m->c;
     const int d = c.d_model, F = c.d_ff, M = nb * R;
     const bool a8 = (c.flags & MT_FLAG_W4A8) != 0;
-    // with few rows the GEMV applies both LayerNorms itself
-    const bool fuse_ln = gemv_fuses_layernorm(M, d);
+    // with few rows (whole sequences of at most 8 rows per GEMV slice) the
+    // GEMV applies both LayerNorms itself
+    const bool fuse_ln = gemv_fuses_layernorm(M, d) && gemv_takes_rows(M, R);
     for (int l = 0; l < c.n_layers; ++l) {
         const float* ln = m->ln + (size_t)l * 4 * d;
         QkvDest dst{q, m->kc, m->vc, d, l, c.batch, c.t_cap, b0, R, m->pos};
@@ -165,7 +166,7 @@ int run_layers(mt_model* m, float* x, float* a, float* q, float* att, float* h, 
             HIP_TRY(launch_w4_matmul(a, d, M, m->proj[l * 4 + 0], nullptr, nullptr, 0.f, nullptr, 0, EPI_QKV, &dst,
                                      false, st, nullptr, a8));
         }
-        if (decode && gemv_fuses_layernorm(M, d)) {
+        if (decode && fuse_ln) {
             // split-K attention; the O projection merges the partials
             SeqPos T{};
             int tmax = 0;
@@ -449,6 +450,15 @@ int mt_decode_step(mt_model* m, const int64_t* token, float* logits, int64_t* ne
     return MT_OK;
 }
 
+int mt_cfg_combine(const float* logits, int32_t pairs, int32_t V, float cfg, float* guided, int64_t* next,
+                   int64_t* token_pair, void* stream) {
+    if (!logits || !next) return fail(MT_ERR_INVALID_ARG, "mt_cfg_combine: NULL argument");
+    if (pairs < 1 || V < 1) return fail(MT_ERR_INVALID_ARG, "mt_cfg_combine: %d pairs of %d logits", pairs, V);
+    if (!std::isfinite(cfg)) return fail(MT_ERR_INVALID_ARG, "mt_cfg_combine: coefficient is not finite");
+    HIP_TRY(launch_cfg_combine(logits, pairs, V, cfg, guided, next, token_pair, (hipStream_t)stream));
+    return MT_OK;
+}
+
 int mt_reset(mt_model* m) {
     if (!m) return fail(MT_ERR_INVALID_ARG, "mt_reset: NULL model");
     m->pos = SeqPos{};
@@ -537,7 +547,7 @@ int mt_debug_matmul(mt_model* m, int32_t layer, int32_t proj, const float* x, in
     if (layer < 0 || layer >= m->c.n_layers || p > 3)
         return fail(MT_ERR_INVALID_ARG, "mt_debug_matmul: bad layer/projection");
     const Int4Mat& w = m->proj[layer * 4 + p];
-    HIP_TRY(launch_w4_matmul(x, w.K, M, w, nullptr, nullptr, 0.f, y, w.N, EPI_STORE, nullptr, force_gemm || M > 8,
+    HIP_TRY(launch_w4_matmul(x, w.K, M, w, nullptr, nullptr, 0.f, y, w.N, EPI_STORE, nullptr, force_gemm,
                              (hipStream_t)stream, nullptr, (m->c.flags & MT_FLAG_W4A8) != 0));
     return MT_OK;
 }

@@ -73,6 +73,10 @@ struct AttnParts {
 hipError_t launch_w4_matmul(const float* x, int ldx, int M, const Int4Mat& w, const float* ln_g,
                             const float* ln_b, float eps, float* y, int ldy, Epilogue epi, const QkvDest* qkv,
                             bool force_gemm, hipStream_t st, const AttnParts* parts = nullptr, bool a8 = false);
+// The GEMV takes M rows (sequences of rows_per_seq rows each) in slices of
+// at most 8 rows; more rows than kGemvRowsMax go to the GEMM.
+constexpr int kGemvRowsMax = 64;
+bool gemv_takes_rows(int M, int rows_per_seq);
 bool gemv_fuses_layernorm(int M, int K);
 // Writes the split-K partials only; the O projection merges them.  Sequence
 // b attends to its first T.t[b] cache positions.
@@ -87,6 +91,11 @@ hipError_t launch_lm_head(const float* z, int B, const float* w, int V, int d, f
                           hipStream_t st);
 hipError_t launch_argmax(const float* logits, int B, int V, int64_t* next, hipStream_t st);
 hipError_t launch_dequant(const Int4Mat& w, float* out, hipStream_t st);
+// Guided logits of `pairs` conditional/unconditional row pairs of logits
+// [2 pairs, V] (row i and row pairs + i), their argmax, and that token for
+// both rows of each pair (guided and token_pair may be null).
+hipError_t launch_cfg_combine(const float* logits, int pairs, int V, float cfg, float* guided, int64_t* next,
+                              int64_t* token_pair, hipStream_t st);
 // GEMV tiling of w.q / w.s into qt (tiled_weight_bytes(w)) and st
 // (tiled_scale_floats(w) floats, INT4 only).
 size_t tiled_weight_bytes(const Int4Mat& w);

@@ -1256,23 +1256,11 @@ __global__ __launch_bounds__(256) void k_lm_head(const float* __restrict__ z, in
 }
 
 // Greedy argmax per sequence; the lowest index wins a tie.
-__global__ __launch_bounds__(256) void k_argmax(const float* __restrict__ logits, int V,
-                                                int64_t* __restrict__ next) {
-    __shared__ float sv[256];
-    __shared__ int si[256];
-    const int b = blockIdx.x, tid = threadIdx.x;
-    const float* lg = logits + (size_t)b * V;
-    float best = -INFINITY;
-    int bi = 0x7fffffff;
-    for (int v = tid; v < V; v += 256) {
-        const float x = lg[v];
-        if (x > best || bi == 0x7fffffff) {
-            if (bi == 0x7fffffff || x > best) {
-                best = x;
-                bi = v;
-            }
-        }
-    }
+// Argmax over one workgroup's candidates: (best, bi) of each thread, bi =
+// INT_MAX when the thread saw no element.  The larger value wins, the lower
+// index on equal values; a row of no candidates gives 0.
+__device__ int block_argmax256(float best, int bi, float* sv, int* si) {
+    const int tid = threadIdx.x;
     sv[tid] = best;
     si[tid] = bi;
     __syncthreads();
@@ -1287,7 +1275,66 @@ __global__ __launch_bounds__(256) void k_argmax(const float* __restrict__ logits
         }
         __syncthreads();
     }
-    if (tid == 0) next[b] = si[0] == 0x7fffffff ? 0 : si[0];
+    return si[0] == 0x7fffffff ? 0 : si[0];
+}
+
+__global__ __launch_bounds__(256) void k_argmax(const float* __restrict__ logits, int V,
+                                                int64_t* __restrict__ next) {
+    __shared__ float sv[256];
+    __shared__ int si[256];
+    const int b = blockIdx.x, tid = threadIdx.x;
+    const float* lg = logits + (size_t)b * V;
+    float best = -INFINITY;
+    int bi = 0x7fffffff;
+    for (int v = tid; v < V; v += 256) {
+        const float x = lg[v];
+        if (bi == 0x7fffffff || x > best) {
+            best = x;
+            bi = v;
+        }
+    }
+    const int r = block_argmax256(best, bi, sv, si);
+    if (tid == 0) next[b] = r;
+}
+
+// Classifier-free guidance over row pairs (MuScriptor model card: optional
+// CFG; the rule is the usual guidance of logits): workgroup i forms
+// g = c + (cfg - 1) (c - u) from conditional row i and its unconditional
+// partner, row pairs + i, as a binary64 difference, product and sum rounded
+// to binary32 (never fused), stores g when `guided` is given, and writes the
+// argmax of g to next[i] and, when `token_pair` is given, to both rows of the
+// pair there.
+__global__ __launch_bounds__(256) void k_cfg_combine(const float* __restrict__ logits, int pairs, int V, float cfg,
+                                                     float* __restrict__ guided, int64_t* __restrict__ next,
+                                                     int64_t* __restrict__ token_pair) {
+#pragma clang fp contract(off)
+    __shared__ float sv[256];
+    __shared__ int si[256];
+    const int i = blockIdx.x, tid = threadIdx.x;
+    const float* c = logits + (size_t)i * V;
+    const float* u = logits + (size_t)(pairs + i) * V;
+    const double w = (double)cfg - 1.0;
+    float best = -INFINITY;
+    int bi = 0x7fffffff;
+    for (int v = tid; v < V; v += 256) {
+        const double cv = (double)c[v];
+        const double diff = cv - (double)u[v];
+        const double step = w * diff;
+        const float g = (float)(cv + step);
+        if (guided) guided[(size_t)i * V + v] = g;
+        if (bi == 0x7fffffff || g > best) {
+            best = g;
+            bi = v;
+        }
+    }
+    const int r = block_argmax256(best, bi, sv, si);
+    if (tid == 0) {
+        next[i] = r;
+        if (token_pair) {
+            token_pair[i] = r;
+            token_pair[pairs + i] = r;
+        }
+    }
 }
 
 // ---------------------------------------------------------------- debug dequant
@@ -1464,18 +1511,23 @@ hipError_t launch_w4_matmul(const float* x, int ldx, int M, const Int4Mat& w, co
     EpiArgs ep{};
     ep.epi = epi;
     if (qkv) ep.qkv = *qkv;
-    if (!force_gemm && M >= 1 && M <= GV_M) {
+    const int per = (epi == EPI_QKV && qkv) ? qkv->rows_per_seq : 1;
+    if (!force_gemm && gemv_takes_rows(M, per)) {
         if (ln_g && w.K > GV_MAXSPAN) return hipErrorInvalidValue;
         if (ap.part && (ln_g || ap.H * 64 != w.K)) return hipErrorInvalidValue;
+        // rows in slices of whole sequences, at most GV_M rows each; every
+        // slice is one launch (the weights it re-reads come from the caches)
+        const int slice = GV_M / per * per;
+        const int ms0 = std::min(M, slice);
         int ksplit, kspan;
         // merged partials: whole heads (64 columns) per k split
         plan_gemv(w.N, w.K, ln_g ? EPI_STORE : epi, ap.part ? 64 : 32, &ksplit, &kspan);
         // activation rows (stride span + 4); merged partials also need their
-        // weights [M][heads][splits]; the A8 form adds the INT8 codes
+        // weights [rows][heads][splits]; the A8 form adds the INT8 codes
         // [GV_M][span] and their scales [span / 32][GV_M]
         const int span = std::min(kspan, GV_MAXSPAN);
-        const size_t wts = ap.part ? (size_t)M * (span / 64) * ap.nsplit : 0;
-        if (ap.part && (span % 64 || (int)(M * (span / 64)) > 256)) return hipErrorInvalidValue;
+        const size_t wts = ap.part ? (size_t)ms0 * (span / 64) * ap.nsplit : 0;
+        if (ap.part && (span % 64 || (int)(ms0 * (span / 64)) > 256)) return hipErrorInvalidValue;
         size_t lds = sizeof(float) * ((size_t)(span + 4) * GV_M + wts);
         if (a8) lds = sizeof(float) * ((size_t)(span + 4) * GV_M + ((wts + 3) & ~(size_t)3)) + (size_t)GV_M * span +
                       sizeof(float) * (size_t)(span / 32) * GV_M;
@@ -1494,11 +1546,22 @@ hipError_t launch_w4_matmul(const float* x, int ldx, int M, const Int4Mat& w, co
         }
         const dim3 grid((w.N + 15) / 16, ksplit);
         if (!w.qt || (w.fmt == WF_INT4 && !w.st)) return hipErrorInvalidValue;  // needs the GEMV tiling
-        const GemvArgs ga{x, ldx, M, w.K, kspan, ln_g, ln_b, eps, ap.part, ap.H, ap.nsplit, w.qt, w.st, w.N, y, ldy, ep};
-        if (w.fmt == WF_F16) gemv_launch<WF_F16, false>(ng, grid, lds, st, ga);
-        else if (w.fmt == WF_F32) gemv_launch<WF_F32, false>(ng, grid, lds, st, ga);
-        else if (a8) gemv_launch<WF_INT4, true>(ng, grid, lds, st, ga);
-        else gemv_launch<WF_INT4, false>(ng, grid, lds, st, ga);
+        for (int r0 = 0; r0 < M; r0 += slice) {
+            const int ms = std::min(slice, M - r0);
+            EpiArgs es = ep;
+            if (epi == EPI_QKV) {
+                es.qkv.q += (size_t)r0 * es.qkv.d;
+                es.qkv.b0 += r0 / per;
+            }
+            const float* xs = x ? x + (size_t)r0 * ldx : nullptr;
+            float* ys = y ? y + (size_t)r0 * ldy : nullptr;
+            const float* ps = ap.part ? ap.part + (size_t)r0 * ap.H * ap.nsplit * PART : nullptr;
+            const GemvArgs ga{xs, ldx, ms, w.K, kspan, ln_g, ln_b, eps, ps, ap.H, ap.nsplit, w.qt, w.st, w.N, ys, ldy, es};
+            if (w.fmt == WF_F16) gemv_launch<WF_F16, false>(ng, grid, lds, st, ga);
+            else if (w.fmt == WF_F32) gemv_launch<WF_F32, false>(ng, grid, lds, st, ga);
+            else if (a8) gemv_launch<WF_INT4, true>(ng, grid, lds, st, ga);
+            else gemv_launch<WF_INT4, false>(ng, grid, lds, st, ga);
+        }
         return hipGetLastError();
     }
     if (ln_g || ap.part) return hipErrorInvalidValue;  // the GEMM path takes plain rows
@@ -1550,7 +1613,10 @@ hipError_t launch_w4_matmul(const float* x, int ldx, int M, const Int4Mat& w, co
     return hipGetLastError();
 }
 
-bool gemv_fuses_layernorm(int M, int K) { return M >= 1 && M <= GV_M && K <= GV_MAXSPAN; }
+bool gemv_takes_rows(int M, int rows_per_seq) {
+    return M >= 1 && M <= kGemvRowsMax && rows_per_seq >= 1 && rows_per_seq <= GV_M;
+}
+bool gemv_fuses_layernorm(int M, int K) { return gemv_takes_rows(M, 1) && K <= GV_MAXSPAN; }
 
 hipError_t launch_attn_decode(const float* q, const float* kc, const float* vc, int layer, int B,
                               int H, int t_cap, const SeqPos& T, float* part, int nsplit, int chunk,
@@ -1594,6 +1660,12 @@ hipError_t launch_lm_head(const float* z, int B, const float* w, int V, int d, f
 
 hipError_t launch_argmax(const float* logits, int B, int V, int64_t* next, hipStream_t st) {
     hipLaunchKernelGGL(k_argmax, dim3(B), dim3(256), 0, st, logits, V, next);
+    return hipGetLastError();
+}
+
+hipError_t launch_cfg_combine(const float* logits, int pairs, int V, float cfg, float* guided, int64_t* next,
+                              int64_t* token_pair, hipStream_t st) {
+    hipLaunchKernelGGL(k_cfg_combine, dim3(pairs), dim3(256), 0, st, logits, pairs, V, cfg, guided, next, token_pair);
     return hipGetLastError();
 }
 

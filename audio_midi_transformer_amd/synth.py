@@ -161,6 +161,21 @@ def workload_prefix(wl: Workload, batch: int | None = None) -> np.ndarray:
                      for b in range(b_n)])
 
 
+def cfg_pair_prefix(wl: Workload, pairs: int | None = None, class_rows: int = 2) -> np.ndarray:
+    """Prefixes of conditional/unconditional pairs, [2 Np, P, d]: rows
+    0 .. Np-1 are workload_prefix; partner Np + i repeats row i's prefix and
+    redraws its last `class_rows` rows (the conditioner's prefix ends with
+    its class rows) from seed prefix_seed_base + 10000 + i."""
+    n = wl.batch if pairs is None else pairs
+    cond = workload_prefix(wl, n)
+    uncond = cond.copy()
+    k = min(class_rows, wl.prefix_len)
+    for i in range(n):
+        if k:
+            uncond[i, -k:] = prefix_rows(wl.shape, wl.prefix_seed_base + 10000 + i, k)
+    return np.concatenate([cond, uncond])
+
+
 def workload_tokens(wl: Workload, batch: int | None = None) -> np.ndarray:
     """Prompt token ids [B, S] (int64), uniform over the vocabulary."""
     b_n = wl.batch if batch is None else batch

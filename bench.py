@@ -89,20 +89,26 @@ def traffic_from_profiles(kernel: str, workload_key: str, variant: str = ""):
 
 
 def cpu_baseline(wl, weights, prefix_np, tokens_np, max_steps: int = 8, w4a8: bool = False,
-                 dense=None):
+                 dense=None, cfg=None):
     """The CPU oracle as it stands, on this host, on a bounded sample of the
-    workload: its prefill, then `max_steps` greedy decode steps."""
+    workload: its prefill, then `max_steps` greedy decode steps (with `cfg`,
+    of the 2B pair rows, each followed by the oracle's guidance)."""
     import oracle
     cores = len(os.sched_getaffinity(0))
     cores = min(cores, int(os.environ.get("OMP_NUM_THREADS", cores)))
     os.environ["OMP_NUM_THREADS"] = str(cores)
-    m = oracle.OracleModel.from_weights(weights, batch=wl.batch, t_cap=wl.t_cap, w4a8=w4a8, dense=dense)
+    rows = wl.batch * (2 if cfg is not None else 1)
+    m = oracle.OracleModel.from_weights(weights, batch=rows, t_cap=wl.t_cap, w4a8=w4a8, dense=dense)
+
+    def pick(lg, nxt):
+        return np.concatenate([oracle.cfg_combine(lg, cfg)[1]] * 2) if cfg is not None else nxt
+
     t0 = time.perf_counter()
-    _, nxt = m.forward(tokens=tokens_np, prefix=prefix_np)
+    nxt = pick(*m.forward(tokens=tokens_np, prefix=prefix_np))
     t1 = time.perf_counter()
     n = min(max_steps, wl.decode_steps)
     for _ in range(n):
-        _, nxt = m.forward(tokens=nxt.reshape(wl.batch, 1))
+        nxt = pick(*m.forward(tokens=nxt.reshape(rows, 1)))
     t2 = time.perf_counter()
     m.close()
     return {
@@ -112,7 +118,8 @@ def cpu_baseline(wl, weights, prefix_np, tokens_np, max_steps: int = 8, w4a8: bo
         "kind": "oracle",
         "sample": (f"oracle prefill of {wl.prefix_len + wl.n_tokens} rows "
                    f"({(t1 - t0) * 1000.0:.0f} ms) then {n} greedy decode steps of the same "
-                   f"workload, B={wl.batch}; value = mean ms per decode step"),
+                   f"workload, B={rows}{' (CFG pairs)' if cfg is not None else ''}; "
+                   f"value = mean ms per decode step"),
         "prefill_ms": (t1 - t0) * 1000.0,
     }
 
@@ -178,6 +185,9 @@ def main() -> int:
                     help="the W4A8 variant: INT8 activation codes per row and group of 32, INT32 group sums")
     ap.add_argument("--weights", choices=["int4", "f16", "f32"], default="int4",
                     help="projection weights: INT4 group-32 (default) or the dense binary16 / binary32 variants")
+    ap.add_argument("--cfg", type=float, default=None, metavar="COEF",
+                    help="classifier-free guidance: each of the workload's sequences becomes a "
+                         "conditional/unconditional pair (2B rows), the guided argmax is fed to both")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="before the bench, copy a buffer of this many MiB device-to-device three "
                          "times (a plain copy of known size, to scale HBM byte counters)")
@@ -228,6 +238,13 @@ def main() -> int:
     weights = synth.model_weights(shape, wl.model_seed)
     prefix_np = synth.workload_prefix(wl) if wl.prefix_len else None
     tokens_np = synth.workload_tokens(wl) if wl.n_tokens else None
+    pairs = None
+    if args.cfg is not None:
+        # each sequence becomes a conditional/unconditional pair of rows
+        pairs = B
+        B = 2 * B
+        prefix_np = synth.cfg_pair_prefix(wl) if wl.prefix_len else None
+        tokens_np = np.concatenate([tokens_np] * 2) if tokens_np is not None else None
     flags = {"": 0, "a8": binding.MT_FLAG_W4A8, "f16": binding.MT_FLAG_DENSE_F16,
              "f32": binding.MT_FLAG_DENSE_F32}[variant]
     dec = binding.Decoder(weights, batch=B, t_cap=wl.t_cap, flags=flags)
@@ -241,12 +258,25 @@ def main() -> int:
     logits = torch.empty((B, shape.vocab), dtype=torch.float32, device=dev)
     nxt = [torch.empty((B,), dtype=torch.int64, device=dev) for _ in range(2)]
     stream = torch.cuda.current_stream()
+    if pairs is not None:
+        guided = torch.empty((pairs, shape.vocab), dtype=torch.float32, device=dev)
+        picked = torch.empty((pairs,), dtype=torch.int64, device=dev)
+        row_next = torch.empty((B,), dtype=torch.int64, device=dev)
+
+    def call(fn, *a, out):
+        # one decoder call; with CFG its logits are guided and the guided
+        # argmax becomes the next token of both rows of every pair
+        if pairs is None:
+            fn(*a, logits, out)
+        else:
+            fn(*a, logits, row_next)
+            binding.cfg_combine(logits, args.cfg, guided=guided, next=picked, token_pair=out, stream=stream)
 
     def one_pass(ev=None):
         dec.reset()
         if ev is not None:
             ev["p0"].record(stream)
-        dec.prefill(tokens, prefix, logits, nxt[0])
+        call(dec.prefill, tokens, prefix, out=nxt[0])
         if ev is not None:
             ev["p1"].record(stream)
         for k in range(n_dec):
@@ -254,7 +284,7 @@ def main() -> int:
                 ev["s0"].record(stream)
             if ev is not None and "per" in ev:
                 ev["per"][k][0].record(stream)
-            dec.decode_step(nxt[k & 1], logits, nxt[(k + 1) & 1])
+            call(dec.decode_step, nxt[k & 1], out=nxt[(k + 1) & 1])
             if ev is not None and "per" in ev:
                 ev["per"][k][1].record(stream)
         if ev is not None:
@@ -283,7 +313,10 @@ def main() -> int:
     n_steady = n_dec - STEADY_FROM
     ms_tok = steady_ms / n_steady
     wbytes = WEIGHT_BYTES[args.weights]
-    launch_bytes = np.array([step_bytes(shape, B, R0 + k + 1, wbytes) for k in range(STEADY_FROM, n_dec)])
+    # with CFG the guidance reads the 2Np logit rows and writes Np guided rows
+    cfg_bytes = 12.0 * pairs * shape.vocab + 24.0 * pairs if pairs is not None else 0.0
+    launch_bytes = np.array([step_bytes(shape, B, R0 + k + 1, wbytes) + cfg_bytes
+                             for k in range(STEADY_FROM, n_dec)])
     gbps = float(launch_bytes.sum()) / (steady_ms * 1e-3) / 1e9
     step_ms = np.concatenate([np.array([a.elapsed_time(b) for a, b in e["per"]])[STEADY_FROM:] for e in evs])
     kernel_name = "mt_decode_step_persistent" if persistent else "decode_step_kernels"
@@ -299,6 +332,9 @@ def main() -> int:
     copy_gbps = measure_copy_peak(torch)
 
     metric = METRIC if wl.key == "2" else f"decode ms/token + achieved HBM GB/s, workload {wl.key}"
+    if pairs is not None:
+        metric = (f"decode ms/token + achieved HBM GB/s, workload {wl.key} as {pairs} CFG pair(s) "
+                  f"(coefficient {args.cfg:g})")
     if args.w4a8:
         metric += " (W4A8 variant)"
     elif args.weights != "int4":
@@ -323,8 +359,10 @@ def main() -> int:
                    "d_model": shape.d_model, "heads": shape.n_heads, "d_ff": shape.d_ff,
                    "vocab": shape.vocab, "batch": B, "prefix_rows": wl.prefix_len,
                    "prompt_tokens": wl.n_tokens, "decode_steps": n_dec, "t_cap": wl.t_cap,
-                   "decode_path": "persistent" if persistent else "kernels"},
-        "decode_tokens_per_s": round(B * 1000.0 / ms_tok, 1),
+                   "decode_path": "persistent" if persistent else "kernels",
+                   **({"cfg": args.cfg, "cfg_pairs": pairs} if pairs is not None else {})},
+        # guided tokens with CFG (one per pair), else one per sequence
+        "decode_tokens_per_s": round((pairs if pairs is not None else B) * 1000.0 / ms_tok, 1),
         "decode_ms_per_token": {"mean": round(float(step_ms.mean()), 5),
                                 "median": round(float(np.median(step_ms)), 5),
                                 "p90": round(float(np.percentile(step_ms, 90)), 5)},
@@ -346,7 +384,8 @@ def main() -> int:
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(wl, weights, prefix_np, tokens_np, w4a8=args.w4a8,
-                                           dense=None if args.weights == "int4" else args.weights)
+                                           dense=None if args.weights == "int4" else args.weights,
+                                           cfg=args.cfg)
     dec.close()
     print(json.dumps(out), flush=True)
     return 0

@@ -199,6 +199,33 @@ int mt_reset_seq(mt_model* m, int32_t b);
 /* Current position T_b of sequence b (host pointer out). */
 int mt_position_seq(const mt_model* m, int32_t b, int32_t* t_past);
 
+/* ---- Classifier-free guidance over row pairs. ----
+ * The MuScriptor model card offers optional CFG; the paper's scaling table
+ * is quoted at CFG = 2; the conditioner's instrument input has a class id
+ * that stands for no condition ("unifolia/muscriptor-small-onnx",
+ * conditioner inputs); released models are run with the coefficient at 1.  The combining
+ * rule is not on the pages; this library takes the usual guidance of logits.
+ * A batch of 2 Np sequences holds Np pairs: sequence i (i < Np) is
+ * conditional, sequence Np + i its unconditional partner (its prefix made
+ * with the no-condition class, same length).  Both rows of a pair are fed
+ * the same tokens.
+ *
+ * From the [2 Np, V] logits of mt_prefill or mt_decode_step:
+ *   guided[i, v] = c + (cfg - 1) * (c - u),  c = logits[i, v], u = logits[Np + i, v]
+ * (= u + cfg (c - u); cfg = 1 returns c bit for bit), the difference,
+ * product and sum taken in binary64 and rounded once to FP32;
+ *   next[i] = argmax_v guided[i, v], lowest index on ties;
+ *   token_pair[i] = token_pair[Np + i] = next[i]   (when token_pair != NULL),
+ * which is the `token` argument of the pair batch's next mt_decode_step.
+ * All pointers are device memory on the stream's device: logits [2 Np, V]
+ * FP32 (read only); guided [Np, V] FP32 or NULL (not stored); next [Np]
+ * int64; token_pair [2 Np] int64 or NULL.  One launch, no allocation, no
+ * synchronisation; needs no model.
+ * Errors: NULL logits or next, Np < 1, V < 1 or a non-finite cfg ->
+ * MT_ERR_INVALID_ARG (nothing launched); launch failure -> MT_ERR_HIP. */
+int mt_cfg_combine(const float* logits, int32_t pairs, int32_t V, float cfg, float* guided, int64_t* next,
+                   int64_t* token_pair, void* stream);
+
 /* Device pointers to the cache, [L, B, t_cap, H, 64] FP32 each.  The cache
  * is updated in place: past and present are the same buffer. */
 int mt_kv_cache(mt_model* m, const float** k, const float** v);
@@ -231,7 +258,8 @@ const char* mt_last_error(void);
 int mt_debug_dequant(mt_model* m, int32_t layer, int32_t proj, float* out, void* stream);
 
 /* y [M, N] = x [M, K] . dequant(W)^T for one projection, on the decode
- * GEMV kernel (M <= 8) or the prefill GEMM kernel (M > 8). */
+ * GEMV kernel (M <= 64, in launches of 8 rows) or the prefill GEMM kernel
+ * (M > 64, or always when bit 8 of `proj` is set). */
 int mt_debug_matmul(mt_model* m, int32_t layer, int32_t proj, const float* x, int32_t M, float* y,
                     void* stream);
 

@@ -47,8 +47,8 @@
  *
  * Classifier-free guidance over row pairs (oracle_cfg_combine): the model
  * card offers optional CFG, the paper's scaling table is quoted at CFG = 2,
- * the conditioner has an "unconditional" instrument class, and released
- * models are run with the coefficient at 1; the combining rule itself is not
+ * the conditioner's instrument input has a class id for no condition, and
+ * released models are run with the coefficient at 1; the combining rule itself is not
  * on the pages.  Reading: the usual guidance of logits, cond + (cfg - 1) *
  * (cond - uncond) (= uncond + cfg * (cond - uncond); cfg = 1 is the plain
  * conditional model), the next token being the argmax of the guided row.

@@ -103,3 +103,19 @@ def test_calls_reject_null_model():
     assert lib.mt_position(None, ctypes.byref(t)) == binding.MT_ERR_INVALID_ARG
     assert lib.mt_set_decode_path(None, 0) == binding.MT_ERR_INVALID_ARG
     lib.mt_destroy(None)  # no-op
+
+
+def test_cfg_combine_rejects_bad_arguments_before_launch():
+    """Argument checks of mt_cfg_combine run on the host (the pointers are
+    never dereferenced: every call here fails before a launch)."""
+    lib = binding.lib()
+    fake = ctypes.c_void_p(0x1000)
+    bad = binding.MT_ERR_INVALID_ARG
+    assert lib.mt_cfg_combine(None, 1, 8, 2.0, None, fake, None, None) == bad
+    assert lib.mt_cfg_combine(fake, 1, 8, 2.0, None, None, None, None) == bad
+    assert lib.mt_cfg_combine(fake, 0, 8, 2.0, None, fake, None, None) == bad
+    assert lib.mt_cfg_combine(fake, 1, 0, 2.0, None, fake, None, None) == bad
+    assert lib.mt_cfg_combine(fake, -2, 8, 2.0, None, fake, None, None) == bad
+    for cfg in (float("inf"), float("-inf"), float("nan")):
+        assert lib.mt_cfg_combine(fake, 1, 8, cfg, None, fake, None, None) == bad
+    assert b"mt_cfg_combine" in lib.mt_last_error()

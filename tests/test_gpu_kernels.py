@@ -55,8 +55,8 @@ def _matmul_bound(x, q, s):
     return K * 2.0 ** -24 * (np.abs(x.astype(np.float64)) @ mag.T) + 1e-30
 
 
-@pytest.mark.parametrize("M,force_gemm", [(1, False), (3, False), (8, False), (1, True), (13, True),
-                                          (64, True), (130, True)])
+@pytest.mark.parametrize("M,force_gemm", [(1, False), (3, False), (8, False), (13, False), (16, False),
+                                          (64, False), (1, True), (13, True), (64, True), (130, True)])
 def test_matmul_vs_oracle(one_layer, oracle_mod, M, force_gemm):
     shape, w, dec = one_layer
     rng = np.random.default_rng(M)
@@ -129,6 +129,21 @@ def test_model_prefix_and_tokens_then_decode(oracle_mod, path):
     prefix = rng.standard_normal((B, P, shape.d_model)).astype(np.float32)
     tokens = rng.integers(0, shape.vocab, size=(B, S))
     _run_pair(oracle_mod, shape, w, B, 100, prefix, tokens, steps=20, path=path)
+
+
+@pytest.mark.parametrize("B,P,S", [(20, 6, 3), (5, 0, 3), (17, 2, 0)])
+def test_model_gemv_slices(oracle_mod, B, P, S):
+    """Batches past 8 rows run the GEMV in launches of 8 whole sequences:
+    B = 20 decodes in slices 8 + 8 + 4 (and prefills 9 rows per sequence on
+    the GEMM); B = 5 with 3 prompt tokens prefills 15 rows in slices of two
+    sequences (6 + 6 + 3 rows, so the K/V scatter starts mid-batch); B = 17
+    decodes with a one-row tail slice."""
+    _dev()
+    shape, w = _tiny(oracle_mod)
+    rng = np.random.default_rng(B)
+    prefix = rng.standard_normal((B, P, shape.d_model)).astype(np.float32) if P else None
+    tokens = rng.integers(0, shape.vocab, size=(B, S)) if S else None
+    _run_pair(oracle_mod, shape, w, B, P + S + 12, prefix, tokens, steps=10)
 
 
 def test_model_tokens_only_small_width(oracle_mod):
