@@ -166,8 +166,9 @@ int run_layers(mt_model* m, float* x, float* a, float* q, float* att, float* h, 
             HIP_TRY(launch_w4_matmul(a, d, M, m->proj[l * 4 + 0], nullptr, nullptr, 0.f, nullptr, 0, EPI_QKV, &dst,
                                      false, st, nullptr, a8));
         }
-        if (decode && fuse_ln) {
-            // split-K attention; the O projection merges the partials
+        if (decode) {
+            // split-K attention; the O projection (GEMV) merges the partials,
+            // or a merge kernel writes attention rows for the GEMM
             SeqPos T{};
             int tmax = 0;
             for (int b = 0; b < c.batch; ++b) {
@@ -178,9 +179,15 @@ int run_layers(mt_model* m, float* x, float* a, float* q, float* att, float* h, 
             attn_split(c.batch, c.n_heads, tmax, &ns, &ch);
             if (ns > kMaxSplit) return fail(MT_ERR_INVALID_ARG, "decode attention: %d splits exceed %d", ns, kMaxSplit);
             HIP_TRY(launch_attn_decode(q, m->kc, m->vc, l, c.batch, c.n_heads, c.t_cap, T, m->part, ns, ch, st));
-            const AttnParts ap{m->part, c.n_heads, ns};
-            HIP_TRY(launch_w4_matmul(nullptr, d, M, m->proj[l * 4 + 1], nullptr, nullptr, 0.f, x, d, EPI_RESID,
-                                     nullptr, false, st, &ap, a8));
+            if (fuse_ln) {
+                const AttnParts ap{m->part, c.n_heads, ns};
+                HIP_TRY(launch_w4_matmul(nullptr, d, M, m->proj[l * 4 + 1], nullptr, nullptr, 0.f, x, d, EPI_RESID,
+                                         nullptr, false, st, &ap, a8));
+            } else {
+                HIP_TRY(launch_attn_merge(m->part, c.batch, c.n_heads, ns, att, st));
+                HIP_TRY(launch_w4_matmul(att, d, M, m->proj[l * 4 + 1], nullptr, nullptr, 0.f, x, d, EPI_RESID,
+                                         nullptr, false, st, nullptr, a8));
+            }
         } else {
             HIP_TRY(launch_attn_prefill(q, m->kc, m->vc, l, c.batch, b0, nb, c.n_heads, c.t_cap, m->pos, R, att, st));
             HIP_TRY(launch_w4_matmul(att, d, M, m->proj[l * 4 + 1], nullptr, nullptr, 0.f, x, d, EPI_RESID, nullptr,

@@ -74,8 +74,9 @@ hipError_t launch_w4_matmul(const float* x, int ldx, int M, const Int4Mat& w, co
                             const float* ln_b, float eps, float* y, int ldy, Epilogue epi, const QkvDest* qkv,
                             bool force_gemm, hipStream_t st, const AttnParts* parts = nullptr, bool a8 = false);
 // The GEMV takes M rows (sequences of rows_per_seq rows each) in slices of
-// at most 8 rows; more rows than kGemvRowsMax go to the GEMM.
-constexpr int kGemvRowsMax = 64;
+// at most 8 rows; more rows than kGemvRowsMax go to the GEMM (a decode
+// batch then merges its attention partials into rows first).
+constexpr int kGemvRowsMax = 16;
 bool gemv_takes_rows(int M, int rows_per_seq);
 bool gemv_fuses_layernorm(int M, int K);
 // Writes the split-K partials only; the O projection merges them.  Sequence
@@ -83,6 +84,8 @@ bool gemv_fuses_layernorm(int M, int K);
 hipError_t launch_attn_decode(const float* q, const float* kc, const float* vc, int layer, int B,
                               int H, int t_cap, const SeqPos& T, float* part, int nsplit, int chunk,
                               hipStream_t st);
+// Attention rows out [B, H * 64] merged from the partials of launch_attn_decode.
+hipError_t launch_attn_merge(const float* part, int B, int H, int nsplit, float* out, hipStream_t st);
 // Causal attention of R new rows of nb sequences b0 .. b0+nb-1 (of Btot in
 // the cache); sequence b0 + b's rows sit at positions t0.t[b0 + b] + i.
 hipError_t launch_attn_prefill(const float* q, const float* kc, const float* vc, int layer, int Btot, int b0,

@@ -901,6 +901,27 @@ __global__ __launch_bounds__(256) void k_attn_decode(const float* __restrict__ q
     }
 }
 
+// Merge of the decode attention's split-K partials into attention rows, for
+// batches whose O projection runs on the GEMM: workgroup (h, b), lane j
+// forms out[b, 64 h + j] = sum_s e^(m_s - M) acc_s[j] / sum_s e^(m_s - M) l_s
+// (M the largest m_s; splits with no keys have m_s = -inf and weigh 0), the
+// same weights as the GEMV's merged-partials staging.
+__global__ __launch_bounds__(64) void k_attn_merge(const float* __restrict__ part, int H, int ns,
+                                                   float* __restrict__ out) {
+    const int h = blockIdx.x, b = blockIdx.y, j = threadIdx.x;
+    const float* pp = part + (size_t)(b * H + h) * ns * PART;
+    float Mx = -INFINITY;
+    for (int sp = 0; sp < ns; ++sp) Mx = fmaxf(Mx, pp[sp * PART]);
+    float L = 0.f, acc = 0.f;
+    for (int sp = 0; sp < ns; ++sp) {
+        const float m = pp[sp * PART];
+        const float e = m == -INFINITY ? 0.f : expf(m - Mx);
+        L = fmaf(e, pp[sp * PART + 1], L);
+        acc = fmaf(e, pp[sp * PART + PART_ACC + j], acc);
+    }
+    out[(size_t)b * H * 64 + h * 64 + j] = acc * (1.0f / L);
+}
+
 // ---------------------------------------------------------------- prefill attention
 
 // Causal attention of R new rows per sequence (positions t0 .. t0+R-1) over
@@ -1565,14 +1586,28 @@ hipError_t launch_w4_matmul(const float* x, int ldx, int M, const Int4Mat& w, co
         return hipGetLastError();
     }
     if (ln_g || ap.part) return hipErrorInvalidValue;  // the GEMM path takes plain rows
-    // one workgroup per tile over all of K: results do not depend on the
-    // order of atomic additions (prefill is bit-reproducible).  32-row tiles
-    // when 64-row tiles would give fewer than two workgroups per CU.
-    const int ksplit = 1;
+    // 32-row tiles when 64-row tiles would give fewer than two workgroups
+    // per CU.  One workgroup per tile over all of K, so that results do not
+    // depend on the order of atomic additions (prefill is bit-reproducible),
+    // except with fewer than 128 tiles on a += epilogue (the O and FFN-down
+    // projections of a decode batch): then K is split over up to 8
+    // workgroups per tile and their products are added atomically, as the
+    // GEMV does.
     const int ntile = (w.N + GN - 1) / GN;
     const bool small = (long)ntile * ((M + 63) / 64) < 512;
     const int TM = small ? 32 : 64, GKs = small ? 128 : 64;
-    const dim3 grid(ntile, (M + TM - 1) / TM, ksplit);
+    const int mtile = (M + TM - 1) / TM;
+    const int stages = (w.K + GKs - 1) / GKs;
+    int ksplit = 1;
+    if (epi == EPI_RESID && !(a8 && w.fmt == WF_INT4) && (long)ntile * mtile < 128) {
+        const int want = std::min(8, std::max(1, 256 / (ntile * mtile)));
+        for (int c = std::min(want, stages); c >= 1; --c)
+            if (stages % c == 0) {
+                ksplit = c;
+                break;
+            }
+    }
+    const dim3 grid(ntile, mtile, ksplit);
     if (a8 && w.fmt == WF_INT4) {
         if (small)
             hipLaunchKernelGGL((k_gemm_w4a8<32, 128>), grid, dim3(256), 0, st, x, ldx, M, w.K, w.q, w.s, w.N, y, ldy,
@@ -1582,7 +1617,7 @@ hipError_t launch_w4_matmul(const float* x, int ldx, int M, const Int4Mat& w, co
                                ep);
         return hipGetLastError();
     }
-    const int kspan = (w.K + GKs - 1) / GKs * GKs;
+    const int kspan = stages / ksplit * GKs;
     static bool attr = false;
     if (!attr) {
         const void* f64[3] = {(const void*)k_gemm_w4<64, 64, WF_INT4>, (const void*)k_gemm_w4<64, 64, WF_F16>,
@@ -1660,6 +1695,12 @@ hipError_t launch_lm_head(const float* z, int B, const float* w, int V, int d, f
 
 hipError_t launch_argmax(const float* logits, int B, int V, int64_t* next, hipStream_t st) {
     hipLaunchKernelGGL(k_argmax, dim3(B), dim3(256), 0, st, logits, V, next);
+    return hipGetLastError();
+}
+
+hipError_t launch_attn_merge(const float* part, int B, int H, int nsplit, float* out, hipStream_t st) {
+    if (B < 1 || H < 1 || nsplit < 1) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_attn_merge, dim3(H, B), dim3(64), 0, st, part, H, nsplit, out);
     return hipGetLastError();
 }
 

@@ -258,8 +258,8 @@ const char* mt_last_error(void);
 int mt_debug_dequant(mt_model* m, int32_t layer, int32_t proj, float* out, void* stream);
 
 /* y [M, N] = x [M, K] . dequant(W)^T for one projection, on the decode
- * GEMV kernel (M <= 64, in launches of 8 rows) or the prefill GEMM kernel
- * (M > 64, or always when bit 8 of `proj` is set). */
+ * GEMV kernel (M <= 16, in launches of 8 rows) or the prefill GEMM kernel
+ * (M > 16, or always when bit 8 of `proj` is set). */
 int mt_debug_matmul(mt_model* m, int32_t layer, int32_t proj, const float* x, int32_t M, float* y,
                     void* stream);
 

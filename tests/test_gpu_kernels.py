@@ -56,7 +56,7 @@ def _matmul_bound(x, q, s):
 
 
 @pytest.mark.parametrize("M,force_gemm", [(1, False), (3, False), (8, False), (13, False), (16, False),
-                                          (64, False), (1, True), (13, True), (64, True), (130, True)])
+                                          (32, False), (1, True), (13, True), (64, True), (130, True)])
 def test_matmul_vs_oracle(one_layer, oracle_mod, M, force_gemm):
     shape, w, dec = one_layer
     rng = np.random.default_rng(M)
@@ -131,16 +131,29 @@ def test_model_prefix_and_tokens_then_decode(oracle_mod, path):
     _run_pair(oracle_mod, shape, w, B, 100, prefix, tokens, steps=20, path=path)
 
 
-@pytest.mark.parametrize("B,P,S", [(20, 6, 3), (5, 0, 3), (17, 2, 0)])
+@pytest.mark.parametrize("B,P,S", [(16, 6, 3), (5, 0, 3), (13, 2, 0)])
 def test_model_gemv_slices(oracle_mod, B, P, S):
-    """Batches past 8 rows run the GEMV in launches of 8 whole sequences:
-    B = 20 decodes in slices 8 + 8 + 4 (and prefills 9 rows per sequence on
-    the GEMM); B = 5 with 3 prompt tokens prefills 15 rows in slices of two
-    sequences (6 + 6 + 3 rows, so the K/V scatter starts mid-batch); B = 17
-    decodes with a one-row tail slice."""
+    """Batches of 9 to 16 rows run the GEMV in launches of 8 whole
+    sequences: B = 16 decodes in slices 8 + 8 (and prefills 9 rows per
+    sequence on the GEMM); B = 5 with 3 prompt tokens prefills 15 rows in
+    slices of two sequences (6 + 6 + 3 rows, so the K/V scatter starts
+    mid-batch); B = 13 decodes with a 5-row tail slice."""
     _dev()
     shape, w = _tiny(oracle_mod)
     rng = np.random.default_rng(B)
+    prefix = rng.standard_normal((B, P, shape.d_model)).astype(np.float32) if P else None
+    tokens = rng.integers(0, shape.vocab, size=(B, S)) if S else None
+    _run_pair(oracle_mod, shape, w, B, P + S + 12, prefix, tokens, steps=10)
+
+
+@pytest.mark.parametrize("B,P,S", [(20, 6, 3), (33, 2, 0)])
+def test_model_gemm_decode(oracle_mod, B, P, S):
+    """Past 16 rows a decode step runs its projections on the GEMM (O and
+    FFN-down with K split over several workgroups) and merges the split-K
+    attention partials into rows with their own kernel."""
+    _dev()
+    shape, w = _tiny(oracle_mod)
+    rng = np.random.default_rng(B + 100)
     prefix = rng.standard_normal((B, P, shape.d_model)).astype(np.float32) if P else None
     tokens = rng.integers(0, shape.vocab, size=(B, S)) if S else None
     _run_pair(oracle_mod, shape, w, B, P + S + 12, prefix, tokens, steps=10)

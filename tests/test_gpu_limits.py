@@ -1,5 +1,6 @@
 """GPU parity at the configuration limits, against the CPU oracle through the
-C ABI: the largest batch (64 sequences), the largest width (d_model 2048,
+C ABI: the largest batch (64 sequences: projections on the GEMM, the decode
+attention's partials merged into rows by their own kernel), the largest width (d_model 2048,
 32 heads, FFN 8192: the LayerNorm GEMV with 16 groups per wave and a
 multi-chunk FFN-down), and the largest cache (16384 positions: the decode
 attention at its 64-split limit), filled to the last slot and then refused."""
@@ -59,6 +60,22 @@ def test_batch_64(oracle_mod):
     om.close()
     dec.close()
     print(f"B=64: max |delta logits| {worst:.3g}")
+
+
+def test_batch_40_medium_width(oracle_mod):
+    """40 sequences at the medium width and vocabulary: the decode projections
+    run on the GEMM with K split over several workgroups for the O and
+    FFN-down products, the attention partials merged into rows first."""
+    _dev()
+    shape = synth.tiny_shape(n_layers=1, d_model=1024, n_heads=16, d_ff=4096, vocab=1393)
+    w = synth.model_weights(shape, 44)
+    rng = np.random.default_rng(44)
+    B = 40
+    prefix = rng.standard_normal((B, 12, shape.d_model)).astype(np.float32)
+    om, dec, _, worst = _run(oracle_mod, w, B, 24, prefix, None, 4, TOL["medium"])
+    om.close()
+    dec.close()
+    print(f"B=40 medium width: max |delta logits| {worst:.3g}")
 
 
 @pytest.mark.parametrize("B", [1, 3])
