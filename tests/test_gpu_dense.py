@@ -133,3 +133,14 @@ def test_dense_model_batch8_medium_width(oracle_mod, fmt):
     w = synth.model_weights(shape, 10)
     prefix = np.random.default_rng(7).standard_normal((8, 33, 1024)).astype(np.float32)
     _run_pair(oracle_mod, w, fmt, 8, 48, prefix, None, 6, TOL["medium"])
+
+
+@pytest.mark.parametrize("fmt,B", [("f16", 12), ("f32", 24)])
+def test_dense_model_large_batches(oracle_mod, fmt, B):
+    """Dense weights past 8 rows: GEMV slices at B = 12; at B = 24 the GEMM,
+    K split for the O and FFN-down products, and merged attention rows."""
+    _dev()
+    shape = synth.tiny_shape(n_layers=2, d_model=128, n_heads=2, d_ff=512, vocab=97)
+    w = synth.model_weights(shape, 80 + B)
+    prefix = np.random.default_rng(B).standard_normal((B, 9, shape.d_model)).astype(np.float32)
+    _run_pair(oracle_mod, w, fmt, B, 24, prefix, None, 8, TOL["tiny"])

@@ -28,6 +28,7 @@ def _t(a, dtype=None):
 
 @pytest.fixture(scope="module", params=["small", "medium", "large"])
 def one_layer(request, oracle_mod):
+    _dev()
     base = {"small": synth.SMALL, "medium": synth.MEDIUM, "large": synth.LARGE}[request.param]
     shape = synth.ModelShape(base.name, 1, base.d_model, base.n_heads, base.d_ff)
     w = synth.model_weights(shape, 77)

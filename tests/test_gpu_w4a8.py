@@ -41,6 +41,7 @@ def _t(a):
 
 @pytest.fixture(scope="module", params=["small", "medium", "large"])
 def one_layer_a8(request, oracle_mod):
+    _dev()
     base = {"small": synth.SMALL, "medium": synth.MEDIUM, "large": synth.LARGE}[request.param]
     shape = synth.ModelShape(base.name, 1, base.d_model, base.n_heads, base.d_ff)
     w = synth.model_weights(shape, 78)
@@ -130,6 +131,17 @@ def test_w4a8_model_batch8_medium_width(oracle_mod):
     w = synth.model_weights(shape, 8)
     prefix = np.random.default_rng(5).standard_normal((8, 33, 1024)).astype(np.float32)
     _run_pair(oracle_mod, w, 8, 48, prefix, None, steps=6)
+
+
+@pytest.mark.parametrize("B", [12, 24])
+def test_w4a8_model_large_batches(oracle_mod, B):
+    """B = 12 runs the W4A8 GEMV in two slices; B = 24 decodes on the W4A8
+    GEMM with the attention partials merged into rows first."""
+    _dev()
+    shape = synth.tiny_shape(n_layers=2, d_model=128, n_heads=2, d_ff=512, vocab=97)
+    w = synth.model_weights(shape, 70 + B)
+    prefix = np.random.default_rng(B).standard_normal((B, 9, shape.d_model)).astype(np.float32)
+    _run_pair(oracle_mod, w, B, 24, prefix, None, steps=8)
 
 
 @pytest.mark.parametrize("width", ["small", "medium", "large"])
