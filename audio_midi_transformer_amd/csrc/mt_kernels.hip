@@ -692,13 +692,15 @@ __global__ __launch_bounds__(256) void k_gemm_w4(const float* __restrict__ X, in
 // block, A = activation codes (lane l: row l % 16, k = 8 (l / 16) .. + 7),
 // B = 16 (u - 8) (lane l: weight row l % 16, same k), D[4 (l / 16) + r][l % 16];
 // the INT32 block is added to the FP32 result as I * s_a * s_w / 16.
+// blockIdx.z takes the kspan-column range of K whose results are added
+// atomically (+= epilogue only), as in the FP32 GEMM.
 constexpr int QS = 8;  // LDS row padding (bytes) of the code tiles
 
 template <int TM, int GK>
 __global__ __launch_bounds__(256) void k_gemm_w4a8(const float* __restrict__ X, int ldx, int M, int K,
                                                    const uint8_t* __restrict__ Wq,
                                                    const float* __restrict__ Ws, int N,
-                                                   float* __restrict__ Y, int ldy, EpiArgs ep) {
+                                                   float* __restrict__ Y, int ldy, EpiArgs ep, int kspan) {
     constexpr int MI = TM / 32;
     constexpr int NG = GK / 32;       // groups per stage
     constexpr int RS = GK + QS;       // code row stride (bytes)
@@ -710,6 +712,7 @@ __global__ __launch_bounds__(256) void k_gemm_w4a8(const float* __restrict__ X, 
     const int wm = wave >> 1, wn = wave & 1;
     const int m0 = blockIdx.y * TM, n0 = blockIdx.x * GN;
     const int G = K / 32;
+    const int kb = blockIdx.z * kspan, ke = min(K, kb + kspan);  // this workgroup's K range
     f32x4 acc[MI][2];
 #pragma unroll
     for (int i = 0; i < MI; ++i)
@@ -729,19 +732,19 @@ __global__ __launch_bounds__(256) void k_gemm_w4a8(const float* __restrict__ X, 
             const int idx = tid + e * 256;
             const int r = idx / (GK / 4), c = (idx % (GK / 4)) * 4;
             pa[e] = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (m0 + r < M && k0 + c < K) pa[e] = *reinterpret_cast<const float4*>(X + (size_t)(m0 + r) * ldx + k0 + c);
+            if (m0 + r < M && k0 + c < ke) pa[e] = *reinterpret_cast<const float4*>(X + (size_t)(m0 + r) * ldx + k0 + c);
         }
         const int c0 = k0 + wq * (GK / 4), g = c0 / 32;
-        const bool ok = n0 + wrow < N && c0 < K;
+        const bool ok = n0 + wrow < N && c0 < ke;
 #pragma unroll
         for (int i = 0; i < NW; ++i)
             pw[i] = ok ? *reinterpret_cast<const unsigned*>(Wq + (size_t)(n0 + wrow) * (K / 2) + c0 / 2 + 4 * i)
                        : 0x88888888u;
         ps = ok ? Ws[(size_t)(n0 + wrow) * G + g] : 0.f;
     };
-    load_stage(0);
-    for (int k0 = 0; k0 < K; k0 += GK) {
-        if (k0) __syncthreads();  // the previous stage has been multiplied
+    load_stage(kb);
+    for (int k0 = kb; k0 < ke; k0 += GK) {
+        if (k0 != kb) __syncthreads();  // the previous stage has been multiplied
         // activation codes: the 8 float4 of a (row, group) sit in 8
         // consecutive lanes; their maximum by DPP within the 8 lanes
 #pragma unroll
@@ -778,7 +781,7 @@ __global__ __launch_bounds__(256) void k_gemm_w4a8(const float* __restrict__ X, 
             if (((wq * (GK / 4)) & 31) == 0) Bs_s[(wq * (GK / 4)) >> 5][wrow] = ps * 0.0625f;
         }
         __syncthreads();
-        if (k0 + GK < K) load_stage(k0 + GK);
+        if (k0 + GK < ke) load_stage(k0 + GK);
         const int kq = lane >> 4, l16 = lane & 15;
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
@@ -812,7 +815,10 @@ __global__ __launch_bounds__(256) void k_gemm_w4a8(const float* __restrict__ X, 
             for (int r = 0; r < 4; ++r) {
                 const int m = m0 + wm * (TM / 2) + i * 16 + 4 * (lane >> 4) + r;
                 const int n = n0 + wn * 32 + j * 16 + (lane & 15);
-                if (m < M && n < N) epilogue(ep, Y, ldy, m, n, acc[i][j][r]);
+                if (m < M && n < N) {
+                    if (gridDim.z > 1) atomicAdd(Y + (size_t)m * ldy + n, acc[i][j][r]);
+                    else epilogue(ep, Y, ldy, m, n, acc[i][j][r]);
+                }
             }
 }
 
@@ -1599,7 +1605,7 @@ hipError_t launch_w4_matmul(const float* x, int ldx, int M, const Int4Mat& w, co
     const int mtile = (M + TM - 1) / TM;
     const int stages = (w.K + GKs - 1) / GKs;
     int ksplit = 1;
-    if (epi == EPI_RESID && !(a8 && w.fmt == WF_INT4) && (long)ntile * mtile < 128) {
+    if (epi == EPI_RESID && (long)ntile * mtile < 128) {
         const int want = std::min(8, std::max(1, 256 / (ntile * mtile)));
         for (int c = std::min(want, stages); c >= 1; --c)
             if (stages % c == 0) {
@@ -1611,10 +1617,10 @@ hipError_t launch_w4_matmul(const float* x, int ldx, int M, const Int4Mat& w, co
     if (a8 && w.fmt == WF_INT4) {
         if (small)
             hipLaunchKernelGGL((k_gemm_w4a8<32, 128>), grid, dim3(256), 0, st, x, ldx, M, w.K, w.q, w.s, w.N, y, ldy,
-                               ep);
+                               ep, stages / ksplit * GKs);
         else
             hipLaunchKernelGGL((k_gemm_w4a8<64, 64>), grid, dim3(256), 0, st, x, ldx, M, w.K, w.q, w.s, w.N, y, ldy,
-                               ep);
+                               ep, stages / ksplit * GKs);
         return hipGetLastError();
     }
     const int kspan = stages / ksplit * GKs;
