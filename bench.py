@@ -17,6 +17,7 @@ oracle timed on a bounded sample of the same workload on this host.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -185,6 +186,9 @@ def main() -> int:
                     help="the W4A8 variant: INT8 activation codes per row and group of 32, INT32 group sums")
     ap.add_argument("--weights", choices=["int4", "f16", "f32"], default="int4",
                     help="projection weights: INT4 group-32 (default) or the dense binary16 / binary32 variants")
+    ap.add_argument("--batch", type=int, default=None,
+                    help="run the workload with this many sequences instead of its own batch "
+                         "(each with its own seeded prefix)")
     ap.add_argument("--cfg", type=float, default=None, metavar="COEF",
                     help="classifier-free guidance: each of the workload's sequences becomes a "
                          "conditional/unconditional pair (2B rows), the guided argmax is fed to both")
@@ -220,6 +224,11 @@ def main() -> int:
         return 1
     torch.cuda.set_device(0)
     wl = synth.WORKLOADS[args.workload]
+    if args.batch is not None:
+        if not 1 <= args.batch <= 64:
+            print("--batch must be 1 .. 64", file=sys.stderr)
+            return 2
+        wl = dataclasses.replace(wl, batch=args.batch)
     shape, B = wl.shape, wl.batch
     n_dec = wl.decode_steps if args.decode_steps is None else args.decode_steps
     R0 = wl.prefix_len + wl.n_tokens
@@ -331,7 +340,9 @@ def main() -> int:
               for T in (505, 1024, 2048) if np.any(t_keys == T)}
     copy_gbps = measure_copy_peak(torch)
 
-    metric = METRIC if wl.key == "2" else f"decode ms/token + achieved HBM GB/s, workload {wl.key}"
+    metric = (METRIC if wl.key == "2" and args.batch is None
+              else f"decode ms/token + achieved HBM GB/s, workload {wl.key}"
+              + (f" at B={args.batch}" if args.batch is not None else ""))
     if pairs is not None:
         metric = (f"decode ms/token + achieved HBM GB/s, workload {wl.key} as {pairs} CFG pair(s) "
                   f"(coefficient {args.cfg:g})")
