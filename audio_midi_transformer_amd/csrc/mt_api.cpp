@@ -332,7 +332,7 @@ int mt_create(const mt_config* cfg, const mt_weights* w, int weights_on_device, 
         so += ns;
     }
     if (hipMemsetAsync(m->err, 0, 16, st)) return bail(fail(MT_ERR_HIP, "mt_create: clearing the error word failed"));
-    // second copy of the projections in the GEMV tiling (decode with B <= 8)
+    // second copy of the projections in the GEMV tiling (decode with B <= 16)
     size_t tbytes = 0, tfloats = 0;
     for (const Int4Mat& pm : m->proj) {
         tbytes += tiled_weight_bytes(pm);
