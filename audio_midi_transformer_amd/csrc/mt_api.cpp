@@ -431,19 +431,29 @@ int mt_decode_step(mt_model* m, const int64_t* token, float* logits, int64_t* ne
             return fail(MT_ERR_CACHE_FULL, "mt_decode_step: cache of sequence %d full at position %d (capacity %d)", b,
                         m->pos.t[b], c.t_cap);
     hipStream_t st = (hipStream_t)stream;
+    int tmax = 0;
+    for (int b = 0; b < c.batch; ++b) tmax = std::max(tmax, m->pos.t[b]);
     const bool persistent = m->persistent_ok && m->decode_path != MT_DECODE_KERNELS &&
-                            m->pos.t[0] <= persistent_max_position(c.d_model, c.d_ff);
+                            tmax <= persistent_max_position(c.d_model, c.d_ff);
     if (persistent) {
-        PersistentArgs pa{};
-        pa.L = c.n_layers; pa.d = c.d_model; pa.H = c.n_heads; pa.F = c.d_ff; pa.V = c.vocab;
-        pa.B = c.batch; pa.t_cap = c.t_cap; pa.eps = c.ln_eps;
-        pa.tok_emb = m->tok_emb; pa.lm_head = m->lm_head; pa.ln = m->ln; pa.ln_final = m->lnf;
-        pa.wq_base = m->wq_all; pa.ws_base = m->ws_all; pa.kc = m->kc; pa.vc = m->vc;
-        pa.token = token; pa.logits = logits; pa.next = next; pa.t0 = m->pos.t[0];
-        pa.epoch = ++m->epoch;
-        pa.a8 = (c.flags & MT_FLAG_W4A8) ? 1 : 0;
-        pa.resid = m->x; pa.xbuf = m->xbuf; pa.err = m->err; pa.trace = m->trace;
-        HIP_TRY(launch_persistent_decode(pa, st));
+        // one launch per sequence (a batch of at most kPersistentMaxSeqs),
+        // each on that sequence's slice of the cache
+        for (int b = 0; b < c.batch; ++b) {
+            PersistentArgs pa{};
+            pa.L = c.n_layers; pa.d = c.d_model; pa.H = c.n_heads; pa.F = c.d_ff; pa.V = c.vocab;
+            pa.B = 1; pa.t_cap = c.t_cap; pa.eps = c.ln_eps;
+            pa.tok_emb = m->tok_emb; pa.lm_head = m->lm_head; pa.ln = m->ln; pa.ln_final = m->lnf;
+            pa.wq_base = m->wq_all; pa.ws_base = m->ws_all;
+            pa.kc = m->kc + (size_t)b * c.t_cap * c.d_model;
+            pa.vc = m->vc + (size_t)b * c.t_cap * c.d_model;
+            pa.kv_seqs = c.batch;
+            pa.token = token + b; pa.logits = logits + (size_t)b * c.vocab; pa.next = next + b;
+            pa.t0 = m->pos.t[b];
+            pa.epoch = ++m->epoch;
+            pa.a8 = (c.flags & MT_FLAG_W4A8) ? 1 : 0;
+            pa.resid = m->x + (size_t)b * c.d_model; pa.xbuf = m->xbuf; pa.err = m->err; pa.trace = m->trace;
+            HIP_TRY(launch_persistent_decode(pa, st));
+        }
     } else {
         const int d = c.d_model;
         HIP_TRY(launch_embed(token, 1, nullptr, 0, m->tok_emb, c.vocab, d, c.batch, m->x, m->err, st));

@@ -155,8 +155,9 @@ struct Args {
     const float* ws;
     long wq_layer;  // bytes per layer
     long ws_layer;  // floats per layer
-    float* kc;
+    float* kc;    // this sequence's rows of layer 0: [t_cap, H, 64]
     float* vc;
+    int kv_seqs;  // sequences in the cache (layer stride kv_seqs * t_cap * D)
     const int64_t* token;
     float* logits;
     int64_t* next;
@@ -1057,7 +1058,7 @@ __device__ __forceinline__ bool attention_role(const Args& a, const Lds<D, F>& S
     const int h = role.head;
     const int p0 = role.split * a.chunk;
     const int npos = max(0, min(a.t0, p0 + a.chunk) - p0);
-    const size_t lstride = (size_t)a.t_cap * D;  // one layer of the cache (B = 1)
+    const size_t lstride = (size_t)a.kv_seqs * a.t_cap * D;  // one layer of the cache
     WBlk<C::CPL_D, C::NP_Q> wqh;
     BcdW<D, F> w;
     LnRegs<D> ln1;
@@ -1149,7 +1150,7 @@ __device__ __forceinline__ bool free_role(const Args& a, const Lds<D, F>& S, con
     using C = Cfg<D, F>;
     using O = Off<D, F>;
     const uint32_t ep = a.epoch;
-    const size_t lstride = (size_t)a.t_cap * D;
+    const size_t lstride = (size_t)a.kv_seqs * a.t_cap * D;
     WBlk<C::CPL_D, C::NP_KV> wkv;
     BcdW<D, F> w;
     LnRegs<D> ln1;
@@ -1347,7 +1348,7 @@ static void build_roles(Role* roles) {
 // ---------------------------------------------------------------- host side
 
 bool persistent_supported(int d, int F, int H, int B, int V) {
-    if (B != 1 || V > pd::NWG * pd::LM_ROWS) return false;
+    if (B < 1 || B > kPersistentMaxSeqs || V > pd::NWG * pd::LM_ROWS) return false;
     const bool shape = (d == 768 && F == 3072) || (d == 1024 && F == 4096) || (d == 1536 && F == 6144);
     if (!shape) return false;
     int dev = 0, cus = 0;
@@ -1413,7 +1414,7 @@ static hipError_t launch_t(const PersistentArgs& p, hipStream_t st) {
     a.wq = p.wq_base; a.ws = p.ws_base;
     a.wq_layer = (3L * D * D + (long)D * D + 2L * F * D) / 2;
     a.ws_layer = (3L * D * D + (long)D * D + 2L * F * D) / 32;
-    a.kc = p.kc; a.vc = p.vc; a.token = p.token; a.logits = p.logits;
+    a.kc = p.kc; a.vc = p.vc; a.kv_seqs = p.kv_seqs; a.token = p.token; a.logits = p.logits;
     a.next = p.next; a.t0 = p.t0; a.epoch = p.epoch; a.x = x; a.roles = roles; a.err = p.err;
     a.nib = 0x0F0F0F0Fu;
     a.a8 = p.a8;
@@ -1434,7 +1435,7 @@ static hipError_t launch_t(const PersistentArgs& p, hipStream_t st) {
 }
 
 hipError_t launch_persistent_decode(const PersistentArgs& p, hipStream_t st) {
-    if (p.B != 1) return hipErrorInvalidValue;
+    if (p.B != 1 || p.kv_seqs < 1 || p.kv_seqs > kPersistentMaxSeqs) return hipErrorInvalidValue;
     if (p.d == 768 && p.F == 3072) return launch_t<768, 3072>(p, st);
     if (p.d == 1024 && p.F == 4096) return launch_t<1024, 4096>(p, st);
     if (p.d == 1536 && p.F == 6144) return launch_t<1536, 6144>(p, st);

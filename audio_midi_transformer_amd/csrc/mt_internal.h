@@ -117,8 +117,9 @@ struct PersistentArgs {
     const float* ln_final;  // [2, d]
     const uint8_t* wq_base;    // INT4 nibbles of all layers, layer after layer
     const float* ws_base;      // group scales, same order
-    float* kc;
+    float* kc;             // the stepped sequence's rows of layer 0
     float* vc;
+    int kv_seqs;           // sequences in the cache (its batch)
     // step
     const int64_t* token;  // [B]
     float* logits;         // [B, V]
@@ -132,6 +133,9 @@ struct PersistentArgs {
     int* err;
     void* trace;           // optional phase timestamps (NULL = off)
 };
+// Batches of up to kPersistentMaxSeqs sequences take the persistent step,
+// one launch per sequence (B = 1 within each launch).
+constexpr int kPersistentMaxSeqs = 2;
 bool persistent_supported(int d, int F, int H, int B, int V);
 size_t persistent_xbuf_bytes(int L, int d, int F, int H, int B, int V);
 hipError_t launch_persistent_decode(const PersistentArgs& a, hipStream_t st);

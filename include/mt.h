@@ -162,10 +162,10 @@ int mt_prefill(mt_model* m, const int64_t* tokens, int32_t S, const float* prefi
  * as `token` of the following call, so greedy decoding never returns to the
  * host.  Same semantics as mt_prefill with P = 0, S = 1, on the dedicated
  * decode kernels.  No allocation, no synchronisation.
- * At B = 1 (d_model 768/1024/1536, 256 or more CUs) the step is one
- * persistent launch that occupies every CU and whose workgroups exchange
- * data while resident: steps of different models must not run concurrently
- * on one GPU (issue them on one stream).  If workgroups cannot all become
+ * At B <= 2 (d_model 768/1024/1536, 256 or more CUs) the step is one
+ * persistent launch per sequence that occupies every CU and whose
+ * workgroups exchange data while resident: steps of different models must
+ * not run concurrently on one GPU (issue them on one stream).  If workgroups cannot all become
  * resident, the step gives up after a bounded wait and mt_check reports
  * MT_ERR_HIP. */
 int mt_decode_step(mt_model* m, const int64_t* token, float* logits, int64_t* next, void* stream);
@@ -237,7 +237,7 @@ int mt_check(mt_model* m);
 /* Decode implementation selector (for measurement and parity of both):
  *   MT_DECODE_AUTO       persistent single-launch step when supported
  *   MT_DECODE_KERNELS    one kernel per operation
- *   MT_DECODE_PERSISTENT one persistent launch per step (B = 1 only; past
+ *   MT_DECODE_PERSISTENT one persistent launch per sequence (B <= 2; past
  *                        its cache reach, 2048 positions or 4096 at
  *                        d_model 768, the kernels run) */
 #define MT_DECODE_AUTO 0

@@ -140,3 +140,57 @@ def test_second_model_of_same_size(oracle_mod):
     prefix = np.random.default_rng(11).standard_normal((1, 20, 768)).astype(np.float32)
     for _ in range(3):
         _teacher_forced(oracle_mod, w, 1, 40, prefix, None, 4, TOL["small"], binding.MT_DECODE_PERSISTENT)
+
+
+@pytest.mark.parametrize("width", ["small", "medium", "large"])
+def test_persistent_two_sequences_vs_oracle(oracle_mod, width):
+    """Two sequences (a conditional/unconditional pair, say) step through the
+    persistent kernel one launch each, on their own slices of the cache."""
+    _dev()
+    base = WIDTHS[width]
+    shape = synth.ModelShape(base.name, 2, base.d_model, base.n_heads, base.d_ff)
+    w = synth.model_weights(shape, 47)
+    prefix = np.random.default_rng(13).standard_normal((2, 90, shape.d_model)).astype(np.float32)
+    _teacher_forced(oracle_mod, w, 2, 110, prefix, None, 10, TOL[width], binding.MT_DECODE_PERSISTENT)
+
+
+def test_persistent_two_sequences_at_different_positions(oracle_mod):
+    """Sequences prefilled to 40 and 333 positions decode in lockstep on the
+    persistent step (each launch takes its own position and cache slice);
+    sequence 0 then restarts with a new chunk while sequence 1 continues."""
+    _dev()
+    shape = synth.ModelShape("medium", 2, 1024, 16, 4096)
+    w = synth.model_weights(shape, 48)
+    rng = np.random.default_rng(14)
+    om = oracle_mod.OracleModel.from_weights(w, batch=2, t_cap=360)
+    dec = binding.Decoder(w, batch=2, t_cap=360)
+    dec.set_decode_path(binding.MT_DECODE_PERSISTENT)
+    tol = TOL["medium"]
+    for b, P in ((0, 40), (1, 333)):
+        x = rng.standard_normal((P, shape.d_model)).astype(np.float32)
+        lo, _ = om.forward_seq(b, prefix=x)
+        lg, _ = dec.prefill_seq(b, None, _t(x))
+        compare_logits(lg.cpu().numpy()[None], lo[None], tol, f"prefill of sequence {b}")
+    worst = 0.0
+    for k in range(12):
+        if k == 6:
+            om.reset_seq(0)
+            dec.reset_seq(0)
+            x = rng.standard_normal((5, shape.d_model)).astype(np.float32)
+            om.forward_seq(0, prefix=x)
+            dec.prefill_seq(0, None, _t(x))
+        tok = rng.integers(0, shape.vocab, size=2)
+        lo, no = om.forward(tokens=tok[:, None])
+        lg, ng = dec.decode_step(_t(tok))
+        worst = max(worst, compare_logits(lg.cpu().numpy(), lo, tol, f"step {k}"))
+        check_argmax(ng.cpu().numpy(), *top2(lo), None, tol)
+    dec.check()
+    assert [dec.position_seq(b) for b in range(2)] == [om.position_seq(b) for b in range(2)] == [11, 345]
+    K, V = dec.kv_cache()
+    Ko, Vo = om.kv()
+    for b, T in ((0, 11), (1, 345)):
+        np.testing.assert_allclose(K[:, b, :T].cpu().numpy(), Ko[:, b, :T], rtol=0, atol=5e-5)
+        np.testing.assert_allclose(V[:, b, :T].cpu().numpy(), Vo[:, b, :T], rtol=0, atol=5e-5)
+    dec.close()
+    om.close()
+    print(f"two sequences at different positions: max |delta logits| {worst:.3g}")
