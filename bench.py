@@ -329,8 +329,15 @@ def main() -> int:
     gbps = float(launch_bytes.sum()) / (steady_ms * 1e-3) / 1e9
     step_ms = np.concatenate([np.array([a.elapsed_time(b) for a, b in e["per"]])[STEADY_FROM:] for e in evs])
     kernel_name = "mt_decode_step_persistent" if persistent else "decode_step_kernels"
-    achieved = float(launch_bytes.sum() * args.steps / (step_ms.sum() * 1e-3) / 1e9)
-    traffic = traffic_from_profiles(kernel_name, wl.key, variant)
+    # the persistent step is one launch per sequence: each reads all weights
+    # and its own sequence's cache
+    lps = B if persistent else 1
+    per_launch = (np.array([step_bytes(shape, 1, R0 + k + 1, wbytes) for k in range(STEADY_FROM, n_dec)])
+                  if lps > 1 else launch_bytes)
+    achieved = float(per_launch.sum() * lps * args.steps / (step_ms.sum() * 1e-3) / 1e9)
+    # the counter record holds for the workload's own configuration only
+    traffic = (traffic_from_profiles(kernel_name, wl.key, variant)
+               if lps == 1 and pairs is None and args.batch is None else None)
     pf_flops = prefill_flops(shape, B, R0)
 
     # point values at T = 505, 1024 and 2048 keys (where the pass reaches them)
@@ -388,8 +395,9 @@ def main() -> int:
         "roofline": {"kernel": kernel_name, "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic,
-                     "algorithmic_bytes_per_launch": round(float(launch_bytes.mean()), 1),
-                     "avg_launch_us": round(float(step_ms.mean()) * 1000.0, 2)},
+                     "algorithmic_bytes_per_launch": round(float(per_launch.mean()), 1),
+                     "avg_launch_us": round(float(step_ms.mean()) * 1000.0 / lps, 2),
+                     "launches_per_step": lps},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
