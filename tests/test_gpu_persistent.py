@@ -130,6 +130,39 @@ def test_persistent_equals_kernel_path_full_depth(width):
     b.close()
 
 
+def test_persistent_pair_equals_kernel_path_full_depth():
+    """Full-depth medium model, B = 2 (two persistent launches per step, each
+    on its sequence's slice of all 24 layers' cache) against the
+    per-operation kernels, 24 teacher-forced steps after prefixes of
+    different content."""
+    _dev()
+    shape = synth.MEDIUM
+    w = synth.model_weights(shape, 49)
+    packed = binding.pack_weights(w)
+    prefix = _t(np.random.default_rng(15).standard_normal((2, 504, shape.d_model)).astype(np.float32))
+    a = binding.Decoder(w, batch=2, t_cap=540, packed=packed)
+    b = binding.Decoder(w, batch=2, t_cap=540, packed=packed)
+    a.set_decode_path(binding.MT_DECODE_PERSISTENT)
+    b.set_decode_path(binding.MT_DECODE_KERNELS)
+    a.prefill(None, prefix)
+    lb, nb = b.prefill(None, prefix)
+    for k in range(24):
+        tok = nb.clone()
+        la, _ = a.decode_step(tok)
+        lb, nb = b.decode_step(tok)
+        d = float((la - lb).abs().max())
+        assert d <= TOL["medium"], f"step {k}: persistent pair vs kernels max |delta| {d}"
+    a.check()
+    b.check()
+    ka, va = a.kv_cache()
+    kb, vb = b.kv_cache()
+    T = a.position
+    assert float((ka[:, :, :T] - kb[:, :, :T]).abs().max()) <= 5e-5
+    assert float((va[:, :, :T] - vb[:, :, :T]).abs().max()) <= 5e-5
+    a.close()
+    b.close()
+
+
 def test_second_model_of_same_size(oracle_mod):
     """A model created after another of the same size has been destroyed (its
     buffers may land at the same addresses) still runs the persistent step:
