@@ -32,7 +32,7 @@ MT_FLAG_DENSE_F16 = 2
 MT_FLAG_DENSE_F32 = 4
 
 # Names declared in include/mt.h; the CPU test checks the library exports all.
-EXPORTED = ("mt_pack_int4", "mt_create", "mt_prefill", "mt_decode_step", "mt_reset",
+EXPORTED = ("mt_pack_int4", "mt_pack_f16", "mt_create", "mt_prefill", "mt_decode_step", "mt_reset",
             "mt_position", "mt_kv_cache", "mt_check", "mt_set_decode_path", "mt_destroy",
             "mt_last_error", "mt_debug_dequant", "mt_debug_matmul", "mt_debug_trace",
             "mt_prefill_seq", "mt_reset_seq", "mt_position_seq", "mt_cfg_combine")
@@ -75,6 +75,7 @@ def lib() -> ctypes.CDLL:
     L = ctypes.CDLL(LIB_PATH)
     vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     L.mt_pack_int4.argtypes = [vp, i32, i32, vp, vp]
+    L.mt_pack_f16.argtypes = [vp, i64, vp]
     L.mt_create.argtypes = [ctypes.POINTER(mt_config), ctypes.POINTER(mt_weights), ctypes.c_int, vp,
                             ctypes.POINTER(vp)]
     L.mt_prefill.argtypes = [vp, vp, i32, vp, i32, vp, vp, vp]
@@ -95,7 +96,7 @@ def lib() -> ctypes.CDLL:
     L.mt_reset_seq.argtypes = [vp, i32]
     L.mt_position_seq.argtypes = [vp, i32, ctypes.POINTER(i32)]
     L.mt_cfg_combine.argtypes = [vp, i32, i32, ctypes.c_float, vp, vp, vp, vp]
-    for name in ("mt_pack_int4", "mt_create", "mt_prefill", "mt_decode_step", "mt_reset",
+    for name in ("mt_pack_int4", "mt_pack_f16", "mt_create", "mt_prefill", "mt_decode_step", "mt_reset",
                  "mt_position", "mt_kv_cache", "mt_check", "mt_set_decode_path",
                  "mt_debug_dequant", "mt_debug_matmul", "mt_debug_trace",
                  "mt_prefill_seq", "mt_reset_seq", "mt_position_seq", "mt_cfg_combine"):
@@ -120,6 +121,15 @@ def mt_pack_int4(W: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
     s = np.empty((N, K // 32), dtype=np.float32)
     check(lib().mt_pack_int4(W.ctypes.data, N, K, q.ctypes.data, s.ctypes.data), "mt_pack_int4")
     return q, s
+
+
+def mt_pack_f16(W: np.ndarray) -> np.ndarray:
+    """Host binary16 packer: float32 array -> float16 array of the same shape
+    (round to nearest, ties to even, done by the library)."""
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    out = np.empty(W.shape, dtype=np.float16)
+    check(lib().mt_pack_f16(W.ctypes.data, W.size, out.ctypes.data), "mt_pack_f16")
+    return out
 
 
 def cfg_combine(logits, cfg: float, guided=None, next=None, token_pair=None, store_guided: bool = True,
@@ -336,12 +346,14 @@ class Decoder:
 
 
 def dense_weights(weights, dtype=np.float32):
-    """Every projection as a contiguous row-major array of `dtype` (float16
-    rounds to nearest even), in mt_weights.dense order."""
+    """Every projection as a contiguous row-major array of `dtype`, in
+    mt_weights.dense order; float16 values come from the library's packer
+    (mt_pack_f16: round to nearest, ties to even)."""
     out = []
     for l in range(weights.shape.n_layers):
         for W in (weights.w_qkv[l], weights.w_o[l], weights.w_up[l], weights.w_down[l]):
-            out.append(np.ascontiguousarray(np.asarray(W, dtype=np.float32).astype(dtype)))
+            W = np.ascontiguousarray(W, dtype=np.float32)
+            out.append(mt_pack_f16(W) if dtype == np.float16 else W)
     return out
 
 

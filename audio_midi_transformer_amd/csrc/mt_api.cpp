@@ -262,6 +262,28 @@ int mt_pack_int4(const float* W, int32_t N, int32_t K, uint8_t* q, float* s) {
     return MT_OK;
 }
 
+int mt_pack_f16(const float* W, int64_t n, uint16_t* out) {
+    if (!W || !out || n < 0) return fail(MT_ERR_INVALID_ARG, "mt_pack_f16: NULL pointer or negative size");
+    // the compiler's binary32 -> binary16 conversion rounds to nearest, ties to even
+    auto work = [&](int64_t i0, int64_t i1) {
+        for (int64_t i = i0; i < i1; ++i) {
+            const _Float16 h = (_Float16)W[i];
+            std::memcpy(out + i, &h, sizeof h);
+        }
+    };
+    const int64_t nthreads = std::max<int64_t>(1, std::min<int64_t>(std::thread::hardware_concurrency(), n >> 20));
+    if (nthreads <= 1) {
+        work(0, n);
+    } else {
+        std::vector<std::thread> th;
+        const int64_t per = (n + nthreads - 1) / nthreads;
+        for (int64_t t = 0; t < nthreads; ++t)
+            th.emplace_back(work, std::min<int64_t>(n, t * per), std::min<int64_t>(n, (t + 1) * per));
+        for (auto& t : th) t.join();
+    }
+    return MT_OK;
+}
+
 int mt_create(const mt_config* cfg, const mt_weights* w, int weights_on_device, void* stream,
               mt_model** out) {
     if (!out) return fail(MT_ERR_INVALID_ARG, "mt_create: out is NULL");

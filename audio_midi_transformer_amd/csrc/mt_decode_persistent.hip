@@ -140,6 +140,26 @@ struct Cfg {
     static_assert(LPR_D > 0 && LPR_F > 0, "width has no GEMV lane mapping");
     static_assert(NFREE >= 64 && KV_ROWS * NFREE >= 2 * D, "K/V rows need workgroups without attention duty");
     static_assert(LDS_FLOATS * 4 <= 160 * 1024, "LDS budget");
+    // Regions that are live in the same phase must not overlap:
+    //   all phases: the K|V chunk (BIG), xs, us, comb, red, flag;
+    //   phases A, A2 (attention, head merge): act, qh, sc, the partials;
+    //   phases B, C: act; phase D: u (which overlays act .. partials).
+    static constexpr bool disjoint(int a, int na, int b, int nb) { return a + na <= b || b + nb <= a; }
+    static_assert(disjoint(0, BIG, OFF_XS, GD) && disjoint(OFF_XS, GD, OFF_US, GF), "chunk / group sums");
+    static_assert(disjoint(OFF_US, GF, OFF_U, F) && disjoint(OFF_XS, GD, OFF_U, F), "group sums / u");
+    static_assert(disjoint(OFF_ACT, D, OFF_QH, 64) && disjoint(OFF_QH, 64, OFF_SC, MAXPOS) &&
+                      disjoint(OFF_SC, MAXPOS, OFF_PART, ATT_S * PW + 128) &&
+                      disjoint(OFF_ACT, D, OFF_PART, ATT_S * PW + 128),
+                  "phase A regions");
+    static_assert(disjoint(OFF_COMB, 4 * 64, OFF_U, F) && disjoint(OFF_COMB, 4 * 64, OFF_PART, ATT_S * PW + 128) &&
+                      disjoint(OFF_COMB, 4 * 64, OFF_ACT, D) && disjoint(OFF_COMB, 4 * 64, 0, BIG),
+                  "staging / vectors");
+    static_assert(disjoint(OFF_RED, 16, OFF_COMB, 4 * 64) && disjoint(OFF_FLAG, 16, OFF_RED, 16) &&
+                      OFF_FLAG + 16 <= LDS_FLOATS,
+                  "reductions / flag");
+    // W4A8 codes of a vector of n inputs take n bytes, followed by n / 32
+    // reciprocal scales, inside the vector's own region
+    static_assert(D / 4 + GD <= D && F / 4 + GF <= F, "W4A8 code layout");
 };
 
 struct Args {

@@ -191,3 +191,22 @@ def random_matrix(seed: int, n: int, k: int, scale: float = 0.02) -> np.ndarray:
 def tiny_shape(n_layers=2, d_model=128, n_heads=2, d_ff=512, vocab=97) -> ModelShape:
     """Small shapes for tests the oracle finishes in well under a second."""
     return ModelShape("tiny", n_layers, d_model, n_heads, d_ff, vocab)
+
+
+def tie_head_rows(w: ModelWeights, rows, seed: int = 0, bias_norm: float = 40.0, gain: float = 4.0) -> ModelWeights:
+    """Inputs with an exact greedy tie at every position.
+
+    The final LayerNorm bias is replaced by a long random direction u
+    (|bias| = bias_norm) and every LM-head row listed in `rows` by the same
+    vector gain * u / |u|.  Those rows then produce bit-equal logits (same
+    row, same input, same arithmetic), near gain * bias_norm, far above every
+    other logit (a random row of N(0, 0.02) entries gives about +-1).
+    Modifies w in place and returns it."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    u = rng.standard_normal(w.shape.d_model)
+    u /= np.sqrt(np.sum(u * u))
+    w.lnf_b = (bias_norm * u).astype(np.float32)
+    row = (gain * u).astype(np.float32)
+    for r in rows:
+        w.lm_head[r] = row
+    return w

@@ -103,7 +103,8 @@ typedef struct {
  *   tok_emb  [V, d]           FP32 token embedding (not quantised)
  *   lm_head  [V, d]           FP32, row v produces logit v (untied, no bias)
  *   ln_final [2, d]           final LayerNorm gain, bias
- *   ln       [L, 4, d]        per layer: gain1, bias1, gain2, bias2
+ *   ln       [L, 4, d]        per layer: gain1, bias1, gain2, bias2 (one
+ *                             contiguous array for all layers)
  *   proj     [L * 4]          per layer, in this order:
  *                               QKV  [3d, d]  rows Q | K | V, head h = rows 64h..64h+63 of each
  *                               O    [d, d]
@@ -111,7 +112,8 @@ typedef struct {
  *                               down [d, F]
  *   dense    [L * 4]          same order; only with MT_FLAG_DENSE_F16 / _F32:
  *                               dense[i] points to W [N, K] row-major, binary16
- *                               or binary32 per the flag (proj may be NULL)
+ *                               or binary32 per the flag (proj may be NULL);
+ *                               mt_pack_f16 makes the binary16 form
  * No projection has a bias. */
 typedef struct {
     const float* tok_emb;
@@ -127,9 +129,22 @@ typedef struct {
  * Uses IEEE binary32 division and round-half-even. */
 int mt_pack_int4(const float* W, int32_t N, int32_t K, uint8_t* q, float* s);
 
+/* Host-side binary16 packer for MT_FLAG_DENSE_F16 weights (host pointers):
+ * out[i] = the IEEE binary16 bits of W[i] rounded to nearest, ties to even
+ * (gradual underflow, overflow to infinity), i < n.  The Core AI conversion
+ * casts the large model's weights to half (its file table).  Errors: NULL
+ * pointer or n < 0 -> MT_ERR_INVALID_ARG. */
+int mt_pack_f16(const float* W, int64_t n, uint16_t* out);
+
 /* Create a model: validates the config, copies the weights to the current
  * HIP device and allocates the KV cache [L, B, t_cap, H, 64] twice (K, V,
- * FP32, 2*L*B*t_cap*d*4 bytes) plus decode scratch.  The projections are
+ * FP32, 2*L*B*t_cap*d*4 bytes) plus decode scratch.  The projections are the
+ * INT4 group-32 MatMulNBits weights and the embeddings and LM head stay FP32
+ * ("MuScriptor Medium -- optimized W4A32 ONNX Runtime" README, "Model
+ * variant"); the cache has a fixed capacity chosen at deployment (the same
+ * README, "Quick smoke test": a maximum cache length, 2504 by default) and is
+ * owned by the model, allocated once, because past and present share one
+ * buffer ("Model variant").  The projections are
  * held twice on the device: as given, and re-tiled for the batched decode
  * kernels (16-row blocks per group, so each load instruction reads one
  * contiguous block).  weights_on_device: 0 = host pointers, 1 = device
@@ -157,7 +172,9 @@ int mt_prefill(mt_model* m, const int64_t* tokens, int32_t S, const float* prefi
                float* logits, int64_t* next, void* stream);
 
 /* One greedy decode step: token[b] (int64) is appended to sequence b at
- * its own position T_b;
+ * its own position T_b (the decoder call with one token row and no prefix
+ * rows; positions are implied by the cache length: "unifolia/muscriptor-
+ * small-onnx", "Files"; greedy decoding of the MT3 tokens, same section);
  * logits [B, V] and next [B] as for mt_prefill.  `next` may be passed back
  * as `token` of the following call, so greedy decoding never returns to the
  * host.  Same semantics as mt_prefill with P = 0, S = 1, on the dedicated
@@ -170,8 +187,10 @@ int mt_prefill(mt_model* m, const int64_t* tokens, int32_t S, const float* prefi
  * MT_ERR_HIP. */
 int mt_decode_step(mt_model* m, const int64_t* token, float* logits, int64_t* next, void* stream);
 
-/* Set every T_b to 0.  Cache contents are left as they are (they are
- * overwritten before they are read again). */
+/* Set every T_b to 0: the next call starts a new chunk on an empty cache
+ * (positions restart because they are implied by the cache length,
+ * "unifolia/muscriptor-small-onnx", "Files").  Cache contents are left as
+ * they are (they are overwritten before they are read again). */
 int mt_reset(mt_model* m);
 
 /* Current position of sequence 0 (the shared T_past of a lockstep batch;
@@ -226,8 +245,12 @@ int mt_position_seq(const mt_model* m, int32_t b, int32_t* t_past);
 int mt_cfg_combine(const float* logits, int32_t pairs, int32_t V, float cfg, float* guided, int64_t* next,
                    int64_t* token_pair, void* stream);
 
-/* Device pointers to the cache, [L, B, t_cap, H, 64] FP32 each.  The cache
- * is updated in place: past and present are the same buffer. */
+/* Device pointers to the cache, [L, B, t_cap, H, 64] FP32 each (the
+ * decoder's past_key / past_value layout with the batch and a fixed capacity:
+ * "unifolia/muscriptor-small-onnx", "Files").  The cache is updated in place:
+ * past and present are the same buffer ("MuScriptor Medium -- optimized
+ * W4A32 ONNX Runtime", "Model variant").  The pointers stay valid until
+ * mt_destroy; the model owns the memory. */
 int mt_kv_cache(mt_model* m, const float** k, const float** v);
 
 /* Synchronise the model's last stream and report sticky device errors

@@ -28,9 +28,10 @@ from audio_midi_transformer_amd import synth  # noqa: E402
 
 OUT = os.path.dirname(os.path.abspath(__file__))
 
-# decode steps stored per workload (the full run where the oracle finishes in
-# minutes; the large B=8 run is sampled at its start)
-STEPS = {"0": 16, "1": 256, "2": 1544, "3": 512, "3c576": 72, "4": 1544, "4b8": 48,
+# decode steps stored per workload: every run is stored in full (the large
+# B=8 run, 8 x 1544 steps of the 48-layer model, takes the oracle about an
+# hour or more on 6 threads)
+STEPS = {"0": 16, "1": 256, "2": 1544, "3": 512, "3c576": 72, "4": 1544, "4b8": 1544,
          # the W4A8 variant (oracle in its W4A8 mode) of three workloads
          "0a8": 16, "2a8": 1544, "3a8": 512,
          # dense-weight variants (oracle with unquantised, or binary16-rounded,

@@ -52,6 +52,23 @@ def test_packer_on_workload_shapes(oracle_mod):
             assert np.array_equal(q1, q2) and np.array_equal(s1.view(np.uint32), s2.view(np.uint32))
 
 
+def test_f16_packer_matches_independent_conversions(oracle_mod):
+    """mt_pack_f16 against numpy's binary16 conversion and the oracle's own
+    rounding written from the definition: bit-identical on values spanning
+    underflow, the subnormal range, exact ties, the largest half and
+    overflow."""
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal(200_000) * np.exp2(rng.uniform(-30, 18, 200_000))).astype(np.float32)
+    ties = np.array([1 + 2.0 ** -11, 1 + 3 * 2.0 ** -11, 2.0 ** -25, 3 * 2.0 ** -25, 65504.0, 65519.0, 65520.0,
+                     -65520.0, 2.0 ** -14, 2.0 ** -24, 0.0, -0.0, np.inf, -np.inf], np.float32)
+    x = np.concatenate([x, ties])
+    got = binding.mt_pack_f16(x)
+    assert np.array_equal(got.view(np.uint16), x.astype(np.float16).view(np.uint16))
+    assert np.array_equal(got.astype(np.float32).view(np.uint32), oracle_mod.round_half(x).view(np.uint32))
+    nan = binding.mt_pack_f16(np.array([np.nan], np.float32))
+    assert np.isnan(nan[0])
+
+
 def test_packer_rejects_bad_width():
     with pytest.raises(binding.MTError) as e:
         binding.mt_pack_int4(np.zeros((2, 40), np.float32))

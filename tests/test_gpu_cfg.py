@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 from audio_midi_transformer_amd import binding, synth
-from parity import TOL, check_argmax, compare_logits, top2
+from parity import TOL, check_argmax, check_own_argmax, compare_logits, top2
 
 pytestmark = pytest.mark.gpu
 
@@ -76,6 +76,7 @@ def _pair_run(oracle_mod, shape, seed, Np, P, steps, cfg, tol):
         gg, ng, tp = binding.cfg_combine(lg, cfg)
         gg, ng, tp = gg.cpu().numpy(), ng.cpu().numpy(), tp.cpu().numpy()
         worst = max(worst, compare_logits(gg, go, gtol, f"guided, call {k}"))
+        check_own_argmax(ng, gg, f"guided, call {k}")
         ties += check_argmax(ng, *top2(go), go[np.arange(Np), ng], gtol)
         assert np.array_equal(tp, np.concatenate([ng, ng]))
         if k == steps:

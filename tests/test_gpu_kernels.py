@@ -7,7 +7,7 @@ import numpy as np
 import pytest
 
 from audio_midi_transformer_amd import binding, synth
-from parity import TOL, check_argmax, compare_logits, top2
+from parity import TOL, check_greedy, compare_logits
 
 pytestmark = pytest.mark.gpu
 
@@ -102,13 +102,13 @@ def _run_pair(oracle_mod, shape, w, B, t_cap, prefix, tokens, steps, path=None):
     lg, ng = dec.prefill(_t(tokens) if tokens is not None else None,
                          _t(prefix) if prefix is not None else None)
     worst = compare_logits(lg.cpu().numpy(), lo, TOL["tiny"], "prefill")
-    ties = check_argmax(ng.cpu().numpy(), *top2(lo), None, TOL["tiny"])
+    ties = check_greedy(ng.cpu().numpy(), lg.cpu().numpy(), lo, TOL["tiny"])
     for k in range(steps):
         tok = no.reshape(B, 1)
         lo, no = om.forward(tokens=tok)
         lg, ng = dec.decode_step(_t(tok.reshape(B)))
         worst = max(worst, compare_logits(lg.cpu().numpy(), lo, TOL["tiny"], f"step {k}"))
-        ties += check_argmax(ng.cpu().numpy(), *top2(lo), None, TOL["tiny"])
+        ties += check_greedy(ng.cpu().numpy(), lg.cpu().numpy(), lo, TOL["tiny"])
     dec.check()
     K, V = dec.kv_cache()
     Ko, Vo = om.kv()

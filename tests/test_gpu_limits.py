@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 
 from audio_midi_transformer_amd import binding, synth
-from parity import TOL, check_argmax, compare_logits, top2
+from parity import TOL, check_greedy, compare_logits
 
 pytestmark = pytest.mark.gpu
 
@@ -31,13 +31,13 @@ def _run(oracle_mod, w, B, t_cap, prefix, tokens, steps, tol):
     lo, no = om.forward(tokens=tokens, prefix=prefix)
     lg, ng = dec.prefill(_t(tokens) if tokens is not None else None, _t(prefix) if prefix is not None else None)
     worst = compare_logits(lg.cpu().numpy(), lo, tol, "prefill")
-    check_argmax(ng.cpu().numpy(), *top2(lo), None, tol)
+    check_greedy(ng.cpu().numpy(), lg.cpu().numpy(), lo, tol)
     for k in range(steps):
         tok = no.reshape(B, 1)
         lo, no = om.forward(tokens=tok)
         lg, ng = dec.decode_step(_t(tok.reshape(B)))
         worst = max(worst, compare_logits(lg.cpu().numpy(), lo, tol, f"step {k}"))
-        check_argmax(ng.cpu().numpy(), *top2(lo), None, tol)
+        check_greedy(ng.cpu().numpy(), lg.cpu().numpy(), lo, tol)
     dec.check()
     assert dec.position == om.position
     return om, dec, no, worst
@@ -109,13 +109,13 @@ def test_cache_16384_filled_then_refused(oracle_mod):
         lo, no = om.forward(prefix=part)
         lg, ng = dec.prefill(None, _t(part))
         worst = max(worst, compare_logits(lg.cpu().numpy(), lo, TOL["tiny"], f"prefill chunk {c}"))
-        check_argmax(ng.cpu().numpy(), *top2(lo), None, TOL["tiny"])
+        check_greedy(ng.cpu().numpy(), lg.cpu().numpy(), lo, TOL["tiny"])
     for k in range(t_cap - P):
         tok = no.reshape(1, 1)
         lo, no = om.forward(tokens=tok)
         lg, ng = dec.decode_step(_t(tok.reshape(1)))
         worst = max(worst, compare_logits(lg.cpu().numpy(), lo, TOL["tiny"], f"step {k}"))
-        check_argmax(ng.cpu().numpy(), *top2(lo), None, TOL["tiny"])
+        check_greedy(ng.cpu().numpy(), lg.cpu().numpy(), lo, TOL["tiny"])
     dec.check()
     assert dec.position == t_cap == om.position
     K, _ = dec.kv_cache()

@@ -7,7 +7,7 @@ import numpy as np
 import pytest
 
 from audio_midi_transformer_amd import binding, synth
-from parity import TOL, check_argmax, compare_logits, top2
+from parity import TOL, check_greedy, compare_logits
 
 pytestmark = pytest.mark.gpu
 
@@ -40,7 +40,7 @@ def _teacher_forced(oracle_mod, w, B, t_cap, prefix, tokens, steps, tol, path):
         lg, ng = dec.decode_step(_t(tok.reshape(B)))
         g = lg.cpu().numpy()
         worst = max(worst, compare_logits(g, lo, tol, f"step {k} (position {om.position - 1})"))
-        ties += check_argmax(ng.cpu().numpy(), *top2(lo), None, tol)
+        ties += check_greedy(ng.cpu().numpy(), lg.cpu().numpy(), lo, tol)
     dec.check()
     K, V = dec.kv_cache()
     Ko, Vo = om.kv()
@@ -216,7 +216,7 @@ def test_persistent_two_sequences_at_different_positions(oracle_mod):
         lo, no = om.forward(tokens=tok[:, None])
         lg, ng = dec.decode_step(_t(tok))
         worst = max(worst, compare_logits(lg.cpu().numpy(), lo, tol, f"step {k}"))
-        check_argmax(ng.cpu().numpy(), *top2(lo), None, tol)
+        check_greedy(ng.cpu().numpy(), lg.cpu().numpy(), lo, tol)
     dec.check()
     assert [dec.position_seq(b) for b in range(2)] == [om.position_seq(b) for b in range(2)] == [11, 345]
     K, V = dec.kv_cache()

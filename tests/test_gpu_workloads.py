@@ -107,6 +107,9 @@ def test_workload_teacher_forced(key, path):
         d = float(np.abs(lg[k].astype(np.float64) - g["sample_logits"][j]).max())
         assert d <= tol, f"call {k}: max |delta logits| {d:.3g} > {tol}"
     # every call: logit at the oracle's argmax, and the argmax itself
+    # the pick is the exact argmax of the GPU's own logits (lowest index on ties)
+    own = np.argmax(lg, axis=2)
+    assert np.array_equal(nx, own), f"pick is not the argmax of the GPU logits at {np.argwhere(nx != own)[:5].tolist()}"
     idx = g["top1"]
     at_top = np.take_along_axis(lg, idx[..., None].astype(np.int64), axis=2)[..., 0]
     dtop = np.abs(at_top.astype(np.float64) - g["top1v"])

@@ -238,6 +238,38 @@ def test_model_zero_projections(oracle_mod):
     assert m.position == P
 
 
+def test_model_argmax_tie_lowest_index(oracle_mod):
+    """Greedy decoding takes the lowest index among bit-equal maxima.  LM-head
+    rows 5 and 6 are identical and dominate (so their logits are exactly
+    equal and largest): every call must pick 5, a tie rule that keeps the
+    last maximum would pick 6.  A three-way tie (7, 20, 52) placed above
+    them must pick 7; making row 6 alone the largest must pick 6."""
+    shape = synth.tiny_shape(n_layers=2, d_model=64, n_heads=1, d_ff=128, vocab=53)
+    B, P = 2, 5
+    prefix = np.random.default_rng(3).standard_normal((B, P, 64)).astype(np.float32)
+    cases = (({5, 6}, 4.0, 5), ({7, 20, 52}, 4.0, 7))
+    for rows, gain, want in cases:
+        w = synth.tie_head_rows(_tiny_weights(shape), sorted(rows), seed=1, gain=gain)
+        if want == 7:  # rows 5 and 6 below the three-way tie
+            w.lm_head[5] = w.lm_head[6] = np.float32(0.5) * w.lm_head[7]
+        m = oracle_mod.OracleModel.from_weights(w, batch=B, t_cap=16)
+        logits, nxt = m.forward(prefix=prefix)
+        for step in range(4):
+            r = sorted(rows)
+            for b in range(B):
+                assert all(logits[b, r[0]] == logits[b, j] for j in r[1:])
+                assert logits[b, r[0]] > np.max(np.delete(logits[b], r))
+            assert list(nxt) == [want] * B, (rows, step, nxt)
+            logits, nxt = m.forward(tokens=nxt.reshape(B, 1))
+        m.close()
+    w = synth.tie_head_rows(_tiny_weights(shape), [5, 6], seed=1)
+    w.lm_head[6] = w.lm_head[6] * np.float32(1.5)
+    m = oracle_mod.OracleModel.from_weights(w, batch=B, t_cap=16)
+    _, nxt = m.forward(prefix=prefix)
+    assert list(nxt) == [6] * B
+    m.close()
+
+
 def _perm(n, seed):
     p = np.random.default_rng(seed).permutation(n)
     M = np.zeros((n, n), np.float32)
