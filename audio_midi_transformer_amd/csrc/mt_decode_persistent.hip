@@ -78,12 +78,14 @@ constexpr int res_lane(int lpr) { return lpr == 64 ? 48 : (lpr == 32 ? 16 : 0); 
 
 // Role of one workgroup (host-built table, constant for a model).
 struct Role {
-    int head;     // attention head, -1 if none
-    int split;    // attention split (0 = head leader)
-    int kv_row0;  // first row of the 2D K|V rows of the fused projection
-    int kv_rows;  // number of K|V rows, 0 if none
-    int o_row0;   // first of this workgroup's O-projection rows, -1 if none
-    int pad0, pad1, pad2;
+    int head;       // attention head, -1 if none
+    int split;      // attention split (0 = head leader)
+    int kv_row0;    // first row of the 2D K|V rows of the fused projection
+    int kv_rows;    // number of K|V rows, 0 if none
+    int o_row0;     // first of this workgroup's O-projection rows, -1 if none
+    int tail_head;  // free workgroups: head of this workgroup's tail split, -1 if none
+    int tail_idx;   // its index among the head's tail splits
+    int pad;
 };
 
 template <int D, int F>
@@ -93,12 +95,22 @@ struct Cfg {
     static constexpr int LPR_D = lpr_for(D), CPL_D = GD / (LPR_D ? LPR_D : 1), RP_D = NT / (LPR_D ? LPR_D : 1);
     static constexpr int LPR_F = lpr_for(F), CPL_F = GF / (LPR_F ? LPR_F : 1), RP_F = NT / (LPR_F ? LPR_F : 1);
     // attention splits per head: 16 where that leaves at least 64 workgroups
-    // for the new K/V rows, else 8 (16 splits at medium width measured slower:
-    // the q projection is recomputed by twice as many workgroups and the head
-    // merge gathers twice as many partials)
+    // for the new K/V rows and the O projection, else 8; each holds up to MP
+    // cached positions in LDS.  (16 splits at medium width leave no such
+    // workgroups: the K/V and O rows then land on the attention workgroups,
+    // whose loads complete in order behind their K/V chunk DMA; measured
+    // 17 % slower.)
     static constexpr int ATT_S = H * 16 + 64 <= NWG ? 16 : 8;
+    static constexpr int MP = MAXPOS;
     static constexpr int NATT = H * ATT_S;
     static constexpr int NFREE = NWG - NATT;
+    // Positions past ATT_S * MP go to tail splits on the free workgroups (TS
+    // per head, up to MAXPOS positions each), which are idle while the
+    // attention workgroups compute q_h and their partials; the head leader
+    // merges them with the other partials.
+    static constexpr int TS = NFREE / H;
+    static constexpr int SLOTS = ATT_S + TS;  // partial slots per head
+    static constexpr int REACH = ATT_S * MP + TS * MAXPOS;
     static constexpr int KV_ROWS = cdiv(2 * D, NFREE);
     static constexpr int UP_ROWS = cdiv(F, NWG);
     static constexpr int O_ROWS = cdiv(D, NFREE);  // O rows: free workgroups only
@@ -112,8 +124,8 @@ struct Cfg {
     // reads are written REP times; the workgroups of XCD x read copy x, so
     // no line is polled by more than 32 workgroups.
     static constexpr int XA_KV = 0;                     // new K|V row [2D]
-    static constexpr int XA_PART = XA_KV + 2 * D;       // partials [H][ATT_S][PW]
-    static constexpr int XB_ATT = XA_PART + NATT * PW;  // merged attention [REP][D]
+    static constexpr int XA_PART = XA_KV + 2 * D;       // partials [H][SLOTS][PW]
+    static constexpr int XB_ATT = XA_PART + H * SLOTS * PW;  // merged attention [REP][D]
     static constexpr int XB_O = XB_ATT + REP * D;       // o [REP][D]
     static constexpr int XC = XB_O + REP * D;           // u [REP][F]
     static constexpr int XD = XC + REP * F;             // f [REP][D]
@@ -121,24 +133,25 @@ struct Cfg {
     // LDS layout (floats).  The K|V chunk of an attention split stays
     // resident across phases B..D (it is the next layer's chunk by then), so
     // u of phase D shares one region with the vectors of phases A..C.
-    static constexpr int BIG = 2 * MAXPOS * 64;           // K|V chunk
+    static constexpr int BIG = 2 * MP * 64;               // K|V chunk
     static constexpr int OFF_XS = BIG;                    // group sums of act [GD]
     static constexpr int OFF_US = OFF_XS + GD;            // group sums of u [GF]
     static constexpr int OFF_U = rup(OFF_US + GF, 4);     // u [F] (phase D) or:
     static constexpr int OFF_ACT = OFF_U;                 //   act [D]
     static constexpr int OFF_QH = OFF_ACT + D;            //   q_h [64]
-    static constexpr int OFF_SC = OFF_QH + 64;            //   scores [MAXPOS]
-    static constexpr int OFF_PART = OFF_SC + MAXPOS;      //   own partial [PW] + gathered [ATT_S-1][PW] + kv_new [128]
+    static constexpr int OFF_SC = OFF_QH + 64;            //   scores [MP]
+    static constexpr int OFF_PART = OFF_SC + MP;          //   own partial [PW] + gathered [SLOTS-1][PW] + kv_new [128]
     // [4][64] scratch, also the staging of each phase's outputs: outside the
     // u region, because phase D writes it while other waves may still be
     // reading u
-    static constexpr int OFF_COMB = rup(cmax(OFF_PART + ATT_S * PW + 128, OFF_U + F), 4);
+    static constexpr int OFF_COMB = rup(cmax(OFF_PART + SLOTS * PW + 128, OFF_U + F), 4);
     static constexpr int OFF_RED = rup(OFF_COMB + 4 * 64, 4);
     static constexpr int OFF_FLAG = OFF_RED + 16;
     static constexpr int LDS_FLOATS = OFF_FLAG + 16;
     static_assert(D % NT == 0 && F % NT == 0 && NT == 256, "widths");
     static_assert(LPR_D > 0 && LPR_F > 0, "width has no GEMV lane mapping");
     static_assert(NFREE >= 64 && KV_ROWS * NFREE >= 2 * D, "K/V rows need workgroups without attention duty");
+    static_assert(TS >= 1 && TS * H <= NFREE, "tail splits");
     static_assert(LDS_FLOATS * 4 <= 160 * 1024, "LDS budget");
     // Regions that are live in the same phase must not overlap:
     //   all phases: the K|V chunk (BIG), xs, us, comb, red, flag;
@@ -147,11 +160,11 @@ struct Cfg {
     static constexpr bool disjoint(int a, int na, int b, int nb) { return a + na <= b || b + nb <= a; }
     static_assert(disjoint(0, BIG, OFF_XS, GD) && disjoint(OFF_XS, GD, OFF_US, GF), "chunk / group sums");
     static_assert(disjoint(OFF_US, GF, OFF_U, F) && disjoint(OFF_XS, GD, OFF_U, F), "group sums / u");
-    static_assert(disjoint(OFF_ACT, D, OFF_QH, 64) && disjoint(OFF_QH, 64, OFF_SC, MAXPOS) &&
-                      disjoint(OFF_SC, MAXPOS, OFF_PART, ATT_S * PW + 128) &&
-                      disjoint(OFF_ACT, D, OFF_PART, ATT_S * PW + 128),
+    static_assert(disjoint(OFF_ACT, D, OFF_QH, 64) && disjoint(OFF_QH, 64, OFF_SC, MP) &&
+                      disjoint(OFF_SC, MP, OFF_PART, SLOTS * PW + 128) &&
+                      disjoint(OFF_ACT, D, OFF_PART, SLOTS * PW + 128),
                   "phase A regions");
-    static_assert(disjoint(OFF_COMB, 4 * 64, OFF_U, F) && disjoint(OFF_COMB, 4 * 64, OFF_PART, ATT_S * PW + 128) &&
+    static_assert(disjoint(OFF_COMB, 4 * 64, OFF_U, F) && disjoint(OFF_COMB, 4 * 64, OFF_PART, SLOTS * PW + 128) &&
                       disjoint(OFF_COMB, 4 * 64, OFF_ACT, D) && disjoint(OFF_COMB, 4 * 64, 0, BIG),
                   "staging / vectors");
     static_assert(disjoint(OFF_RED, 16, OFF_COMB, 4 * 64) && disjoint(OFF_FLAG, 16, OFF_RED, 16) &&
@@ -183,6 +196,8 @@ struct Args {
     int64_t* next;
     int t0;       // position of the appended row (T_past)
     int chunk;    // cached positions per attention split
+    int tail0;    // first position of the tail splits (ATT_S * chunk)
+    int tail_chunk;  // cached positions per tail split, 0 when T_past <= ATT_S * MP
     uint32_t epoch;
     uint64_t* x;  // exchange words
     const Role* roles;
@@ -806,80 +821,86 @@ __device__ __forceinline__ float gelu_erf(float x) {
     return 0.5f * x * (1.0f + erff(x * 0.70710678118654752440f));
 }
 
-// K/V rows of one head at positions [p0, p0 + npos) of one layer's cache,
-// DMA'd into LDS: K at big[0 ..), V at big[MAXPOS * 64 ..), 64 floats each.
-template <int D>
+// K/V rows of one head at positions [p0, p0 + npos) of one layer's cache
+// (npos <= MP), DMA'd into LDS: K at big[0 ..), V at big[MP * 64 ..), 64
+// floats per row.  Row t holds its 16-byte chunk c (dimensions 4c .. 4c+3) in slot
+// (c + t) & 15, so lanes that read chunk c of consecutive rows touch
+// different banks while c itself stays uniform across the wave.  One DMA
+// instruction fills 4 rows: lane L lands in slot L & 15 of row L >> 4 and so
+// fetches that row's chunk ((L & 15) - t) & 15.
+template <int D, int MP>
 __device__ __forceinline__ void kv_chunk_dma(const float* kc_l, const float* vc_l, int head, int p0,
                                              int npos, float* big) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int rounds = (npos + 15) / 16;
     for (int rd = 0; rd < rounds; ++rd) {
         const int pl = rd * 16 + wave * 4;
-        int pos = p0 + pl + (lane >> 4);
-        if (pos >= p0 + npos) pos = p0;  // in-range address; the slot is never read
-        const size_t off = (size_t)pos * D + head * 64 + (lane & 15) * 4;
+        const int t = pl + (lane >> 4);
+        const int pos = t < npos ? p0 + t : p0;  // in-range address; the slot is never read
+        const size_t off = (size_t)pos * D + head * 64 + ((((lane & 15) - t) & 15) << 2);
         __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kc_l + off),
                                          (__attribute__((address_space(3))) void*)(big + pl * 64), 16, 0, 0);
         __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vc_l + off),
-                                         (__attribute__((address_space(3))) void*)(big + MAXPOS * 64 + pl * 64),
+                                         (__attribute__((address_space(3))) void*)(big + MP * 64 + pl * 64),
                                          16, 0, 0);
     }
 }
 
-// Softmax partial of q over the npos cached positions in LDS: one lane per
-// position for the scores (rotated 16-byte reads, four in flight, no
-// cross-lane reduction), then lanes = dimensions for sum_t p_t V_t.  Writes
-// (max, sum, acc[64]) to part[0], part[1], part[2 ..].
+// Softmax partial of q over the npos cached positions in LDS (rows laid out
+// by kv_chunk_dma).  Scores: thread t takes position t; each step reads four
+// chunks of its K row (rotated slots, no bank conflicts) and the same four
+// chunks of q (one address for the whole wave, a broadcast).
+// Then lanes = dimensions for sum_t p_t V_t, four positions per step with
+// two accumulator sets.  Writes (max, sum, acc[64]) to part[0], part[1],
+// part[2 ..].
+template <int MP>
 __device__ __forceinline__ void attend_chunk(const float* big, const float* qh, int npos, float* sc,
                                              float* comb, float* red, float* part, const Args& a, int l) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     float s = -INFINITY;
     if (tid < npos) {
         const float* kr = big + tid * 64;
-        float acc0 = 0.f, acc1 = 0.f;
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int c0 = 0; c0 < 16; c0 += 4) {
             float4 k4[4], q4[4];
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                const int cc = (c0 + c + tid) & 15;
-                k4[c] = *reinterpret_cast<const float4*>(kr + cc * 4);
-                q4[c] = *reinterpret_cast<const float4*>(qh + cc * 4);
+                k4[c] = *reinterpret_cast<const float4*>(kr + (((c0 + c + tid) & 15) << 2));
+                q4[c] = reinterpret_cast<const float4*>(qh)[c0 + c];  // same address in every lane
             }
 #pragma unroll
-            for (int c = 0; c < 4; c += 2) {
-                acc0 = fmaf(q4[c].x, k4[c].x, fmaf(q4[c].y, k4[c].y, fmaf(q4[c].z, k4[c].z, fmaf(q4[c].w, k4[c].w, acc0))));
-                acc1 = fmaf(q4[c + 1].x, k4[c + 1].x,
-                            fmaf(q4[c + 1].y, k4[c + 1].y, fmaf(q4[c + 1].z, k4[c + 1].z, fmaf(q4[c + 1].w, k4[c + 1].w, acc1))));
-            }
+            for (int c = 0; c < 4; ++c)
+                acc[c] = fmaf(q4[c].x, k4[c].x, fmaf(q4[c].y, k4[c].y, fmaf(q4[c].z, k4[c].z, fmaf(q4[c].w, k4[c].w, acc[c]))));
         }
-        s = (acc0 + acc1) * 0.125f;
+        s = ((acc[0] + acc[1]) + (acc[2] + acc[3])) * 0.125f;
     }
     stamp(a, l, 12);
     const float M = block_reduce<true>(s, red);
     const float pe = (tid < npos) ? expf(s - M) : 0.f;
-    if (tid < MAXPOS) sc[tid] = pe;
+    if (tid < MP) sc[tid] = pe;
     const float Ls = block_reduce<false>(pe, red + 4);
     stamp(a, l, 13);
-    // sum_t p_t V_t: lane (wave w, row r, c) takes dims 4c..4c+3 of positions
-    // 4w + r + 16i; the 4 rows of a wave are summed lane-wise, then the 4
-    // waves through LDS.
-    const float* vbase = big + MAXPOS * 64;
+    // sum_t p_t V_t: lane (wave w, row r, c) takes dimensions 4c .. 4c+3 of
+    // positions 4w + r + 16i; the 4 rows of a wave are summed lane-wise,
+    // then the 4 waves through LDS.
+    const float* vbase = big + MP * 64;
     const int row = lane >> 4, c4 = lane & 15;
     float4 a0 = make_float4(0.f, 0.f, 0.f, 0.f), a1 = a0;
+    auto vrow = [&](int t) { return *reinterpret_cast<const float4*>(vbase + t * 64 + (((c4 + t) & 15) << 2)); };
+    auto acc4 = [](float4& acc, float p, const float4& v) {
+        acc.x = fmaf(p, v.x, acc.x); acc.y = fmaf(p, v.y, acc.y); acc.z = fmaf(p, v.z, acc.z); acc.w = fmaf(p, v.w, acc.w);
+    };
     int t = 4 * wave + row;
-    for (; t + 16 < npos; t += 32) {
-        const float p0 = sc[t], p1 = sc[t + 16];
-        const float4 v0 = *reinterpret_cast<const float4*>(vbase + t * 64 + c4 * 4);
-        const float4 v1 = *reinterpret_cast<const float4*>(vbase + (t + 16) * 64 + c4 * 4);
-        a0.x = fmaf(p0, v0.x, a0.x); a0.y = fmaf(p0, v0.y, a0.y); a0.z = fmaf(p0, v0.z, a0.z); a0.w = fmaf(p0, v0.w, a0.w);
-        a1.x = fmaf(p1, v1.x, a1.x); a1.y = fmaf(p1, v1.y, a1.y); a1.z = fmaf(p1, v1.z, a1.z); a1.w = fmaf(p1, v1.w, a1.w);
+    for (; t + 48 < npos; t += 64) {
+        const float p0 = sc[t], p1 = sc[t + 16], p2 = sc[t + 32], p3 = sc[t + 48];
+        const float4 v0 = vrow(t), v1 = vrow(t + 16), v2 = vrow(t + 32), v3 = vrow(t + 48);
+        acc4(a0, p0, v0);
+        acc4(a1, p1, v1);
+        acc4(a0, p2, v2);
+        acc4(a1, p3, v3);
     }
-    for (; t < npos; t += 16) {
-        const float p0 = sc[t];
-        const float4 v0 = *reinterpret_cast<const float4*>(vbase + t * 64 + c4 * 4);
-        a0.x = fmaf(p0, v0.x, a0.x); a0.y = fmaf(p0, v0.y, a0.y); a0.z = fmaf(p0, v0.z, a0.z); a0.w = fmaf(p0, v0.w, a0.w);
-    }
+    for (; t < npos; t += 16) acc4(a0, sc[t], vrow(t));
     float r4[4] = {a0.x + a1.x, a0.y + a1.y, a0.z + a1.z, a0.w + a1.w};
 #pragma unroll
     for (int k = 0; k < 4; ++k) {  // lane-wise sum of the 4 rows
@@ -934,8 +955,8 @@ struct Lds {
         qh = lds + C::OFF_QH;
         sc = lds + C::OFF_SC;
         own = lds + C::OFF_PART;  // own partial [PW]
-        gpart = own + PW;                   // splits 1 .. ATT_S-1 [ATT_S-1][PW]
-        knew = gpart + (C::ATT_S - 1) * PW; // [64]
+        gpart = own + PW;                   // slots 1 .. SLOTS-1 [SLOTS-1][PW]
+        knew = gpart + (C::SLOTS - 1) * PW; // [64]
         vnew = knew + 64;         // [64]
         comb = lds + C::OFF_COMB; // [4][64] scratch
         red = lds + C::OFF_RED;
@@ -1065,8 +1086,10 @@ __device__ __forceinline__ bool phase_a_ln(const Args& a, const Lds<D, F>& S, co
     return true;
 }
 
-// Every layer for an attention workgroup (head h, split s).
-template <int D, int F>
+// Every layer for an attention workgroup (head h, split s).  TAIL: the
+// cache reaches past the attention splits, and the head leader also merges
+// the tail splits' partials.
+template <int D, int F, bool TAIL>
 __device__ __forceinline__ bool attention_role(const Args& a, const Lds<D, F>& S, const Role& role,
                                                float (&r)[LnRegs<D>::PER]) {
     using C = Cfg<D, F>;
@@ -1082,7 +1105,7 @@ __device__ __forceinline__ bool attention_role(const Args& a, const Lds<D, F>& S
     WBlk<C::CPL_D, C::NP_Q> wqh;
     BcdW<D, F> w;
     LnRegs<D> ln1;
-    if (npos > 0) kv_chunk_dma<D>(a.kc, a.vc, h, p0, npos, S.big);
+    if (npos > 0) kv_chunk_dma<D, C::MP>(a.kc, a.vc, h, p0, npos, S.big);
     wblk_load<C::LPR_D, C::CPL_D, C::NP_Q>(wqh, a.wq + O::QO, a.ws + O::QS, D, h * 64, 64);
     ln_load<D>(ln1, a.ln, a.ln + D);
     for (int l = 0; l < a.L; ++l) {
@@ -1110,43 +1133,55 @@ __device__ __forceinline__ bool attention_role(const Args& a, const Lds<D, F>& S
         stamp(a, l, 3);
         // phase B and C weights load behind the attention
         load_bc<D, F>(w, wq, ws, ln, -1);
-        attend_chunk(S.big, S.qh, npos, S.sc, S.comb, S.red + 8, S.own, a, l);
+        attend_chunk<C::MP>(S.big, S.qh, npos, S.sc, S.comb, S.red + 8, S.own, a, l);
         stamp(a, l, 4);
         if (!leader) {
-            uint64_t* pw = X + C::XA_PART + (size_t)(h * AS + role.split) * PW;
+            uint64_t* pw = X + C::XA_PART + (size_t)(h * C::SLOTS + role.split) * PW;
             if (tid < PW) ll_put(pw + tid, S.own[tid], ep);
             // the next layer's chunk: this workgroup's next exchange read
             // (phase C) is microseconds away
-            if (!last && npos > 0) kv_chunk_dma<D>(kc_l + lstride, vc_l + lstride, h, p0, npos, S.big);
+            if (!last && npos > 0) kv_chunk_dma<D, C::MP>(kc_l + lstride, vc_l + lstride, h, p0, npos, S.big);
         } else {
-            // ---- A2: merge the splits and the new position -> attn_h
-            if (!ll_gather<cdiv((AS - 1) * PW + 128, NT), false>(
-                    Range{X + C::XA_PART + (size_t)(h * AS + 1) * PW, (AS - 1) * PW, S.gpart},
+            // ---- A2: merge the splits (and the tail splits when the cache
+            // reaches past them) and the new position -> attn_h
+            constexpr int NS = TAIL ? C::SLOTS : AS;  // partial slots merged
+            if (!ll_gather<cdiv((NS - 1) * PW + 128, NT), false>(
+                    Range{X + C::XA_PART + (size_t)(h * C::SLOTS + 1) * PW, (NS - 1) * PW, S.gpart},
                     Range{X + C::XA_KV + h * 64, 64, S.knew}, Range{X + C::XA_KV + D + h * 64, 64, S.vnew}, ep,
                     a.err, S.s_flag))
                 return false;
             stamp(a, l, 5);
+            stamp(a, l, 16);
             if (tid < 64) {
+                // every split's (max, sum, acc[tid]) into registers first, so
+                // the LDS reads overlap; an empty split has max -inf, sum 0 and
+                // acc 0, and its weight exp(-inf) is exactly 0
+                float pm[NS], pl[NS], pa[NS];
+                pm[0] = S.own[0];
+                pl[0] = S.own[1];
+                pa[0] = S.own[2 + tid];
+#pragma unroll
+                for (int s = 1; s < NS; ++s) {
+                    pm[s] = S.gpart[(s - 1) * PW];
+                    pl[s] = S.gpart[(s - 1) * PW + 1];
+                    pa[s] = S.gpart[(s - 1) * PW + 2 + tid];
+                }
                 const float snew = wave_reduce<false>(S.qh[tid] * S.knew[tid]) * 0.125f;
-                float M = fmaxf(snew, S.own[0]);
-                for (int s = 0; s < AS - 1; ++s) M = fmaxf(M, S.gpart[s * PW]);
+                float M = snew;
+#pragma unroll
+                for (int s = 0; s < NS; ++s) M = fmaxf(M, pm[s]);
                 float Ls = expf(snew - M);
                 float A = Ls * S.vnew[tid];
-                if (S.own[0] != -INFINITY) {
-                    const float wgt = expf(S.own[0] - M);
-                    Ls = fmaf(wgt, S.own[1], Ls);
-                    A = fmaf(wgt, S.own[2 + tid], A);
-                }
-                for (int s = 0; s < AS - 1; ++s) {
-                    const float ms = S.gpart[s * PW];
-                    if (ms == -INFINITY) continue;
-                    const float wgt = expf(ms - M);
-                    Ls = fmaf(wgt, S.gpart[s * PW + 1], Ls);
-                    A = fmaf(wgt, S.gpart[s * PW + 2 + tid], A);
+#pragma unroll
+                for (int s = 0; s < NS; ++s) {
+                    const float wgt = expf(pm[s] - M);
+                    Ls = fmaf(wgt, pl[s], Ls);
+                    A = fmaf(wgt, pa[s], A);
                 }
                 ll_put_rep(X + C::XB_ATT, D, h * 64 + tid, A / Ls, ep);
             }
-            if (!last && npos > 0) kv_chunk_dma<D>(kc_l + lstride, vc_l + lstride, h, p0, npos, S.big);
+            stamp(a, l, 17);
+            if (!last && npos > 0) kv_chunk_dma<D, C::MP>(kc_l + lstride, vc_l + lstride, h, p0, npos, S.big);
         }
         // ---- C, D (no phase B)
         load_d<D, F>(w, wq, ws);
@@ -1163,17 +1198,25 @@ __device__ __forceinline__ bool attention_role(const Args& a, const Lds<D, F>& S
 }
 
 // Every layer for a workgroup without attention duty: new K/V rows in
-// phase A; phases B, C, D like every workgroup.
-template <int D, int F>
+// phase A (with TAIL, then its tail split's partial); phases B, C, D like
+// every workgroup.
+template <int D, int F, bool TAIL>
 __device__ __forceinline__ bool free_role(const Args& a, const Lds<D, F>& S, const Role& role,
                                           float (&r)[LnRegs<D>::PER]) {
     using C = Cfg<D, F>;
     using O = Off<D, F>;
     const uint32_t ep = a.epoch;
+    const int tid = threadIdx.x;
     const size_t lstride = (size_t)a.kv_seqs * a.t_cap * D;
+    // tail split: positions [tp0, tp0 + tnpos) of head th (none while the
+    // cache ends within the attention splits' reach)
+    const int th = TAIL ? role.tail_head : -1;
+    const int tp0 = a.tail0 + role.tail_idx * a.tail_chunk;
+    const int tnpos = th >= 0 ? max(0, min(a.t0, tp0 + a.tail_chunk) - tp0) : 0;
     WBlk<C::CPL_D, C::NP_KV> wkv;
     BcdW<D, F> w;
     LnRegs<D> ln1;
+    if (tnpos > 0) kv_chunk_dma<D, MAXPOS>(a.kc, a.vc, th, tp0, tnpos, S.big);
     if (role.kv_rows > 0)
         wblk_load<C::LPR_D, C::CPL_D, C::NP_KV>(wkv, a.wq + O::QO, a.ws + O::QS, D, D + role.kv_row0, role.kv_rows);
     ln_load<D>(ln1, a.ln, a.ln + D);
@@ -1202,6 +1245,32 @@ __device__ __forceinline__ bool free_role(const Args& a, const Lds<D, F>& S, con
                 }
             }
         }
+        if (tnpos > 0) {
+            // ---- tail split: q_h and the softmax partial over its positions.
+            // The q_h rows are loaded here, not a phase ahead: they would hold
+            // 40 registers through every step, tail or not.
+            WBlk<C::CPL_D, C::NP_Q> wqh;
+            wblk_load<C::LPR_D, C::CPL_D, C::NP_Q>(wqh, wq + O::QO, ws + O::QS, D, th * 64, 64);
+            float o[C::NP_Q];
+            dot_rows<C::LPR_D, C::CPL_D, C::NP_Q>(wqh, S.act, S.xs, o, a);
+#pragma unroll
+            for (int p = 0; p < C::NP_Q; ++p) {
+                const int rr = out_row<C::LPR_D>(p);
+                if (rr >= 0 && rr < 64) S.qh[rr] = o[p];
+            }
+            __builtin_amdgcn_s_waitcnt(0);  // the tail chunk DMA has landed
+            lds_barrier();
+            attend_chunk<MAXPOS>(S.big, S.qh, tnpos, S.sc, S.comb, S.red + 8, S.own, a, l);
+            uint64_t* pw = X + C::XA_PART + (size_t)(th * C::SLOTS + C::ATT_S + role.tail_idx) * PW;
+            if (tid < PW) ll_put(pw + tid, S.own[tid], ep);
+            if (!last) kv_chunk_dma<D, MAXPOS>(kc_l + lstride, vc_l + lstride, th, tp0, tnpos, S.big);
+        } else if (th >= 0) {
+            // a tail split past the last position: the leader still gathers
+            // every tail slot, so publish an empty partial (max -inf, sum 0)
+            uint64_t* pw = X + C::XA_PART + (size_t)(th * C::SLOTS + C::ATT_S + role.tail_idx) * PW;
+            if (tid < PW) ll_put(pw + tid, tid == 0 ? -INFINITY : 0.f, ep);
+        }
+        stamp(a, l, 18);
         load_bc<D, F>(w, wq, ws, ln, role.o_row0);
         // ---- B, C, D
         if (!phase_b<D, F>(a, S, X, w, role.o_row0, l)) return false;
@@ -1218,7 +1287,7 @@ __device__ __forceinline__ bool free_role(const Args& a, const Lds<D, F>& S, con
     return true;
 }
 
-template <int D, int F>
+template <int D, int F, bool TAIL>
 __global__ __launch_bounds__(NT, 1) void k_decode_step(Args a) {
     using C = Cfg<D, F>;
     extern __shared__ float lds[];
@@ -1244,7 +1313,7 @@ __global__ __launch_bounds__(NT, 1) void k_decode_step(Args a) {
         lds_barrier();  // s_flag initialised
     }
 
-    const bool ok = role.head >= 0 ? attention_role<D, F>(a, S, role, r) : free_role<D, F>(a, S, role, r);
+    const bool ok = role.head >= 0 ? attention_role<D, F, TAIL>(a, S, role, r) : free_role<D, F, TAIL>(a, S, role, r);
     if (!ok) return;
     // LM-head rows and LN_f, loaded while the last layer's FFN-down output
     // is still in flight
@@ -1345,7 +1414,7 @@ static void build_roles(Role* roles) {
     for (int h = 0; h < C::H; ++h) ++nh_x[h % NXCD];
     for (int w = 0; w < NWG; ++w) {
         Role& r = roles[w];
-        r = Role{-1, 0, 0, 0, -1, 0, 0, 0};
+        r = Role{-1, 0, 0, 0, -1, -1, 0, 0};
         const int x = w % NXCD, slot = w / NXCD;
         if (slot < nh_x[x] * C::ATT_S) {
             r.head = (slot / C::ATT_S) * NXCD + x;
@@ -1360,6 +1429,23 @@ static void build_roles(Role* roles) {
         r.o_row0 = i * C::O_ROWS < D ? i * C::O_ROWS : -1;
         r.kv_row0 = row0;
         r.kv_rows = row0 < 2 * D ? (2 * D - row0 < C::KV_ROWS ? 2 * D - row0 : C::KV_ROWS) : 0;
+    }
+    // TS tail splits per head on free workgroups, first from the XCD of the
+    // head (its leader's), then from any XCD
+    bool used[NWG] = {};
+    for (int h = 0; h < C::H; ++h) {
+        const int xh = h % NXCD;
+        for (int j = 0; j < C::TS; ++j) {
+            int pick = -1;
+            for (int pass = 0; pass < 2 && pick < 0; ++pass)
+                for (int i = 0; i < nfree && pick < 0; ++i) {
+                    const int w = free_list[i];
+                    if (!used[w] && (pass == 1 || w % NXCD == xh)) pick = w;
+                }
+            used[pick] = true;  // TS * H <= NFREE: a free workgroup is always left
+            roles[pick].tail_head = h;
+            roles[pick].tail_idx = j;
+        }
     }
 }
 
@@ -1391,12 +1477,13 @@ size_t persistent_xbuf_bytes(int L, int d, int F, int H, int B, int V) {
     return 8 * (lw * L + 2 * pd::NWG) + sizeof(pd::Role) * pd::NWG + 256;
 }
 
-// The largest T_past the persistent step handles (its splits of <= MAXPOS
+// The largest T_past the persistent step handles (its attention splits of
+// <= MP positions and tail splits of <= MAXPOS positions;
 // positions each).
 int persistent_max_position(int d, int F) {
-    if (d == 768 && F == 3072) return pd::Cfg<768, 3072>::ATT_S * pd::MAXPOS;
-    if (d == 1024 && F == 4096) return pd::Cfg<1024, 4096>::ATT_S * pd::MAXPOS;
-    if (d == 1536 && F == 6144) return pd::Cfg<1536, 6144>::ATT_S * pd::MAXPOS;
+    if (d == 768 && F == 3072) return pd::Cfg<768, 3072>::REACH;
+    if (d == 1024 && F == 4096) return pd::Cfg<1024, 4096>::REACH;
+    if (d == 1536 && F == 6144) return pd::Cfg<1536, 6144>::REACH;
     return 0;
 }
 
@@ -1439,18 +1526,33 @@ static hipError_t launch_t(const PersistentArgs& p, hipStream_t st) {
     a.nib = 0x0F0F0F0Fu;
     a.a8 = p.a8;
     a.trace = static_cast<uint64_t*>(p.trace);
-    const int chunk = (p.t0 + C::ATT_S - 1) / C::ATT_S;
-    if (chunk > pd::MAXPOS) return hipErrorInvalidValue;
+    // positions [0, t0): ATT_S splits of `chunk`; past ATT_S * MP, the rest
+    // goes to TS tail splits of `tail_chunk`
+    int chunk = (p.t0 + C::ATT_S - 1) / C::ATT_S;
+    int tail_chunk = 0;
+    if (chunk > C::MP) {
+        chunk = C::MP;
+        tail_chunk = (p.t0 - C::ATT_S * C::MP + C::TS - 1) / C::TS;
+        if (tail_chunk > pd::MAXPOS) return hipErrorInvalidValue;
+    }
     a.chunk = chunk < 1 ? 1 : chunk;
+    a.tail0 = C::ATT_S * a.chunk;
+    a.tail_chunk = tail_chunk;
     static bool attr_set = false;
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)pd::k_decode_step<D, F>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           (int)(sizeof(float) * C::LDS_FLOATS));
-        if (e != hipSuccess) return e;
+        for (const void* k : {(const void*)pd::k_decode_step<D, F, false>, (const void*)pd::k_decode_step<D, F, true>}) {
+            hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               (int)(sizeof(float) * C::LDS_FLOATS));
+            if (e != hipSuccess) return e;
+        }
         attr_set = true;
     }
-    pd::k_decode_step<D, F><<<dim3(pd::NWG), dim3(pd::NT), sizeof(float) * C::LDS_FLOATS, st>>>(a);
+    // the tail-capable step only once the cache reaches past the attention
+    // splits; the other keeps the registers the tail code would take
+    if (tail_chunk > 0)
+        pd::k_decode_step<D, F, true><<<dim3(pd::NWG), dim3(pd::NT), sizeof(float) * C::LDS_FLOATS, st>>>(a);
+    else
+        pd::k_decode_step<D, F, false><<<dim3(pd::NWG), dim3(pd::NT), sizeof(float) * C::LDS_FLOATS, st>>>(a);
     return hipGetLastError();
 }
 

@@ -75,15 +75,23 @@ def test_persistent_tokens_only(oracle_mod):
     _teacher_forced(oracle_mod, w, 1, 40, None, tokens, 16, TOL["small"], binding.MT_DECODE_PERSISTENT)
 
 
-def test_decode_across_persistent_limit(oracle_mod):
-    """Large width (8 attention splits of <= 256 positions): positions
-    2040 .. 2055 cross T_past = 2048, where the per-operation kernels take
-    over; both must match the oracle."""
+@pytest.mark.parametrize("width,P,steps", [("medium", 2040, 16), ("medium", 2488, 16), ("large", 2040, 16),
+                                            ("large", 2490, 14), ("small", 4090, 12)])
+def test_persistent_reach_past_attention_splits(oracle_mod, width, P, steps):
+    """The attention splits hold 8 x 256 positions at medium and large width
+    (16 x 256 at small); positions past that go to tail splits on the
+    workgroups without attention duty.  Decoding crosses into the tail
+    (2040 .. 2055) and fills the pages' default 2504-position cache to its
+    last slot ("MuScriptor Medium -- optimized W4A32 ONNX Runtime", "Quick
+    smoke test"), all on the persistent step, against the oracle.  Short
+    tails leave some tail splits without positions (they publish empty
+    partials)."""
     _dev()
-    shape = synth.ModelShape("large", 1, 1536, 24, 6144)
+    base = WIDTHS[width]
+    shape = synth.ModelShape(base.name, 1, base.d_model, base.n_heads, base.d_ff)
     w = synth.model_weights(shape, 43)
-    prefix = np.random.default_rng(9).standard_normal((1, 2040, 1536)).astype(np.float32)
-    _teacher_forced(oracle_mod, w, 1, 2060, prefix, None, 16, TOL["large"], binding.MT_DECODE_AUTO)
+    prefix = np.random.default_rng(9).standard_normal((1, P, shape.d_model)).astype(np.float32)
+    _teacher_forced(oracle_mod, w, 1, P + steps, prefix, None, steps, TOL[width], binding.MT_DECODE_PERSISTENT)
 
 
 def test_persistent_long_cache_small_width(oracle_mod):
