@@ -35,7 +35,7 @@ MT_FLAG_DENSE_F32 = 4
 EXPORTED = ("mt_pack_int4", "mt_pack_f16", "mt_create", "mt_prefill", "mt_decode_step", "mt_reset",
             "mt_position", "mt_kv_cache", "mt_check", "mt_set_decode_path", "mt_destroy",
             "mt_last_error", "mt_debug_dequant", "mt_debug_matmul", "mt_debug_trace",
-            "mt_prefill_seq", "mt_reset_seq", "mt_position_seq", "mt_cfg_combine")
+            "mt_prefill_seq", "mt_reset_seq", "mt_position_seq", "mt_cfg_combine", "mt_prefill_noalloc")
 
 
 class mt_config(ctypes.Structure):
@@ -93,13 +93,14 @@ def lib() -> ctypes.CDLL:
     L.mt_debug_matmul.argtypes = [vp, i32, i32, vp, i32, vp, vp]
     L.mt_debug_trace.argtypes = [vp, vp, i64]
     L.mt_prefill_seq.argtypes = [vp, i32, vp, i32, vp, i32, vp, vp, vp]
+    L.mt_prefill_noalloc.argtypes = [vp, vp, i32, vp, i32, vp, vp, vp]
     L.mt_reset_seq.argtypes = [vp, i32]
     L.mt_position_seq.argtypes = [vp, i32, ctypes.POINTER(i32)]
     L.mt_cfg_combine.argtypes = [vp, i32, i32, ctypes.c_float, vp, vp, vp, vp]
     for name in ("mt_pack_int4", "mt_pack_f16", "mt_create", "mt_prefill", "mt_decode_step", "mt_reset",
                  "mt_position", "mt_kv_cache", "mt_check", "mt_set_decode_path",
                  "mt_debug_dequant", "mt_debug_matmul", "mt_debug_trace",
-                 "mt_prefill_seq", "mt_reset_seq", "mt_position_seq", "mt_cfg_combine"):
+                 "mt_prefill_seq", "mt_reset_seq", "mt_position_seq", "mt_cfg_combine", "mt_prefill_noalloc"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -251,6 +252,18 @@ class Decoder:
             assert prefix.is_contiguous() and prefix.shape[-1] == self.d
         check(lib().mt_prefill(self._h, _ptr(tokens), S, _ptr(prefix), P, _ptr(logits), _ptr(next),
                                _stream(stream)), "mt_prefill")
+        return logits, next
+
+    def prefill_noalloc(self, tokens=None, prefix=None, logits=None, next=None, stream=None):
+        """mt_prefill_noalloc: mt_prefill on the library's fixed device
+        workspace (no allocation by the library)."""
+        logits, next = self._outputs(logits, next)
+        S = 0 if tokens is None else int(tokens.shape[-1])
+        P = 0 if prefix is None else int(prefix.shape[-2])
+        if prefix is not None:
+            assert prefix.is_contiguous() and prefix.shape[-1] == self.d
+        check(lib().mt_prefill_noalloc(self._h, _ptr(tokens), S, _ptr(prefix), P, _ptr(logits), _ptr(next),
+                                       _stream(stream)), "mt_prefill_noalloc")
         return logits, next
 
     def prefill_seq(self, b: int, tokens=None, prefix=None, logits=None, next=None, stream=None):

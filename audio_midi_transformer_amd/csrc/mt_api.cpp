@@ -81,6 +81,8 @@ struct mt_model {
     // prefill workspace
     size_t pf_rows = 0;
     float* pf = nullptr;
+    // this device's fixed workspace of mt_prefill_noalloc (not owned)
+    float* noalloc_ws = nullptr;
 };
 
 namespace {
@@ -310,6 +312,9 @@ int mt_create(const mt_config* cfg, const mt_weights* w, int weights_on_device, 
         return code;
     };
     if (hipGetDevice(&m->device) != hipSuccess) return bail(fail(MT_ERR_HIP, "hipGetDevice failed"));
+    // the fixed workspace of mt_prefill_noalloc on this device; without it
+    // that entry point reports an error, the others are unaffected
+    if (noalloc_scratch_setup(m->device, &m->noalloc_ws) != hipSuccess) m->noalloc_ws = nullptr;
 
     // projection shapes [N, K]
     size_t qbytes = 0, sfloats = 0;
@@ -397,9 +402,10 @@ int mt_create(const mt_config* cfg, const mt_weights* w, int weights_on_device, 
 namespace {
 
 // Rows [prefix ; embed(tokens)] of sequences b0 .. b0+nb-1, each appended at
-// its own position.
+// its own position.  The row workspace is the model's own (grown on demand),
+// or with `fixed_ws` the device's fixed workspace of mt_prefill_noalloc.
 int prefill_rows(mt_model* m, int b0, int nb, const int64_t* tokens, int32_t S, const float* prefix, int32_t P,
-                 float* logits, int64_t* next, void* stream, const char* who) {
+                 float* logits, int64_t* next, void* stream, const char* who, bool fixed_ws = false) {
     if (S < 0 || P < 0 || (int64_t)S + P < 1) return fail(MT_ERR_INVALID_ARG, "%s: need P + S >= 1 (P=%d S=%d)", who, P, S);
     if ((S > 0 && !tokens) || (P > 0 && !prefix)) return fail(MT_ERR_INVALID_ARG, "%s: NULL tokens or prefix", who);
     const mt_config& c = m->c;
@@ -410,10 +416,22 @@ int prefill_rows(mt_model* m, int b0, int nb, const int64_t* tokens, int32_t S, 
                         m->pos.t[b], b, c.t_cap);
     hipStream_t st = (hipStream_t)stream;
     const size_t M = (size_t)nb * R;
-    int rc = ensure_prefill_ws(m, M);
-    if (rc) return rc;
     const int d = c.d_model;
-    float* x = m->pf;
+    float* x = nullptr;
+    int rc = MT_OK;
+    if (fixed_ws) {
+        const size_t need = M * (4 * (size_t)d + c.d_ff), have = noalloc_scratch_floats();
+        if (!m->noalloc_ws) return fail(MT_ERR_HIP, "%s: the fixed device workspace is not available", who);
+        if (need > have)
+            return fail(MT_ERR_UNSUPPORTED,
+                        "%s: %zu rows need %zu workspace floats, the fixed workspace holds %zu (at most %zu rows)", who,
+                        M, need, have, have / (4 * (size_t)d + c.d_ff));
+        x = m->noalloc_ws;
+    } else {
+        rc = ensure_prefill_ws(m, M);
+        if (rc) return rc;
+        x = m->pf;
+    }
     float* a = x + M * d;
     float* q = a + M * d;
     float* att = q + M * d;
@@ -436,6 +454,12 @@ int mt_prefill(mt_model* m, const int64_t* tokens, int32_t S, const float* prefi
                float* logits, int64_t* next, void* stream) {
     if (!m || !logits || !next) return fail(MT_ERR_INVALID_ARG, "mt_prefill: NULL model or output");
     return prefill_rows(m, 0, m->c.batch, tokens, S, prefix, P, logits, next, stream, "mt_prefill");
+}
+
+int mt_prefill_noalloc(mt_model* m, const int64_t* tokens, int32_t S, const float* prefix, int32_t P,
+                       float* logits, int64_t* next, void* stream) {
+    if (!m || !logits || !next) return fail(MT_ERR_INVALID_ARG, "mt_prefill_noalloc: NULL model or output");
+    return prefill_rows(m, 0, m->c.batch, tokens, S, prefix, P, logits, next, stream, "mt_prefill_noalloc", true);
 }
 
 int mt_prefill_seq(mt_model* m, int32_t b, const int64_t* tokens, int32_t S, const float* prefix, int32_t P,

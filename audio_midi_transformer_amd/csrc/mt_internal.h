@@ -144,4 +144,10 @@ hipError_t persistent_prepare(void* xbuf, int L, int d, int F, hipStream_t st);
 int persistent_max_position(int d, int F);
 size_t persistent_trace_bytes(int L);
 
+// Fixed workspace of mt_prefill_noalloc (mt_scratch.hip): its size in
+// floats, and the address of the calling device's copy (call with `device`
+// current; the address is looked up once per device and kept).
+size_t noalloc_scratch_floats();
+hipError_t noalloc_scratch_setup(int device, float** out);
+
 }  // namespace mt

@@ -171,6 +171,21 @@ int mt_create(const mt_config* cfg, const mt_weights* w, int weights_on_device, 
 int mt_prefill(mt_model* m, const int64_t* tokens, int32_t S, const float* prefix, int32_t P,
                float* logits, int64_t* next, void* stream);
 
+/* mt_prefill without any allocation, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): same arguments, semantics and errors as
+ * mt_prefill, but the row workspace is a fixed 32 MiB device array that the
+ * library holds on each GPU it runs on until the process ends, instead of
+ * memory grown with hipMalloc.  Calls no hipMalloc, hipFree or allocating
+ * routine.  The workspace takes B * (P + S) * (4 d + d_ff) floats: at most
+ * 8 Mi floats (1024 rows at d = 1024, d_ff = 4096; 682 rows at d = 1536);
+ * larger calls return MT_ERR_UNSUPPORTED before any launch.  Every call on
+ * one GPU uses the same array (it keeps the last call's contents; nothing in
+ * it needs clearing): calls that overlap on one GPU, from different streams
+ * or threads, race; serialise them. */
+int mt_prefill_noalloc(mt_model* m, const int64_t* tokens, int32_t S, const float* prefix, int32_t P,
+                       float* logits, int64_t* next, void* stream);
+
 /* One greedy decode step: token[b] (int64) is appended to sequence b at
  * its own position T_b (the decoder call with one token row and no prefix
  * rows; positions are implied by the cache length: "unifolia/muscriptor-
