@@ -822,6 +822,167 @@ __global__ __launch_bounds__(256) void k_gemm_w4a8(const float* __restrict__ X, 
             }
 }
 
+// INT4 GEMM on BF16 matrix cores with FP32 results (W4A32).  Per group g
+// of 32 inputs the partial sum P = sum_k x_k (u_k - 8) is formed with exact
+// products: every activation is split into three bf16 pieces
+// x = x1 + x2 + x3 (x1 = bf16(x), x2 = bf16(x - x1), x3 = x - x1 - x2; each
+// remainder is exact in FP32 and the last one has at most 8 significant
+// bits, so the split is exact), u - 8 is a bf16 integer, and a product of
+// the two has at most 12 significant bits.  Three v_mfma_f32_16x16x32_bf16
+// per group and 16 x 16 block accumulate the pieces against the codes in
+// FP32, then acc += s_w * P.  The products are those of the FP32 form
+// (x (u - 8) s with the scale applied per group instead of per weight); only
+// the accumulation order differs, inside the same FP32 error bound.  BF16
+// MFMA runs 16x16x32 in 16 cycles where FP32 MFMA needs 8 x 16x16x4 at 32.
+// Tile TM x NT per workgroup (NT = 64, or 32 where 64-column tiles would
+// leave fewer than two workgroups per CU, as for the 504-row O and FFN-down
+// projections), K stages of GK columns, four waves as 2 x 2 of
+// (TM / 2) x (NT / 2).  Operand layout (as the INT8 16x16x32 form): lane l
+// supplies A row l % 16, k = 8 (l / 16) .. + 7, and B row (output column)
+// l % 16, same k; it receives D[4 (l / 16) + r][l % 16].  blockIdx.z takes
+// the kspan-column range of K whose results are added atomically (+=
+// epilogue only), as in the other GEMMs.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// bf16 bits of (a, b), round to nearest even (v_cvt_pk_bf16_f32)
+__device__ __forceinline__ unsigned pk_bf16(float a, float b) {
+    const bf16x2 h = __builtin_convertvector((f32x2){a, b}, bf16x2);
+    return __builtin_bit_cast(unsigned, h);
+}
+__device__ __forceinline__ float bf16_lo(unsigned p) { return __uint_as_float(p << 16); }
+__device__ __forceinline__ float bf16_hi(unsigned p) { return __uint_as_float(p & 0xFFFF0000u); }
+
+template <int TM, int GK, int NT>
+__global__ __launch_bounds__(256) void k_gemm_w4_bf3(const float* __restrict__ X, int ldx, int M, int K,
+                                                     const uint8_t* __restrict__ Wq,
+                                                     const float* __restrict__ Ws, int N,
+                                                     float* __restrict__ Y, int ldy, EpiArgs ep, int kspan) {
+    constexpr int MI = TM / 32;
+    constexpr int NJ = NT / 32;      // 16-column blocks per wave
+    constexpr int WPR = 256 / NT;    // threads per weight row (each GK / WPR columns)
+    constexpr int NG = GK / 32;      // groups per stage
+    constexpr int RS = GK + 8;       // row stride in bf16 (16-byte rows, shifted 4 banks per row)
+    static_assert((GK / WPR) % 8 == 0 && 32 % (GK / WPR) == 0 || (GK / WPR) % 32 == 0, "weight part inside one group");
+    __shared__ __align__(16) unsigned short Ap[3][TM * RS];  // activation pieces x1, x2, x3
+    __shared__ __align__(16) unsigned short Bu[NT * RS];     // codes u - 8
+    __shared__ float Bs_s[NG][NT];                           // weight scales [group][row]
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int m0 = blockIdx.y * TM, n0 = blockIdx.x * NT;
+    const int G = K / 32;
+    const int kb = blockIdx.z * kspan, ke = min(K, kb + kspan);  // this workgroup's K range
+    f32x4 acc[MI][NJ];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // stage loads: TM * GK / 1024 float4 of X per thread; thread t takes
+    // part t % WPR of weight row t / WPR (GK / WPR columns in one group) and
+    // that group's scale
+    constexpr int NA = TM * GK / 4 / 256;
+    constexpr int NW = GK / WPR / 8;  // nibble dwords per thread
+    float4 pa[NA];
+    unsigned pw[NW];
+    float ps = 0.f;
+    const int wrow = tid / WPR, wq = tid % WPR;
+    auto load_stage = [&](int k0) {
+#pragma unroll
+        for (int e = 0; e < NA; ++e) {
+            const int idx = tid + e * 256;
+            const int r = idx / (GK / 4), c = (idx % (GK / 4)) * 4;
+            pa[e] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (m0 + r < M && k0 + c < ke) pa[e] = *reinterpret_cast<const float4*>(X + (size_t)(m0 + r) * ldx + k0 + c);
+        }
+        const int c0 = k0 + wq * (GK / WPR), g = c0 / 32;
+        const bool ok = n0 + wrow < N && c0 < ke;
+#pragma unroll
+        for (int i = 0; i < NW; ++i)
+            pw[i] = ok ? *reinterpret_cast<const unsigned*>(Wq + (size_t)(n0 + wrow) * (K / 2) + c0 / 2 + 4 * i)
+                       : 0x88888888u;
+        ps = ok ? Ws[(size_t)(n0 + wrow) * G + g] : 0.f;
+    };
+    load_stage(kb);
+    for (int k0 = kb; k0 < ke; k0 += GK) {
+        if (k0 != kb) __syncthreads();  // the previous stage has been multiplied
+        // activations: three bf16 pieces of every value
+#pragma unroll
+        for (int e = 0; e < NA; ++e) {
+            const int idx = tid + e * 256;
+            const int r = idx / (GK / 4), c = (idx % (GK / 4)) * 4;
+            const float v[4] = {pa[e].x, pa[e].y, pa[e].z, pa[e].w};
+            unsigned p1[2], p2[2], p3[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const float a = v[2 * h], b = v[2 * h + 1];
+                p1[h] = pk_bf16(a, b);
+                const float ra = a - bf16_lo(p1[h]), rb = b - bf16_hi(p1[h]);
+                p2[h] = pk_bf16(ra, rb);
+                p3[h] = pk_bf16(ra - bf16_lo(p2[h]), rb - bf16_hi(p2[h]));
+            }
+            *reinterpret_cast<uint2*>(&Ap[0][r * RS + c]) = make_uint2(p1[0], p1[1]);
+            *reinterpret_cast<uint2*>(&Ap[1][r * RS + c]) = make_uint2(p2[0], p2[1]);
+            *reinterpret_cast<uint2*>(&Ap[2][r * RS + c]) = make_uint2(p3[0], p3[1]);
+        }
+        // weights: u - 8 as bf16 (exact), inputs in k order (low nibble of
+        // byte j is input 2 j)
+        {
+            unsigned short* dst = Bu + wrow * RS + wq * (GK / WPR);
+#pragma unroll
+            for (int i = 0; i < NW; ++i) {
+                unsigned o[4];
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const unsigned byte = (pw[i] >> (8 * b)) & 0xFFu;
+                    o[b] = pk_bf16((float)(int)(byte & 15u) - 8.f, (float)(int)(byte >> 4) - 8.f);
+                }
+                *reinterpret_cast<uint4*>(dst + 8 * i) = make_uint4(o[0], o[1], o[2], o[3]);
+            }
+            if (((wq * (GK / WPR)) & 31) == 0) Bs_s[(wq * (GK / WPR)) >> 5][wrow] = ps;
+        }
+        __syncthreads();
+        if (k0 + GK < ke) load_stage(k0 + GK);
+        const int kq = lane >> 4, l16 = lane & 15;
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            bf16x8 a[3][MI], b[NJ];
+#pragma unroll
+            for (int p = 0; p < 3; ++p)
+#pragma unroll
+                for (int i = 0; i < MI; ++i)
+                    a[p][i] = *reinterpret_cast<const bf16x8*>(&Ap[p][(wm * (TM / 2) + i * 16 + l16) * RS + g * 32 + 8 * kq]);
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+                b[j] = *reinterpret_cast<const bf16x8*>(&Bu[(wn * (NT / 2) + j * 16 + l16) * RS + g * 32 + 8 * kq]);
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                    f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0][i], b[j], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                    d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[1][i], b[j], d, 0, 0, 0);
+                    d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[2][i], b[j], d, 0, 0, 0);
+                    const float sw = Bs_s[g][wn * (NT / 2) + j * 16 + l16];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(sw, d[r], acc[i][j][r]);
+                }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = m0 + wm * (TM / 2) + i * 16 + 4 * (lane >> 4) + r;
+                const int n = n0 + wn * (NT / 2) + j * 16 + (lane & 15);
+                if (m < M && n < N) {
+                    if (gridDim.z > 1) atomicAdd(Y + (size_t)m * ldy + n, acc[i][j][r]);
+                    else epilogue(ep, Y, ldy, m, n, acc[i][j][r]);
+                }
+            }
+}
+
 // ---------------------------------------------------------------- decode attention
 
 // Split-K decode attention.  Workgroup (split, h, b) covers positions
@@ -1624,6 +1785,22 @@ hipError_t launch_w4_matmul(const float* x, int ldx, int M, const Int4Mat& w, co
         return hipGetLastError();
     }
     const int kspan = stages / ksplit * GKs;
+    if (w.fmt == WF_INT4) {
+        // 32-column tiles where 64-column ones would leave fewer than two
+        // workgroups per CU (the K range stays whole: no atomics)
+        if (small && ksplit == 1 && (long)ntile * mtile < 512) {
+            const dim3 g32((w.N + 31) / 32, mtile, 1);
+            hipLaunchKernelGGL((k_gemm_w4_bf3<32, 128, 32>), g32, dim3(256), 0, st, x, ldx, M, w.K, w.q, w.s, w.N, y,
+                               ldy, ep, kspan);
+        } else if (small) {
+            hipLaunchKernelGGL((k_gemm_w4_bf3<32, 128, 64>), grid, dim3(256), 0, st, x, ldx, M, w.K, w.q, w.s, w.N, y,
+                               ldy, ep, kspan);
+        } else {
+            hipLaunchKernelGGL((k_gemm_w4_bf3<64, 64, 64>), grid, dim3(256), 0, st, x, ldx, M, w.K, w.q, w.s, w.N, y,
+                               ldy, ep, kspan);
+        }
+        return hipGetLastError();
+    }
     static bool attr = false;
     if (!attr) {
         const void* f64[3] = {(const void*)k_gemm_w4<64, 64, WF_INT4>, (const void*)k_gemm_w4<64, 64, WF_F16>,

@@ -33,6 +33,10 @@ METRIC = "decode ms/token + achieved HBM GB/s, medium W4g32 decoder, cache 2504,
 HBM_PEAK_GBPS = 8000.0
 FP32_MFMA_PEAK_TFLOPS = 157.3
 INT8_MFMA_PEAK_TOPS = 5000.0
+# INT4 projections of W4A32 models run on BF16 MFMA with every activation
+# split into three bf16 pieces: three BF16 products per FP32 product, so the
+# matrix-core ceiling of that form is a third of the dense BF16 peak
+BF16X3_MFMA_PEAK_TFLOPS = 2500.0 / 3
 STEADY_FROM = 8
 
 
@@ -392,6 +396,8 @@ def main() -> int:
         "prefill_ms": round(prefill_ms, 3),
         ("prefill_int8_mfma_frac" if args.w4a8 else "prefill_fp32_mfma_frac"):
             round(pf_flops / (prefill_ms * 1e-3) / 1e12 / (INT8_MFMA_PEAK_TOPS if args.w4a8 else FP32_MFMA_PEAK_TFLOPS), 4),
+        **({} if args.w4a8 or args.weights != "int4" else
+           {"prefill_bf16x3_mfma_frac": round(pf_flops / (prefill_ms * 1e-3) / 1e12 / BF16X3_MFMA_PEAK_TFLOPS, 4)}),
         "roofline": {"kernel": kernel_name, "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic,
