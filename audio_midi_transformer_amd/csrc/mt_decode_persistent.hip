@@ -27,12 +27,15 @@
 //
 // Roles (a table built on the host, see build_roles):
 //   attention WGs  (head h, split s), 16 splits per head at small width, 8
-//                  otherwise, all on one XCD.  Each recomputes q_h and the
-//                  softmax partial over its chunk of cached positions; splits
-//                  1.. publish (max, sum, acc[64]); split 0 (the head leader)
-//                  merges them with the new position and publishes attn_h.
+//                  otherwise, all on one XCD.  Each recomputes q_h (at medium
+//                  width: gathers it) and the softmax partial over its chunk
+//                  of cached positions; splits 1.. publish (max, sum,
+//                  acc[64]); split 0 (the head leader) merges them with the
+//                  new position and publishes attn_h.
 //   free WGs       the rest: the new K/V rows of the fused projection (to the
-//                  cache slot T_past and to the exchange).
+//                  cache slot T_past and to the exchange); at medium width
+//                  also 8 q rows each; tail splits past the attention splits'
+//                  reach.
 //   free WGs       also the O projection (D / free WGs rows each).
 //   all WGs        F/256 rows of FFN-up + GELU and D/256 rows of FFN-down.
 // Per layer: A (attention partials / K,V rows) -> A2 (head merge) -> B (O)
@@ -85,7 +88,7 @@ struct Role {
     int o_row0;     // first of this workgroup's O-projection rows, -1 if none
     int tail_head;  // free workgroups: head of this workgroup's tail split, -1 if none
     int tail_idx;   // its index among the head's tail splits
-    int pad;
+    int q_row0;     // free workgroups with Cfg::QF: first of its Q_ROWS q rows, -1 if none
 };
 
 template <int D, int F>
@@ -112,10 +115,24 @@ struct Cfg {
     static constexpr int SLOTS = ATT_S + TS;  // partial slots per head
     static constexpr int REACH = ATT_S * MP + TS * MAXPOS;
     static constexpr int KV_ROWS = cdiv(2 * D, NFREE);
+    // QF: the q rows are computed by the free workgroups, Q_ROWS each, next
+    // to their K/V rows, and gathered by the attention workgroups, which
+    // then need neither LN1 nor the head's 64 q rows (1.75 us of a medium
+    // layer on the critical path, against one pass of Q_ROWS rows and an
+    // exchange inside the XCD), and nor do the tail splits.  Possible where
+    // every head's q rows fit on free workgroups of the head's own XCD
+    // (medium width); used in the instantiation with tail splits only.
+    // Measured at medium: 383 -> 391 us per step at T = 600 (the free
+    // workgroups' K/V rows, which the head merge waits for, come a pass
+    // later), even at T = 1100 and 2000, 458 -> 443 us at T = 2450 (the tail
+    // splits skip their 64-row dot).
+    static constexpr int Q_ROWS = 8;
+    static constexpr bool QF = NFREE == NATT && NFREE * Q_ROWS == D;
     static constexpr int UP_ROWS = cdiv(F, NWG);
     static constexpr int O_ROWS = cdiv(D, NFREE);  // O rows: free workgroups only
     static constexpr int DN_ROWS = cdiv(D, NWG);
     static constexpr int NP_Q = cdiv(64, RP_D);
+    static constexpr int NP_QF = cdiv(Q_ROWS, RP_D);
     static constexpr int NP_KV = cdiv(KV_ROWS, RP_D);
     static constexpr int NP_O = cdiv(O_ROWS, RP_D);
     static constexpr int NP_UP = cdiv(UP_ROWS, RP_D);
@@ -124,7 +141,8 @@ struct Cfg {
     // reads are written REP times; the workgroups of XCD x read copy x, so
     // no line is polled by more than 32 workgroups.
     static constexpr int XA_KV = 0;                     // new K|V row [2D]
-    static constexpr int XA_PART = XA_KV + 2 * D;       // partials [H][SLOTS][PW]
+    static constexpr int XA_Q = XA_KV + 2 * D;          // q row [D] (QF)
+    static constexpr int XA_PART = XA_Q + (QF ? D : 0); // partials [H][SLOTS][PW]
     static constexpr int XB_ATT = XA_PART + H * SLOTS * PW;  // merged attention [REP][D]
     static constexpr int XB_O = XB_ATT + REP * D;       // o [REP][D]
     static constexpr int XC = XB_O + REP * D;           // u [REP][F]
@@ -1086,6 +1104,25 @@ __device__ __forceinline__ bool phase_a_ln(const Args& a, const Lds<D, F>& S, co
     return true;
 }
 
+// Start of phase A without LN1 (QF attention workgroups): r += f of the
+// previous layer (if any).
+template <int D, int F>
+__device__ __forceinline__ bool phase_a_add(const Args& a, const Lds<D, F>& S, float (&r)[LnRegs<D>::PER], int l) {
+    using C = Cfg<D, F>;
+    stamp(a, l, 0);
+    if (l > 0) {
+        const uint64_t* Xp = a.x + (size_t)(l - 1) * C::LAYER_WORDS;
+        float f[LnRegs<D>::PER];
+        if (!ll_gather_regs<LnRegs<D>::PER>(rep_of(Xp + C::XD, D), D, f, a.epoch, a.err)) *S.s_flag = 1;
+#pragma unroll
+        for (int i = 0; i < LnRegs<D>::PER; ++i) r[i] += f[i];
+        lds_barrier();
+        if (*S.s_flag) return false;
+    }
+    stamp(a, l, 1);
+    return true;
+}
+
 // Every layer for an attention workgroup (head h, split s).  TAIL: the
 // cache reaches past the attention splits, and the head leader also merges
 // the tail splits' partials.
@@ -1097,17 +1134,21 @@ __device__ __forceinline__ bool attention_role(const Args& a, const Lds<D, F>& S
     const uint32_t ep = a.epoch;
     const int tid = threadIdx.x;
     constexpr int AS = C::ATT_S;
+    constexpr bool QF = C::QF && TAIL;  // q rows on the free workgroups (see Cfg::QF)
     const bool leader = role.split == 0;
     const int h = role.head;
     const int p0 = role.split * a.chunk;
     const int npos = max(0, min(a.t0, p0 + a.chunk) - p0);
     const size_t lstride = (size_t)a.kv_seqs * a.t_cap * D;  // one layer of the cache
-    WBlk<C::CPL_D, C::NP_Q> wqh;
+    // (with QF the head's q rows and LN1 come from the free workgroups)
+    WBlk<C::CPL_D, QF ? 1 : C::NP_Q> wqh;
     BcdW<D, F> w;
     LnRegs<D> ln1;
     if (npos > 0) kv_chunk_dma<D, C::MP>(a.kc, a.vc, h, p0, npos, S.big);
-    wblk_load<C::LPR_D, C::CPL_D, C::NP_Q>(wqh, a.wq + O::QO, a.ws + O::QS, D, h * 64, 64);
-    ln_load<D>(ln1, a.ln, a.ln + D);
+    if constexpr (!QF) {
+        wblk_load<C::LPR_D, C::CPL_D, C::NP_Q>(wqh, a.wq + O::QO, a.ws + O::QS, D, h * 64, 64);
+        ln_load<D>(ln1, a.ln, a.ln + D);
+    }
     for (int l = 0; l < a.L; ++l) {
         uint64_t* X = a.x + (size_t)l * C::LAYER_WORDS;
         const uint8_t* wq = a.wq + l * a.wq_layer;
@@ -1116,9 +1157,13 @@ __device__ __forceinline__ bool attention_role(const Args& a, const Lds<D, F>& S
         const float* kc_l = a.kc + (size_t)l * lstride;
         const float* vc_l = a.vc + (size_t)l * lstride;
         const bool last = l + 1 == a.L;
-        // ---- A: r += f_prev; LN1; q_h; softmax partial over the chunk
-        if (!phase_a_ln<D, F>(a, S, ln1, r, l)) return false;
-        {
+        // ---- A: r += f_prev; q_h (LN1 and the dot here, or gathered);
+        // softmax partial over the chunk
+        if constexpr (QF) {
+            if (!phase_a_add<D, F>(a, S, r, l)) return false;
+            if (!ll_gather1<1, false>(X + C::XA_Q + h * 64, 64, S.qh, ep, a.err, S.s_flag)) return false;
+        } else {
+            if (!phase_a_ln<D, F>(a, S, ln1, r, l)) return false;
             float o[C::NP_Q];
             dot_rows<C::LPR_D, C::CPL_D, C::NP_Q>(wqh, S.act, S.xs, o, a);
 #pragma unroll
@@ -1186,11 +1231,13 @@ __device__ __forceinline__ bool attention_role(const Args& a, const Lds<D, F>& S
         // ---- C, D (no phase B)
         load_d<D, F>(w, wq, ws);
         if (!phase_c<D, F>(a, S, X, w, r, l)) return false;
-        if (!last) {
-            const uint8_t* wqn = wq + a.wq_layer;
-            const float* wsn = ws + a.ws_layer;
-            wblk_load<C::LPR_D, C::CPL_D, C::NP_Q>(wqh, wqn + O::QO, wsn + O::QS, D, h * 64, 64);
-            ln_load<D>(ln1, ln + 4 * D, ln + 5 * D);
+        if constexpr (!QF) {
+            if (!last) {
+                const uint8_t* wqn = wq + a.wq_layer;
+                const float* wsn = ws + a.ws_layer;
+                wblk_load<C::LPR_D, C::CPL_D, C::NP_Q>(wqh, wqn + O::QO, wsn + O::QS, D, h * 64, 64);
+                ln_load<D>(ln1, ln + 4 * D, ln + 5 * D);
+            }
         }
         if (!phase_d<D, F>(a, S, X, w, l)) return false;
     }
@@ -1211,12 +1258,16 @@ __device__ __forceinline__ bool free_role(const Args& a, const Lds<D, F>& S, con
     // tail split: positions [tp0, tp0 + tnpos) of head th (none while the
     // cache ends within the attention splits' reach)
     const int th = TAIL ? role.tail_head : -1;
+    constexpr bool QF = C::QF && TAIL;  // q rows on the free workgroups (see Cfg::QF)
     const int tp0 = a.tail0 + role.tail_idx * a.tail_chunk;
     const int tnpos = th >= 0 ? max(0, min(a.t0, tp0 + a.tail_chunk) - tp0) : 0;
     WBlk<C::CPL_D, C::NP_KV> wkv;
+    WBlk<C::CPL_D, C::NP_QF> wqf;  // QF: this workgroup's q rows
     BcdW<D, F> w;
     LnRegs<D> ln1;
     if (tnpos > 0) kv_chunk_dma<D, MAXPOS>(a.kc, a.vc, th, tp0, tnpos, S.big);
+    if (QF && role.q_row0 >= 0)
+        wblk_load<C::LPR_D, C::CPL_D, C::NP_QF>(wqf, a.wq + O::QO, a.ws + O::QS, D, role.q_row0, C::Q_ROWS);
     if (role.kv_rows > 0)
         wblk_load<C::LPR_D, C::CPL_D, C::NP_KV>(wkv, a.wq + O::QO, a.ws + O::QS, D, D + role.kv_row0, role.kv_rows);
     ln_load<D>(ln1, a.ln, a.ln + D);
@@ -1228,8 +1279,18 @@ __device__ __forceinline__ bool free_role(const Args& a, const Lds<D, F>& S, con
         float* kc_l = a.kc + (size_t)l * lstride;
         float* vc_l = a.vc + (size_t)l * lstride;
         const bool last = l + 1 == a.L;
-        // ---- A: r += f_prev; LN1; new K/V rows
+        // ---- A: r += f_prev; LN1; (QF: q rows first, the attention
+        // workgroups wait for them); new K/V rows
         if (!phase_a_ln<D, F>(a, S, ln1, r, l)) return false;
+        if (QF && role.q_row0 >= 0) {
+            float o[C::NP_QF];
+            dot_rows<C::LPR_D, C::CPL_D, C::NP_QF>(wqf, S.act, S.xs, o, a);
+#pragma unroll
+            for (int p = 0; p < C::NP_QF; ++p) {
+                const int rr = out_row<C::LPR_D>(p);
+                if (rr >= 0 && rr < C::Q_ROWS) ll_put(X + C::XA_Q + role.q_row0 + rr, o[p], ep);
+            }
+        }
         if (role.kv_rows > 0) {
             float o[C::NP_KV];
             dot_rows<C::LPR_D, C::CPL_D, C::NP_KV>(wkv, S.act, S.xs, o, a);
@@ -1248,15 +1309,20 @@ __device__ __forceinline__ bool free_role(const Args& a, const Lds<D, F>& S, con
         if (tnpos > 0) {
             // ---- tail split: q_h and the softmax partial over its positions.
             // The q_h rows are loaded here, not a phase ahead: they would hold
-            // 40 registers through every step, tail or not.
-            WBlk<C::CPL_D, C::NP_Q> wqh;
-            wblk_load<C::LPR_D, C::CPL_D, C::NP_Q>(wqh, wq + O::QO, ws + O::QS, D, th * 64, 64);
-            float o[C::NP_Q];
-            dot_rows<C::LPR_D, C::CPL_D, C::NP_Q>(wqh, S.act, S.xs, o, a);
+            // 40 registers through every step, tail or not.  With QF q_h is
+            // gathered like on the attention workgroups.
+            if constexpr (QF) {
+                if (!ll_gather1<1, false>(X + C::XA_Q + th * 64, 64, S.qh, ep, a.err, S.s_flag)) return false;
+            } else {
+                WBlk<C::CPL_D, C::NP_Q> wqh;
+                wblk_load<C::LPR_D, C::CPL_D, C::NP_Q>(wqh, wq + O::QO, ws + O::QS, D, th * 64, 64);
+                float o[C::NP_Q];
+                dot_rows<C::LPR_D, C::CPL_D, C::NP_Q>(wqh, S.act, S.xs, o, a);
 #pragma unroll
-            for (int p = 0; p < C::NP_Q; ++p) {
-                const int rr = out_row<C::LPR_D>(p);
-                if (rr >= 0 && rr < 64) S.qh[rr] = o[p];
+                for (int p = 0; p < C::NP_Q; ++p) {
+                    const int rr = out_row<C::LPR_D>(p);
+                    if (rr >= 0 && rr < 64) S.qh[rr] = o[p];
+                }
             }
             __builtin_amdgcn_s_waitcnt(0);  // the tail chunk DMA has landed
             lds_barrier();
@@ -1277,6 +1343,9 @@ __device__ __forceinline__ bool free_role(const Args& a, const Lds<D, F>& S, con
         load_d<D, F>(w, wq, ws);
         if (!phase_c<D, F>(a, S, X, w, r, l)) return false;
         if (!last) {
+            if (QF && role.q_row0 >= 0)
+                wblk_load<C::LPR_D, C::CPL_D, C::NP_QF>(wqf, wq + a.wq_layer + O::QO, ws + a.ws_layer + O::QS, D,
+                                                        role.q_row0, C::Q_ROWS);
             if (role.kv_rows > 0)
                 wblk_load<C::LPR_D, C::CPL_D, C::NP_KV>(wkv, wq + a.wq_layer + O::QO, ws + a.ws_layer + O::QS, D,
                                                         D + role.kv_row0, role.kv_rows);
@@ -1406,7 +1475,7 @@ __global__ __launch_bounds__(NT, 1) void k_decode_step(Args a) {
 // Role table for the shape: attention heads spread over the XCDs with the 8
 // splits of a head on one XCD; O, FFN-down and K/V-row duties on the rest.
 template <int D, int F>
-static void build_roles(Role* roles) {
+static bool build_roles(Role* roles) {
     using C = Cfg<D, F>;
     int free_list[NWG];
     int nfree = 0;
@@ -1414,7 +1483,7 @@ static void build_roles(Role* roles) {
     for (int h = 0; h < C::H; ++h) ++nh_x[h % NXCD];
     for (int w = 0; w < NWG; ++w) {
         Role& r = roles[w];
-        r = Role{-1, 0, 0, 0, -1, -1, 0, 0};
+        r = Role{-1, 0, 0, 0, -1, -1, 0, -1};
         const int x = w % NXCD, slot = w / NXCD;
         if (slot < nh_x[x] * C::ATT_S) {
             r.head = (slot / C::ATT_S) * NXCD + x;
@@ -1429,6 +1498,20 @@ static void build_roles(Role* roles) {
         r.o_row0 = i * C::O_ROWS < D ? i * C::O_ROWS : -1;
         r.kv_row0 = row0;
         r.kv_rows = row0 < 2 * D ? (2 * D - row0 < C::KV_ROWS ? 2 * D - row0 : C::KV_ROWS) : 0;
+    }
+    // QF: head h's 64 q rows on 64 / Q_ROWS free workgroups of its XCD
+    if (C::QF) {
+        int next[NXCD] = {0};  // next free workgroup (index into free_list) to take, per XCD
+        for (int h = 0; h < C::H; ++h) {
+            const int xh = h % NXCD;
+            for (int j = 0; j < 64 / C::Q_ROWS; ++j) {
+                int i = next[xh];
+                while (i < nfree && free_list[i] % NXCD != xh) ++i;
+                if (i >= nfree) return false;
+                roles[free_list[i]].q_row0 = h * 64 + j * C::Q_ROWS;
+                next[xh] = i + 1;
+            }
+        }
     }
     // TS tail splits per head on free workgroups, first from the XCD of the
     // head (its leader's), then from any XCD
@@ -1447,6 +1530,7 @@ static void build_roles(Role* roles) {
             roles[pick].tail_idx = j;
         }
     }
+    return true;
 }
 
 }  // namespace pd
@@ -1497,7 +1581,7 @@ static pd::Role* role_table(void* xbuf, int L) {
 template <int D, int F>
 static hipError_t prepare_t(void* xbuf, int L, hipStream_t st) {
     pd::Role host[pd::NWG];
-    pd::build_roles<D, F>(host);
+    if (!pd::build_roles<D, F>(host)) return hipErrorInvalidValue;
     hipError_t e = hipMemcpyAsync(role_table<D, F>(xbuf, L), host, sizeof host, hipMemcpyHostToDevice, st);
     if (e != hipSuccess) return e;
     return hipStreamSynchronize(st);
