@@ -349,6 +349,28 @@ def main() -> int:
     t_keys = np.concatenate([np.arange(n_dec) + R0 + 1] * args.steps)
     points = {str(T): round(float(all_ms[t_keys == T].mean()), 5)
               for T in (505, 1024, 2048) if np.any(t_keys == T)}
+    # past the workload's last step, near the end of the cache: one prefill
+    # of t_cap - 64 synthetic rows, then 16 timed decode steps (B = 1
+    # workloads whose pass stops short of that)
+    near_end = None
+    T_far = wl.t_cap - 64
+    if pairs is None and B == 1 and R0 + n_dec < T_far:
+        far = torch.from_numpy(np.random.default_rng(7).standard_normal((1, T_far, shape.d_model))
+                               .astype(np.float32)).to(dev)
+        dec.reset()
+        call(dec.prefill, None, far, out=nxt[0])
+        for k in range(4):
+            call(dec.decode_step, nxt[k & 1], out=nxt[(k + 1) & 1])
+        far_ev = [mk() for _ in range(17)]
+        far_ev[0].record(stream)
+        for k in range(16):
+            call(dec.decode_step, nxt[k & 1], out=nxt[(k + 1) & 1])
+            far_ev[k + 1].record(stream)
+        torch.cuda.synchronize()
+        dec.check()
+        far_ms = [far_ev[k].elapsed_time(far_ev[k + 1]) for k in range(16)]
+        near_end = {"keys": f"{T_far + 5}-{T_far + 20}", "ms_per_token": round(float(np.mean(far_ms)), 5)}
+        del far
     copy_gbps = measure_copy_peak(torch)
 
     metric = (METRIC if wl.key == "2" and args.batch is None
@@ -391,6 +413,7 @@ def main() -> int:
         "achieved_GBps": round(gbps, 1),
         "hbm_frac_of_8TBps": round(gbps / HBM_PEAK_GBPS, 4),
         "decode_ms_at_T": points,
+        "decode_near_cache_end": near_end,
         "hbm_frac_of_measured_copy": round(gbps / copy_gbps, 4),
         "measured_copy_GBps": round(copy_gbps, 1),
         "prefill_ms": round(prefill_ms, 3),
