@@ -154,11 +154,16 @@ def reduce_counters(fetch_csv: str, write_csv: str, workload_key: str, calib_mib
                 if KERNEL_SYMBOLS["mt_decode_step_persistent"] in r["Kernel_Name"]]
         return max(copies), kern
 
+    from audio_midi_transformer_amd import synth
+
     known_kib = float(calib_mib) * 1024.0
     f_copy, f_kern = load(fetch_csv, "FETCH_SIZE")
     w_copy, w_kern = load(write_csv, "WRITE_SIZE")
     f_scale, w_scale = known_kib / f_copy, known_kib / w_copy
-    f_kern, w_kern = f_kern[STEADY_FROM:], w_kern[STEADY_FROM:]
+    # the pass's steady window (launches past it: the bench's point near the
+    # end of the cache)
+    n_dec = synth.WORKLOADS[workload_key].decode_steps
+    f_kern, w_kern = f_kern[STEADY_FROM:n_dec], w_kern[STEADY_FROM:n_dec]
     fetch = float(np.mean(f_kern)) * 1024.0 * f_scale
     write = float(np.mean(w_kern)) * 1024.0 * w_scale
     return {
