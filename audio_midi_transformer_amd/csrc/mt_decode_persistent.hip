@@ -1198,28 +1198,31 @@ __device__ __forceinline__ bool attention_role(const Args& a, const Lds<D, F>& S
             stamp(a, l, 5);
             stamp(a, l, 16);
             if (tid < 64) {
-                // every split's (max, sum, acc[tid]) into registers first, so
-                // the LDS reads overlap; an empty split has max -inf, sum 0 and
-                // acc 0, and its weight exp(-inf) is exactly 0
-                float pm[NS], pl[NS], pa[NS];
-                pm[0] = S.own[0];
+                // every split's (sum, acc[tid]) into registers first, so the
+                // LDS reads overlap; an empty split has max -inf, sum 0 and
+                // acc 0, and its weight exp(-inf) is exactly 0.  The weights
+                // are uniform across the wave: lane s < NS forms split s's,
+                // lane NS the new position's, one exp per lane instead of
+                // NS + 1 in every lane.
+                static_assert(NS < 64, "one lane per partial and one for the new position");
+                float pl[NS], pa[NS];
                 pl[0] = S.own[1];
                 pa[0] = S.own[2 + tid];
 #pragma unroll
                 for (int s = 1; s < NS; ++s) {
-                    pm[s] = S.gpart[(s - 1) * PW];
                     pl[s] = S.gpart[(s - 1) * PW + 1];
                     pa[s] = S.gpart[(s - 1) * PW + 2 + tid];
                 }
                 const float snew = wave_reduce<false>(S.qh[tid] * S.knew[tid]) * 0.125f;
-                float M = snew;
-#pragma unroll
-                for (int s = 0; s < NS; ++s) M = fmaxf(M, pm[s]);
-                float Ls = expf(snew - M);
+                const float mx = tid == 0 ? S.own[0]
+                                          : tid < NS ? S.gpart[(tid - 1) * PW] : tid == NS ? snew : -INFINITY;
+                const float M = wave_reduce<true>(mx);
+                const float wl = tid <= NS ? expf(mx - M) : 0.f;
+                float Ls = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), NS));
                 float A = Ls * S.vnew[tid];
 #pragma unroll
                 for (int s = 0; s < NS; ++s) {
-                    const float wgt = expf(pm[s] - M);
+                    const float wgt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), s));
                     Ls = fmaf(wgt, pl[s], Ls);
                     A = fmaf(wgt, pa[s], A);
                 }
