@@ -1179,8 +1179,6 @@ __device__ __forceinline__ bool attention_role(const Args& a, const Lds<D, F>& S
         __builtin_amdgcn_s_waitcnt(0);  // the K/V chunk DMA (and every earlier load) has landed
         lds_barrier();
         stamp(a, l, 3);
-        // phase B and C weights load behind the attention
-        load_bc<D, F>(w, wq, ws, ln, -1);
         attend_chunk<C::MP>(S.big, S.qh, npos, S.sc, S.comb, S.red + 8, S.own, a, l);
         stamp(a, l, 4);
         if (!leader) {
@@ -1234,7 +1232,10 @@ __device__ __forceinline__ bool attention_role(const Args& a, const Lds<D, F>& S
             stamp(a, l, 17);
             if (!last && npos > 0) kv_chunk_dma<D, C::MP>(kc_l + lstride, vc_l + lstride, h, p0, npos, S.big);
         }
-        // ---- C, D (no phase B)
+        // ---- C, D (no phase B).  The FFN-up rows are requested here, behind
+        // the next chunk's DMA (a few us per step faster than before the
+        // attention at T <= 1100, even at T = 2000).
+        load_bc<D, F>(w, wq, ws, ln, -1);
         if (!phase_c<D, F>(a, S, X, w, r, l)) return false;
         load_d<D, F>(w, wq, ws);
         if constexpr (!QF) {
