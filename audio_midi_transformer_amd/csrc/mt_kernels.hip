@@ -1014,8 +1014,12 @@ __global__ __launch_bounds__(256) void k_attn_decode(const float* __restrict__ q
         const int t = g + 16 * i;
         k4[i] = v4[i] = make_float4(0.f, 0.f, 0.f, 0.f);
         if (t < n) {
-            k4[i] = *reinterpret_cast<const float4*>(kc + base + (size_t)(t0 + t) * d);
-            v4[i] = *reinterpret_cast<const float4*>(vc + base + (size_t)(t0 + t) * d);
+            // non-temporal: the step reads each cached row once, and the
+            // weights the next launches read again should stay cached
+            const f32x4 kv = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(kc + base + (size_t)(t0 + t) * d));
+            const f32x4 vv = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(vc + base + (size_t)(t0 + t) * d));
+            k4[i] = make_float4(kv[0], kv[1], kv[2], kv[3]);
+            v4[i] = make_float4(vv[0], vv[1], vv[2], vv[3]);
         }
     }
     float sc[16];
