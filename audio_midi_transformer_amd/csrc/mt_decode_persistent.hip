@@ -141,8 +141,10 @@ struct Cfg {
     // reads are written REP times; the workgroups of XCD x read copy x, so
     // no line is polled by more than 32 workgroups.
     static constexpr int XA_KV = 0;                     // new K|V row [2D]
-    static constexpr int XA_Q = XA_KV + 2 * D;          // q row [D] (QF)
-    static constexpr int XA_PART = XA_Q + (QF ? D : 0); // partials [H][SLOTS][PW]
+    // q row [D], with tail splits only: with QF all of it from the free
+    // workgroups, else head h's 64 rows from the head's first attention split
+    static constexpr int XA_Q = XA_KV + 2 * D;
+    static constexpr int XA_PART = XA_Q + D;            // partials [H][SLOTS][PW]
     static constexpr int XB_ATT = XA_PART + H * SLOTS * PW;  // merged attention [REP][D]
     static constexpr int XB_O = XB_ATT + REP * D;       // o [REP][D]
     static constexpr int XC = XB_O + REP * D;           // u [REP][F]
@@ -1175,7 +1177,11 @@ __device__ __forceinline__ bool attention_role(const Args& a, const Lds<D, F>& S
 #pragma unroll
             for (int p = 0; p < C::NP_Q; ++p) {
                 const int rr = out_row<C::LPR_D>(p);
-                if (rr >= 0 && rr < 64) S.qh[rr] = o[p];
+                if (rr >= 0 && rr < 64) {
+                    S.qh[rr] = o[p];
+                    // the head's tail splits gather q_h from its first split
+                    if (TAIL && leader) ll_put(X + C::XA_Q + h * 64 + rr, o[p], ep);
+                }
             }
         }
         stamp(a, l, 15);
@@ -1317,23 +1323,13 @@ __device__ __forceinline__ bool free_role(const Args& a, const Lds<D, F>& S, con
             }
         }
         if (tnpos > 0) {
-            // ---- tail split: q_h and the softmax partial over its positions.
-            // The q_h rows are loaded here, not a phase ahead: they would hold
-            // 40 registers through every step, tail or not.  With QF q_h is
-            // gathered like on the attention workgroups.
-            if constexpr (QF) {
-                if (!ll_gather1<1, false>(X + C::XA_Q + th * 64, 64, S.qh, ep, a.err, S.s_flag)) return false;
-            } else {
-                WBlk<C::CPL_D, C::NP_Q> wqh;
-                wblk_load<C::LPR_D, C::CPL_D, C::NP_Q>(wqh, wq + O::QO, ws + O::QS, D, th * 64, 64);
-                float o[C::NP_Q];
-                dot_rows<C::LPR_D, C::CPL_D, C::NP_Q>(wqh, S.act, S.xs, o, a);
-#pragma unroll
-                for (int p = 0; p < C::NP_Q; ++p) {
-                    const int rr = out_row<C::LPR_D>(p);
-                    if (rr >= 0 && rr < 64) S.qh[rr] = o[p];
-                }
-            }
+            // ---- tail split: the softmax partial over its positions, with
+            // q_h gathered (from the free workgroups' q rows with QF, else
+            // from the head's first attention split).  Computing q_h here
+            // instead puts a 64-row dot, whose weights cannot be requested
+            // ahead, on the chain to the head merge, and at large width its
+            // 60 registers made the step spill.
+            if (!ll_gather1<1, false>(X + C::XA_Q + th * 64, 64, S.qh, ep, a.err, S.s_flag)) return false;
             __builtin_amdgcn_s_waitcnt(0);  // the tail chunk DMA has landed
             lds_barrier();
             attend_chunk<MAXPOS>(S.big, S.qh, tnpos, S.sc, S.comb, S.red + 8, S.own, a, l);
