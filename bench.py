@@ -65,7 +65,8 @@ def prefill_flops(shape, B: int, M: int) -> float:
 
 # sources that build and launch each profiled kernel (its traffic record is
 # void once any of them changes)
-KERNEL_SOURCES = {"mt_decode_step_persistent": ("mt_decode_persistent.hip", "mt_internal.h", "mt_api.cpp")}
+KERNEL_SOURCES = {"mt_decode_step_persistent": ("mt_decode_persistent.hip", "mt_pd_common.h", "mt_internal.h",
+                                                  "mt_api.cpp")}
 
 
 def kernel_source_hash(kernel: str = "mt_decode_step_persistent") -> str:
