@@ -26,6 +26,7 @@ MT_ERR_UNSUPPORTED = -5
 MT_DECODE_AUTO = 0
 MT_DECODE_KERNELS = 1
 MT_DECODE_PERSISTENT = 2
+MT_DECODE_BATCHED = 3
 
 MT_FLAG_W4A8 = 1
 MT_FLAG_DENSE_F16 = 2

@@ -20,7 +20,7 @@ LIB = os.path.join(PKG, "libmtdec.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["mt_kernels.hip", "mt_decode_persistent.hip", "mt_scratch.hip"]
+HIP_SOURCES = ["mt_kernels.hip", "mt_decode_persistent.hip", "mt_decode_batched.hip", "mt_scratch.hip"]
 HOST_SOURCES = ["mt_api.cpp"]
 
 COMMON = ["-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function"]

@@ -76,6 +76,9 @@ struct mt_model {
     int decode_path = MT_DECODE_AUTO;
     bool persistent_ok = false;
     void* xbuf = nullptr;
+    // single-launch step for the whole batch, one XCD per sequence
+    bool batched_ok = false;
+    void* bxbuf = nullptr;
     void* trace = nullptr;  // phase timestamps of the last persistent step (MT_TRACE=1)
     uint32_t epoch = 0;
     // prefill workspace
@@ -95,7 +98,7 @@ hipError_t dmalloc(T** p, size_t count) {
 void free_model(mt_model* m) {
     if (!m) return;
     void* ptrs[] = {m->tok_emb, m->lm_head, m->ln, m->lnf, m->wq_all, m->ws_all, m->wt_all, m->wst_all, m->kc, m->vc, m->err, m->x,
-                    m->a, m->q, m->att, m->h, m->part, m->z, m->xbuf, m->trace, m->pf};
+                    m->a, m->q, m->att, m->h, m->part, m->z, m->xbuf, m->bxbuf, m->trace, m->pf};
     for (void* p : ptrs)
         if (p) (void)hipFree(p);
     delete m;
@@ -384,6 +387,15 @@ int mt_create(const mt_config* cfg, const mt_weights* w, int weights_on_device, 
             return bail(fail(MT_ERR_OOM, "mt_create: exchange buffer of %zu bytes", xb));
         if (persistent_prepare(m->xbuf, L, d, F, st) != hipSuccess)
             return bail(fail(MT_ERR_HIP, "mt_create: persistent role table"));
+    }
+    // the batched step computes W4A32 only
+    m->batched_ok = fmt == WF_INT4 && !(c.flags & MT_FLAG_W4A8) && batched_supported(d, F, H, B, V);
+    if (m->batched_ok) {
+        const size_t xb = batched_xbuf_bytes(L, d, F, B);
+        if (hipMalloc(&m->bxbuf, xb) != hipSuccess || hipMemsetAsync(m->bxbuf, 0, xb, st) != hipSuccess)
+            return bail(fail(MT_ERR_OOM, "mt_create: batched exchange buffer of %zu bytes", xb));
+    }
+    if (m->persistent_ok || m->batched_ok) {
         const char* tr = getenv("MT_TRACE");
         if (tr && tr[0] == '1') {
             const size_t tb = persistent_trace_bytes(L);
@@ -479,9 +491,23 @@ int mt_decode_step(mt_model* m, const int64_t* token, float* logits, int64_t* ne
     hipStream_t st = (hipStream_t)stream;
     int tmax = 0;
     for (int b = 0; b < c.batch; ++b) tmax = std::max(tmax, m->pos.t[b]);
-    const bool persistent = m->persistent_ok && m->decode_path != MT_DECODE_KERNELS &&
-                            tmax <= persistent_max_position(c.d_model, c.d_ff);
-    if (persistent) {
+    const bool batched = m->batched_ok && (m->decode_path == MT_DECODE_BATCHED ||
+                                            (m->decode_path == MT_DECODE_AUTO && c.batch >= kBatchedAutoSeqs));
+    const bool persistent = !batched && m->persistent_ok && m->decode_path != MT_DECODE_KERNELS &&
+                            m->decode_path != MT_DECODE_BATCHED && tmax <= persistent_max_position(c.d_model, c.d_ff);
+    if (batched) {
+        BatchedArgs ba{};
+        ba.L = c.n_layers; ba.d = c.d_model; ba.H = c.n_heads; ba.F = c.d_ff; ba.V = c.vocab;
+        ba.B = c.batch; ba.t_cap = c.t_cap; ba.eps = c.ln_eps;
+        ba.tok_emb = m->tok_emb; ba.lm_head = m->lm_head; ba.ln = m->ln; ba.ln_final = m->lnf;
+        ba.wq_base = m->wq_all; ba.ws_base = m->ws_all;
+        ba.kc = m->kc; ba.vc = m->vc; ba.kv_seqs = c.batch;
+        ba.token = token; ba.logits = logits; ba.next = next;
+        for (int b = 0; b < c.batch; ++b) ba.t0[b] = m->pos.t[b];
+        ba.epoch = ++m->epoch;
+        ba.xbuf = m->bxbuf; ba.err = m->err; ba.trace = m->trace;
+        HIP_TRY(launch_batched_decode(ba, st));
+    } else if (persistent) {
         // one launch per sequence (a batch of at most kPersistentMaxSeqs),
         // each on that sequence's slice of the cache
         for (int b = 0; b < c.batch; ++b) {
@@ -570,10 +596,13 @@ int mt_check(mt_model* m) {
 
 int mt_set_decode_path(mt_model* m, int32_t path) {
     if (!m) return fail(MT_ERR_INVALID_ARG, "mt_set_decode_path: NULL model");
-    if (path != MT_DECODE_AUTO && path != MT_DECODE_KERNELS && path != MT_DECODE_PERSISTENT)
+    if (path != MT_DECODE_AUTO && path != MT_DECODE_KERNELS && path != MT_DECODE_PERSISTENT &&
+        path != MT_DECODE_BATCHED)
         return fail(MT_ERR_INVALID_ARG, "mt_set_decode_path: unknown path %d", path);
     if (path == MT_DECODE_PERSISTENT && !m->persistent_ok)
         return fail(MT_ERR_UNSUPPORTED, "persistent decode does not support this configuration");
+    if (path == MT_DECODE_BATCHED && !m->batched_ok)
+        return fail(MT_ERR_UNSUPPORTED, "batched single-launch decode does not support this configuration");
     m->decode_path = path;
     return MT_OK;
 }

@@ -188,7 +188,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="2")
-    ap.add_argument("--path", choices=["auto", "kernels", "persistent"], default="auto")
+    ap.add_argument("--path", choices=["auto", "kernels", "persistent", "batched"], default="auto")
     ap.add_argument("--decode-steps", type=int, default=None,
                     help="override the number of decode steps per pass (default: the workload's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -268,8 +268,9 @@ def main() -> int:
              "f32": binding.MT_FLAG_DENSE_F32}[variant]
     dec = binding.Decoder(weights, batch=B, t_cap=wl.t_cap, flags=flags)
     path = {"auto": binding.MT_DECODE_AUTO, "kernels": binding.MT_DECODE_KERNELS,
-            "persistent": binding.MT_DECODE_PERSISTENT}[args.path]
-    persistent = path != binding.MT_DECODE_KERNELS and dec_is_persistent(dec)
+            "persistent": binding.MT_DECODE_PERSISTENT, "batched": binding.MT_DECODE_BATCHED}[args.path]
+    taken = path_taken(dec, path, B)
+    persistent = taken == "persistent"
     dec.set_decode_path(path)
     dev = torch.device("cuda", 0)
     prefix = torch.from_numpy(prefix_np).to(dev) if prefix_np is not None else None
@@ -338,7 +339,8 @@ def main() -> int:
                              for k in range(STEADY_FROM, n_dec)])
     gbps = float(launch_bytes.sum()) / (steady_ms * 1e-3) / 1e9
     step_ms = np.concatenate([np.array([a.elapsed_time(b) for a, b in e["per"]])[STEADY_FROM:] for e in evs])
-    kernel_name = "mt_decode_step_persistent" if persistent else "decode_step_kernels"
+    kernel_name = {"persistent": "mt_decode_step_persistent", "batched": "mt_decode_step_batched",
+                   "kernels": "decode_step_kernels"}[taken]
     # the persistent step is one launch per sequence: each reads all weights
     # and its own sequence's cache
     lps = B if persistent else 1
@@ -409,7 +411,7 @@ def main() -> int:
                    "d_model": shape.d_model, "heads": shape.n_heads, "d_ff": shape.d_ff,
                    "vocab": shape.vocab, "batch": B, "prefix_rows": wl.prefix_len,
                    "prompt_tokens": wl.n_tokens, "decode_steps": n_dec, "t_cap": wl.t_cap,
-                   "decode_path": "persistent" if persistent else "kernels",
+                   "decode_path": taken,
                    **({"cfg": args.cfg, "cfg_pairs": pairs} if pairs is not None else {})},
         # guided tokens with CFG (one per pair), else one per sequence
         "decode_tokens_per_s": round((pairs if pairs is not None else B) * 1000.0 / ms_tok, 1),
@@ -465,13 +467,27 @@ def measure_copy_peak(torch, gib: int = 4, reps: int = 5) -> float:
     return 2.0 * n / (best * 1e-3) / 1e9
 
 
-def dec_is_persistent(dec) -> bool:
+def path_taken(dec, path: int, B: int) -> str:
+    """The decode implementation the library runs for `path` (its
+    MT_DECODE_AUTO rule: B <= 2 the persistent step per sequence, 3 <= B <= 8
+    the batched step where supported, else the kernels)."""
     from audio_midi_transformer_amd import binding
-    try:
-        dec.set_decode_path(binding.MT_DECODE_PERSISTENT)
-    except binding.MTError:
-        return False
-    return True
+
+    def ok(p):
+        try:
+            dec.set_decode_path(p)
+        except binding.MTError:
+            return False
+        return True
+
+    if path == binding.MT_DECODE_KERNELS:
+        return "kernels"
+    if ok(binding.MT_DECODE_BATCHED) and (path == binding.MT_DECODE_BATCHED or
+                                          (path == binding.MT_DECODE_AUTO and B >= 3)):
+        return "batched"
+    if ok(binding.MT_DECODE_PERSISTENT) and path in (binding.MT_DECODE_AUTO, binding.MT_DECODE_PERSISTENT):
+        return "persistent"
+    return "kernels"
 
 
 if __name__ == "__main__":

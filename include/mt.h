@@ -272,15 +272,24 @@ int mt_kv_cache(mt_model* m, const float** k, const float** v);
  * (MT_ERR_INVALID_ARG after an out-of-range token id).  Clears the flag. */
 int mt_check(mt_model* m);
 
-/* Decode implementation selector (for measurement and parity of both):
- *   MT_DECODE_AUTO       persistent single-launch step when supported
+/* Decode implementation selector (for measurement and parity of all):
+ *   MT_DECODE_AUTO       B <= 2: one persistent launch per sequence;
+ *                        3 <= B <= 8: the batched step where supported;
+ *                        otherwise the kernels
  *   MT_DECODE_KERNELS    one kernel per operation
  *   MT_DECODE_PERSISTENT one persistent launch per sequence (B <= 2; past
- *                        its cache reach, 2048 positions or 4096 at
- *                        d_model 768, the kernels run) */
+ *                        its cache reach, 2560 to 5376 positions by width,
+ *                        the kernels run)
+ *   MT_DECODE_BATCHED    one launch for the whole batch, each sequence on
+ *                        its own XCD (2 <= B <= 8, INT4 weights without
+ *                        MT_FLAG_W4A8, d_model 768 or 1024; any position
+ *                        below t_cap); MT_ERR_UNSUPPORTED otherwise
+ * Every path computes the same decoder step ("MuScriptor Medium --
+ * optimized W4A32 ONNX Runtime", "Model variant"). */
 #define MT_DECODE_AUTO 0
 #define MT_DECODE_KERNELS 1
 #define MT_DECODE_PERSISTENT 2
+#define MT_DECODE_BATCHED 3
 int mt_set_decode_path(mt_model* m, int32_t path);
 
 /* Destroy: synchronises the device, frees every buffer.  NULL is a no-op. */

@@ -1,0 +1,193 @@
+"""GPU parity of the batched single-launch decode step (MT_DECODE_BATCHED:
+every sequence of a batch of 2 .. 8 on its own XCD, one launch per step)
+against the CPU oracle:
+
+  * lockstep batches at small and medium width, prefixes that leave
+    attention splits empty (3 rows) or span several 128-position rounds;
+  * sequences at unrelated positions, from an empty cache (the new row is
+    the only key) to positions on both sides of the rounds' boundaries,
+    each checked against its own one-sequence oracle model;
+  * KV-cache indexing with a NaN-payload sentinel: each step writes exactly
+    slot T_b of sequence b in every layer;
+  * full-depth models against the per-operation kernels.
+
+The step computes the decoder operations of "MuScriptor Medium -- optimized
+W4A32 ONNX Runtime", "Model variant" (INT4 group-32 projections,
+GroupQueryAttention over the in-place FP32 cache, SkipLayerNormalization),
+one decoder call per step returning last-position logits
+("unifolia/muscriptor-small-onnx", "Files")."""
+import numpy as np
+import pytest
+
+from audio_midi_transformer_amd import binding, synth
+from parity import TOL, check_greedy, compare_logits
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+WIDTHS = {"small": synth.SMALL, "medium": synth.MEDIUM}
+SENTINEL = 0x7FC0DEAD
+
+
+def _dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda", 0)
+
+
+def _t(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(_dev())
+
+
+def _shape(width, layers):
+    base = WIDTHS[width]
+    return synth.ModelShape(base.name, layers, base.d_model, base.n_heads, base.d_ff)
+
+
+@pytest.mark.parametrize("width", ["small", "medium"])
+@pytest.mark.parametrize("B", [2, 8])
+@pytest.mark.parametrize("P", [3, 300])
+def test_batched_lockstep_vs_oracle(oracle_mod, width, B, P):
+    """All sequences at one position: prefix of P rows, then 6 teacher-forced
+    steps (P = 300 at medium width: 150 positions per split, two rounds)."""
+    print(f"[batched lockstep] width={width} B={B} P={P}", flush=True)
+    _dev()
+    shape = _shape(width, 2)
+    w = synth.model_weights(shape, 70)
+    steps, t_cap = 6, P + 8
+    prefix = np.random.default_rng(P).standard_normal((B, P, shape.d_model)).astype(np.float32)
+    om = oracle_mod.OracleModel.from_weights(w, batch=B, t_cap=t_cap)
+    dec = binding.Decoder(w, batch=B, t_cap=t_cap)
+    dec.set_decode_path(binding.MT_DECODE_BATCHED)
+    lo, no = om.forward(prefix=prefix)
+    lg, ng = dec.prefill(None, _t(prefix))
+    compare_logits(lg.cpu().numpy(), lo, TOL[width], "prefill")
+    for k in range(steps):
+        tok = no.reshape(B, 1)
+        lo, no = om.forward(tokens=tok)
+        lg, ng = dec.decode_step(_t(tok.reshape(B)))
+        g = lg.cpu().numpy()
+        compare_logits(g, lo, TOL[width], f"step {k}")
+        check_greedy(ng.cpu().numpy(), g, lo, TOL[width], f"step {k}")
+    dec.check()
+    K, V = dec.kv_cache()
+    Ko, Vo = om.kv()
+    T = om.position
+    np.testing.assert_allclose(K[:, :, :T].cpu().numpy(), Ko[:, :, :T], rtol=0, atol=5e-5)
+    np.testing.assert_allclose(V[:, :, :T].cpu().numpy(), Vo[:, :, :T], rtol=0, atol=5e-5)
+    dec.close()
+    om.close()
+
+
+def _fill_sentinel(dec, shape, B, t_cap):
+    n = shape.n_layers * B * t_cap * shape.d_model
+    sentinel = torch.full((n,), SENTINEL, dtype=torch.int32, device=_dev())
+    for p in dec.kv_pointers():
+        binding.hip_copy(p, sentinel.data_ptr(), n * 4)
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("width", ["small", "medium"])
+def test_batched_ragged_positions(oracle_mod, width):
+    """Eight sequences at their own positions (0, 1, 2, 255, 256, 257, 513 and
+    600 rows before the first step: an empty cache, single keys, and both
+    sides of the 128-position round boundaries of each split), four lockstep
+    steps, each sequence against its own oracle model; the cache holds data
+    in exactly slots [0, T_b) of sequence b, every other slot keeps the
+    sentinel bits."""
+    print(f"[batched ragged] width={width}", flush=True)
+    _dev()
+    shape = _shape(width, 2)
+    w = synth.model_weights(shape, 71)
+    lens = [0, 1, 2, 255, 256, 257, 513, 600]
+    B, t_cap, steps = len(lens), 608, 4
+    dec = binding.Decoder(w, batch=B, t_cap=t_cap)
+    dec.set_decode_path(binding.MT_DECODE_BATCHED)
+    oms = [oracle_mod.OracleModel.from_weights(w, batch=1, t_cap=t_cap) for _ in range(B)]
+    _fill_sentinel(dec, shape, B, t_cap)
+    rng = np.random.default_rng(9)
+    for b, P in enumerate(lens):
+        if P == 0:
+            continue
+        x = rng.standard_normal((P, shape.d_model)).astype(np.float32)
+        oms[b].forward(prefix=x[None])
+        dec.prefill_seq(b, None, _t(x))
+    for k in range(steps):
+        tok = rng.integers(0, shape.vocab, size=B)
+        lg, ng = dec.decode_step(_t(tok))
+        g, nx = lg.cpu().numpy(), ng.cpu().numpy()
+        for b in range(B):
+            lo, _ = oms[b].forward(tokens=tok[b:b + 1, None])
+            compare_logits(g[b:b + 1], lo, TOL[width], f"step {k} sequence {b} (position {lens[b] + k})")
+            check_greedy(nx[b:b + 1], g[b:b + 1], lo, TOL[width], f"step {k} sequence {b}")
+    dec.check()
+    torch.cuda.synchronize()
+    K, V = dec.kv_cache()
+    for name, c, idx in (("K", K, 0), ("V", V, 1)):
+        bits = c.view(torch.int32).cpu().numpy()
+        vals = c.cpu().numpy()
+        for b in range(B):
+            tb = lens[b] + steps
+            assert dec.position_seq(b) == tb
+            assert np.all(bits[:, b, tb:] == SENTINEL), f"{name} slots >= {tb} of sequence {b} were written"
+            assert not np.any(bits[:, b, :tb] == SENTINEL), f"a live {name} slot of sequence {b} is unwritten"
+            ref = oms[b].kv()[idx]
+            np.testing.assert_allclose(vals[:, b, :tb], ref[:, 0, :tb], rtol=0, atol=5e-5)
+    dec.close()
+    for m in oms:
+        m.close()
+
+
+@pytest.mark.parametrize("width", ["small", "medium"])
+def test_batched_equals_kernel_path_full_depth(width):
+    """Full-depth models, B = 8, 504-row prefixes, 24 teacher-forced steps:
+    the batched step and the per-operation kernels agree within the
+    tolerance (both are checked against the oracle elsewhere)."""
+    print(f"[batched full depth] width={width}", flush=True)
+    _dev()
+    shape = WIDTHS[width]
+    w = synth.model_weights(shape, 72)
+    packed = binding.pack_weights(w)
+    B = 8
+    prefix = _t(np.random.default_rng(11).standard_normal((B, 504, shape.d_model)).astype(np.float32))
+    a = binding.Decoder(w, batch=B, t_cap=600, packed=packed)
+    b = binding.Decoder(w, batch=B, t_cap=600, packed=packed)
+    a.set_decode_path(binding.MT_DECODE_BATCHED)
+    b.set_decode_path(binding.MT_DECODE_KERNELS)
+    la, na = a.prefill(None, prefix)
+    lb, nb = b.prefill(None, prefix)
+    tol = TOL[width]
+    for k in range(24):
+        tok = nb.clone()
+        la, na = a.decode_step(tok)
+        lb, nb = b.decode_step(tok)
+        d = float((la - lb).abs().max())
+        assert d <= tol, f"step {k}: batched vs kernels max |delta| {d}"
+    a.check()
+    b.check()
+    ka, va = a.kv_cache()
+    kb, vb = b.kv_cache()
+    T = a.position
+    assert float((ka[:, :, :T] - kb[:, :, :T]).abs().max()) <= 5e-5
+    assert float((va[:, :, :T] - vb[:, :, :T]).abs().max()) <= 5e-5
+    a.close()
+    b.close()
+
+
+def test_batched_refused_where_unsupported():
+    """B = 1, W4A8 and large width have no batched step: selecting it fails
+    with MT_ERR_UNSUPPORTED instead of running something else."""
+    _dev()
+    tiny = synth.ModelShape("medium", 1, 1024, 16, 4096)
+    w = synth.model_weights(tiny, 73)
+    for kw in ({"batch": 1}, {"batch": 4, "flags": binding.MT_FLAG_W4A8}):
+        dec = binding.Decoder(w, t_cap=16, **kw)
+        with pytest.raises(binding.MTError):
+            dec.set_decode_path(binding.MT_DECODE_BATCHED)
+        dec.close()
+    large = synth.ModelShape("large", 1, 1536, 24, 6144)
+    dec = binding.Decoder(synth.model_weights(large, 74), batch=4, t_cap=16)
+    with pytest.raises(binding.MTError):
+        dec.set_decode_path(binding.MT_DECODE_BATCHED)
+    dec.close()

@@ -1,6 +1,6 @@
-"""GPU decode edge cases on both decode paths (the persistent single-launch
-step and the per-operation kernels), at medium width so that B <= 2 runs the
-persistent step:
+"""GPU decode edge cases on every decode path (the persistent single-launch
+step, one launch per sequence; the batched single-launch step, one XCD per
+sequence; the per-operation kernels), at medium width:
 
   * exact greedy ties: LM-head rows made identical and dominant give
     bit-equal maximum logits, and the pick must be the lowest index (greedy
@@ -28,7 +28,11 @@ pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 
-PATHS = {"persistent": binding.MT_DECODE_PERSISTENT, "kernels": binding.MT_DECODE_KERNELS}
+PATHS = {"persistent": binding.MT_DECODE_PERSISTENT, "kernels": binding.MT_DECODE_KERNELS,
+         "batched": binding.MT_DECODE_BATCHED}
+# (path, batch) pairs: the persistent step takes B <= 2 (one launch per
+# sequence), the batched step 2 <= B <= 8 (one launch, one XCD per sequence)
+CASES = [("persistent", 1), ("persistent", 2), ("kernels", 1), ("kernels", 2), ("batched", 2), ("batched", 8)]
 MEDIUM2 = synth.ModelShape("medium", 2, 1024, 16, 4096)
 SENTINEL = 0x7FC0DEAD
 
@@ -43,8 +47,7 @@ def _t(a):
     return torch.from_numpy(np.ascontiguousarray(a)).to(_dev())
 
 
-@pytest.mark.parametrize("path", list(PATHS))
-@pytest.mark.parametrize("B", [1, 2])
+@pytest.mark.parametrize("path,B", CASES)
 @pytest.mark.parametrize("rows,want", [((5, 6, 261, 700, 1392), 5), ((700, 701, 956, 1392), 700)])
 def test_exact_tie_takes_lowest_index(oracle_mod, path, B, rows, want):
     _dev()
@@ -128,8 +131,7 @@ def test_persistent_kv_sentinel(oracle_mod, B):
     om.close()
 
 
-@pytest.mark.parametrize("path", list(PATHS))
-@pytest.mark.parametrize("B", [1, 2])
+@pytest.mark.parametrize("path,B", CASES)
 def test_decode_from_empty_cache(oracle_mod, path, B):
     """The first call is a decode step with T_past = 0: the new row is the only
     key, so attention returns its V row; then four more steps."""
