@@ -192,8 +192,8 @@ __device__ __forceinline__ void publish1(uint64_t* base, int i0, const float* st
 // cached row once.
 template <int D>
 __device__ __forceinline__ void round_load(const float* kc_l, const float* vc_l, int h, int p0, int n, int i0,
-                                           f32x4_t (&k4)[NPASS], f32x4_t (&v4)[NPASS]) {
-    const int g = threadIdx.x >> 4, ql = threadIdx.x & 15;
+                                           f32x4_t (&k4)[NPASS], f32x4_t (&v4)[NPASS], int t) {
+    const int g = t >> 4, ql = t & 15;
 #pragma unroll
     for (int u = 0; u < NPASS; ++u) {
         const int i = i0 + g + 16 * u;
@@ -206,8 +206,8 @@ __device__ __forceinline__ void round_load(const float* kc_l, const float* vc_l,
 // One round into the lane group's running softmax state (m, l uniform over
 // the group; acc = its lane's four dimensions of sum_t p_t V_t).
 __device__ __forceinline__ void round_step(const f32x4_t (&k4)[NPASS], const f32x4_t (&v4)[NPASS], f32x4_t q4, int i0,
-                                           int n, float& m, float& l, f32x4_t& acc) {
-    const int g = threadIdx.x >> 4;
+                                           int n, float& m, float& l, f32x4_t& acc, int t) {
+    const int g = t >> 4;
     float sc[NPASS];
     float mx = -INFINITY;
 #pragma unroll
@@ -234,6 +234,57 @@ __device__ __forceinline__ void round_step(const f32x4_t (&k4)[NPASS], const f32
     m = mn;
     l = ls;
     acc = a;
+}
+
+// Softmax partial of q_h over cached positions [p0, p0 + n) of head h,
+// streamed through registers in rounds of RNDP positions (round 0 already
+// requested into ka / va; two register sets, the next round in flight while
+// one is used).  q4 holds this lane's four dimensions of q_h.  Each wave's
+// partial (max, sum, acc[64]) lands in wp[wave * PW ..]; the caller
+// synchronises before reading them.
+template <int D>
+__device__ __forceinline__ void split_waves(const float* kc_l, const float* vc_l, int h, int p0, int n, f32x4_t q4,
+                                            f32x4_t (&ka)[NPASS], f32x4_t (&va)[NPASS], float* wp_all, int tid) {
+    const int lane = tid & 63, wave = tid >> 6;
+    const int nr = cdiv(n, RNDP);
+    f32x4_t kb[NPASS], vb[NPASS];
+    float m = -INFINITY, l = 0.f;
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    for (int r = 0; r < nr; r += 2) {
+        if (r + 1 < nr) round_load<D>(kc_l, vc_l, h, p0, n, (r + 1) * RNDP, kb, vb, tid);
+        round_step(ka, va, q4, r * RNDP, n, m, l, acc, tid);
+        if (r + 1 < nr) {
+            if (r + 2 < nr) round_load<D>(kc_l, vc_l, h, p0, n, (r + 2) * RNDP, ka, va, tid);
+            round_step(kb, vb, q4, (r + 1) * RNDP, n, m, l, acc, tid);
+        }
+    }
+    // the four lane groups of each wave (16 lanes apart)
+    float M = fmaxf(m, __shfl_xor(m, 16));
+    M = fmaxf(M, __shfl_xor(M, 32));
+    {
+        const float e = m == -INFINITY ? 0.f : expf(m - M);
+        l *= e;
+        acc = acc * e;
+#pragma unroll
+        for (int o = 16; o <= 32; o <<= 1) {
+            l += __shfl_xor(l, o);
+            acc.x += __shfl_xor(acc.x, o);
+            acc.y += __shfl_xor(acc.y, o);
+            acc.z += __shfl_xor(acc.z, o);
+            acc.w += __shfl_xor(acc.w, o);
+        }
+    }
+    float* wp = wp_all + wave * PW;
+    if (lane == 0) {
+        wp[0] = M;
+        wp[1] = l;
+    }
+    if (lane < 16) {
+        wp[2 + 4 * lane] = acc.x;
+        wp[3 + 4 * lane] = acc.y;
+        wp[4 + 4 * lane] = acc.z;
+        wp[5 + 4 * lane] = acc.w;
+    }
 }
 
 // LDS regions of one workgroup.
@@ -269,56 +320,14 @@ __device__ __forceinline__ bool attention_item(const XArgs& a, const XLds<D, F>&
     const uint32_t ep = a.epoch;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int ql = tid & 15;
-    const int nr = cdiv(n, RNDP);
-    f32x4_t kb[NPASS], vb[NPASS];
     // the first round is requested before q_h is waited for (pre: already
     // requested by the caller)
-    if (nr > 0 && !pre) round_load<D>(kc_l, vc_l, h, p0, n, 0, ka, va);
+    if (n > 0 && !pre) round_load<D>(kc_l, vc_l, h, p0, n, 0, ka, va, tid);
     const Range rq{X + C::XQKV + h * 64, 64, S.qh};
     const Range rk{X + C::XQKV + D + h * 64, with_new ? 64 : 0, S.knew};
     const Range rv{X + C::XQKV + 2 * D + h * 64, with_new ? 64 : 0, S.vnew};
     if (!ll_gather<1, false>(rq, rk, rv, ep, a.err, S.s_flag)) return false;
-    const f32x4_t q4 = *reinterpret_cast<const f32x4_t*>(S.qh + 4 * ql);
-    float m = -INFINITY, l = 0.f;
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    // two register sets: the next round is in flight while one is used
-    for (int r = 0; r < nr; r += 2) {
-        if (r + 1 < nr) round_load<D>(kc_l, vc_l, h, p0, n, (r + 1) * RNDP, kb, vb);
-        round_step(ka, va, q4, r * RNDP, n, m, l, acc);
-        if (r + 1 < nr) {
-            if (r + 2 < nr) round_load<D>(kc_l, vc_l, h, p0, n, (r + 2) * RNDP, ka, va);
-            round_step(kb, vb, q4, (r + 1) * RNDP, n, m, l, acc);
-        }
-    }
-    // the four lane groups of each wave (16 lanes apart) ...
-    float M = fmaxf(m, __shfl_xor(m, 16));
-    M = fmaxf(M, __shfl_xor(M, 32));
-    {
-        const float e = m == -INFINITY ? 0.f : expf(m - M);
-        l *= e;
-        acc = acc * e;
-#pragma unroll
-        for (int o = 16; o <= 32; o <<= 1) {
-            l += __shfl_xor(l, o);
-            acc.x += __shfl_xor(acc.x, o);
-            acc.y += __shfl_xor(acc.y, o);
-            acc.z += __shfl_xor(acc.z, o);
-            acc.w += __shfl_xor(acc.w, o);
-        }
-    }
-    m = M;
-    // ... then the four waves (and the new position)
-    float* wp = S.wp + wave * PW;
-    if (lane == 0) {
-        wp[0] = m;
-        wp[1] = l;
-    }
-    if (lane < 16) {
-        wp[2 + 4 * lane] = acc.x;
-        wp[3 + 4 * lane] = acc.y;
-        wp[4 + 4 * lane] = acc.z;
-        wp[5 + 4 * lane] = acc.w;
-    }
+    split_waves<D>(kc_l, vc_l, h, p0, n, *reinterpret_cast<const f32x4_t*>(S.qh + 4 * ql), ka, va, S.wp, tid);
     lds_barrier();
     if (wave == 0) {
         float mw[5], lw[5];
@@ -455,7 +464,7 @@ __global__ __launch_bounds__(NT, 1) void k_decode_xcd(XArgs a) {
             {
                 const int h0 = j / C::NS, p00 = (j % C::NS) * chunk;
                 const int n0 = max(0, min(t0, p00 + chunk) - p00);
-                if (n0 > 0) round_load<D>(kc_l, vc_l, h0, p00, n0, 0, ka, va);
+                if (n0 > 0) round_load<D>(kc_l, vc_l, h0, p00, n0, 0, ka, va, tid);
             }
             float o[C::NP_QKV];
             wblk_dot<C::LPR_D, C::CPL_D, C::NP_QKV>(wqkv, S.act, S.xs, o, a.nib);
