@@ -41,6 +41,7 @@ __device__ __forceinline__ T gload(const T* p) {
 }
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint4 gload(const uint4* p) {
     const u32x4_t v = *(const __attribute__((address_space(1))) u32x4_t*)(p);
     return make_uint4(v.x, v.y, v.z, v.w);
@@ -532,17 +533,27 @@ __device__ __forceinline__ void load_group(const float* act, int c, float (&x)[3
     }
 }
 
-// Unsigned byte N of x as float: one v_cvt_f32_ubyte<N> per weight.
-template <int N>
-__device__ __forceinline__ float ubyte(unsigned x) {
-    return (float)(uint8_t)(x >> (8 * N));
+// Two nibble values (0 .. 15, one per byte, bytes 2 sel and 2 sel + 1 of x)
+// as floats, u * 2^-9, in one v_cvt_pk_f32_fp8: an FP8 E4M3 byte whose sign
+// and upper exponent bits are zero encodes u * 2^-9 exactly (u < 8
+// subnormal, 8 <= u < 16 the first binade; u * 2^-10 in the variant with
+// exponent bias 8), so the conversion takes two weights per instruction
+// instead of one v_cvt_f32_ubyte each.  u4_unit() gives the factor back.
+template <bool SEL>
+__device__ __forceinline__ f32x2_t u4_pair(unsigned x) {
+    return __builtin_amdgcn_cvt_pk_f32_fp8((int)x, SEL);
+}
+// 1 / (the float u4_pair gives for u = 1): a power of two.
+__device__ __forceinline__ float u4_unit() {
+    return 8.0f / u4_pair<false>(8u).x;
 }
 
-// sum_k u_k x_k over one group.  Byte j of the group holds input 2j (low
-// nibble) and 2j+1 (high nibble).  `m` is 0x0F0F0F0F, passed in at run time:
-// with a literal mask the compiler knows the upper bits of each byte are
-// zero and extracts every nibble with a bit-field instruction before the
-// conversion instead of converting bytes directly.
+// sum_k u_k x_k / u4_unit() over one group.  Byte j of the group holds
+// input 2j (low nibble) and 2j+1 (high nibble).  Every product is the exact
+// power-of-two multiple of the one with integer u, and the sum is formed in
+// the same order, so after the factor the result is the integer form's bit
+// for bit.  `m` is 0x0F0F0F0F, passed in at run time so that the compiler
+// does not turn the mask and shift into bit-field extracts.
 __device__ __forceinline__ float dot_u(uint4 w, const float (&x)[32], unsigned m) {
     const unsigned wd[4] = {w.x, w.y, w.z, w.w};
     float acc = 0.f;
@@ -550,15 +561,17 @@ __device__ __forceinline__ float dot_u(uint4 w, const float (&x)[32], unsigned m
     for (int k = 0; k < 4; ++k) {
         const unsigned lo = wd[k] & m;
         const unsigned hi = (wd[k] >> 4) & m;
+        const f32x2_t l01 = u4_pair<false>(lo), l23 = u4_pair<true>(lo);
+        const f32x2_t h01 = u4_pair<false>(hi), h23 = u4_pair<true>(hi);
         const float* xm = x + 8 * k;
-        acc = fmaf(ubyte<0>(lo), xm[0], acc);
-        acc = fmaf(ubyte<0>(hi), xm[1], acc);
-        acc = fmaf(ubyte<1>(lo), xm[2], acc);
-        acc = fmaf(ubyte<1>(hi), xm[3], acc);
-        acc = fmaf(ubyte<2>(lo), xm[4], acc);
-        acc = fmaf(ubyte<2>(hi), xm[5], acc);
-        acc = fmaf(ubyte<3>(lo), xm[6], acc);
-        acc = fmaf(ubyte<3>(hi), xm[7], acc);
+        acc = fmaf(l01.x, xm[0], acc);
+        acc = fmaf(h01.x, xm[1], acc);
+        acc = fmaf(l01.y, xm[2], acc);
+        acc = fmaf(h01.y, xm[3], acc);
+        acc = fmaf(l23.x, xm[4], acc);
+        acc = fmaf(h23.x, xm[5], acc);
+        acc = fmaf(l23.y, xm[6], acc);
+        acc = fmaf(h23.y, xm[7], acc);
     }
     return acc;
 }
@@ -571,6 +584,7 @@ template <int LPR, int CPL, int NP>
 __device__ __forceinline__ void wblk_dot(const WBlk<CPL, NP>& w, const float* act, const float* xs,
                                          float (&out)[NP], unsigned m) {
     const int lr = threadIdx.x % LPR;
+    const float unit = u4_unit();
     float acc[NP];
 #pragma unroll
     for (int p = 0; p < NP; ++p) acc[p] = 0.f;
@@ -581,7 +595,7 @@ __device__ __forceinline__ void wblk_dot(const WBlk<CPL, NP>& w, const float* ac
         load_group(act, c, x);
         const float x8 = -8.f * xs[c];
 #pragma unroll
-        for (int p = 0; p < NP; ++p) acc[p] = fmaf(w.s[p][j], dot_u(w.q[p][j], x, m) + x8, acc[p]);
+        for (int p = 0; p < NP; ++p) acc[p] = fmaf(w.s[p][j], fmaf(dot_u(w.q[p][j], x, m), unit, x8), acc[p]);
     }
 #pragma unroll
     for (int p = 0; p < NP; ++p) out[p] = group_reduce<LPR>(acc[p]);
