@@ -81,6 +81,18 @@ struct XCfg {
     static constexpr int QKV_ROWS = 3 * D / NW, O_ROWS = D / NW, UP_ROWS = F / NW, DN_ROWS = D / NW;
     static constexpr int NP_QKV = cdiv(QKV_ROWS, RP_D), NP_O = cdiv(O_ROWS, RP_D);
     static constexpr int NP_UP = cdiv(UP_ROWS, RP_D), NP_DN = cdiv(DN_ROWS, RP_F);
+    // each phase's rows in NCH chunks held in registers one or two at a
+    // time: the whole block where it takes at most 100 registers (small and
+    // medium width), else chunks of at most 50 (large: QKV 3, up and down 4)
+    static constexpr int nch_for(int np, int cpl) {
+        if (np * cpl * 5 <= 100) return 1;
+        for (int c = 2; c <= np; ++c)
+            if (np % c == 0 && (np / c) * cpl * 5 <= 50) return c;
+        return np;
+    }
+    static constexpr int NCH_QKV = nch_for(NP_QKV, CPL_D), NCH_O = nch_for(NP_O, CPL_D);
+    static constexpr int NCH_UP = nch_for(NP_UP, CPL_D), NCH_DN = nch_for(NP_DN, CPL_F);
+    static_assert(NCH_QKV <= 4 && NCH_O <= 4 && NCH_UP <= 4 && NCH_DN <= 4, "chunks");
     static constexpr int STG = cmax(cmax(QKV_ROWS, UP_ROWS), cmax(O_ROWS, DN_ROWS));
     // exchange words per layer of one sequence (one copy of each vector)
     static constexpr int XQKV = 0;                   // q | k | v [3D]
@@ -176,6 +188,42 @@ __device__ __forceinline__ void wload(WBlk<CPL, NP>& w, const uint8_t* __restric
             w.s[p][j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, vs + j * LPR * 4, ss, 0));
         }
     }
+}
+
+// One chunk of a phase's rows: request the next chunk (NEXT) into `nxt`,
+// then dot the rows in `cur` (rows rbase .. of the phase) and emit each
+// output row below nrows.
+template <int LPR, int CPL, int NPC, int CR, bool NEXT, typename Emit>
+__device__ __forceinline__ void chunk_step(const WBlk<CPL, NPC>& cur, WBlk<CPL, NPC>& nxt, const uint8_t* Wq,
+                                           const float* Ws, int K, int row_next, int rbase, int nrows,
+                                           const float* act, const float* xs, unsigned nib, Emit& emit) {
+    if constexpr (NEXT) wload<LPR, CPL, NPC, CR>(nxt, Wq, Ws, K, row_next);
+    float o[NPC];
+    wblk_dot<LPR, CPL, NPC>(cur, act, xs, o, nib);
+#pragma unroll
+    for (int p = 0; p < NPC; ++p) {
+        const int rr = out_row<LPR>(p);
+        if (rr >= 0 && rbase + rr < nrows) emit(rbase + rr, o[p]);
+    }
+}
+
+// The rows row0 .. row0 + NROWS - 1 of one projection against act (group
+// sums xs), in NCH chunks of NP / NCH passes: chunk 0 is in w0 (requested
+// by the caller), chunk c + 1 is requested before chunk c is used, so at
+// most two chunks are in registers.  emit(row, value) for each row.
+template <int LPR, int CPL, int NP, int NCH, int NROWS, typename Emit>
+__device__ __forceinline__ void rows_dot(WBlk<CPL, NP / NCH>& w0, const uint8_t* Wq, const float* Ws, int K, int row0,
+                                         const float* act, const float* xs, unsigned nib, Emit emit) {
+    constexpr int NPC = NP / NCH, CR = NPC * (NT / LPR);
+    static_assert(NP % NCH == 0 && (NCH == 1 || NROWS % CR == 0) && NCH <= 4, "chunks");
+    WBlk<CPL, NPC> w1;
+    chunk_step<LPR, CPL, NPC, CR, (NCH > 1)>(w0, w1, Wq, Ws, K, row0 + CR, 0, NROWS, act, xs, nib, emit);
+    if constexpr (NCH > 1)
+        chunk_step<LPR, CPL, NPC, CR, (NCH > 2)>(w1, w0, Wq, Ws, K, row0 + 2 * CR, CR, NROWS, act, xs, nib, emit);
+    if constexpr (NCH > 2)
+        chunk_step<LPR, CPL, NPC, CR, (NCH > 3)>(w0, w1, Wq, Ws, K, row0 + 3 * CR, 2 * CR, NROWS, act, xs, nib, emit);
+    if constexpr (NCH > 3)
+        chunk_step<LPR, CPL, NPC, CR, false>(w1, w0, Wq, Ws, K, 0, 3 * CR, NROWS, act, xs, nib, emit);
 }
 
 // Words i0 .. i0 + nv - 1 of a vector, staged in LDS by the lanes that
@@ -432,12 +480,18 @@ __global__ __launch_bounds__(NT, 1) void k_decode_xcd(XArgs a) {
     }
 
     const int qrow = j * C::QKV_ROWS, orow = j * C::O_ROWS, urow = j * C::UP_ROWS, drow = j * C::DN_ROWS;
-    WBlk<C::CPL_D, C::NP_QKV> wqkv;
-    WBlk<C::CPL_D, C::NP_O> wo;
-    WBlk<C::CPL_D, C::NP_UP> wu;
-    WBlk<C::CPL_F, C::NP_DN> wd;
+    // the first chunk of each phase's rows (the whole block at small and
+    // medium width)
+    constexpr int QC = C::NP_QKV / C::NCH_QKV, OC = C::NP_O / C::NCH_O;
+    constexpr int UC = C::NP_UP / C::NCH_UP, DC = C::NP_DN / C::NCH_DN;
+    constexpr int QR0 = C::NCH_QKV == 1 ? C::QKV_ROWS : QC * C::RP_D, OR0 = C::NCH_O == 1 ? C::O_ROWS : OC * C::RP_D;
+    constexpr int UR0 = C::NCH_UP == 1 ? C::UP_ROWS : UC * C::RP_D, DR0 = C::NCH_DN == 1 ? C::DN_ROWS : DC * C::RP_F;
+    WBlk<C::CPL_D, QC> wqkv;
+    WBlk<C::CPL_D, OC> wo;
+    WBlk<C::CPL_D, UC> wu;
+    WBlk<C::CPL_F, DC> wd;
     LnRegs<D> ln1, ln2;
-    wload<C::LPR_D, C::CPL_D, C::NP_QKV, C::QKV_ROWS>(wqkv, a.wq + O::QO, a.ws + O::QS, D, qrow);
+    wload<C::LPR_D, C::CPL_D, QC, QR0>(wqkv, a.wq + O::QO, a.ws + O::QS, D, qrow);
     ln_load<D>(ln1, a.ln, a.ln + D);
     for (int l = 0; l < a.L; ++l) {
         uint64_t* X = XS + (size_t)l * C::LAYER_WORDS;
@@ -466,13 +520,8 @@ __global__ __launch_bounds__(NT, 1) void k_decode_xcd(XArgs a) {
                 const int n0 = max(0, min(t0, p00 + chunk) - p00);
                 if (n0 > 0) round_load<D>(kc_l, vc_l, h0, p00, n0, 0, ka, va, tid);
             }
-            float o[C::NP_QKV];
-            wblk_dot<C::LPR_D, C::CPL_D, C::NP_QKV>(wqkv, S.act, S.xs, o, a.nib);
-#pragma unroll
-            for (int p = 0; p < C::NP_QKV; ++p) {
-                const int rr = out_row<C::LPR_D>(p);
-                if (rr >= 0 && rr < C::QKV_ROWS) S.stg[rr] = o[p];
-            }
+            rows_dot<C::LPR_D, C::CPL_D, C::NP_QKV, C::NCH_QKV, C::QKV_ROWS>(
+                wqkv, wq + O::QO, ws + O::QS, D, qrow, S.act, S.xs, a.nib, [&](int rr, float v) { S.stg[rr] = v; });
             lds_barrier();
             for (int t = tid; t < C::QKV_ROWS; t += NT) {
                 const int g = qrow + t;
@@ -495,58 +544,43 @@ __global__ __launch_bounds__(NT, 1) void k_decode_xcd(XArgs a) {
         }
         xstamp(a, l, 3);
         // ---- B: merge the heads; O rows -> exchange
-        wload<C::LPR_D, C::CPL_D, C::NP_O, C::O_ROWS>(wo, wq + O::OO, ws + O::OS, D, orow);
+        wload<C::LPR_D, C::CPL_D, OC, OR0>(wo, wq + O::OO, ws + O::OS, D, orow);
         if (!phase_merge<D, F>(a, S, X)) return;
         xstamp(a, l, 4);
 
         {
-            float o[C::NP_O];
-            wblk_dot<C::LPR_D, C::CPL_D, C::NP_O>(wo, S.act, S.xs, o, a.nib);
-#pragma unroll
-            for (int p = 0; p < C::NP_O; ++p) {
-                const int rr = out_row<C::LPR_D>(p);
-                if (rr >= 0 && rr < C::O_ROWS) S.stg[rr] = o[p];
-            }
+            rows_dot<C::LPR_D, C::CPL_D, C::NP_O, C::NCH_O, C::O_ROWS>(
+                wo, wq + O::OO, ws + O::OS, D, orow, S.act, S.xs, a.nib, [&](int rr, float v) { S.stg[rr] = v; });
             publish1(X + C::XO, orow, S.stg, C::O_ROWS, ep);
         }
         xstamp(a, l, 5);
         // ---- C: r += o; LN2; FFN-up rows + GELU -> exchange
-        wload<C::LPR_D, C::CPL_D, C::NP_UP, C::UP_ROWS>(wu, wq + O::UO, ws + O::US, D, urow);
+        wload<C::LPR_D, C::CPL_D, UC, UR0>(wu, wq + O::UO, ws + O::US, D, urow);
         ln_load<D>(ln2, ln + 2 * D, ln + 3 * D);
         {
             float oi[PER];
             if (!ll_gather_regs<PER>(X + C::XO, D, oi, ep, a.err)) *S.s_flag = 1;
             xstamp(a, l, 6);
             if (!residual_layernorm<D, true>(r, oi, true, ln2, a.eps, S.act, S.xs, S.red, S.s_flag)) return;
-            float o[C::NP_UP];
-            wblk_dot<C::LPR_D, C::CPL_D, C::NP_UP>(wu, S.act, S.xs, o, a.nib);
-#pragma unroll
-            for (int p = 0; p < C::NP_UP; ++p) {
-                const int rr = out_row<C::LPR_D>(p);
-                if (rr >= 0 && rr < C::UP_ROWS) S.stg[rr] = gelu_erf(o[p]);
-            }
+            rows_dot<C::LPR_D, C::CPL_D, C::NP_UP, C::NCH_UP, C::UP_ROWS>(
+                wu, wq + O::UO, ws + O::US, D, urow, S.act, S.xs, a.nib,
+                [&](int rr, float v) { S.stg[rr] = gelu_erf(v); });
             publish1(X + C::XU, urow, S.stg, C::UP_ROWS, ep);
         }
         xstamp(a, l, 7);
         // ---- D: u -> FFN-down rows -> exchange
-        wload<C::LPR_F, C::CPL_F, C::NP_DN, C::DN_ROWS>(wd, wq + O::DO, ws + O::DS, F, drow);
+        wload<C::LPR_F, C::CPL_F, DC, DR0>(wd, wq + O::DO, ws + O::DS, F, drow);
         if (!gather_to_lds<F / NT>(X + C::XU, F, S.u, S.us, ep, a.err, S.s_flag, false)) return;
         xstamp(a, l, 8);
 
         {
-            float o[C::NP_DN];
-            wblk_dot<C::LPR_F, C::CPL_F, C::NP_DN>(wd, S.u, S.us, o, a.nib);
-#pragma unroll
-            for (int p = 0; p < C::NP_DN; ++p) {
-                const int rr = out_row<C::LPR_F>(p);
-                if (rr >= 0 && rr < C::DN_ROWS) S.stg[rr] = o[p];
-            }
+            rows_dot<C::LPR_F, C::CPL_F, C::NP_DN, C::NCH_DN, C::DN_ROWS>(
+                wd, wq + O::DO, ws + O::DS, F, drow, S.u, S.us, a.nib, [&](int rr, float v) { S.stg[rr] = v; });
             publish1(X + C::XF, drow, S.stg, C::DN_ROWS, ep);
         }
         xstamp(a, l, 9);
         if (!last) {
-            wload<C::LPR_D, C::CPL_D, C::NP_QKV, C::QKV_ROWS>(wqkv, wq + a.wq_layer + O::QO, ws + a.ws_layer + O::QS, D,
-                                                              qrow);
+            wload<C::LPR_D, C::CPL_D, QC, QR0>(wqkv, wq + a.wq_layer + O::QO, ws + a.ws_layer + O::QS, D, qrow);
             ln_load<D>(ln1, ln + 4 * D, ln + 5 * D);
         }
     }
@@ -650,7 +684,9 @@ __global__ __launch_bounds__(NT, 1) void k_decode_xcd(XArgs a) {
 
 // ---------------------------------------------------------------- host side
 
-static bool xcd_shape(int d, int F) { return (d == 768 && F == 3072) || (d == 1024 && F == 4096); }
+static bool xcd_shape(int d, int F) {
+    return (d == 768 && F == 3072) || (d == 1024 && F == 4096) || (d == 1536 && F == 6144);
+}
 
 bool batched_supported(int d, int F, int H, int B, int V) {
     if (B < 2 || B > px::MAXB || V < 1 || H * 64 != d || !xcd_shape(d, F)) return false;
@@ -664,6 +700,7 @@ static long seq_words(int L, int d, int F) {
     long lw = 0;
     if (d == 768 && F == 3072) lw = px::XCfg<768, 3072>::LAYER_WORDS;
     else if (d == 1024 && F == 4096) lw = px::XCfg<1024, 4096>::LAYER_WORDS;
+    else if (d == 1536 && F == 6144) lw = px::XCfg<1536, 6144>::LAYER_WORDS;
     else return 0;
     return pd::rup((int)(lw * L + 2 * px::NW), 32);
 }
@@ -706,6 +743,7 @@ hipError_t launch_batched_decode(const BatchedArgs& p, hipStream_t st) {
         if (p.t0[b] < 0 || p.t0[b] >= p.t_cap) return hipErrorInvalidValue;
     if (p.d == 768 && p.F == 3072) return launch_xcd_t<768, 3072>(p, st);
     if (p.d == 1024 && p.F == 4096) return launch_xcd_t<1024, 4096>(p, st);
+    if (p.d == 1536 && p.F == 6144) return launch_xcd_t<1536, 6144>(p, st);
     return hipErrorInvalidValue;
 }
 

@@ -146,7 +146,7 @@ size_t persistent_trace_bytes(int L);
 
 // Single-launch decode step for a batch of 2 .. 8 sequences, one XCD per
 // sequence (mt_decode_batched.hip); INT4 weights, FP32 activations, d_model
-// 768 or 1024.  Sequences may sit at different positions.
+// 768, 1024 or 1536.  Sequences may sit at different positions.
 struct BatchedArgs {
     int L, d, H, F, V, B, t_cap;
     float eps;

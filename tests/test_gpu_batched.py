@@ -2,7 +2,7 @@
 every sequence of a batch of 2 .. 8 on its own XCD, one launch per step)
 against the CPU oracle:
 
-  * lockstep batches at small and medium width, prefixes that leave
+  * lockstep batches at small, medium and large width, prefixes that leave
     attention splits empty (3 rows) or span several 128-position rounds;
   * sequences at unrelated positions, from an empty cache (the new row is
     the only key) to positions on both sides of the rounds' boundaries,
@@ -26,7 +26,7 @@ pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 
-WIDTHS = {"small": synth.SMALL, "medium": synth.MEDIUM}
+WIDTHS = {"small": synth.SMALL, "medium": synth.MEDIUM, "large": synth.LARGE}
 SENTINEL = 0x7FC0DEAD
 
 
@@ -45,7 +45,7 @@ def _shape(width, layers):
     return synth.ModelShape(base.name, layers, base.d_model, base.n_heads, base.d_ff)
 
 
-@pytest.mark.parametrize("width", ["small", "medium"])
+@pytest.mark.parametrize("width", ["small", "medium", "large"])
 @pytest.mark.parametrize("B", [2, 8])
 @pytest.mark.parametrize("P", [3, 300])
 def test_batched_lockstep_vs_oracle(oracle_mod, width, B, P):
@@ -88,7 +88,7 @@ def _fill_sentinel(dec, shape, B, t_cap):
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("width", ["small", "medium"])
+@pytest.mark.parametrize("width", ["small", "medium", "large"])
 def test_batched_ragged_positions(oracle_mod, width):
     """Eight sequences at their own positions (0, 1, 2, 255, 256, 257, 513 and
     600 rows before the first step: an empty cache, single keys, and both
@@ -139,7 +139,7 @@ def test_batched_ragged_positions(oracle_mod, width):
         m.close()
 
 
-@pytest.mark.parametrize("width", ["small", "medium"])
+@pytest.mark.parametrize("width", ["small", "medium", "large"])
 def test_batched_equals_kernel_path_full_depth(width):
     """Full-depth models, B = 8, 504-row prefixes, 24 teacher-forced steps:
     the batched step and the per-operation kernels agree within the
@@ -176,8 +176,8 @@ def test_batched_equals_kernel_path_full_depth(width):
 
 
 def test_batched_refused_where_unsupported():
-    """B = 1, W4A8 and large width have no batched step: selecting it fails
-    with MT_ERR_UNSUPPORTED instead of running something else."""
+    """B = 1 and W4A8 have no batched step: selecting it fails with
+    MT_ERR_UNSUPPORTED instead of running something else."""
     _dev()
     tiny = synth.ModelShape("medium", 1, 1024, 16, 4096)
     w = synth.model_weights(tiny, 73)
@@ -186,8 +186,3 @@ def test_batched_refused_where_unsupported():
         with pytest.raises(binding.MTError):
             dec.set_decode_path(binding.MT_DECODE_BATCHED)
         dec.close()
-    large = synth.ModelShape("large", 1, 1536, 24, 6144)
-    dec = binding.Decoder(synth.model_weights(large, 74), batch=4, t_cap=16)
-    with pytest.raises(binding.MTError):
-        dec.set_decode_path(binding.MT_DECODE_BATCHED)
-    dec.close()
