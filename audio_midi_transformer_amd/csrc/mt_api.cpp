@@ -391,7 +391,7 @@ int mt_create(const mt_config* cfg, const mt_weights* w, int weights_on_device, 
     // the batched step computes W4A32 only
     m->batched_ok = fmt == WF_INT4 && !(c.flags & MT_FLAG_W4A8) && batched_supported(d, F, H, B, V);
     if (m->batched_ok) {
-        const size_t xb = batched_xbuf_bytes(L, d, F, B);
+        const size_t xb = batched_xbuf_bytes(L, d, F, std::min(B, kBatchedGroup));
         if (hipMalloc(&m->bxbuf, xb) != hipSuccess || hipMemsetAsync(m->bxbuf, 0, xb, st) != hipSuccess)
             return bail(fail(MT_ERR_OOM, "mt_create: batched exchange buffer of %zu bytes", xb));
     }
@@ -496,17 +496,24 @@ int mt_decode_step(mt_model* m, const int64_t* token, float* logits, int64_t* ne
     const bool persistent = !batched && m->persistent_ok && m->decode_path != MT_DECODE_KERNELS &&
                             m->decode_path != MT_DECODE_BATCHED && tmax <= persistent_max_position(c.d_model, c.d_ff);
     if (batched) {
-        BatchedArgs ba{};
-        ba.L = c.n_layers; ba.d = c.d_model; ba.H = c.n_heads; ba.F = c.d_ff; ba.V = c.vocab;
-        ba.B = c.batch; ba.t_cap = c.t_cap; ba.eps = c.ln_eps;
-        ba.tok_emb = m->tok_emb; ba.lm_head = m->lm_head; ba.ln = m->ln; ba.ln_final = m->lnf;
-        ba.wq_base = m->wq_all; ba.ws_base = m->ws_all;
-        ba.kc = m->kc; ba.vc = m->vc; ba.kv_seqs = c.batch;
-        ba.token = token; ba.logits = logits; ba.next = next;
-        for (int b = 0; b < c.batch; ++b) ba.t0[b] = m->pos.t[b];
-        ba.epoch = ++m->epoch;
-        ba.xbuf = m->bxbuf; ba.err = m->err; ba.trace = m->trace;
-        HIP_TRY(launch_batched_decode(ba, st));
+        // one launch per group of up to 8 sequences (one XCD each), each on
+        // its group's slice of the cache, one after the other on the stream
+        for (int b0 = 0; b0 < c.batch; b0 += kBatchedGroup) {
+            const int nb = std::min(kBatchedGroup, c.batch - b0);
+            BatchedArgs ba{};
+            ba.L = c.n_layers; ba.d = c.d_model; ba.H = c.n_heads; ba.F = c.d_ff; ba.V = c.vocab;
+            ba.B = nb; ba.t_cap = c.t_cap; ba.eps = c.ln_eps;
+            ba.tok_emb = m->tok_emb; ba.lm_head = m->lm_head; ba.ln = m->ln; ba.ln_final = m->lnf;
+            ba.wq_base = m->wq_all; ba.ws_base = m->ws_all;
+            ba.kc = m->kc + (size_t)b0 * c.t_cap * c.d_model;
+            ba.vc = m->vc + (size_t)b0 * c.t_cap * c.d_model;
+            ba.kv_seqs = c.batch;
+            ba.token = token + b0; ba.logits = logits + (size_t)b0 * c.vocab; ba.next = next + b0;
+            for (int b = 0; b < nb; ++b) ba.t0[b] = m->pos.t[b0 + b];
+            ba.epoch = ++m->epoch;
+            ba.xbuf = m->bxbuf; ba.err = m->err; ba.trace = m->trace;
+            HIP_TRY(launch_batched_decode(ba, st));
+        }
     } else if (persistent) {
         // one launch per sequence (a batch of at most kPersistentMaxSeqs),
         // each on that sequence's slice of the cache

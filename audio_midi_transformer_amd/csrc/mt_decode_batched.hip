@@ -689,7 +689,7 @@ static bool xcd_shape(int d, int F) {
 }
 
 bool batched_supported(int d, int F, int H, int B, int V) {
-    if (B < 2 || B > px::MAXB || V < 1 || H * 64 != d || !xcd_shape(d, F)) return false;
+    if (B < 2 || B > kBatchedMaxSeqs || V < 1 || H * 64 != d || !xcd_shape(d, F)) return false;
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess) return false;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return false;
@@ -738,7 +738,7 @@ static hipError_t launch_xcd_t(const BatchedArgs& p, hipStream_t st) {
 }
 
 hipError_t launch_batched_decode(const BatchedArgs& p, hipStream_t st) {
-    if (p.B < 2 || p.B > px::MAXB || p.kv_seqs < p.B || p.L < 1) return hipErrorInvalidValue;
+    if (p.B < 1 || p.B > px::MAXB || p.kv_seqs < p.B || p.L < 1) return hipErrorInvalidValue;
     for (int b = 0; b < p.B; ++b)
         if (p.t0[b] < 0 || p.t0[b] >= p.t_cap) return hipErrorInvalidValue;
     if (p.d == 768 && p.F == 3072) return launch_xcd_t<768, 3072>(p, st);

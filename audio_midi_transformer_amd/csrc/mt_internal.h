@@ -172,6 +172,10 @@ struct BatchedArgs {
 // the two persistent launches are faster: 0.774 against 0.839 ms per
 // guided token on the medium CFG pair decoding to 2048 positions).
 constexpr int kBatchedAutoSeqs = 3;
+// Sequences per launch of the batched step (one per XCD); batches of up to
+// kBatchedMaxSeqs run as one launch per group of this many.
+constexpr int kBatchedGroup = 8;
+constexpr int kBatchedMaxSeqs = 16;
 bool batched_supported(int d, int F, int H, int B, int V);
 size_t batched_xbuf_bytes(int L, int d, int F, int B);
 hipError_t launch_batched_decode(const BatchedArgs& a, hipStream_t st);

@@ -341,12 +341,14 @@ def main() -> int:
     step_ms = np.concatenate([np.array([a.elapsed_time(b) for a, b in e["per"]])[STEADY_FROM:] for e in evs])
     kernel_name = {"persistent": "mt_decode_step_persistent", "batched": "mt_decode_step_batched",
                    "kernels": "decode_step_kernels"}[taken]
-    # the persistent step is one launch per sequence: each reads all weights
-    # and its own sequence's cache
-    lps = B if persistent else 1
-    per_launch = (np.array([step_bytes(shape, 1, R0 + k + 1, wbytes) for k in range(STEADY_FROM, n_dec)])
-                  if lps > 1 else launch_bytes)
-    achieved = float(per_launch.sum() * lps * args.steps / (step_ms.sum() * 1e-3) / 1e9)
+    # the persistent step is one launch per sequence, the batched step one
+    # per group of up to 8: each launch reads all weights and its own
+    # sequences' cache
+    groups = ([1] * B if persistent else [min(8, B - g) for g in range(0, B, 8)] if taken == "batched" else [B])
+    lps = len(groups)
+    step_launch_bytes = np.array([sum(step_bytes(shape, nb, R0 + k + 1, wbytes) for nb in groups)
+                                  for k in range(STEADY_FROM, n_dec)]) if lps > 1 else launch_bytes
+    achieved = float(step_launch_bytes.sum() * args.steps / (step_ms.sum() * 1e-3) / 1e9)
     # the counter record holds for the workload's own configuration only
     traffic = (traffic_from_profiles(kernel_name, wl.key, variant)
                if lps == 1 and pairs is None and args.batch is None else None)
@@ -432,7 +434,7 @@ def main() -> int:
         "roofline": {"kernel": kernel_name, "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic,
-                     "algorithmic_bytes_per_launch": round(float(per_launch.mean()), 1),
+                     "algorithmic_bytes_per_launch": round(float(step_launch_bytes.mean()) / lps, 1),
                      "avg_launch_us": round(float(step_ms.mean()) * 1000.0 / lps, 2),
                      "launches_per_step": lps},
         "cpu_baseline": None,
@@ -469,7 +471,7 @@ def measure_copy_peak(torch, gib: int = 4, reps: int = 5) -> float:
 
 def path_taken(dec, path: int, B: int) -> str:
     """The decode implementation the library runs for `path` (its
-    MT_DECODE_AUTO rule: B <= 2 the persistent step per sequence, 3 <= B <= 8
+    MT_DECODE_AUTO rule: B <= 2 the persistent step per sequence, 3 <= B <= 16
     the batched step where supported, else the kernels)."""
     from audio_midi_transformer_amd import binding
 

@@ -274,16 +274,17 @@ int mt_check(mt_model* m);
 
 /* Decode implementation selector (for measurement and parity of all):
  *   MT_DECODE_AUTO       B <= 2: one persistent launch per sequence;
- *                        3 <= B <= 8: the batched step where supported;
+ *                        3 <= B <= 16: the batched step where supported;
  *                        otherwise the kernels
  *   MT_DECODE_KERNELS    one kernel per operation
  *   MT_DECODE_PERSISTENT one persistent launch per sequence (B <= 2; past
  *                        its cache reach, 2560 to 5376 positions by width,
  *                        the kernels run)
- *   MT_DECODE_BATCHED    one launch for the whole batch, each sequence on
- *                        its own XCD (2 <= B <= 8, INT4 weights without
- *                        MT_FLAG_W4A8, d_model 768, 1024 or 1536; any
- *                        position below t_cap); MT_ERR_UNSUPPORTED otherwise
+ *   MT_DECODE_BATCHED    one launch per group of up to 8 sequences, each
+ *                        sequence on its own XCD (2 <= B <= 16, INT4
+ *                        weights without MT_FLAG_W4A8, d_model 768, 1024
+ *                        or 1536; any position below t_cap);
+ *                        MT_ERR_UNSUPPORTED otherwise
  * Every path computes the same decoder step ("MuScriptor Medium --
  * optimized W4A32 ONNX Runtime", "Model variant"). */
 #define MT_DECODE_AUTO 0

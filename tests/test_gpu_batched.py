@@ -139,6 +139,52 @@ def test_batched_ragged_positions(oracle_mod, width):
         m.close()
 
 
+@pytest.mark.parametrize("B", [9, 16])
+def test_batched_groups_of_eight(oracle_mod, B):
+    """Batches of 9 and 16 run as one launch per group of up to 8 sequences
+    (the 9th alone on one XCD), each group on its slice of the cache:
+    sequences at staggered positions against their own oracle models, with
+    the NaN-sentinel check of the cache slots."""
+    print(f"[batched groups] B={B}", flush=True)
+    _dev()
+    shape = _shape("medium", 2)
+    w = synth.model_weights(shape, 75)
+    lens = [(37 * b) % 300 for b in range(B)]
+    t_cap, steps = 304, 3
+    dec = binding.Decoder(w, batch=B, t_cap=t_cap)
+    dec.set_decode_path(binding.MT_DECODE_BATCHED)
+    oms = [oracle_mod.OracleModel.from_weights(w, batch=1, t_cap=t_cap) for _ in range(B)]
+    _fill_sentinel(dec, shape, B, t_cap)
+    rng = np.random.default_rng(12)
+    for b, P in enumerate(lens):
+        if P == 0:
+            continue
+        x = rng.standard_normal((P, shape.d_model)).astype(np.float32)
+        oms[b].forward(prefix=x[None])
+        dec.prefill_seq(b, None, _t(x))
+    for k in range(steps):
+        tok = rng.integers(0, shape.vocab, size=B)
+        lg, ng = dec.decode_step(_t(tok))
+        g, nx = lg.cpu().numpy(), ng.cpu().numpy()
+        for b in range(B):
+            lo, _ = oms[b].forward(tokens=tok[b:b + 1, None])
+            compare_logits(g[b:b + 1], lo, TOL["medium"], f"step {k} sequence {b}")
+            check_greedy(nx[b:b + 1], g[b:b + 1], lo, TOL["medium"], f"step {k} sequence {b}")
+    dec.check()
+    torch.cuda.synchronize()
+    K, V = dec.kv_cache()
+    for name, c, idx in (("K", K, 0), ("V", V, 1)):
+        bits = c.view(torch.int32).cpu().numpy()
+        vals = c.cpu().numpy()
+        for b in range(B):
+            tb = lens[b] + steps
+            assert np.all(bits[:, b, tb:] == SENTINEL), f"{name} slots >= {tb} of sequence {b} were written"
+            np.testing.assert_allclose(vals[:, b, :tb], oms[b].kv()[idx][:, 0, :tb], rtol=0, atol=5e-5)
+    dec.close()
+    for m in oms:
+        m.close()
+
+
 @pytest.mark.parametrize("width", ["small", "medium", "large"])
 def test_batched_equals_kernel_path_full_depth(width):
     """Full-depth models, B = 8, 504-row prefixes, 24 teacher-forced steps:
