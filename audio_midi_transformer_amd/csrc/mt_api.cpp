@@ -388,8 +388,7 @@ int mt_create(const mt_config* cfg, const mt_weights* w, int weights_on_device, 
         if (persistent_prepare(m->xbuf, L, d, F, st) != hipSuccess)
             return bail(fail(MT_ERR_HIP, "mt_create: persistent role table"));
     }
-    // the batched step computes W4A32 only
-    m->batched_ok = fmt == WF_INT4 && !(c.flags & MT_FLAG_W4A8) && batched_supported(d, F, H, B, V);
+    m->batched_ok = fmt == WF_INT4 && batched_supported(d, F, H, B, V);
     if (m->batched_ok) {
         const size_t xb = batched_xbuf_bytes(L, d, F, std::min(B, kBatchedGroup));
         if (hipMalloc(&m->bxbuf, xb) != hipSuccess || hipMemsetAsync(m->bxbuf, 0, xb, st) != hipSuccess)
@@ -512,6 +511,7 @@ int mt_decode_step(mt_model* m, const int64_t* token, float* logits, int64_t* ne
             for (int b = 0; b < nb; ++b) ba.t0[b] = m->pos.t[b0 + b];
             ba.epoch = ++m->epoch;
             ba.xbuf = m->bxbuf; ba.err = m->err; ba.trace = m->trace;
+            ba.a8 = (c.flags & MT_FLAG_W4A8) ? 1 : 0;
             HIP_TRY(launch_batched_decode(ba, st));
         }
     } else if (persistent) {

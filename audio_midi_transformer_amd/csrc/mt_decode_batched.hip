@@ -146,6 +146,7 @@ struct XArgs {
     long seq_words;
     int* err;
     unsigned nib;           // 0x0F0F0F0F, see dot_u
+    int a8;                 // 1: W4A8 projections (INT8 activation codes, INT32 group sums)
     uint64_t* trace;        // optional [NWG][L + 1][TRACE_SLOTS] wall-clock stamps
 };
 
@@ -196,10 +197,11 @@ __device__ __forceinline__ void wload(WBlk<CPL, NP>& w, const uint8_t* __restric
 template <int LPR, int CPL, int NPC, int CR, bool NEXT, typename Emit>
 __device__ __forceinline__ void chunk_step(const WBlk<CPL, NPC>& cur, WBlk<CPL, NPC>& nxt, const uint8_t* Wq,
                                            const float* Ws, int K, int row_next, int rbase, int nrows,
-                                           const float* act, const float* xs, unsigned nib, Emit& emit) {
+                                           const float* act, const float* xs, unsigned nib, bool a8, Emit& emit) {
     if constexpr (NEXT) wload<LPR, CPL, NPC, CR>(nxt, Wq, Ws, K, row_next);
     float o[NPC];
-    wblk_dot<LPR, CPL, NPC>(cur, act, xs, o, nib);
+    if (a8) wblk_dot8<LPR, CPL, NPC>(cur, reinterpret_cast<const int8_t*>(act), xs, o);
+    else wblk_dot<LPR, CPL, NPC>(cur, act, xs, o, nib);
 #pragma unroll
     for (int p = 0; p < NPC; ++p) {
         const int rr = out_row<LPR>(p);
@@ -213,17 +215,18 @@ __device__ __forceinline__ void chunk_step(const WBlk<CPL, NPC>& cur, WBlk<CPL, 
 // most two chunks are in registers.  emit(row, value) for each row.
 template <int LPR, int CPL, int NP, int NCH, int NROWS, typename Emit>
 __device__ __forceinline__ void rows_dot(WBlk<CPL, NP / NCH>& w0, const uint8_t* Wq, const float* Ws, int K, int row0,
-                                         const float* act, const float* xs, unsigned nib, Emit emit) {
+                                         const float* act, const float* xs, unsigned nib, bool a8, Emit emit) {
     constexpr int NPC = NP / NCH, CR = NPC * (NT / LPR);
     static_assert(NP % NCH == 0 && (NCH == 1 || NROWS % CR == 0) && NCH <= 4, "chunks");
     WBlk<CPL, NPC> w1;
-    chunk_step<LPR, CPL, NPC, CR, (NCH > 1)>(w0, w1, Wq, Ws, K, row0 + CR, 0, NROWS, act, xs, nib, emit);
+    chunk_step<LPR, CPL, NPC, CR, (NCH > 1)>(w0, w1, Wq, Ws, K, row0 + CR, 0, NROWS, act, xs, nib, a8, emit);
     if constexpr (NCH > 1)
-        chunk_step<LPR, CPL, NPC, CR, (NCH > 2)>(w1, w0, Wq, Ws, K, row0 + 2 * CR, CR, NROWS, act, xs, nib, emit);
+        chunk_step<LPR, CPL, NPC, CR, (NCH > 2)>(w1, w0, Wq, Ws, K, row0 + 2 * CR, CR, NROWS, act, xs, nib, a8, emit);
     if constexpr (NCH > 2)
-        chunk_step<LPR, CPL, NPC, CR, (NCH > 3)>(w0, w1, Wq, Ws, K, row0 + 3 * CR, 2 * CR, NROWS, act, xs, nib, emit);
+        chunk_step<LPR, CPL, NPC, CR, (NCH > 3)>(w0, w1, Wq, Ws, K, row0 + 3 * CR, 2 * CR, NROWS, act, xs, nib, a8,
+                                                 emit);
     if constexpr (NCH > 3)
-        chunk_step<LPR, CPL, NPC, CR, false>(w1, w0, Wq, Ws, K, 0, 3 * CR, NROWS, act, xs, nib, emit);
+        chunk_step<LPR, CPL, NPC, CR, false>(w1, w0, Wq, Ws, K, 0, 3 * CR, NROWS, act, xs, nib, a8, emit);
 }
 
 // Words i0 .. i0 + nv - 1 of a vector, staged in LDS by the lanes that
@@ -414,11 +417,12 @@ __device__ __forceinline__ bool attention_item(const XArgs& a, const XLds<D, F>&
 }
 
 // Phase B: every partial -> merged attention (swizzled, group sums) -> O rows.
-template <int D, int F>
+template <int D, int F, bool A8>
 __device__ __forceinline__ bool phase_merge(const XArgs& a, const XLds<D, F>& S, uint64_t* X) {
     using C = XCfg<D, F>;
     if (!ll_gather1<cdiv(C::ITEMS * PW, NT), false>(X + C::XPART, C::ITEMS * PW, S.p, a.epoch, a.err, S.s_flag))
         return false;
+    float v[D / NT];
 #pragma unroll
     for (int i = 0; i < D / NT; ++i) {
         const int k = threadIdx.x + i * NT;
@@ -435,16 +439,43 @@ __device__ __forceinline__ bool phase_merge(const XArgs& a, const XLds<D, F>& S,
             Ls = fmaf(e, P[s * PW + 1], Ls);
             A = fmaf(e, P[s * PW + 2 + d], A);
         }
-        const float v = A / Ls;
-        S.act[swz(k)] = v;
-        const float t = group_reduce<32>(v);
-        if ((threadIdx.x & 31) == res_lane(32)) S.xs[k >> 5] = t;
+        v[i] = A / Ls;
+    }
+    if constexpr (A8) {
+        // W4A8: codes at cpos(k) and the group scales, the layout the
+        // LayerNorm and the gathers give (group maxima to xs, then scales
+        // and reciprocals once per group, then the codes)
+        lds_barrier();  // the partials are read above; the codes overlay them
+        int8_t* a8p = reinterpret_cast<int8_t*>(S.act);
+        float* rr = S.act + D / 4;
+#pragma unroll
+        for (int i = 0; i < D / NT; ++i) {
+            const int k = threadIdx.x + i * NT;
+            const float am = max32_hi(fabsf(v[i]));
+            if ((threadIdx.x & 31) == res_lane(32)) S.xs[k >> 5] = am;
+        }
+        lds_barrier();
+        group_scales(S.xs, rr, D / 32);
+        lds_barrier();
+#pragma unroll
+        for (int i = 0; i < D / NT; ++i) {
+            const int k = threadIdx.x + i * NT;
+            a8p[cpos(k)] = code8r(v[i], rr[k >> 5]);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < D / NT; ++i) {
+            const int k = threadIdx.x + i * NT;
+            S.act[swz(k)] = v[i];
+            const float t = group_reduce<32>(v[i]);
+            if ((threadIdx.x & 31) == res_lane(32)) S.xs[k >> 5] = t;
+        }
     }
     lds_barrier();
     return true;
 }
 
-template <int D, int F>
+template <int D, int F, bool A8>
 __global__ __launch_bounds__(NT, 1) void k_decode_xcd(XArgs a) {
     using C = XCfg<D, F>;
     using O = XOff<D, F>;
@@ -508,7 +539,7 @@ __global__ __launch_bounds__(NT, 1) void k_decode_xcd(XArgs a) {
             float f[PER] = {};
             if (l > 0 && !ll_gather_regs<PER>(XS + (size_t)(l - 1) * C::LAYER_WORDS + C::XF, D, f, ep, a.err))
                 *S.s_flag = 1;
-            if (!residual_layernorm<D, true>(r, f, l > 0, ln1, a.eps, S.act, S.xs, S.red, S.s_flag)) return;
+            if (!residual_layernorm<D, true>(r, f, l > 0, ln1, a.eps, S.act, S.xs, S.red, S.s_flag, A8)) return;
             xstamp(a, l, 1);
             // the first attention round of the first item is requested
             // here, so it lands during the QKV dot (763 -> 739 us per step
@@ -521,7 +552,7 @@ __global__ __launch_bounds__(NT, 1) void k_decode_xcd(XArgs a) {
                 if (n0 > 0) round_load<D>(kc_l, vc_l, h0, p00, n0, 0, ka, va, tid);
             }
             rows_dot<C::LPR_D, C::CPL_D, C::NP_QKV, C::NCH_QKV, C::QKV_ROWS>(
-                wqkv, wq + O::QO, ws + O::QS, D, qrow, S.act, S.xs, a.nib, [&](int rr, float v) { S.stg[rr] = v; });
+                wqkv, wq + O::QO, ws + O::QS, D, qrow, S.act, S.xs, a.nib, A8, [&](int rr, float v) { S.stg[rr] = v; });
             lds_barrier();
             for (int t = tid; t < C::QKV_ROWS; t += NT) {
                 const int g = qrow + t;
@@ -545,12 +576,12 @@ __global__ __launch_bounds__(NT, 1) void k_decode_xcd(XArgs a) {
         xstamp(a, l, 3);
         // ---- B: merge the heads; O rows -> exchange
         wload<C::LPR_D, C::CPL_D, OC, OR0>(wo, wq + O::OO, ws + O::OS, D, orow);
-        if (!phase_merge<D, F>(a, S, X)) return;
+        if (!phase_merge<D, F, A8>(a, S, X)) return;
         xstamp(a, l, 4);
 
         {
             rows_dot<C::LPR_D, C::CPL_D, C::NP_O, C::NCH_O, C::O_ROWS>(
-                wo, wq + O::OO, ws + O::OS, D, orow, S.act, S.xs, a.nib, [&](int rr, float v) { S.stg[rr] = v; });
+                wo, wq + O::OO, ws + O::OS, D, orow, S.act, S.xs, a.nib, A8, [&](int rr, float v) { S.stg[rr] = v; });
             publish1(X + C::XO, orow, S.stg, C::O_ROWS, ep);
         }
         xstamp(a, l, 5);
@@ -561,21 +592,21 @@ __global__ __launch_bounds__(NT, 1) void k_decode_xcd(XArgs a) {
             float oi[PER];
             if (!ll_gather_regs<PER>(X + C::XO, D, oi, ep, a.err)) *S.s_flag = 1;
             xstamp(a, l, 6);
-            if (!residual_layernorm<D, true>(r, oi, true, ln2, a.eps, S.act, S.xs, S.red, S.s_flag)) return;
+            if (!residual_layernorm<D, true>(r, oi, true, ln2, a.eps, S.act, S.xs, S.red, S.s_flag, A8)) return;
             rows_dot<C::LPR_D, C::CPL_D, C::NP_UP, C::NCH_UP, C::UP_ROWS>(
-                wu, wq + O::UO, ws + O::US, D, urow, S.act, S.xs, a.nib,
+                wu, wq + O::UO, ws + O::US, D, urow, S.act, S.xs, a.nib, A8,
                 [&](int rr, float v) { S.stg[rr] = gelu_erf(v); });
             publish1(X + C::XU, urow, S.stg, C::UP_ROWS, ep);
         }
         xstamp(a, l, 7);
         // ---- D: u -> FFN-down rows -> exchange
         wload<C::LPR_F, C::CPL_F, DC, DR0>(wd, wq + O::DO, ws + O::DS, F, drow);
-        if (!gather_to_lds<F / NT>(X + C::XU, F, S.u, S.us, ep, a.err, S.s_flag, false)) return;
+        if (!gather_to_lds<F / NT>(X + C::XU, F, S.u, S.us, ep, a.err, S.s_flag, A8)) return;
         xstamp(a, l, 8);
 
         {
             rows_dot<C::LPR_F, C::CPL_F, C::NP_DN, C::NCH_DN, C::DN_ROWS>(
-                wd, wq + O::DO, ws + O::DS, F, drow, S.u, S.us, a.nib, [&](int rr, float v) { S.stg[rr] = v; });
+                wd, wq + O::DO, ws + O::DS, F, drow, S.u, S.us, a.nib, A8, [&](int rr, float v) { S.stg[rr] = v; });
             publish1(X + C::XF, drow, S.stg, C::DN_ROWS, ep);
         }
         xstamp(a, l, 9);
@@ -724,16 +755,21 @@ static hipError_t launch_xcd_t(const BatchedArgs& p, hipStream_t st) {
     a.seq_words = seq_words(p.L, D, F);
     a.err = p.err;
     a.nib = 0x0F0F0F0Fu;
+    a.a8 = p.a8;
     a.trace = static_cast<uint64_t*>(p.trace);
     static bool attr_set = false;
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)px::k_decode_xcd<D, F>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           (int)(sizeof(float) * C::LDS_FLOATS));
-        if (e != hipSuccess) return e;
+        for (const void* k : {(const void*)px::k_decode_xcd<D, F, false>, (const void*)px::k_decode_xcd<D, F, true>}) {
+            hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               (int)(sizeof(float) * C::LDS_FLOATS));
+            if (e != hipSuccess) return e;
+        }
         attr_set = true;
     }
-    px::k_decode_xcd<D, F><<<dim3(pd::NWG), dim3(pd::NT), sizeof(float) * C::LDS_FLOATS, st>>>(a);
+    if (p.a8)
+        px::k_decode_xcd<D, F, true><<<dim3(pd::NWG), dim3(pd::NT), sizeof(float) * C::LDS_FLOATS, st>>>(a);
+    else
+        px::k_decode_xcd<D, F, false><<<dim3(pd::NWG), dim3(pd::NT), sizeof(float) * C::LDS_FLOATS, st>>>(a);
     return hipGetLastError();
 }
 

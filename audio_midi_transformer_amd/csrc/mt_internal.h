@@ -145,8 +145,9 @@ int persistent_max_position(int d, int F);
 size_t persistent_trace_bytes(int L);
 
 // Single-launch decode step for a batch of 2 .. 8 sequences, one XCD per
-// sequence (mt_decode_batched.hip); INT4 weights, FP32 activations, d_model
-// 768, 1024 or 1536.  Sequences may sit at different positions.
+// sequence (mt_decode_batched.hip); INT4 weights, FP32 (or W4A8 INT8)
+// activations, d_model 768, 1024 or 1536.  Sequences may sit at different
+// positions.
 struct BatchedArgs {
     int L, d, H, F, V, B, t_cap;
     float eps;
@@ -167,6 +168,7 @@ struct BatchedArgs {
     void* xbuf;             // exchange words, batched_xbuf_bytes
     int* err;
     void* trace;            // optional phase timestamps (NULL = off), persistent_trace_bytes
+    int a8;                 // 1: W4A8 projections
 };
 // MT_DECODE_AUTO takes the batched step from this batch size on (at B = 2
 // the two persistent launches are faster: 0.774 against 0.839 ms per

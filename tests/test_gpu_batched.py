@@ -222,12 +222,12 @@ def test_batched_equals_kernel_path_full_depth(width):
 
 
 def test_batched_refused_where_unsupported():
-    """B = 1 and W4A8 have no batched step: selecting it fails with
-    MT_ERR_UNSUPPORTED instead of running something else."""
+    """B = 1, B > 16 and dense weights have no batched step: selecting it
+    fails with MT_ERR_UNSUPPORTED instead of running something else."""
     _dev()
     tiny = synth.ModelShape("medium", 1, 1024, 16, 4096)
     w = synth.model_weights(tiny, 73)
-    for kw in ({"batch": 1}, {"batch": 4, "flags": binding.MT_FLAG_W4A8}):
+    for kw in ({"batch": 1}, {"batch": 17}, {"batch": 4, "flags": binding.MT_FLAG_DENSE_F16}):
         dec = binding.Decoder(w, t_cap=16, **kw)
         with pytest.raises(binding.MTError):
             dec.set_decode_path(binding.MT_DECODE_BATCHED)

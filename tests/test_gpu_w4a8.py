@@ -202,3 +202,38 @@ def test_w4a8_persistent_vs_kernels_and_oracle(oracle_mod, width):
         d.check()
         d.close()
     om.close()
+
+
+@pytest.mark.parametrize("width", ["small", "medium", "large"])
+def test_w4a8_batched_vs_kernels_and_oracle(oracle_mod, width):
+    """The batched single-launch step (one XCD per sequence) in W4A8 mode at
+    B = 8, sequences at different prefix lengths, against the oracle's W4A8
+    mode and against the per-operation kernels on the same inputs."""
+    _dev()
+    base = {"small": synth.SMALL, "medium": synth.MEDIUM, "large": synth.LARGE}[width]
+    shape = synth.ModelShape(base.name, 2, base.d_model, base.n_heads, base.d_ff)
+    w = synth.model_weights(shape, 10)
+    B, t_cap = 8, 160
+    lens = [1 + 17 * b for b in range(B)]
+    rng = np.random.default_rng(7)
+    xs = [rng.standard_normal((P, shape.d_model)).astype(np.float32) for P in lens]
+    om = oracle_mod.OracleModel.from_weights(w, batch=B, t_cap=t_cap, w4a8=True)
+    for b, x in enumerate(xs):
+        om.forward_seq(b, prefix=x)
+    decs = []
+    for path in (binding.MT_DECODE_BATCHED, binding.MT_DECODE_KERNELS):
+        dec = binding.Decoder(w, batch=B, t_cap=t_cap, flags=A8)
+        dec.set_decode_path(path)
+        for b, x in enumerate(xs):
+            dec.prefill_seq(b, None, _t(x))
+        decs.append(dec)
+    for k in range(8):
+        tok = rng.integers(0, shape.vocab, size=B)
+        lo, _ = om.forward(tokens=tok[:, None])
+        outs = [d.decode_step(_t(tok))[0].cpu().numpy() for d in decs]
+        for o, name in zip(outs, ("batched", "kernels")):
+            _compare(o, lo, f"{name} step {k}")
+    for d in decs:
+        d.check()
+        d.close()
+    om.close()
