@@ -138,13 +138,18 @@ void attn_split(int B, int H, int T, int* nsplit, int* chunk) {
     *chunk = ch;
 }
 
+// Prefill row workspace, per row (floats): x [d] | a [d] | q [d] | att [d] |
+// spare [d] | h [F].  The split-K partials of the O projection go to h
+// (free until FFN-up), those of FFN-down to a .. spare.
+size_t prefill_row_floats(size_t d, size_t F) { return 5 * d + F; }
+
 int ensure_prefill_ws(mt_model* m, size_t rows) {
     if (rows <= m->pf_rows) return MT_OK;
     if (m->pf) HIP_TRY(hipFree(m->pf));
     m->pf = nullptr;
     m->pf_rows = 0;
     const size_t d = m->c.d_model, F = m->c.d_ff;
-    if (dmalloc(&m->pf, rows * (4 * d + F)) != hipSuccess)
+    if (dmalloc(&m->pf, rows * prefill_row_floats(d, F)) != hipSuccess)
         return fail(MT_ERR_OOM, "prefill workspace of %zu rows", rows);
     m->pf_rows = rows;
     return MT_OK;
@@ -152,11 +157,17 @@ int ensure_prefill_ws(mt_model* m, size_t rows) {
 
 // Run every layer over M = B * R rows held in x (row m = b * R + i, position
 // t0 + i).  `decode` selects the split-K decode attention (R == 1).
+// `prefill_ws`: the buffers are the prefill workspace (prefill_row_floats),
+// whose free regions hold split-K partials of the O and FFN-down GEMMs.
 int run_layers(mt_model* m, float* x, float* a, float* q, float* att, float* h, int R, int b0, int nb,
-               bool decode, hipStream_t st) {
+               bool decode, hipStream_t st, bool prefill_ws = false) {
     const mt_config& c = m->c;
     const int d = c.d_model, F = c.d_ff, M = nb * R;
     const bool a8 = (c.flags & MT_FLAG_W4A8) != 0;
+    // GEMM rows of a prefill: O and FFN-down with K split where the 64 x 64
+    // tiles alone leave CUs idle, summed in a fixed order (the result does
+    // not depend on scheduling)
+    const bool splitk = prefill_ws && !decode && !a8 && !gemv_takes_rows(M, R);
     // with few rows (whole sequences of at most 8 rows per GEMV slice) the
     // GEMV applies both LayerNorms itself
     const bool fuse_ln = gemv_fuses_layernorm(M, d) && gemv_takes_rows(M, R);
@@ -195,8 +206,13 @@ int run_layers(mt_model* m, float* x, float* a, float* q, float* att, float* h, 
             }
         } else {
             HIP_TRY(launch_attn_prefill(q, m->kc, m->vc, l, c.batch, b0, nb, c.n_heads, c.t_cap, m->pos, R, att, st));
-            HIP_TRY(launch_w4_matmul(att, d, M, m->proj[l * 4 + 1], nullptr, nullptr, 0.f, x, d, EPI_RESID, nullptr,
-                                     false, st, nullptr, a8));
+            const int so = splitk ? splitk_plan(M, m->proj[l * 4 + 1]) : 1;
+            if (so > 1 && (long)so * d <= F) {
+                HIP_TRY(launch_w4_gemm_splitk(att, d, M, m->proj[l * 4 + 1], x, d, h, so, st));
+            } else {
+                HIP_TRY(launch_w4_matmul(att, d, M, m->proj[l * 4 + 1], nullptr, nullptr, 0.f, x, d, EPI_RESID,
+                                         nullptr, false, st, nullptr, a8));
+            }
         }
         if (fuse_ln) {
             HIP_TRY(launch_w4_matmul(x, d, M, m->proj[l * 4 + 2], ln + 2 * d, ln + 3 * d, c.ln_eps, h, F, EPI_GELU,
@@ -206,8 +222,14 @@ int run_layers(mt_model* m, float* x, float* a, float* q, float* att, float* h, 
             HIP_TRY(launch_w4_matmul(a, d, M, m->proj[l * 4 + 2], nullptr, nullptr, 0.f, h, F, EPI_GELU, nullptr,
                                      false, st, nullptr, a8));
         }
-        HIP_TRY(launch_w4_matmul(h, F, M, m->proj[l * 4 + 3], nullptr, nullptr, 0.f, x, d, EPI_RESID, nullptr,
-                                 false, st, nullptr, a8));
+        const int sd = splitk ? splitk_plan(M, m->proj[l * 4 + 3]) : 1;
+        if (sd > 1 && sd <= 4) {
+            // partials over a, q, att and the spare rows (4 M d floats)
+            HIP_TRY(launch_w4_gemm_splitk(h, F, M, m->proj[l * 4 + 3], x, d, a, sd, st));
+        } else {
+            HIP_TRY(launch_w4_matmul(h, F, M, m->proj[l * 4 + 3], nullptr, nullptr, 0.f, x, d, EPI_RESID, nullptr,
+                                     false, st, nullptr, a8));
+        }
     }
     return MT_OK;
 }
@@ -431,12 +453,12 @@ int prefill_rows(mt_model* m, int b0, int nb, const int64_t* tokens, int32_t S, 
     float* x = nullptr;
     int rc = MT_OK;
     if (fixed_ws) {
-        const size_t need = M * (4 * (size_t)d + c.d_ff), have = noalloc_scratch_floats();
+        const size_t per = prefill_row_floats(d, c.d_ff), need = M * per, have = noalloc_scratch_floats();
         if (!m->noalloc_ws) return fail(MT_ERR_HIP, "%s: the fixed device workspace is not available", who);
         if (need > have)
             return fail(MT_ERR_UNSUPPORTED,
                         "%s: %zu rows need %zu workspace floats, the fixed workspace holds %zu (at most %zu rows)", who,
-                        M, need, have, have / (4 * (size_t)d + c.d_ff));
+                        M, need, have, have / per);
         x = m->noalloc_ws;
     } else {
         rc = ensure_prefill_ws(m, M);
@@ -446,9 +468,9 @@ int prefill_rows(mt_model* m, int b0, int nb, const int64_t* tokens, int32_t S, 
     float* a = x + M * d;
     float* q = a + M * d;
     float* att = q + M * d;
-    float* h = att + M * d;
+    float* h = att + 2 * M * d;  // after the spare rows
     HIP_TRY(launch_embed(tokens, S, prefix, P, m->tok_emb, c.vocab, d, nb, x, m->err, st));
-    rc = run_layers(m, x, a, q, att, h, R, b0, nb, false, st);
+    rc = run_layers(m, x, a, q, att, h, R, b0, nb, false, st, true);
     if (rc) return rc;
     rc = run_head(m, x, R, nb, logits, next, st);
     if (rc) return rc;

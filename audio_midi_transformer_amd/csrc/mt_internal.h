@@ -59,6 +59,12 @@ hipError_t launch_embed(const int64_t* tokens, int S, const float* prefix, int P
                         int V, int d, int B, float* x, int* err, hipStream_t st);
 hipError_t launch_layernorm(const float* x, long ldx, const float* g, const float* b, float eps,
                             int d, int rows, float* y, long ldy, hipStream_t st);
+// Prefill O / FFN-down projections (+= epilogue) with K split nsplit ways
+// (splitk_plan) and a deterministic sum: the products go to part
+// [nsplit][M][N] (nsplit * M * N floats), then are added to y in split order.
+int splitk_plan(int M, const Int4Mat& w);
+hipError_t launch_w4_gemm_splitk(const float* x, int ldx, int M, const Int4Mat& w, float* y, int ldy, float* part,
+                                 int nsplit, hipStream_t st);
 // Split-K partials of the decode attention, [B, H, nsplit, 68] floats.
 struct AttnParts {
     const float* part;

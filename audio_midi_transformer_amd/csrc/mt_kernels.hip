@@ -67,6 +67,10 @@ __device__ __forceinline__ float gelu_erf(float x) {
 struct EpiArgs {
     Epilogue epi;
     QkvDest qkv;
+    // split K with a deterministic sum (k_gemm_w4_bf3 only): workgroup z
+    // of the K split stores its products to part[z][m][n]; k_splitk_add adds
+    // them to y in the order z = 0, 1, ...
+    float* part = nullptr;
 };
 
 __device__ __forceinline__ void epilogue(const EpiArgs& e, float* __restrict__ y, int ldy, int m, int n,
@@ -977,10 +981,38 @@ __global__ __launch_bounds__(256) void k_gemm_w4_bf3(const float* __restrict__ X
                 const int m = m0 + wm * (TM / 2) + i * 16 + 4 * (lane >> 4) + r;
                 const int n = n0 + wn * (NT / 2) + j * 16 + (lane & 15);
                 if (m < M && n < N) {
-                    if (gridDim.z > 1) atomicAdd(Y + (size_t)m * ldy + n, acc[i][j][r]);
+                    if (ep.part) ep.part[((size_t)blockIdx.z * M + m) * N + n] = acc[i][j][r];
+                    else if (gridDim.z > 1) atomicAdd(Y + (size_t)m * ldy + n, acc[i][j][r]);
                     else epilogue(ep, Y, ldy, m, n, acc[i][j][r]);
                 }
             }
+}
+
+// y[m, n] += part[0][m][n] + part[1][m][n] + ... (nsplit terms, added in
+// that order), y with row stride ldy; N a multiple of 4.
+__global__ __launch_bounds__(256) void k_splitk_add(float* __restrict__ y, int ldy, const float* __restrict__ part,
+                                                    int nsplit, int M, int N) {
+    const long n4 = (long)M * N / 4;
+    const long plane = (long)M * N;
+    for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n4; i += (long)gridDim.x * 256) {
+        float4 s = reinterpret_cast<const float4*>(part)[i];
+        for (int z = 1; z < nsplit; ++z) {
+            const float4 p = reinterpret_cast<const float4*>(part + z * plane)[i];
+            s.x += p.x;
+            s.y += p.y;
+            s.z += p.z;
+            s.w += p.w;
+        }
+        const long e = 4 * i;
+        const int m = (int)(e / N), n = (int)(e % N);
+        float4* yp = reinterpret_cast<float4*>(y + (size_t)m * ldy + n);
+        float4 v = *yp;
+        v.x += s.x;
+        v.y += s.y;
+        v.z += s.z;
+        v.w += s.w;
+        *yp = v;
+    }
 }
 
 // ---------------------------------------------------------------- decode attention
@@ -1618,6 +1650,32 @@ hipError_t launch_layernorm(const float* x, long ldx, const float* g, const floa
                             int d, int rows, float* y, long ldy, hipStream_t st) {
     if (d > 8 * 256) return hipErrorInvalidValue;
     hipLaunchKernelGGL(k_layernorm, dim3(rows), dim3(256), 0, st, x, ldx, g, b, eps, d, y, ldy);
+    return hipGetLastError();
+}
+
+int splitk_plan(int M, const Int4Mat& w) {
+    // INT4 weights, 64 x 64 tiles: split K where the unsplit grid would
+    // leave CUs idle, up to 4 ways (at least 256 columns of K each)
+    if (w.fmt != WF_INT4 || w.N % 4) return 1;
+    const long tiles = (long)((M + 63) / 64) * ((w.N + 63) / 64);
+    if (tiles >= 256) return 1;
+    for (int c = 4; c >= 2; --c)
+        if (tiles * c <= 1024 && w.K % (64 * c) == 0 && w.K / c >= 256) return c;
+    return 1;
+}
+
+hipError_t launch_w4_gemm_splitk(const float* x, int ldx, int M, const Int4Mat& w, float* y, int ldy, float* part,
+                                 int nsplit, hipStream_t st) {
+    if (w.fmt != WF_INT4 || nsplit < 1 || w.K % (64 * nsplit) || w.N % 4 || ldy % 4) return hipErrorInvalidValue;
+    EpiArgs ep{};
+    ep.epi = EPI_RESID;
+    ep.part = part;
+    const dim3 grid((w.N + 63) / 64, (M + 63) / 64, nsplit);
+    hipLaunchKernelGGL((k_gemm_w4_bf3<64, 64, 64>), grid, dim3(256), 0, st, x, ldx, M, w.K, w.q, w.s, w.N, y, ldy, ep,
+                       w.K / nsplit);
+    const long n4 = (long)M * w.N / 4;
+    const int blocks = (int)std::min<long>(2048, (n4 + 255) / 256);
+    hipLaunchKernelGGL(k_splitk_add, dim3(blocks), dim3(256), 0, st, y, ldy, part, nsplit, M, w.N);
     return hipGetLastError();
 }
 

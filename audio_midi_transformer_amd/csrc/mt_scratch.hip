@@ -16,7 +16,7 @@
 
 namespace {
 
-constexpr size_t kScratchFloats = size_t(8) << 20;  // 32 MiB
+constexpr size_t kScratchFloats = size_t(9) << 20;  // 36 MiB
 constexpr int kMaxDevices = 64;
 
 }  // namespace

@@ -174,11 +174,11 @@ int mt_prefill(mt_model* m, const int64_t* tokens, int32_t S, const float* prefi
 /* mt_prefill without any allocation, for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc): same arguments, semantics and errors as
- * mt_prefill, but the row workspace is a fixed 32 MiB device array that the
+ * mt_prefill, but the row workspace is a fixed 36 MiB device array that the
  * library holds on each GPU it runs on until the process ends, instead of
  * memory grown with hipMalloc.  Calls no hipMalloc, hipFree or allocating
- * routine.  The workspace takes B * (P + S) * (4 d + d_ff) floats: at most
- * 8 Mi floats (1024 rows at d = 1024, d_ff = 4096; 682 rows at d = 1536);
+ * routine.  The workspace takes B * (P + S) * (5 d + d_ff) floats: at most
+ * 9 Mi floats (1024 rows at d = 1024, d_ff = 4096; 682 rows at d = 1536);
  * larger calls return MT_ERR_UNSUPPORTED before any launch.  Every call on
  * one GPU uses the same array (it keeps the last call's contents; nothing in
  * it needs clearing): calls that overlap on one GPU, from different streams

@@ -69,8 +69,8 @@ def test_noalloc_prefill_matches_prefill():
 
 
 def test_noalloc_refuses_more_rows_than_the_workspace():
-    """8 sequences x 504 rows at d = 1024 need 33 Mi floats; the fixed
-    workspace holds 8 Mi: MT_ERR_UNSUPPORTED, nothing launched, position
+    """8 sequences x 504 rows at d = 1024 need 35.4 Mi floats; the fixed
+    workspace holds 9 Mi: MT_ERR_UNSUPPORTED, nothing launched, position
     unchanged."""
     _dev()
     w = synth.model_weights(MEDIUM2, 62)
