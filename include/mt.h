@@ -282,8 +282,9 @@ int mt_check(mt_model* m);
  *                        the kernels run)
  *   MT_DECODE_BATCHED    one launch per group of up to 8 sequences, each
  *                        sequence on its own XCD (2 <= B <= 16, INT4
- *                        weights without MT_FLAG_W4A8, d_model 768, 1024
- *                        or 1536; any position below t_cap);
+ *                        weights, FP32 or MT_FLAG_W4A8 activations,
+ *                        d_model 768, 1024 or 1536; any position below
+ *                        t_cap);
  *                        MT_ERR_UNSUPPORTED otherwise
  * Every path computes the same decoder step ("MuScriptor Medium --
  * optimized W4A32 ONNX Runtime", "Model variant"). */
