@@ -182,6 +182,42 @@ def reduce_counters(fetch_csv: str, write_csv: str, workload_key: str, calib_mib
     }
 
 
+def phase_summary(trace: np.ndarray, T: int, wl) -> dict:
+    """Median phase durations (us) over layers 1 .. L-2 of one persistent
+    step from its wall-clock stamps [256 workgroups, L + 1, 24 slots] (100 MHz
+    ticks).  Slots per layer: 0 phase start, 1 previous FFN-down output
+    gathered, 2 LN1 done, 15 q_h done, 3 K/V chunk in LDS, 12 scores,
+    13 softmax sums, 14 weighted V sum, 4 partial done, 5 partials gathered
+    (head leader), 17 merged head published, 18 K/V rows done (workgroups
+    without attention duty), 6 attention output gathered, 7 O rows
+    published, 8 O output gathered, 9 FFN-up published, 10 FFN-up output
+    gathered, 11 FFN-down published."""
+    tr = trace.astype(np.int64)
+    L = tr.shape[1] - 1
+    lay = tr[:, 1:L - 1, :]
+    us = 0.01
+
+    def med(mask, a, b):
+        return round(float(np.median((lay[mask, :, b] - lay[mask, :, a]) * us)), 3)
+
+    leader = tr[:, 1, 5] != 0
+    free = (tr[:, 1, 18] != 0) & (tr[:, 1, 6] != 0)
+    per_layer = (tr[:, 2:L, 0] - tr[:, 1:L - 1, 0]) * us
+    lead = {"f_exchange_wait": med(leader, 0, 1), "ln1": med(leader, 1, 2), "q_h": med(leader, 2, 15),
+            "chunk_wait": med(leader, 15, 3), "scores": med(leader, 3, 12), "softmax": med(leader, 12, 13),
+            "weighted_v": med(leader, 13, 14), "partial_out": med(leader, 14, 4),
+            "partials_gather": med(leader, 4, 5), "merge_publish": med(leader, 5, 17),
+            "o_exchange_wait": med(leader, 17, 8), "ln2_up_publish": med(leader, 8, 9),
+            "u_exchange_wait": med(leader, 9, 10), "down_publish": med(leader, 10, 11)}
+    fr = {"f_exchange_wait": med(free, 0, 1), "ln1": med(free, 1, 2), "kv_rows": med(free, 2, 18),
+          "attention_wait": med(free, 18, 6), "o_rows_publish": med(free, 6, 7),
+          "o_exchange_wait": med(free, 7, 8), "ln2_up_publish": med(free, 8, 9),
+          "u_exchange_wait": med(free, 9, 10), "down_publish": med(free, 10, 11)}
+    return {"workload": wl.key, "keys": T, "layers": L, "layer_us_median": round(float(np.median(per_layer)), 3),
+            "head_leader_us": lead, "free_workgroup_us": fr,
+            "workgroups": {"head_leaders": int(leader.sum()), "free": int(free.sum())}}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -208,6 +244,10 @@ def main() -> int:
     ap.add_argument("--reduce-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="reduce two rocprofv3 counter files of a --calibration-copy-mib run to the "
                          "per-launch HBM traffic record (printed as JSON) and exit")
+    ap.add_argument("--phase-trace", type=int, default=None, metavar="T",
+                    help="persistent step only: prefill the workload, decode greedily until the cache "
+                         "holds T positions with per-phase wall-clock stamps (MT_TRACE=1), print the "
+                         "median phase durations of the last step's layers as JSON and exit")
     args = ap.parse_args()
     if args.w4a8 and args.weights != "int4":
         ap.error("--w4a8 needs --weights int4")
@@ -266,6 +306,8 @@ def main() -> int:
         tokens_np = np.concatenate([tokens_np] * 2) if tokens_np is not None else None
     flags = {"": 0, "a8": binding.MT_FLAG_W4A8, "f16": binding.MT_FLAG_DENSE_F16,
              "f32": binding.MT_FLAG_DENSE_F32}[variant]
+    if args.phase_trace is not None:
+        os.environ["MT_TRACE"] = "1"  # read when the model is created
     dec = binding.Decoder(weights, batch=B, t_cap=wl.t_cap, flags=flags)
     path = {"auto": binding.MT_DECODE_AUTO, "kernels": binding.MT_DECODE_KERNELS,
             "persistent": binding.MT_DECODE_PERSISTENT, "batched": binding.MT_DECODE_BATCHED}[args.path]
@@ -309,6 +351,21 @@ def main() -> int:
                 ev["per"][k][1].record(stream)
         if ev is not None:
             ev["s1"].record(stream)
+
+    if args.phase_trace is not None:
+        if taken != "persistent" or not R0 < args.phase_trace <= wl.t_cap:
+            print("--phase-trace needs the persistent path and prefix < T <= t_cap", file=sys.stderr)
+            return 2
+        dec.reset()
+        call(dec.prefill, tokens, prefix, out=nxt[0])
+        k = 0
+        while dec.position < args.phase_trace:
+            call(dec.decode_step, nxt[k & 1], out=nxt[(k + 1) & 1])
+            k += 1
+        torch.cuda.synchronize()
+        dec.check()
+        print(json.dumps(phase_summary(dec.debug_trace(), args.phase_trace, wl)))
+        return 0
 
     for _ in range(args.warmup):
         one_pass()
