@@ -73,6 +73,10 @@ def lib() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run `python -m audio_midi_transformer_amd.build` "
                           "(or __graft_entry__.build())")
+    # torch carries its own HIP runtime; it must be loaded before this
+    # library's.  In the other order this library's device queries fail
+    # (mt_create reports "hipGetDevice failed").
+    import torch  # noqa: F401
     L = ctypes.CDLL(LIB_PATH)
     vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     L.mt_pack_int4.argtypes = [vp, i32, i32, vp, vp]

@@ -171,6 +171,9 @@ int run_layers(mt_model* m, float* x, float* a, float* q, float* att, float* h, 
     // with few rows (whole sequences of at most 8 rows per GEMV slice) the
     // GEMV applies both LayerNorms itself
     const bool fuse_ln = gemv_fuses_layernorm(M, d) && gemv_takes_rows(M, R);
+    // a already holds the LayerNorm the next projection needs: the split-K
+    // sum of the previous projection formed it with the residual update
+    bool a_ready = false;
     for (int l = 0; l < c.n_layers; ++l) {
         const float* ln = m->ln + (size_t)l * 4 * d;
         QkvDest dst{q, m->kc, m->vc, d, l, c.batch, c.t_cap, b0, R, m->pos};
@@ -178,10 +181,11 @@ int run_layers(mt_model* m, float* x, float* a, float* q, float* att, float* h, 
             HIP_TRY(launch_w4_matmul(x, d, M, m->proj[l * 4 + 0], ln, ln + d, c.ln_eps, nullptr, 0, EPI_QKV, &dst,
                                      false, st, nullptr, a8));
         } else {
-            HIP_TRY(launch_layernorm(x, d, ln, ln + d, c.ln_eps, d, M, a, d, st));
+            if (!a_ready) HIP_TRY(launch_layernorm(x, d, ln, ln + d, c.ln_eps, d, M, a, d, st));
             HIP_TRY(launch_w4_matmul(a, d, M, m->proj[l * 4 + 0], nullptr, nullptr, 0.f, nullptr, 0, EPI_QKV, &dst,
                                      false, st, nullptr, a8));
         }
+        a_ready = false;
         if (decode) {
             // split-K attention; the O projection (GEMV) merges the partials,
             // or a merge kernel writes attention rows for the GEMM
@@ -207,8 +211,11 @@ int run_layers(mt_model* m, float* x, float* a, float* q, float* att, float* h, 
         } else {
             HIP_TRY(launch_attn_prefill(q, m->kc, m->vc, l, c.batch, b0, nb, c.n_heads, c.t_cap, m->pos, R, att, st));
             const int so = splitk ? splitk_plan(M, m->proj[l * 4 + 1]) : 1;
-            if (so > 1 && (long)so * d <= F) {
-                HIP_TRY(launch_w4_gemm_splitk(att, d, M, m->proj[l * 4 + 1], x, d, h, so, st));
+            if (so > 1 && (long)so * d <= F && !fuse_ln) {
+                // the sum also forms LN2 of the updated rows into a
+                HIP_TRY(launch_w4_gemm_splitk(att, d, M, m->proj[l * 4 + 1], x, d, h, so, st, ln + 2 * d, ln + 3 * d,
+                                              c.ln_eps, a, d));
+                a_ready = true;
             } else {
                 HIP_TRY(launch_w4_matmul(att, d, M, m->proj[l * 4 + 1], nullptr, nullptr, 0.f, x, d, EPI_RESID,
                                          nullptr, false, st, nullptr, a8));
@@ -218,14 +225,21 @@ int run_layers(mt_model* m, float* x, float* a, float* q, float* att, float* h, 
             HIP_TRY(launch_w4_matmul(x, d, M, m->proj[l * 4 + 2], ln + 2 * d, ln + 3 * d, c.ln_eps, h, F, EPI_GELU,
                                      nullptr, false, st, nullptr, a8));
         } else {
-            HIP_TRY(launch_layernorm(x, d, ln + 2 * d, ln + 3 * d, c.ln_eps, d, M, a, d, st));
+            if (!a_ready) HIP_TRY(launch_layernorm(x, d, ln + 2 * d, ln + 3 * d, c.ln_eps, d, M, a, d, st));
             HIP_TRY(launch_w4_matmul(a, d, M, m->proj[l * 4 + 2], nullptr, nullptr, 0.f, h, F, EPI_GELU, nullptr,
                                      false, st, nullptr, a8));
         }
+        a_ready = false;
         const int sd = splitk ? splitk_plan(M, m->proj[l * 4 + 3]) : 1;
-        if (sd > 1 && sd <= 4) {
-            // partials over a, q, att and the spare rows (4 M d floats)
-            HIP_TRY(launch_w4_gemm_splitk(h, F, M, m->proj[l * 4 + 3], x, d, a, sd, st));
+        if (sd > 1 && sd <= 4 && !fuse_ln) {
+            // partials over a, q, att and the spare rows (4 M d floats); the
+            // sum also forms the next layer's LN1 into a (over the first
+            // partials, each row's read before it is written)
+            const bool next = l + 1 < c.n_layers;
+            const float* lnn = ln + 4 * d;
+            HIP_TRY(launch_w4_gemm_splitk(h, F, M, m->proj[l * 4 + 3], x, d, a, sd, st, next ? lnn : nullptr,
+                                          next ? lnn + d : nullptr, c.ln_eps, a, d));
+            a_ready = next;
         } else {
             HIP_TRY(launch_w4_matmul(h, F, M, m->proj[l * 4 + 3], nullptr, nullptr, 0.f, x, d, EPI_RESID, nullptr,
                                      false, st, nullptr, a8));

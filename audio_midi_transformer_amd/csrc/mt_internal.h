@@ -61,10 +61,13 @@ hipError_t launch_layernorm(const float* x, long ldx, const float* g, const floa
                             int d, int rows, float* y, long ldy, hipStream_t st);
 // Prefill O / FFN-down projections (+= epilogue) with K split nsplit ways
 // (splitk_plan) and a deterministic sum: the products go to part
-// [nsplit][M][N] (nsplit * M * N floats), then are added to y in split order.
+// [nsplit][M][N] (nsplit * M * N floats), then are added to y in split order
+// by one workgroup per row, which with ln_g also writes the next
+// LayerNorm of the updated rows to a (row stride lda; a may be part).
 int splitk_plan(int M, const Int4Mat& w);
 hipError_t launch_w4_gemm_splitk(const float* x, int ldx, int M, const Int4Mat& w, float* y, int ldy, float* part,
-                                 int nsplit, hipStream_t st);
+                                 int nsplit, hipStream_t st, const float* ln_g = nullptr,
+                                 const float* ln_b = nullptr, float eps = 0.f, float* a = nullptr, int lda = 0);
 // Split-K partials of the decode attention, [B, H, nsplit, 68] floats.
 struct AttnParts {
     const float* part;

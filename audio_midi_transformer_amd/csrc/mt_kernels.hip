@@ -988,31 +988,46 @@ __global__ __launch_bounds__(256) void k_gemm_w4_bf3(const float* __restrict__ X
             }
 }
 
+// Row blockIdx.x of y (row stride ldy, N <= 2048 columns):
 // y[m, n] += part[0][m][n] + part[1][m][n] + ... (nsplit terms, added in
-// that order), y with row stride ldy; N a multiple of 4.
-__global__ __launch_bounds__(256) void k_splitk_add(float* __restrict__ y, int ldy, const float* __restrict__ part,
-                                                    int nsplit, int M, int N) {
-    const long n4 = (long)M * N / 4;
-    const long plane = (long)M * N;
-    for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n4; i += (long)gridDim.x * 256) {
-        float4 s = reinterpret_cast<const float4*>(part)[i];
-        for (int z = 1; z < nsplit; ++z) {
-            const float4 p = reinterpret_cast<const float4*>(part + z * plane)[i];
-            s.x += p.x;
-            s.y += p.y;
-            s.z += p.z;
-            s.w += p.w;
-        }
-        const long e = 4 * i;
-        const int m = (int)(e / N), n = (int)(e % N);
-        float4* yp = reinterpret_cast<float4*>(y + (size_t)m * ldy + n);
-        float4 v = *yp;
-        v.x += s.x;
-        v.y += s.y;
-        v.z += s.z;
-        v.w += s.w;
-        *yp = v;
+// that order); then, with g given, a[m, :] = LayerNorm(y[m, :]) * g + b
+// with the statistics formed exactly as k_layernorm forms them (so a is
+// bit-identical to a separate k_layernorm launch).  a may alias
+// part[0]: each thread reads its own elements of the row before writing them.
+__global__ __launch_bounds__(256) void k_splitk_add(float* __restrict__ y, int ldy, const float* part, int nsplit,
+                                                    int M, int N, const float* __restrict__ g,
+                                                    const float* __restrict__ bta, float eps, float* a, int lda) {
+    __shared__ float red[4];
+    const int m = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    float v[8];
+    int n = 0;
+    float s = 0.f;
+    for (int j = tid; j < N; j += 256, ++n) {
+        float p = part[(size_t)m * N + j];
+        for (int z = 1; z < nsplit; ++z) p += part[((size_t)z * M + m) * N + j];
+        const float x = y[(size_t)m * ldy + j] + p;
+        y[(size_t)m * ldy + j] = x;
+        v[n] = x;
+        s += x;
     }
+    if (!g) return;
+    s = wave_sum(s);
+    if (lane == 0) red[wave] = s;
+    __syncthreads();
+    const float mean = ((red[0] + red[1]) + (red[2] + red[3])) / (float)N;
+    __syncthreads();
+    float q = 0.f;
+    for (int k = 0; k < n; ++k) {
+        const float c = v[k] - mean;
+        q = fmaf(c, c, q);
+    }
+    q = wave_sum(q);
+    if (lane == 0) red[wave] = q;
+    __syncthreads();
+    const float var = ((red[0] + red[1]) + (red[2] + red[3])) / (float)N;
+    const float rstd = 1.0f / sqrtf(var + eps);
+    n = 0;
+    for (int j = tid; j < N; j += 256, ++n) a[(size_t)m * lda + j] = (v[n] - mean) * rstd * g[j] + bta[j];
 }
 
 // ---------------------------------------------------------------- decode attention
@@ -1665,17 +1680,17 @@ int splitk_plan(int M, const Int4Mat& w) {
 }
 
 hipError_t launch_w4_gemm_splitk(const float* x, int ldx, int M, const Int4Mat& w, float* y, int ldy, float* part,
-                                 int nsplit, hipStream_t st) {
-    if (w.fmt != WF_INT4 || nsplit < 1 || w.K % (64 * nsplit) || w.N % 4 || ldy % 4) return hipErrorInvalidValue;
+                                 int nsplit, hipStream_t st, const float* ln_g, const float* ln_b, float eps,
+                                 float* a, int lda) {
+    if (w.fmt != WF_INT4 || nsplit < 1 || w.K % (64 * nsplit) || w.N > 8 * 256) return hipErrorInvalidValue;
     EpiArgs ep{};
     ep.epi = EPI_RESID;
     ep.part = part;
     const dim3 grid((w.N + 63) / 64, (M + 63) / 64, nsplit);
     hipLaunchKernelGGL((k_gemm_w4_bf3<64, 64, 64>), grid, dim3(256), 0, st, x, ldx, M, w.K, w.q, w.s, w.N, y, ldy, ep,
                        w.K / nsplit);
-    const long n4 = (long)M * w.N / 4;
-    const int blocks = (int)std::min<long>(2048, (n4 + 255) / 256);
-    hipLaunchKernelGGL(k_splitk_add, dim3(blocks), dim3(256), 0, st, y, ldy, part, nsplit, M, w.N);
+    hipLaunchKernelGGL(k_splitk_add, dim3(M), dim3(256), 0, st, y, ldy, part, nsplit, M, w.N, ln_g, ln_b, eps, a,
+                       lda);
     return hipGetLastError();
 }
 
