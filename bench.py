@@ -66,7 +66,9 @@ def prefill_flops(shape, B: int, M: int) -> float:
 # sources that build and launch each profiled kernel (its traffic record is
 # void once any of them changes)
 KERNEL_SOURCES = {"mt_decode_step_persistent": ("mt_decode_persistent.hip", "mt_pd_common.h", "mt_internal.h",
-                                                  "mt_api.cpp")}
+                                                  "mt_api.cpp"),
+                  "mt_decode_step_batched": ("mt_decode_batched.hip", "mt_pd_common.h", "mt_internal.h",
+                                             "mt_api.cpp")}
 
 
 def kernel_source_hash(kernel: str = "mt_decode_step_persistent") -> str:
@@ -130,12 +132,13 @@ def cpu_baseline(wl, weights, prefix_np, tokens_np, max_steps: int = 8, w4a8: bo
     }
 
 
-KERNEL_SYMBOLS = {"mt_decode_step_persistent": "k_decode_step<"}
+KERNEL_SYMBOLS = {"mt_decode_step_persistent": "k_decode_step<", "mt_decode_step_batched": "k_decode_xcd<"}
 
 
 def reduce_counters(fetch_csv: str, write_csv: str, workload_key: str, calib_mib: int,
                     commands: list) -> dict:
-    """HBM bytes per launch of the persistent decode step from two rocprofv3
+    """HBM bytes per launch of the single-launch decode step (the persistent
+    step at one sequence, the batched step at 3 to 8) from two rocprofv3
     `--pmc FETCH_SIZE` / `--pmc WRITE_SIZE` counter files of one bench pass
     (steps 1, warmup 0, with the calibration copy).  Each counter is scaled by
     the bytes a plain device copy of `calib_mib` MiB really moves over what
@@ -143,6 +146,10 @@ def reduce_counters(fetch_csv: str, write_csv: str, workload_key: str, calib_mib
     library's first kernel), then
     averaged over the launches the bench's steady window covers."""
     import csv
+
+    from audio_midi_transformer_amd import synth
+
+    kernel = "mt_decode_step_persistent" if synth.WORKLOADS[workload_key].batch <= 2 else "mt_decode_step_batched"
 
     def load(path, counter):
         rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
@@ -152,10 +159,8 @@ def reduce_counters(fetch_csv: str, write_csv: str, workload_key: str, calib_mib
         copies = [float(r["Counter_Value"]) for r in rows
                   if "copyBuffer" in r["Kernel_Name"] and int(r["Dispatch_Id"]) < first_mt]
         kern = [float(r["Counter_Value"]) for r in rows
-                if KERNEL_SYMBOLS["mt_decode_step_persistent"] in r["Kernel_Name"]]
+                if KERNEL_SYMBOLS[kernel] in r["Kernel_Name"]]
         return max(copies), kern
-
-    from audio_midi_transformer_amd import synth
 
     known_kib = float(calib_mib) * 1024.0
     f_copy, f_kern = load(fetch_csv, "FETCH_SIZE")
@@ -168,9 +173,9 @@ def reduce_counters(fetch_csv: str, write_csv: str, workload_key: str, calib_mib
     fetch = float(np.mean(f_kern)) * 1024.0 * f_scale
     write = float(np.mean(w_kern)) * 1024.0 * w_scale
     return {
-        "kernel": "mt_decode_step_persistent",
+        "kernel": kernel,
         "workload": workload_key,
-        "source_hash": kernel_source_hash(),
+        "source_hash": kernel_source_hash(kernel),
         "launches": len(f_kern),
         "calibration_copy_bytes": int(known_kib * 1024),
         "fetch_scale": round(f_scale, 4),
