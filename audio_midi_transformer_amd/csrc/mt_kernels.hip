@@ -1671,7 +1671,7 @@ hipError_t launch_layernorm(const float* x, long ldx, const float* g, const floa
 int splitk_plan(int M, const Int4Mat& w) {
     // INT4 weights, 64 x 64 tiles: split K where the unsplit grid would
     // leave CUs idle, up to 4 ways (at least 256 columns of K each)
-    if (w.fmt != WF_INT4 || w.N % 4) return 1;
+    if (w.fmt != WF_INT4 || w.N % 4 || w.N > 8 * 256) return 1;  // k_splitk_add holds a row in 8 per thread
     const long tiles = (long)((M + 63) / 64) * ((w.N + 63) / 64);
     if (tiles >= 256) return 1;
     for (int c = 4; c >= 2; --c)
